@@ -1,0 +1,182 @@
+"""CPU oracle for the 32-bit two-state optimizer update.
+
+TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and
+the CPU-baseline leg of ``bench.py`` may import this package.  The product
+path (``optimizer_update_amd``) never imports it, and the two share no code.
+
+This module is a ctypes wrapper around ``oracle.c`` (a plain per-element C
+loop; see that file for the formulas and the passages they follow).  Arrays
+are numpy: fp32 storage as ``float32``; fp16 and bf16 storage as ``uint16``
+bit patterns; states as ``float32``.  Every call updates its arguments in
+place, exactly like the product entry points.
+
+``oracle_update_f32`` is the parity oracle.  ``oracle_update_f64`` exists to
+check the formulas against closed forms.  Parity is pinned for every function
+here (see ``tests/test_oracle_*.py``) except where a docstring says
+"parity unpinned".
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+import tempfile
+from dataclasses import dataclass
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+SOURCE = os.path.join(HERE, "oracle.c")
+LIBRARY = os.path.join(HERE, "liboracle.so")
+
+ADAM, ADEMAMIX = 0, 1
+F32, F16, BF16 = 0, 1, 2
+KINDS = {"adam": ADAM, "ademamix": ADEMAMIX}
+DTYPES = {"fp32": F32, "fp16": F16, "bf16": BF16}
+
+# -O2 without contraction or fast-math: each C operation is one correctly
+# rounded IEEE operation, and denormals are kept (no crtfastmath, no FTZ/DAZ).
+CFLAGS = ["-O2", "-std=c11", "-ffp-contract=off", "-fno-fast-math",
+          "-fno-unsafe-math-optimizations", "-fopenmp", "-fPIC", "-shared"]
+
+
+def build(out_path: str = LIBRARY, plant: int = 0) -> str:
+    """Compile ``oracle.c`` with gcc into ``out_path`` (atomically).
+
+    ``plant`` != 0 builds a copy with one planted mistake; the test suite uses
+    it to show that the pins catch such mistakes."""
+    cmd = ["gcc", *CFLAGS]
+    if plant:
+        cmd.append(f"-DORACLE_PLANT={int(plant)}")
+    fd, tmp = tempfile.mkstemp(suffix=".so", dir=os.path.dirname(out_path) or ".")
+    os.close(fd)
+    try:
+        subprocess.run(cmd + ["-o", tmp, SOURCE, "-lm"], check=True)
+        os.replace(tmp, out_path)
+    finally:
+        if os.path.exists(tmp):
+            os.unlink(tmp)
+    return out_path
+
+
+class _Scalars32(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_float) for n in ("bc1", "bc2", "decay", "omb1", "omb2", "omb3")]
+
+
+@dataclass(frozen=True)
+class HParams:
+    """Hyperparameters of one step.  beta3 and alpha are used by AdEMAMix only."""
+    lr: float = 1e-3
+    beta1: float = 0.9
+    beta2: float = 0.999
+    beta3: float = 0.9999
+    alpha: float = 5.0
+    eps: float = 1e-8
+    weight_decay: float = 0.0
+    skip_zeros: bool = False
+
+
+def _ptr(a: np.ndarray) -> ctypes.c_void_p:
+    assert a.flags.c_contiguous
+    return ctypes.c_void_p(a.ctypes.data)
+
+
+class Oracle:
+    """A loaded oracle library (the normal one, or a planted-mistake copy)."""
+
+    def __init__(self, path: str):
+        self.path = path
+        lib = ctypes.CDLL(path)
+        self._lib = lib
+        i64, f32, f64, vp, ci = (ctypes.c_int64, ctypes.c_float, ctypes.c_double,
+                                 ctypes.c_void_p, ctypes.c_int)
+        lib.oracle_update_f32.argtypes = [ci, ci, vp, vp, vp, vp, i64,
+                                          f32, f32, f32, f32, f32, f32, i64, f32, ci, ci]
+        lib.oracle_update_f32.restype = ci
+        lib.oracle_update_f64.argtypes = [ci, vp, vp, vp, vp, i64,
+                                          f64, f64, f64, f64, f64, f64, i64, f64, ci]
+        lib.oracle_update_f64.restype = ci
+        lib.oracle_step_scalars.argtypes = [f32, f32, f32, f32, f32, i64,
+                                            ctypes.POINTER(_Scalars32)]
+        lib.oracle_step_scalars.restype = None
+        for name in ("oracle_f32_to_bf16_array", "oracle_f32_to_f16_array",
+                     "oracle_f16_to_f32_array", "oracle_bf16_to_f32_array"):
+            getattr(lib, name).argtypes = [vp, vp, i64]
+            getattr(lib, name).restype = None
+        lib.oracle_max_threads.restype = ci
+        lib.oracle_planted.restype = ci
+        self.planted = lib.oracle_planted()
+
+    # ------------------------------------------------------------ storage
+    def f32_to_storage(self, x: np.ndarray, dtype: int) -> np.ndarray:
+        """fp32 -> storage dtype, round to nearest even (fp32 is a copy)."""
+        x = np.ascontiguousarray(x, dtype=np.float32)
+        if dtype == F32:
+            return x.copy()
+        y = np.empty(x.shape, np.uint16)
+        fn = self._lib.oracle_f32_to_f16_array if dtype == F16 else self._lib.oracle_f32_to_bf16_array
+        fn(_ptr(x), _ptr(y), x.size)
+        return y
+
+    def storage_to_f32(self, x: np.ndarray, dtype: int) -> np.ndarray:
+        """storage dtype -> fp32 (exact)."""
+        if dtype == F32:
+            return np.ascontiguousarray(x, dtype=np.float32).copy()
+        x = np.ascontiguousarray(x, dtype=np.uint16)
+        y = np.empty(x.shape, np.float32)
+        fn = self._lib.oracle_f16_to_f32_array if dtype == F16 else self._lib.oracle_bf16_to_f32_array
+        fn(_ptr(x), _ptr(y), x.size)
+        return y
+
+    # ------------------------------------------------------------ update
+    def step_scalars(self, hp: HParams, step: int) -> dict:
+        out = _Scalars32()
+        self._lib.oracle_step_scalars(hp.beta1, hp.beta2, hp.beta3, hp.lr,
+                                      hp.weight_decay, step, ctypes.byref(out))
+        return {n: getattr(out, n) for n, _ in _Scalars32._fields_}
+
+    def update_f32(self, kind: int, dtype: int, param: np.ndarray, grad: np.ndarray,
+                   state1: np.ndarray, state2: np.ndarray, hp: HParams, step: int,
+                   nthreads: int = 1) -> None:
+        """One step of the fp32 update, in place (see ``oracle_update_f32``)."""
+        n = param.size
+        sdt = np.float32 if dtype == F32 else np.uint16
+        assert param.dtype == sdt and grad.dtype == sdt and grad.size == n
+        assert state1.dtype == np.float32 and state2.dtype == np.float32
+        assert state1.size == (2 * n if kind == ADEMAMIX else n) and state2.size == n
+        rc = self._lib.oracle_update_f32(
+            kind, dtype, _ptr(param), _ptr(grad), _ptr(state1), _ptr(state2), n,
+            hp.beta1, hp.beta2, hp.beta3, hp.alpha, hp.eps, hp.weight_decay, step,
+            hp.lr, int(bool(hp.skip_zeros)), nthreads)
+        if rc != 0:
+            raise ValueError(f"oracle_update_f32 rejected kind={kind} dtype={dtype}")
+
+    def update_f64(self, kind: int, param: np.ndarray, grad: np.ndarray, state1: np.ndarray,
+                   state2: np.ndarray, hp: HParams, step: int) -> None:
+        """One step of the binary64 update, in place (see ``oracle_update_f64``)."""
+        n = param.size
+        for a in (param, grad, state1, state2):
+            assert a.dtype == np.float64 and a.flags.c_contiguous
+        assert state1.size == (2 * n if kind == ADEMAMIX else n) and state2.size == n
+        rc = self._lib.oracle_update_f64(
+            kind, _ptr(param), _ptr(grad), _ptr(state1), _ptr(state2), n,
+            hp.beta1, hp.beta2, hp.beta3, hp.alpha, hp.eps, hp.weight_decay, step,
+            hp.lr, int(bool(hp.skip_zeros)))
+        if rc != 0:
+            raise ValueError(f"oracle_update_f64 rejected kind={kind}")
+
+    def max_threads(self) -> int:
+        return self._lib.oracle_max_threads()
+
+
+_default: Oracle | None = None
+
+
+def load() -> Oracle:
+    """The oracle library next to this file; compiled first only if absent."""
+    global _default
+    if _default is None:
+        if not os.path.exists(LIBRARY):
+            build(LIBRARY)
+        _default = Oracle(LIBRARY)
+    return _default

@@ -1,0 +1,384 @@
+/*
+ * CPU oracle for the 32-bit two-state optimizer update (Adam/AdamW and
+ * AdEMAMix).
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the product path loads, links or
+ * calls this file.  Only the test suite, the smoke check and the benchmark's
+ * CPU-baseline leg use it, and it shares no code, header, table or helper
+ * with the HIP library.
+ *
+ * Subject page: "Investigate a 256-thread SM103 path for small 32-bit
+ * optimizer tensors" (bitsandbytes fork, issue 8).  The page names the two
+ * update kinds ADAM and ADEMAMIX, fp32/fp16/bf16 parameter and gradient
+ * storage with fp32 states (section "Correctness oracle"), decoupled weight
+ * decay (section "Scope") and an unchanged state layout (section
+ * "Non-goals").  It prints no formula, so the formulas are the textbook ones:
+ *   - moments and bias correction: Kingma & Ba 2015, Algorithm 1;
+ *   - decoupled weight decay:     Loshchilov & Hutter 2019, Algorithm 2;
+ *   - slow EMA mixed in with alpha: Pagliardini, Ablin & Grangier 2024,
+ *     Algorithm 1 (the slow EMA is not bias-corrected; alpha and beta3 are
+ *     held constant).
+ *
+ * Two instantiations:
+ *   oracle_update_f32  every operation is one IEEE binary32 operation with
+ *                      round-to-nearest-even (build with -ffp-contract=off,
+ *                      no fast-math, no flush-to-zero).  This is the parity
+ *                      oracle: the page fixes the states at 32 bits.
+ *   oracle_update_f64  the same steps in binary64, used only to check the
+ *                      formulas against closed forms.
+ *
+ * Storage conversions (binary16 and bfloat16) are written out from the IEEE
+ * 754 / bfloat16 encodings: round to nearest, ties to even; overflow goes to
+ * infinity; subnormals are kept; a NaN stays a quiet NaN (payload not kept).
+ *
+ * ORACLE_PLANT (compile-time, default 0) plants one known mistake so that
+ * the test suite can show its pins catch it.  It is never set in a normal
+ * build.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+#ifndef ORACLE_PLANT
+#define ORACLE_PLANT 0
+#endif
+
+enum { ORACLE_ADAM = 0, ORACLE_ADEMAMIX = 1 };
+enum { ORACLE_F32 = 0, ORACLE_F16 = 1, ORACLE_BF16 = 2 };
+
+static float f32_from_bits(uint32_t u) { float f; memcpy(&f, &u, sizeof f); return f; }
+static uint32_t bits_from_f32(float f) { uint32_t u; memcpy(&u, &f, sizeof u); return u; }
+
+/* ---------------------------------------------------------------- storage */
+
+/* bfloat16 is the upper half of a binary32: widening appends 16 zero bits. */
+float oracle_bf16_to_f32(uint16_t h) { return f32_from_bits((uint32_t)h << 16); }
+
+/* binary32 -> bfloat16, round to nearest, ties to even.  The kept part is
+ * the upper 16 bits; the dropped part decides the rounding. */
+uint16_t oracle_f32_to_bf16(float f)
+{
+    uint32_t u = bits_from_f32(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u)          /* NaN -> quiet NaN */
+        return (uint16_t)((u >> 16) | 0x0040u);
+    uint32_t kept = u >> 16;
+    uint32_t dropped = u & 0xffffu;
+#if ORACLE_PLANT == 11
+    dropped = 0;                                    /* planted: truncation */
+#endif
+    if (dropped > 0x8000u || (dropped == 0x8000u && (kept & 1u)))
+        kept += 1;                                  /* carries into the exponent; max finite -> inf */
+    return (uint16_t)kept;
+}
+
+/* binary16 -> binary32 (exact).  value = (-1)^s * m * 2^-24 for subnormals,
+ * (-1)^s * (1024 + m) * 2^(e-25) for normals. */
+float oracle_f16_to_f32(uint16_t h)
+{
+    int sign = h >> 15, e = (h >> 10) & 0x1f, m = h & 0x3ff;
+    float mag;
+    if (e == 0x1f)
+        mag = m ? NAN : INFINITY;
+    else if (e == 0)
+        mag = ldexpf((float)m, -24);
+    else
+        mag = ldexpf((float)(m + 1024), e - 25);
+    return sign ? -mag : mag;
+}
+
+/* binary32 -> binary16, round to nearest, ties to even.
+ * Write |x| = M * 2^E exactly, pick the binary16 quantum 2^Q that applies to
+ * |x| (2^(floor(log2|x|) - 10) in the normal range, 2^-24 below it), round
+ * M * 2^(E-Q) to an integer R (ties to even) and encode R * 2^Q. */
+uint16_t oracle_f32_to_f16(float f)
+{
+    uint32_t u = bits_from_f32(f);
+    uint16_t sign = (uint16_t)((u >> 16) & 0x8000u);
+    uint32_t e = (u >> 23) & 0xffu, frac = u & 0x7fffffu;
+    if (e == 0xffu)
+        return (uint16_t)(sign | (frac ? 0x7e00u : 0x7c00u));
+    if (e == 0 && frac == 0)
+        return sign;
+    uint32_t M;
+    int E;
+    if (e == 0) { M = frac; E = -149; }
+    else        { M = frac | 0x800000u; E = (int)e - 150; }
+    int lead = E;                                   /* exponent of M's top bit */
+    for (uint32_t t = M >> 1; t; t >>= 1) lead++;
+    int Q = (lead >= -14) ? lead - 10 : -24;
+#if ORACLE_PLANT == 12
+    Q = lead - 10;                                  /* planted: no subnormal range */
+#endif
+    int s = Q - E;                                  /* bits dropped, always > 0 here */
+    uint32_t R, rem, half;
+    if (s > 25) {                                   /* M < 2^24 < half: rounds to 0 */
+        R = 0; rem = 0; half = 1;
+    } else {
+        R = M >> s;
+        rem = M - (R << s);
+        half = 1u << (s - 1);
+    }
+    if (rem > half || (rem == half && (R & 1u)))
+        R += 1;
+    if (Q == -24)                                   /* subnormal; R == 1024 is the smallest normal */
+        return (uint16_t)(sign | R);
+    int be = Q + 25;                                /* biased exponent for R in [1024, 2048) */
+    if (R == 2048) { R = 1024; be += 1; }
+    if (be >= 31)
+        return (uint16_t)(sign | 0x7c00u);          /* overflow -> infinity */
+    return (uint16_t)(sign | ((uint32_t)be << 10) | (R - 1024));
+}
+
+void oracle_f32_to_bf16_array(const float* x, uint16_t* y, int64_t n)
+{ for (int64_t i = 0; i < n; i++) y[i] = oracle_f32_to_bf16(x[i]); }
+void oracle_f32_to_f16_array(const float* x, uint16_t* y, int64_t n)
+{ for (int64_t i = 0; i < n; i++) y[i] = oracle_f32_to_f16(x[i]); }
+void oracle_f16_to_f32_array(const uint16_t* x, float* y, int64_t n)
+{ for (int64_t i = 0; i < n; i++) y[i] = oracle_f16_to_f32(x[i]); }
+void oracle_bf16_to_f32_array(const uint16_t* x, float* y, int64_t n)
+{ for (int64_t i = 0; i < n; i++) y[i] = oracle_bf16_to_f32(x[i]); }
+
+static float load_storage(const void* base, int dtype, int64_t i)
+{
+    if (dtype == ORACLE_F32) return ((const float*)base)[i];
+    if (dtype == ORACLE_F16) return oracle_f16_to_f32(((const uint16_t*)base)[i]);
+    return oracle_bf16_to_f32(((const uint16_t*)base)[i]);
+}
+
+static void store_storage(void* base, int dtype, int64_t i, float x)
+{
+    if (dtype == ORACLE_F32) ((float*)base)[i] = x;
+    else if (dtype == ORACLE_F16) ((uint16_t*)base)[i] = oracle_f32_to_f16(x);
+    else ((uint16_t*)base)[i] = oracle_f32_to_bf16(x);
+}
+
+/* --------------------------------------------------------- step scalars */
+
+/* Per-step scalars of the fp32 instantiation.  The bias corrections
+ * 1 - beta^t and the decay factor 1 - lr*wd are formed in binary64 from the
+ * binary32 arguments and then rounded to binary32; 1 - beta is formed in
+ * binary32 (exact for beta in [0.5, 1]). */
+typedef struct {
+    float bc1, bc2, decay, omb1, omb2, omb3;
+} oracle_scalars32;
+
+void oracle_step_scalars(float beta1, float beta2, float beta3, float lr,
+                         float weight_decay, int64_t step, oracle_scalars32* out)
+{
+    double t = (double)step;
+#if ORACLE_PLANT == 13
+    t = (double)(step + 1);                         /* planted: step off by one */
+#endif
+    out->bc1 = (float)(1.0 - pow((double)beta1, t));
+    out->bc2 = (float)(1.0 - pow((double)beta2, t));
+#if ORACLE_PLANT == 4
+    out->decay = (float)(1.0 + (double)lr * (double)weight_decay);  /* planted: decay sign */
+#else
+    out->decay = (float)(1.0 - (double)lr * (double)weight_decay);
+#endif
+    out->omb1 = 1.0f - beta1;
+    out->omb2 = 1.0f - beta2;
+    out->omb3 = 1.0f - beta3;
+}
+
+/* ------------------------------------------------------ fp32 instantiation */
+
+/* One element, binary32.  m, v: first and second moment; m2: slow EMA
+ * (AdEMAMix only).  Returns the new parameter value before rounding to the
+ * storage type. */
+static float element_f32(int kind, float p, float g, float* m, float* v, float* m2,
+                         const oracle_scalars32* s, float beta1, float beta2, float beta3,
+                         float alpha, float eps, float lr)
+{
+    /* first and second moment (Kingma & Ba, Algorithm 1) */
+    float mn = beta1 * (*m) + s->omb1 * g;
+#if ORACLE_PLANT == 9
+    float vn = beta2 * (*v) + s->omb2 * fabsf(g);   /* planted: dropped square */
+#else
+    float vn = beta2 * (*v) + s->omb2 * (g * g);
+#endif
+    float m2n = 0.0f;
+    if (kind == ORACLE_ADEMAMIX)                   /* slow EMA (Pagliardini et al., Algorithm 1) */
+        m2n = beta3 * (*m2) + s->omb3 * g;
+
+    /* bias-corrected moments and the direction */
+    float mh = mn / s->bc1;
+#if ORACLE_PLANT == 1
+    float vh = vn;                                  /* planted: v not bias-corrected */
+#else
+    float vh = vn / s->bc2;
+#endif
+#if ORACLE_PLANT == 2
+    float den = sqrtf(vh + eps);                    /* planted: eps inside the root */
+#else
+    float den = sqrtf(vh) + eps;
+#endif
+    float num = mh;
+    if (kind == ORACLE_ADEMAMIX) {
+#if ORACLE_PLANT == 5
+        num = mh + alpha * (m2n / s->bc1);          /* planted: slow EMA bias-corrected */
+#elif ORACLE_PLANT == 6
+        num = alpha * mh + m2n;                     /* planted: alpha on the wrong EMA */
+#else
+        num = mh + alpha * m2n;
+#endif
+    }
+    float upd = num / den;
+
+    /* decoupled weight decay on the old parameter (Loshchilov & Hutter, Algorithm 2) */
+#if ORACLE_PLANT == 3
+    float pn = (p - lr * upd) * s->decay;           /* planted: decay after the update */
+#else
+    float pn = p * s->decay - lr * upd;
+#endif
+    *m = mn;
+    *v = vn;
+    if (kind == ORACLE_ADEMAMIX) *m2 = m2n;
+    return pn;
+}
+
+/* One optimizer step over n elements, in place.
+ *   param, grad : n elements of the storage dtype (fp32, fp16 or bf16 bits)
+ *   state1      : n floats (ADAM) or 2n floats (ADEMAMIX: fast EMA at [0, n),
+ *                 slow EMA at [n, 2n))
+ *   state2      : n floats
+ *   step        : 1-based index of the update being applied
+ * With skip_zeros set, an element whose gradient compares equal to zero
+ * (+0 or -0) is left untouched: no moment update and no decay.
+ * grad is only read.  Returns 0, or -1 on an invalid kind or dtype. */
+int oracle_update_f32(int kind, int dtype, void* param, const void* grad,
+                      float* state1, float* state2, int64_t n,
+                      float beta1, float beta2, float beta3, float alpha, float eps,
+                      float weight_decay, int64_t step, float lr, int skip_zeros,
+                      int nthreads)
+{
+    if ((kind != ORACLE_ADAM && kind != ORACLE_ADEMAMIX) ||
+        (dtype != ORACLE_F32 && dtype != ORACLE_F16 && dtype != ORACLE_BF16))
+        return -1;
+    oracle_scalars32 s;
+#if ORACLE_PLANT == 7
+    oracle_step_scalars(beta2, beta1, beta3, lr, weight_decay, step, &s);  /* planted: betas swapped */
+    { float t = beta1; beta1 = beta2; beta2 = t; }
+#else
+    oracle_step_scalars(beta1, beta2, beta3, lr, weight_decay, step, &s);
+#endif
+    if (nthreads < 1) nthreads = 1;
+#pragma omp parallel for schedule(static) num_threads(nthreads)
+    for (int64_t i = 0; i < n; i++) {
+        float g = load_storage(grad, dtype, i);
+        if (skip_zeros && g == 0.0f) {
+#if ORACLE_PLANT == 8
+            store_storage(param, dtype, i, load_storage(param, dtype, i) * s.decay);  /* planted: decay on skip */
+#endif
+            continue;
+        }
+        float p = load_storage(param, dtype, i);
+        float* m2 = (kind == ORACLE_ADEMAMIX) ? &state1[n + i] : NULL;
+#if ORACLE_PLANT == 14
+        if (kind == ORACLE_ADEMAMIX) m2 = &state1[2 * n - 1 - i];   /* planted: slow plane reversed */
+#endif
+        float pn = element_f32(kind, p, g, &state1[i], &state2[i], m2, &s,
+                               beta1, beta2, beta3, alpha, eps, lr);
+        store_storage(param, dtype, i, pn);
+#if ORACLE_PLANT == 10
+        if (dtype == ORACLE_F32) ((float*)grad)[i] = pn;           /* planted: grad written */
+#endif
+    }
+    return 0;
+}
+
+/* ------------------------------------------------------ fp64 instantiation */
+
+/* The same update with every operation in binary64 and the step scalars
+ * unrounded.  fp64 arrays only; used to check the formulas against closed
+ * forms.  Layout and arguments as oracle_update_f32. */
+int oracle_update_f64(int kind, double* param, const double* grad, double* state1,
+                      double* state2, int64_t n, double beta1, double beta2, double beta3,
+                      double alpha, double eps, double weight_decay, int64_t step,
+                      double lr, int skip_zeros)
+{
+    if (kind != ORACLE_ADAM && kind != ORACLE_ADEMAMIX)
+        return -1;
+#if ORACLE_PLANT == 7
+    { double t = beta1; beta1 = beta2; beta2 = t; }
+#endif
+    double t = (double)step;
+#if ORACLE_PLANT == 13
+    t = (double)(step + 1);
+#endif
+    double bc1 = 1.0 - pow(beta1, t);
+    double bc2 = 1.0 - pow(beta2, t);
+    (void)bc2;
+#if ORACLE_PLANT == 4
+    double decay = 1.0 + lr * weight_decay;
+#else
+    double decay = 1.0 - lr * weight_decay;
+#endif
+    for (int64_t i = 0; i < n; i++) {
+        double g = grad[i];
+        if (skip_zeros && g == 0.0) {
+#if ORACLE_PLANT == 8
+            param[i] = param[i] * decay;
+#endif
+            continue;
+        }
+        double m = beta1 * state1[i] + (1.0 - beta1) * g;
+#if ORACLE_PLANT == 9
+        double v = beta2 * state2[i] + (1.0 - beta2) * fabs(g);
+#else
+        double v = beta2 * state2[i] + (1.0 - beta2) * (g * g);
+#endif
+        int64_t slow = n + i;
+#if ORACLE_PLANT == 14
+        slow = 2 * n - 1 - i;
+#endif
+        double m2 = 0.0;
+        if (kind == ORACLE_ADEMAMIX)
+            m2 = beta3 * state1[slow] + (1.0 - beta3) * g;
+        double mh = m / bc1;
+#if ORACLE_PLANT == 1
+        double vh = v;
+#else
+        double vh = v / bc2;
+#endif
+#if ORACLE_PLANT == 2
+        double den = sqrt(vh + eps);
+#else
+        double den = sqrt(vh) + eps;
+#endif
+        double num = mh;
+        if (kind == ORACLE_ADEMAMIX) {
+#if ORACLE_PLANT == 5
+            num = mh + alpha * (m2 / bc1);
+#elif ORACLE_PLANT == 6
+            num = alpha * mh + m2;
+#else
+            num = mh + alpha * m2;
+#endif
+        }
+        double upd = num / den;
+#if ORACLE_PLANT == 3
+        param[i] = (param[i] - lr * upd) * decay;
+#else
+        param[i] = param[i] * decay - lr * upd;
+#endif
+        state1[i] = m;
+        state2[i] = v;
+        if (kind == ORACLE_ADEMAMIX) state1[slow] = m2;
+    }
+    return 0;
+}
+
+int oracle_max_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
+
+int oracle_planted(void) { return ORACLE_PLANT; }

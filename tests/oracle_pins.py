@@ -1,0 +1,426 @@
+"""Pins that tie the CPU oracle to something other than itself.
+
+Each ``pin_*`` function takes a loaded ``oracle.Oracle`` and raises
+``AssertionError`` when the oracle disagrees with what the mathematics, the
+IEEE definitions or an independent library routine fix.  The regular suite
+runs every pin against the oracle (all must pass); the planted-mistake suite
+runs them against copies of the oracle with one known mistake compiled in
+(at least one must fail for each).
+
+``INDEPENDENT`` pins check the formulas without retyping them (closed forms,
+invariants, torch's own Adam/AdamW, IEEE conversions).  The exact-emulation
+pin retypes the operation sequence and pins only its rounding.
+
+Formulas are the textbook ones (Kingma & Ba 2015 Alg. 1; Loshchilov & Hutter
+2019 Alg. 2; Pagliardini, Ablin & Grangier 2024 Alg. 1); the page
+"Investigate a 256-thread SM103 path for small 32-bit optimizer tensors"
+names the kinds and storage types (section "Correctness oracle") and prints
+no formula.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+import torch
+
+import oracle as O
+from tests import exact_fp32 as X
+from workloads import cast_storage, rng
+
+HP_CFG1 = O.HParams(lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.0)
+
+
+def _run_f32(orc, kind, dtype, p, grads_per_step, hp, steps, s1=None, s2=None):
+    n = p.size
+    p = p.copy()
+    if s1 is None:
+        s1 = np.zeros((2 if kind == O.ADEMAMIX else 1) * n, np.float32)
+        s2 = np.zeros(n, np.float32)
+    for t in range(1, steps + 1):
+        orc.update_f32(kind, dtype, p, grads_per_step(t), s1, s2, hp, t)
+    return p, s1, s2
+
+
+def _run_f64(orc, kind, p0, g, hp, steps):
+    n = p0.size
+    p = p0.astype(np.float64).copy()
+    s1 = np.zeros((2 if kind == O.ADEMAMIX else 1) * n)
+    s2 = np.zeros(n)
+    gg = g.astype(np.float64)
+    out = []
+    for t in range(1, steps + 1):
+        orc.update_f64(kind, p, gg, s1, s2, hp, t)
+        out.append((p.copy(), s1.copy(), s2.copy()))
+    return out
+
+
+# --------------------------------------------------------------- closed form
+
+def pin_closed_form_f64(orc):
+    """Constant gradient g, zero initial states.  Exactly
+    m_t = (1 - b1^t) g and v_t = (1 - b2^t) g^2, so the bias-corrected
+    moments are g and g^2 and every step moves p by u = lr g / (|g| + eps)
+    after the decay d = 1 - lr wd of the old p:
+        p_t = d^t p0 - u (1 - d^t) / (1 - d)           (p_t = p0 - t u at wd = 0)
+    AdEMAMix: the slow EMA is m2_k = (1 - b3^k) g (not bias-corrected) and
+        p_t = d^t p0 - sum_k d^(t-k) lr g (1 + alpha (1 - b3^k)) / (|g| + eps)."""
+    g = np.array([1.0, -0.5, 3e-3, -2.5e-6, 7.0], np.float64)
+    p0 = np.array([0.5, -0.25, 0.125, 0.9, -0.75], np.float64)
+    T = 1000
+    for kind in (O.ADAM, O.ADEMAMIX):
+        for wd in (0.0, 0.1):
+            hp = O.HParams(lr=1e-3, beta1=0.9, beta2=0.999, beta3=0.9999, alpha=5.0,
+                           eps=1e-8, weight_decay=wd)
+            traj = _run_f64(orc, kind, p0, g, hp, T)
+            d = 1.0 - hp.lr * wd
+            acc = p0.copy()
+            for t in range(1, T + 1):
+                coef = 1.0 + (hp.alpha * (1.0 - hp.beta3 ** t) if kind == O.ADEMAMIX else 0.0)
+                acc = acc * d - hp.lr * g * coef / (np.abs(g) + hp.eps)
+                if t in (1, 2, 10, 100, 1000):
+                    p, s1, s2 = traj[t - 1]
+                    n = g.size
+                    m_ref = (1.0 - hp.beta1 ** t) * g
+                    v_ref = (1.0 - hp.beta2 ** t) * g * g
+                    scale = np.abs(p0) + t * hp.lr * (1 + hp.alpha)
+                    assert np.all(np.abs(p - acc) <= 1e-12 * scale), (kind, wd, t, p, acc)
+                    assert np.allclose(s1[:n], m_ref, rtol=1e-12, atol=0), (kind, wd, t, "m")
+                    assert np.allclose(s2, v_ref, rtol=1e-12, atol=0), (kind, wd, t, "v")
+                    if kind == O.ADEMAMIX:
+                        m2_ref = (1.0 - hp.beta3 ** t) * g
+                        assert np.allclose(s1[n:], m2_ref, rtol=1e-12, atol=0), (wd, t, "m2")
+            if wd == 0.0 and kind == O.ADAM:   # the plain form of the sum
+                p, _, _ = traj[T - 1]
+                u = hp.lr * g / (np.abs(g) + hp.eps)
+                assert np.all(np.abs(p - (p0 - T * u)) <= 1e-12 * (np.abs(p0) + T * hp.lr))
+
+
+def pin_f32_tracks_f64(orc):
+    """The binary32 instantiation follows the same formulas as the binary64
+    one: over 10 steps of random gradients its parameters stay within a
+    bound set by binary32 rounding (1e-5 lr per step), far below the effect
+    of any dropped or misplaced term at lr = 1e-2, wd = 0.1 (decaying after
+    instead of before the update alone moves p by lr^2 wd |u| = 1e-5 per
+    step)."""
+    n, T = 257, 10
+    g0 = rng(7, 1)
+    p0 = g0.uniform(-1, 1, n).astype(np.float32)
+    gs = [g0.standard_normal(n).astype(np.float32) for _ in range(T)]
+    for kind in (O.ADAM, O.ADEMAMIX):
+        hp = O.HParams(lr=1e-2, beta1=0.9, beta2=0.999, beta3=0.9999, alpha=5.0,
+                       eps=1e-8, weight_decay=0.1)
+        # the binary64 run gets the binary32 values of the hyperparameters
+        hp64 = O.HParams(**{k: float(np.float32(v)) if isinstance(v, float) else v
+                            for k, v in hp.__dict__.items()})
+        p32, s1_32, s2_32 = _run_f32(orc, kind, O.F32, p0, lambda t: gs[t - 1], hp, T)
+        p64 = p0.astype(np.float64)
+        s1 = np.zeros((2 if kind == O.ADEMAMIX else 1) * n)
+        s2 = np.zeros(n)
+        for t in range(1, T + 1):
+            orc.update_f64(kind, p64, gs[t - 1].astype(np.float64), s1, s2, hp64, t)
+        assert np.max(np.abs(p32 - p64)) <= 1e-5 * hp.lr * T, (kind, np.max(np.abs(p32 - p64)))
+        assert np.allclose(s2_32, s2, rtol=1e-6, atol=0), kind
+        assert np.allclose(s1_32, s1, rtol=1e-6, atol=1e-7), kind
+
+
+def pin_first_step_by_hand(orc):
+    """The first step from zero states, worked by hand for one element:
+    lr 1e-3, b1 0.9, b2 0.999, eps 1e-8, wd 0.01, p0 = 0.5, g = 0.25 gives
+    m1 = 0.1 * 0.25 = 0.025, v1 = 0.001 * 0.0625 = 6.25e-5, m^ = 0.25,
+    v^ = 0.0625, u = 0.25 / (0.25 + 1e-8) and
+    p1 = 0.5 * (1 - 1e-5) - 1e-3 * u = 0.49899500004.
+    A second step with g = -0.125: m2 = 0.0225 - 0.0125 = 0.01,
+    v2 = 0.999 * 6.25e-5 + 0.001 * 0.015625 = 7.80625e-5, m^ = 0.01 / 0.19,
+    v^ = 7.80625e-5 / 0.001999, p2 = p1 (1 - 1e-5) - 1e-3 m^ / (sqrt(v^) + 1e-8)
+    = 0.4987236...  The binary32 values must agree to binary32 precision
+    (the decimal hyperparameters are not exact in binary32, which moves
+    1 - b2 by 1.3e-5 relative; the bound allows for that)."""
+    hp = O.HParams(lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.01)
+    p = np.array([0.5], np.float32)
+    s1 = np.zeros(1, np.float32)
+    s2 = np.zeros(1, np.float32)
+    orc.update_f32(O.ADAM, O.F32, p, np.array([0.25], np.float32), s1, s2, hp, 1)
+    p1 = 0.5 * (1 - 1e-5) - 1e-3 * 0.25 / (0.25 + 1e-8)
+    assert abs(p[0] - p1) <= 1e-7, p[0]
+    assert abs(s1[0] - 0.025) <= 1e-8, s1[0]
+    assert abs(s2[0] - 6.25e-5) <= 6.25e-5 * 2e-5, s2[0]
+    orc.update_f32(O.ADAM, O.F32, p, np.array([-0.125], np.float32), s1, s2, hp, 2)
+    mh = 0.01 / 0.19
+    vh = 7.80625e-5 / (1 - 0.999 ** 2)
+    p2 = p1 * (1 - 1e-5) - 1e-3 * mh / (math.sqrt(vh) + 1e-8)
+    assert abs(s1[0] - 0.01) <= 1e-8, s1[0]
+    assert abs(s2[0] - 7.80625e-5) <= 7.80625e-5 * 2e-5, s2[0]
+    assert abs(p[0] - p2) <= 1e-7, (p[0], p2)
+
+
+# ------------------------------------------------------------- library routine
+
+def pin_torch_adam(orc):
+    """Adam (wd 0) and AdamW against torch.optim on the CPU in fp32, with
+    dyadic hyperparameters so that both sides start from the same exact
+    constants.  torch arranges the arithmetic differently (lerp for m,
+    sqrt(v)/sqrt(bc2)), so the comparison has a tolerance: v within 8 ulp,
+    m within 1e-6 of max|g| (lerp cancels differently near zero crossings).  p: within 2e-6 relative plus
+    1e-6 lr absolute (near zero crossings torch's rounding of the step
+    differs by a few 1e-7 of lr)."""
+    n, T = 4096, 10
+    for cls, wd in ((torch.optim.Adam, 0.0), (torch.optim.AdamW, 2.0 ** -7)):
+        hp = O.HParams(lr=2.0 ** -10, beta1=0.875, beta2=1 - 2.0 ** -10, eps=2.0 ** -27,
+                       weight_decay=wd)
+        gen = rng(11, int(wd > 0))
+        p0 = gen.uniform(-1, 1, n).astype(np.float32)
+        gs = [gen.standard_normal(n).astype(np.float32) for _ in range(T)]
+        p, s1, s2 = _run_f32(orc, O.ADAM, O.F32, p0, lambda t: gs[t - 1], hp, T)
+
+        tp = torch.nn.Parameter(torch.from_numpy(p0.copy()))
+        opt = cls([tp], lr=hp.lr, betas=(hp.beta1, hp.beta2), eps=hp.eps, weight_decay=wd,
+                  foreach=False)
+        for t in range(T):
+            tp.grad = torch.from_numpy(gs[t].copy())
+            opt.step()
+        st = opt.state[tp]
+        tp_ = tp.detach().numpy()
+        m_ = st["exp_avg"].numpy()
+        v_ = st["exp_avg_sq"].numpy()
+
+        def ulps(a, b):
+            ia = a.view(np.int32).astype(np.int64)
+            ib = b.view(np.int32).astype(np.int64)
+            ia = np.where(ia < 0, -(ia & 0x7fffffff), ia)
+            ib = np.where(ib < 0, -(ib & 0x7fffffff), ib)
+            return np.abs(ia - ib)
+
+        err = np.abs(p - tp_)
+        assert np.all(err <= 2e-6 * np.abs(tp_) + 1e-6 * hp.lr), (cls.__name__, err.max())
+        assert np.max(ulps(s2, v_)) <= 8, (cls.__name__, np.max(ulps(s2, v_)))
+        gmax = max(float(np.max(np.abs(x))) for x in gs)
+        assert np.max(np.abs(s1 - m_)) <= 1e-6 * gmax, (cls.__name__, np.max(np.abs(s1 - m_)))
+
+
+# ---------------------------------------------------------------- invariants
+
+def pin_zero_gradient(orc):
+    """Zero gradient.  wd = 0: p is bitwise unchanged and the states stay +0.
+    wd > 0, skip_zeros off: p follows p <- fl32(p * d) with
+    d = fl32(1 - lr wd) bitwise.  skip_zeros on: p and states are bitwise
+    unchanged for any wd, also for -0 gradients."""
+    n, T = 64, 5
+    p0 = rng(3, 0).uniform(-1, 1, n).astype(np.float32)
+    for dtype in (O.F32, O.F16, O.BF16):
+        ps = p0 if dtype == O.F32 else cast_storage(p0, {O.F16: "fp16", O.BF16: "bf16"}[dtype])
+        zeros = np.zeros(n, np.float32) if dtype == O.F32 else np.zeros(n, np.uint16)
+        negz = (np.full(n, -0.0, np.float32) if dtype == O.F32
+                else np.full(n, 0x8000, np.uint16))
+        for kind in (O.ADAM, O.ADEMAMIX):
+            hp = O.HParams(weight_decay=0.0)
+            p, s1, s2 = _run_f32(orc, kind, dtype, ps, lambda t: zeros, hp, T)
+            assert np.array_equal(p.view(np.uint8), ps.view(np.uint8)), (kind, dtype)
+            assert not np.any(s1.view(np.uint32)) and not np.any(s2.view(np.uint32)), (kind, dtype)
+            for grad in (zeros, negz):
+                hp = O.HParams(weight_decay=0.5, lr=0.01, skip_zeros=True)
+                p, s1, s2 = _run_f32(orc, kind, dtype, ps, lambda t: grad, hp, T)
+                assert np.array_equal(p.view(np.uint8), ps.view(np.uint8)), (kind, dtype, "skip")
+                assert not np.any(s1.view(np.uint32)) and not np.any(s2.view(np.uint32))
+            if dtype == O.F32:
+                hp = O.HParams(weight_decay=0.5, lr=0.01)
+                p, _, _ = _run_f32(orc, kind, dtype, ps, lambda t: zeros, hp, T)
+                d = np.float32(1.0 - 0.01 * float(np.float32(0.5)))
+                ref = p0.copy()
+                lr32 = np.float32(0.01)
+                for _ in range(T):    # m = v = 0: u = 0 / eps = 0, so p' = p d - lr 0
+                    ref = (ref * d) - (lr32 * np.float32(0.0))
+                assert np.array_equal(p.view(np.uint32), ref.view(np.uint32)), kind
+
+
+def pin_ademamix_reduces_to_adam(orc):
+    """AdEMAMix with alpha = 0 adds only alpha * m2 = 0 to the direction, so
+    p, the fast EMA and v equal Adam's bitwise.  With beta3 = beta1 the slow
+    EMA goes through the same operations as the fast one and equals it
+    bitwise."""
+    n, T = 300, 10
+    gen = rng(5, 0)
+    for dtype, name in ((O.F32, "fp32"), (O.F16, "fp16"), (O.BF16, "bf16")):
+        p0 = cast_storage(gen.uniform(-1, 1, n).astype(np.float32), name)
+        gs = [cast_storage(gen.standard_normal(n).astype(np.float32), name) for _ in range(T)]
+        hp = O.HParams(alpha=0.0, weight_decay=0.01)
+        pa, s1a, s2a = _run_f32(orc, O.ADAM, dtype, p0, lambda t: gs[t - 1], hp, T)
+        pm, s1m, s2m = _run_f32(orc, O.ADEMAMIX, dtype, p0, lambda t: gs[t - 1], hp, T)
+        assert np.array_equal(pa.view(np.uint8), pm.view(np.uint8)), name
+        assert np.array_equal(s1a, s1m[:n]) and np.array_equal(s2a, s2m), name
+        hp = O.HParams(beta3=0.9, beta1=0.9, weight_decay=0.01)
+        _, s1m, _ = _run_f32(orc, O.ADEMAMIX, dtype, p0, lambda t: gs[t - 1], hp, T)
+        assert np.array_equal(s1m[:n].view(np.uint32), s1m[n:].view(np.uint32)), name
+
+
+def pin_element_independence(orc):
+    """Each element is updated on its own: element i of an n = 4097 run
+    equals a run of that element alone (n = 1), with its fast EMA at
+    state1[i], its slow EMA at state1[n + i] and v at state2[i]; permuting
+    the inputs permutes the outputs.  The binary32 and 8-thread runs are
+    bitwise equal to the 1-thread run."""
+    n, T = 4097, 3
+    gen = rng(9, 0)
+    for kind in (O.ADAM, O.ADEMAMIX):
+        for dtype, name in ((O.F32, "fp32"), (O.BF16, "bf16")):
+            p0 = cast_storage(gen.uniform(-1, 1, n).astype(np.float32), name)
+            gs = [cast_storage(gen.standard_normal(n).astype(np.float32), name) for _ in range(T)]
+            hp = O.HParams(weight_decay=0.01)
+            p, s1, s2 = _run_f32(orc, kind, dtype, p0, lambda t: gs[t - 1], hp, T)
+            for i in (0, 1, 2048, 4095, 4096):
+                pi, s1i, s2i = _run_f32(orc, kind, dtype, p0[i:i + 1],
+                                        lambda t: gs[t - 1][i:i + 1], hp, T)
+                assert pi.view(np.uint8).tobytes() == p[i:i + 1].view(np.uint8).tobytes(), (kind, name, i)
+                assert s1i[0] == s1[i] and s2i[0] == s2[i], (kind, name, i)
+                if kind == O.ADEMAMIX:
+                    assert s1i[1] == s1[n + i], (name, i)
+            perm = gen.permutation(n)
+            pp, s1p, s2p = _run_f32(orc, kind, dtype, p0[perm], lambda t: gs[t - 1][perm], hp, T)
+            assert np.array_equal(pp.view(np.uint8), p[perm].view(np.uint8)), (kind, name)
+            assert np.array_equal(s2p, s2[perm])
+            if kind == O.ADEMAMIX:
+                assert np.array_equal(s1p[n:], s1[n:][perm])
+            # threads do not change the result
+            p8 = p0.copy()
+            s18 = np.zeros_like(s1)
+            s28 = np.zeros_like(s2)
+            for t in range(1, T + 1):
+                orc.update_f32(kind, dtype, p8, gs[t - 1], s18, s28, hp, t, nthreads=8)
+            assert np.array_equal(p8.view(np.uint8), p.view(np.uint8))
+            assert np.array_equal(s18, s1) and np.array_equal(s28, s2)
+
+
+def pin_grad_unchanged(orc):
+    """The gradient is only read (page section "Correctness oracle")."""
+    n = 1000
+    gen = rng(13, 0)
+    for kind in (O.ADAM, O.ADEMAMIX):
+        for dtype, name in ((O.F32, "fp32"), (O.F16, "fp16"), (O.BF16, "bf16")):
+            p = cast_storage(gen.uniform(-1, 1, n).astype(np.float32), name)
+            g = cast_storage(gen.standard_normal(n).astype(np.float32), name)
+            g0 = g.copy()
+            s1 = np.zeros((2 if kind == O.ADEMAMIX else 1) * n, np.float32)
+            s2 = np.zeros(n, np.float32)
+            for t in (1, 2):
+                orc.update_f32(kind, dtype, p, g, s1, s2, O.HParams(weight_decay=0.01), t)
+            assert g.tobytes() == g0.tobytes(), (kind, name)
+
+
+# --------------------------------------------------------------- conversions
+
+def _f32_of_bits(u32: np.ndarray) -> np.ndarray:
+    return u32.astype(np.uint32).view(np.float32)
+
+
+def check_conversions(orc, bits: np.ndarray) -> None:
+    """binary32 -> fp16 against numpy's IEEE float16 cast and binary32 ->
+    bf16 against torch's bfloat16 cast (both round to nearest even), NaNs
+    excluded (payloads are not part of the contract; NaN must stay NaN);
+    and the exact widening back."""
+    x = _f32_of_bits(bits)
+    nan = np.isnan(x)
+    h = orc.f32_to_storage(x, O.F16)
+    h_ref = x.astype(np.float16).view(np.uint16)
+    assert np.array_equal(h[~nan], h_ref[~nan]), "fp16 rounding"
+    assert np.all((h[nan] & 0x7c00) == 0x7c00) and np.all(h[nan] & 0x3ff), "fp16 NaN"
+    b = orc.f32_to_storage(x, O.BF16)
+    b_ref = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(b[~nan], b_ref[~nan]), "bf16 rounding"
+    assert np.all((b[nan] & 0x7f80) == 0x7f80) and np.all(b[nan] & 0x7f), "bf16 NaN"
+    # widening is exact: fp16 via numpy, bf16 by definition (upper half)
+    wh = orc.storage_to_f32(h[~nan], O.F16)
+    assert np.array_equal(wh, h[~nan].view(np.float16).astype(np.float32)), "fp16 widen"
+    wb = orc.storage_to_f32(b[~nan], O.BF16)
+    assert np.array_equal(wb.view(np.uint32), b[~nan].astype(np.uint32) << 16), "bf16 widen"
+
+
+def pin_conversions_sample(orc):
+    """Storage conversions on every exponent and the rounding boundaries:
+    all 2^16 bf16 patterns and all 2^16 fp16 patterns widened, plus binary32
+    patterns at and around every half-way point, plus 2^20 random patterns."""
+    allh = np.arange(1 << 16, dtype=np.uint32)
+    b32 = allh << 16                                   # every bf16 value exactly
+    mids = [b32 + 0x8000, b32 + 0x7fff, b32 + 0x8001, b32 + 1, b32 + 0xffff]
+    f16v = np.arange(1 << 16, dtype=np.uint16).view(np.float16)
+    f16v = f16v[np.isfinite(f16v)].astype(np.float32).view(np.uint32)
+    f16mids = [f16v + 0x1000, f16v + 0xfff, f16v + 0x1001, f16v + 1, f16v - 1]
+    rnd_bits = rng(17, 0).integers(0, 1 << 32, 1 << 20, dtype=np.uint64).astype(np.uint32)
+    bits = np.concatenate([b32, *mids, f16v, *f16mids, rnd_bits]).astype(np.uint32)
+    check_conversions(orc, bits)
+
+
+# ----------------------------------------------------------- exact emulation
+
+def pin_exact_emulation(orc):
+    """Rounding: on a few elements, every kind, storage, gradient pattern,
+    weight decay and skip_zeros setting, 10 steps of the oracle equal,
+    bitwise, the same operation sequence with each operation rounded exactly
+    once (tests/exact_fp32.py).  Patterns include gradients whose squares
+    fall in the binary32 subnormal range."""
+    n, T = 5, 10
+    gen = rng(19, 0)
+    pats = {
+        "normal": lambda: gen.standard_normal(n),
+        "mixed": lambda: np.where(gen.random(n) < 0.5, -1, 1) * 10.0 ** gen.uniform(-8, 3, n),
+        "zero": lambda: np.array([0.0, -0.0, 0.0, 1.0, -0.0]),
+        "tiny": lambda: np.where(gen.random(n) < 0.5, -1, 1) * 2.0 ** gen.uniform(-75, -60, n),
+    }
+    for kind_name, kind in (("adam", O.ADAM), ("ademamix", O.ADEMAMIX)):
+        for sname, dtype in (("fp32", O.F32), ("fp16", O.F16), ("bf16", O.BF16)):
+            for pat, draw in pats.items():
+                if pat == "tiny" and sname == "fp16":
+                    continue  # all round to zero in fp16: covered by "zero"
+                for wd, skip in ((0.0, False), (0.01, True), (0.01, False)):
+                    hp = O.HParams(weight_decay=wd, skip_zeros=skip)
+                    p = cast_storage(gen.uniform(-1, 1, n).astype(np.float32), sname)
+                    gsteps = [cast_storage(draw().astype(np.float32), sname) for _ in range(T)]
+                    _emulate_and_compare(orc, kind_name, kind, sname, dtype, p, gsteps, hp, T)
+
+
+def _storage_value(a: np.ndarray, sname: str) -> np.ndarray:
+    """Storage array -> float64 values, decoded without the oracle."""
+    if sname == "fp32":
+        return a.astype(np.float64)
+    if sname == "fp16":
+        return a.view(np.float16).astype(np.float64)
+    return (a.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def _emulate_and_compare(orc, kind_name, kind, sname, dtype, p, gsteps, hp, T):
+    n = p.size
+    pv = [X.F.of(float(x)) for x in _storage_value(p, sname)]
+    m = [X.F.of(0.0) for _ in range(n)]
+    v = [X.F.of(0.0) for _ in range(n)]
+    m2 = [X.F.of(0.0) for _ in range(n)]
+    b1, b2, b3 = (X.F.of(float(np.float32(b))) for b in (hp.beta1, hp.beta2, hp.beta3))
+    al, ep, lr = (X.F.of(float(np.float32(x))) for x in (hp.alpha, hp.eps, hp.lr))
+    f32 = lambda x: float(np.float32(x))
+    po = p.copy()
+    s1 = np.zeros((2 if kind == O.ADEMAMIX else 1) * n, np.float32)
+    s2 = np.zeros(n, np.float32)
+    for t in range(1, T + 1):
+        sc = X.step_scalars(f32(hp.beta1), f32(hp.beta2), f32(hp.beta3), f32(hp.lr),
+                            f32(hp.weight_decay), t)
+        gv = _storage_value(gsteps[t - 1], sname)
+        for i in range(n):
+            g = X.F.of(float(gv[i]))
+            pn, m[i], v[i], m2[i], wrote = X.element_step(
+                kind_name, pv[i], g, m[i], v[i], m2[i], sc, b1, b2, b3, al, ep, lr,
+                bool(hp.skip_zeros))
+            if wrote:
+                pv[i] = X.to_storage(pn, sname)
+        orc.update_f32(kind, dtype, po, gsteps[t - 1], s1, s2, hp, t)
+        got_p = _storage_value(po, sname)
+        for i in range(n):
+            ctx = (kind_name, sname, hp, t, i)
+            assert pv[i].bits_equal(float(got_p[i])), ("p", ctx, float(pv[i]), got_p[i])
+            assert m[i].bits_equal(float(s1[i])), ("m", ctx, float(m[i]), s1[i])
+            assert v[i].bits_equal(float(s2[i])), ("v", ctx, float(v[i]), s2[i])
+            if kind == O.ADEMAMIX:
+                assert m2[i].bits_equal(float(s1[n + i])), ("m2", ctx, float(m2[i]), s1[n + i])
+
+
+INDEPENDENT = [pin_closed_form_f64, pin_f32_tracks_f64, pin_first_step_by_hand,
+               pin_torch_adam, pin_zero_gradient, pin_ademamix_reduces_to_adam,
+               pin_element_independence, pin_grad_unchanged, pin_conversions_sample]
+ALL = INDEPENDENT + [pin_exact_emulation]
