@@ -1,0 +1,148 @@
+/*
+ * optimizer_update.h -- C ABI of the MI355X (gfx950) 32-bit two-state
+ * optimizer update: Adam/AdamW with decoupled weight decay, and AdEMAMix
+ * with its extra slow EMA.
+ *
+ * The operation is the one named on the page "Investigate a 256-thread SM103
+ * path for small 32-bit optimizer tensors" (bitsandbytes fork, issue 8):
+ * the per-tensor direct op `optimizer_update_32bit` with a parameter, its
+ * gradient and two fp32 state buffers (sections "Correctness oracle" and
+ * "B300 benchmark and acceptance"), kinds ADAM and ADEMAMIX, parameter and
+ * gradient storage fp32/fp16/bf16, optional skip_zeros.  The page prints no
+ * formula; every entry point computes, per element i (binary32, each
+ * operation correctly rounded, no fused multiply-add):
+ *
+ *   if (skip_zeros && g == 0)  leave p, state1, state2 of i untouched
+ *   m  = beta1*m  + (1-beta1)*g            state1[i]       (Kingma & Ba, Alg. 1)
+ *   v  = beta2*v  + (1-beta2)*(g*g)        state2[i]
+ *   m2 = beta3*m2 + (1-beta3)*g            state1[n+i]     (AdEMAMix only;
+ *                                          Pagliardini et al., Alg. 1)
+ *   u  = (m/bc1 [+ alpha*m2]) / (sqrt(v/bc2) + eps)
+ *   p  = p*d - lr*u                        (decay of the old p; Loshchilov &
+ *                                           Hutter, Alg. 2)
+ *   param[i] = p rounded to the storage type (nearest, ties to even)
+ *
+ * with the per-step scalars bc1 = fl32(1 - fl64(beta1^step)),
+ * bc2 = fl32(1 - fl64(beta2^step)), d = fl32(1 - fl64(lr*weight_decay)),
+ * 1-beta formed in binary32.  step is 1-based (the update being applied).
+ * The slow EMA is not bias-corrected; alpha and beta3 are constants.
+ *
+ * Layout:  param, grad: n elements of the storage dtype.  state1: n floats
+ * (ADAM) or 2n floats (ADEMAMIX: fast EMA at [0,n), slow EMA at [n,2n)).
+ * state2: n floats.  All pointers are device pointers on the current HIP
+ * device and must be aligned to their element size.  16-byte alignment of
+ * all streams selects the dwordx4 path; any other alignment runs the same
+ * arithmetic one element per lane (results are bitwise identical).
+ *
+ * Ownership: the caller owns every buffer.  The library allocates only plan
+ * memory (segment table, work list, graph) and frees it in ou_plan_destroy.
+ * grad is never written.
+ *
+ * Errors: every function returns a status.  Arguments are validated before
+ * anything is launched; on error nothing is launched and nothing is written
+ * (all or nothing across the segments of a multi-tensor call).
+ * ou_last_error() gives a thread-local message for the last failure.
+ * Device faults surface, as usual in HIP, at the caller's next
+ * synchronisation.
+ *
+ * Streams are hipStream_t passed as void* (NULL = the default stream).
+ * Calls enqueue work and return without synchronising, except
+ * optimizer_update_32bit_multi (see there).
+ */
+#ifndef OPTIMIZER_UPDATE_H
+#define OPTIMIZER_UPDATE_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { OU_F32 = 0, OU_F16 = 1, OU_BF16 = 2 } ou_dtype;
+typedef enum { OU_ADAM = 0, OU_ADEMAMIX = 1 } ou_kind;
+
+enum {
+    OU_OK = 0,
+    OU_EINVAL = -1,       /* bad pointer, size, kind, dtype, step or hyperparameter */
+    OU_EUNSUPPORTED = -2, /* device is not gfx950, or no HIP device */
+    OU_EALIGN = -3,       /* a pointer is not aligned to its element size */
+    OU_EOVERLAP = -4,     /* two buffers overlap (a written buffer with anything) */
+    OU_ENOMEM = -5,       /* plan allocation failed */
+    OU_EHIP = -6,         /* a HIP runtime call failed */
+    OU_ECAPTURE = -7      /* call not allowed while the stream is being captured */
+};
+
+/* Hyperparameters of one step (the arguments of optimizer_update_32bit).
+ * beta1, beta2 in [0, 1); beta3 in [0, 1) and alpha finite (AdEMAMix only,
+ * ignored for ADAM); eps >= 0; lr, weight_decay finite; step >= 1;
+ * skip_zeros != 0 enables skipping of zero-gradient elements. */
+typedef struct {
+    float beta1, beta2, beta3, alpha, eps, weight_decay, lr;
+    int32_t skip_zeros;
+    int64_t step;
+} ou_hparams;
+
+/* One tensor of a collection.  dtype is an ou_dtype; layout as above. */
+typedef struct {
+    void* param;
+    const void* grad;
+    float* state1;
+    float* state2;
+    int64_t n;
+    int32_t dtype;
+    int32_t reserved; /* must be 0 */
+} ou_segment;
+
+/* One optimizer step over one tensor of n elements (n = 0: no-op).
+ * The per-tensor direct op of section "B300 benchmark and acceptance" of
+ * the page.  Asynchronous on `stream`; capture-safe (no allocation, no
+ * synchronisation, device properties cached per device). */
+int optimizer_update_32bit(int kind, int dtype, void* param, const void* grad,
+                           float* state1, float* state2, int64_t n,
+                           float beta1, float beta2, float beta3, float alpha,
+                           float eps, float weight_decay, int64_t step, float lr,
+                           int skip_zeros, void* stream);
+
+/* One optimizer step over a collection of nseg tensors (any mix of
+ * dtypes), one launch per dtype group (the eager optimizer.step() of
+ * section "B300 benchmark and acceptance").  Convenience form: builds and
+ * uploads the segment table on every call and synchronises `stream` before
+ * returning; not allowed during stream capture.  For repeated steps use a
+ * plan. */
+int optimizer_update_32bit_multi(int kind, const ou_segment* segs, int32_t nseg,
+                                 const ou_hparams* hp, void* stream);
+
+/* A plan: the device-resident segment table and work list of a fixed
+ * collection.  Pointers and sizes are captured at creation and must stay
+ * valid and unchanged until ou_plan_destroy.  Segments with n = 0 are
+ * dropped.  A plan is not thread-safe. */
+typedef struct ou_plan_s* ou_plan;
+
+int ou_plan_create(int kind, const ou_segment* segs, int32_t nseg, ou_plan* out);
+
+/* One step of the plan's collection: one launch per dtype group, on
+ * `stream`.  Capture-safe. */
+int ou_plan_step(ou_plan plan, const ou_hparams* hp, void* stream);
+
+/* The same step through a HIP graph: built and instantiated on the first
+ * call, then replayed with this step's scalars written into its kernel
+ * nodes.  Bitwise identical to ou_plan_step.  Not allowed while `stream` is
+ * being captured. */
+int ou_plan_graph_step(ou_plan plan, const ou_hparams* hp, void* stream);
+
+/* Shape of a plan: dtype groups (= launches per step), work items, elements. */
+int ou_plan_describe(ou_plan plan, int32_t* n_groups, int64_t* n_work_items,
+                     int64_t* n_elements);
+
+/* Frees the plan (waits for nothing: the caller makes sure no step of it is
+ * still running).  NULL is a no-op. */
+void ou_plan_destroy(ou_plan plan);
+
+const char* ou_status_string(int status);
+const char* ou_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* OPTIMIZER_UPDATE_H */

@@ -1,0 +1,186 @@
+"""MI355X (gfx950) 32-bit two-state optimizer update: Adam/AdamW and AdEMAMix.
+
+Thin torch-facing binding of ``liboptimizer_update.so`` (``include/optimizer_update.h``).
+Functions carry the names of the C entry points and only marshal arguments
+(device pointers, dtype codes, the current stream); every step of the update
+runs in the HIP kernels.  There is no CPU fallback: without the built
+library, or without a GPU, calls raise.
+
+    optimizer_update_32bit(kind, param, grad, state1, state2, step=..., lr=..., ...)
+    optimizer_update_32bit_multi(kind, segments, hp, step)
+    Plan(kind, segments)  -> .step(hp, step) / .graph_step(hp, step) / .close()
+    AdamW32, AdEMAMix32    collection optimizers over a fixed parameter list
+
+Layout: param and grad are contiguous tensors of one storage dtype
+(float32, float16 or bfloat16); state1 holds n floats (Adam) or 2n floats
+(AdEMAMix: fast EMA, then slow EMA); state2 holds n floats.
+"""
+from __future__ import annotations
+
+import ctypes
+from dataclasses import dataclass
+
+import torch
+
+from . import _lib
+from ._lib import OptimizerUpdateError, check, load
+
+__all__ = ["HParams", "optimizer_update_32bit", "optimizer_update_32bit_multi", "Plan",
+           "OptimizerUpdateError", "KINDS", "DTYPES", "load", "state_sizes"]
+
+KINDS = {"adam": _lib.OU_ADAM, "ademamix": _lib.OU_ADEMAMIX}
+DTYPES = {torch.float32: _lib.OU_F32, torch.float16: _lib.OU_F16, torch.bfloat16: _lib.OU_BF16}
+
+
+@dataclass(frozen=True)
+class HParams:
+    """Step hyperparameters; beta3 and alpha are used by AdEMAMix only."""
+    lr: float = 1e-3
+    beta1: float = 0.9
+    beta2: float = 0.999
+    beta3: float = 0.9999
+    alpha: float = 5.0
+    eps: float = 1e-8
+    weight_decay: float = 0.0
+    skip_zeros: bool = False
+
+    def c(self, step: int) -> _lib.ou_hparams:
+        return _lib.ou_hparams(self.beta1, self.beta2, self.beta3, self.alpha, self.eps,
+                               self.weight_decay, self.lr, int(bool(self.skip_zeros)), int(step))
+
+
+def _kind(kind) -> int:
+    return KINDS[kind] if isinstance(kind, str) else int(kind)
+
+
+def state_sizes(kind, n: int) -> tuple[int, int]:
+    """Elements of state1 and state2 for a tensor of n elements."""
+    return (2 * n if _kind(kind) == _lib.OU_ADEMAMIX else n), n
+
+
+def _stream(t: torch.Tensor, stream) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream(t.device)
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _tensor_args(kind: int, param, grad, state1, state2) -> tuple[int, int]:
+    for name, t in (("param", param), ("grad", grad), ("state1", state1), ("state2", state2)):
+        if not isinstance(t, torch.Tensor) or not t.is_cuda:
+            raise ValueError(f"{name} must be a tensor on a HIP device")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    if param.dtype not in DTYPES or grad.dtype != param.dtype:
+        raise ValueError("param and grad must share one of float32/float16/bfloat16")
+    if state1.dtype != torch.float32 or state2.dtype != torch.float32:
+        raise ValueError("states must be float32")
+    n = param.numel()
+    s1, s2 = state_sizes(kind, n)
+    if grad.numel() != n or state1.numel() != s1 or state2.numel() != s2:
+        raise ValueError(f"sizes: param {n}, grad {grad.numel()}, state1 {state1.numel()} "
+                         f"(want {s1}), state2 {state2.numel()} (want {s2})")
+    if len({t.device for t in (param, grad, state1, state2)}) != 1:
+        raise ValueError("all tensors must be on one device")
+    return n, DTYPES[param.dtype]
+
+
+def optimizer_update_32bit(kind, param: torch.Tensor, grad: torch.Tensor, state1: torch.Tensor,
+                           state2: torch.Tensor, *, step: int, lr: float, beta1: float = 0.9,
+                           beta2: float = 0.999, beta3: float = 0.9999, alpha: float = 5.0,
+                           eps: float = 1e-8, weight_decay: float = 0.0, skip_zeros: bool = False,
+                           stream=None) -> None:
+    """One update of one tensor, in place, on ``stream`` (default: current)."""
+    k = _kind(kind)
+    n, dt = _tensor_args(k, param, grad, state1, state2)
+    lib = load()
+    with torch.cuda.device(param.device):
+        st = lib.optimizer_update_32bit(k, dt, param.data_ptr(), grad.data_ptr(),
+                                        state1.data_ptr(), state2.data_ptr(), n, beta1, beta2,
+                                        beta3, alpha, eps, weight_decay, int(step), lr,
+                                        int(bool(skip_zeros)), _stream(param, stream))
+    check(st, lib)
+
+
+def _segments(kind: int, segments) -> ctypes.Array:
+    arr = (_lib.ou_segment * len(segments))()
+    for i, (p, g, s1, s2) in enumerate(segments):
+        n, dt = _tensor_args(kind, p, g, s1, s2)
+        arr[i] = _lib.ou_segment(p.data_ptr(), g.data_ptr(), s1.data_ptr(), s2.data_ptr(), n, dt, 0)
+    return arr
+
+
+def optimizer_update_32bit_multi(kind, segments, hp: HParams, step: int, stream=None) -> None:
+    """One update of a collection [(param, grad, state1, state2), ...]: one
+    launch per dtype group.  Builds the table on every call and waits for
+    the stream; use ``Plan`` for repeated steps."""
+    k = _kind(kind)
+    if not segments:
+        return
+    arr = _segments(k, segments)
+    lib = load()
+    c = hp.c(step)
+    dev = segments[0][0].device
+    with torch.cuda.device(dev):
+        st = lib.optimizer_update_32bit_multi(k, arr, len(segments), ctypes.byref(c),
+                                              _stream(segments[0][0], stream))
+    check(st, lib)
+
+
+class Plan:
+    """Device-resident segment table of a fixed collection (``ou_plan``).
+
+    The tensors' storage must stay allocated and in place until ``close``;
+    the plan keeps references to them."""
+
+    def __init__(self, kind, segments):
+        self.kind = _kind(kind)
+        self._tensors = [tuple(s) for s in segments]
+        self.device = self._tensors[0][0].device if self._tensors else torch.device("cuda")
+        arr = _segments(self.kind, self._tensors)
+        self._lib = load()
+        h = ctypes.c_void_p()
+        with torch.cuda.device(self.device):
+            check(self._lib.ou_plan_create(self.kind, arr, len(self._tensors), ctypes.byref(h)),
+                  self._lib)
+        self._h = h
+
+    def step(self, hp: HParams, step: int, stream=None) -> None:
+        c = hp.c(step)
+        with torch.cuda.device(self.device):
+            check(self._lib.ou_plan_step(self._h, ctypes.byref(c), self._stream(stream)), self._lib)
+
+    def graph_step(self, hp: HParams, step: int, stream=None) -> None:
+        c = hp.c(step)
+        with torch.cuda.device(self.device):
+            check(self._lib.ou_plan_graph_step(self._h, ctypes.byref(c), self._stream(stream)),
+                  self._lib)
+
+    def describe(self) -> dict:
+        g = ctypes.c_int32()
+        w = ctypes.c_int64()
+        e = ctypes.c_int64()
+        check(self._lib.ou_plan_describe(self._h, ctypes.byref(g), ctypes.byref(w), ctypes.byref(e)),
+              self._lib)
+        return {"groups": g.value, "work_items": w.value, "elements": e.value}
+
+    def _stream(self, stream) -> int:
+        if stream is None:
+            return torch.cuda.current_stream(self.device).cuda_stream
+        return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+    def close(self) -> None:
+        if getattr(self, "_h", None) is not None and self._h.value:
+            torch.cuda.synchronize(self.device)
+            self._lib.ou_plan_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+from .optim import AdamW32, AdEMAMix32  # noqa: E402
+
+__all__ += ["AdamW32", "AdEMAMix32"]

@@ -1,0 +1,102 @@
+"""ctypes binding of liboptimizer_update.so (argument marshalling only).
+
+Every function here has the name of the C entry point it calls and does
+nothing but check and convert arguments: all arithmetic runs in the HIP
+kernels.  If the library has not been built, loading it raises; there is no
+fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIBRARY = os.path.join(HERE, "liboptimizer_update.so")
+HEADER = os.path.join(os.path.dirname(HERE), "include", "optimizer_update.h")
+
+OU_F32, OU_F16, OU_BF16 = 0, 1, 2
+OU_ADAM, OU_ADEMAMIX = 0, 1
+STATUS = {0: "OU_OK", -1: "OU_EINVAL", -2: "OU_EUNSUPPORTED", -3: "OU_EALIGN",
+          -4: "OU_EOVERLAP", -5: "OU_ENOMEM", -6: "OU_EHIP", -7: "OU_ECAPTURE"}
+
+
+class OptimizerUpdateError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{STATUS.get(status, status)}: {message}")
+        self.status = status
+
+
+class ou_hparams(ctypes.Structure):
+    _fields_ = [("beta1", ctypes.c_float), ("beta2", ctypes.c_float), ("beta3", ctypes.c_float),
+                ("alpha", ctypes.c_float), ("eps", ctypes.c_float),
+                ("weight_decay", ctypes.c_float), ("lr", ctypes.c_float),
+                ("skip_zeros", ctypes.c_int32), ("step", ctypes.c_int64)]
+
+
+class ou_segment(ctypes.Structure):
+    _fields_ = [("param", ctypes.c_void_p), ("grad", ctypes.c_void_p),
+                ("state1", ctypes.c_void_p), ("state2", ctypes.c_void_p),
+                ("n", ctypes.c_int64), ("dtype", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+
+
+def header_functions(path: str = HEADER) -> list[str]:
+    """Names of the functions the public header declares."""
+    with open(path) as f:
+        text = re.sub(r"/\*.*?\*/", "", f.read(), flags=re.S)
+    return re.findall(r"^\s*(?:const\s+)?\w+\**\s+\**(\w+)\s*\(", text, flags=re.M)
+
+
+_lib = None
+
+
+def load(path: str = LIBRARY) -> ctypes.CDLL:
+    """Load the HIP library (raises if it is missing: no fallback exists)."""
+    global _lib
+    if _lib is not None and path == LIBRARY:
+        return _lib
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is not built; run __graft_entry__.build() "
+                          "(python -c 'import __graft_entry__ as g; g.build()')")
+    lib = ctypes.CDLL(path)
+    i32, i64, f32, vp = ctypes.c_int, ctypes.c_int64, ctypes.c_float, ctypes.c_void_p
+    lib.optimizer_update_32bit.argtypes = [i32, i32, vp, vp, vp, vp, i64, f32, f32, f32, f32,
+                                           f32, f32, i64, f32, i32, vp]
+    lib.optimizer_update_32bit.restype = i32
+    lib.optimizer_update_32bit_multi.argtypes = [i32, ctypes.POINTER(ou_segment), ctypes.c_int32,
+                                                 ctypes.POINTER(ou_hparams), vp]
+    lib.optimizer_update_32bit_multi.restype = i32
+    lib.ou_plan_create.argtypes = [i32, ctypes.POINTER(ou_segment), ctypes.c_int32,
+                                   ctypes.POINTER(vp)]
+    lib.ou_plan_create.restype = i32
+    lib.ou_plan_step.argtypes = [vp, ctypes.POINTER(ou_hparams), vp]
+    lib.ou_plan_step.restype = i32
+    lib.ou_plan_graph_step.argtypes = [vp, ctypes.POINTER(ou_hparams), vp]
+    lib.ou_plan_graph_step.restype = i32
+    lib.ou_plan_describe.argtypes = [vp, ctypes.POINTER(ctypes.c_int32),
+                                     ctypes.POINTER(i64), ctypes.POINTER(i64)]
+    lib.ou_plan_describe.restype = i32
+    lib.ou_plan_destroy.argtypes = [vp]
+    lib.ou_plan_destroy.restype = None
+    lib.ou_status_string.argtypes = [i32]
+    lib.ou_status_string.restype = ctypes.c_char_p
+    lib.ou_last_error.argtypes = []
+    lib.ou_last_error.restype = ctypes.c_char_p
+    # test hooks (not in the public header)
+    lib.ou__select_single.argtypes = [i32, i32, i32, i64, i32, ctypes.POINTER(i64)]
+    lib.ou__select_single.restype = i32
+    lib.ou__force_single.argtypes = [i32, i32, i32, i64, i32]
+    lib.ou__force_single.restype = None
+    lib.ou__force_multi.argtypes = [i32, i32, i32, i32]
+    lib.ou__force_multi.restype = None
+    lib.ou__step_scalars.argtypes = [ctypes.POINTER(ou_hparams), ctypes.POINTER(f32)]
+    lib.ou__step_scalars.restype = i32
+    if path == LIBRARY:
+        _lib = lib
+    return lib
+
+
+def check(status: int, lib: ctypes.CDLL | None = None) -> None:
+    if status != 0:
+        lib = lib or load()
+        raise OptimizerUpdateError(status, lib.ou_last_error().decode(errors="replace"))

@@ -1,0 +1,117 @@
+// elem.hpp -- per-element arithmetic of the 32-bit two-state update (device).
+//
+// Every launch variant (single-tensor dwordx4 and per-lane paths, every
+// block width and unroll, the multi-tensor walk, graph replay) calls the
+// functions in this file, so the arithmetic cannot depend on how the work is
+// mapped to lanes -- the rule of the page "Investigate a 256-thread SM103
+// path for small 32-bit optimizer tensors" (section "Correctness oracle"):
+// changing the launch width must not change the optimizer arithmetic.
+//
+// Operations are plain binary32 with contraction off (the file pragma below
+// and -ffp-contract=off), correctly rounded division and square root (HIP's
+// default lowering for gfx950) and denormals preserved, so each line is one
+// IEEE operation rounded to nearest even.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#pragma clang fp contract(off)
+
+namespace ou {
+
+enum Kind : int { kAdam = 0, kAdemamix = 1 };
+
+// Per-step scalars, formed on the host once per step (see host.hip).
+struct StepScalars {
+    float beta1, beta2, beta3;
+    float omb1, omb2, omb3;   // 1 - beta, binary32
+    float alpha, eps, lr;
+    float bc1, bc2;           // bias corrections fl32(1 - fl64(beta^step))
+    float decay;              // fl32(1 - fl64(lr * weight_decay))
+    int32_t skip_zeros;
+};
+
+// One element.  m: fast first moment, v: second moment, m2: slow EMA
+// (AdEMAMix only).  p is the widened parameter; returns the new parameter
+// before rounding to storage.  Moments and bias correction follow Kingma &
+// Ba (Algorithm 1), the decay of the old parameter Loshchilov & Hutter
+// (Algorithm 2), the slow EMA mixed in with alpha Pagliardini et al.
+// (Algorithm 1).
+template <int KIND>
+__device__ __forceinline__ float update_element(float p, float g, float& m, float& v,
+                                                float& m2, const StepScalars& s)
+{
+    const float mn = s.beta1 * m + s.omb1 * g;
+    const float vn = s.beta2 * v + s.omb2 * (g * g);
+    float m2n = 0.0f;
+    if constexpr (KIND == kAdemamix) m2n = s.beta3 * m2 + s.omb3 * g;
+    const float mh = mn / s.bc1;
+    const float vh = vn / s.bc2;
+    const float den = __builtin_sqrtf(vh) + s.eps;
+    float num = mh;
+    if constexpr (KIND == kAdemamix) num = mh + s.alpha * m2n;
+    const float u = num / den;
+    m = mn;
+    v = vn;
+    if constexpr (KIND == kAdemamix) m2 = m2n;
+    return p * s.decay - s.lr * u;
+}
+
+// ---- storage types ---------------------------------------------------------
+// Storage<T> widens to binary32 exactly and narrows with round to nearest,
+// ties to even (gfx950 conversion instructions: v_cvt_f16_f32 under the
+// default round-to-nearest mode, v_cvt_pk_bf16_f32 for bfloat16).
+struct F32 {
+    using raw = float;
+    static constexpr int bytes = 4;
+    __device__ __forceinline__ static float widen(raw x) { return x; }
+    __device__ __forceinline__ static raw narrow(float x) { return x; }
+};
+
+struct F16 {
+    using raw = uint16_t;
+    static constexpr int bytes = 2;
+    __device__ __forceinline__ static float widen(raw x)
+    {
+        return static_cast<float>(__builtin_bit_cast(_Float16, x));
+    }
+    __device__ __forceinline__ static raw narrow(float x)
+    {
+        return __builtin_bit_cast(uint16_t, static_cast<_Float16>(x));
+    }
+};
+
+struct BF16 {
+    using raw = uint16_t;
+    static constexpr int bytes = 2;
+    __device__ __forceinline__ static float widen(raw x)
+    {
+        return __builtin_bit_cast(float, static_cast<uint32_t>(x) << 16);
+    }
+    __device__ __forceinline__ static raw narrow(float x)
+    {
+        return __builtin_bit_cast(uint16_t, static_cast<__bf16>(x));
+    }
+};
+
+// One element through widen -> update -> narrow.  With skip_zeros and a
+// zero gradient (+0 or -0) nothing of the element is written.
+template <int KIND, typename S>
+__device__ __forceinline__ void update_scalar(typename S::raw* __restrict__ p,
+                                              const typename S::raw* __restrict__ g,
+                                              float* __restrict__ s1, float* __restrict__ s2,
+                                              int64_t n, int64_t i, const StepScalars& s)
+{
+    const float gi = S::widen(g[i]);
+    if (s.skip_zeros && gi == 0.0f) return;
+    float m = s1[i], v = s2[i], m2 = 0.0f;
+    if constexpr (KIND == kAdemamix) m2 = s1[n + i];
+    const float pn = update_element<KIND>(S::widen(p[i]), gi, m, v, m2, s);
+    p[i] = S::narrow(pn);
+    s1[i] = m;
+    s2[i] = v;
+    if constexpr (KIND == kAdemamix) s1[n + i] = m2;
+}
+
+}  // namespace ou

@@ -1,0 +1,664 @@
+// host.hip -- C ABI of the 32-bit two-state optimizer update (host side).
+//
+// Validation, the per-step scalars, launch selection, the per-device
+// property cache, plans (device-resident segment table + work list) and
+// graph replay.  The arithmetic itself lives in elem.hpp and runs only on the
+// GPU.
+//
+// The operation is the per-tensor direct op of the page "Investigate a
+// 256-thread SM103 path for small 32-bit optimizer tensors" (bitsandbytes
+// fork, issue 8), sections "Correctness oracle" and "B300 benchmark and
+// acceptance"; the page's own notes on launch selection (section "Scope")
+// ask for device detection cached per current device and safe under graph
+// capture, which is what DeviceCache does.
+#include <algorithm>
+#include <atomic>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "../../include/optimizer_update.h"
+#include "internal.h"
+#include "ou_testing.h"
+
+namespace ou {
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int status, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+int fail(int status, const char* fmt, ...)
+{
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return status;
+}
+
+int hip_fail(hipError_t e, const char* what)
+{
+    return fail(OU_EHIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+// ---- per-device properties, cached per device id (never per process) --------
+
+struct DeviceProps {
+    int cu_count = 0;
+    bool gfx950 = false;
+    char arch[64] = {0};
+};
+
+constexpr int kMaxDevices = 64;
+
+class DeviceCache {
+public:
+    // Properties of the current device; queried once per device id.
+    int current(const DeviceProps** out)
+    {
+        int dev = 0;
+        hipError_t e = hipGetDevice(&dev);
+        if (e == hipErrorNoDevice) return fail(OU_EUNSUPPORTED, "no HIP device");
+        if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+        if (dev < 0 || dev >= kMaxDevices) return fail(OU_EUNSUPPORTED, "device id %d", dev);
+        if (!ready_[dev].load(std::memory_order_acquire)) {
+            std::lock_guard<std::mutex> lk(mu_);
+            if (!ready_[dev].load(std::memory_order_relaxed)) {
+                DeviceProps p;
+                e = hipDeviceGetAttribute(&p.cu_count, hipDeviceAttributeMultiprocessorCount, dev);
+                if (e != hipSuccess) return hip_fail(e, "hipDeviceGetAttribute");
+                hipDeviceProp_t prop;
+                e = hipGetDeviceProperties(&prop, dev);
+                if (e != hipSuccess) return hip_fail(e, "hipGetDeviceProperties");
+                std::snprintf(p.arch, sizeof p.arch, "%s", prop.gcnArchName);
+                p.gfx950 = std::strncmp(p.arch, "gfx950", 6) == 0;
+                props_[dev] = p;
+                ready_[dev].store(true, std::memory_order_release);
+            }
+        }
+        if (!props_[dev].gfx950)
+            return fail(OU_EUNSUPPORTED, "device %d is %s; this library is built for gfx950", dev,
+                        props_[dev].arch);
+        *out = &props_[dev];
+        return OU_OK;
+    }
+
+private:
+    std::mutex mu_;
+    std::atomic<bool> ready_[kMaxDevices] = {};
+    DeviceProps props_[kMaxDevices];
+};
+
+DeviceCache g_devices;
+
+// ---- test-only forcing of launch shapes (not part of the public ABI) ---------
+
+std::atomic<int> g_force_block{0}, g_force_epl{0}, g_force_unroll{0}, g_force_scalar{0};
+std::atomic<int64_t> g_force_grid{0};
+std::atomic<int> g_force_waves{0}, g_force_mepl{0}, g_force_munroll{0}, g_force_chunk{0};
+
+// ---- validation -------------------------------------------------------------
+
+int storage_bytes(int dtype) { return dtype == OU_F32 ? 4 : 2; }
+
+bool valid_beta(float b) { return std::isfinite(b) && b >= 0.0f && b < 1.0f; }
+
+int check_hparams(int kind, const ou_hparams& h)
+{
+    if (kind != OU_ADAM && kind != OU_ADEMAMIX) return fail(OU_EINVAL, "unknown kind %d", kind);
+    if (!valid_beta(h.beta1) || !valid_beta(h.beta2))
+        return fail(OU_EINVAL, "beta1/beta2 must lie in [0, 1) (got %g, %g)", h.beta1, h.beta2);
+    if (kind == OU_ADEMAMIX && (!valid_beta(h.beta3) || !std::isfinite(h.alpha)))
+        return fail(OU_EINVAL, "beta3 must lie in [0, 1) and alpha be finite (got %g, %g)",
+                    h.beta3, h.alpha);
+    if (!std::isfinite(h.eps) || h.eps < 0.0f) return fail(OU_EINVAL, "eps must be finite and >= 0");
+    if (!std::isfinite(h.lr)) return fail(OU_EINVAL, "lr must be finite");
+    if (!std::isfinite(h.weight_decay)) return fail(OU_EINVAL, "weight_decay must be finite");
+    if (h.step < 1) return fail(OU_EINVAL, "step must be >= 1 (got %lld)", (long long)h.step);
+    return OU_OK;
+}
+
+struct Range {
+    uintptr_t lo, hi;   // [lo, hi)
+    bool written;
+    int seg;
+};
+
+// Pointers, sizes and alignment of one segment; appends its byte ranges.
+int check_segment(int kind, const ou_segment& s, int idx, std::vector<Range>* ranges)
+{
+    if (s.dtype != OU_F32 && s.dtype != OU_F16 && s.dtype != OU_BF16)
+        return fail(OU_EINVAL, "segment %d: unknown dtype %d", idx, s.dtype);
+    if (s.n < 0) return fail(OU_EINVAL, "segment %d: n < 0", idx);
+    if (s.reserved != 0) return fail(OU_EINVAL, "segment %d: reserved field must be 0", idx);
+    if (s.n == 0) return OU_OK;
+    if (!s.param || !s.grad || !s.state1 || !s.state2)
+        return fail(OU_EINVAL, "segment %d: null pointer with n > 0", idx);
+    const uintptr_t sb = static_cast<uintptr_t>(storage_bytes(s.dtype));
+    const uintptr_t P = reinterpret_cast<uintptr_t>(s.param);
+    const uintptr_t G = reinterpret_cast<uintptr_t>(s.grad);
+    const uintptr_t S1 = reinterpret_cast<uintptr_t>(s.state1);
+    const uintptr_t S2 = reinterpret_cast<uintptr_t>(s.state2);
+    if (P % sb || G % sb) return fail(OU_EALIGN, "segment %d: param/grad not %u-byte aligned", idx, (unsigned)sb);
+    if (S1 % 4 || S2 % 4) return fail(OU_EALIGN, "segment %d: states not 4-byte aligned", idx);
+    const uintptr_t n = static_cast<uintptr_t>(s.n);
+    if (n > (uintptr_t(1) << 40)) return fail(OU_EINVAL, "segment %d: n too large", idx);
+    const uintptr_t k = (kind == OU_ADEMAMIX) ? 2 : 1;
+    ranges->push_back({P, P + n * sb, true, idx});
+    ranges->push_back({G, G + n * sb, false, idx});
+    ranges->push_back({S1, S1 + k * n * 4, true, idx});
+    ranges->push_back({S2, S2 + n * 4, true, idx});
+    return OU_OK;
+}
+
+// No written range may overlap any other range (read-only ranges may share).
+int check_overlap(std::vector<Range>& r)
+{
+    std::sort(r.begin(), r.end(), [](const Range& a, const Range& b) { return a.lo < b.lo; });
+    // Sweep: track the written range reaching furthest and any range reaching furthest.
+    uintptr_t any_hi = 0, w_hi = 0;
+    int any_seg = -1, w_seg = -1;
+    for (const Range& x : r) {
+        if (x.lo < w_hi)
+            return fail(OU_EOVERLAP, "segment %d overlaps a written buffer of segment %d", x.seg, w_seg);
+        if (x.written && x.lo < any_hi)
+            return fail(OU_EOVERLAP, "a written buffer of segment %d overlaps segment %d", x.seg, any_seg);
+        if (x.hi > any_hi) { any_hi = x.hi; any_seg = x.seg; }
+        if (x.written && x.hi > w_hi) { w_hi = x.hi; w_seg = x.seg; }
+    }
+    return OU_OK;
+}
+
+bool streams_16b_aligned(int kind, const ou_segment& s)
+{
+    const uintptr_t a = reinterpret_cast<uintptr_t>(s.param) | reinterpret_cast<uintptr_t>(s.grad) |
+                        reinterpret_cast<uintptr_t>(s.state1) | reinterpret_cast<uintptr_t>(s.state2);
+    uintptr_t slow = 0;
+    if (kind == OU_ADEMAMIX) slow = reinterpret_cast<uintptr_t>(s.state1 + s.n);
+    return ((a | slow) & 15u) == 0;
+}
+
+// ---- per-step scalars ---------------------------------------------------------
+
+// bc = fl32(1 - fl64(beta^step)) and d = fl32(1 - fl64(lr * wd)) in binary64
+// from the binary32 arguments; 1 - beta in binary32.
+StepScalars make_scalars(const ou_hparams& h)
+{
+    StepScalars s;
+    const double t = static_cast<double>(h.step);
+    s.beta1 = h.beta1;
+    s.beta2 = h.beta2;
+    s.beta3 = h.beta3;
+    s.omb1 = 1.0f - h.beta1;
+    s.omb2 = 1.0f - h.beta2;
+    s.omb3 = 1.0f - h.beta3;
+    s.alpha = h.alpha;
+    s.eps = h.eps;
+    s.lr = h.lr;
+    s.bc1 = static_cast<float>(1.0 - std::pow(static_cast<double>(h.beta1), t));
+    s.bc2 = static_cast<float>(1.0 - std::pow(static_cast<double>(h.beta2), t));
+    s.decay = static_cast<float>(1.0 - static_cast<double>(h.lr) * static_cast<double>(h.weight_decay));
+    s.skip_zeros = h.skip_zeros ? 1 : 0;
+    return s;
+}
+
+// ---- launch selection ---------------------------------------------------------
+
+// Single tensor.  Small tensors (the launch-latency regime) get one block
+// sized to the tensor; large ones a grid of 256-thread blocks, each lane
+// holding UNROLL groups of 16-byte loads in flight, capped at a few blocks
+// per CU (grid-stride beyond that).
+SingleLaunch select_single(int cu_count, int kind, int dtype, int64_t n, bool vec)
+{
+    (void)kind;
+    SingleLaunch L;
+    L.epl = (dtype == OU_F32) ? 4 : 8;
+    const int64_t units = vec ? (n + L.epl - 1) / L.epl : n;   // lanes' work units
+    if (units <= 1024) {
+        L.unroll = 1;
+        int64_t b = ((units + kWave - 1) / kWave) * kWave;
+        L.block = static_cast<int>(std::max<int64_t>(kWave, std::min<int64_t>(b, 256)));
+        L.grid = (units + L.block - 1) / L.block;
+        if (L.grid < 1) L.grid = 1;
+        return L;
+    }
+    L.block = 256;
+    L.unroll = 2;
+    const int64_t per_block = static_cast<int64_t>(L.block) * L.unroll;
+    const int64_t want = (units + per_block - 1) / per_block;
+    const int64_t cap = static_cast<int64_t>(cu_count > 0 ? cu_count : 256) * 16;
+    L.grid = std::max<int64_t>(1, std::min(want, cap));
+    return L;
+}
+
+// Multi tensor: waves per block, EPL, unroll and the chunk (elements per
+// work item; a multiple of 64 * EPL so chunk starts keep 16-byte alignment).
+MultiLaunch select_multi(int dtype)
+{
+    MultiLaunch L;
+    L.waves = 4;
+    L.epl = (dtype == OU_F32) ? 4 : 8;
+    L.unroll = 2;
+    return L;
+}
+
+int64_t select_chunk(int dtype)
+{
+    return (dtype == OU_F32) ? 4096 : 8192;
+}
+
+void apply_single_forcing(SingleLaunch* L, bool* vec)
+{
+    if (g_force_scalar.load()) *vec = false;
+    if (int b = g_force_block.load()) L->block = b;
+    if (int e = g_force_epl.load()) L->epl = e;
+    if (int u = g_force_unroll.load()) L->unroll = u;
+    if (int64_t gsz = g_force_grid.load()) L->grid = gsz;
+}
+
+hipError_t launch(const void* fn, int64_t grid, int block, void** args, hipStream_t stream)
+{
+    return hipLaunchKernel(fn, dim3(static_cast<unsigned>(grid)), dim3(static_cast<unsigned>(block)),
+                           args, 0, stream);
+}
+
+bool capturing(hipStream_t stream)
+{
+    hipStreamCaptureStatus st = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(stream, &st) != hipSuccess) return false;
+    return st != hipStreamCaptureStatusNone;
+}
+
+}  // namespace
+
+// ---- plans --------------------------------------------------------------------
+
+// One dtype group of a plan: its tables, launch shape and argument storage.
+struct Group {
+    int dtype;
+    MultiLaunch L;
+    int64_t chunk;
+    int64_t n_items;
+    const SegDesc* d_segs;
+    const WorkItem* d_items;
+    const void* fn;
+    int64_t grid;
+    // graph replay
+    hipGraphNode_t node;
+    // argument storage for launches and graph nodes
+    StepScalars sc;
+    int32_t chunk32;
+    void* args[5];
+};
+
+}  // namespace ou
+
+struct ou_plan_s {
+    int kind = 0;
+    int64_t n_elements = 0;
+    void* dmem = nullptr;
+    std::vector<ou::Group> groups;
+    hipGraph_t graph = nullptr;
+    hipGraphExec_t exec = nullptr;
+    int device = -1;
+};
+
+namespace ou {
+namespace {
+
+int build_plan(int kind, const ou_segment* segs, int32_t nseg, ou_plan_s** out)
+{
+    *out = nullptr;
+    if (kind != OU_ADAM && kind != OU_ADEMAMIX) return fail(OU_EINVAL, "unknown kind %d", kind);
+    if (nseg < 0 || (nseg > 0 && !segs)) return fail(OU_EINVAL, "bad segment array");
+    std::vector<Range> ranges;
+    ranges.reserve(static_cast<size_t>(nseg) * 4);
+    for (int i = 0; i < nseg; ++i)
+        if (int st = check_segment(kind, segs[i], i, &ranges)) return st;
+    if (int st = check_overlap(ranges)) return st;
+    const DeviceProps* dp = nullptr;
+    if (int st = g_devices.current(&dp)) return st;
+
+    ou_plan_s* plan = new (std::nothrow) ou_plan_s;
+    if (!plan) return fail(OU_ENOMEM, "plan");
+    plan->kind = kind;
+    (void)hipGetDevice(&plan->device);
+
+    // Host tables per dtype group: descriptors, then work items (largest
+    // chunks first so the long items start early).
+    struct HostGroup {
+        std::vector<SegDesc> segs;
+        std::vector<std::pair<int64_t, WorkItem>> items;   // (length, item)
+        MultiLaunch L;
+        int64_t chunk;
+    };
+    HostGroup hg[3];
+    for (int dt = 0; dt < 3; ++dt) {
+        hg[dt].L = select_multi(dt);
+        if (int w = g_force_waves.load()) hg[dt].L.waves = w;
+        if (int e = g_force_mepl.load()) hg[dt].L.epl = e;
+        if (int u = g_force_munroll.load()) hg[dt].L.unroll = u;
+        hg[dt].chunk = select_chunk(dt);
+        if (int c = g_force_chunk.load()) hg[dt].chunk = c;
+    }
+    for (int i = 0; i < nseg; ++i) {
+        const ou_segment& s = segs[i];
+        if (s.n == 0) continue;
+        HostGroup& G = hg[s.dtype];
+        SegDesc d;
+        d.p = s.param;
+        d.g = s.grad;
+        d.s1 = s.state1;
+        d.s2 = s.state2;
+        d.n = s.n;
+        d.vec_ok = streams_16b_aligned(kind, s) ? 1 : 0;
+        d.pad = 0;
+        const int32_t seg_idx = static_cast<int32_t>(G.segs.size());
+        G.segs.push_back(d);
+        const int64_t nchunks = (s.n + G.chunk - 1) / G.chunk;
+        if (nchunks > INT32_MAX) { delete plan; return fail(OU_EINVAL, "segment %d: too many chunks", i); }
+        for (int64_t c = 0; c < nchunks; ++c) {
+            const int64_t len = std::min<int64_t>(G.chunk, s.n - c * G.chunk);
+            G.items.push_back({len, WorkItem{seg_idx, static_cast<int32_t>(c)}});
+        }
+        plan->n_elements += s.n;
+    }
+    size_t bytes = 0;
+    for (auto& G : hg) {
+        std::stable_sort(G.items.begin(), G.items.end(),
+                         [](const auto& a, const auto& b) { return a.first > b.first; });
+        bytes += G.segs.size() * sizeof(SegDesc) + G.items.size() * sizeof(WorkItem);
+    }
+    if (bytes > 0) {
+        hipError_t e = hipMalloc(&plan->dmem, bytes);
+        if (e != hipSuccess) { delete plan; return fail(OU_ENOMEM, "hipMalloc(%zu): %s", bytes, hipGetErrorString(e)); }
+        std::vector<unsigned char> host(bytes);
+        size_t off = 0;
+        for (int dt = 0; dt < 3; ++dt) {
+            HostGroup& G = hg[dt];
+            if (G.segs.empty()) continue;
+            Group grp{};
+            grp.dtype = dt;
+            grp.L = G.L;
+            grp.chunk = G.chunk;
+            grp.n_items = static_cast<int64_t>(G.items.size());
+            grp.d_segs = reinterpret_cast<const SegDesc*>(static_cast<unsigned char*>(plan->dmem) + off);
+            std::memcpy(host.data() + off, G.segs.data(), G.segs.size() * sizeof(SegDesc));
+            off += G.segs.size() * sizeof(SegDesc);
+            grp.d_items = reinterpret_cast<const WorkItem*>(static_cast<unsigned char*>(plan->dmem) + off);
+            for (size_t k = 0; k < G.items.size(); ++k)
+                std::memcpy(host.data() + off + k * sizeof(WorkItem), &G.items[k].second, sizeof(WorkItem));
+            off += G.items.size() * sizeof(WorkItem);
+            grp.fn = multi_kernel(kind, dt, grp.L.epl, grp.L.unroll);
+            if (!grp.fn || grp.chunk % (kWave * grp.L.epl) != 0 || grp.chunk > INT32_MAX) {
+                (void)hipFree(plan->dmem);
+                delete plan;
+                return fail(OU_EINVAL, "no multi-tensor kernel for epl=%d unroll=%d chunk=%lld",
+                            grp.L.epl, grp.L.unroll, (long long)grp.chunk);
+            }
+            grp.grid = (grp.n_items + grp.L.waves - 1) / grp.L.waves;
+            grp.chunk32 = static_cast<int32_t>(grp.chunk);
+            plan->groups.push_back(grp);
+        }
+        e = hipMemcpy(plan->dmem, host.data(), bytes, hipMemcpyHostToDevice);
+        if (e != hipSuccess) {
+            (void)hipFree(plan->dmem);
+            delete plan;
+            return hip_fail(e, "hipMemcpy(plan tables)");
+        }
+    }
+    *out = plan;
+    return OU_OK;
+}
+
+void set_group_args(Group& g, const StepScalars& sc)
+{
+    g.sc = sc;
+    g.args[0] = const_cast<SegDesc**>(&g.d_segs);
+    g.args[1] = const_cast<WorkItem**>(&g.d_items);
+    g.args[2] = &g.n_items;
+    g.args[3] = &g.chunk32;
+    g.args[4] = &g.sc;
+}
+
+int plan_launch(ou_plan_s* plan, const StepScalars& sc, hipStream_t stream)
+{
+    for (Group& g : plan->groups) {
+        set_group_args(g, sc);
+        hipError_t e = launch(g.fn, g.grid, g.L.waves * kWave, g.args, stream);
+        if (e != hipSuccess) return hip_fail(e, "launch multi-tensor kernel");
+    }
+    return OU_OK;
+}
+
+int check_plan_device(ou_plan_s* plan)
+{
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    if (dev != plan->device) return fail(OU_EINVAL, "plan was created on device %d, current is %d", plan->device, dev);
+    return OU_OK;
+}
+
+}  // namespace
+}  // namespace ou
+
+// =============================================================== C ABI
+
+using namespace ou;
+
+extern "C" {
+
+__attribute__((visibility("default")))
+int optimizer_update_32bit(int kind, int dtype, void* param, const void* grad, float* state1,
+                           float* state2, int64_t n, float beta1, float beta2, float beta3,
+                           float alpha, float eps, float weight_decay, int64_t step, float lr,
+                           int skip_zeros, void* stream)
+{
+    ou_hparams h;
+    h.beta1 = beta1; h.beta2 = beta2; h.beta3 = beta3; h.alpha = alpha; h.eps = eps;
+    h.weight_decay = weight_decay; h.lr = lr; h.skip_zeros = skip_zeros; h.step = step;
+    if (int st = check_hparams(kind, h)) return st;
+    ou_segment s{param, grad, state1, state2, n, dtype, 0};
+    std::vector<Range> ranges;
+    ranges.reserve(4);
+    if (int st = check_segment(kind, s, 0, &ranges)) return st;
+    if (n == 0) return OU_OK;
+    if (int st = check_overlap(ranges)) return st;
+    const DeviceProps* dp = nullptr;
+    if (int st = g_devices.current(&dp)) return st;
+
+    bool vec = streams_16b_aligned(kind, s);
+    SingleLaunch L = select_single(dp->cu_count, kind, dtype, n, vec);
+    apply_single_forcing(&L, &vec);
+    const void* fn = single_kernel(kind, dtype, L.epl, L.unroll);
+    if (!fn || L.block < kWave || L.block > 1024 || L.block % kWave || L.grid < 1 || L.grid > INT32_MAX)
+        return fail(OU_EINVAL, "no kernel for block=%d epl=%d unroll=%d grid=%lld", L.block, L.epl,
+                    L.unroll, (long long)L.grid);
+    StepScalars sc = make_scalars(h);
+    int32_t vec_ok = vec ? 1 : 0;
+    void* args[] = {&param, const_cast<void**>(&grad), &state1, &state2, &n, &sc, &vec_ok};
+    hipError_t e = launch(fn, L.grid, L.block, args, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "launch single-tensor kernel");
+    return OU_OK;
+}
+
+__attribute__((visibility("default")))
+int optimizer_update_32bit_multi(int kind, const ou_segment* segs, int32_t nseg, const ou_hparams* hp,
+                                 void* stream)
+{
+    if (!hp) return fail(OU_EINVAL, "null hparams");
+    if (int st = check_hparams(kind, *hp)) return st;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (capturing(s)) return fail(OU_ECAPTURE, "optimizer_update_32bit_multi allocates; use a plan under capture");
+    ou_plan_s* plan = nullptr;
+    if (int st = build_plan(kind, segs, nseg, &plan)) return st;
+    int st = plan_launch(plan, make_scalars(*hp), s);
+    hipError_t e = hipStreamSynchronize(s);
+    ou_plan_destroy(plan);
+    if (st) return st;
+    if (e != hipSuccess) return hip_fail(e, "hipStreamSynchronize");
+    return OU_OK;
+}
+
+__attribute__((visibility("default")))
+int ou_plan_create(int kind, const ou_segment* segs, int32_t nseg, ou_plan* out)
+{
+    if (!out) return fail(OU_EINVAL, "null output handle");
+    *out = nullptr;
+    return build_plan(kind, segs, nseg, out);
+}
+
+__attribute__((visibility("default")))
+int ou_plan_step(ou_plan plan, const ou_hparams* hp, void* stream)
+{
+    if (!plan || !hp) return fail(OU_EINVAL, "null plan or hparams");
+    if (int st = check_hparams(plan->kind, *hp)) return st;
+    if (int st = check_plan_device(plan)) return st;
+    return plan_launch(plan, make_scalars(*hp), static_cast<hipStream_t>(stream));
+}
+
+__attribute__((visibility("default")))
+int ou_plan_graph_step(ou_plan plan, const ou_hparams* hp, void* stream)
+{
+    if (!plan || !hp) return fail(OU_EINVAL, "null plan or hparams");
+    if (int st = check_hparams(plan->kind, *hp)) return st;
+    if (int st = check_plan_device(plan)) return st;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (capturing(s)) return fail(OU_ECAPTURE, "ou_plan_graph_step inside a stream capture");
+    if (plan->groups.empty()) return OU_OK;
+    const StepScalars sc = make_scalars(*hp);
+    hipError_t e;
+    if (!plan->exec) {
+        e = hipGraphCreate(&plan->graph, 0);
+        if (e != hipSuccess) return hip_fail(e, "hipGraphCreate");
+        for (Group& g : plan->groups) {
+            set_group_args(g, sc);
+            hipKernelNodeParams kp{};
+            kp.func = const_cast<void*>(g.fn);
+            kp.gridDim = dim3(static_cast<unsigned>(g.grid));
+            kp.blockDim = dim3(static_cast<unsigned>(g.L.waves * kWave));
+            kp.sharedMemBytes = 0;
+            kp.kernelParams = g.args;
+            kp.extra = nullptr;
+            // groups touch disjoint memory: independent nodes
+            e = hipGraphAddKernelNode(&g.node, plan->graph, nullptr, 0, &kp);
+            if (e != hipSuccess) return hip_fail(e, "hipGraphAddKernelNode");
+        }
+        e = hipGraphInstantiate(&plan->exec, plan->graph, nullptr, nullptr, 0);
+        if (e != hipSuccess) {
+            plan->exec = nullptr;
+            return hip_fail(e, "hipGraphInstantiate");
+        }
+    } else {
+        for (Group& g : plan->groups) {
+            set_group_args(g, sc);
+            hipKernelNodeParams kp{};
+            kp.func = const_cast<void*>(g.fn);
+            kp.gridDim = dim3(static_cast<unsigned>(g.grid));
+            kp.blockDim = dim3(static_cast<unsigned>(g.L.waves * kWave));
+            kp.sharedMemBytes = 0;
+            kp.kernelParams = g.args;
+            kp.extra = nullptr;
+            e = hipGraphExecKernelNodeSetParams(plan->exec, g.node, &kp);
+            if (e != hipSuccess) return hip_fail(e, "hipGraphExecKernelNodeSetParams");
+        }
+    }
+    e = hipGraphLaunch(plan->exec, s);
+    if (e != hipSuccess) return hip_fail(e, "hipGraphLaunch");
+    return OU_OK;
+}
+
+__attribute__((visibility("default")))
+int ou_plan_describe(ou_plan plan, int32_t* n_groups, int64_t* n_work_items, int64_t* n_elements)
+{
+    if (!plan) return fail(OU_EINVAL, "null plan");
+    int64_t items = 0;
+    for (const Group& g : plan->groups) items += g.n_items;
+    if (n_groups) *n_groups = static_cast<int32_t>(plan->groups.size());
+    if (n_work_items) *n_work_items = items;
+    if (n_elements) *n_elements = plan->n_elements;
+    return OU_OK;
+}
+
+__attribute__((visibility("default")))
+void ou_plan_destroy(ou_plan plan)
+{
+    if (!plan) return;
+    if (plan->exec) (void)hipGraphExecDestroy(plan->exec);
+    if (plan->graph) (void)hipGraphDestroy(plan->graph);
+    if (plan->dmem) (void)hipFree(plan->dmem);
+    delete plan;
+}
+
+__attribute__((visibility("default")))
+const char* ou_status_string(int status)
+{
+    switch (status) {
+    case OU_OK: return "OU_OK";
+    case OU_EINVAL: return "OU_EINVAL: invalid argument";
+    case OU_EUNSUPPORTED: return "OU_EUNSUPPORTED: unsupported device";
+    case OU_EALIGN: return "OU_EALIGN: misaligned pointer";
+    case OU_EOVERLAP: return "OU_EOVERLAP: overlapping buffers";
+    case OU_ENOMEM: return "OU_ENOMEM: allocation failed";
+    case OU_EHIP: return "OU_EHIP: HIP runtime error";
+    case OU_ECAPTURE: return "OU_ECAPTURE: not allowed during stream capture";
+    default: return "unknown status";
+    }
+}
+
+__attribute__((visibility("default")))
+const char* ou_last_error(void) { return g_last_error.c_str(); }
+
+// ---- test hooks (declared in ou_testing.h, not in the public header) -----------
+
+__attribute__((visibility("default")))
+int ou__select_single(int cu_count, int kind, int dtype, int64_t n, int aligned, int64_t out[4])
+{
+    if (!out) return OU_EINVAL;
+    SingleLaunch L = select_single(cu_count, kind, dtype, n, aligned != 0);
+    out[0] = L.block;
+    out[1] = L.epl;
+    out[2] = L.unroll;
+    out[3] = L.grid;
+    return OU_OK;
+}
+
+__attribute__((visibility("default")))
+void ou__force_single(int block, int epl, int unroll, int64_t grid, int scalar_only)
+{
+    g_force_block = block;
+    g_force_epl = epl;
+    g_force_unroll = unroll;
+    g_force_grid = grid;
+    g_force_scalar = scalar_only;
+}
+
+__attribute__((visibility("default")))
+void ou__force_multi(int waves, int epl, int unroll, int chunk)
+{
+    g_force_waves = waves;
+    g_force_mepl = epl;
+    g_force_munroll = unroll;
+    g_force_chunk = chunk;
+}
+
+__attribute__((visibility("default")))
+int ou__step_scalars(const ou_hparams* hp, float out[12])
+{
+    if (!hp || !out) return OU_EINVAL;
+    StepScalars s = make_scalars(*hp);
+    const float v[12] = {s.beta1, s.beta2, s.beta3, s.omb1, s.omb2, s.omb3,
+                         s.alpha, s.eps, s.lr, s.bc1, s.bc2, s.decay};
+    std::memcpy(out, v, sizeof v);
+    return OU_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,54 @@
+// internal.h -- declarations shared by the host library and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "elem.hpp"
+
+namespace ou {
+
+// Segment descriptor of the multi-tensor walk (device-resident table).
+struct SegDesc {
+    void* p;
+    const void* g;
+    float* s1;
+    float* s2;
+    int64_t n;
+    int32_t vec_ok;  // every stream 16-byte aligned (dwordx4 path)
+    int32_t pad;
+};
+static_assert(sizeof(SegDesc) == 48, "SegDesc layout");
+
+// Work item: one wave updates elements [chunk*chunk_elems, min(n, +chunk_elems))
+// of segment seg.
+struct WorkItem {
+    int32_t seg;
+    int32_t chunk;
+};
+static_assert(sizeof(WorkItem) == 8, "WorkItem layout");
+
+// Launch shape of the single-tensor kernel.
+struct SingleLaunch {
+    int block;    // threads per block: 64, 128, 256, 512 or 1024
+    int epl;      // elements per lane per vector group: 4 or 8
+    int unroll;   // vector groups in flight per lane: 1, 2 or 4
+    int64_t grid; // blocks
+};
+
+// Launch shape of the multi-tensor kernel.
+struct MultiLaunch {
+    int waves;    // waves per block: 1, 2, 4 or 8
+    int epl;      // 4 or 8
+    int unroll;   // 1, 2 or 4
+};
+
+// Kernel entry for the single-tensor streaming kernel (nullptr if the
+// combination is not instantiated).
+const void* single_kernel(int kind, int dtype, int epl, int unroll);
+// Kernel entry for the multi-tensor kernel.
+const void* multi_kernel(int kind, int dtype, int epl, int unroll);
+
+constexpr int kWave = 64;
+
+}  // namespace ou

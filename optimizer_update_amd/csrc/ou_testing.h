@@ -1,0 +1,36 @@
+// ou_testing.h -- test-only hooks of liboptimizer_update.so.
+//
+// Not part of the public ABI (include/optimizer_update.h): launch-shape
+// forcing stays out of the public interface, as the page "Investigate a
+// 256-thread SM103 path for small 32-bit optimizer tensors" asks for its own
+// variant forcing (section "Scope").  The tests use these to run every
+// launch variant and compare results bitwise, and to check launch selection
+// on a CPU with fabricated device properties.
+#pragma once
+
+#include <stdint.h>
+
+#include "../../include/optimizer_update.h"
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+// Launch shape the single-tensor entry would pick for a device with
+// cu_count compute units: out = {block, epl, unroll, grid}.
+int ou__select_single(int cu_count, int kind, int dtype, int64_t n, int aligned, int64_t out[4]);
+
+// Force the single-tensor launch shape (0 = no forcing for that field);
+// scalar_only != 0 forces the one-element-per-lane path.  Process-wide.
+void ou__force_single(int block, int epl, int unroll, int64_t grid, int scalar_only);
+
+// Force the multi-tensor shape used by plans created afterwards
+// (0 = no forcing).  chunk must be a multiple of 64 * epl.
+void ou__force_multi(int waves, int epl, int unroll, int chunk);
+
+// The per-step scalars: beta1..3, 1-beta1..3, alpha, eps, lr, bc1, bc2, decay.
+int ou__step_scalars(const ou_hparams* hp, float out[12]);
+
+#ifdef __cplusplus
+}
+#endif

@@ -1,0 +1,103 @@
+"""Collection optimizers over a fixed parameter list (argument marshalling only).
+
+``AdamW32`` and ``AdEMAMix32`` play the part of the 32-bit collection
+optimizers that the page "Investigate a 256-thread SM103 path for small
+32-bit optimizer tensors" times in its eager ``optimizer.step()`` workloads
+(section "B300 benchmark and acceptance"): they own the fp32 states of every
+parameter and update the whole collection per step through one plan (one
+launch per dtype group), its HIP-graph replay, or, for comparison, one
+direct call per tensor.
+
+Parameters and gradients must be contiguous CUDA (HIP) tensors whose
+storage stays in place for the optimizer's lifetime: the plan holds their
+addresses.
+"""
+from __future__ import annotations
+
+import torch
+
+from . import HParams, Plan, optimizer_update_32bit, state_sizes
+
+
+class _Collection:
+    kind = "adam"
+
+    def __init__(self, params, hp: HParams, grads=None):
+        self.params = [p.data if isinstance(p, torch.nn.Parameter) else p for p in params]
+        if grads is None:
+            grads = []
+            for p, src in zip(self.params, params):
+                g = getattr(src, "grad", None)
+                if g is None:
+                    g = torch.zeros_like(p)
+                    if isinstance(src, torch.nn.Parameter):
+                        src.grad = g
+                grads.append(g)
+        self.grads = list(grads)
+        self.hp = hp
+        self.state1, self.state2 = [], []
+        for p in self.params:
+            n1, n2 = state_sizes(self.kind, p.numel())
+            self.state1.append(torch.zeros(n1, dtype=torch.float32, device=p.device))
+            self.state2.append(torch.zeros(n2, dtype=torch.float32, device=p.device))
+        self.step_count = 0
+        self.plan = Plan(self.kind, list(zip(self.params, self.grads, self.state1, self.state2)))
+
+    def segments(self):
+        return list(zip(self.params, self.grads, self.state1, self.state2))
+
+    @torch.no_grad()
+    def step(self, graph: bool = False, stream=None) -> None:
+        """One step of the whole collection: plan launch, or graph replay."""
+        self.step_count += 1
+        if graph:
+            self.plan.graph_step(self.hp, self.step_count, stream)
+        else:
+            self.plan.step(self.hp, self.step_count, stream)
+
+    @torch.no_grad()
+    def step_per_tensor(self, stream=None) -> None:
+        """The same step as one direct call per tensor."""
+        self.step_count += 1
+        h = self.hp
+        for p, g, s1, s2 in self.segments():
+            optimizer_update_32bit(self.kind, p, g, s1, s2, step=self.step_count, lr=h.lr,
+                                   beta1=h.beta1, beta2=h.beta2, beta3=h.beta3, alpha=h.alpha,
+                                   eps=h.eps, weight_decay=h.weight_decay,
+                                   skip_zeros=h.skip_zeros, stream=stream)
+
+    def state_dict(self) -> dict:
+        return {"step": self.step_count,
+                "state1": [s.clone() for s in self.state1],
+                "state2": [s.clone() for s in self.state2]}
+
+    def load_state_dict(self, sd: dict) -> None:
+        self.step_count = int(sd["step"])
+        for dst, src in zip(self.state1, sd["state1"]):
+            dst.copy_(src)
+        for dst, src in zip(self.state2, sd["state2"]):
+            dst.copy_(src)
+
+    def close(self) -> None:
+        self.plan.close()
+
+
+class AdamW32(_Collection):
+    """Adam with decoupled weight decay (weight_decay = 0 gives Adam)."""
+    kind = "adam"
+
+    def __init__(self, params, lr=1e-3, betas=(0.9, 0.999), eps=1e-8, weight_decay=0.01,
+                 skip_zeros=False, grads=None):
+        super().__init__(params, HParams(lr=lr, beta1=betas[0], beta2=betas[1], eps=eps,
+                                         weight_decay=weight_decay, skip_zeros=skip_zeros), grads)
+
+
+class AdEMAMix32(_Collection):
+    """AdEMAMix: Adam plus a slow EMA (beta3) mixed in with weight alpha."""
+    kind = "ademamix"
+
+    def __init__(self, params, lr=1e-3, betas=(0.9, 0.999, 0.9999), alpha=5.0, eps=1e-8,
+                 weight_decay=0.01, skip_zeros=False, grads=None):
+        super().__init__(params, HParams(lr=lr, beta1=betas[0], beta2=betas[1], beta3=betas[2],
+                                         alpha=alpha, eps=eps, weight_decay=weight_decay,
+                                         skip_zeros=skip_zeros), grads)

@@ -74,7 +74,12 @@ def params(n: int, storage: str, g: np.random.Generator) -> np.ndarray:
 
 def grads(n: int, pattern: str, storage: str, g: np.random.Generator,
           sigma: float = 1.0) -> np.ndarray:
-    """Gradients of one pattern, cast to storage.
+    """Gradients of one pattern, cast to storage (see ``grads_f32``)."""
+    return cast_storage(grads_f32(n, pattern, g, sigma), storage)
+
+
+def grads_f32(n: int, pattern: str, g: np.random.Generator, sigma: float = 1.0) -> np.ndarray:
+    """Gradients of one pattern in fp32.
 
     zero   : all +0
     normal : N(0, sigma^2)  (sigma is the standard deviation)
@@ -91,7 +96,7 @@ def grads(n: int, pattern: str, storage: str, g: np.random.Generator,
         x = (sign * 10.0 ** g.uniform(-8.0, 3.0, n)).astype(np.float32)
     else:
         raise ValueError(pattern)
-    return cast_storage(x, storage)
+    return x
 
 
 def zero_states(n: int, kind: str) -> tuple[np.ndarray, np.ndarray]:
