@@ -1,0 +1,277 @@
+"""Benchmark of the 32-bit two-state optimizer update on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--quick]
+
+Headline ("step"): one Adam update (fp32 param/grad/states) of a flat tensor
+of 2^28 elements, inputs resident in HBM.  value = algorithmic bytes
+(28 B/element: read p, g, m, v; write p, m, v) / time per step, in GB/s.
+
+Also measured (same JSON line): the other kinds and storages at 2^28 and
+fp32 Adam at 2^30; a plain device copy as the achievable-bandwidth
+reference; the model-like collection (505 bf16 tensors, AdamW) as an eager
+per-tensor loop, one plan launch and graph replay, its small-tensor subset,
+and the launch floor (a 1-element update); the CPU oracle on a bounded
+sample of the headline workload.
+
+Timing: HIP events on the stream the kernels run on, W untimed warmups, then
+K timed steps between device synchronisations.  Secondary cases report the
+median and p10/p90 of 7 rounds.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+METRIC = "optimizer-update GB/s (% of HBM peak) on 256M elems; µs per mixed small-tensor step"
+KERNEL_SOURCES = ("optimizer_update_amd/csrc/kernels.hip", "optimizer_update_amd/csrc/elem.hpp")
+
+
+def kernel_sha() -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--quick", action="store_true", help="headline only (for profiling runs)")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--case", default="adam:fp32:28",
+                    help="headline case kind:storage:log2n (profiling runs)")
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py: this build runs on one GPU only (the update needs no exchange inside "
+              "a step; see DESIGN.md for how it would shard); rerun with --gpus 1",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import optimizer_update_amd as ou
+    import workloads as W
+
+    assert torch.cuda.is_available(), "bench.py needs a HIP device"
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    lib = ou.load()
+    props = torch.cuda.get_device_properties(dev)
+
+    def make_flat(kind, storage, n, seed):
+        gen = torch.Generator(device=dev)
+        gen.manual_seed(seed)
+        p = torch.empty(n, device=dev).uniform_(-1.0, 1.0, generator=gen).to(W.STORAGE_TORCH[storage])
+        g = (torch.randn(n, device=dev, generator=gen) * 1e-3).to(W.STORAGE_TORCH[storage])
+        s1n, s2n = ou.state_sizes(kind, n)
+        return p, g, torch.zeros(s1n, device=dev), torch.zeros(s2n, device=dev)
+
+    hp_adam = ou.HParams(lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.0)
+    hp_mix = ou.HParams(lr=1e-3, beta1=0.9, beta2=0.999, beta3=0.9999, alpha=5.0, eps=1e-8,
+                        weight_decay=0.01)
+
+    def flat_stepper(kind, tensors, hp):
+        p, g, s1, s2 = tensors
+        state = {"t": 0}
+
+        def step():
+            state["t"] += 1
+            ou.optimizer_update_32bit(kind, p, g, s1, s2, step=state["t"], lr=hp.lr, beta1=hp.beta1,
+                                      beta2=hp.beta2, beta3=hp.beta3, alpha=hp.alpha, eps=hp.eps,
+                                      weight_decay=hp.weight_decay, skip_zeros=hp.skip_zeros)
+        return step
+
+    def time_exact(step, steps, warmup):
+        """W warmups, then exactly K steps between synchronisations; HIP events
+        on the current stream (where the library launches)."""
+        for _ in range(warmup):
+            step()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        t0 = time.perf_counter()
+        e0.record()
+        for _ in range(steps):
+            step()
+        e1.record()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        return e0.elapsed_time(e1) / steps, wall / steps * 1e3
+
+    def time_rounds(step, iters, rounds=7, warmup=20):
+        """Median, p10, p90 of per-step ms over `rounds` samples of `iters` steps."""
+        for _ in range(warmup):
+            step()
+        torch.cuda.synchronize()
+        samples = []
+        for _ in range(rounds):
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(iters):
+                step()
+            e1.record()
+            torch.cuda.synchronize()
+            samples.append(e0.elapsed_time(e1) / iters)
+        samples.sort()
+        q = lambda f: samples[min(len(samples) - 1, int(round(f * (len(samples) - 1))))]
+        return {"median_ms": statistics.median(samples), "p10_ms": q(0.1), "p90_ms": q(0.9)}
+
+    # ---------------------------------------------------------------- headline
+    kind, storage, log2n = args.case.split(":")
+    n = 1 << int(log2n)
+    bpe = W.bytes_per_element(kind, storage)
+    hp_head = hp_adam if kind == "adam" else hp_mix
+    head = make_flat(kind, storage, n, seed=0)
+    ms, wall_ms = time_exact(flat_stepper(kind, head, hp_head), args.steps, args.warmup)
+    gbs = bpe * n / (ms * 1e-3) / 1e9
+
+    out = {
+        "metric": METRIC, "value": round(gbs, 1), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f32", "data": "synthetic",
+        "config": {"workload": f"{kind}_{storage}_flat_2^{log2n}", "n": n, "kind": kind,
+                   "param_grad_storage": storage, "states": "fp32",
+                   "params": "U(-1,1)", "grads": "N(0, (1e-3)^2), fixed",
+                   "hparams": {k: v for k, v in hp_head.__dict__.items()},
+                   "bytes_per_element": bpe, "device": props.name, "cu_count": props.multi_processor_count,
+                   "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None},
+        "host_wall_ms_per_step": round(wall_ms, 4),
+        "kernel_sources_sha": kernel_sha(),
+    }
+    tr = os.path.join(ROOT, "profiles", "traffic_single_adam_fp32_256M.json")
+    if os.path.exists(tr) and args.case == "adam:fp32:28":
+        with open(tr) as f:
+            t = json.load(f)
+        if t.get("kernel_sources_sha") == out["kernel_sources_sha"]:
+            out["roofline"]["traffic"] = t["hbm_bytes_per_launch"]
+    del head
+    torch.cuda.empty_cache()
+
+    if not args.quick:
+        cases = {}
+        # achievable bandwidth reference: device copy of 2^28 floats
+        src = torch.empty(1 << 28, device=dev).uniform_()
+        dst = torch.empty_like(src)
+        r = time_rounds(lambda: dst.copy_(src), iters=20)
+        cases["copy_fp32_2^28"] = {**r, "GBps": round(2 * 4 * (1 << 28) / (r["median_ms"] * 1e-3) / 1e9, 1)}
+        del src, dst
+        torch.cuda.empty_cache()
+        for ck, cs, cl in (("adam", "bf16", 28), ("ademamix", "fp32", 28), ("ademamix", "bf16", 28),
+                           ("adam", "fp32", 30)):
+            cn = 1 << cl
+            hp = hp_adam if ck == "adam" else hp_mix
+            ts = make_flat(ck, cs, cn, seed=cl)
+            r = time_rounds(flat_stepper(ck, ts, hp), iters=10 if cl == 28 else 4)
+            b = W.bytes_per_element(ck, cs)
+            gb = b * cn / (r["median_ms"] * 1e-3) / 1e9
+            cases[f"{ck}_{cs}_2^{cl}"] = {**r, "GBps": round(gb, 1), "frac_of_peak": round(gb / HBM_PEAK_GBS, 4),
+                                          "elements_per_s": round(cn / (r["median_ms"] * 1e-3), 0)}
+            del ts
+            torch.cuda.empty_cache()
+        cases["adam_fp32_2^28"] = {"median_ms": out["ms_per_step"], "GBps": out["value"],
+                                   "frac_of_peak": out["roofline"]["frac"]} if args.case == "adam:fp32:28" else None
+        copy_gbs = cases["copy_fp32_2^28"]["GBps"]
+        out["roofline"]["frac_of_copy"] = round(gbs / copy_gbs, 4)
+        out["cases"] = cases
+        out["small_step_us"] = bench_collection(torch, ou, W, dev, time_rounds)
+        if not args.no_cpu:
+            out["cpu_baseline"] = cpu_baseline(torch, W, dev)
+    print(json.dumps(out))
+
+
+def bench_collection(torch, ou, W, dev, time_rounds):
+    """Model-like collection (bf16 AdamW): full step and small-tensor subset,
+    each as per-tensor loop, one plan launch, graph replay; launch floor."""
+    res = {}
+    shapes = W.model_collection()
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(4)
+
+    def mk(subset):
+        ps, gs = [], []
+        for name, shp in subset:
+            m = W.numel(shp)
+            ps.append(torch.empty(m, device=dev).uniform_(-1, 1, generator=gen).to(torch.bfloat16))
+            gs.append((torch.randn(m, device=dev, generator=gen) * 0.01).to(torch.bfloat16))
+        return ou.AdamW32(ps, lr=1e-3, weight_decay=0.01, grads=gs)
+
+    for label, subset in (("full_505", shapes), ("small_408", [s for s in shapes if W.numel(s[1]) <= 16384])):
+        opt = mk(subset)
+        elems = sum(W.numel(s[1]) for s in subset)
+        bytes_ = elems * W.bytes_per_element("adam", "bf16")
+        d = {"tensors": len(subset), "elements": elems, "roofline_us": round(bytes_ / HBM_PEAK_GBS / 1e3, 2)}
+        for mode, fn in (("per_tensor_loop", opt.step_per_tensor), ("plan", lambda: opt.step()),
+                         ("graph", lambda: opt.step(graph=True))):
+            iters = 5 if mode == "per_tensor_loop" else 50
+            r = time_rounds(fn, iters=iters, rounds=7, warmup=5)
+            d[mode] = {k: round(v * 1e3, 2) for k, v in r.items()}   # ms -> us
+            d[mode] = {"median_us": d[mode]["median_ms"], "p10_us": d[mode]["p10_ms"], "p90_us": d[mode]["p90_ms"]}
+        d["plan_GBps"] = round(bytes_ / (d["plan"]["median_us"] * 1e-6) / 1e9, 1)
+        d["plan_describe"] = opt.plan.describe()
+        res[label] = d
+        opt.close()
+        torch.cuda.empty_cache()
+    # launch floor: a 1-element update through the C ABI, back to back
+    one = [torch.zeros(1, device=dev) for _ in range(4)]
+    t = {"i": 0}
+
+    def tiny():
+        t["i"] += 1
+        ou.optimizer_update_32bit("adam", one[0], one[1], one[2], one[3], step=t["i"], lr=1e-3)
+    r = time_rounds(tiny, iters=200, rounds=7, warmup=50)
+    res["launch_floor_1_element_us"] = round(r["median_ms"] * 1e3, 2)
+    return res
+
+
+def cpu_baseline(torch, W, dev):
+    """The CPU oracle on a bounded sample of the headline workload (2^25
+    elements of fp32 Adam drawn with the same recipe, 3 steps), all host
+    cores."""
+    import numpy as np
+
+    import oracle as O
+
+    orc = O.load()
+    cores = len(os.sched_getaffinity(0))
+    n = 1 << 25
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(0)
+    p = torch.empty(n, device=dev).uniform_(-1.0, 1.0, generator=gen).cpu().numpy()
+    g = (torch.randn(n, device=dev, generator=gen) * 1e-3).cpu().numpy()
+    s1 = np.zeros(n, np.float32)
+    s2 = np.zeros(n, np.float32)
+    hp = O.HParams(lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.0)
+    steps = 3
+    t0 = time.perf_counter()
+    for t in range(1, steps + 1):
+        orc.update_f32(O.ADAM, O.F32, p, g, s1, s2, hp, t, nthreads=cores)
+    dt = time.perf_counter() - t0
+    gbs = W.bytes_per_element("adam", "fp32") * n * steps / dt / 1e9
+    return {"value": round(gbs, 2), "unit": "GB/s", "cores": cores, "kind": "oracle",
+            "sample": f"fp32 Adam on 2^25 elements drawn with the headline's recipe (params U(-1,1), "
+                      f"grads N(0,(1e-3)^2)), {steps} steps, {dt:.2f} s wall, OpenMP static schedule",
+            "elements_per_s": round(n * steps / dt, 0)}
+
+
+if __name__ == "__main__":
+    main()

@@ -7,9 +7,10 @@
 // instruction covers 1 KiB of contiguous memory; UNROLL vector groups per
 // lane are loaded before any is computed, to keep enough bytes in flight.
 //
-//   k_single: one tensor; grid-stride over vector groups, then the ragged
-//             tail (and any tensor whose streams are not all 16-byte
-//             aligned) one element per lane.
+//   k_single: one tensor; one tile of blockDim * UNROLL vector groups per
+//             block (a grid-stride loop takes over only if the grid had to be
+//             capped), then the ragged tail (and any tensor whose streams are
+//             not all 16-byte aligned) one element per lane.
 //   k_multi:  a collection; each wave takes one work item (segment, chunk)
 //             from a device-side list and streams that chunk.  Item and
 //             segment descriptor are wave-uniform (scalar loads), so a small
@@ -17,6 +18,13 @@
 //
 // Both call update_element from elem.hpp, so launch shape never changes
 // the arithmetic.
+//
+// Measured on MI355X (2^28 elements): one tile per block (grid covering the
+// tensor, no grid-stride) with 512 threads and two groups of 4 elements per
+// lane runs fp32 Adam at ~5.9 TB/s, the same as a trivial kernel with the
+// same 4-read/3-write pattern; a capped grid-stride grid loses 10-20%, and 8
+// elements per lane (two dwordx4 per lane per stream) loses up to 40% with
+// non-temporal accesses.
 #include "internal.h"
 
 #pragma clang fp contract(off)
@@ -31,19 +39,25 @@ struct Words {
     uint32_t w[DW];
 };
 
+// Every byte is touched once per step, so loads and stores carry the
+// non-temporal hint (streamed past the caches): on gfx950 this lifts the
+// 4-read/3-write stream of the update by ~5-8% over plain accesses.
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
 template <int DW>
 __device__ __forceinline__ Words<DW> load_words(const void* ptr)
 {
     Words<DW> r;
     if constexpr (DW == 2) {
-        const uint2 x = *reinterpret_cast<const uint2*>(ptr);
+        const u32x2 x = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(ptr));
         r.w[0] = x.x;
         r.w[1] = x.y;
     } else {
         static_assert(DW % 4 == 0, "dwordx4 granularity");
 #pragma unroll
         for (int k = 0; k < DW / 4; ++k) {
-            const uint4 x = reinterpret_cast<const uint4*>(ptr)[k];
+            const u32x4 x = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(ptr) + k);
             r.w[4 * k + 0] = x.x;
             r.w[4 * k + 1] = x.y;
             r.w[4 * k + 2] = x.z;
@@ -57,12 +71,14 @@ template <int DW>
 __device__ __forceinline__ void store_words(void* ptr, const Words<DW>& r)
 {
     if constexpr (DW == 2) {
-        *reinterpret_cast<uint2*>(ptr) = make_uint2(r.w[0], r.w[1]);
+        const u32x2 x = {r.w[0], r.w[1]};
+        __builtin_nontemporal_store(x, reinterpret_cast<u32x2*>(ptr));
     } else {
 #pragma unroll
-        for (int k = 0; k < DW / 4; ++k)
-            reinterpret_cast<uint4*>(ptr)[k] =
-                make_uint4(r.w[4 * k + 0], r.w[4 * k + 1], r.w[4 * k + 2], r.w[4 * k + 3]);
+        for (int k = 0; k < DW / 4; ++k) {
+            const u32x4 x = {r.w[4 * k + 0], r.w[4 * k + 1], r.w[4 * k + 2], r.w[4 * k + 3]};
+            __builtin_nontemporal_store(x, reinterpret_cast<u32x4*>(ptr) + k);
+        }
     }
 }
 
