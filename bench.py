@@ -52,6 +52,11 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--case", default="adam:fp32:28",
                     help="headline case kind:storage:log2n (profiling runs)")
+    ap.add_argument("--collection-only", action="store_true",
+                    help="only the model-like collection measurements (profiling runs)")
+    ap.add_argument("--copy-only", action="store_true",
+                    help="only a plain device copy of 2^28 floats (1 GiB each way): the "
+                         "known-size kernel that calibrates HBM byte counters")
     return ap.parse_args()
 
 
@@ -132,6 +137,19 @@ def main():
         samples.sort()
         q = lambda f: samples[min(len(samples) - 1, int(round(f * (len(samples) - 1))))]
         return {"median_ms": statistics.median(samples), "p10_ms": q(0.1), "p90_ms": q(0.9)}
+
+    if args.copy_only:
+        src = torch.empty(1 << 28, device=dev).uniform_()
+        dst = torch.empty_like(src)
+        for _ in range(args.steps):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_each_way": 4 << 28, "launches": args.steps}))
+        return
+
+    if args.collection_only:
+        print(json.dumps(bench_collection(torch, ou, W, dev, time_rounds)))
+        return
 
     # ---------------------------------------------------------------- headline
     kind, storage, log2n = args.case.split(":")

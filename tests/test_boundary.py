@@ -1,0 +1,226 @@
+"""CPU tests of the C ABI (no GPU): exports, layout, validation, dispatch.
+
+Every call here fails validation (or is n = 0) and so returns before the
+library touches the HIP runtime; nothing is launched.
+"""
+import ctypes
+import os
+import re
+import subprocess
+
+import numpy as np
+import pytest
+
+import oracle as O
+from optimizer_update_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "optimizer_update.h")
+
+OU_OK, OU_EINVAL, OU_EALIGN, OU_EOVERLAP = 0, -1, -3, -4
+
+
+@pytest.fixture(scope="module")
+def L():
+    return _lib.load()
+
+
+def test_exports_every_header_function(L):
+    names = _lib.header_functions()
+    assert set(names) == {"optimizer_update_32bit", "optimizer_update_32bit_multi",
+                          "ou_plan_create", "ou_plan_step", "ou_plan_graph_step",
+                          "ou_plan_describe", "ou_plan_destroy", "ou_status_string",
+                          "ou_last_error"}
+    for n in names:
+        assert hasattr(L, n), n
+    out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIBRARY], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r" T (\w+)$", out, flags=re.M))
+    assert set(names) <= exported
+    # nothing else is exported besides the test hooks
+    assert exported - set(names) == {"ou__select_single", "ou__force_single", "ou__force_multi",
+                                     "ou__step_scalars"}
+
+
+def test_header_is_plain_c_and_matches_ctypes_layout(tmp_path):
+    src = tmp_path / "layout.c"
+    src.write_text(
+        '#include <stddef.h>\n#include <stdio.h>\n#include "optimizer_update.h"\n'
+        'int main(void){printf("%zu %zu %zu %zu %zu %zu\\n", sizeof(ou_hparams), '
+        'offsetof(ou_hparams, skip_zeros), offsetof(ou_hparams, step), sizeof(ou_segment), '
+        'offsetof(ou_segment, n), offsetof(ou_segment, dtype)); return 0;}\n')
+    exe = tmp_path / "layout"
+    subprocess.run(["gcc", "-std=c99", "-Wall", "-Werror", "-I", os.path.dirname(HEADER),
+                    str(src), "-o", str(exe)], check=True)
+    got = list(map(int, subprocess.run([str(exe)], capture_output=True, text=True,
+                                       check=True).stdout.split()))
+    H, S = _lib.ou_hparams, _lib.ou_segment
+    assert got == [ctypes.sizeof(H), H.skip_zeros.offset, H.step.offset, ctypes.sizeof(S),
+                   S.n.offset, S.dtype.offset]
+
+
+def _call(L, kind=0, dtype=0, p=0x10000, g=0x20000, s1=0x30000, s2=0x40000, n=16, b1=0.9,
+          b2=0.999, b3=0.9999, alpha=5.0, eps=1e-8, wd=0.0, step=1, lr=1e-3, skip=0):
+    return L.optimizer_update_32bit(kind, dtype, p, g, s1, s2, n, b1, b2, b3, alpha, eps, wd,
+                                    step, lr, skip, None)
+
+
+def _segs(*rows):
+    arr = (_lib.ou_segment * len(rows))()
+    for i, r in enumerate(rows):
+        arr[i] = _lib.ou_segment(*r)
+    return arr
+
+
+@pytest.mark.parametrize("case,kw,code", [
+    ("unknown kind", dict(kind=2), OU_EINVAL),
+    ("unknown dtype", dict(dtype=3), OU_EINVAL),
+    ("negative n", dict(n=-1), OU_EINVAL),
+    ("step 0", dict(step=0), OU_EINVAL),
+    ("beta1 = 1", dict(b1=1.0), OU_EINVAL),
+    ("beta2 < 0", dict(b2=-0.1), OU_EINVAL),
+    ("beta2 nan", dict(b2=float("nan")), OU_EINVAL),
+    ("ademamix beta3 = 1", dict(kind=1, b3=1.0), OU_EINVAL),
+    ("ademamix alpha inf", dict(kind=1, alpha=float("inf")), OU_EINVAL),
+    ("eps < 0", dict(eps=-1e-8), OU_EINVAL),
+    ("lr inf", dict(lr=float("inf")), OU_EINVAL),
+    ("wd nan", dict(wd=float("nan")), OU_EINVAL),
+    ("null param", dict(p=0), OU_EINVAL),
+    ("null grad", dict(g=0), OU_EINVAL),
+    ("fp32 param 2-byte aligned", dict(p=0x10002), OU_EALIGN),
+    ("fp16 grad odd address", dict(dtype=1, g=0x20001), OU_EALIGN),
+    ("state not 4-byte aligned", dict(s2=0x40002), OU_EALIGN),
+    ("param overlaps grad", dict(p=0x20000 - 32), OU_EOVERLAP),
+    ("grad overlaps state1", dict(g=0x30000 + 4), OU_EOVERLAP),
+    ("ademamix slow plane overlaps state2", dict(kind=1, s2=0x30000 + 4 * 16), OU_EOVERLAP),
+    ("state1 is state2", dict(s2=0x30000), OU_EOVERLAP),
+])
+def test_single_entry_validation(L, case, kw, code):
+    assert _call(L, **kw) == code, case
+    assert L.ou_last_error().decode(), "an error message is set"
+
+
+def test_adjacent_buffers_are_not_overlap_and_n0_is_noop(L):
+    # n = 0 returns before any device work, whatever the pointers
+    assert _call(L, n=0) == OU_OK
+    assert _call(L, n=0, p=0, g=0, s1=0, s2=0) == OU_OK
+    # touching ranges pass validation.  Checked through plan creation, which
+    # launches nothing (on a machine with a GPU it would only upload a table
+    # for these fabricated addresses, then be destroyed).
+    h = ctypes.c_void_p()
+    seg = _segs((0x10000, 0x10000 + 64, 0x10000 + 128, 0x10000 + 192, 16, 0, 0))
+    st = L.ou_plan_create(0, seg, 1, ctypes.byref(h))
+    assert st not in (OU_EINVAL, OU_EALIGN, OU_EOVERLAP)
+    L.ou_plan_destroy(h)
+
+
+def test_plan_and_multi_validation(L):
+    h = ctypes.c_void_p()
+    ok = (0x100000, 0x200000, 0x300000, 0x400000, 1024, 0, 0)
+    cases = {
+        "overlapping params across segments": ([ok, (0x100000 + 4 * 512, 0x500000, 0x600000, 0x700000, 1024, 0, 0)], OU_EOVERLAP),
+        "grad shared with another segment's state": ([ok, (0x800000, 0x300000, 0x900000, 0xa00000, 8, 0, 0)], OU_EOVERLAP),
+        "bad dtype": ([(0x100000, 0x200000, 0x300000, 0x400000, 16, 7, 0)], OU_EINVAL),
+        "reserved not zero": ([(0x100000, 0x200000, 0x300000, 0x400000, 16, 0, 1)], OU_EINVAL),
+        "misaligned bf16": ([(0x100001, 0x200000, 0x300000, 0x400000, 16, 2, 0)], OU_EALIGN),
+    }
+    for name, (rows, code) in cases.items():
+        assert L.ou_plan_create(0, _segs(*rows), len(rows), ctypes.byref(h)) == code, name
+        assert not h.value, name
+        hp = _lib.ou_hparams(0.9, 0.999, 0.9999, 5.0, 1e-8, 0.0, 1e-3, 0, 1)
+        assert L.optimizer_update_32bit_multi(0, _segs(*rows), len(rows), ctypes.byref(hp), None) == code, name
+    # two segments sharing one read-only gradient buffer are allowed by validation
+    shared = [ok, (0x800000, 0x200000, 0x900000, 0xa00000, 1024, 0, 0)]
+    st = L.ou_plan_create(0, _segs(*shared), 2, ctypes.byref(h))
+    assert st not in (OU_EINVAL, OU_EALIGN, OU_EOVERLAP)
+    assert not h.value or L.ou_plan_destroy(h) is None
+    assert L.ou_plan_create(5, _segs(ok), 1, ctypes.byref(h)) == OU_EINVAL
+    assert L.ou_plan_create(0, _segs(ok), 1, None) == OU_EINVAL
+    bad_hp = _lib.ou_hparams(0.9, 0.999, 0.9999, 5.0, 1e-8, 0.0, 1e-3, 0, 0)
+    assert L.optimizer_update_32bit_multi(0, _segs(ok), 1, ctypes.byref(bad_hp), None) == OU_EINVAL
+    assert L.ou_plan_step(None, ctypes.byref(bad_hp), None) == OU_EINVAL
+    assert L.ou_plan_graph_step(None, ctypes.byref(bad_hp), None) == OU_EINVAL
+    assert L.ou_plan_describe(None, None, None, None) == OU_EINVAL
+    L.ou_plan_destroy(None)
+
+
+def test_status_strings(L):
+    for code, name in _lib.STATUS.items():
+        assert L.ou_status_string(code).decode().startswith(name)
+    assert L.ou_status_string(42).decode() == "unknown status"
+
+
+@pytest.mark.parametrize("cu", [80, 256, 304])
+def test_dispatch_with_mocked_device(L, cu):
+    """Launch selection from fabricated device properties: the grid covers
+    the tensor, blocks are whole waves, small tensors get one block, and the
+    choice depends only on the arguments (cached per device, not per process)."""
+    out = (ctypes.c_int64 * 4)()
+    for n in (1, 2, 31, 64, 255, 256, 1023, 1024, 1025, 4095, 4096, 4097, 65539, 1 << 20,
+              (1 << 28) + 3, 1 << 30):
+        for dtype in (0, 1, 2):
+            for aligned in (0, 1):
+                assert L.ou__select_single(cu, 0, dtype, n, aligned, out) == 0
+                block, epl, unroll, grid = list(out)
+                assert block % 64 == 0 and 64 <= block <= 1024
+                assert epl in (4, 8) and unroll in (1, 2, 4)
+                units = -(-n // epl) if aligned else n
+                assert grid * block * (unroll if aligned else 1) >= units or grid * block * unroll >= units
+                if units <= 1024:
+                    assert grid * block >= units and grid <= 16
+                again = (ctypes.c_int64 * 4)()
+                L.ou__select_single(cu, 0, dtype, n, aligned, again)
+                assert list(again) == list(out)
+
+
+def test_step_scalars_match_oracle_bitwise(L):
+    """The library's host-side per-step scalars equal the oracle's, bit for
+    bit (both compute bc = fl32(1 - fl64(beta^t)), d = fl32(1 - fl64(lr wd))
+    and 1 - beta in binary32, independently)."""
+    orc = O.load()
+    out = (ctypes.c_float * 12)()
+    rng = np.random.default_rng(0)
+    betas = [0.9, 0.999, 0.9999, 0.5, 0.0, 0.875, 1 - 2 ** -10, 0.95, 0.99]
+    for _ in range(300):
+        b1, b2, b3 = (float(rng.choice(betas)) for _ in range(3))
+        lr = float(10 ** rng.uniform(-6, 0))
+        wd = float(rng.choice([0.0, 0.01, 0.1, 1e-4]))
+        step = int(rng.choice([1, 2, 3, 10, 100, 1000, 12345, 10 ** 6]))
+        hp = _lib.ou_hparams(b1, b2, b3, 5.0, 1e-8, wd, lr, 0, step)
+        assert L.ou__step_scalars(ctypes.byref(hp), out) == 0
+        ref = orc.step_scalars(O.HParams(lr=lr, beta1=b1, beta2=b2, beta3=b3, weight_decay=wd), step)
+        lib_vals = dict(zip(["omb1", "omb2", "omb3", "bc1", "bc2", "decay"],
+                            [out[3], out[4], out[5], out[9], out[10], out[11]]))
+        for k, v in lib_vals.items():
+            assert np.float32(v).tobytes() == np.float32(ref[k]).tobytes(), (k, v, ref[k], b1, b2, step)
+
+
+def test_missing_library_fails_loudly(tmp_path):
+    with pytest.raises(ImportError):
+        _lib.load(str(tmp_path / "liboptimizer_update.so"))
+
+
+def test_product_path_never_touches_the_oracle():
+    """The package and the benchmark's timed path do not import or load the
+    oracle; only the benchmark's cpu_baseline leg does."""
+    pkg = os.path.join(ROOT, "optimizer_update_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".hpp", ".h", ".cpp")):
+                text = open(os.path.join(dirpath, f)).read()
+                assert not re.search(r"import oracle|from oracle|liboracle|oracle\.c\b|oracle_update",
+                                     text), os.path.join(dirpath, f)
+    bench = open(os.path.join(ROOT, "bench.py")).read()
+    imports = re.findall(r"^\s*import oracle.*$|^\s*from oracle.*$", bench, flags=re.M)
+    assert len(imports) == 1
+    body = bench[bench.index("def cpu_baseline"):]
+    assert "import oracle" in body.split("\ndef ")[0]
+
+
+def test_binding_rejects_host_tensors():
+    import torch
+
+    import optimizer_update_amd as ou
+    p = torch.zeros(8)
+    with pytest.raises(ValueError):
+        ou.optimizer_update_32bit("adam", p, p.clone(), p.clone(), p.clone(), step=1, lr=1e-3)
