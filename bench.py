@@ -10,8 +10,8 @@ Also measured (same JSON line): the other kinds and storages at 2^28 and
 fp32 Adam at 2^30; a plain device copy as the achievable-bandwidth
 reference; the model-like collection (505 bf16 tensors, AdamW) as an eager
 per-tensor loop, one plan launch and graph replay, its small-tensor subset,
-and the launch floor (a 1-element update); the CPU oracle on a bounded
-sample of the headline workload.
+and the launch floor (a 1-element update); the CPU oracle on the headline
+workload for a bounded number of steps.
 
 Timing: HIP events on the stream the kernels run on, W untimed warmups, then
 K timed steps between device synchronisations.  Secondary cases report the
@@ -262,16 +262,16 @@ def bench_collection(torch, ou, W, dev, time_rounds):
 
 
 def cpu_baseline(torch, W, dev):
-    """The CPU oracle on a bounded sample of the headline workload (2^25
-    elements of fp32 Adam drawn with the same recipe, 3 steps), all host
-    cores."""
+    """The CPU oracle on a bounded sample of the headline workload: the same
+    2^28-element fp32 Adam inputs (same generator and seed), 10 steps, on
+    all host cores (about 10 s of single-core work)."""
     import numpy as np
 
     import oracle as O
 
     orc = O.load()
     cores = len(os.sched_getaffinity(0))
-    n = 1 << 25
+    n = 1 << 28
     gen = torch.Generator(device=dev)
     gen.manual_seed(0)
     p = torch.empty(n, device=dev).uniform_(-1.0, 1.0, generator=gen).cpu().numpy()
@@ -279,15 +279,15 @@ def cpu_baseline(torch, W, dev):
     s1 = np.zeros(n, np.float32)
     s2 = np.zeros(n, np.float32)
     hp = O.HParams(lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.0)
-    steps = 3
+    steps = 10
     t0 = time.perf_counter()
     for t in range(1, steps + 1):
         orc.update_f32(O.ADAM, O.F32, p, g, s1, s2, hp, t, nthreads=cores)
     dt = time.perf_counter() - t0
     gbs = W.bytes_per_element("adam", "fp32") * n * steps / dt / 1e9
     return {"value": round(gbs, 2), "unit": "GB/s", "cores": cores, "kind": "oracle",
-            "sample": f"fp32 Adam on 2^25 elements drawn with the headline's recipe (params U(-1,1), "
-                      f"grads N(0,(1e-3)^2)), {steps} steps, {dt:.2f} s wall, OpenMP static schedule",
+            "sample": f"the headline workload itself (fp32 Adam, 2^28 elements, same seed), {steps} "
+                      f"steps, {dt:.2f} s wall on {cores} threads, OpenMP static schedule",
             "elements_per_s": round(n * steps / dt, 0)}
 
 
