@@ -83,11 +83,11 @@ def load(path: str = LIBRARY) -> ctypes.CDLL:
     lib.ou_last_error.argtypes = []
     lib.ou_last_error.restype = ctypes.c_char_p
     # test hooks (not in the public header)
-    lib.ou__select_single.argtypes = [i32, i32, i32, i64, i32, ctypes.POINTER(i64)]
+    lib.ou__select_single.argtypes = [i32, i32, i32, i32, i32, i64, i32, ctypes.POINTER(i64)]
     lib.ou__select_single.restype = i32
-    lib.ou__force_single.argtypes = [i32, i32, i32, i64, i32]
+    lib.ou__force_single.argtypes = [i32, i32, i32, i64, i32, i32]
     lib.ou__force_single.restype = None
-    lib.ou__force_multi.argtypes = [i32, i32, i32, i32]
+    lib.ou__force_multi.argtypes = [i32, i32, i32, i32, i32]
     lib.ou__force_multi.restype = None
     lib.ou__step_scalars.argtypes = [ctypes.POINTER(ou_hparams), ctypes.POINTER(f32)]
     lib.ou__step_scalars.restype = i32

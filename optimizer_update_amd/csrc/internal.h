@@ -34,6 +34,7 @@ struct SingleLaunch {
     int epl;      // elements per lane per vector group: 4 or 8
     int unroll;   // vector groups in flight per lane: 1, 2 or 4
     int64_t grid; // blocks
+    int lds;      // dynamic LDS bytes reserved (not used by the kernel) to cap blocks per CU
 };
 
 // Launch shape of the multi-tensor kernel.
@@ -41,7 +42,21 @@ struct MultiLaunch {
     int waves;    // waves per block: 1, 2, 4 or 8
     int epl;      // 4 or 8
     int unroll;   // 1, 2 or 4
+    int lds;      // dynamic LDS bytes reserved to cap blocks per CU (0 = no cap)
 };
+
+// Device facts the launch selection depends on (cached per device id).
+struct DeviceProps {
+    int cu_count = 0;
+    int lds_per_cu = 0;      // bytes of LDS per compute unit
+    int lds_per_block = 0;   // largest LDS allocation of one block
+    bool gfx950 = false;
+    char arch[64] = {0};
+};
+
+// Dynamic LDS that limits a kernel with no LDS of its own to at most
+// `blocks` resident blocks per CU (0 when the device does not say).
+int lds_cap(const DeviceProps& d, int blocks);
 
 // Kernel entry for the single-tensor streaming kernel (nullptr if the
 // combination is not instantiated).

@@ -16,17 +16,19 @@
 extern "C" {
 #endif
 
-// Launch shape the single-tensor entry would pick for a device with
-// cu_count compute units: out = {block, epl, unroll, grid}.
-int ou__select_single(int cu_count, int kind, int dtype, int64_t n, int aligned, int64_t out[4]);
+// Launch shape the single-tensor entry would pick for a device with the
+// given CU count and LDS sizes: out = {block, epl, unroll, grid, lds}.
+int ou__select_single(int cu_count, int lds_per_cu, int lds_per_block, int kind, int dtype, int64_t n,
+                      int aligned, int64_t out[5]);
 
-// Force the single-tensor launch shape (0 = no forcing for that field);
-// scalar_only != 0 forces the one-element-per-lane path.  Process-wide.
-void ou__force_single(int block, int epl, int unroll, int64_t grid, int scalar_only);
+// Force the single-tensor launch shape (0 = no forcing for that field;
+// lds -1 = no occupancy cap); scalar_only != 0 forces the
+// one-element-per-lane path.  Process-wide.
+void ou__force_single(int block, int epl, int unroll, int64_t grid, int scalar_only, int lds);
 
 // Force the multi-tensor shape used by plans created afterwards
-// (0 = no forcing).  chunk must be a multiple of 64 * epl.
-void ou__force_multi(int waves, int epl, int unroll, int chunk);
+// (0 = no forcing; lds -1 = no cap).  chunk must be a multiple of 64 * epl * unroll.
+void ou__force_multi(int waves, int epl, int unroll, int chunk, int lds);
 
 // The per-step scalars: beta1..3, 1-beta1..3, alpha, eps, lr, bc1, bc2, decay.
 int ou__step_scalars(const ou_hparams* hp, float out[12]);

@@ -150,26 +150,35 @@ def test_status_strings(L):
     assert L.ou_status_string(42).decode() == "unknown status"
 
 
-@pytest.mark.parametrize("cu", [80, 256, 304])
-def test_dispatch_with_mocked_device(L, cu):
+@pytest.mark.parametrize("cu,lds_cu,lds_blk", [(80, 65536, 65536), (256, 163840, 163840),
+                                                (304, 65536, 65536), (256, 0, 0)])
+def test_dispatch_with_mocked_device(L, cu, lds_cu, lds_blk):
     """Launch selection from fabricated device properties: the grid covers
-    the tensor, blocks are whole waves, small tensors get one block, and the
-    choice depends only on the arguments (cached per device, not per process)."""
-    out = (ctypes.c_int64 * 4)()
+    the tensor, blocks are whole waves, small tensors get one block, the
+    occupancy cap reserves LDS so that exactly two blocks fit per CU (or none
+    when the device reports no LDS size), and the choice depends only on the
+    arguments."""
+    out = (ctypes.c_int64 * 5)()
     for n in (1, 2, 31, 64, 255, 256, 1023, 1024, 1025, 4095, 4096, 4097, 65539, 1 << 20,
               (1 << 28) + 3, 1 << 30):
         for dtype in (0, 1, 2):
             for aligned in (0, 1):
-                assert L.ou__select_single(cu, 0, dtype, n, aligned, out) == 0
-                block, epl, unroll, grid = list(out)
+                assert L.ou__select_single(cu, lds_cu, lds_blk, 0, dtype, n, aligned, out) == 0
+                block, epl, unroll, grid, lds = list(out)
                 assert block % 64 == 0 and 64 <= block <= 1024
                 assert epl in (4, 8) and unroll in (1, 2, 4)
                 units = -(-n // epl) if aligned else n
-                assert grid * block * (unroll if aligned else 1) >= units or grid * block * unroll >= units
+                # every lane's first pass covers the tensor (the kernels loop
+                # grid-stride for the rest, so this is about efficiency)
+                assert grid * block * unroll >= units
                 if units <= 1024:
-                    assert grid * block >= units and grid <= 16
-                again = (ctypes.c_int64 * 4)()
-                L.ou__select_single(cu, 0, dtype, n, aligned, again)
+                    assert grid * block >= units and grid <= 16 and lds == 0
+                if lds:
+                    assert 2 * lds <= lds_cu < 3 * lds and lds <= lds_blk and grid >= 8 * cu
+                elif lds_cu and grid >= 8 * cu:
+                    raise AssertionError("large grids get the occupancy cap")
+                again = (ctypes.c_int64 * 5)()
+                L.ou__select_single(cu, lds_cu, lds_blk, 0, dtype, n, aligned, again)
                 assert list(again) == list(out)
 
 

@@ -174,7 +174,7 @@ def _run_single(L, kind, storage, p0, g_host, T, hp, force=None, offset=0):
             st = H.raw_update(L, kind, storage, P, G, S1, S2, n, hp, t, H.stream_handle())
             assert st == 0, H.last_error(L)
     finally:
-        L.ou__force_single(0, 0, 0, 0, 0)
+        L.ou__force_single(0, 0, 0, 0, 0, 0)
     torch.cuda.synchronize()
     return W.from_torch(P), W.from_torch(S1), W.from_torch(S2), W.from_torch(G)
 
@@ -188,8 +188,10 @@ def test_launch_variants_bitwise(orc, L, kind, storage):
     parameters and states, equal to the oracle."""
     T = 3
     hp = _hp(kind, 0.01, True)
-    variants = [(64, 4, 1, 0, 0), (256, 8, 2, 0, 0), (1024, 4, 4, 0, 0), (128, 8, 4, 3, 0),
-                (512, 4, 2, 1, 0), (64, 8, 1, 7, 0), (256, 4, 2, 0, 1), (1024, 8, 1, 2, 1)]
+    variants = [(64, 4, 1, 0, 0, 0), (256, 8, 2, 0, 0, 0), (1024, 4, 4, 0, 0, 0),
+                (128, 8, 4, 3, 0, 0), (512, 4, 2, 1, 0, 0), (64, 8, 1, 7, 0, 0),
+                (256, 4, 2, 0, 1, 0), (1024, 8, 1, 2, 1, 0), (256, 4, 2, 0, 0, -1),
+                (256, 4, 2, 0, 0, 65536), (512, 4, 1, 0, 0, 98304)]
     for n in VARIANT_N:
         gen = W.rng(0, 6, n)
         p0 = W.params(n, storage, gen)
@@ -225,7 +227,8 @@ def test_launch_variants_bitwise(orc, L, kind, storage):
         p0 = W.params(n, storage, gen)
         g_host = W.cast_storage(np.where(gen.random(n) < 0.1, 0.0, gen.standard_normal(n)), storage)
         singles[n] = (p0, g_host, _run_single(L, kind, storage, p0, g_host, T, hp))
-    for shape in ((0, 0, 0, 0), (1, 4, 1, 256 * 4 * 2), (8, 8, 4, 512 * 8), (2, 4, 2, 4096)):
+    for shape in ((0, 0, 0, 0, 0), (1, 4, 1, 256 * 4 * 2, 0), (8, 8, 4, 512 * 8, 0),
+                  (2, 4, 2, 4096, 65536), (4, 4, 2, 1024, -1)):
         for order in (sizes, sizes[::-1]):
             for graph in (False, True):
                 L.ou__force_multi(*shape)
@@ -237,7 +240,7 @@ def test_launch_variants_bitwise(orc, L, kind, storage):
                                      torch.zeros(k * n, device="cuda"), torch.zeros(n, device="cuda")))
                     plan = Plan(kind, segs)
                 finally:
-                    L.ou__force_multi(0, 0, 0, 0)
+                    L.ou__force_multi(0, 0, 0, 0, 0)
                 php = H.pkg_hp(hp)
                 for t in range(1, T + 1):
                     (plan.graph_step if graph else plan.step)(php, t)
