@@ -32,7 +32,9 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 METRIC = "optimizer-update GB/s (% of HBM peak) on 256M elems; µs per mixed small-tensor step"
-KERNEL_SOURCES = ("optimizer_update_amd/csrc/kernels.hip", "optimizer_update_amd/csrc/elem.hpp")
+# the kernels and the launch selection that shapes them
+KERNEL_SOURCES = ("optimizer_update_amd/csrc/kernels.hip", "optimizer_update_amd/csrc/elem.hpp",
+                  "optimizer_update_amd/csrc/host.hip")
 
 
 def kernel_sha() -> str:

@@ -58,10 +58,38 @@ def state_sizes(kind, n: int) -> tuple[int, int]:
     return (2 * n if _kind(kind) == _lib.OU_ADEMAMIX else n), n
 
 
+def _raw_stream(index: int) -> int:
+    """Handle of the current stream of device `index` (torch's own accessor,
+    falling back to the public one)."""
+    get = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+    if get is not None:
+        return get(index)
+    return torch.cuda.current_stream(index).cuda_stream
+
+
 def _stream(t: torch.Tensor, stream) -> int:
     if stream is None:
-        stream = torch.cuda.current_stream(t.device)
+        return _raw_stream(t.device.index)
     return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+class _on_device:
+    """Make `device` current for a call, only if it is not already."""
+
+    __slots__ = ("index", "prev")
+
+    def __init__(self, device: torch.device):
+        self.index = device.index
+
+    def __enter__(self):
+        self.prev = torch.cuda.current_device()
+        if self.prev != self.index:
+            torch.cuda.set_device(self.index)
+
+    def __exit__(self, *exc):
+        if self.prev != self.index:
+            torch.cuda.set_device(self.prev)
+        return False
 
 
 def _tensor_args(kind: int, param, grad, state1, state2) -> tuple[int, int]:
@@ -70,18 +98,20 @@ def _tensor_args(kind: int, param, grad, state1, state2) -> tuple[int, int]:
             raise ValueError(f"{name} must be a tensor on a HIP device")
         if not t.is_contiguous():
             raise ValueError(f"{name} must be contiguous")
-    if param.dtype not in DTYPES or grad.dtype != param.dtype:
+    dt = DTYPES.get(param.dtype)
+    if dt is None or grad.dtype != param.dtype:
         raise ValueError("param and grad must share one of float32/float16/bfloat16")
     if state1.dtype != torch.float32 or state2.dtype != torch.float32:
         raise ValueError("states must be float32")
     n = param.numel()
-    s1, s2 = state_sizes(kind, n)
-    if grad.numel() != n or state1.numel() != s1 or state2.numel() != s2:
+    s1 = 2 * n if kind == _lib.OU_ADEMAMIX else n
+    if grad.numel() != n or state1.numel() != s1 or state2.numel() != n:
         raise ValueError(f"sizes: param {n}, grad {grad.numel()}, state1 {state1.numel()} "
-                         f"(want {s1}), state2 {state2.numel()} (want {s2})")
-    if len({t.device for t in (param, grad, state1, state2)}) != 1:
+                         f"(want {s1}), state2 {state2.numel()} (want {n})")
+    dev = param.device
+    if grad.device != dev or state1.device != dev or state2.device != dev:
         raise ValueError("all tensors must be on one device")
-    return n, DTYPES[param.dtype]
+    return n, dt
 
 
 def optimizer_update_32bit(kind, param: torch.Tensor, grad: torch.Tensor, state1: torch.Tensor,
@@ -93,7 +123,7 @@ def optimizer_update_32bit(kind, param: torch.Tensor, grad: torch.Tensor, state1
     k = _kind(kind)
     n, dt = _tensor_args(k, param, grad, state1, state2)
     lib = load()
-    with torch.cuda.device(param.device):
+    with _on_device(param.device):
         st = lib.optimizer_update_32bit(k, dt, param.data_ptr(), grad.data_ptr(),
                                         state1.data_ptr(), state2.data_ptr(), n, beta1, beta2,
                                         beta3, alpha, eps, weight_decay, int(step), lr,
@@ -120,7 +150,7 @@ def optimizer_update_32bit_multi(kind, segments, hp: HParams, step: int, stream=
     lib = load()
     c = hp.c(step)
     dev = segments[0][0].device
-    with torch.cuda.device(dev):
+    with _on_device(dev):
         st = lib.optimizer_update_32bit_multi(k, arr, len(segments), ctypes.byref(c),
                                               _stream(segments[0][0], stream))
     check(st, lib)
@@ -135,23 +165,24 @@ class Plan:
     def __init__(self, kind, segments):
         self.kind = _kind(kind)
         self._tensors = [tuple(s) for s in segments]
-        self.device = self._tensors[0][0].device if self._tensors else torch.device("cuda")
+        self.device = (self._tensors[0][0].device if self._tensors
+                       else torch.device("cuda", torch.cuda.current_device()))
         arr = _segments(self.kind, self._tensors)
         self._lib = load()
         h = ctypes.c_void_p()
-        with torch.cuda.device(self.device):
+        with _on_device(self.device):
             check(self._lib.ou_plan_create(self.kind, arr, len(self._tensors), ctypes.byref(h)),
                   self._lib)
         self._h = h
 
     def step(self, hp: HParams, step: int, stream=None) -> None:
         c = hp.c(step)
-        with torch.cuda.device(self.device):
+        with _on_device(self.device):
             check(self._lib.ou_plan_step(self._h, ctypes.byref(c), self._stream(stream)), self._lib)
 
     def graph_step(self, hp: HParams, step: int, stream=None) -> None:
         c = hp.c(step)
-        with torch.cuda.device(self.device):
+        with _on_device(self.device):
             check(self._lib.ou_plan_graph_step(self._h, ctypes.byref(c), self._stream(stream)),
                   self._lib)
 
@@ -165,7 +196,7 @@ class Plan:
 
     def _stream(self, stream) -> int:
         if stream is None:
-            return torch.cuda.current_stream(self.device).cuda_stream
+            return _raw_stream(self.device.index)
         return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
 
     def close(self) -> None:

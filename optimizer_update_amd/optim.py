@@ -16,7 +16,8 @@ from __future__ import annotations
 
 import torch
 
-from . import HParams, Plan, optimizer_update_32bit, state_sizes
+from . import (DTYPES, HParams, Plan, _kind, _on_device, _raw_stream, _tensor_args, check, load,
+               state_sizes)
 
 
 class _Collection:
@@ -41,6 +42,7 @@ class _Collection:
             self.state1.append(torch.zeros(n1, dtype=torch.float32, device=p.device))
             self.state2.append(torch.zeros(n2, dtype=torch.float32, device=p.device))
         self.step_count = 0
+        self._direct = None
         self.plan = Plan(self.kind, list(zip(self.params, self.grads, self.state1, self.state2)))
 
     def segments(self):
@@ -57,14 +59,27 @@ class _Collection:
 
     @torch.no_grad()
     def step_per_tensor(self, stream=None) -> None:
-        """The same step as one direct call per tensor."""
+        """The same step as one direct call per tensor (the tensors were
+        checked when the optimizer was built; only the step changes)."""
         self.step_count += 1
         h = self.hp
-        for p, g, s1, s2 in self.segments():
-            optimizer_update_32bit(self.kind, p, g, s1, s2, step=self.step_count, lr=h.lr,
-                                   beta1=h.beta1, beta2=h.beta2, beta3=h.beta3, alpha=h.alpha,
-                                   eps=h.eps, weight_decay=h.weight_decay,
-                                   skip_zeros=h.skip_zeros, stream=stream)
+        if self._direct is None:
+            for p, g, s1, s2 in self.segments():   # full checks once
+                _tensor_args(_kind(self.kind), p, g, s1, s2)
+            self._direct = [(_kind(self.kind), DTYPES[p.dtype], p.data_ptr(), g.data_ptr(),
+                             s1.data_ptr(), s2.data_ptr(), p.numel())
+                            for p, g, s1, s2 in self.segments()]
+        lib = load()
+        sh = (_raw_stream(self.params[0].device.index) if stream is None
+              else (stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)))
+        tail = (h.beta1, h.beta2, h.beta3, h.alpha, h.eps, h.weight_decay, self.step_count, h.lr,
+                int(bool(h.skip_zeros)), sh)
+        fn = lib.optimizer_update_32bit
+        with _on_device(self.params[0].device):
+            for args in self._direct:
+                st = fn(*args, *tail)
+                if st:
+                    check(st, lib)
 
     def state_dict(self) -> dict:
         return {"step": self.step_count,
