@@ -96,6 +96,14 @@ class Oracle:
         lib.oracle_update_f64.argtypes = [ci, vp, vp, vp, vp, i64,
                                           f64, f64, f64, f64, f64, f64, i64, f64, ci]
         lib.oracle_update_f64.restype = ci
+        lib.oracle_update_f32_clip.argtypes = [ci, ci, vp, vp, vp, vp, i64, f32, f32, f32, f32,
+                                               f32, f32, i64, f32, ci, f32,
+                                               ctypes.POINTER(ctypes.c_float)]
+        lib.oracle_update_f32_clip.restype = ci
+        lib.oracle_update_f64_clip.argtypes = [ci, vp, vp, vp, vp, i64, f64, f64, f64, f64, f64,
+                                               f64, i64, f64, ci, f64,
+                                               ctypes.POINTER(ctypes.c_double)]
+        lib.oracle_update_f64_clip.restype = ci
         lib.oracle_step_scalars.argtypes = [f32, f32, f32, f32, f32, i64,
                                             ctypes.POINTER(_Scalars32)]
         lib.oracle_step_scalars.restype = None
@@ -164,6 +172,39 @@ class Oracle:
             hp.lr, int(bool(hp.skip_zeros)))
         if rc != 0:
             raise ValueError(f"oracle_update_f64 rejected kind={kind}")
+
+    def update_f32_clip(self, kind: int, dtype: int, param: np.ndarray, grad: np.ndarray,
+                        state1: np.ndarray, state2: np.ndarray, hp: HParams, step: int,
+                        max_unorm: float) -> float:
+        """One clipped step, in place (see ``oracle_update_f32_clip``);
+        returns the clip factor s."""
+        n = param.size
+        sdt = np.float32 if dtype == F32 else np.uint16
+        assert param.dtype == sdt and grad.dtype == sdt and grad.size == n
+        assert state1.size == (2 * n if kind == ADEMAMIX else n) and state2.size == n
+        out = ctypes.c_float()
+        rc = self._lib.oracle_update_f32_clip(
+            kind, dtype, _ptr(param), _ptr(grad), _ptr(state1), _ptr(state2), n,
+            hp.beta1, hp.beta2, hp.beta3, hp.alpha, hp.eps, hp.weight_decay, step, hp.lr,
+            int(bool(hp.skip_zeros)), max_unorm, ctypes.byref(out))
+        if rc != 0:
+            raise ValueError(f"oracle_update_f32_clip failed ({rc})")
+        return out.value
+
+    def update_f64_clip(self, kind: int, param: np.ndarray, grad: np.ndarray, state1: np.ndarray,
+                        state2: np.ndarray, hp: HParams, step: int, max_unorm: float) -> float:
+        """One clipped binary64 step, in place; returns the clip factor s."""
+        n = param.size
+        for a in (param, grad, state1, state2):
+            assert a.dtype == np.float64 and a.flags.c_contiguous
+        out = ctypes.c_double()
+        rc = self._lib.oracle_update_f64_clip(
+            kind, _ptr(param), _ptr(grad), _ptr(state1), _ptr(state2), n,
+            hp.beta1, hp.beta2, hp.beta3, hp.alpha, hp.eps, hp.weight_decay, step, hp.lr,
+            int(bool(hp.skip_zeros)), max_unorm, ctypes.byref(out))
+        if rc != 0:
+            raise ValueError(f"oracle_update_f64_clip failed ({rc})")
+        return out.value
 
     def max_threads(self) -> int:
         return self._lib.oracle_max_threads()

@@ -31,12 +31,17 @@
  * 754 / bfloat16 encodings: round to nearest, ties to even; overflow goes to
  * infinity; subnormals are kept; a NaN stays a quiet NaN (payload not kept).
  *
+ * oracle_update_f32_clip / oracle_update_f64_clip add update-norm clipping
+ * (the page's "max_unorm"; it names the option only, so the clip rule is
+ * stated at the function).
+ *
  * ORACLE_PLANT (compile-time, default 0) plants one known mistake so that
  * the test suite can show its pins catch it.  It is never set in a normal
  * build.
  */
 #include <math.h>
 #include <stdint.h>
+#include <stdlib.h>
 #include <string.h>
 #ifdef _OPENMP
 #include <omp.h>
@@ -186,12 +191,12 @@ void oracle_step_scalars(float beta1, float beta2, float beta3, float lr,
 
 /* ------------------------------------------------------ fp32 instantiation */
 
-/* One element, binary32.  m, v: first and second moment; m2: slow EMA
- * (AdEMAMix only).  Returns the new parameter value before rounding to the
- * storage type. */
-static float element_f32(int kind, float p, float g, float* m, float* v, float* m2,
-                         const oracle_scalars32* s, float beta1, float beta2, float beta3,
-                         float alpha, float eps, float lr)
+/* The moments and the update direction of one element, binary32.  m, v:
+ * first and second moment; m2: slow EMA (AdEMAMix only).  Updates the
+ * moments and returns the direction u (the parameter moves by lr * u). */
+static float direction_f32(int kind, float g, float* m, float* v, float* m2,
+                           const oracle_scalars32* s, float beta1, float beta2, float beta3,
+                           float alpha, float eps)
 {
     /* first and second moment (Kingma & Ba, Algorithm 1) */
     float mn = beta1 * (*m) + s->omb1 * g;
@@ -227,17 +232,31 @@ static float element_f32(int kind, float p, float g, float* m, float* v, float* 
 #endif
     }
     float upd = num / den;
-
-    /* decoupled weight decay on the old parameter (Loshchilov & Hutter, Algorithm 2) */
-#if ORACLE_PLANT == 3
-    float pn = (p - lr * upd) * s->decay;           /* planted: decay after the update */
-#else
-    float pn = p * s->decay - lr * upd;
-#endif
     *m = mn;
     *v = vn;
     if (kind == ORACLE_ADEMAMIX) *m2 = m2n;
-    return pn;
+    return upd;
+}
+
+/* Decoupled weight decay of the old parameter and the step along u
+ * (Loshchilov & Hutter, Algorithm 2).  Returns the new parameter before
+ * rounding to the storage type. */
+static float param_f32(float p, float upd, float decay, float lr)
+{
+#if ORACLE_PLANT == 3
+    return (p - lr * upd) * decay;                  /* planted: decay after the update */
+#else
+    return p * decay - lr * upd;
+#endif
+}
+
+/* One element, binary32: direction, then parameter. */
+static float element_f32(int kind, float p, float g, float* m, float* v, float* m2,
+                         const oracle_scalars32* s, float beta1, float beta2, float beta3,
+                         float alpha, float eps, float lr)
+{
+    float upd = direction_f32(kind, g, m, v, m2, s, beta1, beta2, beta3, alpha, eps);
+    return param_f32(p, upd, s->decay, lr);
 }
 
 /* One optimizer step over n elements, in place.
@@ -369,6 +388,131 @@ int oracle_update_f64(int kind, double* param, const double* grad, double* state
         state2[i] = v;
         if (kind == ORACLE_ADEMAMIX) state1[slow] = m2;
     }
+    return 0;
+}
+
+/* ------------------------------------------------- update-norm clipping */
+
+/* Clip factor of update-norm clipping: s = min(1, max_unorm * ||p|| / ||u||)
+ * from the squared norms (binary64); 1 when max_unorm <= 0 or ||u|| = 0. */
+static double clip_factor(double max_unorm, double p_sq, double u_sq)
+{
+    if (!(max_unorm > 0.0) || !(u_sq > 0.0))
+        return 1.0;
+#if ORACLE_PLANT == 16
+    double r = max_unorm * sqrt(p_sq) / u_sq;       /* planted: ||u||^2 for ||u|| */
+#else
+    double r = max_unorm * sqrt(p_sq) / sqrt(u_sq);
+#endif
+#if ORACLE_PLANT == 17
+    return r;                                       /* planted: clips when below the bound */
+#else
+    return r < 1.0 ? r : 1.0;
+#endif
+}
+
+/* One step with update-norm clipping.  The update direction u of every
+ * element (the value that oracle_update_f32 multiplies by lr) is scaled,
+ * for the whole tensor, by s = min(1, max_unorm * ||p|| / ||u||): p is the
+ * parameter before the step, both 2-norms run over all n elements, and an
+ * element left alone by skip_zeros contributes u = 0.  The squared norms
+ * are summed in binary64 in index order, s is rounded to binary32, and each
+ * parameter becomes p*d - fl32(lr*s)*u.  The moments are those of the
+ * unclipped step.  max_unorm = 0 gives oracle_update_f32 exactly.
+ * *scale_out (if not NULL) receives s.  Returns 0, -1 on an invalid kind or
+ * dtype, -2 if out of memory. */
+int oracle_update_f32_clip(int kind, int dtype, void* param, const void* grad,
+                           float* state1, float* state2, int64_t n,
+                           float beta1, float beta2, float beta3, float alpha, float eps,
+                           float weight_decay, int64_t step, float lr, int skip_zeros,
+                           float max_unorm, float* scale_out)
+{
+    if ((kind != ORACLE_ADAM && kind != ORACLE_ADEMAMIX) ||
+        (dtype != ORACLE_F32 && dtype != ORACLE_F16 && dtype != ORACLE_BF16))
+        return -1;
+    oracle_scalars32 s;
+    oracle_step_scalars(beta1, beta2, beta3, lr, weight_decay, step, &s);
+    float* u = (float*)malloc((size_t)(n > 0 ? n : 1) * sizeof(float));
+    unsigned char* skip = (unsigned char*)malloc((size_t)(n > 0 ? n : 1));
+    if (!u || !skip) { free(u); free(skip); return -2; }
+    double p_sq = 0.0, u_sq = 0.0;
+    for (int64_t i = 0; i < n; i++) {
+        float p = load_storage(param, dtype, i);
+        p_sq += (double)p * (double)p;
+        float g = load_storage(grad, dtype, i);
+        skip[i] = (unsigned char)(skip_zeros && g == 0.0f);
+        u[i] = 0.0f;
+        if (skip[i]) continue;
+        float* m2 = (kind == ORACLE_ADEMAMIX) ? &state1[n + i] : NULL;
+        u[i] = direction_f32(kind, g, &state1[i], &state2[i], m2, &s, beta1, beta2, beta3,
+                             alpha, eps);
+        u_sq += (double)u[i] * (double)u[i];
+    }
+#if ORACLE_PLANT == 15
+    p_sq = 0.0;                                     /* planted: norm of the new parameter */
+    for (int64_t i = 0; i < n; i++) {
+        float pn = param_f32(load_storage(param, dtype, i), u[i], s.decay, lr);
+        p_sq += (double)pn * (double)pn;
+    }
+#endif
+    float scale = (float)clip_factor((double)max_unorm, p_sq, u_sq);
+    float lr_eff = lr * scale;
+    for (int64_t i = 0; i < n; i++) {
+        if (skip[i]) continue;
+        store_storage(param, dtype, i, param_f32(load_storage(param, dtype, i), u[i], s.decay, lr_eff));
+    }
+    if (scale_out) *scale_out = scale;
+    free(u);
+    free(skip);
+    return 0;
+}
+
+/* The clipped step in binary64 (s unrounded); fp64 arrays only.  u is
+ * taken from an unclipped step with lr = 1 and no decay (as p_old - p_new;
+ * that difference rounds at the level of ulp(p), far below the tolerance of
+ * the closed forms this instantiation is checked against). */
+int oracle_update_f64_clip(int kind, double* param, const double* grad, double* state1,
+                           double* state2, int64_t n, double beta1, double beta2, double beta3,
+                           double alpha, double eps, double weight_decay, int64_t step,
+                           double lr, int skip_zeros, double max_unorm, double* scale_out)
+{
+    if (kind != ORACLE_ADAM && kind != ORACLE_ADEMAMIX)
+        return -1;
+    double* p_new = (double*)malloc((size_t)(n > 0 ? n : 1) * sizeof(double));
+    double* p_old = (double*)malloc((size_t)(n > 0 ? n : 1) * sizeof(double));
+    if (!p_new || !p_old) { free(p_new); free(p_old); return -2; }
+    /* the unclipped step with lr = 1 and no decay gives -u in p_new - p_old */
+    double p_sq = 0.0;
+    for (int64_t i = 0; i < n; i++) {
+        p_old[i] = param[i];
+        p_new[i] = param[i];
+        p_sq += param[i] * param[i];
+    }
+    int rc = oracle_update_f64(kind, p_new, grad, state1, state2, n, beta1, beta2, beta3,
+                               alpha, eps, 0.0, step, 1.0, skip_zeros);
+    if (rc) { free(p_new); free(p_old); return rc; }
+    double u_sq = 0.0;
+    for (int64_t i = 0; i < n; i++) {
+        double u = p_old[i] - p_new[i];
+        u_sq += u * u;
+    }
+#if ORACLE_PLANT == 15
+    p_sq = 0.0;
+    for (int64_t i = 0; i < n; i++) {
+        double pn = p_old[i] * (1.0 - lr * weight_decay) - lr * (p_old[i] - p_new[i]);
+        p_sq += pn * pn;
+    }
+#endif
+    double scale = clip_factor(max_unorm, p_sq, u_sq);
+    double decay = 1.0 - lr * weight_decay;
+    for (int64_t i = 0; i < n; i++) {
+        double u = p_old[i] - p_new[i];
+        if (skip_zeros && grad[i] == 0.0) continue;
+        param[i] = p_old[i] * decay - (lr * scale) * u;
+    }
+    if (scale_out) *scale_out = scale;
+    free(p_new);
+    free(p_old);
     return 0;
 }
 

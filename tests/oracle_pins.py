@@ -420,7 +420,91 @@ def _emulate_and_compare(orc, kind_name, kind, sname, dtype, p, gsteps, hp, T):
                 assert m2[i].bits_equal(float(s1[n + i])), ("m2", ctx, float(m2[i]), s1[n + i])
 
 
+# ------------------------------------------------------ update-norm clipping
+
+def pin_clip_reduces_to_plain(orc):
+    """max_unorm = 0 (off) and a bound far above the update (s = 1) give the
+    unclipped step bitwise, for every kind and storage, skip_zeros on."""
+    n, T = 513, 4
+    gen = rng(21, 0)
+    for kind in (O.ADAM, O.ADEMAMIX):
+        for dtype, name in ((O.F32, "fp32"), (O.F16, "fp16"), (O.BF16, "bf16")):
+            p0 = cast_storage(gen.uniform(-1, 1, n).astype(np.float32), name)
+            gs = [cast_storage(np.where(gen.random(n) < 0.2, 0.0, gen.standard_normal(n)).astype(np.float32), name)
+                  for _ in range(T)]
+            hp = O.HParams(weight_decay=0.01, skip_zeros=True)
+            ref = _run_f32(orc, kind, dtype, p0, lambda t: gs[t - 1], hp, T)
+            for bound in (0.0, 1e30):
+                p = p0.copy()
+                s1 = np.zeros_like(ref[1])
+                s2 = np.zeros_like(ref[2])
+                for t in range(1, T + 1):
+                    sc = orc.update_f32_clip(kind, dtype, p, gs[t - 1], s1, s2, hp, t, bound)
+                    assert sc == 1.0, (bound, sc)
+                assert p.tobytes() == ref[0].tobytes(), (kind, name, bound)
+                assert s1.tobytes() == ref[1].tobytes() and s2.tobytes() == ref[2].tobytes()
+
+
+def pin_clip_closed_form_f64(orc):
+    """Constant gradient g and zero initial states: every step's direction is
+    u_i = g_i / (|g_i| + eps) exactly (Adam; AdEMAMix adds alpha (1 - b3^t) g_i
+    over the same denominator), so the clipped trajectory is
+        s_t = min(1, max_unorm ||p_(t-1)|| / ||u_t||),
+        p_t = d p_(t-1) - lr s_t u_t,
+    iterated here with numpy, independently of the oracle."""
+    g = np.array([1.0, -0.5, 3e-3, -2.5e-6, 7.0, 0.25, -1.5, 0.0], np.float64)
+    p0 = np.array([0.5, -0.25, 0.125, 0.9, -0.75, 0.3, 0.01, -0.6], np.float64)
+    T = 200
+    for kind in (O.ADAM, O.ADEMAMIX):
+        for wd, bound in ((0.0, 2e-3), (0.1, 5e-4), (0.0, 10.0)):
+            hp = O.HParams(lr=1e-2, beta1=0.9, beta2=0.999, beta3=0.99, alpha=5.0, eps=1e-8,
+                           weight_decay=wd)
+            p = p0.copy()
+            s1 = np.zeros((2 if kind == O.ADEMAMIX else 1) * g.size)
+            s2 = np.zeros(g.size)
+            ref = p0.copy()
+            d = 1.0 - hp.lr * wd
+            for t in range(1, T + 1):
+                sc = orc.update_f64_clip(kind, p, g, s1, s2, hp, t, bound)
+                u = g / (np.abs(g) + hp.eps)
+                if kind == O.ADEMAMIX:
+                    u = u * (1.0 + hp.alpha * (1.0 - hp.beta3 ** t))
+                s_ref = min(1.0, bound * np.linalg.norm(ref) / np.linalg.norm(u))
+                ref = ref * d - hp.lr * s_ref * u
+                assert abs(sc - s_ref) <= 1e-12 * s_ref, (kind, wd, bound, t, sc, s_ref)
+                assert np.all(np.abs(p - ref) <= 1e-12 * (np.abs(p0) + t * hp.lr)), (kind, wd, bound, t)
+            if bound < 1:
+                assert s_ref < 1.0     # the clip was active
+
+
+def pin_clip_realised_norm(orc):
+    """binary32: when the clip is active the step moves p by fl32(lr s) u,
+    whose norm is lr max_unorm ||p|| (here the step is ~1e5 times ulp(p), so
+    the rounding of p adds ~1e-5 relative), the moments equal the unclipped
+    step's bitwise, and skipped elements do not move."""
+    n = 4097
+    gen = rng(23, 0)
+    for kind in (O.ADAM, O.ADEMAMIX):
+        p0 = gen.uniform(-1, 1, n).astype(np.float32)
+        g = np.where(gen.random(n) < 0.1, 0.0, gen.standard_normal(n)).astype(np.float32)
+        hp = O.HParams(lr=0.1, weight_decay=0.0, skip_zeros=True)
+        bound = 0.1
+        p = p0.copy()
+        s1, s2 = np.zeros((2 if kind == O.ADEMAMIX else 1) * n, np.float32), np.zeros(n, np.float32)
+        sc = orc.update_f32_clip(kind, O.F32, p, g, s1, s2, hp, 1, bound)
+        assert 0.0 < sc < 1.0
+        step = (p0.astype(np.float64) - p.astype(np.float64))
+        want = hp.lr * bound * np.linalg.norm(p0.astype(np.float64))
+        assert abs(np.linalg.norm(step) - want) <= 1e-4 * want, (np.linalg.norm(step), want)
+        assert np.all(p[g == 0] == p0[g == 0])
+        pr = p0.copy()
+        r1, r2 = np.zeros_like(s1), np.zeros_like(s2)
+        orc.update_f32(kind, O.F32, pr, g, r1, r2, hp, 1)
+        assert r1.tobytes() == s1.tobytes() and r2.tobytes() == s2.tobytes()
+
+
 INDEPENDENT = [pin_closed_form_f64, pin_f32_tracks_f64, pin_first_step_by_hand,
                pin_torch_adam, pin_zero_gradient, pin_ademamix_reduces_to_adam,
-               pin_element_independence, pin_grad_unchanged, pin_conversions_sample]
+               pin_element_independence, pin_grad_unchanged, pin_conversions_sample,
+               pin_clip_reduces_to_plain, pin_clip_closed_form_f64, pin_clip_realised_norm]
 ALL = INDEPENDENT + [pin_exact_emulation]

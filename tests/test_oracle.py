@@ -33,14 +33,15 @@ def test_conversion_strided_sweep(orc):
             P.check_conversions(orc, bits.astype(np.uint32))
 
 
-@pytest.mark.parametrize("plant", range(1, 15))
+@pytest.mark.parametrize("plant", range(1, 18))
 def test_planted_mistake_is_caught(plant, tmp_path):
     """A copy of the oracle with one planted mistake (dropped bias
     correction, eps inside the root, decay after the update, decay sign,
     corrected slow EMA, alpha on the wrong EMA, swapped betas, decay on
     skipped elements, dropped square, written gradient, bf16 truncation,
-    no fp16 subnormals, step off by one, reversed slow plane) must fail at
-    least one pin that does not retype the formulas."""
+    no fp16 subnormals, step off by one, reversed slow plane; for clipping:
+    norm of the new parameter, squared update norm, clipping below the
+    bound) must fail at least one pin that does not retype the formulas."""
     path = O.build(str(tmp_path / f"liboracle_plant{plant}.so"), plant=plant)
     bad = O.Oracle(path)
     assert bad.planted == plant
