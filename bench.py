@@ -208,6 +208,23 @@ def main():
                                           "elements_per_s": round(cn / (r["median_ms"] * 1e-3), 0)}
             del ts
             torch.cuda.empty_cache()
+        # update-norm clipping: three launches, 40 B/element for fp32 Adam
+        # (pass 1 reads p, g, m, v and writes m, v; pass 3 reads p, m, v and writes p)
+        cn = 1 << 28
+        ts = make_flat("adam", "fp32", cn, seed=28)
+        ws = ou.clip_workspace(cn, dev)
+        cstate = {"t": 0}
+
+        def clip_step():
+            cstate["t"] += 1
+            ou.optimizer_update_32bit_clip("adam", *ts, step=cstate["t"], lr=1e-3, max_unorm=1e-3,
+                                           workspace=ws)
+        r = time_rounds(clip_step, iters=10)
+        gb = 40 * cn / (r["median_ms"] * 1e-3) / 1e9
+        cases["adam_fp32_2^28_max_unorm"] = {**r, "GBps": round(gb, 1), "frac_of_peak": round(gb / HBM_PEAK_GBS, 4),
+                                             "bytes_per_element": 40, "clip_factor": ou.clip_scale(ws)}
+        del ts, ws
+        torch.cuda.empty_cache()
         cases["adam_fp32_2^28"] = {"median_ms": out["ms_per_step"], "GBps": out["value"],
                                    "frac_of_peak": out["roofline"]["frac"]} if args.case == "adam:fp32:28" else None
         copy_gbs = cases["copy_fp32_2^28"]["GBps"]

@@ -103,6 +103,31 @@ int optimizer_update_32bit(int kind, int dtype, void* param, const void* grad,
                            float eps, float weight_decay, int64_t step, float lr,
                            int skip_zeros, void* stream);
 
+/* Update-norm clipping (the page's "max_unorm" option, which it names as a
+ * launch predicate and as a separate precondition/reduction kernel but does
+ * not define).  With max_unorm > 0 the direction u of the whole tensor
+ * (the per-element value that the plain update multiplies by lr, zero for
+ * elements skipped by skip_zeros) is scaled by
+ *     s = min(1, max_unorm * ||p||_2 / ||u||_2)      (s = 1 if ||u|| = 0),
+ * p being the parameter before the step, both norms summed in binary64 in a
+ * fixed order; each parameter becomes p*d - fl32(lr*s)*u.  The moments are
+ * those of the plain step.  max_unorm = 0 is exactly optimizer_update_32bit
+ * (workspace unused).
+ *
+ * `workspace` is caller-owned device memory of at least
+ * ou_clip_workspace_bytes(n) bytes, 16-byte aligned, not overlapping any
+ * other buffer; it holds per-chunk partial norms and the clip factor
+ * (workspace bytes [4, 8) hold s as a float after the step).  Three
+ * launches on `stream`; no allocation, capture-safe. */
+int64_t ou_clip_workspace_bytes(int64_t n);
+
+int optimizer_update_32bit_clip(int kind, int dtype, void* param, const void* grad,
+                                float* state1, float* state2, int64_t n,
+                                float beta1, float beta2, float beta3, float alpha,
+                                float eps, float weight_decay, int64_t step, float lr,
+                                int skip_zeros, float max_unorm, void* workspace,
+                                int64_t workspace_bytes, void* stream);
+
 /* One optimizer step over a collection of nseg tensors (any mix of
  * dtypes), one launch per dtype group (the eager optimizer.step() of
  * section "B300 benchmark and acceptance").  Convenience form: builds and

@@ -7,6 +7,7 @@ runs in the HIP kernels.  There is no CPU fallback: without the built
 library, or without a GPU, calls raise.
 
     optimizer_update_32bit(kind, param, grad, state1, state2, step=..., lr=..., ...)
+    optimizer_update_32bit_clip(..., max_unorm=..., workspace=...)   update-norm clipping
     optimizer_update_32bit_multi(kind, segments, hp, step)
     Plan(kind, segments)  -> .step(hp, step) / .graph_step(hp, step) / .close()
     AdamW32, AdEMAMix32    collection optimizers over a fixed parameter list
@@ -25,7 +26,9 @@ import torch
 from . import _lib
 from ._lib import OptimizerUpdateError, check, load
 
-__all__ = ["HParams", "optimizer_update_32bit", "optimizer_update_32bit_multi", "Plan",
+__all__ = ["HParams", "optimizer_update_32bit", "optimizer_update_32bit_clip",
+           "clip_workspace_bytes", "clip_workspace", "clip_scale",
+           "optimizer_update_32bit_multi", "Plan",
            "OptimizerUpdateError", "KINDS", "DTYPES", "load", "state_sizes"]
 
 KINDS = {"adam": _lib.OU_ADAM, "ademamix": _lib.OU_ADEMAMIX}
@@ -129,6 +132,52 @@ def optimizer_update_32bit(kind, param: torch.Tensor, grad: torch.Tensor, state1
                                         beta3, alpha, eps, weight_decay, int(step), lr,
                                         int(bool(skip_zeros)), _stream(param, stream))
     check(st, lib)
+
+
+def clip_workspace_bytes(n: int) -> int:
+    """Bytes of device workspace ``optimizer_update_32bit_clip`` needs for n elements."""
+    return int(load().ou_clip_workspace_bytes(int(n)))
+
+
+def clip_workspace(n: int, device) -> torch.Tensor:
+    """A workspace tensor (uint8) for ``optimizer_update_32bit_clip``."""
+    return torch.empty(clip_workspace_bytes(n), dtype=torch.uint8, device=device)
+
+
+def clip_scale(workspace: torch.Tensor) -> float:
+    """The clip factor s of the last clipped step that used ``workspace``
+    (synchronises with the device)."""
+    return float(workspace[4:8].view(torch.float32).item())
+
+
+def optimizer_update_32bit_clip(kind, param: torch.Tensor, grad: torch.Tensor,
+                                state1: torch.Tensor, state2: torch.Tensor, *, step: int,
+                                lr: float, max_unorm: float, workspace: torch.Tensor | None = None,
+                                beta1: float = 0.9, beta2: float = 0.999, beta3: float = 0.9999,
+                                alpha: float = 5.0, eps: float = 1e-8, weight_decay: float = 0.0,
+                                skip_zeros: bool = False, stream=None) -> torch.Tensor | None:
+    """One update of one tensor with update-norm clipping (max_unorm > 0),
+    in place.  ``workspace``: a uint8 device tensor of
+    ``clip_workspace_bytes(n)`` bytes (allocated here if None); returned so
+    that ``clip_scale`` can read the clip factor."""
+    k = _kind(kind)
+    n, dt = _tensor_args(k, param, grad, state1, state2)
+    if workspace is None and max_unorm > 0 and n > 0:
+        workspace = clip_workspace(n, param.device)
+    if workspace is not None and (not workspace.is_cuda or workspace.dtype != torch.uint8
+                                  or not workspace.is_contiguous()):
+        raise ValueError("workspace must be a contiguous uint8 tensor on the device")
+    lib = load()
+    wp = workspace.data_ptr() if workspace is not None else None
+    wb = workspace.numel() if workspace is not None else 0
+    with _on_device(param.device):
+        st = lib.optimizer_update_32bit_clip(k, dt, param.data_ptr(), grad.data_ptr(),
+                                             state1.data_ptr(), state2.data_ptr(), n, beta1, beta2,
+                                             beta3, alpha, eps, weight_decay, int(step), lr,
+                                             int(bool(skip_zeros)), max_unorm, wp, wb,
+                                             _stream(param, stream))
+    check(st, lib)
+    return workspace
 
 
 def _segments(kind: int, segments) -> ctypes.Array:

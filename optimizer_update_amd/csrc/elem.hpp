@@ -32,30 +32,47 @@ struct StepScalars {
     int32_t skip_zeros;
 };
 
-// One element.  m: fast first moment, v: second moment, m2: slow EMA
-// (AdEMAMix only).  p is the widened parameter; returns the new parameter
-// before rounding to storage.  Moments and bias correction follow Kingma &
-// Ba (Algorithm 1), the decay of the old parameter Loshchilov & Hutter
-// (Algorithm 2), the slow EMA mixed in with alpha Pagliardini et al.
-// (Algorithm 1).
+// The moments of one element.  m: fast first moment, v: second moment,
+// m2: slow EMA (AdEMAMix only).  Kingma & Ba (Algorithm 1) for m and v,
+// Pagliardini et al. (Algorithm 1) for the slow EMA.
+template <int KIND>
+__device__ __forceinline__ void update_moments(float g, float& m, float& v, float& m2,
+                                               const StepScalars& s)
+{
+    m = s.beta1 * m + s.omb1 * g;
+    v = s.beta2 * v + s.omb2 * (g * g);
+    if constexpr (KIND == kAdemamix) m2 = s.beta3 * m2 + s.omb3 * g;
+}
+
+// The update direction from the (new) moments: the parameter moves by
+// lr * direction.  Bias correction of m and v only; alpha mixes in the slow
+// EMA (not bias-corrected).
+template <int KIND>
+__device__ __forceinline__ float direction(float m, float v, float m2, const StepScalars& s)
+{
+    const float mh = m / s.bc1;
+    const float vh = v / s.bc2;
+    const float den = __builtin_sqrtf(vh) + s.eps;
+    float num = mh;
+    if constexpr (KIND == kAdemamix) num = mh + s.alpha * m2;
+    return num / den;
+}
+
+// Decoupled weight decay of the old parameter and the step (Loshchilov &
+// Hutter, Algorithm 2).
+__device__ __forceinline__ float step_param(float p, float u, float decay, float lr)
+{
+    return p * decay - lr * u;
+}
+
+// One element: moments, direction, parameter.  p is the widened parameter;
+// returns the new parameter before rounding to storage.
 template <int KIND>
 __device__ __forceinline__ float update_element(float p, float g, float& m, float& v,
                                                 float& m2, const StepScalars& s)
 {
-    const float mn = s.beta1 * m + s.omb1 * g;
-    const float vn = s.beta2 * v + s.omb2 * (g * g);
-    float m2n = 0.0f;
-    if constexpr (KIND == kAdemamix) m2n = s.beta3 * m2 + s.omb3 * g;
-    const float mh = mn / s.bc1;
-    const float vh = vn / s.bc2;
-    const float den = __builtin_sqrtf(vh) + s.eps;
-    float num = mh;
-    if constexpr (KIND == kAdemamix) num = mh + s.alpha * m2n;
-    const float u = num / den;
-    m = mn;
-    v = vn;
-    if constexpr (KIND == kAdemamix) m2 = m2n;
-    return p * s.decay - s.lr * u;
+    update_moments<KIND>(g, m, v, m2, s);
+    return step_param(p, direction<KIND>(m, v, m2, s), s.decay, s.lr);
 }
 
 // ---- storage types ---------------------------------------------------------

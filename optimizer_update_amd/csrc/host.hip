@@ -523,6 +523,84 @@ int optimizer_update_32bit(int kind, int dtype, void* param, const void* grad, f
 }
 
 __attribute__((visibility("default")))
+int64_t ou_clip_workspace_bytes(int64_t n)
+{
+    const int64_t chunks = n > 0 ? (n + kClipChunkElems - 1) / kClipChunkElems : 0;
+    return 256 + chunks * 16;
+}
+
+__attribute__((visibility("default")))
+int optimizer_update_32bit_clip(int kind, int dtype, void* param, const void* grad, float* state1,
+                                float* state2, int64_t n, float beta1, float beta2, float beta3,
+                                float alpha, float eps, float weight_decay, int64_t step, float lr,
+                                int skip_zeros, float max_unorm, void* workspace,
+                                int64_t workspace_bytes, void* stream)
+{
+    if (!std::isfinite(max_unorm) || max_unorm < 0.0f)
+        return fail(OU_EINVAL, "max_unorm must be finite and >= 0 (got %g)", max_unorm);
+    if (max_unorm == 0.0f)
+        return optimizer_update_32bit(kind, dtype, param, grad, state1, state2, n, beta1, beta2,
+                                      beta3, alpha, eps, weight_decay, step, lr, skip_zeros, stream);
+    ou_hparams h;
+    h.beta1 = beta1; h.beta2 = beta2; h.beta3 = beta3; h.alpha = alpha; h.eps = eps;
+    h.weight_decay = weight_decay; h.lr = lr; h.skip_zeros = skip_zeros; h.step = step;
+    if (int st = check_hparams(kind, h)) return st;
+    ou_segment s{param, grad, state1, state2, n, dtype, 0};
+    std::vector<Range> ranges;
+    ranges.reserve(5);
+    if (int st = check_segment(kind, s, 0, &ranges)) return st;
+    if (n == 0) return OU_OK;
+    const int64_t need = ou_clip_workspace_bytes(n);
+    if (!workspace) return fail(OU_EINVAL, "null workspace with max_unorm > 0");
+    if (reinterpret_cast<uintptr_t>(workspace) % 16) return fail(OU_EALIGN, "workspace not 16-byte aligned");
+    if (workspace_bytes < need)
+        return fail(OU_EINVAL, "workspace has %lld bytes, needs %lld", (long long)workspace_bytes, (long long)need);
+    const uintptr_t W = reinterpret_cast<uintptr_t>(workspace);
+    ranges.push_back({W, W + static_cast<uintptr_t>(need), true, 1});
+    if (int st = check_overlap(ranges)) return st;
+    const DeviceProps* dp = nullptr;
+    if (int st = g_devices.current(&dp)) return st;
+
+    bool vec = streams_16b_aligned(kind, s);
+    SingleLaunch L = select_single(*dp, kind, dtype, n, vec);
+    L.epl = 4;
+    apply_single_forcing(&L, &vec);
+    L.epl = 4;
+    const void* f1 = clip_kernel(1, kind, dtype, 0);
+    const void* f2 = clip_kernel(2, kind, dtype, 0);
+    const void* f3 = clip_kernel(3, kind, dtype, L.unroll);
+    // pass 3 covers groups of 4 elements
+    const int64_t groups = (n + 3) / 4;
+    const int64_t per_block = static_cast<int64_t>(L.block) * L.unroll;
+    int64_t grid3 = g_force_grid.load() ? L.grid : (groups + per_block - 1) / per_block;
+    grid3 = std::max<int64_t>(1, std::min<int64_t>(grid3, INT32_MAX));
+    if (!f1 || !f2 || !f3 || L.block < kWave || L.block > 1024 || L.block % kWave ||
+        L.lds < 0 || L.lds > dp->lds_per_block)
+        return fail(OU_EINVAL, "no clip kernel for block=%d unroll=%d", L.block, L.unroll);
+    const int64_t chunks = (n + kClipChunkElems - 1) / kClipChunkElems;
+    if (chunks > INT32_MAX) return fail(OU_EINVAL, "tensor too large");
+    StepScalars sc = make_scalars(h);
+    int32_t vec_ok = vec ? 1 : 0;
+    float* out = static_cast<float*>(workspace);
+    double2* partials = reinterpret_cast<double2*>(static_cast<unsigned char*>(workspace) + 256);
+    hipStream_t hs = static_cast<hipStream_t>(stream);
+    const void* cp = param;
+    void* a1[] = {&cp, const_cast<void**>(&grad), &state1, &state2, &n, &sc, &vec_ok, &partials};
+    const int lds1 = chunks >= 8LL * dp->cu_count ? lds_cap(*dp, 2) : 0;
+    hipError_t e = launch(f1, chunks, kClipThreadsHost, lds1, a1, hs);
+    if (e != hipSuccess) return hip_fail(e, "launch clip pass 1");
+    float lr_arg = lr;
+    void* a2[] = {&partials, const_cast<int64_t*>(&chunks), &max_unorm, &lr_arg, &out};
+    e = launch(f2, 1, kClipThreadsHost, 0, a2, hs);
+    if (e != hipSuccess) return hip_fail(e, "launch clip pass 2");
+    const float* lr_eff = out;
+    void* a3[] = {&param, const_cast<void**>(&grad), &state1, &state2, &n, &sc, &vec_ok, &lr_eff};
+    e = launch(f3, grid3, L.block, L.lds, a3, hs);
+    if (e != hipSuccess) return hip_fail(e, "launch clip pass 3");
+    return OU_OK;
+}
+
+__attribute__((visibility("default")))
 int optimizer_update_32bit_multi(int kind, const ou_segment* segs, int32_t nseg, const ou_hparams* hp,
                                  void* stream)
 {

@@ -63,6 +63,11 @@ int lds_cap(const DeviceProps& d, int blocks);
 const void* single_kernel(int kind, int dtype, int epl, int unroll);
 // Kernel entry for the multi-tensor kernel.
 const void* multi_kernel(int kind, int dtype, int epl, int unroll);
+// Kernels of update-norm clipping: pass 1 (moments and chunk partial
+// norms), 2 (finalize: clip factor), 3 (parameter step, unroll 1/2/4).
+const void* clip_kernel(int pass, int kind, int dtype, int unroll);
+constexpr int kClipChunkElems = 2048;   // elements per partial-norm chunk
+constexpr int kClipThreadsHost = 256;   // threads of passes 1 and 2
 
 constexpr int kWave = 64;
 

@@ -242,6 +242,208 @@ k_multi(const SegDesc* __restrict__ segs, const WorkItem* __restrict__ items, in
         update_scalar<KIND, S>(p, g, s1, s2, n, i, sc);
 }
 
+// ---- update-norm clipping ------------------------------------------------------
+//
+// Three launches: (1) k_clip_moments updates the moments and writes, for each
+// fixed chunk of kClipChunk elements, the binary64 partial sums of u^2 and
+// p^2; (2) k_clip_finalize sums the partials and forms the clip factor s and
+// fl32(lr * s); (3) k_clip_apply recomputes u from the stored moments (the
+// same operations on the same values, so the same u) and moves p.  The chunk
+// partition, each thread's elements within a chunk and every summation
+// order are fixed, so the result does not depend on the launch shape of
+// pass 3 or on the vector/per-element choice.
+
+constexpr int kClipThreads = 256;
+constexpr int kClipChunk = 2048;   // = kClipThreads * 2 groups * 4 elements
+
+// Sum of (a, b) over a 256-thread block in a fixed order: an xor butterfly
+// inside each wave (partners add the same two values, so every lane ends
+// with the same sum), then the four wave sums as (w0 + w1) + (w2 + w3).
+__device__ __forceinline__ double2 block_sum2(double a, double b, double2* lds)
+{
+#pragma unroll
+    for (int off = kWave / 2; off > 0; off >>= 1) {
+        a += __shfl_xor(a, off);
+        b += __shfl_xor(b, off);
+    }
+    const int wave = static_cast<int>(threadIdx.x) / kWave;
+    if (threadIdx.x % kWave == 0) lds[wave] = make_double2(a, b);
+    __syncthreads();
+    return make_double2((lds[0].x + lds[1].x) + (lds[2].x + lds[3].x),
+                        (lds[0].y + lds[1].y) + (lds[2].y + lds[3].y));
+}
+
+// Four consecutive elements starting at e0 (e0 % 4 == 0): one 16/8-byte
+// access when `vec` and all four exist, else element by element.
+template <typename S>
+__device__ __forceinline__ void load4s(const typename S::raw* base, int64_t e0, int64_t n, bool vec,
+                                       float out[4])
+{
+    constexpr int DW = 4 * S::bytes / 4;
+    if (vec && e0 + 3 < n) {
+        const Words<DW> w = load_words<DW>(base + e0);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) out[j] = S::widen(get_raw<S>(w, j));
+    } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) out[j] = (e0 + j < n) ? S::widen(base[e0 + j]) : 0.0f;
+    }
+}
+
+__device__ __forceinline__ void load4f(const float* base, int64_t e0, int64_t n, bool vec, float out[4])
+{
+    if (vec && e0 + 3 < n) {
+        const Words<4> w = load_words<4>(base + e0);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) out[j] = __builtin_bit_cast(float, w.w[j]);
+    } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) out[j] = (e0 + j < n) ? base[e0 + j] : 0.0f;
+    }
+}
+
+__device__ __forceinline__ void store4f(float* base, int64_t e0, int64_t n, bool vec, const float v[4])
+{
+    if (vec && e0 + 3 < n) {
+        Words<4> w;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) w.w[j] = __builtin_bit_cast(uint32_t, v[j]);
+        store_words<4>(base + e0, w);
+    } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            if (e0 + j < n) base[e0 + j] = v[j];
+    }
+}
+
+template <typename S>
+__device__ __forceinline__ void store4s(typename S::raw* base, int64_t e0, int64_t n, bool vec,
+                                        const typename S::raw v[4])
+{
+    constexpr int DW = 4 * S::bytes / 4;
+    if (vec && e0 + 3 < n) {
+        Words<DW> w;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) set_raw<S>(w, j, v[j]);
+        store_words<DW>(base + e0, w);
+    } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            if (e0 + j < n) base[e0 + j] = v[j];
+    }
+}
+
+// Pass 1: one block per chunk (grid = number of chunks).  Thread t owns the
+// elements chunk*2048 + h*1024 + 4t + j (h = 0, 1; j = 0..3) and adds their
+// u^2 and p^2 in that order.
+template <int KIND, typename S>
+__global__ void __launch_bounds__(kClipThreads)
+k_clip_moments(const typename S::raw* __restrict__ p, const typename S::raw* __restrict__ g,
+               float* __restrict__ s1, float* __restrict__ s2, int64_t n, StepScalars sc,
+               int32_t vec_ok, double2* __restrict__ partials)
+{
+    __shared__ double2 lds[kClipThreads / kWave];
+    const int64_t chunk = blockIdx.x;
+    double usq = 0.0, psq = 0.0;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const int64_t e0 = chunk * kClipChunk + h * (kClipChunk / 2) + 4 * static_cast<int64_t>(threadIdx.x);
+        float pv[4], gv[4], mv[4], vv[4], m2v[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+        load4s<S>(p, e0, n, vec_ok, pv);
+        load4s<S>(g, e0, n, vec_ok, gv);
+        load4f(s1, e0, n, vec_ok, mv);
+        load4f(s2, e0, n, vec_ok, vv);
+        if constexpr (KIND == kAdemamix) load4f(s1 + n, e0, n, vec_ok, m2v);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            if (e0 + j >= n) continue;
+            psq += static_cast<double>(pv[j]) * static_cast<double>(pv[j]);
+            if (sc.skip_zeros && gv[j] == 0.0f) continue;
+            update_moments<KIND>(gv[j], mv[j], vv[j], m2v[j], sc);
+            const float u = direction<KIND>(mv[j], vv[j], m2v[j], sc);
+            usq += static_cast<double>(u) * static_cast<double>(u);
+        }
+        store4f(s1, e0, n, vec_ok, mv);
+        store4f(s2, e0, n, vec_ok, vv);
+        if constexpr (KIND == kAdemamix) store4f(s1 + n, e0, n, vec_ok, m2v);
+    }
+    const double2 tot = block_sum2(usq, psq, lds);
+    if (threadIdx.x == 0) partials[chunk] = tot;
+}
+
+// Pass 2: one block.  Thread t adds the partials of chunks t, t + 256, ...
+// in order; then the block sum.  out[0] = fl32(lr * s), out[1] = s with
+// s = min(1, max_unorm * ||p|| / ||u||) (1 when ||u|| = 0).
+__global__ void __launch_bounds__(kClipThreads)
+k_clip_finalize(const double2* __restrict__ partials, int64_t nchunks, float max_unorm, float lr,
+                float* __restrict__ out)
+{
+    __shared__ double2 lds[kClipThreads / kWave];
+    double usq = 0.0, psq = 0.0;
+    for (int64_t c = threadIdx.x; c < nchunks; c += kClipThreads) {
+        usq += partials[c].x;
+        psq += partials[c].y;
+    }
+    const double2 tot = block_sum2(usq, psq, lds);
+    if (threadIdx.x == 0) {
+        float s = 1.0f;
+        if (max_unorm > 0.0f && tot.x > 0.0) {
+            const double r = static_cast<double>(max_unorm) * __builtin_sqrt(tot.y) / __builtin_sqrt(tot.x);
+            if (r < 1.0) s = static_cast<float>(r);
+        }
+        out[0] = lr * s;
+        out[1] = s;
+    }
+}
+
+// Pass 3: the parameter step with the clipped learning rate *lr_eff, any
+// launch shape (tiles of blockDim * U groups of 4 elements, grid-stride if
+// the grid is capped).  The gradient is read only to find skipped elements.
+template <int KIND, typename S, int U>
+__global__ void __launch_bounds__(1024)
+k_clip_apply(typename S::raw* __restrict__ p, const typename S::raw* __restrict__ g,
+             const float* __restrict__ s1, const float* __restrict__ s2, int64_t n, StepScalars sc,
+             int32_t vec_ok, const float* __restrict__ lr_eff)
+{
+    using raw = typename S::raw;
+    const float lr = lr_eff[0];
+    const int64_t ngroups = (n + 3) / 4;
+    const int64_t bdim = blockDim.x;
+    const int64_t nthreads = static_cast<int64_t>(gridDim.x) * bdim;
+    for (int64_t base = static_cast<int64_t>(blockIdx.x) * bdim * U + threadIdx.x; base < ngroups;
+         base += nthreads * U) {
+        float pv[U][4], gv[U][4], mv[U][4], vv[U][4], m2v[U][4];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int64_t e0 = 4 * (base + u * bdim);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) gv[u][j] = 1.0f;
+            if (e0 >= n) continue;
+            load4s<S>(p, e0, n, vec_ok, pv[u]);
+            if (sc.skip_zeros) load4s<S>(g, e0, n, vec_ok, gv[u]);
+            load4f(s1, e0, n, vec_ok, mv[u]);
+            load4f(s2, e0, n, vec_ok, vv[u]);
+            if constexpr (KIND == kAdemamix) load4f(s1 + n, e0, n, vec_ok, m2v[u]);
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int64_t e0 = 4 * (base + u * bdim);
+            if (e0 >= n) continue;
+            raw out[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                float m2j = 0.0f;
+                if constexpr (KIND == kAdemamix) m2j = m2v[u][j];
+                const float dir = direction<KIND>(mv[u][j], vv[u][j], m2j, sc);
+                const float pn = step_param(pv[u][j], dir, sc.decay, lr);
+                const bool keep = sc.skip_zeros && gv[u][j] == 0.0f;
+                out[j] = keep ? S::narrow(pv[u][j]) : S::narrow(pn);
+            }
+            store4s<S>(p, e0, n, vec_ok, out);
+        }
+    }
+}
+
 // ---- instantiation tables ---------------------------------------------------------
 
 template <int KIND, typename S, int EPL>
@@ -292,7 +494,38 @@ const void* pick_all(bool multi, int kind, int dtype, int epl, int unroll)
     return nullptr;
 }
 
+template <int KIND, typename S>
+const void* pick_clip(int pass, int unroll)
+{
+    if (pass == 1) return reinterpret_cast<const void*>(&k_clip_moments<KIND, S>);
+    switch (unroll) {
+    case 1: return reinterpret_cast<const void*>(&k_clip_apply<KIND, S, 1>);
+    case 2: return reinterpret_cast<const void*>(&k_clip_apply<KIND, S, 2>);
+    case 4: return reinterpret_cast<const void*>(&k_clip_apply<KIND, S, 4>);
+    default: return nullptr;
+    }
+}
+
+template <int KIND>
+const void* pick_clip_dtype(int pass, int dtype, int unroll)
+{
+    switch (dtype) {
+    case 0: return pick_clip<KIND, F32>(pass, unroll);
+    case 1: return pick_clip<KIND, F16>(pass, unroll);
+    case 2: return pick_clip<KIND, BF16>(pass, unroll);
+    default: return nullptr;
+    }
+}
+
 }  // namespace
+
+const void* clip_kernel(int pass, int kind, int dtype, int unroll)
+{
+    if (pass == 2) return reinterpret_cast<const void*>(&k_clip_finalize);
+    if (kind == kAdam) return pick_clip_dtype<kAdam>(pass, dtype, unroll);
+    if (kind == kAdemamix) return pick_clip_dtype<kAdemamix>(pass, dtype, unroll);
+    return nullptr;
+}
 
 const void* single_kernel(int kind, int dtype, int epl, int unroll)
 {

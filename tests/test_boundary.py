@@ -28,6 +28,7 @@ def L():
 def test_exports_every_header_function(L):
     names = _lib.header_functions()
     assert set(names) == {"optimizer_update_32bit", "optimizer_update_32bit_multi",
+                          "ou_clip_workspace_bytes", "optimizer_update_32bit_clip",
                           "ou_plan_create", "ou_plan_step", "ou_plan_graph_step",
                           "ou_plan_describe", "ou_plan_destroy", "ou_status_string",
                           "ou_last_error"}
@@ -142,6 +143,33 @@ def test_plan_and_multi_validation(L):
     assert L.ou_plan_graph_step(None, ctypes.byref(bad_hp), None) == OU_EINVAL
     assert L.ou_plan_describe(None, None, None, None) == OU_EINVAL
     L.ou_plan_destroy(None)
+
+
+def _clip(L, max_unorm=1.0, ws=0x800000, wsb=None, n=4096, p=0x10000, **kw):
+    if wsb is None:
+        wsb = L.ou_clip_workspace_bytes(n)
+    return L.optimizer_update_32bit_clip(0, 0, p, 0x20000, 0x30000, 0x40000, n, 0.9, 0.999, 0.9999,
+                                         5.0, 1e-8, 0.0, kw.get("step", 1), 1e-3, 0, max_unorm,
+                                         ws, wsb, None)
+
+
+def test_clip_entry_validation(L):
+    assert L.ou_clip_workspace_bytes(0) == 256
+    assert L.ou_clip_workspace_bytes(1) == 256 + 16
+    assert L.ou_clip_workspace_bytes(2048) == 256 + 16
+    assert L.ou_clip_workspace_bytes(2049) == 256 + 32
+    assert L.ou_clip_workspace_bytes(1 << 30) == 256 + 16 * (1 << 19)
+    assert _clip(L, max_unorm=-1.0) == OU_EINVAL
+    assert _clip(L, max_unorm=float("nan")) == OU_EINVAL
+    assert _clip(L, max_unorm=float("inf")) == OU_EINVAL
+    assert _clip(L, ws=0) == OU_EINVAL
+    assert _clip(L, ws=0x800008) == OU_EALIGN
+    assert _clip(L, wsb=100) == OU_EINVAL
+    assert _clip(L, ws=0x40000 + 64) == OU_EOVERLAP          # workspace inside state2
+    assert _clip(L, ws=0x10000 - 64) == OU_EOVERLAP          # workspace runs into param
+    assert _clip(L, step=0) == OU_EINVAL
+    assert _clip(L, n=0) == OU_OK                           # nothing to do
+    assert _clip(L, max_unorm=0.0, n=0, ws=0) == OU_OK        # plain step, no workspace
 
 
 def test_status_strings(L):
