@@ -155,6 +155,19 @@ int ou_plan_step(ou_plan plan, const ou_hparams* hp, void* stream);
  * being captured. */
 int ou_plan_graph_step(ou_plan plan, const ou_hparams* hp, void* stream);
 
+/* One step of the plan's collection with update-norm clipping, per tensor
+ * (the rule of optimizer_update_32bit_clip applied to every segment with
+ * its own norms): three launches per dtype group, on `stream`.  Bitwise
+ * identical to optimizer_update_32bit_clip on each tensor.  max_unorm = 0 is
+ * ou_plan_step.  The plan holds the partial norms; capture-safe. */
+int ou_plan_step_clip(ou_plan plan, const ou_hparams* hp, float max_unorm, void* stream);
+
+/* Clip factors s of the last clipped step, in the order of the segments
+ * given to ou_plan_create (1 for segments with n = 0 or before any clipped
+ * step has run).  Synchronous copy to host memory; nseg must equal the
+ * plan's segment count. */
+int ou_plan_clip_factors(ou_plan plan, float* out, int32_t nseg);
+
 /* Shape of a plan: dtype groups (= launches per step), work items, elements. */
 int ou_plan_describe(ou_plan plan, int32_t* n_groups, int64_t* n_work_items,
                      int64_t* n_elements);

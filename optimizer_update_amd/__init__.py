@@ -229,6 +229,21 @@ class Plan:
         with _on_device(self.device):
             check(self._lib.ou_plan_step(self._h, ctypes.byref(c), self._stream(stream)), self._lib)
 
+    def step_clip(self, hp: HParams, step: int, max_unorm: float, stream=None) -> None:
+        """One step with update-norm clipping per tensor (``ou_plan_step_clip``)."""
+        c = hp.c(step)
+        with _on_device(self.device):
+            check(self._lib.ou_plan_step_clip(self._h, ctypes.byref(c), max_unorm,
+                                              self._stream(stream)), self._lib)
+
+    def clip_factors(self) -> list[float]:
+        """Clip factor of every tensor in the last clipped step (synchronous)."""
+        out = (ctypes.c_float * len(self._tensors))()
+        with _on_device(self.device):
+            torch.cuda.synchronize(self.device)
+            check(self._lib.ou_plan_clip_factors(self._h, out, len(self._tensors)), self._lib)
+        return list(out)
+
     def graph_step(self, hp: HParams, step: int, stream=None) -> None:
         c = hp.c(step)
         with _on_device(self.device):

@@ -76,6 +76,10 @@ def load(path: str = LIBRARY) -> ctypes.CDLL:
     lib.ou_plan_create.restype = i32
     lib.ou_plan_step.argtypes = [vp, ctypes.POINTER(ou_hparams), vp]
     lib.ou_plan_step.restype = i32
+    lib.ou_plan_step_clip.argtypes = [vp, ctypes.POINTER(ou_hparams), f32, vp]
+    lib.ou_plan_step_clip.restype = i32
+    lib.ou_plan_clip_factors.argtypes = [vp, ctypes.POINTER(f32), ctypes.c_int32]
+    lib.ou_plan_clip_factors.restype = i32
     lib.ou_plan_graph_step.argtypes = [vp, ctypes.POINTER(ou_hparams), vp]
     lib.ou_plan_graph_step.restype = i32
     lib.ou_plan_describe.argtypes = [vp, ctypes.POINTER(ctypes.c_int32),

@@ -324,6 +324,13 @@ struct Group {
     StepScalars sc;
     int32_t chunk32;
     void* args[5];
+    // update-norm clipping: one item per (segment, 2048-element chunk),
+    // binary64 partial sums per item, two floats (fl32(lr*s), s) per segment
+    int64_t n_segs;
+    int64_t n_clip_items;
+    const WorkItem* d_clip_items;
+    double2* d_partials;
+    float* d_seg_out;
 };
 
 }  // namespace ou
@@ -332,6 +339,7 @@ struct ou_plan_s {
     int kind = 0;
     int64_t n_elements = 0;
     void* dmem = nullptr;
+    std::vector<std::pair<int, int64_t>> seg_map;   // caller's index -> (group, slot), group -1 if n = 0
     std::vector<ou::Group> groups;
     hipGraph_t graph = nullptr;
     hipGraphExec_t exec = nullptr;
@@ -360,10 +368,12 @@ int build_plan(int kind, const ou_segment* segs, int32_t nseg, ou_plan_s** out)
     (void)hipGetDevice(&plan->device);
 
     // Host tables per dtype group: descriptors, then work items (largest
-    // chunks first so the long items start early).
+    // chunks first so the long items start early), then the clip items.
     struct HostGroup {
         std::vector<SegDesc> segs;
         std::vector<std::pair<int64_t, WorkItem>> items;   // (length, item)
+        std::vector<WorkItem> clip_items;
+        int64_t clip_slots = 0;
         MultiLaunch L;
         int64_t chunk;
     };
@@ -379,6 +389,7 @@ int build_plan(int kind, const ou_segment* segs, int32_t nseg, ou_plan_s** out)
         hg[dt].chunk = select_chunk(group_elems[dt]);
         if (int c = g_force_chunk.load()) hg[dt].chunk = c;
     }
+    plan->seg_map.assign(static_cast<size_t>(nseg), {-1, 0});
     for (int i = 0; i < nseg; ++i) {
         const ou_segment& s = segs[i];
         if (s.n == 0) continue;
@@ -391,26 +402,38 @@ int build_plan(int kind, const ou_segment* segs, int32_t nseg, ou_plan_s** out)
         d.n = s.n;
         d.vec_ok = streams_16b_aligned(kind, s) ? 1 : 0;
         d.pad = 0;
+        d.clip_base = G.clip_slots;
         const int32_t seg_idx = static_cast<int32_t>(G.segs.size());
+        plan->seg_map[static_cast<size_t>(i)] = {s.dtype, seg_idx};
         G.segs.push_back(d);
         const int64_t nchunks = (s.n + G.chunk - 1) / G.chunk;
-        if (nchunks > INT32_MAX) { delete plan; return fail(OU_EINVAL, "segment %d: too many chunks", i); }
+        const int64_t nclip = (s.n + kClipChunkElems - 1) / kClipChunkElems;
+        if (nchunks > INT32_MAX || nclip > INT32_MAX) { delete plan; return fail(OU_EINVAL, "segment %d: too many chunks", i); }
         for (int64_t c = 0; c < nchunks; ++c) {
             const int64_t len = std::min<int64_t>(G.chunk, s.n - c * G.chunk);
             G.items.push_back({len, WorkItem{seg_idx, static_cast<int32_t>(c)}});
         }
+        for (int64_t c = 0; c < nclip; ++c) G.clip_items.push_back(WorkItem{seg_idx, static_cast<int32_t>(c)});
+        G.clip_slots += nclip;
         plan->n_elements += s.n;
     }
+    auto align16 = [](size_t x) { return (x + 15) & ~size_t(15); };
     size_t bytes = 0;
     for (auto& G : hg) {
         std::stable_sort(G.items.begin(), G.items.end(),
                          [](const auto& a, const auto& b) { return a.first > b.first; });
-        bytes += G.segs.size() * sizeof(SegDesc) + G.items.size() * sizeof(WorkItem);
+        if (G.segs.empty()) continue;
+        bytes = align16(bytes + G.segs.size() * sizeof(SegDesc));
+        bytes = align16(bytes + G.items.size() * sizeof(WorkItem));
+        bytes = align16(bytes + G.clip_items.size() * sizeof(WorkItem));
+        bytes = align16(bytes + static_cast<size_t>(G.clip_slots) * sizeof(double2));
+        bytes = align16(bytes + G.segs.size() * 2 * sizeof(float));
     }
     if (bytes > 0) {
         hipError_t e = hipMalloc(&plan->dmem, bytes);
         if (e != hipSuccess) { delete plan; return fail(OU_ENOMEM, "hipMalloc(%zu): %s", bytes, hipGetErrorString(e)); }
-        std::vector<unsigned char> host(bytes);
+        std::vector<unsigned char> host(bytes, 0);
+        unsigned char* base = static_cast<unsigned char*>(plan->dmem);
         size_t off = 0;
         for (int dt = 0; dt < 3; ++dt) {
             HostGroup& G = hg[dt];
@@ -420,15 +443,29 @@ int build_plan(int kind, const ou_segment* segs, int32_t nseg, ou_plan_s** out)
             grp.L = G.L;
             grp.chunk = G.chunk;
             grp.n_items = static_cast<int64_t>(G.items.size());
-            grp.d_segs = reinterpret_cast<const SegDesc*>(static_cast<unsigned char*>(plan->dmem) + off);
+            grp.n_segs = static_cast<int64_t>(G.segs.size());
+            grp.n_clip_items = static_cast<int64_t>(G.clip_items.size());
+            grp.d_segs = reinterpret_cast<const SegDesc*>(base + off);
             std::memcpy(host.data() + off, G.segs.data(), G.segs.size() * sizeof(SegDesc));
-            off += G.segs.size() * sizeof(SegDesc);
-            grp.d_items = reinterpret_cast<const WorkItem*>(static_cast<unsigned char*>(plan->dmem) + off);
+            off = align16(off + G.segs.size() * sizeof(SegDesc));
+            grp.d_items = reinterpret_cast<const WorkItem*>(base + off);
             for (size_t k = 0; k < G.items.size(); ++k)
                 std::memcpy(host.data() + off + k * sizeof(WorkItem), &G.items[k].second, sizeof(WorkItem));
-            off += G.items.size() * sizeof(WorkItem);
+            off = align16(off + G.items.size() * sizeof(WorkItem));
+            grp.d_clip_items = reinterpret_cast<const WorkItem*>(base + off);
+            std::memcpy(host.data() + off, G.clip_items.data(), G.clip_items.size() * sizeof(WorkItem));
+            off = align16(off + G.clip_items.size() * sizeof(WorkItem));
+            grp.d_partials = reinterpret_cast<double2*>(base + off);
+            off = align16(off + static_cast<size_t>(G.clip_slots) * sizeof(double2));
+            grp.d_seg_out = reinterpret_cast<float*>(base + off);
+            for (size_t k = 0; k < G.segs.size(); ++k) {   // (lr_eff, s) = (0, 1) until a clipped step
+                const float init[2] = {0.0f, 1.0f};
+                std::memcpy(host.data() + off + k * sizeof(init), init, sizeof(init));
+            }
+            off = align16(off + G.segs.size() * 2 * sizeof(float));
             grp.fn = multi_kernel(kind, dt, grp.L.epl, grp.L.unroll);
-            if (!grp.fn || grp.chunk % (kWave * grp.L.epl) != 0 || grp.chunk > INT32_MAX) {
+            if (!grp.fn || grp.chunk % (kWave * grp.L.epl) != 0 || grp.chunk > INT32_MAX ||
+                grp.chunk % 4 != 0) {
                 (void)hipFree(plan->dmem);
                 delete plan;
                 return fail(OU_EINVAL, "no multi-tensor kernel for epl=%d unroll=%d chunk=%lld",
@@ -465,6 +502,34 @@ int plan_launch(ou_plan_s* plan, const StepScalars& sc, hipStream_t stream)
         set_group_args(g, sc);
         hipError_t e = launch(g.fn, g.grid, g.L.waves * kWave, g.L.lds, g.args, stream);
         if (e != hipSuccess) return hip_fail(e, "launch multi-tensor kernel");
+    }
+    return OU_OK;
+}
+
+// The clipped step of a plan: three launches per dtype group (moments and
+// partial norms per (segment, chunk); one block per segment for the clip
+// factors; the parameter step over the regular work list).
+int plan_launch_clip(ou_plan_s* plan, const StepScalars& sc, float max_unorm, hipStream_t stream)
+{
+    for (Group& g : plan->groups) {
+        const void* f1 = clip_kernel(11, plan->kind, g.dtype, 0);
+        const void* f2 = clip_kernel(12, plan->kind, g.dtype, 0);
+        const void* f3 = clip_kernel(13, plan->kind, g.dtype, 0);
+        if (!f1 || !f2 || !f3) return fail(OU_EINVAL, "no clip kernels for dtype %d", g.dtype);
+        StepScalars s = sc;
+        float mu = max_unorm, lr = sc.lr;
+        void* a1[] = {const_cast<SegDesc**>(&g.d_segs), const_cast<WorkItem**>(&g.d_clip_items), &s,
+                      &g.d_partials};
+        hipError_t e = launch(f1, g.n_clip_items, kClipThreadsHost, g.L.lds, a1, stream);
+        if (e != hipSuccess) return hip_fail(e, "launch clip pass 1 (collection)");
+        void* a2[] = {const_cast<SegDesc**>(&g.d_segs), &g.d_partials, &mu, &lr, &g.d_seg_out};
+        e = launch(f2, g.n_segs, kClipThreadsHost, 0, a2, stream);
+        if (e != hipSuccess) return hip_fail(e, "launch clip pass 2 (collection)");
+        const float* seg_out = g.d_seg_out;
+        void* a3[] = {const_cast<SegDesc**>(&g.d_segs), const_cast<WorkItem**>(&g.d_items), &g.n_items,
+                      &g.chunk32, &s, const_cast<float**>(&seg_out)};
+        e = launch(f3, g.grid, g.L.waves * kWave, g.L.lds, a3, stream);
+        if (e != hipSuccess) return hip_fail(e, "launch clip pass 3 (collection)");
     }
     return OU_OK;
 }
@@ -633,6 +698,38 @@ int ou_plan_step(ou_plan plan, const ou_hparams* hp, void* stream)
     if (int st = check_hparams(plan->kind, *hp)) return st;
     if (int st = check_plan_device(plan)) return st;
     return plan_launch(plan, make_scalars(*hp), static_cast<hipStream_t>(stream));
+}
+
+__attribute__((visibility("default")))
+int ou_plan_step_clip(ou_plan plan, const ou_hparams* hp, float max_unorm, void* stream)
+{
+    if (!plan || !hp) return fail(OU_EINVAL, "null plan or hparams");
+    if (!std::isfinite(max_unorm) || max_unorm < 0.0f)
+        return fail(OU_EINVAL, "max_unorm must be finite and >= 0 (got %g)", max_unorm);
+    if (int st = check_hparams(plan->kind, *hp)) return st;
+    if (int st = check_plan_device(plan)) return st;
+    if (max_unorm == 0.0f) return plan_launch(plan, make_scalars(*hp), static_cast<hipStream_t>(stream));
+    return plan_launch_clip(plan, make_scalars(*hp), max_unorm, static_cast<hipStream_t>(stream));
+}
+
+__attribute__((visibility("default")))
+int ou_plan_clip_factors(ou_plan plan, float* out, int32_t nseg)
+{
+    if (!plan || (!out && nseg > 0)) return fail(OU_EINVAL, "null plan or output");
+    if (nseg != static_cast<int32_t>(plan->seg_map.size()))
+        return fail(OU_EINVAL, "plan has %zu segments, not %d", plan->seg_map.size(), nseg);
+    if (int st = check_plan_device(plan)) return st;
+    for (int32_t i = 0; i < nseg; ++i) {
+        const auto [dt, slot] = plan->seg_map[static_cast<size_t>(i)];
+        out[i] = 1.0f;
+        if (dt < 0) continue;
+        for (const Group& g : plan->groups) {
+            if (g.dtype != dt) continue;
+            hipError_t e = hipMemcpy(&out[i], g.d_seg_out + 2 * slot + 1, sizeof(float), hipMemcpyDeviceToHost);
+            if (e != hipSuccess) return hip_fail(e, "hipMemcpy(clip factor)");
+        }
+    }
+    return OU_OK;
 }
 
 __attribute__((visibility("default")))

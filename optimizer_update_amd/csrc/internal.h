@@ -17,8 +17,9 @@ struct SegDesc {
     int64_t n;
     int32_t vec_ok;  // every stream 16-byte aligned (dwordx4 path)
     int32_t pad;
+    int64_t clip_base;  // first partial-norm slot of this segment (clipped steps)
 };
-static_assert(sizeof(SegDesc) == 48, "SegDesc layout");
+static_assert(sizeof(SegDesc) == 56, "SegDesc layout");
 
 // Work item: one wave updates elements [chunk*chunk_elems, min(n, +chunk_elems))
 // of segment seg.
@@ -64,7 +65,8 @@ const void* single_kernel(int kind, int dtype, int epl, int unroll);
 // Kernel entry for the multi-tensor kernel.
 const void* multi_kernel(int kind, int dtype, int epl, int unroll);
 // Kernels of update-norm clipping: pass 1 (moments and chunk partial
-// norms), 2 (finalize: clip factor), 3 (parameter step, unroll 1/2/4).
+// norms), 2 (finalize: clip factor), 3 (parameter step, unroll 1/2/4);
+// 11, 12, 13: the same passes over a plan's collection.
 const void* clip_kernel(int pass, int kind, int dtype, int unroll);
 constexpr int kClipChunkElems = 2048;   // elements per partial-norm chunk
 constexpr int kClipThreadsHost = 256;   // threads of passes 1 and 2

@@ -333,17 +333,16 @@ __device__ __forceinline__ void store4s(typename S::raw* base, int64_t e0, int64
     }
 }
 
-// Pass 1: one block per chunk (grid = number of chunks).  Thread t owns the
-// elements chunk*2048 + h*1024 + 4t + j (h = 0, 1; j = 0..3) and adds their
-// u^2 and p^2 in that order.
+// Pass 1 body for one chunk: thread t owns the elements
+// chunk*2048 + h*1024 + 4t + j (h = 0, 1; j = 0..3) and adds their u^2 and
+// p^2 in that order; returns the block's sums (same value in every thread).
 template <int KIND, typename S>
-__global__ void __launch_bounds__(kClipThreads)
-k_clip_moments(const typename S::raw* __restrict__ p, const typename S::raw* __restrict__ g,
-               float* __restrict__ s1, float* __restrict__ s2, int64_t n, StepScalars sc,
-               int32_t vec_ok, double2* __restrict__ partials)
+__device__ __forceinline__ double2 clip_chunk(const typename S::raw* __restrict__ p,
+                                              const typename S::raw* __restrict__ g,
+                                              float* __restrict__ s1, float* __restrict__ s2,
+                                              int64_t n, const StepScalars& sc, bool vec_ok,
+                                              int64_t chunk, double2* lds)
 {
-    __shared__ double2 lds[kClipThreads / kWave];
-    const int64_t chunk = blockIdx.x;
     double usq = 0.0, psq = 0.0;
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
@@ -367,18 +366,45 @@ k_clip_moments(const typename S::raw* __restrict__ p, const typename S::raw* __r
         store4f(s2, e0, n, vec_ok, vv);
         if constexpr (KIND == kAdemamix) store4f(s1 + n, e0, n, vec_ok, m2v);
     }
-    const double2 tot = block_sum2(usq, psq, lds);
-    if (threadIdx.x == 0) partials[chunk] = tot;
+    return block_sum2(usq, psq, lds);
 }
 
-// Pass 2: one block.  Thread t adds the partials of chunks t, t + 256, ...
-// in order; then the block sum.  out[0] = fl32(lr * s), out[1] = s with
-// s = min(1, max_unorm * ||p|| / ||u||) (1 when ||u|| = 0).
+// Pass 1, one tensor: one block per chunk (grid = number of chunks).
+template <int KIND, typename S>
 __global__ void __launch_bounds__(kClipThreads)
-k_clip_finalize(const double2* __restrict__ partials, int64_t nchunks, float max_unorm, float lr,
-                float* __restrict__ out)
+k_clip_moments(const typename S::raw* __restrict__ p, const typename S::raw* __restrict__ g,
+               float* __restrict__ s1, float* __restrict__ s2, int64_t n, StepScalars sc,
+               int32_t vec_ok, double2* __restrict__ partials)
 {
     __shared__ double2 lds[kClipThreads / kWave];
+    const double2 tot = clip_chunk<KIND, S>(p, g, s1, s2, n, sc, vec_ok != 0, blockIdx.x, lds);
+    if (threadIdx.x == 0) partials[blockIdx.x] = tot;
+}
+
+// Pass 1, collection: one block per (segment, chunk) item; the chunk's sums
+// go to the segment's slice of the partials.
+template <int KIND, typename S>
+__global__ void __launch_bounds__(kClipThreads)
+k_clip_moments_multi(const SegDesc* __restrict__ segs, const WorkItem* __restrict__ items,
+                     StepScalars sc, double2* __restrict__ partials)
+{
+    using raw = typename S::raw;
+    __shared__ double2 lds[kClipThreads / kWave];
+    const WorkItem it = items[blockIdx.x];
+    const SegDesc d = segs[__builtin_amdgcn_readfirstlane(it.seg)];
+    const int64_t chunk = __builtin_amdgcn_readfirstlane(it.chunk);
+    const double2 tot = clip_chunk<KIND, S>(static_cast<const raw*>(d.p), static_cast<const raw*>(d.g),
+                                            d.s1, d.s2, d.n, sc, d.vec_ok != 0, chunk, lds);
+    if (threadIdx.x == 0) partials[d.clip_base + chunk] = tot;
+}
+
+// Pass 2 body: thread t adds the partials of chunks t, t + 256, ... in
+// order, then the block sum.  out[0] = fl32(lr * s), out[1] = s with
+// s = min(1, max_unorm * ||p|| / ||u||) (1 when ||u|| = 0).
+__device__ __forceinline__ void clip_finalize(const double2* __restrict__ partials, int64_t nchunks,
+                                              float max_unorm, float lr, float* __restrict__ out,
+                                              double2* lds)
+{
     double usq = 0.0, psq = 0.0;
     for (int64_t c = threadIdx.x; c < nchunks; c += kClipThreads) {
         usq += partials[c].x;
@@ -394,6 +420,27 @@ k_clip_finalize(const double2* __restrict__ partials, int64_t nchunks, float max
         out[0] = lr * s;
         out[1] = s;
     }
+}
+
+// Pass 2, one tensor: a single block.
+__global__ void __launch_bounds__(kClipThreads)
+k_clip_finalize(const double2* __restrict__ partials, int64_t nchunks, float max_unorm, float lr,
+                float* __restrict__ out)
+{
+    __shared__ double2 lds[kClipThreads / kWave];
+    clip_finalize(partials, nchunks, max_unorm, lr, out, lds);
+}
+
+// Pass 2, collection: one block per segment; out holds two floats per segment.
+__global__ void __launch_bounds__(kClipThreads)
+k_clip_finalize_multi(const SegDesc* __restrict__ segs, const double2* __restrict__ partials,
+                      float max_unorm, float lr, float* __restrict__ out)
+{
+    __shared__ double2 lds[kClipThreads / kWave];
+    const SegDesc d = segs[blockIdx.x];
+    const int64_t nchunks = (d.n + kClipChunk - 1) / kClipChunk;
+    clip_finalize(partials + d.clip_base, nchunks, max_unorm, lr, out + 2 * static_cast<int64_t>(blockIdx.x),
+                  lds);
 }
 
 // Pass 3: the parameter step with the clipped learning rate *lr_eff, any
@@ -441,6 +488,47 @@ k_clip_apply(typename S::raw* __restrict__ p, const typename S::raw* __restrict_
             }
             store4s<S>(p, e0, n, vec_ok, out);
         }
+    }
+}
+
+// Pass 3, collection: one wave per item of the plan's regular work list,
+// with the segment's clipped learning rate.
+template <int KIND, typename S>
+__global__ void __launch_bounds__(512)
+k_clip_apply_multi(const SegDesc* __restrict__ segs, const WorkItem* __restrict__ items,
+                   int64_t n_items, int32_t chunk, StepScalars sc, const float* __restrict__ seg_out)
+{
+    using raw = typename S::raw;
+    const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) / kWave);
+    const int lane = static_cast<int>(threadIdx.x) % kWave;
+    const int64_t w = static_cast<int64_t>(blockIdx.x) * (blockDim.x / kWave) + wave;
+    if (w >= n_items) return;
+    const WorkItem it = items[w];
+    const int seg = __builtin_amdgcn_readfirstlane(it.seg);
+    const SegDesc d = segs[seg];
+    const float lr = seg_out[2 * static_cast<int64_t>(seg)];
+    raw* __restrict__ p = static_cast<raw*>(d.p);
+    const raw* __restrict__ g = static_cast<const raw*>(d.g);
+    const int64_t n = d.n;
+    const int64_t start = static_cast<int64_t>(__builtin_amdgcn_readfirstlane(it.chunk)) * chunk;
+    const int64_t end = (n - start < chunk) ? n : start + chunk;
+    const bool vec = d.vec_ok != 0;
+    for (int64_t e0 = start + 4 * static_cast<int64_t>(lane); e0 < end; e0 += 4 * kWave) {
+        float pv[4], gv[4] = {1.0f, 1.0f, 1.0f, 1.0f}, mv[4], vv[4], m2v[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+        load4s<S>(p, e0, n, vec, pv);
+        if (sc.skip_zeros) load4s<S>(g, e0, n, vec, gv);
+        load4f(d.s1, e0, n, vec, mv);
+        load4f(d.s2, e0, n, vec, vv);
+        if constexpr (KIND == kAdemamix) load4f(d.s1 + n, e0, n, vec, m2v);
+        raw out[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const float dir = direction<KIND>(mv[j], vv[j], m2v[j], sc);
+            const float pn = step_param(pv[j], dir, sc.decay, lr);
+            const bool keep = sc.skip_zeros && gv[j] == 0.0f;
+            out[j] = keep ? S::narrow(pv[j]) : S::narrow(pn);
+        }
+        store4s<S>(p, e0, n, vec, out);
     }
 }
 
@@ -498,6 +586,8 @@ template <int KIND, typename S>
 const void* pick_clip(int pass, int unroll)
 {
     if (pass == 1) return reinterpret_cast<const void*>(&k_clip_moments<KIND, S>);
+    if (pass == 11) return reinterpret_cast<const void*>(&k_clip_moments_multi<KIND, S>);
+    if (pass == 13) return reinterpret_cast<const void*>(&k_clip_apply_multi<KIND, S>);
     switch (unroll) {
     case 1: return reinterpret_cast<const void*>(&k_clip_apply<KIND, S, 1>);
     case 2: return reinterpret_cast<const void*>(&k_clip_apply<KIND, S, 2>);
@@ -522,6 +612,7 @@ const void* pick_clip_dtype(int pass, int dtype, int unroll)
 const void* clip_kernel(int pass, int kind, int dtype, int unroll)
 {
     if (pass == 2) return reinterpret_cast<const void*>(&k_clip_finalize);
+    if (pass == 12) return reinterpret_cast<const void*>(&k_clip_finalize_multi);
     if (kind == kAdam) return pick_clip_dtype<kAdam>(pass, dtype, unroll);
     if (kind == kAdemamix) return pick_clip_dtype<kAdemamix>(pass, dtype, unroll);
     return nullptr;

@@ -16,14 +16,14 @@ from __future__ import annotations
 
 import torch
 
-from . import (DTYPES, HParams, Plan, _kind, _on_device, _raw_stream, _tensor_args, check, load,
-               state_sizes)
+from . import (DTYPES, HParams, Plan, _kind, _on_device, _raw_stream, _tensor_args, check,
+               clip_workspace, load, optimizer_update_32bit_clip, state_sizes)
 
 
 class _Collection:
     kind = "adam"
 
-    def __init__(self, params, hp: HParams, grads=None):
+    def __init__(self, params, hp: HParams, grads=None, max_unorm: float = 0.0):
         self.params = [p.data if isinstance(p, torch.nn.Parameter) else p for p in params]
         if grads is None:
             grads = []
@@ -42,6 +42,8 @@ class _Collection:
             self.state1.append(torch.zeros(n1, dtype=torch.float32, device=p.device))
             self.state2.append(torch.zeros(n2, dtype=torch.float32, device=p.device))
         self.step_count = 0
+        self.max_unorm = float(max_unorm)
+        self._workspace = None
         self._direct = None
         self.plan = Plan(self.kind, list(zip(self.params, self.grads, self.state1, self.state2)))
 
@@ -50,9 +52,15 @@ class _Collection:
 
     @torch.no_grad()
     def step(self, graph: bool = False, stream=None) -> None:
-        """One step of the whole collection: plan launch, or graph replay."""
+        """One step of the whole collection: plan launch, or graph replay.
+        With max_unorm > 0 every tensor's update is clipped by its own norms
+        (plan path only)."""
+        if graph and self.max_unorm > 0:
+            raise ValueError("update-norm clipping runs through the plan step, not graph replay")
         self.step_count += 1
-        if graph:
+        if self.max_unorm > 0:
+            self.plan.step_clip(self.hp, self.step_count, self.max_unorm, stream)
+        elif graph:
             self.plan.graph_step(self.hp, self.step_count, stream)
         else:
             self.plan.step(self.hp, self.step_count, stream)
@@ -63,6 +71,18 @@ class _Collection:
         checked when the optimizer was built; only the step changes)."""
         self.step_count += 1
         h = self.hp
+        if self.max_unorm > 0:
+            if self._workspace is None:
+                self._workspace = clip_workspace(max(p.numel() for p in self.params),
+                                                 self.params[0].device)
+            for p, g, s1, s2 in self.segments():   # one workspace, reused in stream order
+                optimizer_update_32bit_clip(self.kind, p, g, s1, s2, step=self.step_count,
+                                            lr=h.lr, max_unorm=self.max_unorm,
+                                            workspace=self._workspace, beta1=h.beta1,
+                                            beta2=h.beta2, beta3=h.beta3, alpha=h.alpha,
+                                            eps=h.eps, weight_decay=h.weight_decay,
+                                            skip_zeros=h.skip_zeros, stream=stream)
+            return
         if self._direct is None:
             for p, g, s1, s2 in self.segments():   # full checks once
                 _tensor_args(_kind(self.kind), p, g, s1, s2)
@@ -102,9 +122,10 @@ class AdamW32(_Collection):
     kind = "adam"
 
     def __init__(self, params, lr=1e-3, betas=(0.9, 0.999), eps=1e-8, weight_decay=0.01,
-                 skip_zeros=False, grads=None):
+                 skip_zeros=False, grads=None, max_unorm=0.0):
         super().__init__(params, HParams(lr=lr, beta1=betas[0], beta2=betas[1], eps=eps,
-                                         weight_decay=weight_decay, skip_zeros=skip_zeros), grads)
+                                         weight_decay=weight_decay, skip_zeros=skip_zeros), grads,
+                         max_unorm)
 
 
 class AdEMAMix32(_Collection):
@@ -112,7 +133,7 @@ class AdEMAMix32(_Collection):
     kind = "ademamix"
 
     def __init__(self, params, lr=1e-3, betas=(0.9, 0.999, 0.9999), alpha=5.0, eps=1e-8,
-                 weight_decay=0.01, skip_zeros=False, grads=None):
+                 weight_decay=0.01, skip_zeros=False, grads=None, max_unorm=0.0):
         super().__init__(params, HParams(lr=lr, beta1=betas[0], beta2=betas[1], beta3=betas[2],
                                          alpha=alpha, eps=eps, weight_decay=weight_decay,
-                                         skip_zeros=skip_zeros), grads)
+                                         skip_zeros=skip_zeros), grads, max_unorm)

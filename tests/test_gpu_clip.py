@@ -156,3 +156,81 @@ def test_clip_large_tensor_full_compare():
     H.assert_parity(P, pr, "fp32", "p 2^26", bitwise=False)
     H.assert_parity(S1, s1r, "fp32", "m 2^26")
     H.assert_parity(S2, s2r, "fp32", "v 2^26")
+
+
+MIXED = [("fp32", 1000), ("bf16", 4096), ("fp16", 77), ("fp32", 1 << 16), ("bf16", 3),
+         ("fp16", 20000), ("fp32", 1), ("bf16", 70001), ("fp32", 2048), ("fp16", 2049)]
+
+
+@pytest.mark.parametrize("kind", ["adam", "ademamix"])
+def test_plan_clip_equals_per_tensor_clip(kind):
+    """A mixed-dtype collection: the plan's clipped step (per-tensor norms,
+    three launches per dtype group) equals optimizer_update_32bit_clip on
+    each tensor bitwise, clip factors included, and matches the oracle."""
+    import optimizer_update_amd as ou
+    orc = O.load()
+    hp = O.HParams(lr=1e-2, weight_decay=0.01, skip_zeros=True)
+    php = H.pkg_hp(hp)
+    k = 2 if kind == "ademamix" else 1
+    gen = W.rng(0, 15, 1)
+    host = [(s, W.params(n, s, gen), [W.cast_storage(np.where(gen.random(n) < 0.1, 0.0,
+                                                              gen.standard_normal(n)), s)
+                                      for _ in range(4)]) for s, n in MIXED]
+
+    def dev():
+        return [(H.to_dev(p0, s), torch.empty(p0.size, dtype=W.STORAGE_TORCH[s], device="cuda"),
+                 torch.zeros(k * p0.size, device="cuda"), torch.zeros(p0.size, device="cuda"))
+                for s, p0, _ in host]
+    a, b = dev(), dev()
+    plan = ou.Plan(kind, a)
+    ws = ou.clip_workspace(max(p0.size for _, p0, _ in host), "cuda")
+    bound = 0.3
+    last_b = []
+    for t in range(1, 5):
+        for (s, _, gs), x, y in zip(host, a, b):
+            x[1].copy_(W.to_torch(gs[t - 1], s, "cuda"))
+            y[1].copy_(W.to_torch(gs[t - 1], s, "cuda"))
+        plan.step_clip(php, t, bound)
+        last_b = []
+        for (s, _, _), y in zip(host, b):
+            ou.optimizer_update_32bit_clip(kind, *y, step=t, lr=hp.lr, weight_decay=hp.weight_decay,
+                                           skip_zeros=True, max_unorm=bound, workspace=ws)
+            last_b.append(ou.clip_scale(ws))
+    torch.cuda.synchronize()
+    fa = plan.clip_factors()
+    assert fa == last_b, (fa, last_b)
+    assert min(fa) < 1.0
+    for i, ((s, p0, gs), x, y) in enumerate(zip(host, a, b)):
+        for j in (0, 2, 3):
+            assert W.from_torch(x[j]).tobytes() == W.from_torch(y[j]).tobytes(), (kind, i, j)
+        pr = p0.copy()
+        s1r, s2r = W.zero_states(p0.size, kind)
+        for t in range(1, 5):
+            orc.update_f32_clip(H.KIND[kind], H.DT[s], pr, gs[t - 1], s1r, s2r, hp, t, bound)
+        H.assert_parity(W.from_torch(x[0]), pr, s, f"p {i}", bitwise=False)
+        H.assert_parity(W.from_torch(x[2]), s1r, "fp32", f"s1 {i}")
+        H.assert_parity(W.from_torch(x[3]), s2r, "fp32", f"s2 {i}")
+    plan.close()
+
+
+def test_collection_optimizer_clip_plan_equals_per_tensor():
+    """AdEMAMix32(max_unorm=...): plan steps and per-tensor steps agree bitwise."""
+    import optimizer_update_amd as ou
+    gen = W.rng(0, 16, 0)
+    sizes = [1024, 4096, 16384, 1 << 20, 33]
+    ps = [W.params(n, "bf16", gen) for n in sizes]
+    gs = [W.grads(n, "normal", "bf16", gen, sigma=0.01) for n in sizes]
+    mk = lambda: ou.AdEMAMix32([H.to_dev(p, "bf16") for p in ps], lr=1e-3, weight_decay=0.01,
+                               grads=[H.to_dev(g, "bf16") for g in gs], max_unorm=1e-3)
+    x, y = mk(), mk()
+    for _ in range(5):
+        x.step()
+        y.step_per_tensor()
+    torch.cuda.synchronize()
+    for u, v in zip(x.params + x.state1 + x.state2, y.params + y.state1 + y.state2):
+        assert W.from_torch(u).tobytes() == W.from_torch(v).tobytes()
+    assert min(x.plan.clip_factors()) < 1.0
+    with pytest.raises(ValueError):
+        x.step(graph=True)
+    x.close()
+    y.close()
