@@ -520,10 +520,10 @@ int plan_launch_clip(ou_plan_s* plan, const StepScalars& sc, float max_unorm, hi
         float mu = max_unorm, lr = sc.lr;
         void* a1[] = {const_cast<SegDesc**>(&g.d_segs), const_cast<WorkItem**>(&g.d_clip_items), &s,
                       &g.d_partials};
-        hipError_t e = launch(f1, g.n_clip_items, kClipThreadsHost, g.L.lds, a1, stream);
+        hipError_t e = launch(f1, g.n_clip_items, kClipThreadsHost, 0, a1, stream);
         if (e != hipSuccess) return hip_fail(e, "launch clip pass 1 (collection)");
         void* a2[] = {const_cast<SegDesc**>(&g.d_segs), &g.d_partials, &mu, &lr, &g.d_seg_out};
-        e = launch(f2, g.n_segs, kClipThreadsHost, 0, a2, stream);
+        e = launch(f2, g.n_segs, kClipFinalThreadsHost, 0, a2, stream);
         if (e != hipSuccess) return hip_fail(e, "launch clip pass 2 (collection)");
         const float* seg_out = g.d_seg_out;
         void* a3[] = {const_cast<SegDesc**>(&g.d_segs), const_cast<WorkItem**>(&g.d_items), &g.n_items,
@@ -651,12 +651,14 @@ int optimizer_update_32bit_clip(int kind, int dtype, void* param, const void* gr
     hipStream_t hs = static_cast<hipStream_t>(stream);
     const void* cp = param;
     void* a1[] = {&cp, const_cast<void**>(&grad), &state1, &state2, &n, &sc, &vec_ok, &partials};
-    const int lds1 = chunks >= 8LL * dp->cu_count ? lds_cap(*dp, 2) : 0;
+    // pass 1 ends in a block barrier: it runs best at full occupancy
+    int lds1 = 0;
+    if (int c = g_force_lds.load()) lds1 = c < 0 ? 0 : c;
     hipError_t e = launch(f1, chunks, kClipThreadsHost, lds1, a1, hs);
     if (e != hipSuccess) return hip_fail(e, "launch clip pass 1");
     float lr_arg = lr;
     void* a2[] = {&partials, const_cast<int64_t*>(&chunks), &max_unorm, &lr_arg, &out};
-    e = launch(f2, 1, kClipThreadsHost, 0, a2, hs);
+    e = launch(f2, 1, kClipFinalThreadsHost, 0, a2, hs);
     if (e != hipSuccess) return hip_fail(e, "launch clip pass 2");
     const float* lr_eff = out;
     void* a3[] = {&param, const_cast<void**>(&grad), &state1, &state2, &n, &sc, &vec_ok, &lr_eff};

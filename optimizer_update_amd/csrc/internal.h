@@ -69,7 +69,8 @@ const void* multi_kernel(int kind, int dtype, int epl, int unroll);
 // 11, 12, 13: the same passes over a plan's collection.
 const void* clip_kernel(int pass, int kind, int dtype, int unroll);
 constexpr int kClipChunkElems = 2048;   // elements per partial-norm chunk
-constexpr int kClipThreadsHost = 256;   // threads of passes 1 and 2
+constexpr int kClipThreadsHost = 256;   // threads of pass 1
+constexpr int kClipFinalThreadsHost = 1024;   // threads of pass 2
 
 constexpr int kWave = 64;
 

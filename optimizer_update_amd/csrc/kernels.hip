@@ -256,9 +256,11 @@ k_multi(const SegDesc* __restrict__ segs, const WorkItem* __restrict__ items, in
 constexpr int kClipThreads = 256;
 constexpr int kClipChunk = 2048;   // = kClipThreads * 2 groups * 4 elements
 
-// Sum of (a, b) over a 256-thread block in a fixed order: an xor butterfly
-// inside each wave (partners add the same two values, so every lane ends
-// with the same sum), then the four wave sums as (w0 + w1) + (w2 + w3).
+// Sum of (a, b) over a block of NW waves in a fixed order: an xor
+// butterfly inside each wave (partners add the same two values, so every
+// lane ends with the same sum), then the wave sums as a balanced pairwise
+// tree (w0 + w1) + (w2 + w3) ...  lds holds NW entries.
+template <int NW>
 __device__ __forceinline__ double2 block_sum2(double a, double b, double2* lds)
 {
 #pragma unroll
@@ -269,73 +271,26 @@ __device__ __forceinline__ double2 block_sum2(double a, double b, double2* lds)
     const int wave = static_cast<int>(threadIdx.x) / kWave;
     if (threadIdx.x % kWave == 0) lds[wave] = make_double2(a, b);
     __syncthreads();
-    return make_double2((lds[0].x + lds[1].x) + (lds[2].x + lds[3].x),
-                        (lds[0].y + lds[1].y) + (lds[2].y + lds[3].y));
-}
-
-// Four consecutive elements starting at e0 (e0 % 4 == 0): one 16/8-byte
-// access when `vec` and all four exist, else element by element.
-template <typename S>
-__device__ __forceinline__ void load4s(const typename S::raw* base, int64_t e0, int64_t n, bool vec,
-                                       float out[4])
-{
-    constexpr int DW = 4 * S::bytes / 4;
-    if (vec && e0 + 3 < n) {
-        const Words<DW> w = load_words<DW>(base + e0);
+    double2 v[NW];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) out[j] = S::widen(get_raw<S>(w, j));
-    } else {
+    for (int w = 0; w < NW; ++w) v[w] = lds[w];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) out[j] = (e0 + j < n) ? S::widen(base[e0 + j]) : 0.0f;
-    }
-}
-
-__device__ __forceinline__ void load4f(const float* base, int64_t e0, int64_t n, bool vec, float out[4])
-{
-    if (vec && e0 + 3 < n) {
-        const Words<4> w = load_words<4>(base + e0);
+    for (int width = 1; width < NW; width *= 2)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) out[j] = __builtin_bit_cast(float, w.w[j]);
-    } else {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) out[j] = (e0 + j < n) ? base[e0 + j] : 0.0f;
-    }
-}
-
-__device__ __forceinline__ void store4f(float* base, int64_t e0, int64_t n, bool vec, const float v[4])
-{
-    if (vec && e0 + 3 < n) {
-        Words<4> w;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) w.w[j] = __builtin_bit_cast(uint32_t, v[j]);
-        store_words<4>(base + e0, w);
-    } else {
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-            if (e0 + j < n) base[e0 + j] = v[j];
-    }
-}
-
-template <typename S>
-__device__ __forceinline__ void store4s(typename S::raw* base, int64_t e0, int64_t n, bool vec,
-                                        const typename S::raw v[4])
-{
-    constexpr int DW = 4 * S::bytes / 4;
-    if (vec && e0 + 3 < n) {
-        Words<DW> w;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) set_raw<S>(w, j, v[j]);
-        store_words<DW>(base + e0, w);
-    } else {
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-            if (e0 + j < n) base[e0 + j] = v[j];
-    }
+        for (int w = 0; w + width < NW; w += 2 * width) {
+            v[w].x += v[w + width].x;
+            v[w].y += v[w + width].y;
+        }
+    return v[0];
 }
 
 // Pass 1 body for one chunk: thread t owns the elements
 // chunk*2048 + h*1024 + 4t + j (h = 0, 1; j = 0..3) and adds their u^2 and
 // p^2 in that order; returns the block's sums (same value in every thread).
+// A chunk that lies wholly inside a 16-byte-aligned tensor is moved with
+// 16-byte accesses, all loads issued before any arithmetic; the last,
+// partial chunk (and unaligned tensors) go element by element.  Both paths
+// add in the same order.
 template <int KIND, typename S>
 __device__ __forceinline__ double2 clip_chunk(const typename S::raw* __restrict__ p,
                                               const typename S::raw* __restrict__ g,
@@ -343,30 +298,86 @@ __device__ __forceinline__ double2 clip_chunk(const typename S::raw* __restrict_
                                               int64_t n, const StepScalars& sc, bool vec_ok,
                                               int64_t chunk, double2* lds)
 {
+    constexpr int SDW = 4 * S::bytes / 4;
+    const int64_t first = chunk * kClipChunk + 4 * static_cast<int64_t>(threadIdx.x);
+    const bool full = vec_ok && (chunk + 1) * kClipChunk <= n;
+    float pv[2][4], gv[2][4], mv[2][4], vv[2][4], m2v[2][4];
+    if (full) {
+        Words<SDW> wp[2], wg[2];
+        Words<4> wm[2], wv[2], wm2[2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int64_t e0 = first + h * (kClipChunk / 2);
+            wp[h] = load_words<SDW>(p + e0);
+            wg[h] = load_words<SDW>(g + e0);
+            wm[h] = load_words<4>(s1 + e0);
+            wv[h] = load_words<4>(s2 + e0);
+            if constexpr (KIND == kAdemamix) wm2[h] = load_words<4>(s1 + n + e0);
+        }
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                pv[h][j] = S::widen(get_raw<S>(wp[h], j));
+                gv[h][j] = S::widen(get_raw<S>(wg[h], j));
+                mv[h][j] = __builtin_bit_cast(float, wm[h].w[j]);
+                vv[h][j] = __builtin_bit_cast(float, wv[h].w[j]);
+                m2v[h][j] = (KIND == kAdemamix) ? __builtin_bit_cast(float, wm2[h].w[j]) : 0.0f;
+            }
+    } else {
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int64_t e = first + h * (kClipChunk / 2) + j;
+                const bool in = e < n;
+                pv[h][j] = in ? S::widen(p[e]) : 0.0f;
+                gv[h][j] = in ? S::widen(g[e]) : 0.0f;
+                mv[h][j] = in ? s1[e] : 0.0f;
+                vv[h][j] = in ? s2[e] : 0.0f;
+                m2v[h][j] = (KIND == kAdemamix && in) ? s1[n + e] : 0.0f;
+            }
+    }
     double usq = 0.0, psq = 0.0;
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-        const int64_t e0 = chunk * kClipChunk + h * (kClipChunk / 2) + 4 * static_cast<int64_t>(threadIdx.x);
-        float pv[4], gv[4], mv[4], vv[4], m2v[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-        load4s<S>(p, e0, n, vec_ok, pv);
-        load4s<S>(g, e0, n, vec_ok, gv);
-        load4f(s1, e0, n, vec_ok, mv);
-        load4f(s2, e0, n, vec_ok, vv);
-        if constexpr (KIND == kAdemamix) load4f(s1 + n, e0, n, vec_ok, m2v);
+    for (int h = 0; h < 2; ++h)
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            if (e0 + j >= n) continue;
-            psq += static_cast<double>(pv[j]) * static_cast<double>(pv[j]);
-            if (sc.skip_zeros && gv[j] == 0.0f) continue;
-            update_moments<KIND>(gv[j], mv[j], vv[j], m2v[j], sc);
-            const float u = direction<KIND>(mv[j], vv[j], m2v[j], sc);
+            if (first + h * (kClipChunk / 2) + j >= n) continue;
+            psq += static_cast<double>(pv[h][j]) * static_cast<double>(pv[h][j]);
+            if (sc.skip_zeros && gv[h][j] == 0.0f) continue;
+            update_moments<KIND>(gv[h][j], mv[h][j], vv[h][j], m2v[h][j], sc);
+            const float u = direction<KIND>(mv[h][j], vv[h][j], m2v[h][j], sc);
             usq += static_cast<double>(u) * static_cast<double>(u);
         }
-        store4f(s1, e0, n, vec_ok, mv);
-        store4f(s2, e0, n, vec_ok, vv);
-        if constexpr (KIND == kAdemamix) store4f(s1 + n, e0, n, vec_ok, m2v);
+    if (full) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int64_t e0 = first + h * (kClipChunk / 2);
+            Words<4> wm, wv, wm2;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                wm.w[j] = __builtin_bit_cast(uint32_t, mv[h][j]);
+                wv.w[j] = __builtin_bit_cast(uint32_t, vv[h][j]);
+                wm2.w[j] = __builtin_bit_cast(uint32_t, m2v[h][j]);
+            }
+            store_words<4>(s1 + e0, wm);
+            store_words<4>(s2 + e0, wv);
+            if constexpr (KIND == kAdemamix) store_words<4>(s1 + n + e0, wm2);
+        }
+    } else {
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int64_t e = first + h * (kClipChunk / 2) + j;
+                if (e >= n) continue;
+                s1[e] = mv[h][j];
+                s2[e] = vv[h][j];
+                if constexpr (KIND == kAdemamix) s1[n + e] = m2v[h][j];
+            }
     }
-    return block_sum2(usq, psq, lds);
+    return block_sum2<kClipThreads / kWave>(usq, psq, lds);
 }
 
 // Pass 1, one tensor: one block per chunk (grid = number of chunks).
@@ -398,19 +409,34 @@ k_clip_moments_multi(const SegDesc* __restrict__ segs, const WorkItem* __restric
     if (threadIdx.x == 0) partials[d.clip_base + chunk] = tot;
 }
 
-// Pass 2 body: thread t adds the partials of chunks t, t + 256, ... in
-// order, then the block sum.  out[0] = fl32(lr * s), out[1] = s with
+// Pass 2 body (kFinalThreads threads): thread t adds the partials of
+// chunks t, t + kFinalThreads, ... in order (kAhead loads in flight), then
+// the block sum.  out[0] = fl32(lr * s), out[1] = s with
 // s = min(1, max_unorm * ||p|| / ||u||) (1 when ||u|| = 0).
+constexpr int kFinalThreads = 1024;
+
 __device__ __forceinline__ void clip_finalize(const double2* __restrict__ partials, int64_t nchunks,
                                               float max_unorm, float lr, float* __restrict__ out,
                                               double2* lds)
 {
     double usq = 0.0, psq = 0.0;
-    for (int64_t c = threadIdx.x; c < nchunks; c += kClipThreads) {
+    constexpr int kAhead = 16;
+    int64_t c = threadIdx.x;
+    for (; c + (kAhead - 1) * kFinalThreads < nchunks; c += kAhead * kFinalThreads) {
+        double2 v[kAhead];
+#pragma unroll
+        for (int k = 0; k < kAhead; ++k) v[k] = partials[c + k * kFinalThreads];
+#pragma unroll
+        for (int k = 0; k < kAhead; ++k) {
+            usq += v[k].x;
+            psq += v[k].y;
+        }
+    }
+    for (; c < nchunks; c += kFinalThreads) {
         usq += partials[c].x;
         psq += partials[c].y;
     }
-    const double2 tot = block_sum2(usq, psq, lds);
+    const double2 tot = block_sum2<kFinalThreads / kWave>(usq, psq, lds);
     if (threadIdx.x == 0) {
         float s = 1.0f;
         if (max_unorm > 0.0f && tot.x > 0.0) {
@@ -423,72 +449,104 @@ __device__ __forceinline__ void clip_finalize(const double2* __restrict__ partia
 }
 
 // Pass 2, one tensor: a single block.
-__global__ void __launch_bounds__(kClipThreads)
+__global__ void __launch_bounds__(kFinalThreads)
 k_clip_finalize(const double2* __restrict__ partials, int64_t nchunks, float max_unorm, float lr,
                 float* __restrict__ out)
 {
-    __shared__ double2 lds[kClipThreads / kWave];
+    __shared__ double2 lds[kFinalThreads / kWave];
     clip_finalize(partials, nchunks, max_unorm, lr, out, lds);
 }
 
 // Pass 2, collection: one block per segment; out holds two floats per segment.
-__global__ void __launch_bounds__(kClipThreads)
+__global__ void __launch_bounds__(kFinalThreads)
 k_clip_finalize_multi(const SegDesc* __restrict__ segs, const double2* __restrict__ partials,
                       float max_unorm, float lr, float* __restrict__ out)
 {
-    __shared__ double2 lds[kClipThreads / kWave];
+    __shared__ double2 lds[kFinalThreads / kWave];
     const SegDesc d = segs[blockIdx.x];
     const int64_t nchunks = (d.n + kClipChunk - 1) / kClipChunk;
     clip_finalize(partials + d.clip_base, nchunks, max_unorm, lr, out + 2 * static_cast<int64_t>(blockIdx.x),
                   lds);
 }
 
+// The parameter step of pass 3 for 4 elements already in registers.
+template <int KIND, typename S>
+__device__ __forceinline__ void clip_step4(float pv[4], const float gv[4], const float mv[4],
+                                           const float vv[4], const float m2v[4],
+                                           const StepScalars& sc, float lr)
+{
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const float dir = direction<KIND>(mv[j], vv[j], m2v[j], sc);
+        const float pn = step_param(pv[j], dir, sc.decay, lr);
+        if (!(sc.skip_zeros && gv[j] == 0.0f)) pv[j] = pn;
+    }
+}
+
+// One element of pass 3 (tails and unaligned tensors).
+template <int KIND, typename S>
+__device__ __forceinline__ void clip_step1(typename S::raw* __restrict__ p,
+                                           const typename S::raw* __restrict__ g,
+                                           const float* __restrict__ s1, const float* __restrict__ s2,
+                                           int64_t n, int64_t i, const StepScalars& sc, float lr)
+{
+    if (sc.skip_zeros && S::widen(g[i]) == 0.0f) return;
+    const float m2 = (KIND == kAdemamix) ? s1[n + i] : 0.0f;
+    const float dir = direction<KIND>(s1[i], s2[i], m2, sc);
+    p[i] = S::narrow(step_param(S::widen(p[i]), dir, sc.decay, lr));
+}
+
 // Pass 3: the parameter step with the clipped learning rate *lr_eff, any
-// launch shape (tiles of blockDim * U groups of 4 elements, grid-stride if
-// the grid is capped).  The gradient is read only to find skipped elements.
+// launch shape: U dwordx4 groups per lane (tiles, grid-stride if the grid
+// is capped), then the ragged tail one element per lane.  The gradient is
+// read only to find skipped elements.
 template <int KIND, typename S, int U>
 __global__ void __launch_bounds__(1024)
 k_clip_apply(typename S::raw* __restrict__ p, const typename S::raw* __restrict__ g,
              const float* __restrict__ s1, const float* __restrict__ s2, int64_t n, StepScalars sc,
              int32_t vec_ok, const float* __restrict__ lr_eff)
 {
-    using raw = typename S::raw;
+    constexpr int SDW = 4 * S::bytes / 4;
     const float lr = lr_eff[0];
-    const int64_t ngroups = (n + 3) / 4;
+    const int64_t nvec = vec_ok ? n / 4 : 0;
     const int64_t bdim = blockDim.x;
     const int64_t nthreads = static_cast<int64_t>(gridDim.x) * bdim;
-    for (int64_t base = static_cast<int64_t>(blockIdx.x) * bdim * U + threadIdx.x; base < ngroups;
+    for (int64_t base = static_cast<int64_t>(blockIdx.x) * bdim * U + threadIdx.x; base < nvec;
          base += nthreads * U) {
-        float pv[U][4], gv[U][4], mv[U][4], vv[U][4], m2v[U][4];
+        Words<SDW> wp[U], wg[U];
+        Words<4> wm[U], wv[U], wm2[U];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            const int64_t e0 = 4 * (base + u * bdim);
-#pragma unroll
-            for (int j = 0; j < 4; ++j) gv[u][j] = 1.0f;
-            if (e0 >= n) continue;
-            load4s<S>(p, e0, n, vec_ok, pv[u]);
-            if (sc.skip_zeros) load4s<S>(g, e0, n, vec_ok, gv[u]);
-            load4f(s1, e0, n, vec_ok, mv[u]);
-            load4f(s2, e0, n, vec_ok, vv[u]);
-            if constexpr (KIND == kAdemamix) load4f(s1 + n, e0, n, vec_ok, m2v[u]);
+            const int64_t vi = base + u * bdim;
+            if (vi >= nvec) continue;
+            wp[u] = load_words<SDW>(p + 4 * vi);
+            if (sc.skip_zeros) wg[u] = load_words<SDW>(g + 4 * vi);
+            wm[u] = load_words<4>(s1 + 4 * vi);
+            wv[u] = load_words<4>(s2 + 4 * vi);
+            if constexpr (KIND == kAdemamix) wm2[u] = load_words<4>(s1 + n + 4 * vi);
         }
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            const int64_t e0 = 4 * (base + u * bdim);
-            if (e0 >= n) continue;
-            raw out[4];
+            const int64_t vi = base + u * bdim;
+            if (vi >= nvec) continue;
+            float pv[4], gv[4], mv[4], vv[4], m2v[4];
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                float m2j = 0.0f;
-                if constexpr (KIND == kAdemamix) m2j = m2v[u][j];
-                const float dir = direction<KIND>(mv[u][j], vv[u][j], m2j, sc);
-                const float pn = step_param(pv[u][j], dir, sc.decay, lr);
-                const bool keep = sc.skip_zeros && gv[u][j] == 0.0f;
-                out[j] = keep ? S::narrow(pv[u][j]) : S::narrow(pn);
+                pv[j] = S::widen(get_raw<S>(wp[u], j));
+                gv[j] = sc.skip_zeros ? S::widen(get_raw<S>(wg[u], j)) : 1.0f;
+                mv[j] = __builtin_bit_cast(float, wm[u].w[j]);
+                vv[j] = __builtin_bit_cast(float, wv[u].w[j]);
+                m2v[j] = (KIND == kAdemamix) ? __builtin_bit_cast(float, wm2[u].w[j]) : 0.0f;
             }
-            store4s<S>(p, e0, n, vec_ok, out);
+            clip_step4<KIND, S>(pv, gv, mv, vv, m2v, sc, lr);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) set_raw<S>(wp[u], j, S::narrow(pv[j]));
+            store_words<SDW>(p + 4 * vi, wp[u]);
         }
     }
+    for (int64_t i = 4 * nvec + static_cast<int64_t>(blockIdx.x) * bdim + threadIdx.x; i < n;
+         i += nthreads)
+        clip_step1<KIND, S>(p, g, s1, s2, n, i, sc, lr);
 }
 
 // Pass 3, collection: one wave per item of the plan's regular work list,
@@ -511,25 +569,34 @@ k_clip_apply_multi(const SegDesc* __restrict__ segs, const WorkItem* __restrict_
     const raw* __restrict__ g = static_cast<const raw*>(d.g);
     const int64_t n = d.n;
     const int64_t start = static_cast<int64_t>(__builtin_amdgcn_readfirstlane(it.chunk)) * chunk;
-    const int64_t end = (n - start < chunk) ? n : start + chunk;
-    const bool vec = d.vec_ok != 0;
-    for (int64_t e0 = start + 4 * static_cast<int64_t>(lane); e0 < end; e0 += 4 * kWave) {
-        float pv[4], gv[4] = {1.0f, 1.0f, 1.0f, 1.0f}, mv[4], vv[4], m2v[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-        load4s<S>(p, e0, n, vec, pv);
-        if (sc.skip_zeros) load4s<S>(g, e0, n, vec, gv);
-        load4f(d.s1, e0, n, vec, mv);
-        load4f(d.s2, e0, n, vec, vv);
-        if constexpr (KIND == kAdemamix) load4f(d.s1 + n, e0, n, vec, m2v);
-        raw out[4];
+    const int64_t len = (n - start < chunk) ? (n - start) : chunk;
+    constexpr int SDW = 4 * S::bytes / 4;
+    const float* __restrict__ s1 = d.s1;
+    const float* __restrict__ s2 = d.s2;
+    const int64_t nv = d.vec_ok ? len / 4 : 0;   // chunk starts are multiples of 4
+    for (int64_t j4 = lane; j4 < nv; j4 += kWave) {
+        const int64_t e0 = start + 4 * j4;
+        Words<SDW> wp = load_words<SDW>(p + e0), wg;
+        if (sc.skip_zeros) wg = load_words<SDW>(g + e0);
+        const Words<4> wm = load_words<4>(s1 + e0), wv = load_words<4>(s2 + e0);
+        Words<4> wm2;
+        if constexpr (KIND == kAdemamix) wm2 = load_words<4>(s1 + n + e0);
+        float pv[4], gv[4], mv[4], vv[4], m2v[4];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            const float dir = direction<KIND>(mv[j], vv[j], m2v[j], sc);
-            const float pn = step_param(pv[j], dir, sc.decay, lr);
-            const bool keep = sc.skip_zeros && gv[j] == 0.0f;
-            out[j] = keep ? S::narrow(pv[j]) : S::narrow(pn);
+            pv[j] = S::widen(get_raw<S>(wp, j));
+            gv[j] = sc.skip_zeros ? S::widen(get_raw<S>(wg, j)) : 1.0f;
+            mv[j] = __builtin_bit_cast(float, wm.w[j]);
+            vv[j] = __builtin_bit_cast(float, wv.w[j]);
+            m2v[j] = (KIND == kAdemamix) ? __builtin_bit_cast(float, wm2.w[j]) : 0.0f;
         }
-        store4s<S>(p, e0, n, vec, out);
+        clip_step4<KIND, S>(pv, gv, mv, vv, m2v, sc, lr);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) set_raw<S>(wp, j, S::narrow(pv[j]));
+        store_words<SDW>(p + e0, wp);
     }
+    for (int64_t i = start + 4 * nv + lane; i < start + len; i += kWave)
+        clip_step1<KIND, S>(p, g, s1, s2, n, i, sc, lr);
 }
 
 // ---- instantiation tables ---------------------------------------------------------
