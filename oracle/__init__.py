@@ -30,8 +30,11 @@ SOURCE = os.path.join(HERE, "oracle.c")
 LIBRARY = os.path.join(HERE, "liboracle.so")
 
 ADAM, ADEMAMIX = 0, 1
+MOMENTUM, RMSPROP, ADAGRAD, LION = 2, 3, 4, 5
 F32, F16, BF16 = 0, 1, 2
-KINDS = {"adam": ADAM, "ademamix": ADEMAMIX}
+KINDS = {"adam": ADAM, "ademamix": ADEMAMIX, "momentum": MOMENTUM, "rmsprop": RMSPROP,
+         "adagrad": ADAGRAD, "lion": LION}
+ONE_STATE = (MOMENTUM, RMSPROP, ADAGRAD, LION)
 DTYPES = {"fp32": F32, "fp16": F16, "bf16": BF16}
 
 # -O2 without contraction or fast-math: each C operation is one correctly
@@ -104,6 +107,11 @@ class Oracle:
                                                f64, i64, f64, ci, f64,
                                                ctypes.POINTER(ctypes.c_double)]
         lib.oracle_update_f64_clip.restype = ci
+        lib.oracle_update1_f32.argtypes = [ci, ci, vp, vp, vp, i64, f32, f32, f32, f32, i64, f32,
+                                           ci, ci]
+        lib.oracle_update1_f32.restype = ci
+        lib.oracle_update1_f64.argtypes = [ci, vp, vp, vp, i64, f64, f64, f64, f64, i64, f64, ci]
+        lib.oracle_update1_f64.restype = ci
         lib.oracle_step_scalars.argtypes = [f32, f32, f32, f32, f32, i64,
                                             ctypes.POINTER(_Scalars32)]
         lib.oracle_step_scalars.restype = None
@@ -172,6 +180,30 @@ class Oracle:
             hp.lr, int(bool(hp.skip_zeros)))
         if rc != 0:
             raise ValueError(f"oracle_update_f64 rejected kind={kind}")
+
+    def update1_f32(self, kind: int, dtype: int, param: np.ndarray, grad: np.ndarray,
+                    state1: np.ndarray, hp: HParams, step: int, nthreads: int = 1) -> None:
+        """One step of a one-state kind, in place (see ``oracle_update1_f32``)."""
+        n = param.size
+        sdt = np.float32 if dtype == F32 else np.uint16
+        assert param.dtype == sdt and grad.dtype == sdt and grad.size == n
+        assert state1.dtype == np.float32 and state1.size == n
+        rc = self._lib.oracle_update1_f32(kind, dtype, _ptr(param), _ptr(grad), _ptr(state1), n,
+                                          hp.beta1, hp.beta2, hp.eps, hp.weight_decay, step, hp.lr,
+                                          int(bool(hp.skip_zeros)), nthreads)
+        if rc != 0:
+            raise ValueError(f"oracle_update1_f32 rejected kind={kind} dtype={dtype}")
+
+    def update1_f64(self, kind: int, param: np.ndarray, grad: np.ndarray, state1: np.ndarray,
+                    hp: HParams, step: int) -> None:
+        """One binary64 step of a one-state kind, in place."""
+        for a in (param, grad, state1):
+            assert a.dtype == np.float64 and a.flags.c_contiguous and a.size == param.size
+        rc = self._lib.oracle_update1_f64(kind, _ptr(param), _ptr(grad), _ptr(state1), param.size,
+                                          hp.beta1, hp.beta2, hp.eps, hp.weight_decay, step, hp.lr,
+                                          int(bool(hp.skip_zeros)))
+        if rc != 0:
+            raise ValueError(f"oracle_update1_f64 rejected kind={kind}")
 
     def update_f32_clip(self, kind: int, dtype: int, param: np.ndarray, grad: np.ndarray,
                         state1: np.ndarray, state2: np.ndarray, hp: HParams, step: int,

@@ -31,6 +31,10 @@
  * 754 / bfloat16 encodings: round to nearest, ties to even; overflow goes to
  * infinity; subnormals are kept; a NaN stays a quiet NaN (payload not kept).
  *
+ * oracle_update1_f32 / oracle_update1_f64 cover the one-state kinds
+ * (momentum SGD, RMSprop, Adagrad, Lion; the page implies a one-state sibling
+ * of the two-state path without naming one).
+ *
  * oracle_update_f32_clip / oracle_update_f64_clip add update-norm clipping
  * (the page's "max_unorm"; it names the option only, so the clip rule is
  * stated at the function).
@@ -51,7 +55,8 @@
 #define ORACLE_PLANT 0
 #endif
 
-enum { ORACLE_ADAM = 0, ORACLE_ADEMAMIX = 1 };
+enum { ORACLE_ADAM = 0, ORACLE_ADEMAMIX = 1,
+       ORACLE_MOMENTUM = 2, ORACLE_RMSPROP = 3, ORACLE_ADAGRAD = 4, ORACLE_LION = 5 };
 enum { ORACLE_F32 = 0, ORACLE_F16 = 1, ORACLE_BF16 = 2 };
 
 static float f32_from_bits(uint32_t u) { float f; memcpy(&f, &u, sizeof f); return f; }
@@ -387,6 +392,136 @@ int oracle_update_f64(int kind, double* param, const double* grad, double* state
         state1[i] = m;
         state2[i] = v;
         if (kind == ORACLE_ADEMAMIX) state1[slow] = m2;
+    }
+    return 0;
+}
+
+/* ------------------------------------------------------ one-state kinds */
+
+/* One element of a one-state update, binary32; m is the element's state.
+ * Returns the new parameter before rounding to storage.
+ *   MOMENTUM  (SGD with momentum, Sutskever et al. 2013 / torch.optim.SGD,
+ *             dampening 0): gd = g + wd*p (L2 term, only when wd != 0);
+ *             m = gd on the first step, else beta1*m + gd; p - lr*m
+ *   RMSPROP   (Tieleman & Hinton 2012): gd as above;
+ *             m = beta1*m + (1-beta1)*(gd*gd); p - lr*(gd/(sqrt(m)+eps))
+ *   ADAGRAD   (Duchi et al. 2011): gd as above; m = m + gd*gd;
+ *             p - lr*(gd/(sqrt(m)+eps))
+ *   LION      (Chen et al. 2023): c = beta1*m + (1-beta1)*g; u = sign(c)
+ *             (0 for c = 0, NaN stays NaN); p*d - lr*u with the decoupled
+ *             decay d = fl32(1 - fl64(lr*wd)); then m = beta2*m + (1-beta2)*g */
+static float one_state_f32(int kind, float p, float g, float* m, float beta1, float beta2,
+                           float eps, float wd, float lr, float decay, int first)
+{
+    if (kind == ORACLE_LION) {
+#if ORACLE_PLANT == 18
+        *m = beta2 * (*m) + (1.0f - beta2) * g;     /* planted: moment updated before the sign */
+#endif
+        float c = beta1 * (*m) + (1.0f - beta1) * g;
+        float u = (c != c) ? c : (float)((c > 0.0f) - (c < 0.0f));
+        float pn = p * decay - lr * u;
+#if ORACLE_PLANT != 18
+        *m = beta2 * (*m) + (1.0f - beta2) * g;
+#endif
+        return pn;
+    }
+    float gd = (wd != 0.0f) ? g + wd * p : g;
+    if (kind == ORACLE_MOMENTUM) {
+#if ORACLE_PLANT == 21
+        float mn = first ? gd : beta1 * (*m) + (1.0f - beta1) * gd;   /* planted: dampening */
+#else
+        float mn = first ? gd : beta1 * (*m) + gd;
+#endif
+        *m = mn;
+        return p - lr * mn;
+    }
+#if ORACLE_PLANT == 20
+    float vn = (kind == ORACLE_RMSPROP) ? beta1 * (*m) + (1.0f - beta1) * (gd * gd)
+                                        : (*m) + fabsf(gd);                /* planted: no square */
+#else
+    float vn = (kind == ORACLE_RMSPROP) ? beta1 * (*m) + (1.0f - beta1) * (gd * gd)
+                                        : (*m) + gd * gd;
+#endif
+    *m = vn;
+#if ORACLE_PLANT == 19
+    return p - lr * (gd / sqrtf(vn + eps));       /* planted: eps inside the root */
+#else
+    return p - lr * (gd / (sqrtf(vn) + eps));
+#endif
+}
+
+/* One step of a one-state kind over n elements, in place.  state1: n
+ * floats; skip_zeros as for the two-state kinds (an element with g == 0 is
+ * left untouched).  step is 1-based (MOMENTUM starts its buffer at step 1).
+ * Returns 0, or -1 on an invalid kind or dtype. */
+int oracle_update1_f32(int kind, int dtype, void* param, const void* grad, float* state1,
+                       int64_t n, float beta1, float beta2, float eps, float weight_decay,
+                       int64_t step, float lr, int skip_zeros, int nthreads)
+{
+    if (kind < ORACLE_MOMENTUM || kind > ORACLE_LION ||
+        (dtype != ORACLE_F32 && dtype != ORACLE_F16 && dtype != ORACLE_BF16))
+        return -1;
+    float decay = (float)(1.0 - (double)lr * (double)weight_decay);
+    int first = step == 1;
+    if (nthreads < 1) nthreads = 1;
+#pragma omp parallel for schedule(static) num_threads(nthreads)
+    for (int64_t i = 0; i < n; i++) {
+        float g = load_storage(grad, dtype, i);
+        if (skip_zeros && g == 0.0f) continue;
+        float p = load_storage(param, dtype, i);
+        store_storage(param, dtype, i, one_state_f32(kind, p, g, &state1[i], beta1, beta2, eps,
+                                                     weight_decay, lr, decay, first));
+    }
+    return 0;
+}
+
+/* The one-state kinds in binary64 (fp64 arrays), for closed forms. */
+int oracle_update1_f64(int kind, double* param, const double* grad, double* state1, int64_t n,
+                       double beta1, double beta2, double eps, double weight_decay,
+                       int64_t step, double lr, int skip_zeros)
+{
+    if (kind < ORACLE_MOMENTUM || kind > ORACLE_LION)
+        return -1;
+    double decay = 1.0 - lr * weight_decay;
+    for (int64_t i = 0; i < n; i++) {
+        double g = grad[i], p = param[i], m = state1[i];
+        if (skip_zeros && g == 0.0) continue;
+        if (kind == ORACLE_LION) {
+#if ORACLE_PLANT == 18
+            m = beta2 * m + (1.0 - beta2) * g;
+#endif
+            double c = beta1 * m + (1.0 - beta1) * g;
+            double u = (c != c) ? c : (double)((c > 0.0) - (c < 0.0));
+            param[i] = p * decay - lr * u;
+#if ORACLE_PLANT == 18
+            state1[i] = m;
+#else
+            state1[i] = beta2 * m + (1.0 - beta2) * g;
+#endif
+            continue;
+        }
+        double gd = (weight_decay != 0.0) ? g + weight_decay * p : g;
+        if (kind == ORACLE_MOMENTUM) {
+#if ORACLE_PLANT == 21
+            double mn = (step == 1) ? gd : beta1 * m + (1.0 - beta1) * gd;
+#else
+            double mn = (step == 1) ? gd : beta1 * m + gd;
+#endif
+            state1[i] = mn;
+            param[i] = p - lr * mn;
+            continue;
+        }
+#if ORACLE_PLANT == 20
+        double vn = (kind == ORACLE_RMSPROP) ? beta1 * m + (1.0 - beta1) * (gd * gd) : m + fabs(gd);
+#else
+        double vn = (kind == ORACLE_RMSPROP) ? beta1 * m + (1.0 - beta1) * (gd * gd) : m + gd * gd;
+#endif
+        state1[i] = vn;
+#if ORACLE_PLANT == 19
+        param[i] = p - lr * (gd / sqrt(vn + eps));
+#else
+        param[i] = p - lr * (gd / (sqrt(vn) + eps));
+#endif
     }
     return 0;
 }

@@ -185,3 +185,27 @@ def element_step(kind: str, p: F, g: F, m: F, v: F, m2: F | None, sc: dict[str, 
     u = div(num, den)
     p = sub(mul(p, sc["decay"]), mul(lr, u))
     return p, m, v, m2, True
+
+
+def element_step1(kind: str, p: F, g: F, m: F, beta1: F, beta2: F, eps: F, wd: F, lr: F,
+                  decay: F, first: bool, skip_zeros: bool) -> tuple[F, F, bool]:
+    """One element of a one-state kind (momentum, rmsprop, adagrad, lion),
+    operation by operation; returns (p, m, written) with p in binary32."""
+    if skip_zeros and g.v == 0:
+        return p, m, False
+    one = F(Fraction(1))
+    if kind == "lion":
+        c = add(mul(beta1, m), mul(sub(one, beta1), g))
+        u = F(Fraction((c.v > 0) - (c.v < 0)))
+        pn = sub(mul(p, decay), mul(lr, u))
+        m = add(mul(beta2, m), mul(sub(one, beta2), g))
+        return pn, m, True
+    gd = add(g, mul(wd, p)) if wd.v != 0 else g
+    if kind == "momentum":
+        m = gd if first else add(mul(beta1, m), gd)
+        return sub(p, mul(lr, m)), m, True
+    if kind == "rmsprop":
+        m = add(mul(beta1, m), mul(sub(one, beta1), mul(gd, gd)))
+    else:
+        m = add(m, mul(gd, gd))
+    return sub(p, mul(lr, div(gd, add(sqrt(m), eps)))), m, True

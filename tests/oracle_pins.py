@@ -20,6 +20,7 @@ no formula.
 from __future__ import annotations
 
 import math
+from fractions import Fraction
 
 import numpy as np
 import torch
@@ -503,8 +504,171 @@ def pin_clip_realised_norm(orc):
         assert r1.tobytes() == s1.tobytes() and r2.tobytes() == s2.tobytes()
 
 
+# ------------------------------------------------------------ one-state kinds
+
+ONE_STATE_TORCH = {
+    O.MOMENTUM: lambda prm, hp: torch.optim.SGD([prm], lr=hp.lr, momentum=hp.beta1, dampening=0.0,
+                                                weight_decay=hp.weight_decay),
+    O.RMSPROP: lambda prm, hp: torch.optim.RMSprop([prm], lr=hp.lr, alpha=hp.beta1, eps=hp.eps,
+                                                   weight_decay=hp.weight_decay, momentum=0.0,
+                                                   centered=False),
+    O.ADAGRAD: lambda prm, hp: torch.optim.Adagrad([prm], lr=hp.lr, lr_decay=0.0, eps=hp.eps,
+                                                   weight_decay=hp.weight_decay,
+                                                   initial_accumulator_value=0.0),
+}
+ONE_STATE_KEY = {O.MOMENTUM: "momentum_buffer", O.RMSPROP: "square_avg", O.ADAGRAD: "sum"}
+
+
+def pin_one_state_torch(orc):
+    """Momentum SGD, RMSprop and Adagrad against torch.optim (CPU, fp32,
+    foreach off) with dyadic hyperparameters, with and without weight
+    decay, 10 steps.  torch arranges the arithmetic differently, so: p
+    within 2e-6 relative plus 1e-6 lr, the state within 1e-6 relative plus
+    an absolute floor of 1e-6 of its scale."""
+    n, T = 2048, 10
+    for kind, make in ONE_STATE_TORCH.items():
+        for wd in (0.0, 2.0 ** -7):
+            hp = O.HParams(lr=2.0 ** -10, beta1=0.875, eps=2.0 ** -27, weight_decay=wd)
+            gen = rng(25, kind, int(wd > 0))
+            p0 = gen.uniform(-1, 1, n).astype(np.float32)
+            gs = [gen.standard_normal(n).astype(np.float32) for _ in range(T)]
+            p = p0.copy()
+            s = np.zeros(n, np.float32)
+            for t in range(1, T + 1):
+                orc.update1_f32(kind, O.F32, p, gs[t - 1], s, hp, t)
+            prm = torch.nn.Parameter(torch.from_numpy(p0.copy()))
+            opt = make(prm, hp)
+            for param_group in opt.param_groups:
+                param_group["foreach"] = False
+            for t in range(T):
+                prm.grad = torch.from_numpy(gs[t].copy())
+                opt.step()
+            tp = prm.detach().numpy()
+            ts = opt.state[prm][ONE_STATE_KEY[kind]].numpy()
+            err = np.abs(p - tp)
+            assert np.all(err <= 2e-6 * np.abs(tp) + 1e-6 * hp.lr), (kind, wd, err.max())
+            scale = float(np.max(np.abs(ts)))
+            assert np.all(np.abs(s - ts) <= 1e-6 * np.abs(ts) + 1e-6 * scale), (kind, wd)
+
+
+def pin_one_state_closed_form_f64(orc):
+    """Constant gradient g, zero state, binary64:
+    momentum (wd 0): m_t = g (1 - b^t)/(1 - b), p_t = p0 - lr sum_k m_k;
+    RMSprop (wd 0):  v_t = (1 - b^t) g^2, p_t = p0 - lr sum_k g/(sqrt(1-b^k)|g| + eps);
+    Adagrad (wd 0):  v_t = t g^2,         p_t = p0 - lr sum_k g/(sqrt(k)|g| + eps);
+    Lion:            m_t = (1 - b2^t) g and c_t has the sign of g, so
+                     p_t = d p_(t-1) - lr sign(g) with d = 1 - lr wd."""
+    g = np.array([1.0, -0.5, 3e-3, -2.5e-6, 7.0], np.float64)
+    p0 = np.array([0.5, -0.25, 0.125, 0.9, -0.75], np.float64)
+    T = 300
+    b, b2, eps, lr = 0.9, 0.99, 1e-8, 1e-3
+    for kind in O.ONE_STATE:
+        for wd in ((0.0, 0.1) if kind == O.LION else (0.0,)):
+            hp = O.HParams(lr=lr, beta1=b, beta2=b2, eps=eps, weight_decay=wd)
+            p = p0.copy()
+            s = np.zeros_like(g)
+            ref = p0.copy()
+            for t in range(1, T + 1):
+                orc.update1_f64(kind, p, g, s, hp, t)
+                if kind == O.MOMENTUM:
+                    m_ref = g * (1 - b ** t) / (1 - b)
+                    ref = ref - lr * m_ref
+                elif kind == O.RMSPROP:
+                    m_ref = (1 - b ** t) * g * g
+                    ref = ref - lr * g / (np.sqrt(1 - b ** t) * np.abs(g) + eps)
+                elif kind == O.ADAGRAD:
+                    m_ref = t * g * g
+                    ref = ref - lr * g / (np.sqrt(t) * np.abs(g) + eps)
+                else:
+                    m_ref = (1 - b2 ** t) * g
+                    ref = ref * (1 - lr * wd) - lr * np.sign(g)
+                assert np.allclose(s, m_ref, rtol=1e-12, atol=0), (kind, wd, t)
+                assert np.all(np.abs(p - ref) <= 1e-12 * (np.abs(p0) + t * lr * 10)), (kind, wd, t)
+
+
+def pin_one_state_zero_gradient(orc):
+    """Zero gradient, zero state: momentum, RMSprop and Adagrad leave p
+    unchanged when wd = 0 (their step is 0 / (0 + eps) = 0 or lr * 0); Lion
+    applies only the decay (sign(0) = 0); skip_zeros leaves everything
+    untouched, also for -0 gradients and wd > 0."""
+    n = 100
+    p0 = rng(27, 0).uniform(-1, 1, n).astype(np.float32)
+    for kind in O.ONE_STATE:
+        for grad in (np.zeros(n, np.float32), np.full(n, -0.0, np.float32)):
+            p = p0.copy()
+            s = np.zeros(n, np.float32)
+            orc.update1_f32(kind, O.F32, p, grad, s, O.HParams(weight_decay=0.0, lr=0.1), 1)
+            assert p.tobytes() == p0.tobytes() and not np.any(s), kind
+            p = p0.copy()
+            orc.update1_f32(kind, O.F32, p, grad, s, O.HParams(weight_decay=0.5, lr=0.1,
+                                                                skip_zeros=True), 3)
+            assert p.tobytes() == p0.tobytes() and not np.any(s), kind
+        p = p0.copy()
+        s = np.zeros(n, np.float32)
+        orc.update1_f32(O.LION, O.F32, p, np.zeros(n, np.float32), s,
+                        O.HParams(weight_decay=0.5, lr=0.1), 1)
+        d = np.float32(1.0 - 0.1 * float(np.float32(0.5)))
+        assert p.tobytes() == ((p0 * d) - np.float32(0.1) * np.float32(0.0)).tobytes()
+
+
+def pin_lion_by_hand(orc):
+    """Lion's sign uses the interpolation c = b1 m + (1 - b1) g of the *old*
+    moment; the moment is updated after (Chen et al. 2023, Algorithm 2).
+    By hand, b1 0.9, b2 0.99, lr 0.1, p0 0.5: g1 = 1 gives c = 0.1 > 0,
+    p1 = 0.4, m1 = 0.01; g2 = -0.085 gives c = 0.009 - 0.0085 = 0.0005 > 0,
+    p2 = 0.3, m2 = 0.0099 - 0.00085 = 0.00905 (1 - b2 in binary32 is
+    0.0099999905, hence the 1e-7 bound on m).  (Updating m first would give
+    c = 0.00891 - 0.009265 < 0 and p2 = 0.5.)"""
+    hp = O.HParams(lr=0.1, beta1=0.9, beta2=0.99, weight_decay=0.0)
+    p = np.array([0.5], np.float32)
+    m = np.zeros(1, np.float32)
+    orc.update1_f32(O.LION, O.F32, p, np.array([1.0], np.float32), m, hp, 1)
+    assert abs(p[0] - 0.4) <= 1e-7 and abs(m[0] - 0.01) <= 1e-7, (p, m)
+    orc.update1_f32(O.LION, O.F32, p, np.array([-0.085], np.float32), m, hp, 2)
+    assert abs(p[0] - 0.3) <= 1e-7 and abs(m[0] - 0.00905) <= 1e-7, (p, m)
+
+
+def pin_exact_emulation_one_state(orc):
+    """Rounding of the one-state kinds: 10 steps on a few elements, every
+    storage, with and without weight decay and skip_zeros, bitwise equal to
+    the same operations each rounded once (tests/exact_fp32.py)."""
+    n, T = 5, 10
+    gen = rng(29, 0)
+    names = {O.MOMENTUM: "momentum", O.RMSPROP: "rmsprop", O.ADAGRAD: "adagrad", O.LION: "lion"}
+    for kind, kname in names.items():
+        for sname, dtype in (("fp32", O.F32), ("fp16", O.F16), ("bf16", O.BF16)):
+            for wd, skip in ((0.0, False), (0.01, True)):
+                hp = O.HParams(lr=1e-2, beta1=0.9, beta2=0.99, eps=1e-8, weight_decay=wd,
+                               skip_zeros=skip)
+                p = cast_storage(gen.uniform(-1, 1, n).astype(np.float32), sname)
+                gsteps = [cast_storage(np.where(gen.random(n) < 0.2, 0.0, gen.standard_normal(n)).astype(np.float32), sname)
+                          for _ in range(T)]
+                f32 = lambda x: float(np.float32(x))
+                pv = [X.F.of(float(x)) for x in _storage_value(p, sname)]
+                mv = [X.F.of(0.0) for _ in range(n)]
+                b1, b2, ep, w, lr = (X.F.of(f32(x)) for x in (hp.beta1, hp.beta2, hp.eps, hp.weight_decay, hp.lr))
+                decay = X.rnd(X.f64(1 - X.f64(Fraction(f32(hp.lr)) * Fraction(f32(hp.weight_decay)))), False)
+                po = p.copy()
+                so = np.zeros(n, np.float32)
+                for t in range(1, T + 1):
+                    gv = _storage_value(gsteps[t - 1], sname)
+                    for i in range(n):
+                        pn, mv[i], wrote = X.element_step1(kname, pv[i], X.F.of(float(gv[i])), mv[i],
+                                                           b1, b2, ep, w, lr, decay, t == 1, skip)
+                        if wrote:
+                            pv[i] = X.to_storage(pn, sname)
+                    orc.update1_f32(kind, dtype, po, gsteps[t - 1], so, hp, t)
+                    got = _storage_value(po, sname)
+                    for i in range(n):
+                        ctx = (kname, sname, wd, skip, t, i)
+                        assert pv[i].bits_equal(float(got[i])), ("p", ctx, float(pv[i]), got[i])
+                        assert mv[i].bits_equal(float(so[i])), ("m", ctx, float(mv[i]), so[i])
+
+
 INDEPENDENT = [pin_closed_form_f64, pin_f32_tracks_f64, pin_first_step_by_hand,
                pin_torch_adam, pin_zero_gradient, pin_ademamix_reduces_to_adam,
                pin_element_independence, pin_grad_unchanged, pin_conversions_sample,
-               pin_clip_reduces_to_plain, pin_clip_closed_form_f64, pin_clip_realised_norm]
-ALL = INDEPENDENT + [pin_exact_emulation]
+               pin_clip_reduces_to_plain, pin_clip_closed_form_f64, pin_clip_realised_norm,
+               pin_one_state_torch, pin_one_state_closed_form_f64, pin_one_state_zero_gradient,
+               pin_lion_by_hand]
+ALL = INDEPENDENT + [pin_exact_emulation, pin_exact_emulation_one_state]

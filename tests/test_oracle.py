@@ -33,7 +33,7 @@ def test_conversion_strided_sweep(orc):
             P.check_conversions(orc, bits.astype(np.uint32))
 
 
-@pytest.mark.parametrize("plant", range(1, 18))
+@pytest.mark.parametrize("plant", range(1, 22))
 def test_planted_mistake_is_caught(plant, tmp_path):
     """A copy of the oracle with one planted mistake (dropped bias
     correction, eps inside the root, decay after the update, decay sign,
@@ -41,7 +41,10 @@ def test_planted_mistake_is_caught(plant, tmp_path):
     skipped elements, dropped square, written gradient, bf16 truncation,
     no fp16 subnormals, step off by one, reversed slow plane; for clipping:
     norm of the new parameter, squared update norm, clipping below the
-    bound) must fail at least one pin that does not retype the formulas."""
+    bound; one-state kinds: Lion's moment updated before its sign, eps
+    inside RMSprop's root, Adagrad without the square, momentum with
+    dampening) must fail at least one pin that does not retype the
+    formulas."""
     path = O.build(str(tmp_path / f"liboracle_plant{plant}.so"), plant=plant)
     bad = O.Oracle(path)
     assert bad.planted == plant
