@@ -87,11 +87,17 @@ def main():
         p = torch.empty(n, device=dev).uniform_(-1.0, 1.0, generator=gen).to(W.STORAGE_TORCH[storage])
         g = (torch.randn(n, device=dev, generator=gen) * 1e-3).to(W.STORAGE_TORCH[storage])
         s1n, s2n = ou.state_sizes(kind, n)
-        return p, g, torch.zeros(s1n, device=dev), torch.zeros(s2n, device=dev)
+        return (p, g, torch.zeros(s1n, device=dev),
+                torch.zeros(s2n, device=dev) if s2n else None)
 
     hp_adam = ou.HParams(lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.0)
     hp_mix = ou.HParams(lr=1e-3, beta1=0.9, beta2=0.999, beta3=0.9999, alpha=5.0, eps=1e-8,
                         weight_decay=0.01)
+    hp_kind = {"adam": hp_adam, "ademamix": hp_mix,
+               "momentum": ou.HParams(lr=1e-2, beta1=0.9, beta2=0.0, eps=0.0, weight_decay=0.0),
+               "rmsprop": ou.HParams(lr=1e-2, beta1=0.99, beta2=0.0, eps=1e-8, weight_decay=0.0),
+               "adagrad": ou.HParams(lr=1e-2, beta1=0.0, beta2=0.0, eps=1e-10, weight_decay=0.0),
+               "lion": ou.HParams(lr=1e-4, beta1=0.9, beta2=0.99, eps=0.0, weight_decay=0.1)}
 
     def flat_stepper(kind, tensors, hp):
         p, g, s1, s2 = tensors
@@ -157,7 +163,7 @@ def main():
     kind, storage, log2n = args.case.split(":")
     n = 1 << int(log2n)
     bpe = W.bytes_per_element(kind, storage)
-    hp_head = hp_adam if kind == "adam" else hp_mix
+    hp_head = hp_kind[kind]
     head = make_flat(kind, storage, n, seed=0)
     ms, wall_ms = time_exact(flat_stepper(kind, head, hp_head), args.steps, args.warmup)
     gbs = bpe * n / (ms * 1e-3) / 1e9
@@ -197,9 +203,9 @@ def main():
         del src, dst
         torch.cuda.empty_cache()
         for ck, cs, cl in (("adam", "bf16", 28), ("ademamix", "fp32", 28), ("ademamix", "bf16", 28),
-                           ("adam", "fp32", 30)):
+                           ("adam", "fp32", 30), ("lion", "fp32", 28), ("momentum", "bf16", 28)):
             cn = 1 << cl
-            hp = hp_adam if ck == "adam" else hp_mix
+            hp = hp_kind[ck]
             ts = make_flat(ck, cs, cn, seed=cl)
             r = time_rounds(flat_stepper(ck, ts, hp), iters=10 if cl == 28 else 4)
             b = W.bytes_per_element(ck, cs)

@@ -29,7 +29,7 @@
  *
  * Layout:  param, grad: n elements of the storage dtype.  state1: n floats
  * (ADAM) or 2n floats (ADEMAMIX: fast EMA at [0,n), slow EMA at [n,2n)).
- * state2: n floats.  All pointers are device pointers on the current HIP
+ * state2: n floats (two-state kinds only).  All pointers are device pointers on the current HIP
  * device and must be aligned to their element size.  16-byte alignment of
  * all streams selects the dwordx4 path; any other alignment runs the same
  * arithmetic one element per lane (results are bitwise identical).
@@ -59,7 +59,29 @@ extern "C" {
 #endif
 
 typedef enum { OU_F32 = 0, OU_F16 = 1, OU_BF16 = 2 } ou_dtype;
-typedef enum { OU_ADAM = 0, OU_ADEMAMIX = 1 } ou_kind;
+/* Kinds.  ADAM and ADEMAMIX are the two-state update above.  The
+ * one-state kinds keep state1 only (n floats); state2 is ignored and may be
+ * NULL.  They are the textbook rules of the optimizers that the 32-bit
+ * update family of the same library also carries (per element, binary32,
+ * g' = g + weight_decay*p when weight_decay != 0, else g' = g):
+ *   OU_MOMENTUM  m = g' on step 1, else beta1*m + g';  p = p - lr*m
+ *                (heavy ball, no dampening, no Nesterov)
+ *   OU_RMSPROP   m = beta1*m + (1-beta1)*(g'*g');  p = p - lr*(g'/(sqrt(m)+eps))
+ *                (beta1 is RMSprop's smoothing constant)
+ *   OU_ADAGRAD   m = m + g'*g';  p = p - lr*(g'/(sqrt(m)+eps))
+ *   OU_LION      c = beta1*m + (1-beta1)*g;  p = p*d - lr*sign(c), sign(0) = 0;
+ *                then m = beta2*m + (1-beta2)*g  (decoupled decay d as above)
+ * skip_zeros applies to them as to the two-state kinds.  beta1 and beta2
+ * must lie in [0, 1) for every kind (pass 0 where a kind has no beta).
+ * Update-norm clipping is defined for ADAM and ADEMAMIX only. */
+typedef enum {
+    OU_ADAM = 0,
+    OU_ADEMAMIX = 1,
+    OU_MOMENTUM = 2,
+    OU_RMSPROP = 3,
+    OU_ADAGRAD = 4,
+    OU_LION = 5
+} ou_kind;
 
 enum {
     OU_OK = 0,
@@ -118,7 +140,8 @@ int optimizer_update_32bit(int kind, int dtype, void* param, const void* grad,
  * ou_clip_workspace_bytes(n) bytes, 16-byte aligned, not overlapping any
  * other buffer; it holds per-chunk partial norms and the clip factor
  * (workspace bytes [4, 8) hold s as a float after the step).  Three
- * launches on `stream`; no allocation, capture-safe. */
+ * launches on `stream`; no allocation, capture-safe.  A one-state kind with
+ * max_unorm > 0 is rejected (OU_EINVAL). */
 int64_t ou_clip_workspace_bytes(int64_t n);
 
 int optimizer_update_32bit_clip(int kind, int dtype, void* param, const void* grad,

@@ -1,4 +1,5 @@
-"""MI355X (gfx950) 32-bit two-state optimizer update: Adam/AdamW and AdEMAMix.
+"""MI355X (gfx950) 32-bit optimizer update: Adam/AdamW and AdEMAMix (two
+fp32 states), and momentum SGD, RMSprop, Adagrad and Lion (one fp32 state).
 
 Thin torch-facing binding of ``liboptimizer_update.so`` (``include/optimizer_update.h``).
 Functions carry the names of the C entry points and only marshal arguments
@@ -10,11 +11,13 @@ library, or without a GPU, calls raise.
     optimizer_update_32bit_clip(..., max_unorm=..., workspace=...)   update-norm clipping
     optimizer_update_32bit_multi(kind, segments, hp, step)
     Plan(kind, segments)  -> .step(hp, step) / .graph_step(hp, step) / .close()
-    AdamW32, AdEMAMix32    collection optimizers over a fixed parameter list
+    AdamW32, AdEMAMix32, Momentum32, RMSprop32, Adagrad32, Lion32
+                           collection optimizers over a fixed parameter list
 
 Layout: param and grad are contiguous tensors of one storage dtype
 (float32, float16 or bfloat16); state1 holds n floats (Adam) or 2n floats
-(AdEMAMix: fast EMA, then slow EMA); state2 holds n floats.
+(AdEMAMix: fast EMA, then slow EMA); state2 holds n floats for the
+two-state kinds and is None for the one-state kinds.
 """
 from __future__ import annotations
 
@@ -31,13 +34,18 @@ __all__ = ["HParams", "optimizer_update_32bit", "optimizer_update_32bit_clip",
            "optimizer_update_32bit_multi", "Plan",
            "OptimizerUpdateError", "KINDS", "DTYPES", "load", "state_sizes"]
 
-KINDS = {"adam": _lib.OU_ADAM, "ademamix": _lib.OU_ADEMAMIX}
+KINDS = {"adam": _lib.OU_ADAM, "ademamix": _lib.OU_ADEMAMIX, "momentum": _lib.OU_MOMENTUM,
+         "rmsprop": _lib.OU_RMSPROP, "adagrad": _lib.OU_ADAGRAD, "lion": _lib.OU_LION}
+TWO_STATE = (_lib.OU_ADAM, _lib.OU_ADEMAMIX)
 DTYPES = {torch.float32: _lib.OU_F32, torch.float16: _lib.OU_F16, torch.bfloat16: _lib.OU_BF16}
 
 
 @dataclass(frozen=True)
 class HParams:
-    """Step hyperparameters; beta3 and alpha are used by AdEMAMix only."""
+    """Step hyperparameters; beta3 and alpha are used by AdEMAMix only.
+    For the one-state kinds beta1 is the momentum (momentum SGD), the
+    smoothing constant (RMSprop) or Lion's interpolation beta, beta2 Lion's
+    moment beta; Adagrad uses neither."""
     lr: float = 1e-3
     beta1: float = 0.9
     beta2: float = 0.999
@@ -57,8 +65,10 @@ def _kind(kind) -> int:
 
 
 def state_sizes(kind, n: int) -> tuple[int, int]:
-    """Elements of state1 and state2 for a tensor of n elements."""
-    return (2 * n if _kind(kind) == _lib.OU_ADEMAMIX else n), n
+    """Elements of state1 and state2 for a tensor of n elements (state2 is 0
+    for the one-state kinds)."""
+    k = _kind(kind)
+    return (2 * n if k == _lib.OU_ADEMAMIX else n), (n if k in TWO_STATE else 0)
 
 
 def _raw_stream(index: int) -> int:
@@ -96,7 +106,13 @@ class _on_device:
 
 
 def _tensor_args(kind: int, param, grad, state1, state2) -> tuple[int, int]:
-    for name, t in (("param", param), ("grad", grad), ("state1", state1), ("state2", state2)):
+    two = kind in TWO_STATE
+    if not two and state2 is not None:
+        raise ValueError("the one-state kinds take state2=None")
+    named = [("param", param), ("grad", grad), ("state1", state1)]
+    if two:
+        named.append(("state2", state2))
+    for name, t in named:
         if not isinstance(t, torch.Tensor) or not t.is_cuda:
             raise ValueError(f"{name} must be a tensor on a HIP device")
         if not t.is_contiguous():
@@ -104,21 +120,26 @@ def _tensor_args(kind: int, param, grad, state1, state2) -> tuple[int, int]:
     dt = DTYPES.get(param.dtype)
     if dt is None or grad.dtype != param.dtype:
         raise ValueError("param and grad must share one of float32/float16/bfloat16")
-    if state1.dtype != torch.float32 or state2.dtype != torch.float32:
+    if state1.dtype != torch.float32 or (two and state2.dtype != torch.float32):
         raise ValueError("states must be float32")
     n = param.numel()
     s1 = 2 * n if kind == _lib.OU_ADEMAMIX else n
-    if grad.numel() != n or state1.numel() != s1 or state2.numel() != n:
+    s2 = state2.numel() if two else 0
+    if grad.numel() != n or state1.numel() != s1 or (two and s2 != n):
         raise ValueError(f"sizes: param {n}, grad {grad.numel()}, state1 {state1.numel()} "
-                         f"(want {s1}), state2 {state2.numel()} (want {n})")
+                         f"(want {s1}), state2 {s2} (want {n if two else 0})")
     dev = param.device
-    if grad.device != dev or state1.device != dev or state2.device != dev:
+    if grad.device != dev or state1.device != dev or (two and state2.device != dev):
         raise ValueError("all tensors must be on one device")
     return n, dt
 
 
+def _ptr(t) -> int | None:
+    return None if t is None else t.data_ptr()
+
+
 def optimizer_update_32bit(kind, param: torch.Tensor, grad: torch.Tensor, state1: torch.Tensor,
-                           state2: torch.Tensor, *, step: int, lr: float, beta1: float = 0.9,
+                           state2: torch.Tensor | None, *, step: int, lr: float, beta1: float = 0.9,
                            beta2: float = 0.999, beta3: float = 0.9999, alpha: float = 5.0,
                            eps: float = 1e-8, weight_decay: float = 0.0, skip_zeros: bool = False,
                            stream=None) -> None:
@@ -128,7 +149,7 @@ def optimizer_update_32bit(kind, param: torch.Tensor, grad: torch.Tensor, state1
     lib = load()
     with _on_device(param.device):
         st = lib.optimizer_update_32bit(k, dt, param.data_ptr(), grad.data_ptr(),
-                                        state1.data_ptr(), state2.data_ptr(), n, beta1, beta2,
+                                        state1.data_ptr(), _ptr(state2), n, beta1, beta2,
                                         beta3, alpha, eps, weight_decay, int(step), lr,
                                         int(bool(skip_zeros)), _stream(param, stream))
     check(st, lib)
@@ -151,7 +172,7 @@ def clip_scale(workspace: torch.Tensor) -> float:
 
 
 def optimizer_update_32bit_clip(kind, param: torch.Tensor, grad: torch.Tensor,
-                                state1: torch.Tensor, state2: torch.Tensor, *, step: int,
+                                state1: torch.Tensor, state2: torch.Tensor | None, *, step: int,
                                 lr: float, max_unorm: float, workspace: torch.Tensor | None = None,
                                 beta1: float = 0.9, beta2: float = 0.999, beta3: float = 0.9999,
                                 alpha: float = 5.0, eps: float = 1e-8, weight_decay: float = 0.0,
@@ -172,7 +193,7 @@ def optimizer_update_32bit_clip(kind, param: torch.Tensor, grad: torch.Tensor,
     wb = workspace.numel() if workspace is not None else 0
     with _on_device(param.device):
         st = lib.optimizer_update_32bit_clip(k, dt, param.data_ptr(), grad.data_ptr(),
-                                             state1.data_ptr(), state2.data_ptr(), n, beta1, beta2,
+                                             state1.data_ptr(), _ptr(state2), n, beta1, beta2,
                                              beta3, alpha, eps, weight_decay, int(step), lr,
                                              int(bool(skip_zeros)), max_unorm, wp, wb,
                                              _stream(param, stream))
@@ -184,12 +205,13 @@ def _segments(kind: int, segments) -> ctypes.Array:
     arr = (_lib.ou_segment * len(segments))()
     for i, (p, g, s1, s2) in enumerate(segments):
         n, dt = _tensor_args(kind, p, g, s1, s2)
-        arr[i] = _lib.ou_segment(p.data_ptr(), g.data_ptr(), s1.data_ptr(), s2.data_ptr(), n, dt, 0)
+        arr[i] = _lib.ou_segment(p.data_ptr(), g.data_ptr(), s1.data_ptr(), _ptr(s2), n, dt, 0)
     return arr
 
 
 def optimizer_update_32bit_multi(kind, segments, hp: HParams, step: int, stream=None) -> None:
-    """One update of a collection [(param, grad, state1, state2), ...]: one
+    """One update of a collection [(param, grad, state1, state2), ...]
+    (state2 None for the one-state kinds): one
     launch per dtype group.  Builds the table on every call and waits for
     the stream; use ``Plan`` for repeated steps."""
     k = _kind(kind)
@@ -276,6 +298,7 @@ class Plan:
             pass
 
 
-from .optim import AdamW32, AdEMAMix32  # noqa: E402
+from .optim import AdamW32, AdEMAMix32, Adagrad32, Lion32, Momentum32, RMSprop32  # noqa: E402
 
-__all__ += ["AdamW32", "AdEMAMix32"]
+__all__ += ["AdamW32", "AdEMAMix32", "Momentum32", "RMSprop32", "Adagrad32", "Lion32",
+            "TWO_STATE"]

@@ -20,7 +20,12 @@
 
 namespace ou {
 
-enum Kind : int { kAdam = 0, kAdemamix = 1 };
+enum Kind : int { kAdam = 0, kAdemamix = 1, kMomentum = 2, kRmsprop = 3, kAdagrad = 4, kLion = 5 };
+
+// Adam and AdEMAMix keep two fp32 states (state1, state2); the one-state
+// kinds keep state1 only.
+template <int KIND>
+inline constexpr bool kTwoState = KIND <= kAdemamix;
 
 // Per-step scalars, formed on the host once per step (see host.hip).
 struct StepScalars {
@@ -29,7 +34,9 @@ struct StepScalars {
     float alpha, eps, lr;
     float bc1, bc2;           // bias corrections fl32(1 - fl64(beta^step))
     float decay;              // fl32(1 - fl64(lr * weight_decay))
+    float weight_decay;       // L2 coefficient of the momentum/RMSprop/Adagrad kinds
     int32_t skip_zeros;
+    int32_t first_step;       // step == 1 (momentum starts its buffer from the gradient)
 };
 
 // The moments of one element.  m: fast first moment, v: second moment,
@@ -65,14 +72,52 @@ __device__ __forceinline__ float step_param(float p, float u, float decay, float
     return p * decay - lr * u;
 }
 
-// One element: moments, direction, parameter.  p is the widened parameter;
-// returns the new parameter before rounding to storage.
+// One element of a one-state kind; m is the element's state.  gd adds the
+// L2 term wd*p to the gradient (only when wd != 0), as torch.optim does.
+//   momentum (Sutskever et al. 2013; dampening 0): m = gd on the first
+//            step, else beta1*m + gd; p - lr*m
+//   RMSprop  (Tieleman & Hinton 2012): m = beta1*m + (1-beta1)*(gd*gd);
+//            p - lr*(gd/(sqrt(m)+eps))
+//   Adagrad  (Duchi et al. 2011): m = m + gd*gd; p - lr*(gd/(sqrt(m)+eps))
+//   Lion     (Chen et al. 2023): c = beta1*m + (1-beta1)*g; p*d - lr*sign(c)
+//            (sign(0) = 0, NaN stays NaN); then m = beta2*m + (1-beta2)*g
+template <int KIND>
+__device__ __forceinline__ float update_one_state(float p, float g, float& m, const StepScalars& s)
+{
+    if constexpr (KIND == kLion) {
+        const float c = s.beta1 * m + s.omb1 * g;
+        const float u = (c != c) ? c : static_cast<float>((c > 0.0f) - (c < 0.0f));
+        const float pn = p * s.decay - s.lr * u;
+        m = s.beta2 * m + s.omb2 * g;
+        return pn;
+    } else {
+        const float gd = (s.weight_decay != 0.0f) ? g + s.weight_decay * p : g;
+        if constexpr (KIND == kMomentum) {
+            m = s.first_step ? gd : s.beta1 * m + gd;
+            return p - s.lr * m;
+        } else {
+            if constexpr (KIND == kRmsprop)
+                m = s.beta1 * m + s.omb1 * (gd * gd);
+            else
+                m = m + gd * gd;
+            return p - s.lr * (gd / (__builtin_sqrtf(m) + s.eps));
+        }
+    }
+}
+
+// One element: moments, direction, parameter (two-state kinds), or the
+// one-state rule.  p is the widened parameter; returns the new parameter
+// before rounding to storage.
 template <int KIND>
 __device__ __forceinline__ float update_element(float p, float g, float& m, float& v,
                                                 float& m2, const StepScalars& s)
 {
-    update_moments<KIND>(g, m, v, m2, s);
-    return step_param(p, direction<KIND>(m, v, m2, s), s.decay, s.lr);
+    if constexpr (kTwoState<KIND>) {
+        update_moments<KIND>(g, m, v, m2, s);
+        return step_param(p, direction<KIND>(m, v, m2, s), s.decay, s.lr);
+    } else {
+        return update_one_state<KIND>(p, g, m, s);
+    }
 }
 
 // ---- storage types ---------------------------------------------------------
@@ -122,12 +167,13 @@ __device__ __forceinline__ void update_scalar(typename S::raw* __restrict__ p,
 {
     const float gi = S::widen(g[i]);
     if (s.skip_zeros && gi == 0.0f) return;
-    float m = s1[i], v = s2[i], m2 = 0.0f;
+    float m = s1[i], v = 0.0f, m2 = 0.0f;
+    if constexpr (kTwoState<KIND>) v = s2[i];
     if constexpr (KIND == kAdemamix) m2 = s1[n + i];
     const float pn = update_element<KIND>(S::widen(p[i]), gi, m, v, m2, s);
     p[i] = S::narrow(pn);
     s1[i] = m;
-    s2[i] = v;
+    if constexpr (kTwoState<KIND>) s2[i] = v;
     if constexpr (KIND == kAdemamix) s1[n + i] = m2;
 }
 

@@ -122,9 +122,14 @@ int storage_bytes(int dtype) { return dtype == OU_F32 ? 4 : 2; }
 
 bool valid_beta(float b) { return std::isfinite(b) && b >= 0.0f && b < 1.0f; }
 
+bool valid_kind(int kind) { return kind >= OU_ADAM && kind <= OU_LION; }
+
+// Adam and AdEMAMix read and write state2; the one-state kinds ignore it.
+bool two_state(int kind) { return kind == OU_ADAM || kind == OU_ADEMAMIX; }
+
 int check_hparams(int kind, const ou_hparams& h)
 {
-    if (kind != OU_ADAM && kind != OU_ADEMAMIX) return fail(OU_EINVAL, "unknown kind %d", kind);
+    if (!valid_kind(kind)) return fail(OU_EINVAL, "unknown kind %d", kind);
     if (!valid_beta(h.beta1) || !valid_beta(h.beta2))
         return fail(OU_EINVAL, "beta1/beta2 must lie in [0, 1) (got %g, %g)", h.beta1, h.beta2);
     if (kind == OU_ADEMAMIX && (!valid_beta(h.beta3) || !std::isfinite(h.alpha)))
@@ -151,13 +156,14 @@ int check_segment(int kind, const ou_segment& s, int idx, std::vector<Range>* ra
     if (s.n < 0) return fail(OU_EINVAL, "segment %d: n < 0", idx);
     if (s.reserved != 0) return fail(OU_EINVAL, "segment %d: reserved field must be 0", idx);
     if (s.n == 0) return OU_OK;
-    if (!s.param || !s.grad || !s.state1 || !s.state2)
+    const bool two = two_state(kind);
+    if (!s.param || !s.grad || !s.state1 || (two && !s.state2))
         return fail(OU_EINVAL, "segment %d: null pointer with n > 0", idx);
     const uintptr_t sb = static_cast<uintptr_t>(storage_bytes(s.dtype));
     const uintptr_t P = reinterpret_cast<uintptr_t>(s.param);
     const uintptr_t G = reinterpret_cast<uintptr_t>(s.grad);
     const uintptr_t S1 = reinterpret_cast<uintptr_t>(s.state1);
-    const uintptr_t S2 = reinterpret_cast<uintptr_t>(s.state2);
+    const uintptr_t S2 = two ? reinterpret_cast<uintptr_t>(s.state2) : 0;
     if (P % sb || G % sb) return fail(OU_EALIGN, "segment %d: param/grad not %u-byte aligned", idx, (unsigned)sb);
     if (S1 % 4 || S2 % 4) return fail(OU_EALIGN, "segment %d: states not 4-byte aligned", idx);
     const uintptr_t n = static_cast<uintptr_t>(s.n);
@@ -166,7 +172,7 @@ int check_segment(int kind, const ou_segment& s, int idx, std::vector<Range>* ra
     ranges->push_back({P, P + n * sb, true, idx});
     ranges->push_back({G, G + n * sb, false, idx});
     ranges->push_back({S1, S1 + k * n * 4, true, idx});
-    ranges->push_back({S2, S2 + n * 4, true, idx});
+    if (two) ranges->push_back({S2, S2 + n * 4, true, idx});
     return OU_OK;
 }
 
@@ -190,8 +196,9 @@ int check_overlap(std::vector<Range>& r)
 
 bool streams_16b_aligned(int kind, const ou_segment& s)
 {
-    const uintptr_t a = reinterpret_cast<uintptr_t>(s.param) | reinterpret_cast<uintptr_t>(s.grad) |
-                        reinterpret_cast<uintptr_t>(s.state1) | reinterpret_cast<uintptr_t>(s.state2);
+    uintptr_t a = reinterpret_cast<uintptr_t>(s.param) | reinterpret_cast<uintptr_t>(s.grad) |
+                  reinterpret_cast<uintptr_t>(s.state1);
+    if (two_state(kind)) a |= reinterpret_cast<uintptr_t>(s.state2);
     uintptr_t slow = 0;
     if (kind == OU_ADEMAMIX) slow = reinterpret_cast<uintptr_t>(s.state1 + s.n);
     return ((a | slow) & 15u) == 0;
@@ -217,7 +224,9 @@ StepScalars make_scalars(const ou_hparams& h)
     s.bc1 = static_cast<float>(1.0 - std::pow(static_cast<double>(h.beta1), t));
     s.bc2 = static_cast<float>(1.0 - std::pow(static_cast<double>(h.beta2), t));
     s.decay = static_cast<float>(1.0 - static_cast<double>(h.lr) * static_cast<double>(h.weight_decay));
+    s.weight_decay = h.weight_decay;
     s.skip_zeros = h.skip_zeros ? 1 : 0;
+    s.first_step = h.step == 1 ? 1 : 0;
     return s;
 }
 
@@ -352,7 +361,7 @@ namespace {
 int build_plan(int kind, const ou_segment* segs, int32_t nseg, ou_plan_s** out)
 {
     *out = nullptr;
-    if (kind != OU_ADAM && kind != OU_ADEMAMIX) return fail(OU_EINVAL, "unknown kind %d", kind);
+    if (!valid_kind(kind)) return fail(OU_EINVAL, "unknown kind %d", kind);
     if (nseg < 0 || (nseg > 0 && !segs)) return fail(OU_EINVAL, "bad segment array");
     std::vector<Range> ranges;
     ranges.reserve(static_cast<size_t>(nseg) * 4);
@@ -398,7 +407,7 @@ int build_plan(int kind, const ou_segment* segs, int32_t nseg, ou_plan_s** out)
         d.p = s.param;
         d.g = s.grad;
         d.s1 = s.state1;
-        d.s2 = s.state2;
+        d.s2 = two_state(kind) ? s.state2 : nullptr;
         d.n = s.n;
         d.vec_ok = streams_16b_aligned(kind, s) ? 1 : 0;
         d.pad = 0;
@@ -606,6 +615,8 @@ int optimizer_update_32bit_clip(int kind, int dtype, void* param, const void* gr
     if (max_unorm == 0.0f)
         return optimizer_update_32bit(kind, dtype, param, grad, state1, state2, n, beta1, beta2,
                                       beta3, alpha, eps, weight_decay, step, lr, skip_zeros, stream);
+    if (valid_kind(kind) && !two_state(kind))
+        return fail(OU_EINVAL, "update-norm clipping is defined for ADAM and ADEMAMIX only");
     ou_hparams h;
     h.beta1 = beta1; h.beta2 = beta2; h.beta3 = beta3; h.alpha = alpha; h.eps = eps;
     h.weight_decay = weight_decay; h.lr = lr; h.skip_zeros = skip_zeros; h.step = step;
@@ -711,6 +722,8 @@ int ou_plan_step_clip(ou_plan plan, const ou_hparams* hp, float max_unorm, void*
     if (int st = check_hparams(plan->kind, *hp)) return st;
     if (int st = check_plan_device(plan)) return st;
     if (max_unorm == 0.0f) return plan_launch(plan, make_scalars(*hp), static_cast<hipStream_t>(stream));
+    if (!two_state(plan->kind))
+        return fail(OU_EINVAL, "update-norm clipping is defined for ADAM and ADEMAMIX only");
     return plan_launch_clip(plan, make_scalars(*hp), max_unorm, static_cast<hipStream_t>(stream));
 }
 

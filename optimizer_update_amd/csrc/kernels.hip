@@ -125,7 +125,7 @@ struct Group {
         p = load_words<SDW>(pp + e);
         g = load_words<SDW>(gp + e);
         m = load_words<FDW>(s1 + e);
-        v = load_words<FDW>(s2 + e);
+        if constexpr (kTwoState<KIND>) v = load_words<FDW>(s2 + e);
         if constexpr (KIND == kAdemamix) m2 = load_words<FDW>(s1 + n + e);
     }
 
@@ -136,7 +136,8 @@ struct Group {
             const float gj = S::widen(get_raw<S>(g, j));
             const typename S::raw praw = get_raw<S>(p, j);
             float mj = __builtin_bit_cast(float, m.w[j]);
-            float vj = __builtin_bit_cast(float, v.w[j]);
+            float vj = 0.0f;
+            if constexpr (kTwoState<KIND>) vj = __builtin_bit_cast(float, v.w[j]);
             float m2j = 0.0f;
             if constexpr (KIND == kAdemamix) m2j = __builtin_bit_cast(float, m2.w[j]);
             const float pn = update_element<KIND>(S::widen(praw), gj, mj, vj, m2j, sc);
@@ -144,7 +145,7 @@ struct Group {
             set_raw<S>(p, j, keep ? praw : S::narrow(pn));
             if (!keep) {
                 m.w[j] = __builtin_bit_cast(uint32_t, mj);
-                v.w[j] = __builtin_bit_cast(uint32_t, vj);
+                if constexpr (kTwoState<KIND>) v.w[j] = __builtin_bit_cast(uint32_t, vj);
                 if constexpr (KIND == kAdemamix) m2.w[j] = __builtin_bit_cast(uint32_t, m2j);
             }
         }
@@ -156,7 +157,7 @@ struct Group {
         const int64_t e = vi * EPL;
         store_words<SDW>(pp + e, p);
         store_words<FDW>(s1 + e, m);
-        store_words<FDW>(s2 + e, v);
+        if constexpr (kTwoState<KIND>) store_words<FDW>(s2 + e, v);
         if constexpr (KIND == kAdemamix) store_words<FDW>(s1 + n + e, m2);
     }
 };
@@ -627,7 +628,9 @@ template <int KIND, typename S>
 const void* pick(bool multi, int epl, int unroll)
 {
     if (epl == 4) return multi ? pick_multi<KIND, S, 4>(unroll) : pick_single<KIND, S, 4>(unroll);
-    if (epl == 8) return multi ? pick_multi<KIND, S, 8>(unroll) : pick_single<KIND, S, 8>(unroll);
+    if constexpr (kTwoState<KIND>) {   // 8 elements per lane only for the two-state kinds
+        if (epl == 8) return multi ? pick_multi<KIND, S, 8>(unroll) : pick_single<KIND, S, 8>(unroll);
+    }
     return nullptr;
 }
 
@@ -644,9 +647,15 @@ const void* pick_dtype(bool multi, int dtype, int epl, int unroll)
 
 const void* pick_all(bool multi, int kind, int dtype, int epl, int unroll)
 {
-    if (kind == kAdam) return pick_dtype<kAdam>(multi, dtype, epl, unroll);
-    if (kind == kAdemamix) return pick_dtype<kAdemamix>(multi, dtype, epl, unroll);
-    return nullptr;
+    switch (kind) {
+    case kAdam: return pick_dtype<kAdam>(multi, dtype, epl, unroll);
+    case kAdemamix: return pick_dtype<kAdemamix>(multi, dtype, epl, unroll);
+    case kMomentum: return pick_dtype<kMomentum>(multi, dtype, epl, unroll);
+    case kRmsprop: return pick_dtype<kRmsprop>(multi, dtype, epl, unroll);
+    case kAdagrad: return pick_dtype<kAdagrad>(multi, dtype, epl, unroll);
+    case kLion: return pick_dtype<kLion>(multi, dtype, epl, unroll);
+    default: return nullptr;
+    }
 }
 
 template <int KIND, typename S>

@@ -1,12 +1,14 @@
 """Collection optimizers over a fixed parameter list (argument marshalling only).
 
-``AdamW32`` and ``AdEMAMix32`` play the part of the 32-bit collection
+``AdamW32`` and ``AdEMAMix32`` (two fp32 states per parameter) play the part of the 32-bit collection
 optimizers that the page "Investigate a 256-thread SM103 path for small
 32-bit optimizer tensors" times in its eager ``optimizer.step()`` workloads
 (section "B300 benchmark and acceptance"): they own the fp32 states of every
 parameter and update the whole collection per step through one plan (one
 launch per dtype group), its HIP-graph replay, or, for comparison, one
-direct call per tensor.
+direct call per tensor.  ``Momentum32``, ``RMSprop32``, ``Adagrad32`` and
+``Lion32`` are the one-state kinds of the same 32-bit update family, with the
+same three step paths.
 
 Parameters and gradients must be contiguous CUDA (HIP) tensors whose
 storage stays in place for the optimizer's lifetime: the plan holds their
@@ -16,8 +18,9 @@ from __future__ import annotations
 
 import torch
 
-from . import (DTYPES, HParams, Plan, _kind, _on_device, _raw_stream, _tensor_args, check,
-               clip_workspace, load, optimizer_update_32bit_clip, state_sizes)
+from . import (DTYPES, TWO_STATE, HParams, Plan, _kind, _on_device, _ptr, _raw_stream,
+               _tensor_args, check, clip_workspace, load, optimizer_update_32bit_clip,
+               state_sizes)
 
 
 class _Collection:
@@ -36,11 +39,15 @@ class _Collection:
                 grads.append(g)
         self.grads = list(grads)
         self.hp = hp
+        two = _kind(self.kind) in TWO_STATE
+        if max_unorm and not two:
+            raise ValueError("update-norm clipping is defined for Adam and AdEMAMix only")
         self.state1, self.state2 = [], []
         for p in self.params:
             n1, n2 = state_sizes(self.kind, p.numel())
             self.state1.append(torch.zeros(n1, dtype=torch.float32, device=p.device))
-            self.state2.append(torch.zeros(n2, dtype=torch.float32, device=p.device))
+            self.state2.append(torch.zeros(n2, dtype=torch.float32, device=p.device)
+                               if two else None)
         self.step_count = 0
         self.max_unorm = float(max_unorm)
         self._workspace = None
@@ -87,7 +94,7 @@ class _Collection:
             for p, g, s1, s2 in self.segments():   # full checks once
                 _tensor_args(_kind(self.kind), p, g, s1, s2)
             self._direct = [(_kind(self.kind), DTYPES[p.dtype], p.data_ptr(), g.data_ptr(),
-                             s1.data_ptr(), s2.data_ptr(), p.numel())
+                             s1.data_ptr(), _ptr(s2), p.numel())
                             for p, g, s1, s2 in self.segments()]
         lib = load()
         sh = (_raw_stream(self.params[0].device.index) if stream is None
@@ -104,14 +111,15 @@ class _Collection:
     def state_dict(self) -> dict:
         return {"step": self.step_count,
                 "state1": [s.clone() for s in self.state1],
-                "state2": [s.clone() for s in self.state2]}
+                "state2": [None if s is None else s.clone() for s in self.state2]}
 
     def load_state_dict(self, sd: dict) -> None:
         self.step_count = int(sd["step"])
         for dst, src in zip(self.state1, sd["state1"]):
             dst.copy_(src)
         for dst, src in zip(self.state2, sd["state2"]):
-            dst.copy_(src)
+            if dst is not None:
+                dst.copy_(src)
 
     def close(self) -> None:
         self.plan.close()
@@ -137,3 +145,47 @@ class AdEMAMix32(_Collection):
         super().__init__(params, HParams(lr=lr, beta1=betas[0], beta2=betas[1], beta3=betas[2],
                                          alpha=alpha, eps=eps, weight_decay=weight_decay,
                                          skip_zeros=skip_zeros), grads, max_unorm)
+
+
+class Momentum32(_Collection):
+    """SGD with heavy-ball momentum (no dampening, no Nesterov) and L2
+    weight decay added to the gradient."""
+    kind = "momentum"
+
+    def __init__(self, params, lr=1e-2, momentum=0.9, weight_decay=0.0, skip_zeros=False,
+                 grads=None):
+        super().__init__(params, HParams(lr=lr, beta1=momentum, beta2=0.0, eps=0.0,
+                                         weight_decay=weight_decay, skip_zeros=skip_zeros), grads)
+
+
+class RMSprop32(_Collection):
+    """RMSprop (smoothing constant alpha, eps outside the root, L2 weight
+    decay added to the gradient)."""
+    kind = "rmsprop"
+
+    def __init__(self, params, lr=1e-2, alpha=0.99, eps=1e-8, weight_decay=0.0,
+                 skip_zeros=False, grads=None):
+        super().__init__(params, HParams(lr=lr, beta1=alpha, beta2=0.0, eps=eps,
+                                         weight_decay=weight_decay, skip_zeros=skip_zeros), grads)
+
+
+class Adagrad32(_Collection):
+    """Adagrad (accumulator starts at zero, no learning-rate decay, L2
+    weight decay added to the gradient)."""
+    kind = "adagrad"
+
+    def __init__(self, params, lr=1e-2, eps=1e-10, weight_decay=0.0, skip_zeros=False,
+                 grads=None):
+        super().__init__(params, HParams(lr=lr, beta1=0.0, beta2=0.0, eps=eps,
+                                         weight_decay=weight_decay, skip_zeros=skip_zeros), grads)
+
+
+class Lion32(_Collection):
+    """Lion: sign of the beta1 interpolation, moment tracked with beta2,
+    decoupled weight decay."""
+    kind = "lion"
+
+    def __init__(self, params, lr=1e-4, betas=(0.9, 0.99), weight_decay=0.0, skip_zeros=False,
+                 grads=None):
+        super().__init__(params, HParams(lr=lr, beta1=betas[0], beta2=betas[1], eps=0.0,
+                                         weight_decay=weight_decay, skip_zeros=skip_zeros), grads)

@@ -75,7 +75,11 @@ def _segs(*rows):
 
 
 @pytest.mark.parametrize("case,kw,code", [
-    ("unknown kind", dict(kind=2), OU_EINVAL),
+    ("unknown kind", dict(kind=6), OU_EINVAL),
+    ("negative kind", dict(kind=-1), OU_EINVAL),
+    ("adam null state2", dict(s2=0), OU_EINVAL),
+    ("lion beta2 = 1", dict(kind=5, b2=1.0), OU_EINVAL),
+    ("momentum state1 overlaps param", dict(kind=2, s1=0x10000 + 32), OU_EOVERLAP),
     ("unknown dtype", dict(dtype=3), OU_EINVAL),
     ("negative n", dict(n=-1), OU_EINVAL),
     ("step 0", dict(step=0), OU_EINVAL),
@@ -100,6 +104,15 @@ def _segs(*rows):
 def test_single_entry_validation(L, case, kw, code):
     assert _call(L, **kw) == code, case
     assert L.ou_last_error().decode(), "an error message is set"
+
+
+@pytest.mark.parametrize("kind", [2, 3, 4, 5])
+def test_one_state_kinds_ignore_state2(L, kind):
+    # passes validation (then stops at the device query on a machine without a GPU)
+    for s2 in (0, 0x40002, 0x30000, 0x10000):
+        assert _call(L, kind=kind, s2=s2) not in (OU_EINVAL, OU_EALIGN, OU_EOVERLAP)
+    assert _call(L, kind=kind, s1=0x30002) == OU_EALIGN
+    assert _call(L, kind=kind, s1=0x20000 + 8) == OU_EOVERLAP
 
 
 def test_adjacent_buffers_are_not_overlap_and_n0_is_noop(L):
@@ -136,7 +149,13 @@ def test_plan_and_multi_validation(L):
     st = L.ou_plan_create(0, _segs(*shared), 2, ctypes.byref(h))
     assert st not in (OU_EINVAL, OU_EALIGN, OU_EOVERLAP)
     assert not h.value or L.ou_plan_destroy(h) is None
-    assert L.ou_plan_create(5, _segs(ok), 1, ctypes.byref(h)) == OU_EINVAL
+    assert L.ou_plan_create(6, _segs(ok), 1, ctypes.byref(h)) == OU_EINVAL
+    # a one-state plan ignores state2: NULL, or overlapping anything, passes validation
+    for s2 in (0, 0x100000):
+        st = L.ou_plan_create(4, _segs((0x100000, 0x200000, 0x300000, s2, 1024, 0, 0)), 1,
+                              ctypes.byref(h))
+        assert st not in (OU_EINVAL, OU_EALIGN, OU_EOVERLAP)
+        assert not h.value or L.ou_plan_destroy(h) is None
     assert L.ou_plan_create(0, _segs(ok), 1, None) == OU_EINVAL
     bad_hp = _lib.ou_hparams(0.9, 0.999, 0.9999, 5.0, 1e-8, 0.0, 1e-3, 0, 0)
     assert L.optimizer_update_32bit_multi(0, _segs(ok), 1, ctypes.byref(bad_hp), None) == OU_EINVAL
@@ -148,10 +167,10 @@ def test_plan_and_multi_validation(L):
     L.ou_plan_destroy(None)
 
 
-def _clip(L, max_unorm=1.0, ws=0x800000, wsb=None, n=4096, p=0x10000, **kw):
+def _clip(L, max_unorm=1.0, ws=0x800000, wsb=None, n=4096, p=0x10000, kind=0, **kw):
     if wsb is None:
         wsb = L.ou_clip_workspace_bytes(n)
-    return L.optimizer_update_32bit_clip(0, 0, p, 0x20000, 0x30000, 0x40000, n, 0.9, 0.999, 0.9999,
+    return L.optimizer_update_32bit_clip(kind, 0, p, 0x20000, 0x30000, 0x40000, n, 0.9, 0.999, 0.9999,
                                          5.0, 1e-8, 0.0, kw.get("step", 1), 1e-3, 0, max_unorm,
                                          ws, wsb, None)
 
@@ -173,6 +192,9 @@ def test_clip_entry_validation(L):
     assert _clip(L, step=0) == OU_EINVAL
     assert _clip(L, n=0) == OU_OK                           # nothing to do
     assert _clip(L, max_unorm=0.0, n=0, ws=0) == OU_OK        # plain step, no workspace
+    for kind in (2, 3, 4, 5):                                # clipping: two-state kinds only
+        assert _clip(L, kind=kind) == OU_EINVAL
+        assert _clip(L, kind=kind, max_unorm=0.0, n=0, ws=0) == OU_OK
 
 
 def test_status_strings(L):

@@ -136,9 +136,13 @@ def numel(shape: tuple[int, ...]) -> int:
     return r
 
 
+# fp32 state planes per element: Adam m, v; AdEMAMix m, v, m2; one-state kinds m.
+STATE_PLANES = {"adam": 2, "ademamix": 3, "momentum": 1, "rmsprop": 1, "adagrad": 1, "lion": 1}
+
+
 def bytes_per_element(kind: str, storage: str) -> int:
     """Algorithmic HBM bytes per element and step: read p, g, the fp32 states;
     write p and the fp32 states (the gradient is only read)."""
     s = STORAGE_BYTES[storage]
-    k = 2 if kind == "ademamix" else 1
-    return (2 * s + 4 * (k + 1)) + (s + 4 * (k + 1))
+    k = STATE_PLANES[kind]
+    return (2 * s + 4 * k) + (s + 4 * k)
