@@ -35,6 +35,9 @@ F32, F16, BF16 = 0, 1, 2
 KINDS = {"adam": ADAM, "ademamix": ADEMAMIX, "momentum": MOMENTUM, "rmsprop": RMSPROP,
          "adagrad": ADAGRAD, "lion": LION}
 ONE_STATE = (MOMENTUM, RMSPROP, ADAGRAD, LION)
+# OR'ed into a kind: decoupled decay applied to the updated parameter,
+# (p - lr*u)*d, instead of the default p*d - lr*u (ADAM, ADEMAMIX, LION).
+DECAY_AFTER = 0x100
 DTYPES = {"fp32": F32, "fp16": F16, "bf16": BF16}
 
 # -O2 without contraction or fast-math: each C operation is one correctly
@@ -159,7 +162,7 @@ class Oracle:
         sdt = np.float32 if dtype == F32 else np.uint16
         assert param.dtype == sdt and grad.dtype == sdt and grad.size == n
         assert state1.dtype == np.float32 and state2.dtype == np.float32
-        assert state1.size == (2 * n if kind == ADEMAMIX else n) and state2.size == n
+        assert state1.size == (2 * n if kind & 0xff == ADEMAMIX else n) and state2.size == n
         rc = self._lib.oracle_update_f32(
             kind, dtype, _ptr(param), _ptr(grad), _ptr(state1), _ptr(state2), n,
             hp.beta1, hp.beta2, hp.beta3, hp.alpha, hp.eps, hp.weight_decay, step,
@@ -173,7 +176,7 @@ class Oracle:
         n = param.size
         for a in (param, grad, state1, state2):
             assert a.dtype == np.float64 and a.flags.c_contiguous
-        assert state1.size == (2 * n if kind == ADEMAMIX else n) and state2.size == n
+        assert state1.size == (2 * n if kind & 0xff == ADEMAMIX else n) and state2.size == n
         rc = self._lib.oracle_update_f64(
             kind, _ptr(param), _ptr(grad), _ptr(state1), _ptr(state2), n,
             hp.beta1, hp.beta2, hp.beta3, hp.alpha, hp.eps, hp.weight_decay, step,
@@ -213,7 +216,7 @@ class Oracle:
         n = param.size
         sdt = np.float32 if dtype == F32 else np.uint16
         assert param.dtype == sdt and grad.dtype == sdt and grad.size == n
-        assert state1.size == (2 * n if kind == ADEMAMIX else n) and state2.size == n
+        assert state1.size == (2 * n if kind & 0xff == ADEMAMIX else n) and state2.size == n
         out = ctypes.c_float()
         rc = self._lib.oracle_update_f32_clip(
             kind, dtype, _ptr(param), _ptr(grad), _ptr(state1), _ptr(state2), n,

@@ -39,6 +39,14 @@
  * (the page's "max_unorm"; it names the option only, so the clip rule is
  * stated at the function).
  *
+ * Weight-decay order.  The page (section "Scope") says the order of the
+ * decoupled decay and the step is being changed upstream without saying
+ * which order is right.  The default here decays the old parameter,
+ * p*d - lr*u (Loshchilov & Hutter, Algorithm 2; torch.optim.AdamW).  A kind
+ * OR'ed with ORACLE_DECAY_AFTER applies the decay to the updated parameter
+ * instead, (p - lr*u)*d.  The flag is valid for the kinds with decoupled
+ * decay (ADAM, ADEMAMIX, LION); the L2 kinds reject it.
+ *
  * ORACLE_PLANT (compile-time, default 0) plants one known mistake so that
  * the test suite can show its pins catch it.  It is never set in a normal
  * build.
@@ -58,6 +66,21 @@
 enum { ORACLE_ADAM = 0, ORACLE_ADEMAMIX = 1,
        ORACLE_MOMENTUM = 2, ORACLE_RMSPROP = 3, ORACLE_ADAGRAD = 4, ORACLE_LION = 5 };
 enum { ORACLE_F32 = 0, ORACLE_F16 = 1, ORACLE_BF16 = 2 };
+#define ORACLE_DECAY_AFTER 0x100
+
+/* Splits a kind argument into the kind and the decay-order flag; -1 for
+ * unknown flag bits. */
+static int split_kind(int kind_arg, int* kind, int* after)
+{
+    if (kind_arg & ~(0xff | ORACLE_DECAY_AFTER))
+        return -1;
+    *kind = kind_arg & 0xff;
+    *after = (kind_arg & ORACLE_DECAY_AFTER) != 0;
+#if ORACLE_PLANT == 22
+    *after = 0;                                     /* planted: decay-order flag ignored */
+#endif
+    return 0;
+}
 
 static float f32_from_bits(uint32_t u) { float f; memcpy(&f, &u, sizeof f); return f; }
 static uint32_t bits_from_f32(float f) { uint32_t u; memcpy(&u, &f, sizeof u); return u; }
@@ -244,10 +267,13 @@ static float direction_f32(int kind, float g, float* m, float* v, float* m2,
 }
 
 /* Decoupled weight decay of the old parameter and the step along u
- * (Loshchilov & Hutter, Algorithm 2).  Returns the new parameter before
- * rounding to the storage type. */
-static float param_f32(float p, float upd, float decay, float lr)
+ * (Loshchilov & Hutter, Algorithm 2); with `after`, the decay of the
+ * updated parameter.  Returns the new parameter before rounding to the
+ * storage type. */
+static float param_f32(float p, float upd, float decay, float lr, int after)
 {
+    if (after)
+        return (p - lr * upd) * decay;
 #if ORACLE_PLANT == 3
     return (p - lr * upd) * decay;                  /* planted: decay after the update */
 #else
@@ -258,10 +284,10 @@ static float param_f32(float p, float upd, float decay, float lr)
 /* One element, binary32: direction, then parameter. */
 static float element_f32(int kind, float p, float g, float* m, float* v, float* m2,
                          const oracle_scalars32* s, float beta1, float beta2, float beta3,
-                         float alpha, float eps, float lr)
+                         float alpha, float eps, float lr, int after)
 {
     float upd = direction_f32(kind, g, m, v, m2, s, beta1, beta2, beta3, alpha, eps);
-    return param_f32(p, upd, s->decay, lr);
+    return param_f32(p, upd, s->decay, lr, after);
 }
 
 /* One optimizer step over n elements, in place.
@@ -272,14 +298,17 @@ static float element_f32(int kind, float p, float g, float* m, float* v, float* 
  *   step        : 1-based index of the update being applied
  * With skip_zeros set, an element whose gradient compares equal to zero
  * (+0 or -0) is left untouched: no moment update and no decay.
- * grad is only read.  Returns 0, or -1 on an invalid kind or dtype. */
-int oracle_update_f32(int kind, int dtype, void* param, const void* grad,
+ * grad is only read.  kind may carry ORACLE_DECAY_AFTER.  Returns 0, or -1
+ * on an invalid kind or dtype. */
+int oracle_update_f32(int kind_arg, int dtype, void* param, const void* grad,
                       float* state1, float* state2, int64_t n,
                       float beta1, float beta2, float beta3, float alpha, float eps,
                       float weight_decay, int64_t step, float lr, int skip_zeros,
                       int nthreads)
 {
-    if ((kind != ORACLE_ADAM && kind != ORACLE_ADEMAMIX) ||
+    int kind, after;
+    if (split_kind(kind_arg, &kind, &after) ||
+        (kind != ORACLE_ADAM && kind != ORACLE_ADEMAMIX) ||
         (dtype != ORACLE_F32 && dtype != ORACLE_F16 && dtype != ORACLE_BF16))
         return -1;
     oracle_scalars32 s;
@@ -305,7 +334,7 @@ int oracle_update_f32(int kind, int dtype, void* param, const void* grad,
         if (kind == ORACLE_ADEMAMIX) m2 = &state1[2 * n - 1 - i];   /* planted: slow plane reversed */
 #endif
         float pn = element_f32(kind, p, g, &state1[i], &state2[i], m2, &s,
-                               beta1, beta2, beta3, alpha, eps, lr);
+                               beta1, beta2, beta3, alpha, eps, lr, after);
         store_storage(param, dtype, i, pn);
 #if ORACLE_PLANT == 10
         if (dtype == ORACLE_F32) ((float*)grad)[i] = pn;           /* planted: grad written */
@@ -319,12 +348,13 @@ int oracle_update_f32(int kind, int dtype, void* param, const void* grad,
 /* The same update with every operation in binary64 and the step scalars
  * unrounded.  fp64 arrays only; used to check the formulas against closed
  * forms.  Layout and arguments as oracle_update_f32. */
-int oracle_update_f64(int kind, double* param, const double* grad, double* state1,
+int oracle_update_f64(int kind_arg, double* param, const double* grad, double* state1,
                       double* state2, int64_t n, double beta1, double beta2, double beta3,
                       double alpha, double eps, double weight_decay, int64_t step,
                       double lr, int skip_zeros)
 {
-    if (kind != ORACLE_ADAM && kind != ORACLE_ADEMAMIX)
+    int kind, after;
+    if (split_kind(kind_arg, &kind, &after) || (kind != ORACLE_ADAM && kind != ORACLE_ADEMAMIX))
         return -1;
 #if ORACLE_PLANT == 7
     { double t = beta1; beta1 = beta2; beta2 = t; }
@@ -387,7 +417,7 @@ int oracle_update_f64(int kind, double* param, const double* grad, double* state
 #if ORACLE_PLANT == 3
         param[i] = (param[i] - lr * upd) * decay;
 #else
-        param[i] = param[i] * decay - lr * upd;
+        param[i] = after ? (param[i] - lr * upd) * decay : param[i] * decay - lr * upd;
 #endif
         state1[i] = m;
         state2[i] = v;
@@ -411,7 +441,7 @@ int oracle_update_f64(int kind, double* param, const double* grad, double* state
  *             (0 for c = 0, NaN stays NaN); p*d - lr*u with the decoupled
  *             decay d = fl32(1 - fl64(lr*wd)); then m = beta2*m + (1-beta2)*g */
 static float one_state_f32(int kind, float p, float g, float* m, float beta1, float beta2,
-                           float eps, float wd, float lr, float decay, int first)
+                           float eps, float wd, float lr, float decay, int first, int after)
 {
     if (kind == ORACLE_LION) {
 #if ORACLE_PLANT == 18
@@ -419,7 +449,7 @@ static float one_state_f32(int kind, float p, float g, float* m, float beta1, fl
 #endif
         float c = beta1 * (*m) + (1.0f - beta1) * g;
         float u = (c != c) ? c : (float)((c > 0.0f) - (c < 0.0f));
-        float pn = p * decay - lr * u;
+        float pn = after ? (p - lr * u) * decay : p * decay - lr * u;
 #if ORACLE_PLANT != 18
         *m = beta2 * (*m) + (1.0f - beta2) * g;
 #endif
@@ -453,12 +483,15 @@ static float one_state_f32(int kind, float p, float g, float* m, float beta1, fl
 /* One step of a one-state kind over n elements, in place.  state1: n
  * floats; skip_zeros as for the two-state kinds (an element with g == 0 is
  * left untouched).  step is 1-based (MOMENTUM starts its buffer at step 1).
- * Returns 0, or -1 on an invalid kind or dtype. */
-int oracle_update1_f32(int kind, int dtype, void* param, const void* grad, float* state1,
+ * ORACLE_DECAY_AFTER is accepted for LION only.  Returns 0, or -1 on an
+ * invalid kind or dtype. */
+int oracle_update1_f32(int kind_arg, int dtype, void* param, const void* grad, float* state1,
                        int64_t n, float beta1, float beta2, float eps, float weight_decay,
                        int64_t step, float lr, int skip_zeros, int nthreads)
 {
-    if (kind < ORACLE_MOMENTUM || kind > ORACLE_LION ||
+    int kind, after;
+    if (split_kind(kind_arg, &kind, &after) || kind < ORACLE_MOMENTUM || kind > ORACLE_LION ||
+        (after && kind != ORACLE_LION) ||
         (dtype != ORACLE_F32 && dtype != ORACLE_F16 && dtype != ORACLE_BF16))
         return -1;
     float decay = (float)(1.0 - (double)lr * (double)weight_decay);
@@ -470,17 +503,19 @@ int oracle_update1_f32(int kind, int dtype, void* param, const void* grad, float
         if (skip_zeros && g == 0.0f) continue;
         float p = load_storage(param, dtype, i);
         store_storage(param, dtype, i, one_state_f32(kind, p, g, &state1[i], beta1, beta2, eps,
-                                                     weight_decay, lr, decay, first));
+                                                     weight_decay, lr, decay, first, after));
     }
     return 0;
 }
 
 /* The one-state kinds in binary64 (fp64 arrays), for closed forms. */
-int oracle_update1_f64(int kind, double* param, const double* grad, double* state1, int64_t n,
-                       double beta1, double beta2, double eps, double weight_decay,
+int oracle_update1_f64(int kind_arg, double* param, const double* grad, double* state1,
+                       int64_t n, double beta1, double beta2, double eps, double weight_decay,
                        int64_t step, double lr, int skip_zeros)
 {
-    if (kind < ORACLE_MOMENTUM || kind > ORACLE_LION)
+    int kind, after;
+    if (split_kind(kind_arg, &kind, &after) || kind < ORACLE_MOMENTUM || kind > ORACLE_LION ||
+        (after && kind != ORACLE_LION))
         return -1;
     double decay = 1.0 - lr * weight_decay;
     for (int64_t i = 0; i < n; i++) {
@@ -492,7 +527,7 @@ int oracle_update1_f64(int kind, double* param, const double* grad, double* stat
 #endif
             double c = beta1 * m + (1.0 - beta1) * g;
             double u = (c != c) ? c : (double)((c > 0.0) - (c < 0.0));
-            param[i] = p * decay - lr * u;
+            param[i] = after ? (p - lr * u) * decay : p * decay - lr * u;
 #if ORACLE_PLANT == 18
             state1[i] = m;
 #else
@@ -553,16 +588,19 @@ static double clip_factor(double max_unorm, double p_sq, double u_sq)
  * element left alone by skip_zeros contributes u = 0.  The squared norms
  * are summed in binary64 in index order, s is rounded to binary32, and each
  * parameter becomes p*d - fl32(lr*s)*u.  The moments are those of the
- * unclipped step.  max_unorm = 0 gives oracle_update_f32 exactly.
+ * unclipped step.  max_unorm = 0 gives oracle_update_f32 exactly.  With
+ * ORACLE_DECAY_AFTER each parameter becomes (p - fl32(lr*s)*u)*d.
  * *scale_out (if not NULL) receives s.  Returns 0, -1 on an invalid kind or
  * dtype, -2 if out of memory. */
-int oracle_update_f32_clip(int kind, int dtype, void* param, const void* grad,
+int oracle_update_f32_clip(int kind_arg, int dtype, void* param, const void* grad,
                            float* state1, float* state2, int64_t n,
                            float beta1, float beta2, float beta3, float alpha, float eps,
                            float weight_decay, int64_t step, float lr, int skip_zeros,
                            float max_unorm, float* scale_out)
 {
-    if ((kind != ORACLE_ADAM && kind != ORACLE_ADEMAMIX) ||
+    int kind, after;
+    if (split_kind(kind_arg, &kind, &after) ||
+        (kind != ORACLE_ADAM && kind != ORACLE_ADEMAMIX) ||
         (dtype != ORACLE_F32 && dtype != ORACLE_F16 && dtype != ORACLE_BF16))
         return -1;
     oracle_scalars32 s;
@@ -586,7 +624,7 @@ int oracle_update_f32_clip(int kind, int dtype, void* param, const void* grad,
 #if ORACLE_PLANT == 15
     p_sq = 0.0;                                     /* planted: norm of the new parameter */
     for (int64_t i = 0; i < n; i++) {
-        float pn = param_f32(load_storage(param, dtype, i), u[i], s.decay, lr);
+        float pn = param_f32(load_storage(param, dtype, i), u[i], s.decay, lr, after);
         p_sq += (double)pn * (double)pn;
     }
 #endif
@@ -594,7 +632,7 @@ int oracle_update_f32_clip(int kind, int dtype, void* param, const void* grad,
     float lr_eff = lr * scale;
     for (int64_t i = 0; i < n; i++) {
         if (skip[i]) continue;
-        store_storage(param, dtype, i, param_f32(load_storage(param, dtype, i), u[i], s.decay, lr_eff));
+        store_storage(param, dtype, i, param_f32(load_storage(param, dtype, i), u[i], s.decay, lr_eff, after));
     }
     if (scale_out) *scale_out = scale;
     free(u);
@@ -606,12 +644,13 @@ int oracle_update_f32_clip(int kind, int dtype, void* param, const void* grad,
  * taken from an unclipped step with lr = 1 and no decay (as p_old - p_new;
  * that difference rounds at the level of ulp(p), far below the tolerance of
  * the closed forms this instantiation is checked against). */
-int oracle_update_f64_clip(int kind, double* param, const double* grad, double* state1,
+int oracle_update_f64_clip(int kind_arg, double* param, const double* grad, double* state1,
                            double* state2, int64_t n, double beta1, double beta2, double beta3,
                            double alpha, double eps, double weight_decay, int64_t step,
                            double lr, int skip_zeros, double max_unorm, double* scale_out)
 {
-    if (kind != ORACLE_ADAM && kind != ORACLE_ADEMAMIX)
+    int kind, after;
+    if (split_kind(kind_arg, &kind, &after) || (kind != ORACLE_ADAM && kind != ORACLE_ADEMAMIX))
         return -1;
     double* p_new = (double*)malloc((size_t)(n > 0 ? n : 1) * sizeof(double));
     double* p_old = (double*)malloc((size_t)(n > 0 ? n : 1) * sizeof(double));
@@ -643,7 +682,7 @@ int oracle_update_f64_clip(int kind, double* param, const double* grad, double* 
     for (int64_t i = 0; i < n; i++) {
         double u = p_old[i] - p_new[i];
         if (skip_zeros && grad[i] == 0.0) continue;
-        param[i] = p_old[i] * decay - (lr * scale) * u;
+        param[i] = after ? (p_old[i] - (lr * scale) * u) * decay : p_old[i] * decay - (lr * scale) * u;
     }
     if (scale_out) *scale_out = scale;
     free(p_new);

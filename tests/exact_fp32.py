@@ -168,10 +168,11 @@ def step_scalars(beta1: float, beta2: float, beta3: float, lr: float, wd: float,
 
 def element_step(kind: str, p: F, g: F, m: F, v: F, m2: F | None, sc: dict[str, F],
                  beta1: F, beta2: F, beta3: F, alpha: F, eps: F, lr: F,
-                 skip_zeros: bool) -> tuple[F, F, F, F | None, bool]:
+                 skip_zeros: bool, after: bool = False) -> tuple[F, F, F, F | None, bool]:
     """One element of the update, operation by operation.  Returns
     (p, m, v, m2, written) with p still in binary32 (round it to storage
-    afterwards); written is False when skip_zeros leaves the element alone."""
+    afterwards); written is False when skip_zeros leaves the element alone.
+    after: the decay multiplies the updated parameter, (p - lr u) d."""
     if skip_zeros and g.v == 0:
         return p, m, v, m2, False
     m = add(mul(beta1, m), mul(sc["omb1"], g))
@@ -183,12 +184,16 @@ def element_step(kind: str, p: F, g: F, m: F, v: F, m2: F | None, sc: dict[str, 
     den = add(sqrt(vh), eps)
     num = add(mh, mul(alpha, m2)) if kind == "ademamix" else mh
     u = div(num, den)
-    p = sub(mul(p, sc["decay"]), mul(lr, u))
+    if after:
+        p = mul(sub(p, mul(lr, u)), sc["decay"])
+    else:
+        p = sub(mul(p, sc["decay"]), mul(lr, u))
     return p, m, v, m2, True
 
 
 def element_step1(kind: str, p: F, g: F, m: F, beta1: F, beta2: F, eps: F, wd: F, lr: F,
-                  decay: F, first: bool, skip_zeros: bool) -> tuple[F, F, bool]:
+                  decay: F, first: bool, skip_zeros: bool,
+                  after: bool = False) -> tuple[F, F, bool]:
     """One element of a one-state kind (momentum, rmsprop, adagrad, lion),
     operation by operation; returns (p, m, written) with p in binary32."""
     if skip_zeros and g.v == 0:
@@ -197,7 +202,7 @@ def element_step1(kind: str, p: F, g: F, m: F, beta1: F, beta2: F, eps: F, wd: F
     if kind == "lion":
         c = add(mul(beta1, m), mul(sub(one, beta1), g))
         u = F(Fraction((c.v > 0) - (c.v < 0)))
-        pn = sub(mul(p, decay), mul(lr, u))
+        pn = mul(sub(p, mul(lr, u)), decay) if after else sub(mul(p, decay), mul(lr, u))
         m = add(mul(beta2, m), mul(sub(one, beta2), g))
         return pn, m, True
     gd = add(g, mul(wd, p)) if wd.v != 0 else g

@@ -36,7 +36,7 @@ def _run_f32(orc, kind, dtype, p, grads_per_step, hp, steps, s1=None, s2=None):
     n = p.size
     p = p.copy()
     if s1 is None:
-        s1 = np.zeros((2 if kind == O.ADEMAMIX else 1) * n, np.float32)
+        s1 = np.zeros((2 if kind & 0xff == O.ADEMAMIX else 1) * n, np.float32)
         s2 = np.zeros(n, np.float32)
     for t in range(1, steps + 1):
         orc.update_f32(kind, dtype, p, grads_per_step(t), s1, s2, hp, t)
@@ -46,7 +46,7 @@ def _run_f32(orc, kind, dtype, p, grads_per_step, hp, steps, s1=None, s2=None):
 def _run_f64(orc, kind, p0, g, hp, steps):
     n = p0.size
     p = p0.astype(np.float64).copy()
-    s1 = np.zeros((2 if kind == O.ADEMAMIX else 1) * n)
+    s1 = np.zeros((2 if kind & 0xff == O.ADEMAMIX else 1) * n)
     s2 = np.zeros(n)
     gg = g.astype(np.float64)
     out = []
@@ -387,7 +387,7 @@ def _storage_value(a: np.ndarray, sname: str) -> np.ndarray:
     return (a.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
 
 
-def _emulate_and_compare(orc, kind_name, kind, sname, dtype, p, gsteps, hp, T):
+def _emulate_and_compare(orc, kind_name, kind, sname, dtype, p, gsteps, hp, T, after=False):
     n = p.size
     pv = [X.F.of(float(x)) for x in _storage_value(p, sname)]
     m = [X.F.of(0.0) for _ in range(n)]
@@ -399,6 +399,7 @@ def _emulate_and_compare(orc, kind_name, kind, sname, dtype, p, gsteps, hp, T):
     po = p.copy()
     s1 = np.zeros((2 if kind == O.ADEMAMIX else 1) * n, np.float32)
     s2 = np.zeros(n, np.float32)
+    karg = kind | (O.DECAY_AFTER if after else 0)
     for t in range(1, T + 1):
         sc = X.step_scalars(f32(hp.beta1), f32(hp.beta2), f32(hp.beta3), f32(hp.lr),
                             f32(hp.weight_decay), t)
@@ -407,10 +408,10 @@ def _emulate_and_compare(orc, kind_name, kind, sname, dtype, p, gsteps, hp, T):
             g = X.F.of(float(gv[i]))
             pn, m[i], v[i], m2[i], wrote = X.element_step(
                 kind_name, pv[i], g, m[i], v[i], m2[i], sc, b1, b2, b3, al, ep, lr,
-                bool(hp.skip_zeros))
+                bool(hp.skip_zeros), after)
             if wrote:
                 pv[i] = X.to_storage(pn, sname)
-        orc.update_f32(kind, dtype, po, gsteps[t - 1], s1, s2, hp, t)
+        orc.update_f32(karg, dtype, po, gsteps[t - 1], s1, s2, hp, t)
         got_p = _storage_value(po, sname)
         for i in range(n):
             ctx = (kind_name, sname, hp, t, i)
@@ -665,10 +666,174 @@ def pin_exact_emulation_one_state(orc):
                         assert mv[i].bits_equal(float(so[i])), ("m", ctx, float(mv[i]), so[i])
 
 
+# ------------------------------------------------------ weight-decay order
+
+def pin_decay_after_by_hand(orc):
+    """The two decay orders on one element where they differ grossly:
+    lr 0.5, wd 1 (d = 0.5), p0 = 0.5, g = 0.25, zero states.  At step 1 the
+    bias-corrected moments are g and g^2, so u = g/(|g| + eps) ~ 1 and
+        old-parameter decay:    p*d - lr*u   = 0.25 - 0.5  ~ -0.25
+        updated-parameter decay: (p - lr*u)*d = (0.5 - 0.5) * 0.5 ~ 0
+    (both within the rounding of u, ~1e-7).  The same for Lion, whose u is
+    sign(c) = 1 exactly: -0.25 and 0 exactly."""
+    hp = O.HParams(lr=0.5, beta1=0.9, beta2=0.999, beta3=0.9999, alpha=0.0, eps=1e-8,
+                   weight_decay=1.0)
+    for kind in (O.ADAM, O.ADEMAMIX):
+        for after, want in ((False, -0.25), (True, 0.0)):
+            p = np.array([0.5], np.float32)
+            s1 = np.zeros(2 if kind == O.ADEMAMIX else 1, np.float32)
+            s2 = np.zeros(1, np.float32)
+            orc.update_f32(kind | (O.DECAY_AFTER if after else 0), O.F32, p,
+                           np.array([0.25], np.float32), s1, s2, hp, 1)
+            assert abs(float(p[0]) - want) <= 1e-6, (kind, after, p)
+    for after, want in ((False, -0.25), (True, 0.0)):
+        p = np.array([0.5], np.float32)
+        m = np.zeros(1, np.float32)
+        orc.update1_f32(O.LION | (O.DECAY_AFTER if after else 0), O.F32, p,
+                        np.array([0.25], np.float32), m, hp, 1)
+        assert float(p[0]) == want, (after, p)
+
+
+def pin_decay_after_closed_form_f64(orc):
+    """Constant gradient g, zero states, decay after the update: each step
+    is p_t = (p_(t-1) - c_t) d with c_t = lr g (1 + alpha (1 - b3^t)) /
+    (|g| + eps) (alpha = 0 for Adam), so
+        p_t = d^t p0 - sum_k d^(t-k+1) c_k;
+    Lion: c_t = lr sign(g).  Compared with the binary64 oracle at several
+    steps (1e-12 relative)."""
+    g = np.array([1.0, -0.5, 3e-3, -2.5e-6, 7.0], np.float64)
+    p0 = np.array([0.5, -0.25, 0.125, 0.9, -0.75], np.float64)
+    T = 300
+    hp = O.HParams(lr=1e-3, beta1=0.9, beta2=0.999, beta3=0.9999, alpha=5.0, eps=1e-8,
+                   weight_decay=0.1)
+    d = 1.0 - hp.lr * hp.weight_decay
+    for kind in (O.ADAM, O.ADEMAMIX, O.LION):
+        p = p0.copy()
+        n = g.size
+        s1 = np.zeros((2 if kind == O.ADEMAMIX else 1) * n)
+        s2 = np.zeros(n)
+        for t in range(1, T + 1):
+            if kind == O.LION:
+                orc.update1_f64(kind | O.DECAY_AFTER, p, g, s1, hp, t)
+            else:
+                orc.update_f64(kind | O.DECAY_AFTER, p, g, s1, s2, hp, t)
+            if t in (1, 2, 10, 300):
+                ref = d ** t * p0
+                for k in range(1, t + 1):
+                    if kind == O.LION:
+                        c = hp.lr * np.sign(g)
+                    else:
+                        coef = 1.0 + (hp.alpha * (1.0 - hp.beta3 ** k) if kind == O.ADEMAMIX else 0.0)
+                        c = hp.lr * g * coef / (np.abs(g) + hp.eps)
+                    ref = ref - d ** (t - k + 1) * c
+                assert np.all(np.abs(p - ref) <= 1e-12 * (np.abs(p0) + t * hp.lr * 6)), (kind, t, p, ref)
+
+
+def pin_decay_after_invariants(orc):
+    """With wd = 0 (d = 1 exactly) both orders give the same bits for every
+    decoupled kind; with wd > 0 they differ; the flag is refused by the L2
+    kinds (their decay is part of the gradient, so it has no order)."""
+    n, T = 257, 5
+    gen = rng(31, 0)
+    p0 = gen.uniform(-1, 1, n).astype(np.float32)
+    gs = [gen.standard_normal(n).astype(np.float32) for _ in range(T)]
+    for wd, same in ((0.0, True), (0.05, False)):
+        hp = O.HParams(lr=0.01, weight_decay=wd)
+        for kind in (O.ADAM, O.ADEMAMIX):
+            a = _run_f32(orc, kind, O.F32, p0, lambda t: gs[t - 1], hp, T)
+            b = _run_f32(orc, kind | O.DECAY_AFTER, O.F32, p0, lambda t: gs[t - 1], hp, T)
+            assert (a[0].tobytes() == b[0].tobytes()) == same, (kind, wd)
+            assert a[1].tobytes() == b[1].tobytes() and a[2].tobytes() == b[2].tobytes()
+        res = []
+        for karg in (O.LION, O.LION | O.DECAY_AFTER):
+            p, m = p0.copy(), np.zeros(n, np.float32)
+            for t in range(1, T + 1):
+                orc.update1_f32(karg, O.F32, p, gs[t - 1], m, O.HParams(lr=0.01, weight_decay=wd), t)
+            res.append((p, m))
+        assert (res[0][0].tobytes() == res[1][0].tobytes()) == same, ("lion", wd)
+        assert res[0][1].tobytes() == res[1][1].tobytes()
+    for kind in (O.MOMENTUM, O.RMSPROP, O.ADAGRAD):
+        try:
+            orc.update1_f32(kind | O.DECAY_AFTER, O.F32, p0.copy(), gs[0], np.zeros(n, np.float32),
+                            O.HParams(), 1)
+        except ValueError:
+            continue
+        raise AssertionError(f"kind {kind} accepted the decay-order flag")
+
+
+def pin_decay_after_clip(orc):
+    """Clipping with the decay after the update: a bound far above the
+    update (s = 1) gives the unclipped flagged step bitwise; an active
+    bound moves p to (p - fl32(lr s) u) d, checked through the realised
+    step norm at wd = 0.5, lr = 0.1 (d = 0.95)."""
+    n, T = 513, 3
+    gen = rng(33, 0)
+    p0 = gen.uniform(-1, 1, n).astype(np.float32)
+    gs = [np.where(gen.random(n) < 0.2, 0.0, gen.standard_normal(n)).astype(np.float32)
+          for _ in range(T)]
+    for kind in (O.ADAM, O.ADEMAMIX):
+        karg = kind | O.DECAY_AFTER
+        hp = O.HParams(weight_decay=0.01, skip_zeros=True)
+        ref = _run_f32(orc, karg, O.F32, p0, lambda t: gs[t - 1], hp, T)
+        p = p0.copy()
+        s1, s2 = np.zeros_like(ref[1]), np.zeros_like(ref[2])
+        for t in range(1, T + 1):
+            assert orc.update_f32_clip(karg, O.F32, p, gs[t - 1], s1, s2, hp, t, 1e30) == 1.0
+        assert p.tobytes() == ref[0].tobytes() and s1.tobytes() == ref[1].tobytes()
+        hp = O.HParams(lr=0.1, weight_decay=0.5)
+        bound = 0.1
+        p = p0.copy()
+        s1, s2 = np.zeros_like(ref[1]), np.zeros_like(ref[2])
+        sc = orc.update_f32_clip(karg, O.F32, p, gs[0], s1, s2, hp, 1, bound)
+        assert 0.0 < sc < 1.0
+        d = float(np.float32(1.0 - 0.1 * float(np.float32(0.5))))
+        step = p0.astype(np.float64) - p.astype(np.float64) / d
+        want = hp.lr * bound * np.linalg.norm(p0.astype(np.float64))
+        assert abs(np.linalg.norm(step) - want) <= 1e-4 * want, (np.linalg.norm(step), want)
+
+
+def pin_exact_emulation_decay_after(orc):
+    """Rounding of the decay-after order: a few elements, both two-state
+    kinds and Lion, every storage, 6 steps, bitwise equal to the operations
+    each rounded once."""
+    n, T = 5, 6
+    gen = rng(35, 0)
+    for kind_name, kind in (("adam", O.ADAM), ("ademamix", O.ADEMAMIX)):
+        for sname, dtype in (("fp32", O.F32), ("fp16", O.F16), ("bf16", O.BF16)):
+            hp = O.HParams(lr=1e-2, weight_decay=0.1, skip_zeros=True)
+            p = cast_storage(gen.uniform(-1, 1, n).astype(np.float32), sname)
+            gsteps = [cast_storage(np.where(gen.random(n) < 0.2, 0.0, gen.standard_normal(n)).astype(np.float32), sname)
+                      for _ in range(T)]
+            _emulate_and_compare(orc, kind_name, kind, sname, dtype, p, gsteps, hp, T, after=True)
+    f32 = lambda x: float(np.float32(x))
+    for sname, dtype in (("fp32", O.F32), ("bf16", O.BF16)):
+        hp = O.HParams(lr=1e-2, beta1=0.9, beta2=0.99, weight_decay=0.5)
+        p = cast_storage(gen.uniform(-1, 1, n).astype(np.float32), sname)
+        pv = [X.F.of(float(x)) for x in _storage_value(p, sname)]
+        mv = [X.F.of(0.0) for _ in range(n)]
+        b1, b2, ep, w, lr = (X.F.of(f32(x)) for x in (hp.beta1, hp.beta2, hp.eps, hp.weight_decay, hp.lr))
+        decay = X.rnd(X.f64(1 - X.f64(Fraction(f32(hp.lr)) * Fraction(f32(hp.weight_decay)))), False)
+        po, so = p.copy(), np.zeros(n, np.float32)
+        for t in range(1, T + 1):
+            gst = cast_storage(gen.standard_normal(n).astype(np.float32), sname)
+            gv = _storage_value(gst, sname)
+            for i in range(n):
+                pn, mv[i], _ = X.element_step1("lion", pv[i], X.F.of(float(gv[i])), mv[i], b1, b2,
+                                               ep, w, lr, decay, t == 1, False, after=True)
+                pv[i] = X.to_storage(pn, sname)
+            orc.update1_f32(O.LION | O.DECAY_AFTER, dtype, po, gst, so, hp, t)
+            got = _storage_value(po, sname)
+            for i in range(n):
+                assert pv[i].bits_equal(float(got[i])), ("lion p", sname, t, i)
+                assert mv[i].bits_equal(float(so[i])), ("lion m", sname, t, i)
+
+
 INDEPENDENT = [pin_closed_form_f64, pin_f32_tracks_f64, pin_first_step_by_hand,
                pin_torch_adam, pin_zero_gradient, pin_ademamix_reduces_to_adam,
                pin_element_independence, pin_grad_unchanged, pin_conversions_sample,
                pin_clip_reduces_to_plain, pin_clip_closed_form_f64, pin_clip_realised_norm,
                pin_one_state_torch, pin_one_state_closed_form_f64, pin_one_state_zero_gradient,
-               pin_lion_by_hand]
-ALL = INDEPENDENT + [pin_exact_emulation, pin_exact_emulation_one_state]
+               pin_lion_by_hand, pin_decay_after_by_hand, pin_decay_after_closed_form_f64,
+               pin_decay_after_invariants, pin_decay_after_clip]
+ALL = INDEPENDENT + [pin_exact_emulation, pin_exact_emulation_one_state,
+                     pin_exact_emulation_decay_after]
