@@ -83,6 +83,17 @@ typedef enum {
     OU_LION = 5
 } ou_kind;
 
+/* Weight-decay order.  The page says (section "Scope") that the order of
+ * the decoupled decay and the step differs between versions of the update
+ * without saying which is right.  By default the decay applies to the old
+ * parameter, p*d - lr*u (Loshchilov & Hutter, Alg. 2; torch.optim.AdamW).
+ * Every `kind` argument below may be OR'ed with OU_DECAY_AFTER to decay the
+ * updated parameter instead: (p - lr*u)*d, rounded once per operation as
+ * written.  Valid with ADAM, ADEMAMIX and LION (the kinds with decoupled
+ * decay); OU_EINVAL with the others.  With weight_decay = 0 (d = 1) both
+ * orders give the same bits.  A plan keeps the order it was created with. */
+#define OU_DECAY_AFTER 0x100
+
 enum {
     OU_OK = 0,
     OU_EINVAL = -1,       /* bad pointer, size, kind, dtype, step or hyperparameter */

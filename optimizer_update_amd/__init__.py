@@ -60,14 +60,17 @@ class HParams:
                                self.weight_decay, self.lr, int(bool(self.skip_zeros)), int(step))
 
 
-def _kind(kind) -> int:
-    return KINDS[kind] if isinstance(kind, str) else int(kind)
+def _kind(kind, decay_after: bool = False) -> int:
+    """The C kind argument: an ou_kind, OR'ed with OU_DECAY_AFTER when the
+    decoupled decay is to apply to the updated parameter, (p - lr*u)*d."""
+    k = KINDS[kind] if isinstance(kind, str) else int(kind)
+    return k | (_lib.OU_DECAY_AFTER if decay_after else 0)
 
 
 def state_sizes(kind, n: int) -> tuple[int, int]:
     """Elements of state1 and state2 for a tensor of n elements (state2 is 0
     for the one-state kinds)."""
-    k = _kind(kind)
+    k = _kind(kind) & ~_lib.OU_DECAY_AFTER
     return (2 * n if k == _lib.OU_ADEMAMIX else n), (n if k in TWO_STATE else 0)
 
 
@@ -106,6 +109,7 @@ class _on_device:
 
 
 def _tensor_args(kind: int, param, grad, state1, state2) -> tuple[int, int]:
+    kind &= ~_lib.OU_DECAY_AFTER
     two = kind in TWO_STATE
     if not two and state2 is not None:
         raise ValueError("the one-state kinds take state2=None")
@@ -142,9 +146,11 @@ def optimizer_update_32bit(kind, param: torch.Tensor, grad: torch.Tensor, state1
                            state2: torch.Tensor | None, *, step: int, lr: float, beta1: float = 0.9,
                            beta2: float = 0.999, beta3: float = 0.9999, alpha: float = 5.0,
                            eps: float = 1e-8, weight_decay: float = 0.0, skip_zeros: bool = False,
-                           stream=None) -> None:
-    """One update of one tensor, in place, on ``stream`` (default: current)."""
-    k = _kind(kind)
+                           decay_after: bool = False, stream=None) -> None:
+    """One update of one tensor, in place, on ``stream`` (default: current).
+    decay_after: decay the updated parameter, (p - lr*u)*d (Adam, AdEMAMix,
+    Lion)."""
+    k = _kind(kind, decay_after)
     n, dt = _tensor_args(k, param, grad, state1, state2)
     lib = load()
     with _on_device(param.device):
@@ -176,12 +182,13 @@ def optimizer_update_32bit_clip(kind, param: torch.Tensor, grad: torch.Tensor,
                                 lr: float, max_unorm: float, workspace: torch.Tensor | None = None,
                                 beta1: float = 0.9, beta2: float = 0.999, beta3: float = 0.9999,
                                 alpha: float = 5.0, eps: float = 1e-8, weight_decay: float = 0.0,
-                                skip_zeros: bool = False, stream=None) -> torch.Tensor | None:
+                                skip_zeros: bool = False, decay_after: bool = False,
+                                stream=None) -> torch.Tensor | None:
     """One update of one tensor with update-norm clipping (max_unorm > 0),
     in place.  ``workspace``: a uint8 device tensor of
     ``clip_workspace_bytes(n)`` bytes (allocated here if None); returned so
     that ``clip_scale`` can read the clip factor."""
-    k = _kind(kind)
+    k = _kind(kind, decay_after)
     n, dt = _tensor_args(k, param, grad, state1, state2)
     if workspace is None and max_unorm > 0 and n > 0:
         workspace = clip_workspace(n, param.device)
@@ -209,12 +216,13 @@ def _segments(kind: int, segments) -> ctypes.Array:
     return arr
 
 
-def optimizer_update_32bit_multi(kind, segments, hp: HParams, step: int, stream=None) -> None:
+def optimizer_update_32bit_multi(kind, segments, hp: HParams, step: int, stream=None,
+                                 decay_after: bool = False) -> None:
     """One update of a collection [(param, grad, state1, state2), ...]
     (state2 None for the one-state kinds): one
     launch per dtype group.  Builds the table on every call and waits for
     the stream; use ``Plan`` for repeated steps."""
-    k = _kind(kind)
+    k = _kind(kind, decay_after)
     if not segments:
         return
     arr = _segments(k, segments)
@@ -233,8 +241,8 @@ class Plan:
     The tensors' storage must stay allocated and in place until ``close``;
     the plan keeps references to them."""
 
-    def __init__(self, kind, segments):
-        self.kind = _kind(kind)
+    def __init__(self, kind, segments, decay_after: bool = False):
+        self.kind = _kind(kind, decay_after)
         self._tensors = [tuple(s) for s in segments]
         self.device = (self._tensors[0][0].device if self._tensors
                        else torch.device("cuda", torch.cuda.current_device()))

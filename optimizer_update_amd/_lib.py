@@ -17,6 +17,7 @@ HEADER = os.path.join(os.path.dirname(HERE), "include", "optimizer_update.h")
 
 OU_F32, OU_F16, OU_BF16 = 0, 1, 2
 OU_ADAM, OU_ADEMAMIX, OU_MOMENTUM, OU_RMSPROP, OU_ADAGRAD, OU_LION = 0, 1, 2, 3, 4, 5
+OU_DECAY_AFTER = 0x100
 STATUS = {0: "OU_OK", -1: "OU_EINVAL", -2: "OU_EUNSUPPORTED", -3: "OU_EALIGN",
           -4: "OU_EOVERLAP", -5: "OU_ENOMEM", -6: "OU_EHIP", -7: "OU_ECAPTURE"}
 

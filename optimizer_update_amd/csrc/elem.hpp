@@ -37,6 +37,8 @@ struct StepScalars {
     float weight_decay;       // L2 coefficient of the momentum/RMSprop/Adagrad kinds
     int32_t skip_zeros;
     int32_t first_step;       // step == 1 (momentum starts its buffer from the gradient)
+    int32_t decay_after;      // decoupled decay of the updated parameter: (p - lr*u)*d
+    int32_t pad;
 };
 
 // The moments of one element.  m: fast first moment, v: second moment,
@@ -66,10 +68,12 @@ __device__ __forceinline__ float direction(float m, float v, float m2, const Ste
 }
 
 // Decoupled weight decay of the old parameter and the step (Loshchilov &
-// Hutter, Algorithm 2).
-__device__ __forceinline__ float step_param(float p, float u, float decay, float lr)
+// Hutter, Algorithm 2), or, with `after`, the decay of the updated
+// parameter (the other order the update family has used).  The flag is
+// uniform over a launch; both forms are plain binary32 operations.
+__device__ __forceinline__ float step_param(float p, float u, float decay, float lr, int32_t after)
 {
-    return p * decay - lr * u;
+    return after ? (p - lr * u) * decay : p * decay - lr * u;
 }
 
 // One element of a one-state kind; m is the element's state.  gd adds the
@@ -80,14 +84,15 @@ __device__ __forceinline__ float step_param(float p, float u, float decay, float
 //            p - lr*(gd/(sqrt(m)+eps))
 //   Adagrad  (Duchi et al. 2011): m = m + gd*gd; p - lr*(gd/(sqrt(m)+eps))
 //   Lion     (Chen et al. 2023): c = beta1*m + (1-beta1)*g; p*d - lr*sign(c)
-//            (sign(0) = 0, NaN stays NaN); then m = beta2*m + (1-beta2)*g
+//            (sign(0) = 0, NaN stays NaN; decay order as for Adam); then
+//            m = beta2*m + (1-beta2)*g
 template <int KIND>
 __device__ __forceinline__ float update_one_state(float p, float g, float& m, const StepScalars& s)
 {
     if constexpr (KIND == kLion) {
         const float c = s.beta1 * m + s.omb1 * g;
         const float u = (c != c) ? c : static_cast<float>((c > 0.0f) - (c < 0.0f));
-        const float pn = p * s.decay - s.lr * u;
+        const float pn = step_param(p, u, s.decay, s.lr, s.decay_after);
         m = s.beta2 * m + s.omb2 * g;
         return pn;
     } else {
@@ -114,7 +119,7 @@ __device__ __forceinline__ float update_element(float p, float g, float& m, floa
 {
     if constexpr (kTwoState<KIND>) {
         update_moments<KIND>(g, m, v, m2, s);
-        return step_param(p, direction<KIND>(m, v, m2, s), s.decay, s.lr);
+        return step_param(p, direction<KIND>(m, v, m2, s), s.decay, s.lr, s.decay_after);
     } else {
         return update_one_state<KIND>(p, g, m, s);
     }

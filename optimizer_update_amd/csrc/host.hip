@@ -127,6 +127,19 @@ bool valid_kind(int kind) { return kind >= OU_ADAM && kind <= OU_LION; }
 // Adam and AdEMAMix read and write state2; the one-state kinds ignore it.
 bool two_state(int kind) { return kind == OU_ADAM || kind == OU_ADEMAMIX; }
 
+// A kind argument is an ou_kind, optionally OR'ed with OU_DECAY_AFTER
+// (kinds with decoupled decay only: ADAM, ADEMAMIX, LION).
+int split_kind(int arg, int* kind, int* after)
+{
+    const int base = arg & ~OU_DECAY_AFTER;
+    if (!valid_kind(base)) return fail(OU_EINVAL, "unknown kind %d", arg);
+    *kind = base;
+    *after = (arg & OU_DECAY_AFTER) ? 1 : 0;
+    if (*after && !two_state(base) && base != OU_LION)
+        return fail(OU_EINVAL, "OU_DECAY_AFTER applies to ADAM, ADEMAMIX and LION only (kind %d)", base);
+    return OU_OK;
+}
+
 int check_hparams(int kind, const ou_hparams& h)
 {
     if (!valid_kind(kind)) return fail(OU_EINVAL, "unknown kind %d", kind);
@@ -208,7 +221,7 @@ bool streams_16b_aligned(int kind, const ou_segment& s)
 
 // bc = fl32(1 - fl64(beta^step)) and d = fl32(1 - fl64(lr * wd)) in binary64
 // from the binary32 arguments; 1 - beta in binary32.
-StepScalars make_scalars(const ou_hparams& h)
+StepScalars make_scalars(const ou_hparams& h, int decay_after)
 {
     StepScalars s;
     const double t = static_cast<double>(h.step);
@@ -227,6 +240,8 @@ StepScalars make_scalars(const ou_hparams& h)
     s.weight_decay = h.weight_decay;
     s.skip_zeros = h.skip_zeros ? 1 : 0;
     s.first_step = h.step == 1 ? 1 : 0;
+    s.decay_after = decay_after;
+    s.pad = 0;
     return s;
 }
 
@@ -346,6 +361,7 @@ struct Group {
 
 struct ou_plan_s {
     int kind = 0;
+    int decay_after = 0;
     int64_t n_elements = 0;
     void* dmem = nullptr;
     std::vector<std::pair<int, int64_t>> seg_map;   // caller's index -> (group, slot), group -1 if n = 0
@@ -358,10 +374,11 @@ struct ou_plan_s {
 namespace ou {
 namespace {
 
-int build_plan(int kind, const ou_segment* segs, int32_t nseg, ou_plan_s** out)
+int build_plan(int kind_arg, const ou_segment* segs, int32_t nseg, ou_plan_s** out)
 {
     *out = nullptr;
-    if (!valid_kind(kind)) return fail(OU_EINVAL, "unknown kind %d", kind);
+    int kind = 0, after = 0;
+    if (int st = split_kind(kind_arg, &kind, &after)) return st;
     if (nseg < 0 || (nseg > 0 && !segs)) return fail(OU_EINVAL, "bad segment array");
     std::vector<Range> ranges;
     ranges.reserve(static_cast<size_t>(nseg) * 4);
@@ -374,6 +391,7 @@ int build_plan(int kind, const ou_segment* segs, int32_t nseg, ou_plan_s** out)
     ou_plan_s* plan = new (std::nothrow) ou_plan_s;
     if (!plan) return fail(OU_ENOMEM, "plan");
     plan->kind = kind;
+    plan->decay_after = after;
     (void)hipGetDevice(&plan->device);
 
     // Host tables per dtype group: descriptors, then work items (largest
@@ -562,11 +580,13 @@ using namespace ou;
 extern "C" {
 
 __attribute__((visibility("default")))
-int optimizer_update_32bit(int kind, int dtype, void* param, const void* grad, float* state1,
+int optimizer_update_32bit(int kind_arg, int dtype, void* param, const void* grad, float* state1,
                            float* state2, int64_t n, float beta1, float beta2, float beta3,
                            float alpha, float eps, float weight_decay, int64_t step, float lr,
                            int skip_zeros, void* stream)
 {
+    int kind = 0, after = 0;
+    if (int st = split_kind(kind_arg, &kind, &after)) return st;
     ou_hparams h;
     h.beta1 = beta1; h.beta2 = beta2; h.beta3 = beta3; h.alpha = alpha; h.eps = eps;
     h.weight_decay = weight_decay; h.lr = lr; h.skip_zeros = skip_zeros; h.step = step;
@@ -588,7 +608,7 @@ int optimizer_update_32bit(int kind, int dtype, void* param, const void* grad, f
         L.lds < 0 || L.lds > dp->lds_per_block)
         return fail(OU_EINVAL, "no kernel for block=%d epl=%d unroll=%d grid=%lld", L.block, L.epl,
                     L.unroll, (long long)L.grid);
-    StepScalars sc = make_scalars(h);
+    StepScalars sc = make_scalars(h, after);
     int32_t vec_ok = vec ? 1 : 0;
     void* args[] = {&param, const_cast<void**>(&grad), &state1, &state2, &n, &sc, &vec_ok};
     hipError_t e = launch(fn, L.grid, L.block, L.lds, args, static_cast<hipStream_t>(stream));
@@ -604,7 +624,7 @@ int64_t ou_clip_workspace_bytes(int64_t n)
 }
 
 __attribute__((visibility("default")))
-int optimizer_update_32bit_clip(int kind, int dtype, void* param, const void* grad, float* state1,
+int optimizer_update_32bit_clip(int kind_arg, int dtype, void* param, const void* grad, float* state1,
                                 float* state2, int64_t n, float beta1, float beta2, float beta3,
                                 float alpha, float eps, float weight_decay, int64_t step, float lr,
                                 int skip_zeros, float max_unorm, void* workspace,
@@ -613,9 +633,11 @@ int optimizer_update_32bit_clip(int kind, int dtype, void* param, const void* gr
     if (!std::isfinite(max_unorm) || max_unorm < 0.0f)
         return fail(OU_EINVAL, "max_unorm must be finite and >= 0 (got %g)", max_unorm);
     if (max_unorm == 0.0f)
-        return optimizer_update_32bit(kind, dtype, param, grad, state1, state2, n, beta1, beta2,
+        return optimizer_update_32bit(kind_arg, dtype, param, grad, state1, state2, n, beta1, beta2,
                                       beta3, alpha, eps, weight_decay, step, lr, skip_zeros, stream);
-    if (valid_kind(kind) && !two_state(kind))
+    int kind = 0, after = 0;
+    if (int st = split_kind(kind_arg, &kind, &after)) return st;
+    if (!two_state(kind))
         return fail(OU_EINVAL, "update-norm clipping is defined for ADAM and ADEMAMIX only");
     ou_hparams h;
     h.beta1 = beta1; h.beta2 = beta2; h.beta3 = beta3; h.alpha = alpha; h.eps = eps;
@@ -655,7 +677,7 @@ int optimizer_update_32bit_clip(int kind, int dtype, void* param, const void* gr
         return fail(OU_EINVAL, "no clip kernel for block=%d unroll=%d", L.block, L.unroll);
     const int64_t chunks = (n + kClipChunkElems - 1) / kClipChunkElems;
     if (chunks > INT32_MAX) return fail(OU_EINVAL, "tensor too large");
-    StepScalars sc = make_scalars(h);
+    StepScalars sc = make_scalars(h, after);
     int32_t vec_ok = vec ? 1 : 0;
     float* out = static_cast<float*>(workspace);
     double2* partials = reinterpret_cast<double2*>(static_cast<unsigned char*>(workspace) + 256);
@@ -679,16 +701,18 @@ int optimizer_update_32bit_clip(int kind, int dtype, void* param, const void* gr
 }
 
 __attribute__((visibility("default")))
-int optimizer_update_32bit_multi(int kind, const ou_segment* segs, int32_t nseg, const ou_hparams* hp,
+int optimizer_update_32bit_multi(int kind_arg, const ou_segment* segs, int32_t nseg, const ou_hparams* hp,
                                  void* stream)
 {
     if (!hp) return fail(OU_EINVAL, "null hparams");
+    int kind = 0, after = 0;
+    if (int st = split_kind(kind_arg, &kind, &after)) return st;
     if (int st = check_hparams(kind, *hp)) return st;
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (capturing(s)) return fail(OU_ECAPTURE, "optimizer_update_32bit_multi allocates; use a plan under capture");
     ou_plan_s* plan = nullptr;
-    if (int st = build_plan(kind, segs, nseg, &plan)) return st;
-    int st = plan_launch(plan, make_scalars(*hp), s);
+    if (int st = build_plan(kind_arg, segs, nseg, &plan)) return st;
+    int st = plan_launch(plan, make_scalars(*hp, after), s);
     hipError_t e = hipStreamSynchronize(s);
     ou_plan_destroy(plan);
     if (st) return st;
@@ -710,7 +734,7 @@ int ou_plan_step(ou_plan plan, const ou_hparams* hp, void* stream)
     if (!plan || !hp) return fail(OU_EINVAL, "null plan or hparams");
     if (int st = check_hparams(plan->kind, *hp)) return st;
     if (int st = check_plan_device(plan)) return st;
-    return plan_launch(plan, make_scalars(*hp), static_cast<hipStream_t>(stream));
+    return plan_launch(plan, make_scalars(*hp, plan->decay_after), static_cast<hipStream_t>(stream));
 }
 
 __attribute__((visibility("default")))
@@ -721,10 +745,11 @@ int ou_plan_step_clip(ou_plan plan, const ou_hparams* hp, float max_unorm, void*
         return fail(OU_EINVAL, "max_unorm must be finite and >= 0 (got %g)", max_unorm);
     if (int st = check_hparams(plan->kind, *hp)) return st;
     if (int st = check_plan_device(plan)) return st;
-    if (max_unorm == 0.0f) return plan_launch(plan, make_scalars(*hp), static_cast<hipStream_t>(stream));
+    const StepScalars sc = make_scalars(*hp, plan->decay_after);
+    if (max_unorm == 0.0f) return plan_launch(plan, sc, static_cast<hipStream_t>(stream));
     if (!two_state(plan->kind))
         return fail(OU_EINVAL, "update-norm clipping is defined for ADAM and ADEMAMIX only");
-    return plan_launch_clip(plan, make_scalars(*hp), max_unorm, static_cast<hipStream_t>(stream));
+    return plan_launch_clip(plan, sc, max_unorm, static_cast<hipStream_t>(stream));
 }
 
 __attribute__((visibility("default")))
@@ -756,7 +781,7 @@ int ou_plan_graph_step(ou_plan plan, const ou_hparams* hp, void* stream)
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (capturing(s)) return fail(OU_ECAPTURE, "ou_plan_graph_step inside a stream capture");
     if (plan->groups.empty()) return OU_OK;
-    const StepScalars sc = make_scalars(*hp);
+    const StepScalars sc = make_scalars(*hp, plan->decay_after);
     hipError_t e;
     if (!plan->exec) {
         e = hipGraphCreate(&plan->graph, 0);
@@ -885,7 +910,7 @@ __attribute__((visibility("default")))
 int ou__step_scalars(const ou_hparams* hp, float out[12])
 {
     if (!hp || !out) return OU_EINVAL;
-    StepScalars s = make_scalars(*hp);
+    StepScalars s = make_scalars(*hp, 0);
     const float v[12] = {s.beta1, s.beta2, s.beta3, s.omb1, s.omb2, s.omb3,
                          s.alpha, s.eps, s.lr, s.bc1, s.bc2, s.decay};
     std::memcpy(out, v, sizeof v);

@@ -479,7 +479,7 @@ __device__ __forceinline__ void clip_step4(float pv[4], const float gv[4], const
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
         const float dir = direction<KIND>(mv[j], vv[j], m2v[j], sc);
-        const float pn = step_param(pv[j], dir, sc.decay, lr);
+        const float pn = step_param(pv[j], dir, sc.decay, lr, sc.decay_after);
         if (!(sc.skip_zeros && gv[j] == 0.0f)) pv[j] = pn;
     }
 }
@@ -494,7 +494,7 @@ __device__ __forceinline__ void clip_step1(typename S::raw* __restrict__ p,
     if (sc.skip_zeros && S::widen(g[i]) == 0.0f) return;
     const float m2 = (KIND == kAdemamix) ? s1[n + i] : 0.0f;
     const float dir = direction<KIND>(s1[i], s2[i], m2, sc);
-    p[i] = S::narrow(step_param(S::widen(p[i]), dir, sc.decay, lr));
+    p[i] = S::narrow(step_param(S::widen(p[i]), dir, sc.decay, lr, sc.decay_after));
 }
 
 // Pass 3: the parameter step with the clipped learning rate *lr_eff, any

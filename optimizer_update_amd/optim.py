@@ -26,7 +26,8 @@ from . import (DTYPES, TWO_STATE, HParams, Plan, _kind, _on_device, _ptr, _raw_s
 class _Collection:
     kind = "adam"
 
-    def __init__(self, params, hp: HParams, grads=None, max_unorm: float = 0.0):
+    def __init__(self, params, hp: HParams, grads=None, max_unorm: float = 0.0,
+                 decay_after: bool = False):
         self.params = [p.data if isinstance(p, torch.nn.Parameter) else p for p in params]
         if grads is None:
             grads = []
@@ -39,6 +40,7 @@ class _Collection:
                 grads.append(g)
         self.grads = list(grads)
         self.hp = hp
+        self.decay_after = bool(decay_after)
         two = _kind(self.kind) in TWO_STATE
         if max_unorm and not two:
             raise ValueError("update-norm clipping is defined for Adam and AdEMAMix only")
@@ -52,7 +54,8 @@ class _Collection:
         self.max_unorm = float(max_unorm)
         self._workspace = None
         self._direct = None
-        self.plan = Plan(self.kind, list(zip(self.params, self.grads, self.state1, self.state2)))
+        self.plan = Plan(self.kind, list(zip(self.params, self.grads, self.state1, self.state2)),
+                         decay_after=self.decay_after)
 
     def segments(self):
         return list(zip(self.params, self.grads, self.state1, self.state2))
@@ -88,12 +91,13 @@ class _Collection:
                                             workspace=self._workspace, beta1=h.beta1,
                                             beta2=h.beta2, beta3=h.beta3, alpha=h.alpha,
                                             eps=h.eps, weight_decay=h.weight_decay,
-                                            skip_zeros=h.skip_zeros, stream=stream)
+                                            skip_zeros=h.skip_zeros,
+                                            decay_after=self.decay_after, stream=stream)
             return
         if self._direct is None:
             for p, g, s1, s2 in self.segments():   # full checks once
                 _tensor_args(_kind(self.kind), p, g, s1, s2)
-            self._direct = [(_kind(self.kind), DTYPES[p.dtype], p.data_ptr(), g.data_ptr(),
+            self._direct = [(_kind(self.kind, self.decay_after), DTYPES[p.dtype], p.data_ptr(), g.data_ptr(),
                              s1.data_ptr(), _ptr(s2), p.numel())
                             for p, g, s1, s2 in self.segments()]
         lib = load()
@@ -130,10 +134,10 @@ class AdamW32(_Collection):
     kind = "adam"
 
     def __init__(self, params, lr=1e-3, betas=(0.9, 0.999), eps=1e-8, weight_decay=0.01,
-                 skip_zeros=False, grads=None, max_unorm=0.0):
+                 skip_zeros=False, grads=None, max_unorm=0.0, decay_after=False):
         super().__init__(params, HParams(lr=lr, beta1=betas[0], beta2=betas[1], eps=eps,
                                          weight_decay=weight_decay, skip_zeros=skip_zeros), grads,
-                         max_unorm)
+                         max_unorm, decay_after)
 
 
 class AdEMAMix32(_Collection):
@@ -141,10 +145,11 @@ class AdEMAMix32(_Collection):
     kind = "ademamix"
 
     def __init__(self, params, lr=1e-3, betas=(0.9, 0.999, 0.9999), alpha=5.0, eps=1e-8,
-                 weight_decay=0.01, skip_zeros=False, grads=None, max_unorm=0.0):
+                 weight_decay=0.01, skip_zeros=False, grads=None, max_unorm=0.0,
+                 decay_after=False):
         super().__init__(params, HParams(lr=lr, beta1=betas[0], beta2=betas[1], beta3=betas[2],
                                          alpha=alpha, eps=eps, weight_decay=weight_decay,
-                                         skip_zeros=skip_zeros), grads, max_unorm)
+                                         skip_zeros=skip_zeros), grads, max_unorm, decay_after)
 
 
 class Momentum32(_Collection):
@@ -186,6 +191,7 @@ class Lion32(_Collection):
     kind = "lion"
 
     def __init__(self, params, lr=1e-4, betas=(0.9, 0.99), weight_decay=0.0, skip_zeros=False,
-                 grads=None):
+                 grads=None, decay_after=False):
         super().__init__(params, HParams(lr=lr, beta1=betas[0], beta2=betas[1], eps=0.0,
-                                         weight_decay=weight_decay, skip_zeros=skip_zeros), grads)
+                                         weight_decay=weight_decay, skip_zeros=skip_zeros), grads,
+                         0.0, decay_after)

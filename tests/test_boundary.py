@@ -80,6 +80,12 @@ def _segs(*rows):
     ("adam null state2", dict(s2=0), OU_EINVAL),
     ("lion beta2 = 1", dict(kind=5, b2=1.0), OU_EINVAL),
     ("momentum state1 overlaps param", dict(kind=2, s1=0x10000 + 32), OU_EOVERLAP),
+    ("decay-after with momentum", dict(kind=2 | 0x100), OU_EINVAL),
+    ("decay-after with rmsprop", dict(kind=3 | 0x100), OU_EINVAL),
+    ("decay-after with adagrad", dict(kind=4 | 0x100), OU_EINVAL),
+    ("unknown flag bit", dict(kind=0 | 0x200), OU_EINVAL),
+    ("decay-after, unknown kind", dict(kind=6 | 0x100), OU_EINVAL),
+    ("decay-after adam, bad beta", dict(kind=0 | 0x100, b1=1.0), OU_EINVAL),
     ("unknown dtype", dict(dtype=3), OU_EINVAL),
     ("negative n", dict(n=-1), OU_EINVAL),
     ("step 0", dict(step=0), OU_EINVAL),
@@ -104,6 +110,18 @@ def _segs(*rows):
 def test_single_entry_validation(L, case, kw, code):
     assert _call(L, **kw) == code, case
     assert L.ou_last_error().decode(), "an error message is set"
+
+
+@pytest.mark.parametrize("kind", [0x100, 0x101, 0x105])
+def test_decay_after_flag_passes_validation(L, kind):
+    assert _call(L, kind=kind, s2=0x40000 if kind != 0x105 else 0) not in (OU_EINVAL, OU_EALIGN, OU_EOVERLAP)
+    h = ctypes.c_void_p()
+    st = L.ou_plan_create(kind, _segs((0x100000, 0x200000, 0x300000, 0x400000, 1024, 0, 0)), 1,
+                          ctypes.byref(h))
+    assert st not in (OU_EINVAL, OU_EALIGN, OU_EOVERLAP)
+    assert not h.value or L.ou_plan_destroy(h) is None
+    assert L.ou_plan_create(0x102, _segs((0x100000, 0x200000, 0x300000, 0, 1024, 0, 0)), 1,
+                            ctypes.byref(h)) == OU_EINVAL
 
 
 @pytest.mark.parametrize("kind", [2, 3, 4, 5])
@@ -192,7 +210,7 @@ def test_clip_entry_validation(L):
     assert _clip(L, step=0) == OU_EINVAL
     assert _clip(L, n=0) == OU_OK                           # nothing to do
     assert _clip(L, max_unorm=0.0, n=0, ws=0) == OU_OK        # plain step, no workspace
-    for kind in (2, 3, 4, 5):                                # clipping: two-state kinds only
+    for kind in (2, 3, 4, 5, 0x105):                         # clipping: two-state kinds only
         assert _clip(L, kind=kind) == OU_EINVAL
         assert _clip(L, kind=kind, max_unorm=0.0, n=0, ws=0) == OU_OK
 
