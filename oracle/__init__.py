@@ -38,6 +38,8 @@ ONE_STATE = (MOMENTUM, RMSPROP, ADAGRAD, LION)
 # OR'ed into a kind: decoupled decay applied to the updated parameter,
 # (p - lr*u)*d, instead of the default p*d - lr*u (ADAM, ADEMAMIX, LION).
 DECAY_AFTER = 0x100
+# elements per block of the 8-bit block-wise states
+QBLOCK = 256
 DTYPES = {"fp32": F32, "fp16": F16, "bf16": BF16}
 
 # -O2 without contraction or fast-math: each C operation is one correctly
@@ -115,6 +117,15 @@ class Oracle:
         lib.oracle_update1_f32.restype = ci
         lib.oracle_update1_f64.argtypes = [ci, vp, vp, vp, i64, f64, f64, f64, f64, i64, f64, ci]
         lib.oracle_update1_f64.restype = ci
+        lib.oracle_qmap.argtypes = [ci, vp]
+        lib.oracle_qmap.restype = ci
+        lib.oracle_qcode.argtypes = [ci, f32]
+        lib.oracle_qcode.restype = ci
+        lib.oracle_qvalue.argtypes = [ci, ci]
+        lib.oracle_qvalue.restype = f32
+        lib.oracle_update_8bit_f32.argtypes = [ci, ci, vp, vp, vp, vp, vp, vp, i64, f32, f32, f32,
+                                               f32, f32, f32, i64, f32, ci, ci]
+        lib.oracle_update_8bit_f32.restype = ci
         lib.oracle_step_scalars.argtypes = [f32, f32, f32, f32, f32, i64,
                                             ctypes.POINTER(_Scalars32)]
         lib.oracle_step_scalars.restype = None
@@ -207,6 +218,40 @@ class Oracle:
                                           int(bool(hp.skip_zeros)))
         if rc != 0:
             raise ValueError(f"oracle_update1_f64 rejected kind={kind}")
+
+    def qmap(self, signed: bool) -> np.ndarray:
+        """Magnitudes of the 8-bit dynamic type: 128 (signed) or 256 (unsigned)."""
+        out = np.zeros(256, np.float32)
+        count = self._lib.oracle_qmap(int(bool(signed)), _ptr(out))
+        return out[:count].copy()
+
+    def qcode(self, signed: bool, x: float) -> int:
+        """Code of a normalised value (``oracle_qcode``)."""
+        return int(self._lib.oracle_qcode(int(bool(signed)), float(x)))
+
+    def qvalue(self, signed: bool, code: int) -> float:
+        """Normalised value of a code (``oracle_qvalue``)."""
+        return float(self._lib.oracle_qvalue(int(bool(signed)), int(code)))
+
+    def update_8bit_f32(self, kind: int, dtype: int, param: np.ndarray, grad: np.ndarray,
+                        state1: np.ndarray, state2: np.ndarray, absmax1: np.ndarray,
+                        absmax2: np.ndarray, hp: HParams, step: int, nthreads: int = 1) -> None:
+        """One step with 8-bit block-wise states, in place (``oracle_update_8bit_f32``)."""
+        n = param.size
+        k = 2 if kind & 0xff == ADEMAMIX else 1
+        nb = -(-n // QBLOCK)
+        sdt = np.float32 if dtype == F32 else np.uint16
+        assert param.dtype == sdt and grad.dtype == sdt and grad.size == n
+        assert state1.dtype == np.uint8 and state1.size == k * n
+        assert state2.dtype == np.uint8 and state2.size == n
+        assert absmax1.dtype == np.float32 and absmax1.size == k * nb
+        assert absmax2.dtype == np.float32 and absmax2.size == nb
+        rc = self._lib.oracle_update_8bit_f32(
+            kind, dtype, _ptr(param), _ptr(grad), _ptr(state1), _ptr(state2), _ptr(absmax1),
+            _ptr(absmax2), n, hp.beta1, hp.beta2, hp.beta3, hp.alpha, hp.eps, hp.weight_decay,
+            step, hp.lr, int(bool(hp.skip_zeros)), nthreads)
+        if rc != 0:
+            raise ValueError(f"oracle_update_8bit_f32 rejected kind={kind} dtype={dtype}")
 
     def update_f32_clip(self, kind: int, dtype: int, param: np.ndarray, grad: np.ndarray,
                         state1: np.ndarray, state2: np.ndarray, hp: HParams, step: int,

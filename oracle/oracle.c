@@ -39,6 +39,11 @@
  * (the page's "max_unorm"; it names the option only, so the clip rule is
  * stated at the function).
  *
+ * oracle_update_8bit_f32 keeps the moments in 8-bit block-wise states
+ * (the page's AdamW8bit collections, whose tensors below min_8bit_size fall
+ * back to the 32-bit path); the data type and the step are stated at the
+ * functions.
+ *
  * Weight-decay order.  The page (section "Scope") says the order of the
  * decoupled decay and the step is being changed upstream without saying
  * which order is right.  The default here decays the old parameter,
@@ -687,6 +692,222 @@ int oracle_update_f64_clip(int kind_arg, double* param, const double* grad, doub
     if (scale_out) *scale_out = scale;
     free(p_new);
     free(p_old);
+    return 0;
+}
+
+
+/* ------------------------------------------------ 8-bit block-wise states */
+
+/* The 8-bit dynamic data type of block-wise quantized optimizer states
+ * (Dettmers, "8-bit approximations for parallelism in deep learning", 2016,
+ * dynamic tree quantization; Dettmers, Lewis, Shleifer & Zettlemoyer,
+ * "8-bit Optimizers via Block-wise Quantization", 2022, section 2).  The page
+ * names the 8-bit optimizers only (section "B300 benchmark and
+ * acceptance"), so the type is written from that description:
+ *
+ *   signed code (first moments):  bit 7 = sign; the 7 payload bits hold the
+ *       magnitude index 0..127.
+ *   unsigned code (second moment): the sign bit is given to the payload; 8
+ *       payload bits, magnitude index 0..255.
+ *
+ * Magnitude index 0 is zero.  The others enumerate, for E = P-1 down to 0
+ * (P = payload bits), the decade 10^-E: in the tree code, E leading zero
+ * bits, a 1 ending the exponent, and F = P-1-E fraction bits that split
+ * [0.1, 1] into 2^F equal bins; a value is its bin's centre
+ *     fl32( (0.1 + ((j + 1/2) * 0.9) / 2^F) / 10^E )   (binary64, then rounded)
+ * with j = 0 .. 2^F - 1 ascending.  The largest magnitude (E = 0, last bin)
+ * is replaced by 1, so that a block's largest state, which normalises to
+ * +-1, is kept exactly.  Magnitudes increase with the index. */
+#define OQ_BLOCK 256
+
+static int qmap_payload(int is_signed) { return is_signed ? 7 : 8; }
+
+/* Writes the 2^P magnitudes (128 signed, 256 unsigned); returns the count. */
+int oracle_qmap(int is_signed, float* mags)
+{
+    int P = qmap_payload(is_signed);
+    int k = 0;
+    mags[k++] = 0.0f;
+    for (int E = P - 1; E >= 0; E--) {
+        int F = P - 1 - E;
+        double bins = (double)(1 << F);
+        double decade = 1.0;
+        for (int e = 0; e < E; e++) decade *= 10.0;
+        for (int j = 0; j < (1 << F); j++) {
+            double centre = 0.1 + (((double)j + 0.5) * 0.9) / bins;
+            mags[k++] = (float)(centre / decade);
+        }
+    }
+#if ORACLE_PLANT != 28
+    mags[k - 1] = 1.0f;
+#endif
+    return k;
+}
+
+/* Decision points between neighbouring magnitudes: the midpoint of two
+ * binary32 values, formed exactly in binary64 and rounded to binary32.  A
+ * magnitude a rounds to index #{k : b_k < a}: to the nearest magnitude, a
+ * value exactly on a decision point going to the smaller one. */
+static int qmap_index(const float* mags, int count, float a)
+{
+    int idx = 0;
+    for (int k = 0; k + 1 < count; k++) {
+        float b = (float)(((double)mags[k] + (double)mags[k + 1]) * 0.5);
+#if ORACLE_PLANT == 23
+        b = mags[k + 1];                            /* planted: truncation, not nearest */
+#endif
+        if (b < a) idx++;
+    }
+    return idx;
+}
+
+/* Code of a normalised value x in [-1, 1] (x >= 0 for the unsigned type). */
+int oracle_qcode(int is_signed, float x)
+{
+    float mags[256];
+    int count = oracle_qmap(is_signed, mags);
+    float a = fabsf(x);
+    int idx = qmap_index(mags, count, a);
+    if (is_signed && x < 0.0f) idx |= 0x80;
+    return idx;
+}
+
+/* Normalised value of a code. */
+float oracle_qvalue(int is_signed, int code)
+{
+    float mags[256];
+    oracle_qmap(is_signed, mags);
+    if (!is_signed) return mags[code & 0xff];
+    float v = mags[code & 0x7f];
+    return (code & 0x80) ? -v : v;
+}
+
+/* One step with 8-bit block-wise states (kinds ADAM, ADEMAMIX; the kind may
+ * carry ORACLE_DECAY_AFTER), in place.
+ *   state1  : n signed codes (ADAM) or 2n (ADEMAMIX: fast EMA, then slow EMA)
+ *   state2  : n unsigned codes
+ *   absmax1 : one float per block of 256 elements (ADAM) or two planes
+ *             (ADEMAMIX: [0, nb) fast, [nb, 2nb) slow), nb = ceil(n / 256)
+ *   absmax2 : nb floats
+ * Block b covers elements [256 b, min(n, 256 (b + 1))).  Per block:
+ *   1. each state is its code's value times the block's absmax;
+ *   2. the 32-bit rule of oracle_update_f32 updates the moments and the
+ *      parameter from these values (skip_zeros: the element's moments keep
+ *      their values and its parameter is not written);
+ *   3. the new absmax of each state is the largest |value| in the block
+ *      (maxNum: a NaN is passed over);
+ *   4. each state is stored as the code of value / absmax (0 when the absmax
+ *      is 0).
+ * The parameter moves with the moments before they are quantized.  Zero
+ * codes with zero absmax are the zero state.  Returns 0, -1 on an invalid
+ * kind or dtype, -2 if out of memory. */
+int oracle_update_8bit_f32(int kind_arg, int dtype, void* param, const void* grad,
+                           uint8_t* state1, uint8_t* state2, float* absmax1, float* absmax2,
+                           int64_t n, float beta1, float beta2, float beta3, float alpha,
+                           float eps, float weight_decay, int64_t step, float lr,
+                           int skip_zeros, int nthreads)
+{
+    int kind, after;
+    if (split_kind(kind_arg, &kind, &after) ||
+        (kind != ORACLE_ADAM && kind != ORACLE_ADEMAMIX) ||
+        (dtype != ORACLE_F32 && dtype != ORACLE_F16 && dtype != ORACLE_BF16))
+        return -1;
+    int block = OQ_BLOCK;
+#if ORACLE_PLANT == 27
+    block = 2 * OQ_BLOCK;                           /* planted: wrong block size */
+#endif
+    float smag[128], umag[256];
+    oracle_qmap(1, smag);
+    oracle_qmap(0, umag);
+    oracle_scalars32 s;
+    oracle_step_scalars(beta1, beta2, beta3, lr, weight_decay, step, &s);
+    const int64_t nb = (n + block - 1) / block;
+    const int two = kind == ORACLE_ADEMAMIX;
+    if (nthreads < 1) nthreads = 1;
+#pragma omp parallel for schedule(static) num_threads(nthreads)
+    for (int64_t b = 0; b < nb; b++) {
+        float m[2 * OQ_BLOCK], v[2 * OQ_BLOCK], m2[2 * OQ_BLOCK];
+        const int64_t i0 = b * block;
+        const int len = (int)((n - i0) < block ? (n - i0) : block);
+        /* 1. dequantize */
+        for (int k = 0; k < len; k++) {
+            int64_t i = i0 + k;
+            uint8_t c1 = state1[i], c2 = state2[i];
+            float q1 = (c1 & 0x80) ? -smag[c1 & 0x7f] : smag[c1 & 0x7f];
+#if ORACLE_PLANT == 26
+            q1 = umag[c1];                          /* planted: sign of the first moment lost */
+#endif
+            m[k] = q1 * absmax1[b];
+            v[k] = umag[c2] * absmax2[b];
+            m2[k] = 0.0f;
+            if (two) {
+                uint8_t c3 = state1[n + i];
+                m2[k] = ((c3 & 0x80) ? -smag[c3 & 0x7f] : smag[c3 & 0x7f]) * absmax1[nb + b];
+            }
+        }
+#if ORACLE_PLANT == 24
+        float old_a1 = 0.0f, old_a2 = 0.0f;         /* planted: absmax of the old states */
+        for (int k = 0; k < len; k++) { old_a1 = fmaxf(old_a1, fabsf(m[k])); old_a2 = fmaxf(old_a2, v[k]); }
+#endif
+        /* 2. the 32-bit update */
+        for (int k = 0; k < len; k++) {
+            int64_t i = i0 + k;
+            float g = load_storage(grad, dtype, i);
+            if (skip_zeros && g == 0.0f) continue;
+            float p = load_storage(param, dtype, i);
+            float pn = element_f32(kind, p, g, &m[k], &v[k], two ? &m2[k] : NULL, &s,
+                                   beta1, beta2, beta3, alpha, eps, lr, after);
+#if ORACLE_PLANT != 25
+            store_storage(param, dtype, i, pn);
+#else
+            (void)pn;
+#endif
+        }
+        /* 3. new absmax */
+        float a1 = 0.0f, a2 = 0.0f, a3 = 0.0f;
+        for (int k = 0; k < len; k++) {
+            a1 = fmaxf(a1, fabsf(m[k]));
+            a2 = fmaxf(a2, v[k]);
+            if (two) a3 = fmaxf(a3, fabsf(m2[k]));
+        }
+#if ORACLE_PLANT == 24
+        a1 = old_a1 > 0.0f ? old_a1 : a1;
+        a2 = old_a2 > 0.0f ? old_a2 : a2;
+#endif
+        /* 4. quantize */
+        for (int k = 0; k < len; k++) {
+            int64_t i = i0 + k;
+            float x1 = a1 > 0.0f ? m[k] / a1 : 0.0f;
+            float x2 = a2 > 0.0f ? v[k] / a2 : 0.0f;
+            int c1 = qmap_index(smag, 128, fabsf(x1));
+            if (x1 < 0.0f) c1 |= 0x80;
+            state1[i] = (uint8_t)c1;
+            state2[i] = (uint8_t)qmap_index(umag, 256, fabsf(x2));
+            if (two) {
+                float x3 = a3 > 0.0f ? m2[k] / a3 : 0.0f;
+                int c3 = qmap_index(smag, 128, fabsf(x3));
+                if (x3 < 0.0f) c3 |= 0x80;
+                state1[n + i] = (uint8_t)c3;
+            }
+        }
+        absmax1[b] = a1;
+        absmax2[b] = a2;
+        if (two) absmax1[nb + b] = a3;
+#if ORACLE_PLANT == 25
+        /* planted: the parameter moves with the quantized new moments */
+        for (int k = 0; k < len; k++) {
+            int64_t i = i0 + k;
+            float g = load_storage(grad, dtype, i);
+            if (skip_zeros && g == 0.0f) continue;
+            uint8_t c1 = state1[i];
+            float mq = ((c1 & 0x80) ? -smag[c1 & 0x7f] : smag[c1 & 0x7f]) * a1;
+            float vq = umag[state2[i]] * a2;
+            float den = sqrtf(vq / s.bc2) + eps;
+            float u = (mq / s.bc1) / den;
+            store_storage(param, dtype, i, param_f32(load_storage(param, dtype, i), u, s.decay, lr, after));
+        }
+#endif
+    }
     return 0;
 }
 

@@ -828,12 +828,276 @@ def pin_exact_emulation_decay_after(orc):
                 assert mv[i].bits_equal(float(so[i])), ("lion m", sname, t, i)
 
 
+
+# ------------------------------------------------- 8-bit block-wise states
+
+QB = O.QBLOCK
+
+
+def _blocks(n: int) -> int:
+    return -(-n // QB)
+
+
+def _zero_8bit(kind, n):
+    k = 2 if kind == O.ADEMAMIX else 1
+    return (np.zeros(k * n, np.uint8), np.zeros(n, np.uint8), np.zeros(k * _blocks(n), np.float32),
+            np.zeros(_blocks(n), np.float32))
+
+
+def _deq(orc, codes: np.ndarray, absmax: np.ndarray, signed: bool) -> np.ndarray:
+    """Dequantized block states, decoded from the map's magnitudes and the
+    code layout (sign bit, magnitude index), not with the oracle's decoder."""
+    mags = orc.qmap(signed).astype(np.float32)
+    c = codes.astype(np.int64)
+    if signed:
+        v = mags[c & 0x7f]
+        v = np.where(c & 0x80, -v, v).astype(np.float32)
+    else:
+        v = mags[c]
+    scale = np.repeat(absmax, QB)[:codes.size]
+    return (v * scale).astype(np.float32)
+
+
+def pin_qmap_structure(orc):
+    """The 8-bit dynamic type: 128 signed / 256 unsigned magnitudes, strictly
+    increasing from 0 to 1.  Decade E (values in (0.1, 1] x 10^-E) holds
+    2^(P-1-E) values (P = 7 payload bits signed, 8 unsigned) that form an
+    arithmetic progression with step 0.9 x 10^-E / 2^F starting half a step
+    above 0.1 x 10^-E, except that the top value of decade 0 is 1."""
+    for signed, P in ((True, 7), (False, 8)):
+        mags = orc.qmap(signed).astype(np.float64)
+        assert mags.size == 2 ** P and mags[0] == 0.0 and mags[-1] == 1.0
+        assert np.all(np.diff(mags) > 0)
+        for E in range(P):
+            F = P - 1 - E
+            lo, hi = 0.1 * 10.0 ** -E, 10.0 ** -E
+            dec = mags[(mags > lo * (1 - 1e-6)) & (mags <= hi * (1 + 1e-6))]
+            assert dec.size == 2 ** F, (signed, E, dec.size)
+            step = 0.9 * 10.0 ** -E / 2 ** F
+            want = lo + step * (np.arange(2 ** F) + 0.5)
+            if E == 0:
+                want[-1] = 1.0
+            assert np.allclose(dec, want, rtol=1e-6, atol=0), (signed, E)
+
+
+def pin_quantizer_nearest(orc):
+    """The quantizer picks a nearest magnitude (exact arithmetic), either one
+    when x lies within 2 binary32 ulps of the midpoint; every magnitude maps
+    to itself; the code is monotone in x; the sign bit carries the sign."""
+    gen = rng(41, 0)
+    for signed in (True, False):
+        mags = orc.qmap(signed).astype(np.float64)
+        mids = (mags[:-1] + mags[1:]) / 2
+        xs = np.concatenate([gen.uniform(0, 1, 3000), 10.0 ** gen.uniform(-9, 0, 3000),
+                             mids, np.nextafter(mids.astype(np.float32), 2).astype(np.float64),
+                             np.nextafter(mids.astype(np.float32), -1).astype(np.float64)])
+        xs = np.clip(xs.astype(np.float32), 0, 1)
+        for k, m in enumerate(mags):
+            assert orc.qcode(signed, float(np.float32(m))) == k, (signed, k)
+            if signed and k > 0:
+                assert orc.qcode(True, -float(np.float32(m))) == (k | 0x80)
+        prev = -1
+        for x in np.sort(xs):
+            c = orc.qcode(signed, float(x))
+            assert c >= prev, (signed, x)
+            prev = c
+            d = np.abs(mags - float(x))
+            near = np.flatnonzero(d <= d.min() * (1 + 1e-12))
+            if c not in near:
+                ulp = float(np.spacing(np.float32(x)))
+                assert np.min(np.abs(mids - float(x))) <= 2 * ulp, (signed, x, c, near)
+        if signed:
+            for x in gen.uniform(-1, 0, 500).astype(np.float32):
+                c = orc.qcode(True, float(x))
+                assert c == (orc.qcode(True, -float(x)) | 0x80), x
+
+
+def _uniform_block_grads(n, T, storage, gen):
+    """Gradients whose magnitude is constant inside each 256-element block
+    (drawn per block and step) with a fixed sign per element."""
+    sign = np.where(gen.random(n) < 0.5, -1.0, 1.0)
+    out = []
+    for _ in range(T):
+        mag = np.repeat(10.0 ** gen.uniform(-4, 0, _blocks(n)), QB)[:n]
+        mag = cast_storage(mag.astype(np.float32), storage)
+        mag = _storage_value(mag, storage)
+        out.append(cast_storage((sign * mag).astype(np.float32), storage))
+    return out
+
+
+def pin_8bit_uniform_blocks_match_32bit(orc):
+    """When every element of a block has the same gradient magnitude at each
+    step (signs fixed per element), every state in the block has the same
+    magnitude, normalises to +-1 and is stored exactly: the 8-bit trajectory
+    then equals the 32-bit oracle's bitwise (parameters, dequantized
+    moments, and absmax = |moment|), for both kinds, with weight decay, both
+    decay orders."""
+    n, T = 3 * QB + 77, 8
+    gen = rng(43, 0)
+    for kind in (O.ADAM, O.ADEMAMIX):
+        for sname, dtype in (("fp32", O.F32), ("bf16", O.BF16)):
+            for flag in (0, O.DECAY_AFTER):
+                hp = O.HParams(lr=1e-2, weight_decay=0.05)
+                p0 = cast_storage(gen.uniform(-1, 1, n).astype(np.float32), sname)
+                gs = _uniform_block_grads(n, T, sname, gen)
+                p8 = p0.copy()
+                s1, s2, a1, a2 = _zero_8bit(kind, n)
+                p32, r1, r2 = p0.copy(), *W_zero(kind, n)
+                for t in range(1, T + 1):
+                    orc.update_8bit_f32(kind | flag, dtype, p8, gs[t - 1], s1, s2, a1, a2, hp, t)
+                    orc.update_f32(kind | flag, dtype, p32, gs[t - 1], r1, r2, hp, t)
+                    ctx = (kind, sname, flag, t)
+                    assert p8.tobytes() == p32.tobytes(), ctx
+                    assert _deq(orc, s1[:n], a1[:_blocks(n)], True).tobytes() == r1[:n].tobytes(), ctx
+                    assert _deq(orc, s2, a2, False).tobytes() == r2.tobytes(), ctx
+                    if kind == O.ADEMAMIX:
+                        assert _deq(orc, s1[n:], a1[_blocks(n):], True).tobytes() == r1[n:].tobytes(), ctx
+
+
+def W_zero(kind, n):
+    return np.zeros((2 if kind == O.ADEMAMIX else 1) * n, np.float32), np.zeros(n, np.float32)
+
+
+def pin_8bit_first_step(orc):
+    """From the zero state, step 1 moves the parameters exactly as the 32-bit
+    step (the update uses the moments before they are quantized); the absmax
+    of each block is max |fl32((1-b1) g)| and max fl32((1-b2) fl32(g g)),
+    computed here with numpy; every stored state is a nearest quantization
+    of its moment relative to that absmax (within half the largest gap of
+    the type), and the block's largest moment is stored exactly."""
+    n = 4 * QB + 5
+    gen = rng(45, 0)
+    for kind in (O.ADAM, O.ADEMAMIX):
+        for sname, dtype in (("fp32", O.F32), ("fp16", O.F16), ("bf16", O.BF16)):
+            for pat in ("normal", "mixed"):
+                hp = O.HParams(lr=1e-3, weight_decay=0.01, skip_zeros=True)
+                p0 = cast_storage(gen.uniform(-1, 1, n).astype(np.float32), sname)
+                if pat == "normal":
+                    g = np.where(gen.random(n) < 0.1, 0.0, gen.standard_normal(n))
+                else:
+                    g = np.where(gen.random(n) < 0.5, -1, 1) * 10.0 ** gen.uniform(-6, 2, n)
+                g = cast_storage(g.astype(np.float32), sname)
+                p8 = p0.copy()
+                s1, s2, a1, a2 = _zero_8bit(kind, n)
+                orc.update_8bit_f32(kind, dtype, p8, g, s1, s2, a1, a2, hp, 1)
+                p32, r1, r2 = p0.copy(), *W_zero(kind, n)
+                orc.update_f32(kind, dtype, p32, g, r1, r2, hp, 1)
+                assert p8.tobytes() == p32.tobytes(), (kind, sname, pat)
+                gv = _storage_value(g, sname).astype(np.float32)
+                m_ref = (np.float32(1) - np.float32(hp.beta1)) * gv
+                v_ref = (np.float32(1) - np.float32(hp.beta2)) * (gv * gv)
+                pad = _blocks(n) * QB - n
+                A1 = np.abs(np.r_[m_ref, np.zeros(pad, np.float32)]).reshape(-1, QB).max(axis=1)
+                A2 = np.r_[v_ref, np.zeros(pad, np.float32)].reshape(-1, QB).max(axis=1)
+                assert a1[:_blocks(n)].tobytes() == A1.astype(np.float32).tobytes(), (kind, sname, pat)
+                assert a2.tobytes() == A2.astype(np.float32).tobytes()
+                for signed, codes, absmax, ref in ((True, s1[:n], A1, m_ref), (False, s2, A2, v_ref)):
+                    mags = orc.qmap(signed).astype(np.float64)
+                    half = np.max(np.diff(mags)) / 2
+                    deq = _deq(orc, codes, absmax.astype(np.float32), signed).astype(np.float64)
+                    scale = np.repeat(absmax, QB)[:n].astype(np.float64)
+                    assert np.all(np.abs(deq - ref) <= half * scale * (1 + 1e-6) + 1e-45), (kind, sname, pat)
+                    top = np.abs(ref) == scale
+                    assert np.all(deq[top] == ref[top]), "the block maximum is kept exactly"
+
+
+def pin_8bit_zero_gradient(orc):
+    """Zero gradients from the zero state: codes and absmax stay 0; with
+    wd = 0 the parameters do not move, with wd > 0 they follow the 32-bit
+    path (iterated decay) bitwise; skip_zeros leaves them untouched."""
+    n = 2 * QB + 3
+    p0 = rng(47, 0).uniform(-1, 1, n).astype(np.float32)
+    g = np.zeros(n, np.float32)
+    for kind in (O.ADAM, O.ADEMAMIX):
+        for wd, skip in ((0.0, False), (0.1, False), (0.1, True)):
+            hp = O.HParams(lr=0.1, weight_decay=wd, skip_zeros=skip)
+            p8 = p0.copy()
+            s1, s2, a1, a2 = _zero_8bit(kind, n)
+            p32, r1, r2 = p0.copy(), *W_zero(kind, n)
+            for t in range(1, 4):
+                orc.update_8bit_f32(kind, O.F32, p8, g, s1, s2, a1, a2, hp, t)
+                orc.update_f32(kind, O.F32, p32, g, r1, r2, hp, t)
+            assert not s1.any() and not s2.any() and not a1.any() and not a2.any()
+            assert p8.tobytes() == p32.tobytes(), (kind, wd, skip)
+            if wd == 0.0 or skip:
+                assert p8.tobytes() == p0.tobytes()
+
+
+def pin_8bit_block_independence(orc):
+    """A block's result depends on that block only: running each block as a
+    tensor of its own (the partial last block too) gives the same bits, and
+    permuting whole blocks permutes the results."""
+    n, T = 3 * QB + 77, 4
+    gen = rng(49, 0)
+    for kind in (O.ADAM, O.ADEMAMIX):
+        hp = O.HParams(lr=1e-2, weight_decay=0.01)
+        p0 = gen.uniform(-1, 1, n).astype(np.float32)
+        gs = [gen.standard_normal(n).astype(np.float32) for _ in range(T)]
+        full = (p0.copy(), *_zero_8bit(kind, n))
+        for t in range(1, T + 1):
+            orc.update_8bit_f32(kind, O.F32, full[0], gs[t - 1], *full[1:], hp, t)
+        nb = _blocks(n)
+        for b in range(nb):
+            lo, hi = b * QB, min(n, (b + 1) * QB)
+            part = (p0[lo:hi].copy(), *_zero_8bit(kind, hi - lo))
+            for t in range(1, T + 1):
+                orc.update_8bit_f32(kind, O.F32, part[0], gs[t - 1][lo:hi].copy(), *part[1:], hp, t)
+            assert part[0].tobytes() == full[0][lo:hi].tobytes(), (kind, b)
+            assert part[1][:hi - lo].tobytes() == full[1][lo:hi].tobytes()
+            assert part[2].tobytes() == full[2][lo:hi].tobytes()
+            assert part[3][0] == full[3][b] and part[4][0] == full[4][b]
+            if kind == O.ADEMAMIX:
+                assert part[1][hi - lo:].tobytes() == full[1][n + lo:n + hi].tobytes()
+                assert part[3][1] == full[3][nb + b]
+        m = 3 * QB                                   # permute the three full blocks
+        perm = [2, 0, 1]
+        idx = np.concatenate([np.arange(b * QB, (b + 1) * QB) for b in perm])
+        pp = (p0[:m][idx].copy(), *_zero_8bit(kind, m))
+        for t in range(1, T + 1):
+            orc.update_8bit_f32(kind, O.F32, pp[0], gs[t - 1][:m][idx].copy(), *pp[1:], hp, t)
+        assert pp[0].tobytes() == full[0][:m][idx].tobytes()
+        assert pp[2].tobytes() == full[2][:m][idx].tobytes()
+
+
+def pin_8bit_tracks_32bit(orc):
+    """Quantization error bound: the 8-bit and 32-bit moments obey the same
+    recurrence m_t = b m_(t-1) + (1-b) g_t, except that the 8-bit one is
+    requantized each step with an error of at most h A_t (h: half the largest
+    gap of the type, A_t: the block's absmax at step t).  So
+    |m8_t - m32_t| <= e_t with e_t = b e_(t-1) + h A_t, checked for every
+    element over 20 steps of random gradients (1e-6 relative slack for the
+    binary32 rounding of both paths)."""
+    n, T = 2 * QB + 31, 20
+    gen = rng(51, 0)
+    hp = O.HParams(lr=1e-3, weight_decay=0.0)
+    hs = np.max(np.diff(orc.qmap(True).astype(np.float64))) / 2
+    hu = np.max(np.diff(orc.qmap(False).astype(np.float64))) / 2
+    p0 = gen.uniform(-1, 1, n).astype(np.float32)
+    p8 = p0.copy()
+    s1, s2, a1, a2 = _zero_8bit(O.ADAM, n)
+    p32, r1, r2 = p0.copy(), *W_zero(O.ADAM, n)
+    e1 = np.zeros(n)
+    e2 = np.zeros(n)
+    for t in range(1, T + 1):
+        g = gen.standard_normal(n).astype(np.float32)
+        orc.update_8bit_f32(O.ADAM, O.F32, p8, g, s1, s2, a1, a2, hp, t)
+        orc.update_f32(O.ADAM, O.F32, p32, g, r1, r2, hp, t)
+        e1 = hp.beta1 * e1 + hs * np.repeat(a1, QB)[:n]
+        e2 = hp.beta2 * e2 + hu * np.repeat(a2, QB)[:n]
+        m8 = _deq(orc, s1, a1, True).astype(np.float64)
+        v8 = _deq(orc, s2, a2, False).astype(np.float64)
+        assert np.all(np.abs(m8 - r1) <= e1 * (1 + 1e-6) + 1e-6 * np.abs(r1)), t
+        assert np.all(np.abs(v8 - r2) <= e2 * (1 + 1e-6) + 1e-6 * np.abs(r2)), t
+
+
 INDEPENDENT = [pin_closed_form_f64, pin_f32_tracks_f64, pin_first_step_by_hand,
                pin_torch_adam, pin_zero_gradient, pin_ademamix_reduces_to_adam,
                pin_element_independence, pin_grad_unchanged, pin_conversions_sample,
                pin_clip_reduces_to_plain, pin_clip_closed_form_f64, pin_clip_realised_norm,
                pin_one_state_torch, pin_one_state_closed_form_f64, pin_one_state_zero_gradient,
                pin_lion_by_hand, pin_decay_after_by_hand, pin_decay_after_closed_form_f64,
-               pin_decay_after_invariants, pin_decay_after_clip]
+               pin_decay_after_invariants, pin_decay_after_clip, pin_qmap_structure,
+               pin_quantizer_nearest, pin_8bit_uniform_blocks_match_32bit, pin_8bit_first_step,
+               pin_8bit_zero_gradient, pin_8bit_block_independence, pin_8bit_tracks_32bit]
 ALL = INDEPENDENT + [pin_exact_emulation, pin_exact_emulation_one_state,
                      pin_exact_emulation_decay_after]

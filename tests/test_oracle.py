@@ -33,7 +33,7 @@ def test_conversion_strided_sweep(orc):
             P.check_conversions(orc, bits.astype(np.uint32))
 
 
-@pytest.mark.parametrize("plant", range(1, 23))
+@pytest.mark.parametrize("plant", range(1, 29))
 def test_planted_mistake_is_caught(plant, tmp_path):
     """A copy of the oracle with one planted mistake (dropped bias
     correction, eps inside the root, decay after the update, decay sign,
