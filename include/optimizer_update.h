@@ -210,6 +210,74 @@ int ou_plan_describe(ou_plan plan, int32_t* n_groups, int64_t* n_work_items,
  * still running).  NULL is a no-op. */
 void ou_plan_destroy(ou_plan plan);
 
+/* ---- 8-bit block-wise states ------------------------------------------
+ *
+ * The page times AdamW8bit collections, in which tensors of fewer than
+ * min_8bit_size = 4,096 elements take the 32-bit path above (sections
+ * "Problem" and "B300 benchmark and acceptance").  These entry points are
+ * the other leg: ADAM and ADEMAMIX (optionally | OU_DECAY_AFTER) with each
+ * moment kept as 8-bit codes plus one fp32 absmax per block of
+ * OU_8BIT_BLOCK elements (block-wise quantization, Dettmers et al. 2022).
+ *
+ * Codes.  First moments use the signed dynamic type (bit 7 = sign, bits 0-6
+ * = magnitude index), the second moment the unsigned one (bits 0-7 =
+ * magnitude index).  Magnitude index 0 is 0; the others are the centres of
+ * 2^F equal bins of [0.1, 1] in the decades 10^-E (the dynamic tree type of
+ * Dettmers 2016 with E + F = 6 signed, 7 unsigned), increasing with the
+ * index, the largest set to 1.  ou_8bit_qmap returns them.
+ *
+ * Step, per block of elements [256 b, min(n, 256 (b+1))):
+ *   1. each moment = magnitude(code) (signed as coded) * absmax[b];
+ *   2. the 32-bit rule above updates the moments and the parameter
+ *      (skip_zeros: the element's moments keep their values, its parameter
+ *      is not written);
+ *   3. the new absmax of each moment is its largest |value| in the block;
+ *   4. each moment is stored as the code of the magnitude nearest to
+ *      |value| / absmax (0 when absmax is 0), a value exactly halfway going
+ *      to the smaller magnitude; the midpoints are binary32 roundings of the
+ *      exact midpoints.
+ * All-zero codes with zero absmax are the zero state.
+ *
+ * Layout: state1 holds n codes (ADAM) or 2n (ADEMAMIX: fast EMA at [0, n),
+ * slow EMA at [n, 2n)); state2 n codes; absmax1 nb floats (ADAM) or 2nb
+ * (ADEMAMIX: [0, nb) fast, [nb, 2nb) slow); absmax2 nb floats, with
+ * nb = ceil(n / 256).  Device pointers, aligned to their element size; the
+ * wide path needs param and grad aligned to 4 elements and the code planes
+ * to 4 bytes (otherwise the same steps run element by element).  Errors,
+ * ownership and asynchrony as for optimizer_update_32bit. */
+#define OU_8BIT_BLOCK 256
+
+/* Copies the magnitudes of the signed (128) or unsigned (256) type to host
+ * memory `out`; count must be 128 or 256 accordingly. */
+int ou_8bit_qmap(int is_signed, float* out, int32_t count);
+
+int optimizer_update_8bit_blockwise(int kind, int dtype, void* param, const void* grad,
+                                    uint8_t* state1, uint8_t* state2, float* absmax1,
+                                    float* absmax2, int64_t n, float beta1, float beta2,
+                                    float beta3, float alpha, float eps, float weight_decay,
+                                    int64_t step, float lr, int skip_zeros, void* stream);
+
+/* One tensor of an 8-bit collection; layout as above. */
+typedef struct {
+    void* param;
+    const void* grad;
+    uint8_t* state1;
+    uint8_t* state2;
+    float* absmax1;
+    float* absmax2;
+    int64_t n;
+    int32_t dtype;
+    int32_t reserved; /* must be 0 */
+} ou_segment8;
+
+/* A plan over a fixed 8-bit collection: device-resident segment table and
+ * work list, one launch per dtype group per step (capture-safe).  Pointers
+ * must stay valid until ou_plan8_destroy.  Not thread-safe. */
+typedef struct ou_plan8_s* ou_plan8;
+int ou_plan8_create(int kind, const ou_segment8* segs, int32_t nseg, ou_plan8* out);
+int ou_plan8_step(ou_plan8 plan, const ou_hparams* hp, void* stream);
+void ou_plan8_destroy(ou_plan8 plan);
+
 const char* ou_status_string(int status);
 const char* ou_last_error(void);
 

@@ -306,7 +306,117 @@ class Plan:
             pass
 
 
+# ---------------------------------------------------- 8-bit block-wise states
+
+QBLOCK = _lib.OU_8BIT_BLOCK
+
+
+def qmap(signed: bool) -> torch.Tensor:
+    """Magnitudes of the 8-bit dynamic type (128 signed, 256 unsigned), as
+    the library defines them (``ou_8bit_qmap``)."""
+    count = 128 if signed else 256
+    out = (ctypes.c_float * count)()
+    lib = load()
+    check(lib.ou_8bit_qmap(int(bool(signed)), out, count), lib)
+    return torch.tensor(list(out), dtype=torch.float32)
+
+
+def state8_sizes(kind, n: int) -> tuple[int, int, int, int]:
+    """Sizes of (state1 codes, state2 codes, absmax1, absmax2) for n elements."""
+    k = 2 if (_kind(kind) & ~_lib.OU_DECAY_AFTER) == _lib.OU_ADEMAMIX else 1
+    nb = -(-n // QBLOCK)
+    return k * n, n, k * nb, nb
+
+
+def _tensor8_args(kind: int, param, grad, state1, state2, absmax1, absmax2) -> tuple[int, int]:
+    for name, t in (("param", param), ("grad", grad), ("state1", state1), ("state2", state2),
+                    ("absmax1", absmax1), ("absmax2", absmax2)):
+        if not isinstance(t, torch.Tensor) or not t.is_cuda:
+            raise ValueError(f"{name} must be a tensor on a HIP device")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+        if t.device != param.device:
+            raise ValueError("all tensors must be on one device")
+    dt = DTYPES.get(param.dtype)
+    if dt is None or grad.dtype != param.dtype:
+        raise ValueError("param and grad must share one of float32/float16/bfloat16")
+    if state1.dtype != torch.uint8 or state2.dtype != torch.uint8:
+        raise ValueError("8-bit states must be uint8")
+    if absmax1.dtype != torch.float32 or absmax2.dtype != torch.float32:
+        raise ValueError("absmax buffers must be float32")
+    n = param.numel()
+    want = state8_sizes(kind, n)
+    got = (state1.numel(), state2.numel(), absmax1.numel(), absmax2.numel())
+    if grad.numel() != n or got != want:
+        raise ValueError(f"sizes: n {n}, grad {grad.numel()}, states/absmax {got} (want {want})")
+    return n, dt
+
+
+def optimizer_update_8bit_blockwise(kind, param: torch.Tensor, grad: torch.Tensor,
+                                    state1: torch.Tensor, state2: torch.Tensor,
+                                    absmax1: torch.Tensor, absmax2: torch.Tensor, *, step: int,
+                                    lr: float, beta1: float = 0.9, beta2: float = 0.999,
+                                    beta3: float = 0.9999, alpha: float = 5.0, eps: float = 1e-8,
+                                    weight_decay: float = 0.0, skip_zeros: bool = False,
+                                    decay_after: bool = False, stream=None) -> None:
+    """One update with 8-bit block-wise states (uint8 codes, fp32 absmax per
+    256 elements), in place."""
+    k = _kind(kind, decay_after)
+    n, dt = _tensor8_args(k, param, grad, state1, state2, absmax1, absmax2)
+    lib = load()
+    with _on_device(param.device):
+        st = lib.optimizer_update_8bit_blockwise(k, dt, param.data_ptr(), grad.data_ptr(),
+                                                 state1.data_ptr(), state2.data_ptr(),
+                                                 absmax1.data_ptr(), absmax2.data_ptr(), n, beta1,
+                                                 beta2, beta3, alpha, eps, weight_decay, int(step),
+                                                 lr, int(bool(skip_zeros)), _stream(param, stream))
+    check(st, lib)
+
+
+class Plan8:
+    """Device-resident segment table of a fixed 8-bit collection
+    (``ou_plan8``): [(param, grad, state1, state2, absmax1, absmax2), ...]."""
+
+    def __init__(self, kind, segments, decay_after: bool = False):
+        self.kind = _kind(kind, decay_after)
+        self._tensors = [tuple(s) for s in segments]
+        self.device = (self._tensors[0][0].device if self._tensors
+                       else torch.device("cuda", torch.cuda.current_device()))
+        arr = (_lib.ou_segment8 * len(self._tensors))()
+        for i, s in enumerate(self._tensors):
+            n, dt = _tensor8_args(self.kind, *s)
+            arr[i] = _lib.ou_segment8(*(t.data_ptr() for t in s), n, dt, 0)
+        self._lib = load()
+        h = ctypes.c_void_p()
+        with _on_device(self.device):
+            check(self._lib.ou_plan8_create(self.kind, arr, len(self._tensors), ctypes.byref(h)),
+                  self._lib)
+        self._h = h
+
+    def step(self, hp: HParams, step: int, stream=None) -> None:
+        c = hp.c(step)
+        sh = (_raw_stream(self.device.index) if stream is None
+              else (stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)))
+        with _on_device(self.device):
+            check(self._lib.ou_plan8_step(self._h, ctypes.byref(c), sh), self._lib)
+
+    def close(self) -> None:
+        if getattr(self, "_h", None) is not None and self._h.value:
+            torch.cuda.synchronize(self.device)
+            self._lib.ou_plan8_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+__all__ += ["QBLOCK", "qmap", "state8_sizes", "optimizer_update_8bit_blockwise", "Plan8"]
+
 from .optim import AdamW32, AdEMAMix32, Adagrad32, Lion32, Momentum32, RMSprop32  # noqa: E402
+from .optim import AdamW8bit, AdEMAMix8bit  # noqa: E402
 
 __all__ += ["AdamW32", "AdEMAMix32", "Momentum32", "RMSprop32", "Adagrad32", "Lion32",
-            "TWO_STATE"]
+            "TWO_STATE", "AdamW8bit", "AdEMAMix8bit"]

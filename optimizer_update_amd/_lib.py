@@ -41,6 +41,16 @@ class ou_segment(ctypes.Structure):
                 ("n", ctypes.c_int64), ("dtype", ctypes.c_int32), ("reserved", ctypes.c_int32)]
 
 
+class ou_segment8(ctypes.Structure):
+    _fields_ = [("param", ctypes.c_void_p), ("grad", ctypes.c_void_p),
+                ("state1", ctypes.c_void_p), ("state2", ctypes.c_void_p),
+                ("absmax1", ctypes.c_void_p), ("absmax2", ctypes.c_void_p),
+                ("n", ctypes.c_int64), ("dtype", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+
+
+OU_8BIT_BLOCK = 256
+
+
 def header_functions(path: str = HEADER) -> list[str]:
     """Names of the functions the public header declares."""
     with open(path) as f:
@@ -88,6 +98,18 @@ def load(path: str = LIBRARY) -> ctypes.CDLL:
     lib.ou_plan_describe.restype = i32
     lib.ou_plan_destroy.argtypes = [vp]
     lib.ou_plan_destroy.restype = None
+    lib.ou_8bit_qmap.argtypes = [i32, ctypes.POINTER(f32), ctypes.c_int32]
+    lib.ou_8bit_qmap.restype = i32
+    lib.optimizer_update_8bit_blockwise.argtypes = [i32, i32, vp, vp, vp, vp, vp, vp, i64, f32, f32,
+                                                    f32, f32, f32, f32, i64, f32, i32, vp]
+    lib.optimizer_update_8bit_blockwise.restype = i32
+    lib.ou_plan8_create.argtypes = [i32, ctypes.POINTER(ou_segment8), ctypes.c_int32,
+                                    ctypes.POINTER(vp)]
+    lib.ou_plan8_create.restype = i32
+    lib.ou_plan8_step.argtypes = [vp, ctypes.POINTER(ou_hparams), vp]
+    lib.ou_plan8_step.restype = i32
+    lib.ou_plan8_destroy.argtypes = [vp]
+    lib.ou_plan8_destroy.restype = None
     lib.ou_status_string.argtypes = [i32]
     lib.ou_status_string.restype = ctypes.c_char_p
     lib.ou_last_error.argtypes = []
@@ -101,6 +123,8 @@ def load(path: str = LIBRARY) -> ctypes.CDLL:
     lib.ou__force_multi.restype = None
     lib.ou__step_scalars.argtypes = [ctypes.POINTER(ou_hparams), ctypes.POINTER(f32)]
     lib.ou__step_scalars.restype = i32
+    lib.ou__force_8bit.argtypes = [i32, i32, i32, i32]
+    lib.ou__force_8bit.restype = None
     if path == LIBRARY:
         _lib = lib
     return lib

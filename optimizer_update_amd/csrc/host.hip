@@ -23,15 +23,14 @@
 #include <vector>
 
 #include "../../include/optimizer_update.h"
+#include "host_internal.h"
 #include "internal.h"
 #include "ou_testing.h"
 
 namespace ou {
-namespace {
 
 thread_local std::string g_last_error;
 
-int fail(int status, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
 int fail(int status, const char* fmt, ...)
 {
     char buf[512];
@@ -96,7 +95,7 @@ private:
 
 DeviceCache g_devices;
 
-}  // namespace
+int current_device(const DeviceProps** out) { return g_devices.current(out); }
 
 int lds_cap(const DeviceProps& d, int blocks)
 {
@@ -106,8 +105,6 @@ int lds_cap(const DeviceProps& d, int blocks)
     if (x * blocks > d.lds_per_cu || x > d.lds_per_block) return 0;
     return x;
 }
-
-namespace {
 
 // ---- test-only forcing of launch shapes (not part of the public ABI) ---------
 
@@ -154,12 +151,6 @@ int check_hparams(int kind, const ou_hparams& h)
     if (h.step < 1) return fail(OU_EINVAL, "step must be >= 1 (got %lld)", (long long)h.step);
     return OU_OK;
 }
-
-struct Range {
-    uintptr_t lo, hi;   // [lo, hi)
-    bool written;
-    int seg;
-};
 
 // Pointers, sizes and alignment of one segment; appends its byte ranges.
 int check_segment(int kind, const ou_segment& s, int idx, std::vector<Range>* ranges)
@@ -327,8 +318,6 @@ bool capturing(hipStream_t stream)
     if (hipStreamIsCapturing(stream, &st) != hipSuccess) return false;
     return st != hipStreamCaptureStatusNone;
 }
-
-}  // namespace
 
 // ---- plans --------------------------------------------------------------------
 

@@ -1,0 +1,44 @@
+// host_internal.h -- host-side helpers shared by the 32-bit and the 8-bit
+// entry points (validation, errors, per-step scalars, launches).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <vector>
+
+#include "../../include/optimizer_update.h"
+#include "internal.h"
+
+namespace ou {
+
+// Records a thread-local message for ou_last_error() and returns status.
+int fail(int status, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+int hip_fail(hipError_t e, const char* what);
+
+// Properties of the current device (cached per device id); OU_EUNSUPPORTED
+// unless it is a gfx950.
+int current_device(const DeviceProps** out);
+
+int storage_bytes(int dtype);
+bool valid_kind(int kind);
+bool two_state(int kind);
+// Splits a kind argument into an ou_kind and the OU_DECAY_AFTER flag.
+int split_kind(int arg, int* kind, int* after);
+int check_hparams(int kind, const ou_hparams& h);
+
+// A byte range of one buffer, for the overlap check.
+struct Range {
+    uintptr_t lo, hi;   // [lo, hi)
+    bool written;
+    int seg;
+};
+// No written range may overlap any other range (read-only ranges may share).
+int check_overlap(std::vector<Range>& r);
+
+StepScalars make_scalars(const ou_hparams& h, int decay_after);
+
+hipError_t launch(const void* fn, int64_t grid, int block, int lds, void** args, hipStream_t stream);
+bool capturing(hipStream_t stream);
+
+}  // namespace ou

@@ -74,4 +74,26 @@ constexpr int kClipFinalThreadsHost = 1024;   // threads of pass 2
 
 constexpr int kWave = 64;
 
+// Segment descriptor of the 8-bit block-wise path: codes c1 ([K][n] signed,
+// K = 1 Adam, 2 AdEMAMix), c2 ([n] unsigned), absmax a1 ([K][nb]) and a2
+// ([nb]) with nb = ceil(n / 256).
+struct Seg8 {
+    void* p;
+    const void* g;
+    uint8_t* c1;
+    uint8_t* c2;
+    float* a1;
+    float* a2;
+    int64_t n;
+    int64_t nb;
+    int32_t vec_ok;   // p, g aligned for 4-element accesses, code planes 4-byte aligned
+    int32_t pad;
+};
+static_assert(sizeof(Seg8) == 72, "Seg8 layout");
+
+// Kernels of the 8-bit path: k8_single (Seg8 by value, StepScalars,
+// int32 blocks per wave) or k8_multi (Seg8 table, work items, item count,
+// int32 blocks per item, StepScalars).  nullptr for other kinds.
+const void* kernel8(bool multi, int kind, int dtype);
+
 }  // namespace ou

@@ -1,0 +1,291 @@
+// kernels8.hip -- the update with 8-bit block-wise states (device).
+//
+// The page "Investigate a 256-thread SM103 path for small 32-bit optimizer
+// tensors" times AdamW8bit collections whose tensors below min_8bit_size
+// (4,096 elements) take the 32-bit path (sections "Problem" and "B300
+// benchmark and acceptance").  This file is the other leg: Adam/AdamW and
+// AdEMAMix with each moment stored as 8-bit codes of the dynamic type of
+// qmap.hpp plus one fp32 absmax per block of 256 elements.
+//
+// One wave owns one block: lane l holds elements 4l .. 4l+3 (one dwordx4 of
+// an fp32 stream, dwordx2 of a 16-bit one, one dword of codes per state).
+// Per block: dequantize (code value x absmax), the 32-bit rule of elem.hpp
+// on the fp32 values, the block's new absmax by a wave max (exact, so the
+// order does not matter), then each state is requantized to the nearest
+// magnitude of value / absmax by a binary search over the decision points.
+// The tables (3 KiB) are copied to LDS once per workgroup.  The parameter
+// moves with the moments before quantization.  A partial last block, or a
+// tensor whose streams are not aligned for the wide accesses, runs the same
+// steps one element per slot.
+#include "internal.h"
+#include "qmap.hpp"
+
+#pragma clang fp contract(off)
+
+namespace ou {
+namespace {
+
+__constant__ QTables kQ = make_qtables();
+
+using u32x4 = uint32_t __attribute__((ext_vector_type(4)));
+using u32x2 = uint32_t __attribute__((ext_vector_type(2)));
+
+// Copies the tables into LDS; every thread of the block must call it.
+__device__ __forceinline__ void load_qtables(QTables* T)
+{
+    const float* src = reinterpret_cast<const float*>(&kQ);
+    float* dst = reinterpret_cast<float*>(T);
+    for (int i = static_cast<int>(threadIdx.x); i < 768; i += static_cast<int>(blockDim.x))
+        dst[i] = src[i];
+    __syncthreads();
+}
+
+// #{k : bound[k] < a} by halving over 127 (signed) / 255 (unsigned) sorted
+// decision points.
+__device__ __forceinline__ uint32_t qindex_signed(const QTables& T, float a)
+{
+    uint32_t i = 0;
+#pragma unroll
+    for (uint32_t s = 64; s >= 1; s >>= 1) i += (T.sbound[i + s - 1] < a) ? s : 0u;
+    return i;
+}
+
+__device__ __forceinline__ uint32_t qindex_unsigned(const QTables& T, float a)
+{
+    uint32_t i = 0;
+#pragma unroll
+    for (uint32_t s = 128; s >= 1; s >>= 1) i += (T.ubound[i + s - 1] < a) ? s : 0u;
+    return i;
+}
+
+__device__ __forceinline__ float deq_signed(const QTables& T, uint32_t code)
+{
+    const float v = T.smag[code & 0x7fu];
+    return (code & 0x80u) ? -v : v;
+}
+
+__device__ __forceinline__ uint32_t quant_signed(const QTables& T, float x)
+{
+    const uint32_t i = qindex_signed(T, __builtin_fabsf(x));
+    return (x < 0.0f) ? (i | 0x80u) : i;
+}
+
+// Largest value over the wave (maxNum: a NaN is passed over).
+__device__ __forceinline__ float wave_max(float x)
+{
+#pragma unroll
+    for (int off = kWave / 2; off > 0; off >>= 1) x = __builtin_fmaxf(x, __shfl_xor(x, off));
+    return x;
+}
+
+// One quantization block b of segment d, by one wave.
+template <int KIND, typename S>
+__device__ __forceinline__ void update_block8(const Seg8& d, int64_t b, const QTables& T,
+                                              const StepScalars& sc, int lane)
+{
+    using raw = typename S::raw;
+    constexpr bool kMix = KIND == kAdemamix;
+    raw* __restrict__ p = static_cast<raw*>(d.p);
+    const raw* __restrict__ g = static_cast<const raw*>(d.g);
+    uint8_t* __restrict__ c1 = d.c1;
+    uint8_t* __restrict__ c2 = d.c2;
+    const int64_t n = d.n;
+    const int64_t e0 = b * kQBlock + 4 * lane;
+    const bool full = d.vec_ok && (b + 1) * kQBlock <= n;
+    const float A1 = d.a1[b];
+    const float A2 = d.a2[b];
+    float A3 = 0.0f;
+    if constexpr (kMix) A3 = d.a1[d.nb + b];
+
+    raw praw[4], graw[4];
+    uint32_t w1 = 0, w2 = 0, w3 = 0;
+    bool live[4];
+    if (full) {
+        if constexpr (S::bytes == 4) {
+            const u32x4 xp = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p + e0));
+            const u32x4 xg = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(g + e0));
+            // Elements are copied to scalars before the bit cast: this
+            // compiler reads element 0 for a bit cast of a vector element.
+            const uint32_t p0 = xp.x, p1 = xp.y, p2 = xp.z, p3 = xp.w;
+            const uint32_t g0 = xg.x, g1 = xg.y, g2 = xg.z, g3 = xg.w;
+            praw[0] = __builtin_bit_cast(float, p0); praw[1] = __builtin_bit_cast(float, p1);
+            praw[2] = __builtin_bit_cast(float, p2); praw[3] = __builtin_bit_cast(float, p3);
+            graw[0] = __builtin_bit_cast(float, g0); graw[1] = __builtin_bit_cast(float, g1);
+            graw[2] = __builtin_bit_cast(float, g2); graw[3] = __builtin_bit_cast(float, g3);
+        } else {
+            const u32x2 xp = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p + e0));
+            const u32x2 xg = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(g + e0));
+            praw[0] = static_cast<raw>(xp.x & 0xffffu); praw[1] = static_cast<raw>(xp.x >> 16);
+            praw[2] = static_cast<raw>(xp.y & 0xffffu); praw[3] = static_cast<raw>(xp.y >> 16);
+            graw[0] = static_cast<raw>(xg.x & 0xffffu); graw[1] = static_cast<raw>(xg.x >> 16);
+            graw[2] = static_cast<raw>(xg.y & 0xffffu); graw[3] = static_cast<raw>(xg.y >> 16);
+        }
+        w1 = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(c1 + e0));
+        w2 = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(c2 + e0));
+        if constexpr (kMix) w3 = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(c1 + n + e0));
+#pragma unroll
+        for (int j = 0; j < 4; ++j) live[j] = true;
+    } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int64_t e = e0 + j;
+            live[j] = e < n;
+            praw[j] = 0;
+            graw[j] = 0;
+            if (live[j]) {
+                praw[j] = p[e];
+                graw[j] = g[e];
+                w1 |= static_cast<uint32_t>(c1[e]) << (8 * j);
+                w2 |= static_cast<uint32_t>(c2[e]) << (8 * j);
+                if constexpr (kMix) w3 |= static_cast<uint32_t>(c1[n + e]) << (8 * j);
+            }
+        }
+    }
+
+    // dequantize and update
+    float m[4], v[4], m2[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        m[j] = deq_signed(T, (w1 >> (8 * j)) & 0xffu) * A1;
+        v[j] = T.umag[(w2 >> (8 * j)) & 0xffu] * A2;
+        m2[j] = 0.0f;
+        if constexpr (kMix) m2[j] = deq_signed(T, (w3 >> (8 * j)) & 0xffu) * A3;
+        if (!live[j]) {
+            m[j] = 0.0f;
+            v[j] = 0.0f;
+            m2[j] = 0.0f;
+            continue;
+        }
+        const float gj = S::widen(graw[j]);
+        if (sc.skip_zeros && gj == 0.0f) continue;   // moments keep their values, p is not written
+        const float pn = update_element<KIND>(S::widen(praw[j]), gj, m[j], v[j], m2[j], sc);
+        praw[j] = S::narrow(pn);
+    }
+
+    // new absmax of each state
+    float l1 = 0.0f, l2 = 0.0f, l3 = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        l1 = __builtin_fmaxf(l1, __builtin_fabsf(m[j]));
+        l2 = __builtin_fmaxf(l2, v[j]);
+        if constexpr (kMix) l3 = __builtin_fmaxf(l3, __builtin_fabsf(m2[j]));
+    }
+    l1 = wave_max(l1);
+    l2 = wave_max(l2);
+    if constexpr (kMix) l3 = wave_max(l3);
+
+    // requantize
+    uint32_t o1 = 0, o2 = 0, o3 = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const float x1 = (l1 > 0.0f) ? m[j] / l1 : 0.0f;
+        const float x2 = (l2 > 0.0f) ? v[j] / l2 : 0.0f;
+        o1 |= quant_signed(T, x1) << (8 * j);
+        o2 |= qindex_unsigned(T, __builtin_fabsf(x2)) << (8 * j);
+        if constexpr (kMix) {
+            const float x3 = (l3 > 0.0f) ? m2[j] / l3 : 0.0f;
+            o3 |= quant_signed(T, x3) << (8 * j);
+        }
+    }
+
+    // store
+    if (full) {
+        if constexpr (S::bytes == 4) {
+            const u32x4 xp = {__builtin_bit_cast(uint32_t, praw[0]), __builtin_bit_cast(uint32_t, praw[1]),
+                              __builtin_bit_cast(uint32_t, praw[2]), __builtin_bit_cast(uint32_t, praw[3])};
+            __builtin_nontemporal_store(xp, reinterpret_cast<u32x4*>(p + e0));
+        } else {
+            const u32x2 xp = {static_cast<uint32_t>(praw[0]) | (static_cast<uint32_t>(praw[1]) << 16),
+                              static_cast<uint32_t>(praw[2]) | (static_cast<uint32_t>(praw[3]) << 16)};
+            __builtin_nontemporal_store(xp, reinterpret_cast<u32x2*>(p + e0));
+        }
+        __builtin_nontemporal_store(o1, reinterpret_cast<uint32_t*>(c1 + e0));
+        __builtin_nontemporal_store(o2, reinterpret_cast<uint32_t*>(c2 + e0));
+        if constexpr (kMix) __builtin_nontemporal_store(o3, reinterpret_cast<uint32_t*>(c1 + n + e0));
+    } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int64_t e = e0 + j;
+            if (!live[j]) continue;
+            p[e] = praw[j];
+            c1[e] = static_cast<uint8_t>(o1 >> (8 * j));
+            c2[e] = static_cast<uint8_t>(o2 >> (8 * j));
+            if constexpr (kMix) c1[n + e] = static_cast<uint8_t>(o3 >> (8 * j));
+        }
+    }
+    if (lane == 0) {
+        d.a1[b] = l1;
+        d.a2[b] = l2;
+        if constexpr (kMix) d.a1[d.nb + b] = l3;
+    }
+}
+
+// Single tensor: workgroup w takes blocks [w*W*R, (w+1)*W*R) with W waves
+// of R blocks each, interleaved so that the W waves work on W neighbouring
+// blocks at a time.
+template <int KIND, typename S>
+__global__ void __launch_bounds__(1024)
+k8_single(Seg8 d, StepScalars sc, int32_t blocks_per_wave)
+{
+    __shared__ QTables T;
+    load_qtables(&T);
+    const int waves = static_cast<int>(blockDim.x) / kWave;
+    const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) / kWave);
+    const int lane = static_cast<int>(threadIdx.x) % kWave;
+    const int64_t first = static_cast<int64_t>(blockIdx.x) * waves * blocks_per_wave;
+    for (int r = 0; r < blocks_per_wave; ++r) {
+        const int64_t b = first + static_cast<int64_t>(r) * waves + wave;
+        if (b < d.nb) update_block8<KIND, S>(d, b, T, sc, lane);
+    }
+}
+
+// Collection: one wave per work item (segment, run of `chunk_blocks`
+// blocks starting at chunk * chunk_blocks).
+template <int KIND, typename S>
+__global__ void __launch_bounds__(1024)
+k8_multi(const Seg8* __restrict__ segs, const WorkItem* __restrict__ items, int64_t n_items,
+         int32_t chunk_blocks, StepScalars sc)
+{
+    __shared__ QTables T;
+    load_qtables(&T);
+    const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) / kWave);
+    const int lane = static_cast<int>(threadIdx.x) % kWave;
+    const int64_t w = static_cast<int64_t>(blockIdx.x) * (blockDim.x / kWave) + wave;
+    if (w >= n_items) return;
+    const WorkItem it = items[w];
+    const Seg8 d = segs[__builtin_amdgcn_readfirstlane(it.seg)];
+    const int64_t b0 = static_cast<int64_t>(__builtin_amdgcn_readfirstlane(it.chunk)) * chunk_blocks;
+    for (int r = 0; r < chunk_blocks; ++r) {
+        const int64_t b = b0 + r;
+        if (b < d.nb) update_block8<KIND, S>(d, b, T, sc, lane);
+    }
+}
+
+template <int KIND, typename S>
+const void* pick8(bool multi)
+{
+    return multi ? reinterpret_cast<const void*>(&k8_multi<KIND, S>)
+                 : reinterpret_cast<const void*>(&k8_single<KIND, S>);
+}
+
+template <int KIND>
+const void* pick8_dtype(bool multi, int dtype)
+{
+    switch (dtype) {
+    case 0: return pick8<KIND, F32>(multi);
+    case 1: return pick8<KIND, F16>(multi);
+    case 2: return pick8<KIND, BF16>(multi);
+    default: return nullptr;
+    }
+}
+
+}  // namespace
+
+const void* kernel8(bool multi, int kind, int dtype)
+{
+    if (kind == kAdam) return pick8_dtype<kAdam>(multi, dtype);
+    if (kind == kAdemamix) return pick8_dtype<kAdemamix>(multi, dtype);
+    return nullptr;
+}
+
+}  // namespace ou

@@ -33,6 +33,12 @@ void ou__force_multi(int waves, int epl, int unroll, int chunk, int lds);
 // The per-step scalars: beta1..3, 1-beta1..3, alpha, eps, lr, bc1, bc2, decay.
 int ou__step_scalars(const ou_hparams* hp, float out[12]);
 
+// Force the 8-bit launch shape (0 = no forcing): waves per workgroup,
+// blocks per wave of the single-tensor kernel, blocks per work item of
+// plans created afterwards; scalar_only != 0 forces the element-by-element
+// path.  Process-wide.
+void ou__force_8bit(int waves, int blocks_per_wave, int chunk_blocks, int scalar_only);
+
 #ifdef __cplusplus
 }
 #endif

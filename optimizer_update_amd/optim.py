@@ -8,7 +8,10 @@ parameter and update the whole collection per step through one plan (one
 launch per dtype group), its HIP-graph replay, or, for comparison, one
 direct call per tensor.  ``Momentum32``, ``RMSprop32``, ``Adagrad32`` and
 ``Lion32`` are the one-state kinds of the same 32-bit update family, with the
-same three step paths.
+same three step paths.  ``AdamW8bit`` and ``AdEMAMix8bit`` keep the
+moments of tensors of at least ``min_8bit_size`` elements (4,096 by
+default, the page's setting) as 8-bit block-wise states and route the
+smaller ones to the 32-bit path, one plan each.
 
 Parameters and gradients must be contiguous CUDA (HIP) tensors whose
 storage stays in place for the optimizer's lifetime: the plan holds their
@@ -18,9 +21,9 @@ from __future__ import annotations
 
 import torch
 
-from . import (DTYPES, TWO_STATE, HParams, Plan, _kind, _on_device, _ptr, _raw_stream,
-               _tensor_args, check, clip_workspace, load, optimizer_update_32bit_clip,
-               state_sizes)
+from . import (DTYPES, TWO_STATE, HParams, Plan, Plan8, _kind, _on_device, _ptr, _raw_stream,
+               _tensor_args, check, clip_workspace, load, optimizer_update_8bit_blockwise,
+               optimizer_update_32bit, optimizer_update_32bit_clip, state8_sizes, state_sizes)
 
 
 class _Collection:
@@ -195,3 +198,117 @@ class Lion32(_Collection):
         super().__init__(params, HParams(lr=lr, beta1=betas[0], beta2=betas[1], eps=0.0,
                                          weight_decay=weight_decay, skip_zeros=skip_zeros), grads,
                          0.0, decay_after)
+
+
+def _params_and_grads(params, grads):
+    ps = [p.data if isinstance(p, torch.nn.Parameter) else p for p in params]
+    if grads is None:
+        grads = []
+        for p, src in zip(ps, params):
+            g = getattr(src, "grad", None)
+            if g is None:
+                g = torch.zeros_like(p)
+                if isinstance(src, torch.nn.Parameter):
+                    src.grad = g
+            grads.append(g)
+    return ps, list(grads)
+
+
+class _Collection8:
+    """Tensors of at least ``min_8bit_size`` elements keep 8-bit block-wise
+    states (uint8 codes, fp32 absmax per 256 elements) and step through one
+    8-bit plan; smaller tensors keep fp32 states and step through one 32-bit
+    plan."""
+    kind = "adam"
+
+    def __init__(self, params, hp: HParams, grads=None, min_8bit_size: int = 4096,
+                 decay_after: bool = False):
+        self.params, self.grads = _params_and_grads(params, grads)
+        self.hp = hp
+        self.min_8bit_size = int(min_8bit_size)
+        self.decay_after = bool(decay_after)
+        self.step_count = 0
+        self.state = []            # per parameter: ("8bit", s1, s2, a1, a2) or ("32bit", s1, s2)
+        seg8, seg32 = [], []
+        for p, g in zip(self.params, self.grads):
+            if p.numel() >= self.min_8bit_size:
+                n1, n2, na1, na2 = state8_sizes(self.kind, p.numel())
+                st = ("8bit", torch.zeros(n1, dtype=torch.uint8, device=p.device),
+                      torch.zeros(n2, dtype=torch.uint8, device=p.device),
+                      torch.zeros(na1, dtype=torch.float32, device=p.device),
+                      torch.zeros(na2, dtype=torch.float32, device=p.device))
+                seg8.append((p, g, *st[1:]))
+            else:
+                n1, n2 = state_sizes(self.kind, p.numel())
+                st = ("32bit", torch.zeros(n1, dtype=torch.float32, device=p.device),
+                      torch.zeros(n2, dtype=torch.float32, device=p.device))
+                seg32.append((p, g, *st[1:]))
+            self.state.append(st)
+        self.plan8 = Plan8(self.kind, seg8, decay_after=self.decay_after) if seg8 else None
+        self.plan32 = Plan(self.kind, seg32, decay_after=self.decay_after) if seg32 else None
+
+    @torch.no_grad()
+    def step(self, stream=None) -> None:
+        """One step: the 8-bit plan, then the 32-bit plan (one launch per
+        dtype group each)."""
+        self.step_count += 1
+        if self.plan8 is not None:
+            self.plan8.step(self.hp, self.step_count, stream)
+        if self.plan32 is not None:
+            self.plan32.step(self.hp, self.step_count, stream)
+
+    @torch.no_grad()
+    def step_per_tensor(self, stream=None) -> None:
+        """The same step as one direct call per tensor (the eager loop)."""
+        self.step_count += 1
+        h = self.hp
+        kw = dict(step=self.step_count, lr=h.lr, beta1=h.beta1, beta2=h.beta2, beta3=h.beta3,
+                  alpha=h.alpha, eps=h.eps, weight_decay=h.weight_decay,
+                  skip_zeros=h.skip_zeros, decay_after=self.decay_after, stream=stream)
+        for p, g, st in zip(self.params, self.grads, self.state):
+            if st[0] == "8bit":
+                optimizer_update_8bit_blockwise(self.kind, p, g, *st[1:], **kw)
+            else:
+                optimizer_update_32bit(self.kind, p, g, *st[1:], **kw)
+
+    def state_dict(self) -> dict:
+        return {"step": self.step_count,
+                "state": [(st[0], *[x.clone() for x in st[1:]]) for st in self.state]}
+
+    def load_state_dict(self, sd: dict) -> None:
+        self.step_count = int(sd["step"])
+        for dst, src in zip(self.state, sd["state"]):
+            if dst[0] != src[0]:
+                raise ValueError("state layout differs (min_8bit_size or shapes changed)")
+            for a, b in zip(dst[1:], src[1:]):
+                a.copy_(b)
+
+    def close(self) -> None:
+        for plan in (self.plan8, self.plan32):
+            if plan is not None:
+                plan.close()
+
+
+class AdamW8bit(_Collection8):
+    """AdamW with 8-bit block-wise moments for tensors of at least
+    min_8bit_size elements (32-bit states below)."""
+    kind = "adam"
+
+    def __init__(self, params, lr=1e-3, betas=(0.9, 0.999), eps=1e-8, weight_decay=0.01,
+                 skip_zeros=False, grads=None, min_8bit_size=4096, decay_after=False):
+        super().__init__(params, HParams(lr=lr, beta1=betas[0], beta2=betas[1], eps=eps,
+                                         weight_decay=weight_decay, skip_zeros=skip_zeros), grads,
+                         min_8bit_size, decay_after)
+
+
+class AdEMAMix8bit(_Collection8):
+    """AdEMAMix with 8-bit block-wise moments for tensors of at least
+    min_8bit_size elements (32-bit states below)."""
+    kind = "ademamix"
+
+    def __init__(self, params, lr=1e-3, betas=(0.9, 0.999, 0.9999), alpha=5.0, eps=1e-8,
+                 weight_decay=0.01, skip_zeros=False, grads=None, min_8bit_size=4096,
+                 decay_after=False):
+        super().__init__(params, HParams(lr=lr, beta1=betas[0], beta2=betas[1], beta3=betas[2],
+                                         alpha=alpha, eps=eps, weight_decay=weight_decay,
+                                         skip_zeros=skip_zeros), grads, min_8bit_size, decay_after)

@@ -32,7 +32,8 @@ def test_exports_every_header_function(L):
                           "ou_plan_step_clip", "ou_plan_clip_factors",
                           "ou_plan_create", "ou_plan_step", "ou_plan_graph_step",
                           "ou_plan_describe", "ou_plan_destroy", "ou_status_string",
-                          "ou_last_error"}
+                          "ou_last_error", "ou_8bit_qmap", "optimizer_update_8bit_blockwise",
+                          "ou_plan8_create", "ou_plan8_step", "ou_plan8_destroy"}
     for n in names:
         assert hasattr(L, n), n
     out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIBRARY], capture_output=True,
@@ -41,24 +42,25 @@ def test_exports_every_header_function(L):
     assert set(names) <= exported
     # nothing else is exported besides the test hooks
     assert exported - set(names) == {"ou__select_single", "ou__force_single", "ou__force_multi",
-                                     "ou__step_scalars"}
+                                     "ou__step_scalars", "ou__force_8bit"}
 
 
 def test_header_is_plain_c_and_matches_ctypes_layout(tmp_path):
     src = tmp_path / "layout.c"
     src.write_text(
         '#include <stddef.h>\n#include <stdio.h>\n#include "optimizer_update.h"\n'
-        'int main(void){printf("%zu %zu %zu %zu %zu %zu\\n", sizeof(ou_hparams), '
+        'int main(void){printf("%zu %zu %zu %zu %zu %zu %zu %zu %zu\\n", sizeof(ou_hparams), '
         'offsetof(ou_hparams, skip_zeros), offsetof(ou_hparams, step), sizeof(ou_segment), '
-        'offsetof(ou_segment, n), offsetof(ou_segment, dtype)); return 0;}\n')
+        'offsetof(ou_segment, n), offsetof(ou_segment, dtype), sizeof(ou_segment8), '
+        'offsetof(ou_segment8, n), offsetof(ou_segment8, dtype)); return 0;}\n')
     exe = tmp_path / "layout"
     subprocess.run(["gcc", "-std=c99", "-Wall", "-Werror", "-I", os.path.dirname(HEADER),
                     str(src), "-o", str(exe)], check=True)
     got = list(map(int, subprocess.run([str(exe)], capture_output=True, text=True,
                                        check=True).stdout.split()))
-    H, S = _lib.ou_hparams, _lib.ou_segment
+    H, S, S8 = _lib.ou_hparams, _lib.ou_segment, _lib.ou_segment8
     assert got == [ctypes.sizeof(H), H.skip_zeros.offset, H.step.offset, ctypes.sizeof(S),
-                   S.n.offset, S.dtype.offset]
+                   S.n.offset, S.dtype.offset, ctypes.sizeof(S8), S8.n.offset, S8.dtype.offset]
 
 
 def _call(L, kind=0, dtype=0, p=0x10000, g=0x20000, s1=0x30000, s2=0x40000, n=16, b1=0.9,
@@ -304,3 +306,63 @@ def test_binding_rejects_host_tensors():
     p = torch.zeros(8)
     with pytest.raises(ValueError):
         ou.optimizer_update_32bit("adam", p, p.clone(), p.clone(), p.clone(), step=1, lr=1e-3)
+
+
+# ------------------------------------------------------- 8-bit block-wise states
+
+def _call8(L, kind=0, dtype=0, p=0x10000, g=0x20000, c1=0x30000, c2=0x40000, a1=0x50000,
+           a2=0x60000, n=1000, b1=0.9, step=1):
+    return L.optimizer_update_8bit_blockwise(kind, dtype, p, g, c1, c2, a1, a2, n, b1, 0.999, 0.9999,
+                                             5.0, 1e-8, 0.0, step, 1e-3, 0, None)
+
+
+@pytest.mark.parametrize("case,kw,code", [
+    ("one-state kind", dict(kind=2), OU_EINVAL),
+    ("lion", dict(kind=5), OU_EINVAL),
+    ("unknown kind", dict(kind=7), OU_EINVAL),
+    ("bad dtype", dict(dtype=3), OU_EINVAL),
+    ("null absmax1", dict(a1=0), OU_EINVAL),
+    ("null state2", dict(c2=0), OU_EINVAL),
+    ("absmax misaligned", dict(a2=0x60002), OU_EALIGN),
+    ("fp32 param misaligned", dict(p=0x10002), OU_EALIGN),
+    ("codes overlap param", dict(c1=0x10000 + 100), OU_EOVERLAP),
+    ("ademamix slow codes overlap state2", dict(kind=1, c2=0x30000 + 1500), OU_EOVERLAP),
+    ("absmax1 overlaps absmax2", dict(a2=0x50000 + 8), OU_EOVERLAP),
+    ("ademamix absmax planes overlap absmax2", dict(kind=1, a2=0x50000 + 4 * 5), OU_EOVERLAP),
+    ("step 0", dict(step=0), OU_EINVAL),
+    ("beta1 = 1", dict(b1=1.0), OU_EINVAL),
+])
+def test_8bit_entry_validation(L, case, kw, code):
+    assert _call8(L, **kw) == code, case
+
+
+def test_8bit_valid_calls_reach_the_device_query(L):
+    # unaligned codes are allowed (element-by-element path); n = 0 is a no-op
+    for kw in (dict(), dict(kind=1), dict(kind=0x100), dict(c1=0x30001, c2=0x40003), dict(dtype=2)):
+        assert _call8(L, **kw) not in (OU_EINVAL, OU_EALIGN, OU_EOVERLAP), kw
+    assert _call8(L, n=0, p=0, g=0, c1=0, c2=0, a1=0, a2=0) == OU_OK
+    h = ctypes.c_void_p()
+    seg = (_lib.ou_segment8 * 1)(_lib.ou_segment8(0x100000, 0x200000, 0x300000, 0x400000, 0x500000,
+                                                  0x600000, 4096, 0, 0))
+    st = L.ou_plan8_create(0, seg, 1, ctypes.byref(h))
+    assert st not in (OU_EINVAL, OU_EALIGN, OU_EOVERLAP)
+    L.ou_plan8_destroy(h if h.value else None)
+    assert L.ou_plan8_create(3, seg, 1, ctypes.byref(h)) == OU_EINVAL
+    bad = (_lib.ou_segment8 * 1)(_lib.ou_segment8(0x100000, 0x200000, 0x300000, 0x400000, 0x500000,
+                                                  0x500000, 4096, 0, 0))
+    assert L.ou_plan8_create(0, bad, 1, ctypes.byref(h)) == OU_EOVERLAP
+    assert L.ou_plan8_step(None, None, None) == OU_EINVAL
+
+
+def test_8bit_qmap_matches_the_oracle(L):
+    """The library builds the 8-bit type at compile time, the oracle at run
+    time, each from the definition: the magnitudes agree bitwise."""
+    import numpy as np
+    import oracle as O
+    orc = O.load()
+    for signed, count in ((1, 128), (0, 256)):
+        out = (ctypes.c_float * count)()
+        assert L.ou_8bit_qmap(signed, out, count) == OU_OK
+        got = np.frombuffer(out, dtype=np.float32)
+        assert got.tobytes() == orc.qmap(bool(signed)).tobytes()
+        assert L.ou_8bit_qmap(signed, out, count - 1) == OU_EINVAL

@@ -1,0 +1,276 @@
+"""GPU parity of the 8-bit block-wise path against the CPU oracle.
+
+The page "Investigate a 256-thread SM103 path for small 32-bit optimizer
+tensors" times AdamW8bit collections whose small tensors (below
+min_8bit_size = 4,096 elements) take the 32-bit path; these tests cover the
+8-bit leg and the routing.  The kernels perform the oracle's steps with the
+same binary32 operations, the same decision points and an exact (order-free)
+block maximum, so parameters, codes and absmax must be bit-identical to the
+oracle, across the kernel's launch shapes, the element-by-element path and
+plans.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import workloads as W
+from tests import gpu_helpers as H
+
+pytestmark = pytest.mark.gpu
+
+KIND = {"adam": O.ADAM, "ademamix": O.ADEMAMIX}
+QB = O.QBLOCK
+SIZES = (1, 33, 255, 256, 257, 1023, 1024, 4095, 4096, 4097, 65539)
+
+
+@pytest.fixture(scope="module")
+def orc():
+    return O.load()
+
+
+@pytest.fixture(scope="module")
+def L():
+    assert torch.cuda.is_available(), "GPU tests need a HIP device"
+    return H.lib()
+
+
+def _nb(n):
+    return -(-n // QB)
+
+
+def _zero_host(kind, n):
+    k = 2 if kind == "ademamix" else 1
+    return (np.zeros(k * n, np.uint8), np.zeros(n, np.uint8), np.zeros(k * _nb(n), np.float32),
+            np.zeros(_nb(n), np.float32))
+
+
+def _dev_states(kind, n, offset=0):
+    """Zero states on the device, each placed `offset` bytes/elements past an
+    aligned start (offset > 0 exercises the element-by-element path)."""
+    k = 2 if kind == "ademamix" else 1
+    c1 = torch.zeros(k * n + offset, dtype=torch.uint8, device="cuda")[offset:]
+    c2 = torch.zeros(n + offset, dtype=torch.uint8, device="cuda")[offset:]
+    a1 = torch.zeros(k * _nb(n), dtype=torch.float32, device="cuda")
+    a2 = torch.zeros(_nb(n), dtype=torch.float32, device="cuda")
+    return c1, c2, a1, a2
+
+
+def _raw8(L, kind, storage, P, G, st, n, hp, t, flag=0):
+    c1, c2, a1, a2 = st
+    return L.optimizer_update_8bit_blockwise(KIND[kind] | flag, H.DT[storage], P.data_ptr(),
+                                             G.data_ptr(), c1.data_ptr(), c2.data_ptr(),
+                                             a1.data_ptr(), a2.data_ptr(), n, hp.beta1, hp.beta2,
+                                             hp.beta3, hp.alpha, hp.eps, hp.weight_decay, t, hp.lr,
+                                             int(hp.skip_zeros), H.stream_handle())
+
+
+def _gpu_run(L, kind, storage, p0, gsteps, hp, offset=0, flag=0, force=None):
+    n = p0.size
+    P = H.to_dev(np.concatenate([np.zeros(offset, p0.dtype), p0]), storage)[offset:]
+    G = torch.empty(n + offset, dtype=W.STORAGE_TORCH[storage], device="cuda")[offset:]
+    st = _dev_states(kind, n, offset)
+    if force:
+        L.ou__force_8bit(*force)
+    try:
+        for t, g in enumerate(gsteps, start=1):
+            G.copy_(W.to_torch(g, storage, "cuda"))
+            rc = _raw8(L, kind, storage, P, G, st, n, hp, t, flag)
+            assert rc == 0, H.last_error(L)
+    finally:
+        L.ou__force_8bit(0, 0, 0, 0)
+    torch.cuda.synchronize()
+    return (W.from_torch(P), *(x.cpu().numpy() for x in st))
+
+
+def _oracle_run(orc, kind, storage, p0, gsteps, hp, flag=0):
+    p = p0.copy()
+    st = _zero_host(kind, p0.size)
+    for t, g in enumerate(gsteps, start=1):
+        orc.update_8bit_f32(KIND[kind] | flag, H.DT[storage], p, g.copy(), *st, hp, t)
+    return (p, *st)
+
+
+def _assert_same(got, ref, storage, what):
+    H.assert_parity(got[0], ref[0], storage, "p " + what)
+    names = ("state1 codes", "state2 codes", "absmax1", "absmax2")
+    for a, b, name in zip(got[1:], ref[1:], names):
+        assert a.tobytes() == b.tobytes(), f"{name} {what}: {np.count_nonzero(a != b)} differ"
+
+
+def _grads(storage, n, T, pattern, key):
+    return [W.grads(n, pattern, storage, W.rng(3, *key, t)) for t in range(T)]
+
+
+@pytest.mark.parametrize("kind", list(KIND))
+@pytest.mark.parametrize("storage", ["fp32", "fp16", "bf16"])
+def test_8bit_matches_oracle(orc, L, kind, storage):
+    """Every size of the list (partial blocks, one block, many), zero/normal/
+    mixed gradients, wd 0 / 0.01, skip_zeros off/on, 10 steps: parameters,
+    codes and absmax bitwise equal to the oracle's."""
+    T = 10
+    for pattern in W.GRAD_PATTERNS:
+        for wd, skip in ((0.0, False), (0.01, True), (0.01, False)):
+            hp = O.HParams(lr=1e-3, beta1=0.9, beta2=0.999, beta3=0.9999, alpha=5.0, eps=1e-8,
+                           weight_decay=wd, skip_zeros=skip)
+            for n in SIZES:
+                key = (list(KIND).index(kind), H.DT[storage], W.GRAD_PATTERNS.index(pattern), n)
+                p0 = W.params(n, storage, W.rng(3, 0, *key))
+                gs = _grads(storage, n, T, pattern, key)
+                got = _gpu_run(L, kind, storage, p0, gs, hp)
+                ref = _oracle_run(orc, kind, storage, p0, gs, hp)
+                _assert_same(got, ref, storage, f"{kind} {storage} {pattern} wd={wd} skip={skip} n={n}")
+
+
+@pytest.mark.parametrize("kind", list(KIND))
+@pytest.mark.parametrize("storage", ["fp32", "bf16"])
+def test_8bit_launch_variants_and_paths(orc, L, kind, storage):
+    """Waves per workgroup, blocks per wave, the element-by-element path and
+    misaligned buffers give the same bits."""
+    T = 4
+    hp = O.HParams(lr=1e-2, weight_decay=0.05, skip_zeros=True)
+    for n in (257, 4097, 65539, (1 << 18) + 3):
+        gen = W.rng(3, 9, n)
+        p0 = W.params(n, storage, gen)
+        gs = [W.cast_storage(np.where(gen.random(n) < 0.1, 0.0, gen.standard_normal(n)), storage)
+              for _ in range(T)]
+        base = _gpu_run(L, kind, storage, p0, gs, hp)
+        if n < 70000:
+            _assert_same(base, _oracle_run(orc, kind, storage, p0, gs, hp), storage, f"n={n}")
+        for force in ((1, 1, 0, 0), (4, 1, 0, 0), (2, 8, 0, 0), (16, 2, 0, 0), (4, 4, 0, 1)):
+            got = _gpu_run(L, kind, storage, p0, gs, hp, force=force)
+            for a, b in zip(got, base):
+                assert a.tobytes() == b.tobytes(), (force, n)
+        for off in (1, 3):
+            got = _gpu_run(L, kind, storage, p0, gs, hp, offset=off)
+            for a, b in zip(got, base):
+                assert a.tobytes() == b.tobytes(), ("offset", off, n)
+
+
+@pytest.mark.parametrize("kind", list(KIND))
+def test_8bit_decay_after(orc, L, kind):
+    """OU_DECAY_AFTER with 8-bit states: bitwise equal to the oracle's
+    flagged path, and different from the default order in binary32."""
+    T = 5
+    hp = O.HParams(lr=1e-2, weight_decay=0.1)
+    n = 4097
+    p0 = W.params(n, "fp32", W.rng(3, 11, n))
+    gs = _grads("fp32", n, T, "normal", (11, n))
+    got = _gpu_run(L, kind, "fp32", p0, gs, hp, flag=O.DECAY_AFTER)
+    _assert_same(got, _oracle_run(orc, kind, "fp32", p0, gs, hp, flag=O.DECAY_AFTER), "fp32", "flag")
+    assert got[0].tobytes() != _oracle_run(orc, kind, "fp32", p0, gs, hp)[0].tobytes()
+
+
+@pytest.mark.parametrize("kind,storage", [("adam", "fp32"), ("ademamix", "bf16")])
+def test_8bit_large_tensor_sampled_blocks(orc, L, kind, storage):
+    """2^26 + 3 elements, 3 steps: blocks are independent, so whole blocks
+    (the first 8, the partial last one, and every 1,031st) are checked
+    against the oracle run on those blocks alone."""
+    n = (1 << 26) + 3
+    T = 3
+    hp = O.HParams(lr=1e-3, weight_decay=0.01)
+    p0 = W.params(n, storage, W.rng(3, 12, n))
+    gs = [W.grads(n, "normal", storage, W.rng(3, 13, t)) for t in range(T)]
+    got = _gpu_run(L, kind, storage, p0, gs, hp)
+    nb = _nb(n)
+    blocks = np.unique(np.r_[0:8, nb - 1, 0:nb:1031])
+    for b in blocks:
+        lo, hi = b * QB, min(n, (b + 1) * QB)
+        ref = _oracle_run(orc, kind, storage, p0[lo:hi].copy(), [g[lo:hi].copy() for g in gs], hp)
+        what = f"block {b}"
+        H.assert_parity(got[0][lo:hi], ref[0], storage, "p " + what)
+        assert got[1][lo:hi].tobytes() == ref[1][:hi - lo].tobytes(), what
+        assert got[2][lo:hi].tobytes() == ref[2].tobytes(), what
+        assert got[3][b] == ref[3][0] and got[4][b] == ref[4][0], what
+        if kind == "ademamix":
+            assert got[1][n + lo:n + hi].tobytes() == ref[1][hi - lo:].tobytes(), what
+            assert got[3][nb + b] == ref[3][1], what
+
+
+@pytest.mark.parametrize("kind", list(KIND))
+def test_8bit_plan_equals_direct(L, kind):
+    """A plan over several tensors (all dtypes, several work-item sizes)
+    gives the bits of one direct call per tensor."""
+    import optimizer_update_amd as ou
+    T = 3
+    hp = O.HParams(lr=1e-3, weight_decay=0.01, skip_zeros=True)
+    specs = [(4096, "bf16"), (257, "fp32"), (65539, "fp16"), (1 << 16, "bf16"), (5000, "fp32")]
+    inputs = []
+    for i, (n, storage) in enumerate(specs):
+        gen = W.rng(3, 14, i)
+        p0 = W.params(n, storage, gen)
+        gs = [W.cast_storage(np.where(gen.random(n) < 0.1, 0.0, gen.standard_normal(n)), storage)
+              for _ in range(T)]
+        inputs.append((n, storage, p0, gs, _gpu_run(L, kind, storage, p0, gs, hp)))
+    for chunk in (0, 1, 3):
+        L.ou__force_8bit(0, 0, chunk, 0)
+        try:
+            tensors = []
+            for n, storage, p0, gs, _ in inputs:
+                P = H.to_dev(p0, storage)
+                G = torch.empty(n, dtype=W.STORAGE_TORCH[storage], device="cuda")
+                tensors.append((P, G, *_dev_states(kind, n)))
+            plan = ou.Plan8(kind, tensors)
+        finally:
+            L.ou__force_8bit(0, 0, 0, 0)
+        try:
+            for t in range(1, T + 1):
+                for (n, storage, p0, gs, _), tt in zip(inputs, tensors):
+                    tt[1].copy_(W.to_torch(gs[t - 1], storage, "cuda"))
+                plan.step(H.pkg_hp(hp), t)
+            torch.cuda.synchronize()
+        finally:
+            plan.close()
+        for (n, storage, p0, gs, ref), tt in zip(inputs, tensors):
+            got = (W.from_torch(tt[0]), *(x.cpu().numpy() for x in tt[2:]))
+            for a, b in zip(got, ref):
+                assert a.tobytes() == b.tobytes(), (chunk, n, storage)
+
+
+@pytest.mark.parametrize("cls", ["AdamW8bit", "AdEMAMix8bit"])
+def test_8bit_collection_routing(orc, cls):
+    """min_8bit_size = 4,096 (the page's default): tensors below it keep fp32
+    states and take the 32-bit path, the others 8-bit states.  The plan step
+    equals the per-tensor loop bitwise and each tensor equals its oracle
+    (8-bit or 32-bit)."""
+    import optimizer_update_amd as ou
+    shapes = [(1024,), (4096,), (16, 1024), (4095,), (64,), (1024, 16), (3000, 7)]
+    rows = [(W.params(W.numel(s), "bf16", W.rng(3, 15, i)),
+             W.grads(W.numel(s), "normal", "bf16", W.rng(3, 16, i))) for i, s in enumerate(shapes)]
+    runs = {}
+    for mode in ("plan", "per_tensor"):
+        ps = [H.to_dev(p0, "bf16") for p0, _ in rows]
+        gs = [H.to_dev(g, "bf16") for _, g in rows]
+        opt = getattr(ou, cls)(ps, grads=gs, lr=1e-3, weight_decay=0.01)
+        assert [s[0] for s in opt.state] == ["32bit" if W.numel(s) < 4096 else "8bit" for s in shapes]
+        for _ in range(3):
+            if mode == "plan":
+                opt.step()
+            else:
+                opt.step_per_tensor()
+        torch.cuda.synchronize()
+        runs[mode] = [(W.from_torch(p), [x.cpu().numpy() for x in st[1:]]) for p, st in zip(ps, opt.state)]
+        hp = O.HParams(**{k: getattr(opt.hp, k) for k in ("lr", "beta1", "beta2", "beta3", "alpha",
+                                                          "eps", "weight_decay", "skip_zeros")})
+        kind = ou.optim.__dict__[cls].kind
+        opt.close()
+    for (pa, sa), (pb, sb) in zip(runs["plan"], runs["per_tensor"]):
+        assert pa.tobytes() == pb.tobytes()
+        for x, y in zip(sa, sb):
+            assert x.tobytes() == y.tobytes()
+    for (p0, g), (p, states), shape in zip(rows, runs["plan"], shapes):
+        n = W.numel(shape)
+        if n >= 4096:
+            ref = _oracle_run(orc, kind, "bf16", p0, [g] * 3, hp)
+            H.assert_parity(p, ref[0], "bf16", f"{cls} 8-bit p n={n}")
+            for a, b in zip(states, ref[1:]):
+                assert a.tobytes() == b.tobytes(), n
+        else:
+            pr = p0.copy()
+            s1, s2 = W.zero_states(n, kind)
+            for t in range(1, 4):
+                orc.update_f32(KIND[kind], O.BF16, pr, g.copy(), s1, s2, hp, t)
+            H.assert_parity(p, pr, "bf16", f"{cls} 32-bit p n={n}")
+            H.assert_parity(states[0], s1, "fp32", f"{cls} 32-bit m n={n}")
