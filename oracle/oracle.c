@@ -796,8 +796,11 @@ float oracle_qvalue(int is_signed, int code)
  *      their values and its parameter is not written);
  *   3. the new absmax of each state is the largest |value| in the block
  *      (maxNum: a NaN is passed over);
- *   4. each state is stored as the code of value / absmax (0 when the absmax
- *      is 0).
+ *   4. each state is stored as the code of x = value * fl32(1 / absmax) (one
+ *      correctly rounded reciprocal per block, then a product per element;
+ *      x = 0 when the absmax is 0).  The code's magnitude index counts the
+ *      decision points below |x|, so an x just above 1 (or infinite, when
+ *      1 / absmax overflows) takes the largest magnitude and a NaN takes 0.
  * The parameter moves with the moments before they are quantized.  Zero
  * codes with zero absmax are the zero state.  Returns 0, -1 on an invalid
  * kind or dtype, -2 if out of memory. */
@@ -875,16 +878,19 @@ int oracle_update_8bit_f32(int kind_arg, int dtype, void* param, const void* gra
         a2 = old_a2 > 0.0f ? old_a2 : a2;
 #endif
         /* 4. quantize */
+        float r1 = a1 > 0.0f ? 1.0f / a1 : 0.0f;
+        float r2 = a2 > 0.0f ? 1.0f / a2 : 0.0f;
+        float r3 = a3 > 0.0f ? 1.0f / a3 : 0.0f;
         for (int k = 0; k < len; k++) {
             int64_t i = i0 + k;
-            float x1 = a1 > 0.0f ? m[k] / a1 : 0.0f;
-            float x2 = a2 > 0.0f ? v[k] / a2 : 0.0f;
+            float x1 = a1 > 0.0f ? m[k] * r1 : 0.0f;
+            float x2 = a2 > 0.0f ? v[k] * r2 : 0.0f;
             int c1 = qmap_index(smag, 128, fabsf(x1));
             if (x1 < 0.0f) c1 |= 0x80;
             state1[i] = (uint8_t)c1;
             state2[i] = (uint8_t)qmap_index(umag, 256, fabsf(x2));
             if (two) {
-                float x3 = a3 > 0.0f ? m2[k] / a3 : 0.0f;
+                float x3 = a3 > 0.0f ? m2[k] * r3 : 0.0f;
                 int c3 = qmap_index(smag, 128, fabsf(x3));
                 if (x3 < 0.0f) c3 |= 0x80;
                 state1[n + i] = (uint8_t)c3;
