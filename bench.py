@@ -86,6 +86,11 @@ def main():
         gen.manual_seed(seed)
         p = torch.empty(n, device=dev).uniform_(-1.0, 1.0, generator=gen).to(W.STORAGE_TORCH[storage])
         g = (torch.randn(n, device=dev, generator=gen) * 1e-3).to(W.STORAGE_TORCH[storage])
+        if kind.endswith("8"):         # 8-bit block-wise states
+            c1, c2, a1, a2 = ou.state8_sizes(kind[:-1], n)
+            return (p, g, torch.zeros(c1, dtype=torch.uint8, device=dev),
+                    torch.zeros(c2, dtype=torch.uint8, device=dev),
+                    torch.zeros(a1, device=dev), torch.zeros(a2, device=dev))
         s1n, s2n = ou.state_sizes(kind, n)
         return (p, g, torch.zeros(s1n, device=dev),
                 torch.zeros(s2n, device=dev) if s2n else None)
@@ -100,8 +105,16 @@ def main():
                "lion": ou.HParams(lr=1e-4, beta1=0.9, beta2=0.99, eps=0.0, weight_decay=0.1)}
 
     def flat_stepper(kind, tensors, hp):
-        p, g, s1, s2 = tensors
         state = {"t": 0}
+        if kind.endswith("8"):
+            def step8():
+                state["t"] += 1
+                ou.optimizer_update_8bit_blockwise(kind[:-1], *tensors, step=state["t"], lr=hp.lr,
+                                                   beta1=hp.beta1, beta2=hp.beta2, beta3=hp.beta3,
+                                                   alpha=hp.alpha, eps=hp.eps,
+                                                   weight_decay=hp.weight_decay)
+            return step8
+        p, g, s1, s2 = tensors
 
         def step():
             state["t"] += 1
@@ -162,8 +175,9 @@ def main():
     # ---------------------------------------------------------------- headline
     kind, storage, log2n = args.case.split(":")
     n = 1 << int(log2n)
-    bpe = W.bytes_per_element(kind, storage)
-    hp_head = hp_kind[kind]
+    bpe = (W.bytes_per_element_8bit(kind[:-1], storage) if kind.endswith("8")
+           else W.bytes_per_element(kind, storage))
+    hp_head = hp_kind[kind.rstrip("8")]
     head = make_flat(kind, storage, n, seed=0)
     ms, wall_ms = time_exact(flat_stepper(kind, head, hp_head), args.steps, args.warmup)
     gbs = bpe * n / (ms * 1e-3) / 1e9
@@ -174,7 +188,8 @@ def main():
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "f32", "data": "synthetic",
         "config": {"workload": f"{kind}_{storage}_flat_2^{log2n}", "n": n, "kind": kind,
-                   "param_grad_storage": storage, "states": "fp32",
+                   "param_grad_storage": storage,
+                   "states": "8-bit block-wise, 256 per block" if kind.endswith("8") else "fp32",
                    "params": "U(-1,1)", "grads": "N(0, (1e-3)^2), fixed",
                    "hparams": {k: v for k, v in hp_head.__dict__.items()},
                    "bytes_per_element": bpe, "device": props.name, "cu_count": props.multi_processor_count,
@@ -203,15 +218,18 @@ def main():
         del src, dst
         torch.cuda.empty_cache()
         for ck, cs, cl in (("adam", "bf16", 28), ("ademamix", "fp32", 28), ("ademamix", "bf16", 28),
-                           ("adam", "fp32", 30), ("lion", "fp32", 28), ("momentum", "bf16", 28)):
+                           ("adam", "fp32", 30), ("lion", "fp32", 28), ("momentum", "bf16", 28),
+                           ("adam8", "fp32", 28), ("adam8", "bf16", 28), ("ademamix8", "bf16", 28)):
             cn = 1 << cl
-            hp = hp_kind[ck]
+            hp = hp_kind[ck.rstrip("8")]
             ts = make_flat(ck, cs, cn, seed=cl)
             r = time_rounds(flat_stepper(ck, ts, hp), iters=10 if cl == 28 else 4)
-            b = W.bytes_per_element(ck, cs)
+            b = (W.bytes_per_element_8bit(ck[:-1], cs) if ck.endswith("8")
+                 else W.bytes_per_element(ck, cs))
             gb = b * cn / (r["median_ms"] * 1e-3) / 1e9
             cases[f"{ck}_{cs}_2^{cl}"] = {**r, "GBps": round(gb, 1), "frac_of_peak": round(gb / HBM_PEAK_GBS, 4),
-                                          "elements_per_s": round(cn / (r["median_ms"] * 1e-3), 0)}
+                                          "elements_per_s": round(cn / (r["median_ms"] * 1e-3), 0),
+                                          "bytes_per_element": b}
             del ts
             torch.cuda.empty_cache()
         # update-norm clipping: three launches, 40 B/element for fp32 Adam
@@ -274,6 +292,30 @@ def bench_collection(torch, ou, W, dev, time_rounds):
         res[label] = d
         opt.close()
         torch.cuda.empty_cache()
+    # the page's AdamW8bit collection: tensors of >= 4,096 elements keep 8-bit
+    # block-wise states, smaller ones fp32 states (min_8bit_size = 4,096)
+    ps, gs = [], []
+    for name, shp in shapes:
+        m = W.numel(shp)
+        ps.append(torch.empty(m, device=dev).uniform_(-1, 1, generator=gen).to(torch.bfloat16))
+        gs.append((torch.randn(m, device=dev, generator=gen) * 0.01).to(torch.bfloat16))
+    opt = ou.AdamW8bit(ps, lr=1e-3, weight_decay=0.01, grads=gs, min_8bit_size=4096)
+    big = [W.numel(s[1]) for s in shapes if W.numel(s[1]) >= 4096]
+    small = [W.numel(s[1]) for s in shapes if W.numel(s[1]) < 4096]
+    bytes8 = (sum(big) * W.bytes_per_element_8bit("adam", "bf16")
+              + sum(small) * W.bytes_per_element("adam", "bf16"))
+    d = {"tensors": len(shapes), "tensors_8bit": len(big), "tensors_32bit": len(small),
+         "elements": sum(big) + sum(small), "roofline_us": round(bytes8 / HBM_PEAK_GBS / 1e3, 2)}
+    for mode, fn in (("per_tensor_loop", opt.step_per_tensor), ("plans", lambda: opt.step())):
+        iters = 5 if mode == "per_tensor_loop" else 50
+        r = time_rounds(fn, iters=iters, rounds=7, warmup=5)
+        d[mode] = {"median_us": round(r["median_ms"] * 1e3, 2), "p10_us": round(r["p10_ms"] * 1e3, 2),
+                   "p90_us": round(r["p90_ms"] * 1e3, 2)}
+    d["plans_GBps"] = round(bytes8 / (d["plans"]["median_us"] * 1e-6) / 1e9, 1)
+    res["adamw8bit_505"] = d
+    opt.close()
+    del ps, gs
+    torch.cuda.empty_cache()
     # launch floor: a 1-element update through the C ABI, back to back
     one = [torch.zeros(1, device=dev) for _ in range(4)]
     t = {"i": 0}

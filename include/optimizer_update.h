@@ -233,9 +233,11 @@ void ou_plan_destroy(ou_plan plan);
  *      is not written);
  *   3. the new absmax of each moment is its largest |value| in the block;
  *   4. each moment is stored as the code of the magnitude nearest to
- *      |value| / absmax (0 when absmax is 0), a value exactly halfway going
- *      to the smaller magnitude; the midpoints are binary32 roundings of the
- *      exact midpoints.
+ *      |x|, x = value * fl32(1 / absmax) (one reciprocal per block; x = 0
+ *      when absmax is 0): its index counts the decision points below |x|,
+ *      the binary32 roundings of the exact midpoints between neighbouring
+ *      magnitudes, so a value exactly halfway goes to the smaller magnitude,
+ *      an x above 1 to the largest and a NaN to 0.
  * All-zero codes with zero absmax are the zero state.
  *
  * Layout: state1 holds n codes (ADAM) or 2n (ADEMAMIX: fast EMA at [0, n),

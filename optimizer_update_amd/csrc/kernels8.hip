@@ -11,9 +11,13 @@
 // an fp32 stream, dwordx2 of a 16-bit one, one dword of codes per state).
 // Per block: dequantize (code value x absmax), the 32-bit rule of elem.hpp
 // on the fp32 values, the block's new absmax by a wave max (exact, so the
-// order does not matter), then each state is requantized to the nearest
-// magnitude of value / absmax by a binary search over the decision points.
-// The tables (3 KiB) are copied to LDS once per workgroup.  The parameter
+// order does not matter: DPP rotations inside each 16-lane row, then the
+// four row results), then each state is requantized: x = value *
+// fl32(1 / absmax), and the magnitude index of |x| comes from a key table
+// indexed by the top bits of x plus one decision point (qmap.hpp).  The
+// tables (10 KiB) are copied to LDS once per workgroup.  The kernel is
+// bound by VALU issue: the 32-bit rule alone is ~67 instructions per
+// element, and with 8-bit states the bytes per element drop to 10-16.  The parameter
 // moves with the moments before quantization.  A partial last block, or a
 // tensor whose streams are not aligned for the wide accesses, runs the same
 // steps one element per slot.
@@ -25,62 +29,73 @@
 namespace ou {
 namespace {
 
-__constant__ QTables kQ = make_qtables();
+struct QLds {
+    QTables t;
+    QKeys k;
+};
+static_assert(sizeof(QLds) % 4 == 0, "QLds is copied in dwords");
+
+__constant__ QLds kQ = {make_qtables(), make_qkeys(make_qtables())};
 
 using u32x4 = uint32_t __attribute__((ext_vector_type(4)));
 using u32x2 = uint32_t __attribute__((ext_vector_type(2)));
 
 // Copies the tables into LDS; every thread of the block must call it.
-__device__ __forceinline__ void load_qtables(QTables* T)
+__device__ __forceinline__ void load_qtables(QLds* T)
 {
-    const float* src = reinterpret_cast<const float*>(&kQ);
-    float* dst = reinterpret_cast<float*>(T);
-    for (int i = static_cast<int>(threadIdx.x); i < 768; i += static_cast<int>(blockDim.x))
+    const uint32_t* src = reinterpret_cast<const uint32_t*>(&kQ);
+    uint32_t* dst = reinterpret_cast<uint32_t*>(T);
+    constexpr int kWords = static_cast<int>(sizeof(QLds) / 4);
+    for (int i = static_cast<int>(threadIdx.x); i < kWords; i += static_cast<int>(blockDim.x))
         dst[i] = src[i];
     __syncthreads();
 }
 
-// #{k : bound[k] < a} by halving over 127 (signed) / 255 (unsigned) sorted
-// decision points.
-__device__ __forceinline__ uint32_t qindex_signed(const QTables& T, float a)
+__device__ __forceinline__ float deq_signed(const QLds& T, uint32_t code)
 {
-    uint32_t i = 0;
-#pragma unroll
-    for (uint32_t s = 64; s >= 1; s >>= 1) i += (T.sbound[i + s - 1] < a) ? s : 0u;
-    return i;
-}
-
-__device__ __forceinline__ uint32_t qindex_unsigned(const QTables& T, float a)
-{
-    uint32_t i = 0;
-#pragma unroll
-    for (uint32_t s = 128; s >= 1; s >>= 1) i += (T.ubound[i + s - 1] < a) ? s : 0u;
-    return i;
-}
-
-__device__ __forceinline__ float deq_signed(const QTables& T, uint32_t code)
-{
-    const float v = T.smag[code & 0x7fu];
+    const float v = T.t.smag[code & 0x7fu];
     return (code & 0x80u) ? -v : v;
 }
 
-__device__ __forceinline__ uint32_t quant_signed(const QTables& T, float x)
+__device__ __forceinline__ uint32_t quant_signed(const QLds& T, float x)
 {
-    const uint32_t i = qindex_signed(T, __builtin_fabsf(x));
+    const uint32_t i = qindex<7>(T.k.s, T.t.sbound, __builtin_fabsf(x));
     return (x < 0.0f) ? (i | 0x80u) : i;
 }
 
-// Largest value over the wave (maxNum: a NaN is passed over).
+__device__ __forceinline__ uint32_t quant_unsigned(const QLds& T, float x)
+{
+    return qindex<8>(T.k.u, T.t.ubound, __builtin_fabsf(x));
+}
+
+// Value of lane (l + N) mod 16 of the same 16-lane row (DPP row_ror:N).
+template <int N>
+__device__ __forceinline__ float row_ror(float x)
+{
+    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x120 + N, 0xf, 0xf, false));
+}
+
+__device__ __forceinline__ float lane_value(float x, int lane)
+{
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), lane));
+}
+
+// Largest value over the wave (maxNum: a NaN is passed over); every lane
+// must be active.  Rotations by 1, 2, 4, 8 leave each row's maximum in all
+// its lanes; the four rows are then combined.
 __device__ __forceinline__ float wave_max(float x)
 {
-#pragma unroll
-    for (int off = kWave / 2; off > 0; off >>= 1) x = __builtin_fmaxf(x, __shfl_xor(x, off));
-    return x;
+    x = __builtin_fmaxf(x, row_ror<1>(x));
+    x = __builtin_fmaxf(x, row_ror<2>(x));
+    x = __builtin_fmaxf(x, row_ror<4>(x));
+    x = __builtin_fmaxf(x, row_ror<8>(x));
+    return __builtin_fmaxf(__builtin_fmaxf(lane_value(x, 0), lane_value(x, 16)),
+                           __builtin_fmaxf(lane_value(x, 32), lane_value(x, 48)));
 }
 
 // One quantization block b of segment d, by one wave.
 template <int KIND, typename S>
-__device__ __forceinline__ void update_block8(const Seg8& d, int64_t b, const QTables& T,
+__device__ __forceinline__ void update_block8(const Seg8& d, int64_t b, const QLds& T,
                                               const StepScalars& sc, int lane)
 {
     using raw = typename S::raw;
@@ -147,7 +162,7 @@ __device__ __forceinline__ void update_block8(const Seg8& d, int64_t b, const QT
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
         m[j] = deq_signed(T, (w1 >> (8 * j)) & 0xffu) * A1;
-        v[j] = T.umag[(w2 >> (8 * j)) & 0xffu] * A2;
+        v[j] = T.t.umag[(w2 >> (8 * j)) & 0xffu] * A2;
         m2[j] = 0.0f;
         if constexpr (kMix) m2[j] = deq_signed(T, (w3 >> (8 * j)) & 0xffu) * A3;
         if (!live[j]) {
@@ -174,16 +189,20 @@ __device__ __forceinline__ void update_block8(const Seg8& d, int64_t b, const QT
     l2 = wave_max(l2);
     if constexpr (kMix) l3 = wave_max(l3);
 
-    // requantize
+    // requantize: x = value * fl32(1 / absmax)
+    const float r1 = (l1 > 0.0f) ? 1.0f / l1 : 0.0f;
+    const float r2 = (l2 > 0.0f) ? 1.0f / l2 : 0.0f;
+    float r3 = 0.0f;
+    if constexpr (kMix) r3 = (l3 > 0.0f) ? 1.0f / l3 : 0.0f;
     uint32_t o1 = 0, o2 = 0, o3 = 0;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-        const float x1 = (l1 > 0.0f) ? m[j] / l1 : 0.0f;
-        const float x2 = (l2 > 0.0f) ? v[j] / l2 : 0.0f;
+        const float x1 = (l1 > 0.0f) ? m[j] * r1 : 0.0f;
+        const float x2 = (l2 > 0.0f) ? v[j] * r2 : 0.0f;
         o1 |= quant_signed(T, x1) << (8 * j);
-        o2 |= qindex_unsigned(T, __builtin_fabsf(x2)) << (8 * j);
+        o2 |= quant_unsigned(T, x2) << (8 * j);
         if constexpr (kMix) {
-            const float x3 = (l3 > 0.0f) ? m2[j] / l3 : 0.0f;
+            const float x3 = (l3 > 0.0f) ? m2[j] * r3 : 0.0f;
             o3 |= quant_signed(T, x3) << (8 * j);
         }
     }
@@ -227,7 +246,7 @@ template <int KIND, typename S>
 __global__ void __launch_bounds__(1024)
 k8_single(Seg8 d, StepScalars sc, int32_t blocks_per_wave)
 {
-    __shared__ QTables T;
+    __shared__ QLds T;
     load_qtables(&T);
     const int waves = static_cast<int>(blockDim.x) / kWave;
     const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) / kWave);
@@ -246,7 +265,7 @@ __global__ void __launch_bounds__(1024)
 k8_multi(const Seg8* __restrict__ segs, const WorkItem* __restrict__ items, int64_t n_items,
          int32_t chunk_blocks, StepScalars sc)
 {
-    __shared__ QTables T;
+    __shared__ QLds T;
     load_qtables(&T);
     const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) / kWave);
     const int lane = static_cast<int>(threadIdx.x) % kWave;

@@ -75,4 +75,62 @@ constexpr QTables make_qtables()
 
 inline constexpr QTables kQTablesHost = make_qtables();
 
+// Quantizing without a search.  The magnitude index of a >= 0 is
+// #{k : bound[k] < a}.  The binary32 pattern of a, shifted right by 16 (sign,
+// exponent, top 7 mantissa bits), names a bucket [s, s') of width at most
+// 2^-7 of its binade; for a in [2^-27, 2) the key is that number minus
+// 100 * 128, and smaller or larger a clamp to the first or last key.  A
+// bucket never holds more than one decision point, so with est = the index
+// of the bucket's start s, the index of any a in the bucket is
+// est + (bound[est] < a) (checked for every binary32 value in [0, 2) by the
+// test suite).  Below 2^-27 every a has index 0; NaN is mapped to 0, and a
+// >= 2 (infinity, after a reciprocal that overflowed) to the largest index.
+constexpr int kQKeyBase = 100 << 7;   // bits >> 16 of 2^-27
+constexpr int kQKeys = 28 << 7;       // binades 2^-27 .. 2^0
+
+constexpr uint32_t count_below(const float* bound, int count, float a)
+{
+    int lo = 0, hi = count - 1;   // bound[0 .. count-2] sorted
+    while (lo < hi) {
+        const int mid = (lo + hi) / 2;
+        if (bound[mid] < a) lo = mid + 1; else hi = mid;
+    }
+    return static_cast<uint32_t>(lo);
+}
+
+struct QKeys {
+    uint8_t s[kQKeys];   // signed type: index of each bucket's start
+    uint8_t u[kQKeys];   // unsigned type
+};
+
+constexpr QKeys make_qkeys(const QTables& t)
+{
+    QKeys k{};
+    for (int i = 0; i < kQKeys; ++i) {
+        const float start = __builtin_bit_cast(float, static_cast<uint32_t>(i + kQKeyBase) << 16);
+        k.s[i] = static_cast<uint8_t>(count_below(t.sbound, 128, start));
+        k.u[i] = static_cast<uint8_t>(count_below(t.ubound, 256, start));
+    }
+    return k;
+}
+
+inline constexpr QKeys kQKeysHost = make_qkeys(kQTablesHost);
+
+constexpr uint32_t qkey(float a)
+{
+    const int hi = static_cast<int>(__builtin_bit_cast(uint32_t, a) >> 16) - kQKeyBase;
+    return static_cast<uint32_t>(hi < 0 ? 0 : (hi > kQKeys - 1 ? kQKeys - 1 : hi));
+}
+
+// Magnitude index of a = |x| (a >= 0 or NaN) from the key table and one
+// decision point; P = 7 (signed type) or 8 (unsigned).
+template <int P>
+constexpr uint32_t qindex(const uint8_t* keys, const float* bound, float a)
+{
+    const uint32_t est = keys[qkey(a)];
+    uint32_t idx = est + ((bound[est] < a) ? 1u : 0u);
+    idx = idx > (1u << P) - 1 ? (1u << P) - 1 : idx;
+    return (a == a) ? idx : 0u;
+}
+
 }  // namespace ou

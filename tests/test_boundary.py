@@ -366,3 +366,16 @@ def test_8bit_qmap_matches_the_oracle(L):
         got = np.frombuffer(out, dtype=np.float32)
         assert got.tobytes() == orc.qmap(bool(signed)).tobytes()
         assert L.ou_8bit_qmap(signed, out, count - 1) == OU_EINVAL
+
+
+def test_8bit_quantizer_exhaustive(tmp_path):
+    """The kernels' key-table quantizer (qmap.hpp), compiled for the host:
+    for every binary32 value in [0, 2], infinity and NaN it returns the index
+    of the definition, #{k : bound[k] < a} (NaN -> 0)."""
+    src = os.path.join(os.path.dirname(__file__), "native", "qindex_check.cpp")
+    inc = os.path.join(os.path.dirname(os.path.dirname(__file__)), "optimizer_update_amd", "csrc")
+    exe = tmp_path / "qindex_check"
+    subprocess.run(["g++", "-O2", "-std=c++17", "-ffp-contract=off", "-fopenmp", "-I", inc, src,
+                    "-o", str(exe)], check=True)
+    out = subprocess.run([str(exe)], capture_output=True, text=True, timeout=600)
+    assert out.returncode == 0 and out.stdout.startswith("ok"), out.stdout + out.stderr

@@ -140,6 +140,15 @@ def numel(shape: tuple[int, ...]) -> int:
 STATE_PLANES = {"adam": 2, "ademamix": 3, "momentum": 1, "rmsprop": 1, "adagrad": 1, "lion": 1}
 
 
+def bytes_per_element_8bit(kind: str, storage: str) -> float:
+    """Algorithmic HBM bytes per element and step of the 8-bit block-wise
+    path: read p, g, one code per moment; write p and the codes; plus one
+    fp32 absmax per moment and 256-element block, read and written."""
+    s = STORAGE_BYTES[storage]
+    k = STATE_PLANES[kind]            # moments: Adam 2, AdEMAMix 3
+    return (2 * s + k) + (s + k) + 2 * 4 * k / 256
+
+
 def bytes_per_element(kind: str, storage: str) -> int:
     """Algorithmic HBM bytes per element and step: read p, g, the fp32 states;
     write p and the fp32 states (the gradient is only read)."""
