@@ -53,8 +53,7 @@ __device__ __forceinline__ void load_qtables(QLds* T)
 
 __device__ __forceinline__ float deq_signed(const QLds& T, uint32_t code)
 {
-    const float v = T.t.smag[code & 0x7fu];
-    return (code & 0x80u) ? -v : v;
+    return T.t.svalue[code];
 }
 
 __device__ __forceinline__ uint32_t quant_signed(const QLds& T, float x)
@@ -70,52 +69,66 @@ __device__ __forceinline__ uint32_t quant_unsigned(const QLds& T, float x)
 
 // Value of lane (l + N) mod 16 of the same 16-lane row (DPP row_ror:N).
 template <int N>
-__device__ __forceinline__ float row_ror(float x)
+__device__ __forceinline__ uint32_t row_ror(uint32_t x)
 {
-    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x120 + N, 0xf, 0xf, false));
+    return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(x), 0x120 + N, 0xf, 0xf, false));
 }
 
-__device__ __forceinline__ float lane_value(float x, int lane)
+__device__ __forceinline__ uint32_t lane_value(uint32_t x, int lane)
 {
-    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), lane));
+    return static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(x), lane));
 }
 
-// Largest value over the wave (maxNum: a NaN is passed over); every lane
-// must be active.  Rotations by 1, 2, 4, 8 leave each row's maximum in all
-// its lanes; the four rows are then combined.
+// Largest of the lanes' values, each a non-negative binary32 that is not a
+// NaN (so that the order of the bit patterns as integers is the order of
+// the values); every lane must be active.  Rotations by 1, 2, 4, 8 leave
+// each 16-lane row's maximum in all its lanes; the four rows are then
+// combined on the scalar unit.
 __device__ __forceinline__ float wave_max(float x)
 {
-    x = __builtin_fmaxf(x, row_ror<1>(x));
-    x = __builtin_fmaxf(x, row_ror<2>(x));
-    x = __builtin_fmaxf(x, row_ror<4>(x));
-    x = __builtin_fmaxf(x, row_ror<8>(x));
-    return __builtin_fmaxf(__builtin_fmaxf(lane_value(x, 0), lane_value(x, 16)),
-                           __builtin_fmaxf(lane_value(x, 32), lane_value(x, 48)));
+    uint32_t b = __builtin_bit_cast(uint32_t, x);
+    b = max(b, row_ror<1>(b));
+    b = max(b, row_ror<2>(b));
+    b = max(b, row_ror<4>(b));
+    b = max(b, row_ror<8>(b));
+    const uint32_t r = max(max(lane_value(b, 0), lane_value(b, 16)),
+                           max(lane_value(b, 32), lane_value(b, 48)));
+    return __builtin_bit_cast(float, r);
 }
 
-// One quantization block b of segment d, by one wave.
+// The inputs of one quantization block, as loaded by one wave: lane l
+// holds elements 4l .. 4l+3.
+template <typename S>
+struct Block8 {
+    typename S::raw praw[4], graw[4];
+    uint32_t w1, w2, w3;   // four codes of each state
+    float A1, A2, A3;      // the block's absmax of each state
+    bool live[4];          // element inside the tensor
+    bool full;             // whole block on the wide path
+};
+
 template <int KIND, typename S>
-__device__ __forceinline__ void update_block8(const Seg8& d, int64_t b, const QLds& T,
-                                              const StepScalars& sc, int lane)
+__device__ __forceinline__ Block8<S> load_block8(const Seg8& d, int64_t b, int lane)
 {
     using raw = typename S::raw;
     constexpr bool kMix = KIND == kAdemamix;
-    raw* __restrict__ p = static_cast<raw*>(d.p);
+    const raw* __restrict__ p = static_cast<const raw*>(d.p);
     const raw* __restrict__ g = static_cast<const raw*>(d.g);
-    uint8_t* __restrict__ c1 = d.c1;
-    uint8_t* __restrict__ c2 = d.c2;
+    const uint8_t* __restrict__ c1 = d.c1;
+    const uint8_t* __restrict__ c2 = d.c2;
     const int64_t n = d.n;
     const int64_t e0 = b * kQBlock + 4 * lane;
-    const bool full = d.vec_ok && (b + 1) * kQBlock <= n;
-    const float A1 = d.a1[b];
-    const float A2 = d.a2[b];
-    float A3 = 0.0f;
-    if constexpr (kMix) A3 = d.a1[d.nb + b];
-
-    raw praw[4], graw[4];
+    Block8<S> in;
+    in.full = d.vec_ok && (b + 1) * kQBlock <= n;
+    in.A1 = d.a1[b];
+    in.A2 = d.a2[b];
+    in.A3 = 0.0f;
+    if constexpr (kMix) in.A3 = d.a1[d.nb + b];
+    raw* praw = in.praw;
+    raw* graw = in.graw;
+    bool* live = in.live;
     uint32_t w1 = 0, w2 = 0, w3 = 0;
-    bool live[4];
-    if (full) {
+    if (in.full) {
         if constexpr (S::bytes == 4) {
             const u32x4 xp = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p + e0));
             const u32x4 xg = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(g + e0));
@@ -156,6 +169,30 @@ __device__ __forceinline__ void update_block8(const Seg8& d, int64_t b, const QL
             }
         }
     }
+    in.w1 = w1;
+    in.w2 = w2;
+    in.w3 = w3;
+    return in;
+}
+
+// Dequantize, update, requantize and store one block loaded by load_block8.
+template <int KIND, typename S>
+__device__ __forceinline__ void finish_block8(const Seg8& d, int64_t b, const QLds& T,
+                                              const StepScalars& sc, int lane, Block8<S>& in)
+{
+    using raw = typename S::raw;
+    constexpr bool kMix = KIND == kAdemamix;
+    raw* __restrict__ p = static_cast<raw*>(d.p);
+    uint8_t* __restrict__ c1 = d.c1;
+    uint8_t* __restrict__ c2 = d.c2;
+    const int64_t n = d.n;
+    const int64_t e0 = b * kQBlock + 4 * lane;
+    const bool full = in.full;
+    const float A1 = in.A1, A2 = in.A2, A3 = in.A3;
+    const uint32_t w1 = in.w1, w2 = in.w2, w3 = in.w3;
+    raw* praw = in.praw;
+    const raw* graw = in.graw;
+    const bool* live = in.live;
 
     // dequantize and update
     float m[4], v[4], m2[4];
@@ -177,19 +214,22 @@ __device__ __forceinline__ void update_block8(const Seg8& d, int64_t b, const QL
         praw[j] = S::narrow(pn);
     }
 
-    // new absmax of each state
+    // new absmax of each state (maxNum from 0: a NaN is passed over, so
+    // each lane's value is a non-negative number)
     float l1 = 0.0f, l2 = 0.0f, l3 = 0.0f;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
         l1 = __builtin_fmaxf(l1, __builtin_fabsf(m[j]));
-        l2 = __builtin_fmaxf(l2, v[j]);
+        l2 = __builtin_fmaxf(l2, __builtin_fabsf(v[j]));
         if constexpr (kMix) l3 = __builtin_fmaxf(l3, __builtin_fabsf(m2[j]));
     }
     l1 = wave_max(l1);
     l2 = wave_max(l2);
     if constexpr (kMix) l3 = wave_max(l3);
 
-    // requantize: x = value * fl32(1 / absmax)
+    // requantize: x = value * fl32(1 / absmax).  With absmax = 0 every
+    // value is +-0 or NaN, and r = 0 gives x = +-0 or NaN: code 0, as for
+    // the definition's x = 0.
     const float r1 = (l1 > 0.0f) ? 1.0f / l1 : 0.0f;
     const float r2 = (l2 > 0.0f) ? 1.0f / l2 : 0.0f;
     float r3 = 0.0f;
@@ -197,14 +237,9 @@ __device__ __forceinline__ void update_block8(const Seg8& d, int64_t b, const QL
     uint32_t o1 = 0, o2 = 0, o3 = 0;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-        const float x1 = (l1 > 0.0f) ? m[j] * r1 : 0.0f;
-        const float x2 = (l2 > 0.0f) ? v[j] * r2 : 0.0f;
-        o1 |= quant_signed(T, x1) << (8 * j);
-        o2 |= quant_unsigned(T, x2) << (8 * j);
-        if constexpr (kMix) {
-            const float x3 = (l3 > 0.0f) ? m2[j] * r3 : 0.0f;
-            o3 |= quant_signed(T, x3) << (8 * j);
-        }
+        o1 |= quant_signed(T, m[j] * r1) << (8 * j);
+        o2 |= quant_unsigned(T, v[j] * r2) << (8 * j);
+        if constexpr (kMix) o3 |= quant_signed(T, m2[j] * r3) << (8 * j);
     }
 
     // store
@@ -239,6 +274,27 @@ __device__ __forceinline__ void update_block8(const Seg8& d, int64_t b, const QL
     }
 }
 
+// Blocks b0, b0 + stride, ... (count of them, stopping at the tensor's
+// end) by one wave, the next block's loads issued before the current block
+// is computed.
+template <int KIND, typename S>
+__device__ __forceinline__ void run_blocks8(const Seg8& d, int64_t b0, int64_t stride, int count,
+                                            const QLds& T, const StepScalars& sc, int lane)
+{
+    if (count <= 0 || b0 >= d.nb) return;
+    Block8<S> cur = load_block8<KIND, S>(d, b0, lane);
+    for (int r = 0; r < count; ++r) {
+        const int64_t b = b0 + static_cast<int64_t>(r) * stride;
+        const int64_t bn = b + stride;
+        const bool more = (r + 1 < count) && bn < d.nb;
+        Block8<S> nxt;
+        if (more) nxt = load_block8<KIND, S>(d, bn, lane);
+        finish_block8<KIND, S>(d, b, T, sc, lane, cur);
+        if (!more) break;
+        cur = nxt;
+    }
+}
+
 // Single tensor: workgroup w takes blocks [w*W*R, (w+1)*W*R) with W waves
 // of R blocks each, interleaved so that the W waves work on W neighbouring
 // blocks at a time.
@@ -252,10 +308,7 @@ k8_single(Seg8 d, StepScalars sc, int32_t blocks_per_wave)
     const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) / kWave);
     const int lane = static_cast<int>(threadIdx.x) % kWave;
     const int64_t first = static_cast<int64_t>(blockIdx.x) * waves * blocks_per_wave;
-    for (int r = 0; r < blocks_per_wave; ++r) {
-        const int64_t b = first + static_cast<int64_t>(r) * waves + wave;
-        if (b < d.nb) update_block8<KIND, S>(d, b, T, sc, lane);
-    }
+    run_blocks8<KIND, S>(d, first + wave, waves, blocks_per_wave, T, sc, lane);
 }
 
 // Collection: one wave per work item (segment, run of `chunk_blocks`
@@ -274,10 +327,7 @@ k8_multi(const Seg8* __restrict__ segs, const WorkItem* __restrict__ items, int6
     const WorkItem it = items[w];
     const Seg8 d = segs[__builtin_amdgcn_readfirstlane(it.seg)];
     const int64_t b0 = static_cast<int64_t>(__builtin_amdgcn_readfirstlane(it.chunk)) * chunk_blocks;
-    for (int r = 0; r < chunk_blocks; ++r) {
-        const int64_t b = b0 + r;
-        if (b < d.nb) update_block8<KIND, S>(d, b, T, sc, lane);
-    }
+    run_blocks8<KIND, S>(d, b0, 1, chunk_blocks, T, sc, lane);
 }
 
 template <int KIND, typename S>

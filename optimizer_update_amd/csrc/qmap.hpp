@@ -33,11 +33,12 @@ constexpr int kQBlock = 256;   // elements per quantization block (one wave x 4)
 
 struct QTables {
     float smag[128];     // signed type: magnitudes by index
-    float sbound[128];   // decision points 0..126 (entry 127 unused)
+    float sbound[128];   // decision points 0..126; entry 127 = +inf
     float umag[256];     // unsigned type
-    float ubound[256];   // decision points 0..254 (entry 255 unused)
+    float ubound[256];   // decision points 0..254; entry 255 = +inf
+    float svalue[256];   // signed type: value of each code byte (sign bit 7)
 };
-static_assert(sizeof(QTables) == 768 * 4, "QTables layout");
+static_assert(sizeof(QTables) == 1024 * 4, "QTables layout");
 
 constexpr void build_magnitudes(float* mag, int payload)
 {
@@ -60,7 +61,7 @@ constexpr void build_bounds(const float* mag, float* bound, int count)
 {
     for (int k = 0; k + 1 < count; ++k)
         bound[k] = static_cast<float>((static_cast<double>(mag[k]) + static_cast<double>(mag[k + 1])) * 0.5);
-    bound[count - 1] = 2.0f;   // never compared
+    bound[count - 1] = __builtin_huge_valf();   // no value lies above it
 }
 
 constexpr QTables make_qtables()
@@ -70,6 +71,7 @@ constexpr QTables make_qtables()
     build_magnitudes(t.umag, 8);
     build_bounds(t.smag, t.sbound, 128);
     build_bounds(t.umag, t.ubound, 256);
+    for (int c = 0; c < 256; ++c) t.svalue[c] = (c & 0x80) ? -t.smag[c & 0x7f] : t.smag[c & 0x7f];
     return t;
 }
 
@@ -84,7 +86,8 @@ inline constexpr QTables kQTablesHost = make_qtables();
 // of the bucket's start s, the index of any a in the bucket is
 // est + (bound[est] < a) (checked for every binary32 value in [0, 2) by the
 // test suite).  Below 2^-27 every a has index 0; NaN is mapped to 0, and a
-// >= 2 (infinity, after a reciprocal that overflowed) to the largest index.
+// >= 2 (infinity, after a reciprocal that overflowed) to the largest index,
+// where the +inf sentinel stops the count.
 constexpr int kQKeyBase = 100 << 7;   // bits >> 16 of 2^-27
 constexpr int kQKeys = 28 << 7;       // binades 2^-27 .. 2^0
 
@@ -127,9 +130,9 @@ constexpr uint32_t qkey(float a)
 template <int P>
 constexpr uint32_t qindex(const uint8_t* keys, const float* bound, float a)
 {
+    static_assert(P == 7 || P == 8, "payload bits");
     const uint32_t est = keys[qkey(a)];
-    uint32_t idx = est + ((bound[est] < a) ? 1u : 0u);
-    idx = idx > (1u << P) - 1 ? (1u << P) - 1 : idx;
+    const uint32_t idx = est + ((bound[est] < a) ? 1u : 0u);
     return (a == a) ? idx : 0u;
 }
 
