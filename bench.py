@@ -35,11 +35,18 @@ METRIC = "optimizer-update GB/s (% of HBM peak) on 256M elems; µs per mixed sma
 # the kernels and the launch selection that shapes them
 KERNEL_SOURCES = ("optimizer_update_amd/csrc/kernels.hip", "optimizer_update_amd/csrc/elem.hpp",
                   "optimizer_update_amd/csrc/host.hip")
+# the 8-bit kernels and their launch selection
+KERNEL8_SOURCES = ("optimizer_update_amd/csrc/kernels8.hip", "optimizer_update_amd/csrc/qmap.hpp",
+                   "optimizer_update_amd/csrc/elem.hpp", "optimizer_update_amd/csrc/host8.hip")
+# VALU issue peak from MI355X's fp32 vector rate, 157.3 TFLOP/s = 256 CUs x
+# 128 lanes x 2 (FMA) x 2.4 GHz: 78.6 T lane-instructions/s, i.e. 1,228.8 G
+# wave64 instructions/s (one per 2 cycles per SIMD)
+VALU_PEAK_G = 157.3e3 / 2 / 64
 
 
-def kernel_sha() -> str:
+def kernel_sha(files=KERNEL_SOURCES) -> str:
     h = hashlib.sha256()
-    for f in KERNEL_SOURCES:
+    for f in files:
         with open(os.path.join(ROOT, f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -172,14 +179,45 @@ def main():
         print(json.dumps(bench_collection(torch, ou, W, dev, time_rounds)))
         return
 
+    valu8 = None   # committed VALU instruction counts of the 8-bit kernel
+    vf = os.path.join(ROOT, "profiles", "valu_k8_single_256M.json")
+    if os.path.exists(vf):
+        with open(vf) as f:
+            v = json.load(f)
+        if v.get("kernel8_sources_sha") == kernel_sha(KERNEL8_SOURCES):
+            valu8 = v["valu_wave_instructions_per_block"]
+
+    def alu_roofline(case_key, n, ms):
+        """VALU issue rate of an 8-bit case from the committed counter value."""
+        if not valu8 or case_key not in valu8:
+            return None
+        achieved = valu8[case_key] * (n // 256) / (ms * 1e-3) / 1e9
+        return {"bound": "alu", "achieved": round(achieved, 1), "peak": VALU_PEAK_G,
+                "unit": "G VALU wave-instructions/s", "frac": round(achieved / VALU_PEAK_G, 4)}
+
     # ---------------------------------------------------------------- headline
-    kind, storage, log2n = args.case.split(":")
+    parts = args.case.split(":")
+    kind, storage, log2n = parts[:3]
+    clip = len(parts) > 3 and parts[3] == "clip"
     n = 1 << int(log2n)
     bpe = (W.bytes_per_element_8bit(kind[:-1], storage) if kind.endswith("8")
            else W.bytes_per_element(kind, storage))
     hp_head = hp_kind[kind.rstrip("8")]
     head = make_flat(kind, storage, n, seed=0)
-    ms, wall_ms = time_exact(flat_stepper(kind, head, hp_head), args.steps, args.warmup)
+    stepper = flat_stepper(kind, head, hp_head)
+    if clip:   # update-norm clipping (profiling runs): three launches, 40 B/element
+        ws = ou.clip_workspace(n, dev)
+        cst = {"t": 0}
+
+        def stepper():
+            cst["t"] += 1
+            ou.optimizer_update_32bit_clip(kind, *head, step=cst["t"], lr=hp_head.lr,
+                                           beta1=hp_head.beta1, beta2=hp_head.beta2,
+                                           beta3=hp_head.beta3, alpha=hp_head.alpha,
+                                           eps=hp_head.eps, weight_decay=hp_head.weight_decay,
+                                           max_unorm=1e-3, workspace=ws)
+        bpe = 40 if (kind, storage) == ("adam", "fp32") else bpe
+    ms, wall_ms = time_exact(stepper, args.steps, args.warmup)
     gbs = bpe * n / (ms * 1e-3) / 1e9
 
     out = {
@@ -187,7 +225,8 @@ def main():
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "f32", "data": "synthetic",
-        "config": {"workload": f"{kind}_{storage}_flat_2^{log2n}", "n": n, "kind": kind,
+        "config": {"workload": f"{kind}_{storage}_flat_2^{log2n}" + ("_max_unorm" if clip else ""),
+                   "n": n, "kind": kind,
                    "param_grad_storage": storage,
                    "states": "8-bit block-wise, 256 per block" if kind.endswith("8") else "fp32",
                    "params": "U(-1,1)", "grads": "N(0, (1e-3)^2), fixed",
@@ -199,6 +238,11 @@ def main():
         "host_wall_ms_per_step": round(wall_ms, 4),
         "kernel_sources_sha": kernel_sha(),
     }
+    if kind.endswith("8") and not clip:
+        alu = alu_roofline(f"{kind[:-1]}_{storage}", n, ms)
+        if alu:   # the 8-bit kernel is bound by VALU issue, not by HBM
+            out["roofline_hbm"] = out["roofline"]
+            out["roofline"] = {**alu, "traffic": None}
     tr = os.path.join(ROOT, "profiles", "traffic_single_adam_fp32_256M.json")
     if os.path.exists(tr) and args.case == "adam:fp32:28":
         with open(tr) as f:
@@ -230,6 +274,9 @@ def main():
             cases[f"{ck}_{cs}_2^{cl}"] = {**r, "GBps": round(gb, 1), "frac_of_peak": round(gb / HBM_PEAK_GBS, 4),
                                           "elements_per_s": round(cn / (r["median_ms"] * 1e-3), 0),
                                           "bytes_per_element": b}
+            if ck.endswith("8"):
+                cases[f"{ck}_{cs}_2^{cl}"]["alu_roofline"] = alu_roofline(f"{ck[:-1]}_{cs}", cn,
+                                                                          r["median_ms"])
             del ts
             torch.cuda.empty_cache()
         # update-norm clipping: three launches, 40 B/element for fp32 Adam
