@@ -274,3 +274,87 @@ def test_8bit_collection_routing(orc, cls):
                 orc.update_f32(KIND[kind], O.BF16, pr, g.copy(), s1, s2, hp, t)
             H.assert_parity(p, pr, "bf16", f"{cls} 32-bit p n={n}")
             H.assert_parity(states[0], s1, "fp32", f"{cls} 32-bit m n={n}")
+
+
+@pytest.mark.parametrize("kind", list(KIND))
+def test_8bit_long_run(orc, L, kind):
+    """1,000 steps (the coverage matrix's horizon), bf16 storage, normal and
+    mixed-magnitude gradients redrawn every step, wd 0.01: parameters, codes
+    and absmax bitwise equal to the oracle at steps 1, 2, 10 and 1,000."""
+    T = 1000
+    hp = O.HParams(lr=1e-3, weight_decay=0.01)
+    for pattern in ("normal", "mixed"):
+        for n in (1, 257, 4097):
+            key = (20, list(KIND).index(kind), W.GRAD_PATTERNS.index(pattern), n)
+            p0 = W.params(n, "bf16", W.rng(3, *key))
+            P = H.to_dev(p0, "bf16")
+            G = torch.empty(n, dtype=torch.bfloat16, device="cuda")
+            st = _dev_states(kind, n)
+            ref = (p0.copy(), *_zero_host(kind, n))
+            for t in range(1, T + 1):
+                g = W.grads(n, pattern, "bf16", W.rng(3, *key, t))
+                G.copy_(W.to_torch(g, "bf16", "cuda"))
+                rc = _raw8(L, kind, "bf16", P, G, st, n, hp, t)
+                assert rc == 0, H.last_error(L)
+                orc.update_8bit_f32(KIND[kind], O.BF16, ref[0], g, *ref[1:], hp, t)
+                if t in (1, 2, 10, T):
+                    torch.cuda.synchronize()
+                    got = (W.from_torch(P), *(x.cpu().numpy() for x in st))
+                    _assert_same(got, ref, "bf16", f"{kind} {pattern} n={n} step {t}")
+
+
+def test_8bit_beyond_2_31_elements(orc):
+    """bf16 Adam with 8-bit states on n = 2^31 + 3 elements (element indices
+    past the 32-bit range, 8,388,609 blocks), single entry and a one-segment
+    plan, 2 steps: the two are bitwise equal, and sampled whole blocks (the
+    first, the partial last, those around element 2^31, a stride) equal the
+    oracle run on those blocks alone."""
+    import optimizer_update_amd as ou
+    n, T = (1 << 31) + 3, 2
+    hp = O.HParams(lr=1e-3, weight_decay=0.01)
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(231)
+    P = torch.empty(n, device="cuda").uniform_(-1.0, 1.0, generator=gen).to(torch.bfloat16)
+    G = (torch.randn(n, device="cuda", generator=gen) * 1e-3).to(torch.bfloat16)
+    P2 = P.clone()
+    nb = _nb(n)
+    blocks = np.unique(np.r_[0:2, nb - 2:nb, (1 << 23) - 2:(1 << 23) + 2, 0:nb:500009])
+    blocks = blocks[blocks < nb]          # element 2^31 lies in block 2^23, the last full one
+    idx = np.concatenate([np.arange(b * QB, min(n, (b + 1) * QB)) for b in blocks])
+    idx_dev = torch.from_numpy(idx).cuda()
+    p0 = W.from_torch(P.index_select(0, idx_dev))
+    g0 = W.from_torch(G.index_select(0, idx_dev))
+    a = _dev_states("adam", n)
+    b = _dev_states("adam", n)
+    plan = ou.Plan8("adam", [(P2, G, *b)])
+    try:
+        for t in range(1, T + 1):
+            ou.optimizer_update_8bit_blockwise("adam", P, G, *a, step=t, lr=hp.lr,
+                                               weight_decay=hp.weight_decay)
+            plan.step(H.pkg_hp(hp), t)
+        torch.cuda.synchronize()
+    finally:
+        plan.close()
+    assert torch.equal(P.view(torch.int16), P2.view(torch.int16))
+    for x, y in zip(a, b):
+        assert torch.equal(x.view(torch.uint8), y.view(torch.uint8))
+    got_p = W.from_torch(P.index_select(0, idx_dev))
+    got_c1 = a[0].index_select(0, idx_dev).cpu().numpy()
+    got_c2 = a[1].index_select(0, idx_dev).cpu().numpy()
+    a1 = a[2].cpu().numpy()
+    a2 = a[3].cpu().numpy()
+    off = 0
+    for blk in blocks:
+        lo, hi = blk * QB, min(n, (blk + 1) * QB)
+        m = hi - lo
+        ref = (p0[off:off + m].copy(), *_zero_host("adam", m))
+        for t in range(1, T + 1):
+            orc.update_8bit_f32(O.ADAM, O.BF16, ref[0], g0[off:off + m].copy(), *ref[1:], hp, t)
+        what = f"block {blk}"
+        H.assert_parity(got_p[off:off + m], ref[0], "bf16", "p " + what)
+        assert got_c1[off:off + m].tobytes() == ref[1].tobytes(), what
+        assert got_c2[off:off + m].tobytes() == ref[2].tobytes(), what
+        assert a1[blk] == ref[3][0] and a2[blk] == ref[4][0], what
+        off += m
+    del P, P2, G, a, b
+    torch.cuda.empty_cache()
