@@ -309,7 +309,9 @@ def main():
 
 def bench_collection(torch, ou, W, dev, time_rounds):
     """Model-like collection (bf16 AdamW): full step and small-tensor subset,
-    each as per-tensor loop, one plan launch, graph replay; launch floor."""
+    each as per-tensor loop, one plan launch, graph replay; the same
+    collection as AdamW8bit (min_8bit_size 4,096) and AdEMAMix32; the page's
+    direct cells; launch floor."""
     res = {}
     shapes = W.model_collection()
     gen = torch.Generator(device=dev)
@@ -361,8 +363,45 @@ def bench_collection(torch, ou, W, dev, time_rounds):
     d["plans_GBps"] = round(bytes8 / (d["plans"]["median_us"] * 1e-6) / 1e9, 1)
     res["adamw8bit_505"] = d
     opt.close()
+    # the page's AdEMAMix32bit collection: fp32 states for every tensor
+    opt = ou.AdEMAMix32(ps, lr=1e-3, weight_decay=0.01, grads=gs)
+    bytes_m = sum(big + small) * W.bytes_per_element("ademamix", "bf16")
+    d = {"tensors": len(shapes), "elements": sum(big) + sum(small),
+         "roofline_us": round(bytes_m / HBM_PEAK_GBS / 1e3, 2)}
+    for mode, fn in (("per_tensor_loop", opt.step_per_tensor), ("plan", lambda: opt.step())):
+        iters = 5 if mode == "per_tensor_loop" else 30
+        r = time_rounds(fn, iters=iters, rounds=7, warmup=5)
+        d[mode] = {"median_us": round(r["median_ms"] * 1e3, 2), "p10_us": round(r["p10_ms"] * 1e3, 2),
+                   "p90_us": round(r["p90_ms"] * 1e3, 2)}
+    d["plan_GBps"] = round(bytes_m / (d["plan"]["median_us"] * 1e-6) / 1e9, 1)
+    res["ademamix32_505"] = d
+    opt.close()
     del ps, gs
     torch.cuda.empty_cache()
+    # the page's direct cells: one preallocated tensor per (kind, storage, n),
+    # one optimizer_update_32bit call per step through the C ABI (ctypes)
+    lib = ou.load()
+    stream = torch.cuda.current_stream().cuda_stream
+    cells = {}
+    for kind, code in (("adam", 0), ("ademamix", 1)):
+        for storage, dt in (("fp32", 0), ("fp16", 1), ("bf16", 2)):
+            for n in W.DIRECT_N:
+                p = torch.zeros(n, dtype=W.STORAGE_TORCH[storage], device=dev)
+                g = torch.full((n,), 1e-3, dtype=W.STORAGE_TORCH[storage], device=dev)
+                s1 = torch.zeros((2 if kind == "ademamix" else 1) * n, device=dev)
+                s2 = torch.zeros(n, device=dev)
+                args = (code, dt, p.data_ptr(), g.data_ptr(), s1.data_ptr(), s2.data_ptr(), n,
+                        0.9, 0.999, 0.9999, 5.0, 1e-8, 0.01)
+                assert lib.optimizer_update_32bit(*args, 1, 1e-3, 0, stream) == 0, \
+                    lib.ou_last_error().decode()
+                st = {"t": 1}
+
+                def call():
+                    st["t"] += 1
+                    lib.optimizer_update_32bit(*args, st["t"], 1e-3, 0, stream)
+                r = time_rounds(call, iters=100, rounds=7, warmup=20)
+                cells[f"{kind}_{storage}_{n}"] = round(r["median_ms"] * 1e3, 2)
+    res["direct_cells_us"] = cells
     # launch floor: a 1-element update through the C ABI, back to back
     one = [torch.zeros(1, device=dev) for _ in range(4)]
     t = {"i": 0}

@@ -15,12 +15,17 @@
 // four row results), then each state is requantized: x = value *
 // fl32(1 / absmax), and the magnitude index of |x| comes from a key table
 // indexed by the top bits of x plus one decision point (qmap.hpp).  The
-// tables (10 KiB) are copied to LDS once per workgroup.  The kernel is
-// bound by VALU issue: the 32-bit rule alone is ~67 instructions per
-// element, and with 8-bit states the bytes per element drop to 10-16.  The parameter
+// tables (10 KiB) are copied to LDS once per workgroup.  The parameter
 // moves with the moments before quantization.  A partial last block, or a
 // tensor whose streams are not aligned for the wide accesses, runs the same
 // steps one element per slot.
+//
+// With 10-16 bytes per element against ~470 VALU instructions per block
+// (268 of them the 32-bit rule), the kernel reaches about half of the HBM
+// rate and half of the VALU issue rate at 2^28 elements: each block is one
+// dependent chain (loads, table reads, the cross-lane maximum, a
+// reciprocal, the quantizer), so each wave issues the next block's loads
+// before computing the current block.
 #include "internal.h"
 #include "qmap.hpp"
 
