@@ -748,15 +748,17 @@ int ou_plan_clip_factors(ou_plan plan, float* out, int32_t nseg)
     if (nseg != static_cast<int32_t>(plan->seg_map.size()))
         return fail(OU_EINVAL, "plan has %zu segments, not %d", plan->seg_map.size(), nseg);
     if (int st = check_plan_device(plan)) return st;
+    // one copy per dtype group of its (fl32(lr*s), s) pairs, then scatter
+    std::vector<float> pairs[3];
+    for (const Group& g : plan->groups) {
+        std::vector<float>& h = pairs[g.dtype];
+        h.resize(static_cast<size_t>(2 * g.n_segs));
+        hipError_t e = hipMemcpy(h.data(), g.d_seg_out, h.size() * sizeof(float), hipMemcpyDeviceToHost);
+        if (e != hipSuccess) return hip_fail(e, "hipMemcpy(clip factors)");
+    }
     for (int32_t i = 0; i < nseg; ++i) {
         const auto [dt, slot] = plan->seg_map[static_cast<size_t>(i)];
-        out[i] = 1.0f;
-        if (dt < 0) continue;
-        for (const Group& g : plan->groups) {
-            if (g.dtype != dt) continue;
-            hipError_t e = hipMemcpy(&out[i], g.d_seg_out + 2 * slot + 1, sizeof(float), hipMemcpyDeviceToHost);
-            if (e != hipSuccess) return hip_fail(e, "hipMemcpy(clip factor)");
-        }
+        out[i] = dt < 0 ? 1.0f : pairs[dt][static_cast<size_t>(2 * slot + 1)];
     }
     return OU_OK;
 }
