@@ -355,7 +355,8 @@ def bench_collection(torch, ou, W, dev, time_rounds):
               + sum(small) * W.bytes_per_element("adam", "bf16"))
     d = {"tensors": len(shapes), "tensors_8bit": len(big), "tensors_32bit": len(small),
          "elements": sum(big) + sum(small), "roofline_us": round(bytes8 / HBM_PEAK_GBS / 1e3, 2)}
-    for mode, fn in (("per_tensor_loop", opt.step_per_tensor), ("plans", lambda: opt.step())):
+    for mode, fn in (("per_tensor_loop", opt.step_per_tensor), ("plans", lambda: opt.step()),
+                     ("graph", lambda: opt.step(graph=True))):
         iters = 5 if mode == "per_tensor_loop" else 50
         r = time_rounds(fn, iters=iters, rounds=7, warmup=5)
         d[mode] = {"median_us": round(r["median_ms"] * 1e3, 2), "p10_us": round(r["p10_ms"] * 1e3, 2),

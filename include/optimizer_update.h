@@ -278,6 +278,13 @@ typedef struct {
 typedef struct ou_plan8_s* ou_plan8;
 int ou_plan8_create(int kind, const ou_segment8* segs, int32_t nseg, ou_plan8* out);
 int ou_plan8_step(ou_plan8 plan, const ou_hparams* hp, void* stream);
+
+/* The same step through a HIP graph built on the first call and replayed
+ * with this step's scalars written into its kernel nodes (as
+ * ou_plan_graph_step).  Bitwise identical to ou_plan8_step.  Not allowed
+ * while `stream` is being captured. */
+int ou_plan8_graph_step(ou_plan8 plan, const ou_hparams* hp, void* stream);
+
 void ou_plan8_destroy(ou_plan8 plan);
 
 const char* ou_status_string(int status);

@@ -400,6 +400,14 @@ class Plan8:
         with _on_device(self.device):
             check(self._lib.ou_plan8_step(self._h, ctypes.byref(c), sh), self._lib)
 
+    def graph_step(self, hp: HParams, step: int, stream=None) -> None:
+        """The same step replayed from a HIP graph (``ou_plan8_graph_step``)."""
+        c = hp.c(step)
+        sh = (_raw_stream(self.device.index) if stream is None
+              else (stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)))
+        with _on_device(self.device):
+            check(self._lib.ou_plan8_graph_step(self._h, ctypes.byref(c), sh), self._lib)
+
     def close(self) -> None:
         if getattr(self, "_h", None) is not None and self._h.value:
             torch.cuda.synchronize(self.device)

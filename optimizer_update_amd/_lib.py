@@ -108,6 +108,8 @@ def load(path: str = LIBRARY) -> ctypes.CDLL:
     lib.ou_plan8_create.restype = i32
     lib.ou_plan8_step.argtypes = [vp, ctypes.POINTER(ou_hparams), vp]
     lib.ou_plan8_step.restype = i32
+    lib.ou_plan8_graph_step.argtypes = [vp, ctypes.POINTER(ou_hparams), vp]
+    lib.ou_plan8_graph_step.restype = i32
     lib.ou_plan8_destroy.argtypes = [vp]
     lib.ou_plan8_destroy.restype = None
     lib.ou_status_string.argtypes = [i32]
@@ -125,6 +127,8 @@ def load(path: str = LIBRARY) -> ctypes.CDLL:
     lib.ou__step_scalars.restype = i32
     lib.ou__force_8bit.argtypes = [i32, i32, i32, i32]
     lib.ou__force_8bit.restype = None
+    lib.ou__validate_only.argtypes = [i32]
+    lib.ou__validate_only.restype = None
     if path == LIBRARY:
         _lib = lib
     return lib

@@ -97,6 +97,10 @@ DeviceCache g_devices;
 
 int current_device(const DeviceProps** out) { return g_devices.current(out); }
 
+// test-only: entry points stop after their argument checks (ou__validate_only)
+std::atomic<int> g_validate_only{0};
+bool validate_only() { return g_validate_only.load(std::memory_order_relaxed) != 0; }
+
 int lds_cap(const DeviceProps& d, int blocks)
 {
     if (blocks < 1 || d.lds_per_cu <= 0 || d.lds_per_block <= 0) return 0;
@@ -374,6 +378,7 @@ int build_plan(int kind_arg, const ou_segment* segs, int32_t nseg, ou_plan_s** o
     for (int i = 0; i < nseg; ++i)
         if (int st = check_segment(kind, segs[i], i, &ranges)) return st;
     if (int st = check_overlap(ranges)) return st;
+    if (validate_only()) return OU_OK;
     const DeviceProps* dp = nullptr;
     if (int st = g_devices.current(&dp)) return st;
 
@@ -586,6 +591,7 @@ int optimizer_update_32bit(int kind_arg, int dtype, void* param, const void* gra
     if (int st = check_segment(kind, s, 0, &ranges)) return st;
     if (n == 0) return OU_OK;
     if (int st = check_overlap(ranges)) return st;
+    if (validate_only()) return OU_OK;
     const DeviceProps* dp = nullptr;
     if (int st = g_devices.current(&dp)) return st;
 
@@ -645,6 +651,7 @@ int optimizer_update_32bit_clip(int kind_arg, int dtype, void* param, const void
     const uintptr_t W = reinterpret_cast<uintptr_t>(workspace);
     ranges.push_back({W, W + static_cast<uintptr_t>(need), true, 1});
     if (int st = check_overlap(ranges)) return st;
+    if (validate_only()) return OU_OK;
     const DeviceProps* dp = nullptr;
     if (int st = g_devices.current(&dp)) return st;
 
@@ -698,9 +705,11 @@ int optimizer_update_32bit_multi(int kind_arg, const ou_segment* segs, int32_t n
     if (int st = split_kind(kind_arg, &kind, &after)) return st;
     if (int st = check_hparams(kind, *hp)) return st;
     hipStream_t s = static_cast<hipStream_t>(stream);
-    if (capturing(s)) return fail(OU_ECAPTURE, "optimizer_update_32bit_multi allocates; use a plan under capture");
+    if (!validate_only() && capturing(s))
+        return fail(OU_ECAPTURE, "optimizer_update_32bit_multi allocates; use a plan under capture");
     ou_plan_s* plan = nullptr;
     if (int st = build_plan(kind_arg, segs, nseg, &plan)) return st;
+    if (!plan) return OU_OK;   // validate-only mode
     int st = plan_launch(plan, make_scalars(*hp, after), s);
     hipError_t e = hipStreamSynchronize(s);
     ou_plan_destroy(plan);
@@ -896,6 +905,9 @@ void ou__force_multi(int waves, int epl, int unroll, int chunk, int lds)
     g_force_munroll = unroll;
     g_force_chunk = chunk;
 }
+
+__attribute__((visibility("default")))
+void ou__validate_only(int on) { g_validate_only = on ? 1 : 0; }
 
 __attribute__((visibility("default")))
 int ou__step_scalars(const ou_hparams* hp, float out[12])

@@ -106,11 +106,57 @@ struct ou_plan8_s {
         const void* fn = nullptr;
         int waves = 0;
         int32_t chunk_blocks = 0;
+        int64_t grid = 0;
+        // argument storage of the launch and of the graph node
+        ou::StepScalars sc{};
+        void* args[5] = {};
+        hipGraphNode_t node = nullptr;
     };
     std::vector<Group> groups;
+    hipGraph_t graph = nullptr;
+    hipGraphExec_t exec = nullptr;
 };
 
 using namespace ou;
+
+namespace {
+
+// Points the group's argument array at its own storage, with this step's
+// scalars (k8_multi: segs, items, n_items, chunk_blocks, scalars).
+void set_args8(ou_plan8_s::Group& g, const StepScalars& sc)
+{
+    g.sc = sc;
+    g.args[0] = &g.d_segs;
+    g.args[1] = &g.d_items;
+    g.args[2] = &g.n_items;
+    g.args[3] = &g.chunk_blocks;
+    g.args[4] = &g.sc;
+}
+
+hipKernelNodeParams node_params8(ou_plan8_s::Group& g)
+{
+    hipKernelNodeParams kp{};
+    kp.func = const_cast<void*>(g.fn);
+    kp.gridDim = dim3(static_cast<unsigned>(g.grid));
+    kp.blockDim = dim3(static_cast<unsigned>(g.waves * kWave));
+    kp.sharedMemBytes = 0;
+    kp.kernelParams = g.args;
+    kp.extra = nullptr;
+    return kp;
+}
+
+int check_plan8(ou_plan8 plan, const ou_hparams* hp)
+{
+    if (!plan || !hp) return fail(OU_EINVAL, "null plan or hparams");
+    if (int st = check_hparams(plan->kind, *hp)) return st;
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    if (dev != plan->device) return fail(OU_EINVAL, "plan was created on device %d, current is %d", plan->device, dev);
+    return OU_OK;
+}
+
+}  // namespace
 
 extern "C" {
 
@@ -142,6 +188,7 @@ int optimizer_update_8bit_blockwise(int kind_arg, int dtype, void* param, const 
     if (int st = check_segment8(kind, s, 0, &ranges)) return st;
     if (n == 0) return OU_OK;
     if (int st = check_overlap(ranges)) return st;
+    if (validate_only()) return OU_OK;
     const DeviceProps* dp = nullptr;
     if (int st = current_device(&dp)) return st;
 
@@ -175,6 +222,7 @@ int ou_plan8_create(int kind_arg, const ou_segment8* segs, int32_t nseg, ou_plan
     for (int i = 0; i < nseg; ++i)
         if (int st = check_segment8(kind, segs[i], i, &ranges)) return st;
     if (int st = check_overlap(ranges)) return st;
+    if (validate_only()) return OU_OK;
     const DeviceProps* dp = nullptr;
     if (int st = current_device(&dp)) return st;
 
@@ -225,13 +273,14 @@ int ou_plan8_create(int kind_arg, const ou_segment8* segs, int32_t nseg, ou_plan
             g.chunk_blocks = chunk;
             g.n_items = static_cast<int64_t>(hi[dt].size());
             g.fn = kernel8(true, kind, dt);
+            g.grid = (g.n_items + waves - 1) / waves;
             std::memcpy(host.data() + off, hs[dt].data(), hs[dt].size() * sizeof(Seg8));
             g.d_segs = reinterpret_cast<const Seg8*>(static_cast<unsigned char*>(plan->dmem) + off);
             off = align16(off + hs[dt].size() * sizeof(Seg8));
             std::memcpy(host.data() + off, hi[dt].data(), hi[dt].size() * sizeof(WorkItem));
             g.d_items = reinterpret_cast<const WorkItem*>(static_cast<unsigned char*>(plan->dmem) + off);
             off = align16(off + hi[dt].size() * sizeof(WorkItem));
-            if (!g.fn) {
+            if (!g.fn || g.grid > INT32_MAX) {
                 (void)hipFree(plan->dmem);
                 delete plan;
                 return fail(OU_EINVAL, "no 8-bit multi-tensor kernel");
@@ -252,24 +301,50 @@ int ou_plan8_create(int kind_arg, const ou_segment8* segs, int32_t nseg, ou_plan
 __attribute__((visibility("default")))
 int ou_plan8_step(ou_plan8 plan, const ou_hparams* hp, void* stream)
 {
-    if (!plan || !hp) return fail(OU_EINVAL, "null plan or hparams");
-    if (int st = check_hparams(plan->kind, *hp)) return st;
-    int dev = -1;
-    hipError_t e = hipGetDevice(&dev);
-    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
-    if (dev != plan->device) return fail(OU_EINVAL, "plan was created on device %d, current is %d", plan->device, dev);
-    StepScalars sc = make_scalars(*hp, plan->decay_after);
+    if (int st = check_plan8(plan, hp)) return st;
+    const StepScalars sc = make_scalars(*hp, plan->decay_after);
     for (ou_plan8_s::Group& g : plan->groups) {
-        const int64_t grid = (g.n_items + g.waves - 1) / g.waves;
-        if (grid > INT32_MAX) return fail(OU_EINVAL, "plan too large");
-        int64_t n_items = g.n_items;
-        int32_t chunk = g.chunk_blocks;
-        const Seg8* segs = g.d_segs;
-        const WorkItem* items = g.d_items;
-        void* args[] = {&segs, &items, &n_items, &chunk, &sc};
-        e = launch(g.fn, grid, g.waves * kWave, 0, args, static_cast<hipStream_t>(stream));
+        set_args8(g, sc);
+        hipError_t e = launch(g.fn, g.grid, g.waves * kWave, 0, g.args, static_cast<hipStream_t>(stream));
         if (e != hipSuccess) return hip_fail(e, "launch 8-bit multi-tensor kernel");
     }
+    return OU_OK;
+}
+
+__attribute__((visibility("default")))
+int ou_plan8_graph_step(ou_plan8 plan, const ou_hparams* hp, void* stream)
+{
+    if (int st = check_plan8(plan, hp)) return st;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (capturing(s)) return fail(OU_ECAPTURE, "ou_plan8_graph_step inside a stream capture");
+    if (plan->groups.empty()) return OU_OK;
+    const StepScalars sc = make_scalars(*hp, plan->decay_after);
+    hipError_t e;
+    if (!plan->exec) {
+        e = hipGraphCreate(&plan->graph, 0);
+        if (e != hipSuccess) return hip_fail(e, "hipGraphCreate");
+        for (ou_plan8_s::Group& g : plan->groups) {
+            set_args8(g, sc);
+            const hipKernelNodeParams kp = node_params8(g);
+            // groups touch disjoint memory: independent nodes
+            e = hipGraphAddKernelNode(&g.node, plan->graph, nullptr, 0, &kp);
+            if (e != hipSuccess) return hip_fail(e, "hipGraphAddKernelNode");
+        }
+        e = hipGraphInstantiate(&plan->exec, plan->graph, nullptr, nullptr, 0);
+        if (e != hipSuccess) {
+            plan->exec = nullptr;
+            return hip_fail(e, "hipGraphInstantiate");
+        }
+    } else {
+        for (ou_plan8_s::Group& g : plan->groups) {
+            set_args8(g, sc);
+            const hipKernelNodeParams kp = node_params8(g);
+            e = hipGraphExecKernelNodeSetParams(plan->exec, g.node, &kp);
+            if (e != hipSuccess) return hip_fail(e, "hipGraphExecKernelNodeSetParams");
+        }
+    }
+    e = hipGraphLaunch(plan->exec, s);
+    if (e != hipSuccess) return hip_fail(e, "hipGraphLaunch");
     return OU_OK;
 }
 
@@ -277,6 +352,8 @@ __attribute__((visibility("default")))
 void ou_plan8_destroy(ou_plan8 plan)
 {
     if (!plan) return;
+    if (plan->exec) (void)hipGraphExecDestroy(plan->exec);
+    if (plan->graph) (void)hipGraphDestroy(plan->graph);
     if (plan->dmem) (void)hipFree(plan->dmem);
     delete plan;
 }

@@ -19,6 +19,9 @@ int hip_fail(hipError_t e, const char* what);
 // Properties of the current device (cached per device id); OU_EUNSUPPORTED
 // unless it is a gfx950.
 int current_device(const DeviceProps** out);
+// Test-only switch (ou__validate_only): entry points return OU_OK after their
+// argument checks, before they query or touch a device.
+bool validate_only();
 
 int storage_bytes(int dtype);
 bool valid_kind(int kind);

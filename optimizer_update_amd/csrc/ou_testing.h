@@ -30,6 +30,12 @@ void ou__force_single(int block, int epl, int unroll, int64_t grid, int scalar_o
 // (0 = no forcing; lds -1 = no cap).  chunk must be a multiple of 64 * epl * unroll.
 void ou__force_multi(int waves, int epl, int unroll, int chunk, int lds);
 
+// While on != 0, every entry point returns OU_OK right after its argument
+// checks, before it queries or touches a device: no launch, no allocation
+// (plan creation returns a NULL handle).  Lets the validation tests pass
+// fabricated addresses on any machine.  Process-wide.
+void ou__validate_only(int on);
+
 // The per-step scalars: beta1..3, 1-beta1..3, alpha, eps, lr, bc1, bc2, decay.
 int ou__step_scalars(const ou_hparams* hp, float out[12]);
 

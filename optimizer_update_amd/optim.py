@@ -248,14 +248,14 @@ class _Collection8:
         self.plan32 = Plan(self.kind, seg32, decay_after=self.decay_after) if seg32 else None
 
     @torch.no_grad()
-    def step(self, stream=None) -> None:
+    def step(self, graph: bool = False, stream=None) -> None:
         """One step: the 8-bit plan, then the 32-bit plan (one launch per
-        dtype group each)."""
+        dtype group each), or the replay of their HIP graphs."""
         self.step_count += 1
         if self.plan8 is not None:
-            self.plan8.step(self.hp, self.step_count, stream)
+            (self.plan8.graph_step if graph else self.plan8.step)(self.hp, self.step_count, stream)
         if self.plan32 is not None:
-            self.plan32.step(self.hp, self.step_count, stream)
+            (self.plan32.graph_step if graph else self.plan32.step)(self.hp, self.step_count, stream)
 
     @torch.no_grad()
     def step_per_tensor(self, stream=None) -> None:

@@ -1,7 +1,9 @@
-"""CPU tests of the C ABI (no GPU): exports, layout, validation, dispatch.
+"""CPU tests of the C ABI: exports, layout, validation, dispatch.
 
-Every call here fails validation (or is n = 0) and so returns before the
-library touches the HIP runtime; nothing is launched.
+The calls pass fabricated addresses.  The module runs with the library's
+validate-only switch on (ou__validate_only), so every entry point returns
+right after its argument checks, before it queries or touches a device: the
+tests launch nothing and allocate nothing, with or without a GPU present.
 """
 import ctypes
 import os
@@ -22,7 +24,10 @@ OU_OK, OU_EINVAL, OU_EALIGN, OU_EOVERLAP = 0, -1, -3, -4
 
 @pytest.fixture(scope="module")
 def L():
-    return _lib.load()
+    lib = _lib.load()
+    lib.ou__validate_only(1)
+    yield lib
+    lib.ou__validate_only(0)
 
 
 def test_exports_every_header_function(L):
@@ -33,7 +38,8 @@ def test_exports_every_header_function(L):
                           "ou_plan_create", "ou_plan_step", "ou_plan_graph_step",
                           "ou_plan_describe", "ou_plan_destroy", "ou_status_string",
                           "ou_last_error", "ou_8bit_qmap", "optimizer_update_8bit_blockwise",
-                          "ou_plan8_create", "ou_plan8_step", "ou_plan8_destroy"}
+                          "ou_plan8_create", "ou_plan8_step", "ou_plan8_graph_step",
+                          "ou_plan8_destroy"}
     for n in names:
         assert hasattr(L, n), n
     out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIBRARY], capture_output=True,
@@ -42,7 +48,7 @@ def test_exports_every_header_function(L):
     assert set(names) <= exported
     # nothing else is exported besides the test hooks
     assert exported - set(names) == {"ou__select_single", "ou__force_single", "ou__force_multi",
-                                     "ou__step_scalars", "ou__force_8bit"}
+                                     "ou__step_scalars", "ou__force_8bit", "ou__validate_only"}
 
 
 def test_header_is_plain_c_and_matches_ctypes_layout(tmp_path):
@@ -116,21 +122,20 @@ def test_single_entry_validation(L, case, kw, code):
 
 @pytest.mark.parametrize("kind", [0x100, 0x101, 0x105])
 def test_decay_after_flag_passes_validation(L, kind):
-    assert _call(L, kind=kind, s2=0x40000 if kind != 0x105 else 0) not in (OU_EINVAL, OU_EALIGN, OU_EOVERLAP)
+    assert _call(L, kind=kind, s2=0x40000 if kind != 0x105 else 0) == OU_OK
     h = ctypes.c_void_p()
     st = L.ou_plan_create(kind, _segs((0x100000, 0x200000, 0x300000, 0x400000, 1024, 0, 0)), 1,
                           ctypes.byref(h))
-    assert st not in (OU_EINVAL, OU_EALIGN, OU_EOVERLAP)
-    assert not h.value or L.ou_plan_destroy(h) is None
+    assert st == OU_OK and not h.value
     assert L.ou_plan_create(0x102, _segs((0x100000, 0x200000, 0x300000, 0, 1024, 0, 0)), 1,
                             ctypes.byref(h)) == OU_EINVAL
 
 
 @pytest.mark.parametrize("kind", [2, 3, 4, 5])
 def test_one_state_kinds_ignore_state2(L, kind):
-    # passes validation (then stops at the device query on a machine without a GPU)
+    # state2 is not checked: NULL, misaligned or overlapping, it passes validation
     for s2 in (0, 0x40002, 0x30000, 0x10000):
-        assert _call(L, kind=kind, s2=s2) not in (OU_EINVAL, OU_EALIGN, OU_EOVERLAP)
+        assert _call(L, kind=kind, s2=s2) == OU_OK
     assert _call(L, kind=kind, s1=0x30002) == OU_EALIGN
     assert _call(L, kind=kind, s1=0x20000 + 8) == OU_EOVERLAP
 
@@ -139,14 +144,11 @@ def test_adjacent_buffers_are_not_overlap_and_n0_is_noop(L):
     # n = 0 returns before any device work, whatever the pointers
     assert _call(L, n=0) == OU_OK
     assert _call(L, n=0, p=0, g=0, s1=0, s2=0) == OU_OK
-    # touching ranges pass validation.  Checked through plan creation, which
-    # launches nothing (on a machine with a GPU it would only upload a table
-    # for these fabricated addresses, then be destroyed).
+    # touching ranges pass validation
+    assert _call(L, p=0x10000, g=0x10000 + 64, s1=0x10000 + 128, s2=0x10000 + 192) == OU_OK
     h = ctypes.c_void_p()
     seg = _segs((0x10000, 0x10000 + 64, 0x10000 + 128, 0x10000 + 192, 16, 0, 0))
-    st = L.ou_plan_create(0, seg, 1, ctypes.byref(h))
-    assert st not in (OU_EINVAL, OU_EALIGN, OU_EOVERLAP)
-    L.ou_plan_destroy(h)
+    assert L.ou_plan_create(0, seg, 1, ctypes.byref(h)) == OU_OK and not h.value
 
 
 def test_plan_and_multi_validation(L):
@@ -166,16 +168,15 @@ def test_plan_and_multi_validation(L):
         assert L.optimizer_update_32bit_multi(0, _segs(*rows), len(rows), ctypes.byref(hp), None) == code, name
     # two segments sharing one read-only gradient buffer are allowed by validation
     shared = [ok, (0x800000, 0x200000, 0x900000, 0xa00000, 1024, 0, 0)]
-    st = L.ou_plan_create(0, _segs(*shared), 2, ctypes.byref(h))
-    assert st not in (OU_EINVAL, OU_EALIGN, OU_EOVERLAP)
-    assert not h.value or L.ou_plan_destroy(h) is None
+    assert L.ou_plan_create(0, _segs(*shared), 2, ctypes.byref(h)) == OU_OK
+    hp = _lib.ou_hparams(0.9, 0.999, 0.9999, 5.0, 1e-8, 0.0, 1e-3, 0, 1)
+    assert L.optimizer_update_32bit_multi(0, _segs(*shared), 2, ctypes.byref(hp), None) == OU_OK
     assert L.ou_plan_create(6, _segs(ok), 1, ctypes.byref(h)) == OU_EINVAL
     # a one-state plan ignores state2: NULL, or overlapping anything, passes validation
     for s2 in (0, 0x100000):
         st = L.ou_plan_create(4, _segs((0x100000, 0x200000, 0x300000, s2, 1024, 0, 0)), 1,
                               ctypes.byref(h))
-        assert st not in (OU_EINVAL, OU_EALIGN, OU_EOVERLAP)
-        assert not h.value or L.ou_plan_destroy(h) is None
+        assert st == OU_OK
     assert L.ou_plan_create(0, _segs(ok), 1, None) == OU_EINVAL
     bad_hp = _lib.ou_hparams(0.9, 0.999, 0.9999, 5.0, 1e-8, 0.0, 1e-3, 0, 0)
     assert L.optimizer_update_32bit_multi(0, _segs(ok), 1, ctypes.byref(bad_hp), None) == OU_EINVAL
@@ -210,6 +211,7 @@ def test_clip_entry_validation(L):
     assert _clip(L, ws=0x40000 + 64) == OU_EOVERLAP          # workspace inside state2
     assert _clip(L, ws=0x10000 - 64) == OU_EOVERLAP          # workspace runs into param
     assert _clip(L, step=0) == OU_EINVAL
+    assert _clip(L) == OU_OK                                # passes validation
     assert _clip(L, n=0) == OU_OK                           # nothing to do
     assert _clip(L, max_unorm=0.0, n=0, ws=0) == OU_OK        # plain step, no workspace
     for kind in (2, 3, 4, 5, 0x105):                         # clipping: two-state kinds only
@@ -336,22 +338,21 @@ def test_8bit_entry_validation(L, case, kw, code):
     assert _call8(L, **kw) == code, case
 
 
-def test_8bit_valid_calls_reach_the_device_query(L):
+def test_8bit_valid_calls_pass_validation(L):
     # unaligned codes are allowed (element-by-element path); n = 0 is a no-op
     for kw in (dict(), dict(kind=1), dict(kind=0x100), dict(c1=0x30001, c2=0x40003), dict(dtype=2)):
-        assert _call8(L, **kw) not in (OU_EINVAL, OU_EALIGN, OU_EOVERLAP), kw
+        assert _call8(L, **kw) == OU_OK, kw
     assert _call8(L, n=0, p=0, g=0, c1=0, c2=0, a1=0, a2=0) == OU_OK
     h = ctypes.c_void_p()
     seg = (_lib.ou_segment8 * 1)(_lib.ou_segment8(0x100000, 0x200000, 0x300000, 0x400000, 0x500000,
                                                   0x600000, 4096, 0, 0))
-    st = L.ou_plan8_create(0, seg, 1, ctypes.byref(h))
-    assert st not in (OU_EINVAL, OU_EALIGN, OU_EOVERLAP)
-    L.ou_plan8_destroy(h if h.value else None)
+    assert L.ou_plan8_create(0, seg, 1, ctypes.byref(h)) == OU_OK and not h.value
     assert L.ou_plan8_create(3, seg, 1, ctypes.byref(h)) == OU_EINVAL
     bad = (_lib.ou_segment8 * 1)(_lib.ou_segment8(0x100000, 0x200000, 0x300000, 0x400000, 0x500000,
                                                   0x500000, 4096, 0, 0))
     assert L.ou_plan8_create(0, bad, 1, ctypes.byref(h)) == OU_EOVERLAP
     assert L.ou_plan8_step(None, None, None) == OU_EINVAL
+    assert L.ou_plan8_graph_step(None, None, None) == OU_EINVAL
 
 
 def test_8bit_qmap_matches_the_oracle(L):

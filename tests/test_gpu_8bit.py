@@ -233,33 +233,37 @@ def test_8bit_plan_equals_direct(L, kind):
 def test_8bit_collection_routing(orc, cls):
     """min_8bit_size = 4,096 (the page's default): tensors below it keep fp32
     states and take the 32-bit path, the others 8-bit states.  The plan step
-    equals the per-tensor loop bitwise and each tensor equals its oracle
-    (8-bit or 32-bit)."""
+    equals the per-tensor loop and the graph replay bitwise (eager work
+    between replays) and each tensor equals its oracle (8-bit or 32-bit)."""
     import optimizer_update_amd as ou
     shapes = [(1024,), (4096,), (16, 1024), (4095,), (64,), (1024, 16), (3000, 7)]
     rows = [(W.params(W.numel(s), "bf16", W.rng(3, 15, i)),
              W.grads(W.numel(s), "normal", "bf16", W.rng(3, 16, i))) for i, s in enumerate(shapes)]
     runs = {}
-    for mode in ("plan", "per_tensor"):
+    for mode in ("plan", "per_tensor", "graph"):
         ps = [H.to_dev(p0, "bf16") for p0, _ in rows]
         gs = [H.to_dev(g, "bf16") for _, g in rows]
         opt = getattr(ou, cls)(ps, grads=gs, lr=1e-3, weight_decay=0.01)
         assert [s[0] for s in opt.state] == ["32bit" if W.numel(s) < 4096 else "8bit" for s in shapes]
-        for _ in range(3):
-            if mode == "plan":
-                opt.step()
-            else:
+        for i in range(3):
+            if mode == "per_tensor":
                 opt.step_per_tensor()
+            else:
+                opt.step(graph=(mode == "graph"))
+            if i == 1:          # eager work between replays
+                torch.cuda.synchronize()
+                _ = (ps[0].float() * 2).sum().item()
         torch.cuda.synchronize()
         runs[mode] = [(W.from_torch(p), [x.cpu().numpy() for x in st[1:]]) for p, st in zip(ps, opt.state)]
         hp = O.HParams(**{k: getattr(opt.hp, k) for k in ("lr", "beta1", "beta2", "beta3", "alpha",
                                                           "eps", "weight_decay", "skip_zeros")})
         kind = ou.optim.__dict__[cls].kind
         opt.close()
-    for (pa, sa), (pb, sb) in zip(runs["plan"], runs["per_tensor"]):
-        assert pa.tobytes() == pb.tobytes()
-        for x, y in zip(sa, sb):
-            assert x.tobytes() == y.tobytes()
+    for mode in ("per_tensor", "graph"):
+        for (pa, sa), (pb, sb) in zip(runs["plan"], runs[mode]):
+            assert pa.tobytes() == pb.tobytes(), mode
+            for x, y in zip(sa, sb):
+                assert x.tobytes() == y.tobytes(), mode
     for (p0, g), (p, states), shape in zip(rows, runs["plan"], shapes):
         n = W.numel(shape)
         if n >= 4096:
