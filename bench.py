@@ -34,10 +34,11 @@ HBM_PEAK_GBS = 8000.0
 METRIC = "optimizer-update GB/s (% of HBM peak) on 256M elems; µs per mixed small-tensor step"
 # the kernels and the launch selection that shapes them
 KERNEL_SOURCES = ("optimizer_update_amd/csrc/kernels.hip", "optimizer_update_amd/csrc/elem.hpp",
-                  "optimizer_update_amd/csrc/host.hip")
+                  "optimizer_update_amd/csrc/stepdiv.hpp", "optimizer_update_amd/csrc/host.hip")
 # the 8-bit kernels and their launch selection
 KERNEL8_SOURCES = ("optimizer_update_amd/csrc/kernels8.hip", "optimizer_update_amd/csrc/qmap.hpp",
-                   "optimizer_update_amd/csrc/elem.hpp", "optimizer_update_amd/csrc/host8.hip")
+                   "optimizer_update_amd/csrc/elem.hpp", "optimizer_update_amd/csrc/stepdiv.hpp",
+                   "optimizer_update_amd/csrc/host8.hip")
 # VALU issue peak from MI355X's fp32 vector rate, 157.3 TFLOP/s = 256 CUs x
 # 128 lanes x 2 (FMA) x 2.4 GHz: 78.6 T lane-instructions/s, i.e. 1,228.8 G
 # wave64 instructions/s (one per 2 cycles per SIMD)

@@ -10,11 +10,15 @@
 // Operations are plain binary32 with contraction off (the file pragma below
 // and -ffp-contract=off), correctly rounded division and square root (HIP's
 // default lowering for gfx950) and denormals preserved, so each line is one
-// IEEE operation rounded to nearest even.
+// IEEE operation rounded to nearest even.  The two divisions by the bias
+// corrections take a cheaper route to the same correctly rounded quotient
+// (div_step_constant, stepdiv.hpp).
 #pragma once
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+
+#include "stepdiv.hpp"
 
 #pragma clang fp contract(off)
 
@@ -39,7 +43,9 @@ struct StepScalars {
     int32_t first_step;       // step == 1 (momentum starts its buffer from the gradient)
     int32_t decay_after;      // decoupled decay of the updated parameter: (p - lr*u)*d
     int32_t pad;
+    double rbc1, rbc2;        // binary64 nearest to 1/bc1 and 1/bc2
 };
+
 
 // The moments of one element.  m: fast first moment, v: second moment,
 // m2: slow EMA (AdEMAMix only).  Kingma & Ba (Algorithm 1) for m and v,
@@ -59,8 +65,8 @@ __device__ __forceinline__ void update_moments(float g, float& m, float& v, floa
 template <int KIND>
 __device__ __forceinline__ float direction(float m, float v, float m2, const StepScalars& s)
 {
-    const float mh = m / s.bc1;
-    const float vh = v / s.bc2;
+    const float mh = div_step_constant(m, s.rbc1);   // m / bc1
+    const float vh = div_step_constant(v, s.rbc2);   // v / bc2
     const float den = __builtin_sqrtf(vh) + s.eps;
     float num = mh;
     if constexpr (KIND == kAdemamix) num = mh + s.alpha * m2;

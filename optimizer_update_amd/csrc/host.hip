@@ -237,6 +237,8 @@ StepScalars make_scalars(const ou_hparams& h, int decay_after)
     s.first_step = h.step == 1 ? 1 : 0;
     s.decay_after = decay_after;
     s.pad = 0;
+    s.rbc1 = step_reciprocal(s.bc1);
+    s.rbc2 = step_reciprocal(s.bc2);
     return s;
 }
 

@@ -102,7 +102,8 @@ __device__ __forceinline__ float wave_max(float x)
 }
 
 // The inputs of one quantization block, as loaded by one wave: lane l
-// holds elements 4l .. 4l+3.
+// holds elements 4l .. 4l+3.  WIDE: the block is known to be whole and on
+// the wide path (no per-element checks).
 template <typename S>
 struct Block8 {
     typename S::raw praw[4], graw[4];
@@ -112,7 +113,7 @@ struct Block8 {
     bool full;             // whole block on the wide path
 };
 
-template <int KIND, typename S>
+template <int KIND, typename S, bool WIDE>
 __device__ __forceinline__ Block8<S> load_block8(const Seg8& d, int64_t b, int lane)
 {
     using raw = typename S::raw;
@@ -124,7 +125,7 @@ __device__ __forceinline__ Block8<S> load_block8(const Seg8& d, int64_t b, int l
     const int64_t n = d.n;
     const int64_t e0 = b * kQBlock + 4 * lane;
     Block8<S> in;
-    in.full = d.vec_ok && (b + 1) * kQBlock <= n;
+    in.full = WIDE || (d.vec_ok && (b + 1) * kQBlock <= n);
     in.A1 = d.a1[b];
     in.A2 = d.a2[b];
     in.A3 = 0.0f;
@@ -181,7 +182,7 @@ __device__ __forceinline__ Block8<S> load_block8(const Seg8& d, int64_t b, int l
 }
 
 // Dequantize, update, requantize and store one block loaded by load_block8.
-template <int KIND, typename S>
+template <int KIND, typename S, bool WIDE>
 __device__ __forceinline__ void finish_block8(const Seg8& d, int64_t b, const QLds& T,
                                               const StepScalars& sc, int lane, Block8<S>& in)
 {
@@ -192,7 +193,7 @@ __device__ __forceinline__ void finish_block8(const Seg8& d, int64_t b, const QL
     uint8_t* __restrict__ c2 = d.c2;
     const int64_t n = d.n;
     const int64_t e0 = b * kQBlock + 4 * lane;
-    const bool full = in.full;
+    const bool full = WIDE || in.full;
     const float A1 = in.A1, A2 = in.A2, A3 = in.A3;
     const uint32_t w1 = in.w1, w2 = in.w2, w3 = in.w3;
     raw* praw = in.praw;
@@ -207,7 +208,7 @@ __device__ __forceinline__ void finish_block8(const Seg8& d, int64_t b, const QL
         v[j] = T.t.umag[(w2 >> (8 * j)) & 0xffu] * A2;
         m2[j] = 0.0f;
         if constexpr (kMix) m2[j] = deq_signed(T, (w3 >> (8 * j)) & 0xffu) * A3;
-        if (!live[j]) {
+        if (!WIDE && !live[j]) {
             m[j] = 0.0f;
             v[j] = 0.0f;
             m2[j] = 0.0f;
@@ -272,32 +273,61 @@ __device__ __forceinline__ void finish_block8(const Seg8& d, int64_t b, const QL
             if constexpr (kMix) c1[n + e] = static_cast<uint8_t>(o3 >> (8 * j));
         }
     }
-    if (lane == 0) {
-        d.a1[b] = l1;
-        d.a2[b] = l2;
-        if constexpr (kMix) d.a1[d.nb + b] = l3;
-    }
+    // every lane holds the block maxima: all store them (one address each),
+    // which keeps the store out of a branch
+    d.a1[b] = l1;
+    d.a2[b] = l2;
+    if constexpr (kMix) d.a1[d.nb + b] = l3;
 }
 
 // Blocks b0, b0 + stride, ... (count of them, stopping at the tensor's
 // end) by one wave, the next block's loads issued before the current block
-// is computed.
+// is computed.  Any block: partial, or on the element-by-element path.
 template <int KIND, typename S>
 __device__ __forceinline__ void run_blocks8(const Seg8& d, int64_t b0, int64_t stride, int count,
                                             const QLds& T, const StepScalars& sc, int lane)
 {
     if (count <= 0 || b0 >= d.nb) return;
-    Block8<S> cur = load_block8<KIND, S>(d, b0, lane);
+    Block8<S> cur = load_block8<KIND, S, false>(d, b0, lane);
     for (int r = 0; r < count; ++r) {
         const int64_t b = b0 + static_cast<int64_t>(r) * stride;
         const int64_t bn = b + stride;
         const bool more = (r + 1 < count) && bn < d.nb;
         Block8<S> nxt;
-        if (more) nxt = load_block8<KIND, S>(d, bn, lane);
-        finish_block8<KIND, S>(d, b, T, sc, lane, cur);
+        if (more) nxt = load_block8<KIND, S, false>(d, bn, lane);
+        finish_block8<KIND, S, false>(d, b, T, sc, lane, cur);
         if (!more) break;
         cur = nxt;
     }
+}
+
+// Whether blocks b0 + r * stride (r < count) can all take run_wide8: an
+// even count, every block whole, the tensor on the wide path.
+__device__ __forceinline__ bool wide_run8(const Seg8& d, int64_t b0, int64_t stride, int count)
+{
+    return d.vec_ok && count >= 2 && count % 2 == 0 &&
+           (b0 + static_cast<int64_t>(count - 1) * stride + 1) * kQBlock <= d.n;
+}
+
+// The same blocks when wide_run8 holds, with `a` holding block b0's
+// inputs.  Two block buffers alternate and every load is unconditional,
+// so the loads of one block stay in flight while the other is computed
+// (no register copies between iterations, whose waits would drain them).
+template <int KIND, typename S>
+__device__ __forceinline__ void run_wide8(const Seg8& d, int64_t b0, int64_t stride, int count,
+                                          const QLds& T, const StepScalars& sc, int lane, Block8<S> a)
+{
+    int64_t b = b0;
+    for (int r = 2; r < count; r += 2) {
+        Block8<S> c = load_block8<KIND, S, true>(d, b + stride, lane);
+        finish_block8<KIND, S, true>(d, b, T, sc, lane, a);
+        a = load_block8<KIND, S, true>(d, b + 2 * stride, lane);
+        finish_block8<KIND, S, true>(d, b + stride, T, sc, lane, c);
+        b += 2 * stride;
+    }
+    Block8<S> c = load_block8<KIND, S, true>(d, b + stride, lane);
+    finish_block8<KIND, S, true>(d, b, T, sc, lane, a);
+    finish_block8<KIND, S, true>(d, b + stride, T, sc, lane, c);
 }
 
 // Single tensor: workgroup w takes blocks [w*W*R, (w+1)*W*R) with W waves
@@ -308,12 +338,19 @@ __global__ void __launch_bounds__(1024)
 k8_single(Seg8 d, StepScalars sc, int32_t blocks_per_wave)
 {
     __shared__ QLds T;
-    load_qtables(&T);
     const int waves = static_cast<int>(blockDim.x) / kWave;
     const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) / kWave);
     const int lane = static_cast<int>(threadIdx.x) % kWave;
-    const int64_t first = static_cast<int64_t>(blockIdx.x) * waves * blocks_per_wave;
-    run_blocks8<KIND, S>(d, first + wave, waves, blocks_per_wave, T, sc, lane);
+    const int64_t first = static_cast<int64_t>(blockIdx.x) * waves * blocks_per_wave + wave;
+    // the first block's loads overlap the table copy
+    const bool wide = wide_run8(d, first, waves, blocks_per_wave);
+    Block8<S> a;
+    if (wide) a = load_block8<KIND, S, true>(d, first, lane);
+    load_qtables(&T);
+    if (wide)
+        run_wide8<KIND, S>(d, first, waves, blocks_per_wave, T, sc, lane, a);
+    else
+        run_blocks8<KIND, S>(d, first, waves, blocks_per_wave, T, sc, lane);
 }
 
 // Collection: one wave per work item (segment, run of `chunk_blocks`
@@ -324,15 +361,28 @@ k8_multi(const Seg8* __restrict__ segs, const WorkItem* __restrict__ items, int6
          int32_t chunk_blocks, StepScalars sc)
 {
     __shared__ QLds T;
-    load_qtables(&T);
     const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) / kWave);
     const int lane = static_cast<int>(threadIdx.x) % kWave;
     const int64_t w = static_cast<int64_t>(blockIdx.x) * (blockDim.x / kWave) + wave;
-    if (w >= n_items) return;
-    const WorkItem it = items[w];
-    const Seg8 d = segs[__builtin_amdgcn_readfirstlane(it.seg)];
-    const int64_t b0 = static_cast<int64_t>(__builtin_amdgcn_readfirstlane(it.chunk)) * chunk_blocks;
-    run_blocks8<KIND, S>(d, b0, 1, chunk_blocks, T, sc, lane);
+    const bool active = w < n_items;
+    Seg8 d{};
+    int64_t b0 = 0;
+    bool wide = false;
+    Block8<S> a;
+    if (active) {
+        const WorkItem it = items[w];
+        d = segs[__builtin_amdgcn_readfirstlane(it.seg)];
+        b0 = static_cast<int64_t>(__builtin_amdgcn_readfirstlane(it.chunk)) * chunk_blocks;
+        // the first block's loads overlap the table copy
+        wide = wide_run8(d, b0, 1, chunk_blocks);
+        if (wide) a = load_block8<KIND, S, true>(d, b0, lane);
+    }
+    load_qtables(&T);   // every thread reaches the barrier
+    if (!active) return;
+    if (wide)
+        run_wide8<KIND, S>(d, b0, 1, chunk_blocks, T, sc, lane, a);
+    else
+        run_blocks8<KIND, S>(d, b0, 1, chunk_blocks, T, sc, lane);
 }
 
 template <int KIND, typename S>

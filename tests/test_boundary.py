@@ -380,3 +380,18 @@ def test_8bit_quantizer_exhaustive(tmp_path):
                     "-o", str(exe)], check=True)
     out = subprocess.run([str(exe)], capture_output=True, text=True, timeout=600)
     assert out.returncode == 0 and out.stdout.startswith("ok"), out.stdout + out.stderr
+
+
+def test_step_constant_division_exhaustive(tmp_path):
+    """The kernels divide by the bias corrections through a binary64 product
+    (stepdiv.hpp), compiled here for the host: for bias corrections formed
+    as the library forms them and for the ends of [2^-24, 1], it equals the
+    correctly rounded binary32 quotient for every binary32 numerator (a
+    sample of them for most divisors)."""
+    src = os.path.join(os.path.dirname(__file__), "native", "stepdiv_check.cpp")
+    inc = os.path.join(os.path.dirname(os.path.dirname(__file__)), "optimizer_update_amd", "csrc")
+    exe = tmp_path / "stepdiv_check"
+    subprocess.run(["g++", "-O2", "-std=c++17", "-ffp-contract=off", "-fopenmp", "-I", inc, src,
+                    "-o", str(exe)], check=True)
+    out = subprocess.run([str(exe)], capture_output=True, text=True, timeout=600)
+    assert out.returncode == 0 and out.stdout.startswith("ok"), out.stdout + out.stderr

@@ -139,7 +139,10 @@ def test_8bit_launch_variants_and_paths(orc, L, kind, storage):
         base = _gpu_run(L, kind, storage, p0, gs, hp)
         if n < 70000:
             _assert_same(base, _oracle_run(orc, kind, storage, p0, gs, hp), storage, f"n={n}")
-        for force in ((1, 1, 0, 0), (4, 1, 0, 0), (2, 8, 0, 0), (16, 2, 0, 0), (4, 4, 0, 1)):
+        # even blocks per wave take the pipelined wide path, odd ones the
+        # generic path; the last force is the element-by-element path
+        for force in ((1, 1, 0, 0), (4, 1, 0, 0), (2, 8, 0, 0), (16, 2, 0, 0), (4, 3, 0, 0),
+                      (8, 6, 0, 0), (4, 4, 0, 1)):
             got = _gpu_run(L, kind, storage, p0, gs, hp, force=force)
             for a, b in zip(got, base):
                 assert a.tobytes() == b.tobytes(), (force, n)
@@ -204,7 +207,7 @@ def test_8bit_plan_equals_direct(L, kind):
         gs = [W.cast_storage(np.where(gen.random(n) < 0.1, 0.0, gen.standard_normal(n)), storage)
               for _ in range(T)]
         inputs.append((n, storage, p0, gs, _gpu_run(L, kind, storage, p0, gs, hp)))
-    for chunk in (0, 1, 3):
+    for chunk in (0, 1, 2, 3, 6):
         L.ou__force_8bit(0, 0, chunk, 0)
         try:
             tensors = []
