@@ -20,17 +20,30 @@
 namespace ou {
 namespace {
 
-// Launch shape: 4 waves per workgroup; a wave takes 4 blocks (single tensor)
-// or one work item of 4 blocks (collection), so a workgroup's table copy
-// into LDS serves 16 blocks (4,096 elements).
+// Launch shape: 4 waves per workgroup; a wave takes a run of blocks (single
+// tensor, select_bpw8) or one work item of up to 16 blocks (collection; 16
+// measured best on the bf16 AdamW8bit collection against 2, 4, 8 and 32),
+// so a workgroup's table copy into LDS serves 4 runs.
 constexpr int kWaves8 = 4;
-constexpr int kBlocksPerWave8 = 4;
-constexpr int kChunkBlocks8 = 4;
+constexpr int kChunkBlocks8 = 16;
 
 // test-only forcing (not part of the public ABI)
 std::atomic<int> g8_waves{0}, g8_bpw{0}, g8_chunk{0}, g8_scalar{0};
 
 int64_t nblocks(int64_t n) { return (n + kQBlock - 1) / kQBlock; }
+
+// Blocks per wave of the single-tensor kernel: as many as still leave 4
+// workgroups per CU (a longer run amortizes the table copy and keeps the
+// two-block pipeline full), even (the wide path takes blocks in pairs), and
+// at most 16 for 16-bit storage, 8 for fp32 (measured at 2^28 elements:
+// longer runs stop paying there).
+int32_t select_bpw8(const DeviceProps& dp, int dtype, int64_t nb, int waves)
+{
+    const int64_t cap = dtype == OU_F32 ? 8 : 16;
+    const int64_t cus = dp.cu_count > 0 ? dp.cu_count : 1;
+    const int64_t b = std::min(cap, std::max<int64_t>(2, nb / (cus * 4 * waves)));
+    return static_cast<int32_t>(b & ~int64_t(1));
+}
 
 int split_kind8(int arg, int* kind, int* after)
 {
@@ -193,12 +206,13 @@ int optimizer_update_8bit_blockwise(int kind_arg, int dtype, void* param, const 
     if (int st = current_device(&dp)) return st;
 
     int waves = kWaves8;
-    int32_t bpw = kBlocksPerWave8;
     if (int w = g8_waves.load()) waves = w;
-    if (int b = g8_bpw.load()) bpw = b;
     const void* fn = kernel8(false, kind, dtype);
-    if (!fn || waves < 1 || waves > 16 || bpw < 1) return fail(OU_EINVAL, "no 8-bit kernel for waves=%d", waves);
+    if (!fn || waves < 1 || waves > 16) return fail(OU_EINVAL, "no 8-bit kernel for waves=%d", waves);
     Seg8 d = make_seg8(kind, s);
+    int32_t bpw = select_bpw8(*dp, dtype, d.nb, waves);
+    if (int b = g8_bpw.load()) bpw = b;
+    if (bpw < 1) return fail(OU_EINVAL, "blocks per wave must be >= 1");
     const int64_t per_group = static_cast<int64_t>(waves) * bpw;
     const int64_t grid = (d.nb + per_group - 1) / per_group;
     if (grid > INT32_MAX) return fail(OU_EINVAL, "tensor too large");

@@ -20,12 +20,12 @@
 // tensor whose streams are not aligned for the wide accesses, runs the same
 // steps one element per slot.
 //
-// With 10-16 bytes per element against ~470 VALU instructions per block
-// (268 of them the 32-bit rule), the kernel reaches about half of the HBM
-// rate and half of the VALU issue rate at 2^28 elements: each block is one
-// dependent chain (loads, table reads, the cross-lane maximum, a
-// reciprocal, the quantizer), so each wave issues the next block's loads
-// before computing the current block.
+// Each block is one dependent chain (loads, table reads, the cross-lane
+// maximum, a reciprocal, the quantizer), so a wave keeps the next block's
+// loads in flight while it computes one (run_wide8), and runs of blocks
+// are long enough to amortize the table copy.  Per block the chain costs
+// about 300 VALU instructions against 2.5-4 KiB of HBM traffic, so the
+// kernel sits between the two rooflines rather than on either.
 #include "internal.h"
 #include "qmap.hpp"
 
@@ -34,13 +34,25 @@
 namespace ou {
 namespace {
 
-struct QLds {
+// The tables as built, copied into LDS per workgroup.
+struct QSrc {
     QTables t;
     QKeys k;
 };
-static_assert(sizeof(QLds) % 4 == 0, "QLds is copied in dwords");
+static_assert(sizeof(QTables) % 4 == 0 && sizeof(QKeys) % 4 == 0, "tables are copied in dwords");
 
-__constant__ QLds kQ = {make_qtables(), make_qkeys(make_qtables())};
+__constant__ QSrc kQ = {make_qtables(), make_qkeys(make_qtables())};
+
+// LDS layout: each key table starts at the byte offset of its first key
+// (kQKeyBase) so that a clamped key, plus 0 or kQKeys, is the entry's LDS
+// address with no subtraction; the gap below holds nothing.
+struct QLds {
+    QTables t;
+    uint8_t gap[kQKeyBase - sizeof(QTables)];
+    uint8_t ks[kQKeys];   // signed type: entry of key k at byte k
+    uint8_t ku[kQKeys];   // unsigned type: at byte k + kQKeys
+};
+static_assert(offsetof(QLds, ks) == kQKeyBase && offsetof(QLds, ku) == kQKeyBase + kQKeys, "QLds layout");
 
 using u32x4 = uint32_t __attribute__((ext_vector_type(4)));
 using u32x2 = uint32_t __attribute__((ext_vector_type(2)));
@@ -48,11 +60,12 @@ using u32x2 = uint32_t __attribute__((ext_vector_type(2)));
 // Copies the tables into LDS; every thread of the block must call it.
 __device__ __forceinline__ void load_qtables(QLds* T)
 {
+    constexpr int kTableWords = static_cast<int>(sizeof(QTables) / 4);
+    constexpr int kKeyWords = static_cast<int>(sizeof(QKeys) / 4);
     const uint32_t* src = reinterpret_cast<const uint32_t*>(&kQ);
     uint32_t* dst = reinterpret_cast<uint32_t*>(T);
-    constexpr int kWords = static_cast<int>(sizeof(QLds) / 4);
-    for (int i = static_cast<int>(threadIdx.x); i < kWords; i += static_cast<int>(blockDim.x))
-        dst[i] = src[i];
+    for (int i = static_cast<int>(threadIdx.x); i < kTableWords + kKeyWords; i += static_cast<int>(blockDim.x))
+        dst[i < kTableWords ? i : i - kTableWords + kQKeyBase / 4] = src[i];
     __syncthreads();
 }
 
@@ -61,15 +74,19 @@ __device__ __forceinline__ float deq_signed(const QLds& T, uint32_t code)
     return T.t.svalue[code];
 }
 
+// Codes of a product x (qmap.hpp): the key is the LDS address of its entry.
 __device__ __forceinline__ uint32_t quant_signed(const QLds& T, float x)
 {
-    const uint32_t i = qindex<7>(T.k.s, T.t.sbound, __builtin_fabsf(x));
-    return (x < 0.0f) ? (i | 0x80u) : i;
+    const float a = qmagnitude(x);
+    const uint32_t est = reinterpret_cast<const uint8_t*>(&T)[qkey(a)];
+    return qsigned(x, qindex(est, T.t.sbound, a));
 }
 
 __device__ __forceinline__ uint32_t quant_unsigned(const QLds& T, float x)
 {
-    return qindex<8>(T.k.u, T.t.ubound, __builtin_fabsf(x));
+    const float a = qmagnitude(x);
+    const uint32_t est = reinterpret_cast<const uint8_t*>(&T)[qkey(a) + kQKeys];
+    return qindex(est, T.t.ubound, a);
 }
 
 // Value of lane (l + N) mod 16 of the same 16-lane row (DPP row_ror:N).
@@ -82,6 +99,11 @@ __device__ __forceinline__ uint32_t row_ror(uint32_t x)
 __device__ __forceinline__ uint32_t lane_value(uint32_t x, int lane)
 {
     return static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(x), lane));
+}
+
+__device__ __forceinline__ float lane_float(float x, int lane)
+{
+    return __builtin_bit_cast(float, lane_value(__builtin_bit_cast(uint32_t, x), lane));
 }
 
 // Largest of the lanes' values, each a non-negative binary32 that is not a
@@ -235,11 +257,15 @@ __device__ __forceinline__ void finish_block8(const Seg8& d, int64_t b, const QL
 
     // requantize: x = value * fl32(1 / absmax).  With absmax = 0 every
     // value is +-0 or NaN, and r = 0 gives x = +-0 or NaN: code 0, as for
-    // the definition's x = 0.
-    const float r1 = (l1 > 0.0f) ? 1.0f / l1 : 0.0f;
-    const float r2 = (l2 > 0.0f) ? 1.0f / l2 : 0.0f;
+    // the definition's x = 0.  The states' maxima are wave-uniform: one
+    // division serves them all (lanes 0-31 / 32-63, or thirds for three).
+    float l = (lane < (kMix ? 21 : 32)) ? l1 : l2;
+    if constexpr (kMix) l = (lane < 42) ? l : l3;
+    const float r = (l > 0.0f) ? 1.0f / l : 0.0f;
+    const float r1 = lane_float(r, 0);
+    const float r2 = lane_float(r, kMix ? 21 : 32);
     float r3 = 0.0f;
-    if constexpr (kMix) r3 = (l3 > 0.0f) ? 1.0f / l3 : 0.0f;
+    if constexpr (kMix) r3 = lane_float(r, 42);
     uint32_t o1 = 0, o2 = 0, o3 = 0;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {

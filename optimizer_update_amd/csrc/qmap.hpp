@@ -80,14 +80,15 @@ inline constexpr QTables kQTablesHost = make_qtables();
 // Quantizing without a search.  The magnitude index of a >= 0 is
 // #{k : bound[k] < a}.  The binary32 pattern of a, shifted right by 16 (sign,
 // exponent, top 7 mantissa bits), names a bucket [s, s') of width at most
-// 2^-7 of its binade; for a in [2^-27, 2) the key is that number minus
-// 100 * 128, and smaller or larger a clamp to the first or last key.  A
-// bucket never holds more than one decision point, so with est = the index
-// of the bucket's start s, the index of any a in the bucket is
-// est + (bound[est] < a) (checked for every binary32 value in [0, 2) by the
-// test suite).  Below 2^-27 every a has index 0; NaN is mapped to 0, and a
-// >= 2 (infinity, after a reciprocal that overflowed) to the largest index,
-// where the +inf sentinel stops the count.
+// 2^-7 of its binade; for a in [2^-27, 2) the key is that number, and
+// smaller or larger a clamp to the first or last key (kQKeyBase and
+// kQKeyBase + kQKeys - 1).  A bucket never holds more than one decision
+// point, so with est = the index of the bucket's start s (the key table's
+// entry key - kQKeyBase), the index of any a in the bucket is
+// est + (bound[est] < a).  Below 2^-27 every a has index 0; a >= 2
+// (infinity, after a reciprocal that overflowed) takes the largest index,
+// where the +inf sentinel stops the count.  The test suite checks the
+// composition below against the definition for every binary32 input.
 constexpr int kQKeyBase = 100 << 7;   // bits >> 16 of 2^-27
 constexpr int kQKeys = 28 << 7;       // binades 2^-27 .. 2^0
 
@@ -119,21 +120,29 @@ constexpr QKeys make_qkeys(const QTables& t)
 
 inline constexpr QKeys kQKeysHost = make_qkeys(kQTablesHost);
 
+// The magnitude the quantizer classifies: |x|, with NaN mapped to 0 (maxNum
+// returns the number when one operand is a quiet NaN), so a NaN takes index
+// 0.  x is a product (a state times its block's reciprocal), never a
+// signaling NaN.
+constexpr float qmagnitude(float x) { return __builtin_fmaxf(__builtin_fabsf(x), 0.0f); }
+
+// Key of a = qmagnitude(x): bits >> 16 clamped to
+// [kQKeyBase, kQKeyBase + kQKeys - 1].
 constexpr uint32_t qkey(float a)
 {
-    const int hi = static_cast<int>(__builtin_bit_cast(uint32_t, a) >> 16) - kQKeyBase;
-    return static_cast<uint32_t>(hi < 0 ? 0 : (hi > kQKeys - 1 ? kQKeys - 1 : hi));
+    const uint32_t k = __builtin_bit_cast(uint32_t, a) >> 16;
+    constexpr uint32_t lo = kQKeyBase, hi = kQKeyBase + kQKeys - 1;
+    return k < lo ? lo : (k > hi ? hi : k);
 }
 
-// Magnitude index of a = |x| (a >= 0 or NaN) from the key table and one
-// decision point; P = 7 (signed type) or 8 (unsigned).
-template <int P>
-constexpr uint32_t qindex(const uint8_t* keys, const float* bound, float a)
+// Magnitude index of a from est = the key table's entry for qkey(a).
+constexpr uint32_t qindex(uint32_t est, const float* bound, float a)
 {
-    static_assert(P == 7 || P == 8, "payload bits");
-    const uint32_t est = keys[qkey(a)];
-    const uint32_t idx = est + ((bound[est] < a) ? 1u : 0u);
-    return (a == a) ? idx : 0u;
+    return est + ((bound[est] < a) ? 1u : 0u);
 }
+
+// Signed code: the sign bit for x < 0 (not for -0 or NaN, whose magnitude
+// index is 0).
+constexpr uint32_t qsigned(float x, uint32_t idx) { return (x < 0.0f) ? (idx | 0x80u) : idx; }
 
 }  // namespace ou
