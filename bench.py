@@ -39,10 +39,11 @@ KERNEL_SOURCES = ("optimizer_update_amd/csrc/kernels.hip", "optimizer_update_amd
 KERNEL8_SOURCES = ("optimizer_update_amd/csrc/kernels8.hip", "optimizer_update_amd/csrc/qmap.hpp",
                    "optimizer_update_amd/csrc/elem.hpp", "optimizer_update_amd/csrc/stepdiv.hpp",
                    "optimizer_update_amd/csrc/host8.hip")
-# VALU issue peak from MI355X's fp32 vector rate, 157.3 TFLOP/s = 256 CUs x
-# 128 lanes x 2 (FMA) x 2.4 GHz: 78.6 T lane-instructions/s, i.e. 1,228.8 G
-# wave64 instructions/s (one per 2 cycles per SIMD)
-VALU_PEAK_G = 157.3e3 / 2 / 64
+# VALU issue peak for the kernels as built (packed-fp32 instructions off):
+# MI355X's 157.3 TFLOP/s fp32 vector rate counts packed FMAs (2 per lane);
+# unpacked, each SIMD retires 16 lanes per cycle, one wave64 instruction per
+# 4 cycles: 256 CUs x 4 SIMDs x 2.4 GHz / 4 = 614.4 G wave64 instructions/s
+VALU_PEAK_G = 256 * 4 * 2.4 / 4
 
 
 def kernel_sha(files=KERNEL_SOURCES) -> str:
