@@ -116,6 +116,7 @@ std::atomic<int> g_force_block{0}, g_force_epl{0}, g_force_unroll{0}, g_force_sc
 std::atomic<int64_t> g_force_grid{0};
 std::atomic<int> g_force_waves{0}, g_force_mepl{0}, g_force_munroll{0}, g_force_chunk{0};
 std::atomic<int> g_force_lds{0}, g_force_mlds{0};   // -1 = no cap
+std::atomic<int> g_force_xcd{0};                     // tile run length; -1 = block order
 
 // ---- validation -------------------------------------------------------------
 
@@ -253,6 +254,27 @@ StepScalars make_scalars(const ou_hparams& h, int decay_after)
 // over full occupancy (fp32 Adam 5.9 -> 6.4 TB/s), because fewer tiles in
 // flight keep the seven streams' DRAM accesses more local.  Grid-stride and
 // persistent grids, with or without register double-buffering, were slower.
+// Tiles per XCD run of large single-tensor launches and of plan blocks
+// (measured on MI355X).
+constexpr int kXcdRun = 16;
+constexpr int kXcdRunMulti = 16;
+
+// Tile runs per XCD (xcd_tile): log2 of the run length for grids of at
+// least 64 runs, else -1 (block order).
+int xcd_log2_for(int64_t grid, int run)
+{
+    if (run <= 0 || (run & (run - 1)) != 0) return -1;
+    const int lg = __builtin_ctz(static_cast<unsigned>(run));
+    return grid >= 64 * int64_t(run) ? lg : -1;
+}
+
+// The run after test forcing (ou__force_xcd): -1 = block order.
+int xcd_run_forced(int run)
+{
+    const int f = g_force_xcd.load();
+    return f == 0 ? run : f;
+}
+
 SingleLaunch select_single(const DeviceProps& d, int kind, int dtype, int64_t n, bool vec)
 {
     (void)kind;
@@ -260,6 +282,7 @@ SingleLaunch select_single(const DeviceProps& d, int kind, int dtype, int64_t n,
     SingleLaunch L;
     L.epl = 4;
     L.lds = 0;
+    L.xcd_log2 = -1;
     const int64_t units = vec ? (n + L.epl - 1) / L.epl : n;   // lanes' work units
     if (units <= 1024) {
         L.unroll = 1;
@@ -275,6 +298,7 @@ SingleLaunch select_single(const DeviceProps& d, int kind, int dtype, int64_t n,
     L.grid = std::max<int64_t>(1, std::min<int64_t>((units + per_block - 1) / per_block, INT32_MAX));
     // cap only when the grid oversubscribes the CUs several times over
     if (d.cu_count > 0 && L.grid >= 8LL * d.cu_count) L.lds = lds_cap(d, 2);
+    L.xcd_log2 = xcd_log2_for(L.grid, kXcdRun);
     return L;
 }
 
@@ -310,6 +334,7 @@ void apply_single_forcing(SingleLaunch* L, bool* vec)
     if (int u = g_force_unroll.load()) L->unroll = u;
     if (int64_t gsz = g_force_grid.load()) L->grid = gsz;
     if (int c = g_force_lds.load()) L->lds = c < 0 ? 0 : c;
+    if (g_force_xcd.load()) L->xcd_log2 = xcd_log2_for(L->grid, xcd_run_forced(kXcdRun));
 }
 
 hipError_t launch(const void* fn, int64_t grid, int block, int lds, void** args, hipStream_t stream)
@@ -445,6 +470,8 @@ int build_plan(int kind_arg, const ou_segment* segs, int32_t nseg, ou_plan_s** o
     for (auto& G : hg) {
         std::stable_sort(G.items.begin(), G.items.end(),
                          [](const auto& a, const auto& b) { return a.first > b.first; });
+        const int64_t nblk = static_cast<int64_t>(G.items.size()) / G.L.waves;
+        xcd_order(G.items, G.L.waves, xcd_log2_for(nblk, xcd_run_forced(kXcdRunMulti)));
         if (G.segs.empty()) continue;
         bytes = align16(bytes + G.segs.size() * sizeof(SegDesc));
         bytes = align16(bytes + G.items.size() * sizeof(WorkItem));
@@ -607,7 +634,8 @@ int optimizer_update_32bit(int kind_arg, int dtype, void* param, const void* gra
                     L.unroll, (long long)L.grid);
     StepScalars sc = make_scalars(h, after);
     int32_t vec_ok = vec ? 1 : 0;
-    void* args[] = {&param, const_cast<void**>(&grad), &state1, &state2, &n, &sc, &vec_ok};
+    int32_t xcd = L.xcd_log2;
+    void* args[] = {&param, const_cast<void**>(&grad), &state1, &state2, &n, &sc, &vec_ok, &xcd};
     hipError_t e = launch(fn, L.grid, L.block, L.lds, args, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail(e, "launch single-tensor kernel");
     return OU_OK;
@@ -910,6 +938,9 @@ void ou__force_multi(int waves, int epl, int unroll, int chunk, int lds)
 
 __attribute__((visibility("default")))
 void ou__validate_only(int on) { g_validate_only = on ? 1 : 0; }
+
+__attribute__((visibility("default")))
+void ou__force_xcd(int run) { g_force_xcd = run; }
 
 __attribute__((visibility("default")))
 int ou__step_scalars(const ou_hparams* hp, float out[12])

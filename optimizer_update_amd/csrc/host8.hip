@@ -26,6 +26,8 @@ namespace {
 // so a workgroup's table copy into LDS serves 4 runs.
 constexpr int kWaves8 = 4;
 constexpr int kChunkBlocks8 = 16;
+// Workgroups per XCD run in the launch order of plan work items (xcd_tile).
+constexpr int kXcdRun8 = 16;
 
 // test-only forcing (not part of the public ABI)
 std::atomic<int> g8_waves{0}, g8_bpw{0}, g8_chunk{0}, g8_scalar{0};
@@ -266,6 +268,11 @@ int ou_plan8_create(int kind_arg, const ou_segment8* segs, int32_t nseg, ou_plan
         const int32_t idx = static_cast<int32_t>(hs[s.dtype].size());
         hs[s.dtype].push_back(d);
         for (int64_t c = 0; c < items; ++c) hi[s.dtype].push_back(WorkItem{idx, static_cast<int32_t>(c)});
+    }
+    // launch order of the work items: runs of blocks per XCD (xcd_tile)
+    for (int dt = 0; dt < 3; ++dt) {
+        const int64_t nblk = static_cast<int64_t>(hi[dt].size()) / waves;
+        xcd_order(hi[dt], waves, xcd_log2_for(nblk, xcd_run_forced(kXcdRun8)));
     }
     auto align16 = [](size_t x) { return (x + 15) & ~size_t(15); };
     size_t bytes = 0;

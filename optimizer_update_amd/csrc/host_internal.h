@@ -42,6 +42,24 @@ int check_overlap(std::vector<Range>& r);
 StepScalars make_scalars(const ou_hparams& h, int decay_after);
 
 hipError_t launch(const void* fn, int64_t grid, int block, int lds, void** args, hipStream_t stream);
+
+// log2 of the XCD tile run for a grid (xcd_tile), or -1, after forcing.
+int xcd_log2_for(int64_t grid, int run);
+int xcd_run_forced(int run);
+
+// A plan's work list in launch order: block b (items [b*per_block,
+// (b+1)*per_block)) gets the items of tile xcd_tile(b); whole blocks only.
+template <typename T>
+void xcd_order(std::vector<T>& items, int per_block, int log2c)
+{
+    if (log2c < 0 || per_block < 1) return;
+    const int64_t nfull = static_cast<int64_t>(items.size()) / per_block;
+    const std::vector<T> in(items);
+    for (int64_t b = 0; b < nfull; ++b) {
+        const int64_t t = xcd_tile(b, nfull, log2c);
+        for (int w = 0; w < per_block; ++w) items[b * per_block + w] = in[t * per_block + w];
+    }
+}
 bool capturing(hipStream_t stream);
 
 }  // namespace ou

@@ -36,6 +36,7 @@ struct SingleLaunch {
     int unroll;   // vector groups in flight per lane: 1, 2 or 4
     int64_t grid; // blocks
     int lds;      // dynamic LDS bytes reserved (not used by the kernel) to cap blocks per CU
+    int xcd_log2; // XCD tile runs of 2^xcd_log2 tiles (k_single's xcd_tile), -1: block order
 };
 
 // Launch shape of the multi-tensor kernel.
@@ -73,6 +74,22 @@ constexpr int kClipThreadsHost = 256;   // threads of pass 1
 constexpr int kClipFinalThreadsHost = 1024;   // threads of pass 2
 
 constexpr int kWave = 64;
+
+// Tile (or work-item group) of block b of a grid of g blocks.  MI355X deals
+// workgroups to its 8 XCDs round-robin (block b runs on XCD b mod 8).  With
+// log2c >= 0, XCD x takes the runs of c = 2^log2c consecutive tiles at x*c of
+// every 8c: each XCD streams contiguous memory while the eight stay within
+// one window.  Blocks past the last whole 8c keep their order.  A
+// permutation of [0, g): it changes only which block does which tile.
+// Plans apply it on the host, to the order of their work lists.
+__host__ __device__ __forceinline__ int64_t xcd_tile(int64_t b, int64_t g, int32_t log2c)
+{
+    if (log2c < 0) return b;
+    const int64_t span = int64_t(8) << log2c;
+    if (b >= (g & ~(span - 1))) return b;
+    const int64_t r = b >> 3;
+    return ((r >> log2c) << (log2c + 3)) + ((b & 7) << log2c) + (r & ((int64_t(1) << log2c) - 1));
+}
 
 // Segment descriptor of the 8-bit block-wise path: codes c1 ([K][n] signed,
 // K = 1 Adam, 2 AdEMAMix), c2 ([n] unsigned), absmax a1 ([K][nb]) and a2

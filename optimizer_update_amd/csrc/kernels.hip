@@ -164,16 +164,18 @@ struct Group {
 
 // ---- single tensor ------------------------------------------------------------
 
+
 template <int KIND, typename S, int EPL, int U>
 __global__ void __launch_bounds__(1024)
 k_single(typename S::raw* __restrict__ p, const typename S::raw* __restrict__ g,
          float* __restrict__ s1, float* __restrict__ s2, int64_t n, StepScalars sc,
-         int32_t vec_ok)
+         int32_t vec_ok, int32_t xcd_log2)
 {
     const int64_t nvec = vec_ok ? n / EPL : 0;
     const int64_t bdim = blockDim.x;
     const int64_t nthreads = static_cast<int64_t>(gridDim.x) * bdim;
-    for (int64_t base = static_cast<int64_t>(blockIdx.x) * bdim * U + threadIdx.x; base < nvec;
+    const int64_t bid = xcd_tile(blockIdx.x, gridDim.x, xcd_log2);
+    for (int64_t base = bid * bdim * U + threadIdx.x; base < nvec;
          base += nthreads * U) {
         Group<KIND, S, EPL> grp[U];
 #pragma unroll
@@ -190,8 +192,7 @@ k_single(typename S::raw* __restrict__ p, const typename S::raw* __restrict__ g,
             }
         }
     }
-    for (int64_t i = nvec * EPL + static_cast<int64_t>(blockIdx.x) * bdim + threadIdx.x; i < n;
-         i += nthreads)
+    for (int64_t i = nvec * EPL + bid * bdim + threadIdx.x; i < n; i += nthreads)
         update_scalar<KIND, S>(p, g, s1, s2, n, i, sc);
 }
 

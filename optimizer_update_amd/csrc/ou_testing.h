@@ -30,6 +30,12 @@ void ou__force_single(int block, int epl, int unroll, int64_t grid, int scalar_o
 // (0 = no forcing; lds -1 = no cap).  chunk must be a multiple of 64 * epl * unroll.
 void ou__force_multi(int waves, int epl, int unroll, int chunk, int lds);
 
+// Force the XCD tile runs (xcd_tile) of the single-tensor kernel and of
+// plans created afterwards: run > 0 = runs of `run` tiles (a power of two;
+// block order for grids under 64 runs), -1 = block order, 0 = no forcing.
+// Process-wide.
+void ou__force_xcd(int run);
+
 // While on != 0, every entry point returns OU_OK right after its argument
 // checks, before it queries or touches a device: no launch, no allocation
 // (plan creation returns a NULL handle).  Lets the validation tests pass

@@ -48,7 +48,8 @@ def test_exports_every_header_function(L):
     assert set(names) <= exported
     # nothing else is exported besides the test hooks
     assert exported - set(names) == {"ou__select_single", "ou__force_single", "ou__force_multi",
-                                     "ou__step_scalars", "ou__force_8bit", "ou__validate_only"}
+                                     "ou__step_scalars", "ou__force_8bit", "ou__validate_only",
+                                     "ou__force_xcd"}
 
 
 def test_header_is_plain_c_and_matches_ctypes_layout(tmp_path):

@@ -253,6 +253,69 @@ def test_launch_variants_bitwise(orc, L, kind, storage):
                 plan.close()
 
 
+@pytest.mark.parametrize("kind", KINDS)
+@pytest.mark.parametrize("storage", ["fp32", "bf16"])
+def test_xcd_tile_runs_bitwise(orc, L, kind, storage):
+    """The order in which blocks take tiles (runs of tiles per XCD) only
+    moves work between blocks: every run length, block order, and a
+    grid-stride grid with runs give the default's bits, equal to the oracle
+    on a sample; a plan's work list in each order gives the direct calls'
+    bits.  n = 2^21 - 3 puts 1,024 blocks on the default shape (runs apply)
+    and leaves a one-element tail."""
+    T = 2
+    hp = _hp(kind, 0.01, True)
+    n = (1 << 21) - 3
+    gen = W.rng(0, 7, n)
+    p0 = W.params(n, storage, gen)
+    g_host = W.cast_storage(np.where(gen.random(n) < 0.1, 0.0, gen.standard_normal(n)), storage)
+    base = _run_single(L, kind, storage, p0, g_host, T, hp)
+    idx = np.unique(np.r_[0:4096, n - 4096:n, 0:n:4099])
+    p_ref = p0[idx].copy()
+    s1_ref, s2_ref = W.zero_states(idx.size, kind)
+    for t in range(1, T + 1):
+        orc.update_f32(H.KIND[kind], H.DT[storage], p_ref, g_host[idx].copy(), s1_ref, s2_ref, hp, t)
+    H.assert_parity(base[0][idx], p_ref, storage, "p")
+    H.assert_parity(base[2][idx], s2_ref, "fp32", "v")
+    for run, force in ((-1, None), (1, None), (4, None), (16, None), (128, None),
+                       (8, (256, 4, 2, 512, 0, 0))):
+        L.ou__force_xcd(run)
+        try:
+            out = _run_single(L, kind, storage, p0, g_host, T, hp, force=force)
+        finally:
+            L.ou__force_xcd(0)
+        for a, b_, name in zip(base[:3], out[:3], ("p", "state1", "state2")):
+            assert a.tobytes() == b_.tobytes(), f"run {run} force {force} differs in {name}"
+    # plans order their work lists by the same runs (6,144 items of 512
+    # elements: 1,536 blocks, so runs up to 16 apply)
+    from optimizer_update_amd import Plan
+    k = 2 if kind == "ademamix" else 1
+    m = 1 << 20
+    inputs = []
+    for i in range(3):
+        gen = W.rng(0, 8, i)
+        pi = W.params(m, storage, gen)
+        gi = W.cast_storage(gen.standard_normal(m), storage)
+        inputs.append((pi, gi, _run_single(L, kind, storage, pi, gi, T, hp)))
+    for run in (-1, 1, 16):
+        L.ou__force_xcd(run)
+        try:
+            segs = [(H.to_dev(pi, storage), H.to_dev(gi, storage), torch.zeros(k * m, device="cuda"),
+                     torch.zeros(m, device="cuda")) for pi, gi, _ in inputs]
+            plan = Plan(kind, segs)
+        finally:
+            L.ou__force_xcd(0)
+        try:
+            for t in range(1, T + 1):
+                plan.step(H.pkg_hp(hp), t)
+            torch.cuda.synchronize()
+        finally:
+            plan.close()
+        for (_, _, ref), (P, G, S1, S2) in zip(inputs, segs):
+            for a, b_, name in zip(ref[:3], (W.from_torch(P), W.from_torch(S1), W.from_torch(S2)),
+                                   ("p", "state1", "state2")):
+                assert a.tobytes() == b_.tobytes(), f"plan run {run} differs in {name}"
+
+
 # ----------------------------------------------------------------- sentinel
 
 def test_public_path_ademamix_fp16_n64_first_update(orc, L):
