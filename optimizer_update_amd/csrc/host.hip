@@ -472,6 +472,9 @@ int build_plan(int kind_arg, const ou_segment* segs, int32_t nseg, ou_plan_s** o
                          [](const auto& a, const auto& b) { return a.first > b.first; });
         const int64_t nblk = static_cast<int64_t>(G.items.size()) / G.L.waves;
         xcd_order(G.items, G.L.waves, xcd_log2_for(nblk, xcd_run_forced(kXcdRunMulti)));
+        // clip pass 1 runs one block per clip item
+        const int64_t nclip = static_cast<int64_t>(G.clip_items.size());
+        xcd_order(G.clip_items, 1, xcd_log2_for(nclip, xcd_run_forced(kXcdRunMulti)));
         if (G.segs.empty()) continue;
         bytes = align16(bytes + G.segs.size() * sizeof(SegDesc));
         bytes = align16(bytes + G.items.size() * sizeof(WorkItem));
@@ -709,7 +712,9 @@ int optimizer_update_32bit_clip(int kind_arg, int dtype, void* param, const void
     double2* partials = reinterpret_cast<double2*>(static_cast<unsigned char*>(workspace) + 256);
     hipStream_t hs = static_cast<hipStream_t>(stream);
     const void* cp = param;
-    void* a1[] = {&cp, const_cast<void**>(&grad), &state1, &state2, &n, &sc, &vec_ok, &partials};
+    int32_t xcd1 = xcd_log2_for(chunks, xcd_run_forced(kXcdRun));
+    int32_t xcd3 = xcd_log2_for(grid3, xcd_run_forced(kXcdRun));
+    void* a1[] = {&cp, const_cast<void**>(&grad), &state1, &state2, &n, &sc, &vec_ok, &partials, &xcd1};
     // pass 1 ends in a block barrier: it runs best at full occupancy
     int lds1 = 0;
     if (int c = g_force_lds.load()) lds1 = c < 0 ? 0 : c;
@@ -720,7 +725,7 @@ int optimizer_update_32bit_clip(int kind_arg, int dtype, void* param, const void
     e = launch(f2, 1, kClipFinalThreadsHost, 0, a2, hs);
     if (e != hipSuccess) return hip_fail(e, "launch clip pass 2");
     const float* lr_eff = out;
-    void* a3[] = {&param, const_cast<void**>(&grad), &state1, &state2, &n, &sc, &vec_ok, &lr_eff};
+    void* a3[] = {&param, const_cast<void**>(&grad), &state1, &state2, &n, &sc, &vec_ok, &lr_eff, &xcd3};
     e = launch(f3, grid3, L.block, L.lds, a3, hs);
     if (e != hipSuccess) return hip_fail(e, "launch clip pass 3");
     return OU_OK;

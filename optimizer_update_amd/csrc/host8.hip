@@ -26,7 +26,8 @@ namespace {
 // so a workgroup's table copy into LDS serves 4 runs.
 constexpr int kWaves8 = 4;
 constexpr int kChunkBlocks8 = 16;
-// Workgroups per XCD run in the launch order of plan work items (xcd_tile).
+// Workgroups per XCD run (xcd_tile), single tensors and the launch order of
+// plan work items.
 constexpr int kXcdRun8 = 16;
 
 // test-only forcing (not part of the public ABI)
@@ -219,7 +220,8 @@ int optimizer_update_8bit_blockwise(int kind_arg, int dtype, void* param, const 
     const int64_t grid = (d.nb + per_group - 1) / per_group;
     if (grid > INT32_MAX) return fail(OU_EINVAL, "tensor too large");
     StepScalars sc = make_scalars(h, after);
-    void* args[] = {&d, &sc, &bpw};
+    int32_t xcd = xcd_log2_for(grid, xcd_run_forced(kXcdRun8));
+    void* args[] = {&d, &sc, &bpw, &xcd};
     hipError_t e = launch(fn, grid, waves * kWave, 0, args, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail(e, "launch 8-bit kernel");
     return OU_OK;

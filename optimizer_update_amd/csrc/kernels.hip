@@ -382,16 +382,19 @@ __device__ __forceinline__ double2 clip_chunk(const typename S::raw* __restrict_
     return block_sum2<kClipThreads / kWave>(usq, psq, lds);
 }
 
-// Pass 1, one tensor: one block per chunk (grid = number of chunks).
+// Pass 1, one tensor: one block per chunk (grid = number of chunks), the
+// chunk of a block in XCD runs (xcd_tile); each chunk's sums go to its own
+// slot, so the order does not reach the result.
 template <int KIND, typename S>
 __global__ void __launch_bounds__(kClipThreads)
 k_clip_moments(const typename S::raw* __restrict__ p, const typename S::raw* __restrict__ g,
                float* __restrict__ s1, float* __restrict__ s2, int64_t n, StepScalars sc,
-               int32_t vec_ok, double2* __restrict__ partials)
+               int32_t vec_ok, double2* __restrict__ partials, int32_t xcd_log2)
 {
     __shared__ double2 lds[kClipThreads / kWave];
-    const double2 tot = clip_chunk<KIND, S>(p, g, s1, s2, n, sc, vec_ok != 0, blockIdx.x, lds);
-    if (threadIdx.x == 0) partials[blockIdx.x] = tot;
+    const int64_t chunk = xcd_tile(blockIdx.x, gridDim.x, xcd_log2);
+    const double2 tot = clip_chunk<KIND, S>(p, g, s1, s2, n, sc, vec_ok != 0, chunk, lds);
+    if (threadIdx.x == 0) partials[chunk] = tot;
 }
 
 // Pass 1, collection: one block per (segment, chunk) item; the chunk's sums
@@ -506,14 +509,15 @@ template <int KIND, typename S, int U>
 __global__ void __launch_bounds__(1024)
 k_clip_apply(typename S::raw* __restrict__ p, const typename S::raw* __restrict__ g,
              const float* __restrict__ s1, const float* __restrict__ s2, int64_t n, StepScalars sc,
-             int32_t vec_ok, const float* __restrict__ lr_eff)
+             int32_t vec_ok, const float* __restrict__ lr_eff, int32_t xcd_log2)
 {
     constexpr int SDW = 4 * S::bytes / 4;
     const float lr = lr_eff[0];
     const int64_t nvec = vec_ok ? n / 4 : 0;
     const int64_t bdim = blockDim.x;
     const int64_t nthreads = static_cast<int64_t>(gridDim.x) * bdim;
-    for (int64_t base = static_cast<int64_t>(blockIdx.x) * bdim * U + threadIdx.x; base < nvec;
+    const int64_t bid = xcd_tile(blockIdx.x, gridDim.x, xcd_log2);
+    for (int64_t base = bid * bdim * U + threadIdx.x; base < nvec;
          base += nthreads * U) {
         Words<SDW> wp[U], wg[U];
         Words<4> wm[U], wv[U], wm2[U];
@@ -546,8 +550,7 @@ k_clip_apply(typename S::raw* __restrict__ p, const typename S::raw* __restrict_
             store_words<SDW>(p + 4 * vi, wp[u]);
         }
     }
-    for (int64_t i = 4 * nvec + static_cast<int64_t>(blockIdx.x) * bdim + threadIdx.x; i < n;
-         i += nthreads)
+    for (int64_t i = 4 * nvec + bid * bdim + threadIdx.x; i < n; i += nthreads)
         clip_step1<KIND, S>(p, g, s1, s2, n, i, sc, lr);
 }
 

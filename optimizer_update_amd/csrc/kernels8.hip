@@ -356,18 +356,19 @@ __device__ __forceinline__ void run_wide8(const Seg8& d, int64_t b0, int64_t str
     finish_block8<KIND, S, true>(d, b + stride, T, sc, lane, c);
 }
 
-// Single tensor: workgroup w takes blocks [w*W*R, (w+1)*W*R) with W waves
-// of R blocks each, interleaved so that the W waves work on W neighbouring
-// blocks at a time.
+// Single tensor: workgroup w (in XCD runs, xcd_tile) takes blocks
+// [w*W*R, (w+1)*W*R) with W waves of R blocks each, interleaved so that the
+// W waves work on W neighbouring blocks at a time.
 template <int KIND, typename S>
 __global__ void __launch_bounds__(1024)
-k8_single(Seg8 d, StepScalars sc, int32_t blocks_per_wave)
+k8_single(Seg8 d, StepScalars sc, int32_t blocks_per_wave, int32_t xcd_log2)
 {
     __shared__ QLds T;
     const int waves = static_cast<int>(blockDim.x) / kWave;
     const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) / kWave);
     const int lane = static_cast<int>(threadIdx.x) % kWave;
-    const int64_t first = static_cast<int64_t>(blockIdx.x) * waves * blocks_per_wave + wave;
+    const int64_t wg = xcd_tile(blockIdx.x, gridDim.x, xcd_log2);
+    const int64_t first = wg * waves * blocks_per_wave + wave;
     // the first block's loads overlap the table copy
     const bool wide = wide_run8(d, first, waves, blocks_per_wave);
     Block8<S> a;

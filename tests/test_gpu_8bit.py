@@ -150,6 +150,14 @@ def test_8bit_launch_variants_and_paths(orc, L, kind, storage):
             got = _gpu_run(L, kind, storage, p0, gs, hp, offset=off)
             for a, b in zip(got, base):
                 assert a.tobytes() == b.tobytes(), ("offset", off, n)
+        for run in (4, 16):   # XCD runs of workgroups (one block each: 1,025 of them)
+            L.ou__force_xcd(run)
+            try:
+                got = _gpu_run(L, kind, storage, p0, gs, hp, force=(1, 1, 0, 0))
+            finally:
+                L.ou__force_xcd(0)
+            for a, b in zip(got, base):
+                assert a.tobytes() == b.tobytes(), ("xcd run", run, n)
 
 
 @pytest.mark.parametrize("kind", list(KIND))
@@ -199,7 +207,10 @@ def test_8bit_plan_equals_direct(L, kind):
     import optimizer_update_amd as ou
     T = 3
     hp = O.HParams(lr=1e-3, weight_decay=0.01, skip_zeros=True)
-    specs = [(4096, "bf16"), (257, "fp32"), (65539, "fp16"), (1 << 16, "bf16"), (5000, "fp32")]
+    # with one-block items the bf16 group has 4,368 items (1,092 workgroups):
+    # its work list takes the XCD-run order
+    specs = [(4096, "bf16"), (257, "fp32"), (65539, "fp16"), (1 << 16, "bf16"), (5000, "fp32"),
+             (1 << 20, "bf16")]
     inputs = []
     for i, (n, storage) in enumerate(specs):
         gen = W.rng(3, 14, i)

@@ -90,7 +90,8 @@ def test_clip_matches_oracle(kind, storage):
 @pytest.mark.parametrize("kind", ["adam", "ademamix"])
 def test_clip_launch_variants_bitwise(kind):
     """Pass-3 launch shapes, the per-element path (forced, or from unaligned
-    starts) and repeated runs give bit-identical results and clip factors."""
+    starts), XCD tile runs of passes 1 and 3, and repeated runs give
+    bit-identical results and clip factors."""
     L = H.lib()
     hp = O.HParams(lr=1e-2, weight_decay=0.01, skip_zeros=True)
     for storage in ("fp32", "bf16"):
@@ -107,6 +108,12 @@ def test_clip_launch_variants_bitwise(kind):
                     L.ou__force_single(0, 0, 0, 0, 0, 0)
             for off in (1, 3):
                 runs.append(_gpu_run(kind, storage, p0, gsteps, hp, 0.3, offset=off))
+            for run in (4, 8, -1):   # XCD tile runs (apply from 64 runs of blocks)
+                L.ou__force_xcd(run)
+                try:
+                    runs.append(_gpu_run(kind, storage, p0, gsteps, hp, 0.3))
+                finally:
+                    L.ou__force_xcd(0)
             for i, r in enumerate(runs):
                 for a, b, name in zip(base[:3], r[:3], ("p", "state1", "state2")):
                     assert a.tobytes() == b.tobytes(), (kind, storage, n, i, name)
@@ -234,3 +241,41 @@ def test_collection_optimizer_clip_plan_equals_per_tensor():
         x.step(graph=True)
     x.close()
     y.close()
+
+
+@pytest.mark.parametrize("kind", ["adam", "ademamix"])
+def test_plan_clip_xcd_orders(kind):
+    """A plan's work lists in XCD-run order (regular and clip items) give
+    the block-order plan's bits and clip factors: 2,049 + 1,024 items and
+    769 clip items, so runs of 4 apply to both lists."""
+    import optimizer_update_amd as ou
+    L = H.lib()
+    hp = O.HParams(lr=1e-2, weight_decay=0.01, skip_zeros=True)
+    php = H.pkg_hp(hp)
+    k = 2 if kind == "ademamix" else 1
+    gen = W.rng(0, 16, 1)
+    host = [(s, W.params(n, s, gen), [W.cast_storage(gen.standard_normal(n), s) for _ in range(3)])
+            for s, n in (("bf16", (1 << 20) + 7), ("fp32", 1 << 19))]
+    results = {}
+    for run in (-1, 4, 16):
+        segs = [(H.to_dev(p0, s), torch.empty(p0.size, dtype=W.STORAGE_TORCH[s], device="cuda"),
+                 torch.zeros(k * p0.size, device="cuda"), torch.zeros(p0.size, device="cuda"))
+                for s, p0, _ in host]
+        L.ou__force_xcd(run)
+        try:
+            plan = ou.Plan(kind, segs)
+        finally:
+            L.ou__force_xcd(0)
+        try:
+            for t in range(1, 4):
+                for (s, _, gs), x in zip(host, segs):
+                    x[1].copy_(W.to_torch(gs[t - 1], s, "cuda"))
+                plan.step_clip(php, t, 0.3)
+            torch.cuda.synchronize()
+            results[run] = ([tuple(W.from_torch(x[j]).tobytes() for j in (0, 2, 3)) for x in segs],
+                            plan.clip_factors())
+        finally:
+            plan.close()
+    assert min(results[-1][1]) < 1.0
+    for run in (4, 16):
+        assert results[run] == results[-1], run
