@@ -74,9 +74,10 @@ def parse():
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py: this build runs on one GPU only (the update needs no exchange inside "
-              "a step; see DESIGN.md for how it would shard); rerun with --gpus 1",
-              file=sys.stderr)
+        print("bench.py: measures one GPU only. The update is elementwise, so it shards with no "
+              "exchange inside a step: each GPU would run the same kernels on its own slice of "
+              "the parameters (grads reduce-scattered before, parameters all-gathered after). "
+              "Rerun with --gpus 1", file=sys.stderr)
         sys.exit(2)
 
     import torch
@@ -245,6 +246,40 @@ def main():
         if alu:   # the 8-bit kernel is bound by VALU issue, not by HBM
             out["roofline_hbm"] = out["roofline"]
             out["roofline"] = {**alu, "traffic": None}
+    probe = None
+    if not args.quick and args.case == "adam:fp32:28":
+        # the same traffic in the same launch shape with no arithmetic, on the
+        # same buffers (p, g, m, v read; p, m, v written back unchanged): what
+        # this read/write mix reaches on this device, in this run
+        # in several launch shapes (block, groups per lane, blocks per CU,
+        # XCD run); the best is a measured lower bound on the mix's ceiling
+        lib = ou._lib.load()
+        sh = torch.cuda.current_stream().cuda_stream
+
+        def probe_step():
+            st = lib.ou__stream_probe(head[0].data_ptr(), head[1].data_ptr(), head[2].data_ptr(),
+                                      head[3].data_ptr(), n, sh)
+            if st != 0:
+                raise RuntimeError(lib.ou_last_error().decode())
+        shapes = {"128x4 2/CU run32": (128, 4, 55296, 32), "256x2 2/CU run16": (256, 2, 55296, 16),
+                  "256x2 full run16": (256, 2, -1, 16), "256x1 full run16": (256, 1, -1, 16),
+                  "512x2 2/CU run16": (512, 2, 55296, 16), "256x4 2/CU run32": (256, 4, 55296, 32),
+                  "256x2 2/CU block order": (256, 2, 55296, -1)}
+        probe = {}
+        try:
+            for name, (blk, unr, lds, run) in shapes.items():
+                lib.ou__force_single(blk, 4, unr, 0, 0, lds)
+                lib.ou__force_xcd(run)
+                r = time_rounds(probe_step, iters=10, rounds=5, warmup=5)
+                probe[name] = round(28 * n / (r["median_ms"] * 1e-3) / 1e9, 1)
+        finally:
+            lib.ou__force_single(0, 0, 0, 0, 0, 0)
+            lib.ou__force_xcd(0)
+        best = max(probe, key=probe.get)
+        probe = {"GBps_by_shape": probe, "best_shape": best, "GBps": probe[best],
+                 "what": "4 fp32 streams read, 3 written back unchanged, no arithmetic"}
+        out["roofline"]["stream_probe_GBps"] = probe["GBps"]
+        out["roofline"]["frac_of_stream_probe"] = round(gbs / probe["GBps"], 4)
     tr = os.path.join(ROOT, "profiles", "traffic_single_adam_fp32_256M.json")
     if os.path.exists(tr) and args.case == "adam:fp32:28":
         with open(tr) as f:
@@ -261,6 +296,8 @@ def main():
         dst = torch.empty_like(src)
         r = time_rounds(lambda: dst.copy_(src), iters=20)
         cases["copy_fp32_2^28"] = {**r, "GBps": round(2 * 4 * (1 << 28) / (r["median_ms"] * 1e-3) / 1e9, 1)}
+        if probe:
+            cases["stream_probe_4r3w_fp32_2^28"] = probe
         del src, dst
         torch.cuda.empty_cache()
         for ck, cs, cl in (("adam", "bf16", 28), ("ademamix", "fp32", 28), ("ademamix", "bf16", 28),

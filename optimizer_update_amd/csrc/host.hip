@@ -959,6 +959,32 @@ __attribute__((visibility("default")))
 void ou__force_xcd(int run) { g_force_xcd = run; }
 
 __attribute__((visibility("default")))
+int ou__stream_probe(float* p, const float* g, float* s1, float* s2, int64_t n, void* stream)
+{
+    if (!p || !g || !s1 || !s2 || n <= 0 || n % 4) return fail(OU_EINVAL, "stream probe: bad arguments");
+    const uintptr_t a = reinterpret_cast<uintptr_t>(p) | reinterpret_cast<uintptr_t>(g) |
+                        reinterpret_cast<uintptr_t>(s1) | reinterpret_cast<uintptr_t>(s2);
+    if (a % 16) return fail(OU_EALIGN, "stream probe: buffers must be 16-byte aligned");
+    if (validate_only()) return OU_OK;
+    const DeviceProps* dp = nullptr;
+    if (int st = g_devices.current(&dp)) return st;
+    bool vec = true;
+    SingleLaunch L = select_single(*dp, OU_ADAM, OU_F32, n, vec, true);
+    apply_single_forcing(&L, &vec);
+    const void* fn = stream_probe_kernel(L.unroll);
+    if (!fn || L.epl != 4 || !vec || L.block < kWave || L.block > 1024 || L.block % kWave ||
+        L.grid < 1 || L.grid > INT32_MAX || L.lds < 0 || L.lds > dp->lds_per_block)
+        return fail(OU_EINVAL, "stream probe: no kernel for this shape");
+    int64_t nvec = n / 4;
+    uint32_t mask = 0;
+    int32_t xcd = L.xcd_log2;
+    void* args[] = {&p, const_cast<float**>(&g), &s1, &s2, &nvec, &mask, &xcd};
+    hipError_t e = launch(fn, L.grid, L.block, L.lds, args, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "launch stream probe");
+    return OU_OK;
+}
+
+__attribute__((visibility("default")))
 int ou__step_scalars(const ou_hparams* hp, float out[12])
 {
     if (!hp || !out) return OU_EINVAL;

@@ -69,6 +69,9 @@ const void* multi_kernel(int kind, int dtype, int epl, int unroll);
 // norms), 2 (finalize: clip factor), 3 (parameter step, unroll 1/2/4);
 // 11, 12, 13: the same passes over a plan's collection.
 const void* clip_kernel(int pass, int kind, int dtype, int unroll);
+
+// Bandwidth probe with the plain fp32 Adam update's traffic (test hook).
+const void* stream_probe_kernel(int unroll);
 constexpr int kClipChunkElems = 2048;   // elements per partial-norm chunk
 constexpr int kClipThreadsHost = 256;   // threads of pass 1
 constexpr int kClipFinalThreadsHost = 1024;   // threads of pass 2

@@ -698,6 +698,65 @@ const void* clip_kernel(int pass, int kind, int dtype, int unroll)
     return nullptr;
 }
 
+namespace {
+
+// ---- bandwidth probe (test hook) ------------------------------------------------
+
+// The plain fp32 Adam update's traffic with no arithmetic: four fp32 streams
+// read, three written back, in k_single's tiles, groups, non-temporal
+// accesses and XCD runs.  Each stored value is the loaded one xor (g & mask)
+// with mask = 0 from the host: the gradient is really read, no store can be
+// dropped as rewriting the loaded value, and every value written equals the
+// one read.  It measures what this read/write mix reaches on the device.
+template <int U>
+__global__ void __launch_bounds__(1024)
+k_stream_probe(float* __restrict__ p, const float* __restrict__ g, float* __restrict__ s1,
+               float* __restrict__ s2, int64_t nvec, uint32_t mask, int32_t xcd_log2)
+{
+    const int64_t bdim = blockDim.x;
+    const int64_t nthreads = static_cast<int64_t>(gridDim.x) * bdim;
+    const int64_t bid = xcd_tile(blockIdx.x, gridDim.x, xcd_log2);
+    for (int64_t base = bid * bdim * U + threadIdx.x; base < nvec; base += nthreads * U) {
+        Words<4> wp[U], wg[U], wm[U], wv[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int64_t vi = base + u * bdim;
+            if (vi >= nvec) continue;
+            wp[u] = load_words<4>(p + 4 * vi);
+            wg[u] = load_words<4>(g + 4 * vi);
+            wm[u] = load_words<4>(s1 + 4 * vi);
+            wv[u] = load_words<4>(s2 + 4 * vi);
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int64_t vi = base + u * bdim;
+            if (vi >= nvec) continue;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {   // every stored value depends on the mask
+                const uint32_t x = wg[u].w[j] & mask;
+                wp[u].w[j] ^= x;
+                wm[u].w[j] ^= x;
+                wv[u].w[j] ^= x;
+            }
+            store_words<4>(p + 4 * vi, wp[u]);
+            store_words<4>(s1 + 4 * vi, wm[u]);
+            store_words<4>(s2 + 4 * vi, wv[u]);
+        }
+    }
+}
+
+}  // namespace
+
+const void* stream_probe_kernel(int unroll)
+{
+    switch (unroll) {
+    case 1: return reinterpret_cast<const void*>(&k_stream_probe<1>);
+    case 2: return reinterpret_cast<const void*>(&k_stream_probe<2>);
+    case 4: return reinterpret_cast<const void*>(&k_stream_probe<4>);
+    default: return nullptr;
+    }
+}
+
 const void* single_kernel(int kind, int dtype, int epl, int unroll)
 {
     return pick_all(false, kind, dtype, epl, unroll);

@@ -36,6 +36,12 @@ void ou__force_multi(int waves, int epl, int unroll, int chunk, int lds);
 // Process-wide.
 void ou__force_xcd(int run);
 
+// Bandwidth probe: the traffic of the plain fp32 Adam update of n elements
+// (p, g, s1, s2 read; p, s1, s2 written back unchanged) in the same launch
+// shape, with no arithmetic; n a multiple of 4, buffers 16-byte aligned.
+// Asynchronous on `stream`.  For measuring what the read/write mix reaches.
+int ou__stream_probe(float* p, const float* g, float* s1, float* s2, int64_t n, void* stream);
+
 // While on != 0, every entry point returns OU_OK right after its argument
 // checks, before it queries or touches a device: no launch, no allocation
 // (plan creation returns a NULL handle).  Lets the validation tests pass

@@ -49,7 +49,7 @@ def test_exports_every_header_function(L):
     # nothing else is exported besides the test hooks
     assert exported - set(names) == {"ou__select_single", "ou__force_single", "ou__force_multi",
                                      "ou__step_scalars", "ou__force_8bit", "ou__validate_only",
-                                     "ou__force_xcd"}
+                                     "ou__force_xcd", "ou__stream_probe"}
 
 
 def test_header_is_plain_c_and_matches_ctypes_layout(tmp_path):
@@ -396,3 +396,12 @@ def test_step_constant_division_exhaustive(tmp_path):
                     "-o", str(exe)], check=True)
     out = subprocess.run([str(exe)], capture_output=True, text=True, timeout=600)
     assert out.returncode == 0 and out.stdout.startswith("ok"), out.stdout + out.stderr
+
+
+def test_stream_probe_validation(L):
+    """The bandwidth probe's argument checks (test hook)."""
+    assert L.ou__stream_probe(0x10000, 0x20000, 0x30000, 0x40000, 1 << 20, None) == OU_OK
+    assert L.ou__stream_probe(0x10000, 0x20000, 0x30000, 0x40000, 6, None) == OU_EINVAL
+    assert L.ou__stream_probe(0x10000, 0x20000, 0x30000, 0x40000, 0, None) == OU_EINVAL
+    assert L.ou__stream_probe(0, 0x20000, 0x30000, 0x40000, 16, None) == OU_EINVAL
+    assert L.ou__stream_probe(0x10004, 0x20000, 0x30000, 0x40000, 16, None) == OU_EALIGN

@@ -316,6 +316,21 @@ def test_xcd_tile_runs_bitwise(orc, L, kind, storage):
                 assert a.tobytes() == b_.tobytes(), f"plan run {run} differs in {name}"
 
 
+def test_stream_probe_leaves_buffers_unchanged(L):
+    """The bandwidth probe reads four streams and writes three back: every
+    buffer keeps its bits (the sizes put it on the large-tensor shape, with
+    XCD runs and a partial last run)."""
+    n = (1 << 22) + 4 * 1000
+    gen = W.rng(0, 9, n)
+    host = [gen.standard_normal(n).astype(np.float32) for _ in range(4)]
+    dev = [torch.from_numpy(h).cuda() for h in host]
+    st = L.ou__stream_probe(*(d.data_ptr() for d in dev), n, H.stream_handle())
+    assert st == 0, H.last_error(L)
+    torch.cuda.synchronize()
+    for h, d in zip(host, dev):
+        assert d.cpu().numpy().tobytes() == h.tobytes()
+
+
 # ----------------------------------------------------------------- sentinel
 
 def test_public_path_ademamix_fp16_n64_first_update(orc, L):
