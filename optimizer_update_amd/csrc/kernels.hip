@@ -745,7 +745,25 @@ k_stream_probe(float* __restrict__ p, const float* __restrict__ g, float* __rest
     }
 }
 
+// The storage rounding of the update kernels (S::narrow of elem.hpp) on n
+// binary32 values, for testing it on every bit pattern (test hook).
+template <typename S>
+__global__ void __launch_bounds__(256)
+k_narrow(const float* __restrict__ in, typename S::raw* __restrict__ out, int64_t n)
+{
+    const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
+    for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < n; i += stride)
+        out[i] = S::narrow(in[i]);
+}
+
 }  // namespace
+
+const void* narrow_kernel(int dtype)
+{
+    if (dtype == 1) return reinterpret_cast<const void*>(&k_narrow<F16>);
+    if (dtype == 2) return reinterpret_cast<const void*>(&k_narrow<BF16>);
+    return nullptr;
+}
 
 const void* stream_probe_kernel(int unroll)
 {

@@ -36,6 +36,10 @@ void ou__force_multi(int waves, int epl, int unroll, int chunk, int lds);
 // Process-wide.
 void ou__force_xcd(int run);
 
+// The update kernels' rounding of binary32 to the storage dtype (OU_F16 or
+// OU_BF16) on n values: out[i] = narrow(in[i]).  Asynchronous on `stream`.
+int ou__narrow(int dtype, const float* in, uint16_t* out, int64_t n, void* stream);
+
 // Bandwidth probe: the traffic of the plain fp32 Adam update of n elements
 // (p, g, s1, s2 read; p, s1, s2 written back unchanged) in the same launch
 // shape, with no arithmetic; n a multiple of 4, buffers 16-byte aligned.

@@ -1,0 +1,41 @@
+"""GPU: the update kernels' storage rounding (elem.hpp's narrow, through the
+ou__narrow test hook) on every binary32 bit pattern, against the oracle.
+
+The oracle's conversions are themselves checked on every pattern against
+the x86 F16C conversion and an exact-midpoint bfloat16 rule
+(tests/native/conv_check.c)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from tests import gpu_helpers as H
+
+pytestmark = pytest.mark.gpu
+
+
+def _nan16(h: np.ndarray, exp_mask: int, man_mask: int) -> np.ndarray:
+    return ((h & exp_mask) == exp_mask) & ((h & man_mask) != 0)
+
+
+def test_kernel_rounding_exhaustive():
+    """All 2^32 patterns in 16 chunks of 2^28: binary16 and bfloat16 codes
+    equal the oracle's bitwise; a NaN gives a NaN (payloads are not part of
+    the contract)."""
+    assert torch.cuda.is_available(), "GPU tests need a HIP device"
+    L = H.lib()
+    orc = O.load()
+    chunk = 1 << 28
+    out = torch.empty(chunk, dtype=torch.int16, device="cuda")
+    for lo in range(-(1 << 31), 1 << 31, chunk):
+        x_dev = torch.arange(lo, lo + chunk, dtype=torch.int32, device="cuda").view(torch.float32)
+        x = np.arange(lo, lo + chunk, dtype=np.int32).view(np.float32)
+        nan = np.isnan(x)
+        for dtype, exp_mask, man_mask in ((O.F16, 0x7c00, 0x03ff), (O.BF16, 0x7f80, 0x007f)):
+            st = L.ou__narrow(dtype, x_dev.data_ptr(), out.data_ptr(), chunk, H.stream_handle())
+            assert st == 0, H.last_error(L)
+            got = out.cpu().numpy().view(np.uint16)
+            want = orc.f32_to_storage(x, dtype)
+            same = (got == want) | (nan & _nan16(got, exp_mask, man_mask))
+            assert same.all(), (dtype, lo, int(np.argmin(same)), int((~same).sum()))
+        del x_dev

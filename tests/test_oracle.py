@@ -33,6 +33,21 @@ def test_conversion_strided_sweep(orc):
             P.check_conversions(orc, bits.astype(np.uint32))
 
 
+def test_conversion_exhaustive_native(tmp_path):
+    """Every binary32 bit pattern through the oracle's storage conversions
+    (tests/native/conv_check.c, built with oracle/oracle.c): binary16
+    against the x86 F16C conversion, bfloat16 against the nearer bfloat16
+    neighbour in exact binary64 arithmetic (ties to even)."""
+    import subprocess
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    exe = tmp_path / "conv_check"
+    subprocess.run(["gcc", "-O2", "-std=c11", "-ffp-contract=off", "-fopenmp", "-mf16c",
+                    os.path.join(root, "tests", "native", "conv_check.c"),
+                    os.path.join(root, "oracle", "oracle.c"), "-lm", "-o", str(exe)], check=True)
+    out = subprocess.run([str(exe)], capture_output=True, text=True, timeout=600)
+    assert out.returncode == 0 and out.stdout.startswith("ok"), out.stdout + out.stderr
+
+
 @pytest.mark.parametrize("plant", range(1, 29))
 def test_planted_mistake_is_caught(plant, tmp_path):
     """A copy of the oracle with one planted mistake (dropped bias
