@@ -136,7 +136,9 @@ def pin_first_step_by_hand(orc):
     v^ = 7.80625e-5 / 0.001999, p2 = p1 (1 - 1e-5) - 1e-3 m^ / (sqrt(v^) + 1e-8)
     = 0.4987236...  The binary32 values must agree to binary32 precision
     (the decimal hyperparameters are not exact in binary32, which moves
-    1 - b2 by 1.3e-5 relative; the bound allows for that)."""
+    1 - b2 by 1.3e-5 relative; the bound allows for that), and bitwise to
+    the exact emulation of the binary32 operation sequence, for AdamW and
+    for AdEMAMix."""
     hp = O.HParams(lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.01)
     p = np.array([0.5], np.float32)
     s1 = np.zeros(1, np.float32)
@@ -153,6 +155,16 @@ def pin_first_step_by_hand(orc):
     assert abs(s1[0] - 0.01) <= 1e-8, s1[0]
     assert abs(s2[0] - 7.80625e-5) <= 7.80625e-5 * 2e-5, s2[0]
     assert abs(p[0] - p2) <= 1e-7, (p[0], p2)
+    # the same two steps, and AdEMAMix's (beta3 0.9999, alpha 5), bitwise
+    # against the exact-rational emulation of each rounded operation
+    # (p = 0x3eff7c46 then 0x3eff58b5 for AdamW, 0x3eff7c35 then 0x3eff589a
+    # for AdEMAMix)
+    hp2 = O.HParams(lr=1e-3, beta1=0.9, beta2=0.999, beta3=0.9999, alpha=5.0, eps=1e-8,
+                    weight_decay=0.01)
+    gsteps = [np.array([0.25], np.float32), np.array([-0.125], np.float32)]
+    for kind_name, kind in (("adam", O.ADAM), ("ademamix", O.ADEMAMIX)):
+        _emulate_and_compare(orc, kind_name, kind, "fp32", O.F32, np.array([0.5], np.float32),
+                             gsteps, hp2, 2)
 
 
 # ------------------------------------------------------------- library routine
