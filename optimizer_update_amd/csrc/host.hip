@@ -294,13 +294,15 @@ SingleLaunch select_single(const DeviceProps& d, int kind, int dtype, int64_t n,
     L.block = 256;
     L.unroll = 2;
     int run = kXcdRun;
-    // The plain fp32 Adam update (four fp32 streams in, three out): the same
-    // 2,048-element tile as 128 threads x 4 groups, in runs of 32 tiles per
-    // XCD -- 2.5-3 % faster at 2^28 on MI355X, measured on three boxes.  Not
+    // The plain fp32 Adam update of a large tensor (four fp32 streams in,
+    // three out; the grids that get the occupancy cap): the same 2,048-element
+    // tile as 128 threads x 4 groups, in runs of 32 tiles per XCD -- 2.5-3 %
+    // faster at 2^28 on MI355X, measured on three boxes.  Not
     // for the other kinds: with AdEMAMix's fifth stream four groups per lane
     // spill, and 16-bit storage runs 10 % slower in that shape; not for the
     // clip's parameter pass either (10 % slower).
-    if (plain && kind == OU_ADAM && dtype == OU_F32) {
+    const int64_t tiles = (units + 511) / 512;   // both shapes take 512 groups per block
+    if (plain && kind == OU_ADAM && dtype == OU_F32 && d.cu_count > 0 && tiles >= 8LL * d.cu_count) {
         L.block = 128;
         L.unroll = 4;
         run = 32;

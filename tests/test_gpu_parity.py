@@ -191,7 +191,8 @@ def test_launch_variants_bitwise(orc, L, kind, storage):
     variants = [(64, 4, 1, 0, 0, 0), (256, 8, 2, 0, 0, 0), (1024, 4, 4, 0, 0, 0),
                 (128, 8, 4, 3, 0, 0), (512, 4, 2, 1, 0, 0), (64, 8, 1, 7, 0, 0),
                 (256, 4, 2, 0, 1, 0), (1024, 8, 1, 2, 1, 0), (256, 4, 2, 0, 0, -1),
-                (256, 4, 2, 0, 0, 65536), (512, 4, 1, 0, 0, 98304)]
+                (256, 4, 2, 0, 0, 65536), (512, 4, 1, 0, 0, 98304),
+                (128, 4, 4, 0, 0, 0)]   # the large fp32 Adam shape
     for n in VARIANT_N:
         gen = W.rng(0, 6, n)
         p0 = W.params(n, storage, gen)
