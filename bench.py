@@ -347,10 +347,12 @@ def main():
 
 
 def bench_collection(torch, ou, W, dev, time_rounds):
-    """Model-like collection (bf16 AdamW): full step and small-tensor subset,
-    each as per-tensor loop, one plan launch, graph replay; the same
-    collection as AdamW8bit (min_8bit_size 4,096) and AdEMAMix32; the page's
-    direct cells; launch floor."""
+    """Model-like collection (bf16 AdamW): full step, the subsets of tensors
+    of <= 16,384 and <= 4,096 elements, each as per-tensor loop, one plan
+    launch, graph replay; the same collection as AdamW8bit (min_8bit_size
+    4,096) and AdEMAMix32; the page's direct cells; launch floors (a
+    one-element update through the binding, a bare one-element kernel, a
+    one-node graph replay)."""
     res = {}
     shapes = W.model_collection()
     gen = torch.Generator(device=dev)
@@ -364,7 +366,8 @@ def bench_collection(torch, ou, W, dev, time_rounds):
             gs.append((torch.randn(m, device=dev, generator=gen) * 0.01).to(torch.bfloat16))
         return ou.AdamW32(ps, lr=1e-3, weight_decay=0.01, grads=gs)
 
-    for label, subset in (("full_505", shapes), ("small_408", [s for s in shapes if W.numel(s[1]) <= 16384])):
+    for label, subset in (("full_505", shapes), ("small_408", [s for s in shapes if W.numel(s[1]) <= 16384]),
+                          ("le4096_216", [s for s in shapes if W.numel(s[1]) <= 4096])):
         opt = mk(subset)
         elems = sum(W.numel(s[1]) for s in subset)
         bytes_ = elems * W.bytes_per_element("adam", "bf16")
@@ -451,6 +454,26 @@ def bench_collection(torch, ou, W, dev, time_rounds):
         ou.optimizer_update_32bit("adam", one[0], one[1], one[2], one[3], step=t["i"], lr=1e-3)
     r = time_rounds(tiny, iters=200, rounds=7, warmup=50)
     res["launch_floor_1_element_us"] = round(r["median_ms"] * 1e3, 2)
+    # the floors under it: a one-element kernel launched straight through
+    # ctypes (the library's test hook that rounds one value to bf16), and the
+    # replay of a one-node graph (a plan over one one-element tensor)
+    one_in = torch.zeros(1, device=dev)
+    one_out = torch.zeros(1, dtype=torch.int16, device=dev)
+
+    def empty_launch():
+        lib.ou__narrow(2, one_in.data_ptr(), one_out.data_ptr(), 1, stream)
+    r = time_rounds(empty_launch, iters=200, rounds=7, warmup=50)
+    res["launch_floor_bare_kernel_us"] = round(r["median_ms"] * 1e3, 2)
+    plan1 = ou.Plan("adam", [tuple(one)])
+    hp1 = ou.HParams(lr=1e-3)
+    t1 = {"i": 0}
+
+    def graph1():
+        t1["i"] += 1
+        plan1.graph_step(hp1, t1["i"])
+    r = time_rounds(graph1, iters=100, rounds=7, warmup=20)
+    res["graph_floor_1_node_us"] = round(r["median_ms"] * 1e3, 2)
+    plan1.close()
     return res
 
 

@@ -22,6 +22,7 @@ two-state kinds and is None for the one-state kinds.
 from __future__ import annotations
 
 import ctypes
+import functools
 from dataclasses import dataclass
 
 import torch
@@ -55,9 +56,18 @@ class HParams:
     weight_decay: float = 0.0
     skip_zeros: bool = False
 
-    def c(self, step: int) -> _lib.ou_hparams:
+    @functools.cached_property
+    def _struct(self) -> _lib.ou_hparams:
         return _lib.ou_hparams(self.beta1, self.beta2, self.beta3, self.alpha, self.eps,
-                               self.weight_decay, self.lr, int(bool(self.skip_zeros)), int(step))
+                               self.weight_decay, self.lr, int(bool(self.skip_zeros)), 1)
+
+    def c(self, step: int) -> _lib.ou_hparams:
+        """The C struct for `step`.  The instance is frozen, so the struct is
+        built once and only its step is set; it is passed on at once (the
+        library copies what it needs), never kept."""
+        s = self._struct
+        s.step = int(step)
+        return s
 
 
 def _kind(kind, decay_after: bool = False) -> int:
@@ -74,18 +84,32 @@ def state_sizes(kind, n: int) -> tuple[int, int]:
     return (2 * n if k == _lib.OU_ADEMAMIX else n), (n if k in TWO_STATE else 0)
 
 
+_GET_RAW_STREAM = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+
+
 def _raw_stream(index: int) -> int:
     """Handle of the current stream of device `index` (torch's own accessor,
     falling back to the public one)."""
-    get = getattr(torch._C, "_cuda_getCurrentRawStream", None)
-    if get is not None:
-        return get(index)
+    if _GET_RAW_STREAM is not None:
+        return _GET_RAW_STREAM(index)
     return torch.cuda.current_stream(index).cuda_stream
+
+
+def _on(index: int, fn, *args):
+    """fn(*args) with device `index` current, switching only when it is not."""
+    prev = torch.cuda.current_device()
+    if prev == index:
+        return fn(*args)
+    torch.cuda.set_device(index)
+    try:
+        return fn(*args)
+    finally:
+        torch.cuda.set_device(prev)
 
 
 def _stream(t: torch.Tensor, stream) -> int:
     if stream is None:
-        return _raw_stream(t.device.index)
+        return _raw_stream(t.get_device())
     return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
 
 
@@ -132,8 +156,8 @@ def _tensor_args(kind: int, param, grad, state1, state2) -> tuple[int, int]:
     if grad.numel() != n or state1.numel() != s1 or (two and s2 != n):
         raise ValueError(f"sizes: param {n}, grad {grad.numel()}, state1 {state1.numel()} "
                          f"(want {s1}), state2 {s2} (want {n if two else 0})")
-    dev = param.device
-    if grad.device != dev or state1.device != dev or (two and state2.device != dev):
+    dev = param.get_device()
+    if grad.get_device() != dev or state1.get_device() != dev or (two and state2.get_device() != dev):
         raise ValueError("all tensors must be on one device")
     return n, dt
 
@@ -153,11 +177,9 @@ def optimizer_update_32bit(kind, param: torch.Tensor, grad: torch.Tensor, state1
     k = _kind(kind, decay_after)
     n, dt = _tensor_args(k, param, grad, state1, state2)
     lib = load()
-    with _on_device(param.device):
-        st = lib.optimizer_update_32bit(k, dt, param.data_ptr(), grad.data_ptr(),
-                                        state1.data_ptr(), _ptr(state2), n, beta1, beta2,
-                                        beta3, alpha, eps, weight_decay, int(step), lr,
-                                        int(bool(skip_zeros)), _stream(param, stream))
+    st = _on(param.get_device(), lib.optimizer_update_32bit, k, dt, param.data_ptr(),
+             grad.data_ptr(), state1.data_ptr(), _ptr(state2), n, beta1, beta2, beta3, alpha,
+             eps, weight_decay, int(step), lr, int(bool(skip_zeros)), _stream(param, stream))
     check(st, lib)
 
 
@@ -256,8 +278,8 @@ class Plan:
 
     def step(self, hp: HParams, step: int, stream=None) -> None:
         c = hp.c(step)
-        with _on_device(self.device):
-            check(self._lib.ou_plan_step(self._h, ctypes.byref(c), self._stream(stream)), self._lib)
+        check(_on(self.device.index, self._lib.ou_plan_step, self._h, ctypes.byref(c),
+                  self._stream(stream)), self._lib)
 
     def step_clip(self, hp: HParams, step: int, max_unorm: float, stream=None) -> None:
         """One step with update-norm clipping per tensor (``ou_plan_step_clip``)."""
@@ -397,8 +419,8 @@ class Plan8:
         c = hp.c(step)
         sh = (_raw_stream(self.device.index) if stream is None
               else (stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)))
-        with _on_device(self.device):
-            check(self._lib.ou_plan8_step(self._h, ctypes.byref(c), sh), self._lib)
+        check(_on(self.device.index, self._lib.ou_plan8_step, self._h, ctypes.byref(c), sh),
+              self._lib)
 
     def graph_step(self, hp: HParams, step: int, stream=None) -> None:
         """The same step replayed from a HIP graph (``ou_plan8_graph_step``)."""
