@@ -240,6 +240,11 @@ def main():
                      "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None},
         "host_wall_ms_per_step": round(wall_ms, 4),
         "kernel_sources_sha": kernel_sha(),
+        "env": {"torch": torch.__version__, "hip": getattr(torch.version, "hip", None),
+                "device": props.name, "arch": getattr(props, "gcnArchName", None),
+                "cu_count": props.multi_processor_count,
+                "hbm_bytes": props.total_memory, "l2_bytes": getattr(props, "L2_cache_size", None),
+                "kernel_sources_sha": kernel_sha(), "kernel8_sources_sha": kernel_sha(KERNEL8_SOURCES)},
     }
     if kind.endswith("8") and not clip:
         alu = alu_roofline(f"{kind[:-1]}_{storage}", n, ms)
