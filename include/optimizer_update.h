@@ -196,6 +196,13 @@ int ou_plan_graph_step(ou_plan plan, const ou_hparams* hp, void* stream);
  * ou_plan_step.  The plan holds the partial norms; capture-safe. */
 int ou_plan_step_clip(ou_plan plan, const ou_hparams* hp, float max_unorm, void* stream);
 
+/* The clipped step through a HIP graph of its own (a chain of the three
+ * launches per dtype group), built and instantiated on the first call, then
+ * replayed with this step's scalars and max_unorm written into its kernel
+ * nodes.  Bitwise identical to ou_plan_step_clip; max_unorm = 0 is
+ * ou_plan_graph_step.  Not allowed while `stream` is being captured. */
+int ou_plan_graph_step_clip(ou_plan plan, const ou_hparams* hp, float max_unorm, void* stream);
+
 /* Clip factors s of the last clipped step, in the order of the segments
  * given to ou_plan_create (1 for segments with n = 0 or before any clipped
  * step has run).  Synchronous copy to host memory; nseg must equal the

@@ -302,6 +302,13 @@ class Plan:
             check(self._lib.ou_plan_graph_step(self._h, ctypes.byref(c), self._stream(stream)),
                   self._lib)
 
+    def graph_step_clip(self, hp: HParams, step: int, max_unorm: float, stream=None) -> None:
+        """The clipped step through its HIP graph (``ou_plan_graph_step_clip``)."""
+        c = hp.c(step)
+        with _on_device(self.device):
+            check(self._lib.ou_plan_graph_step_clip(self._h, ctypes.byref(c), max_unorm,
+                                                    self._stream(stream)), self._lib)
+
     def describe(self) -> dict:
         g = ctypes.c_int32()
         w = ctypes.c_int64()

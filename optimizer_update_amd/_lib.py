@@ -93,6 +93,8 @@ def load(path: str = LIBRARY) -> ctypes.CDLL:
     lib.ou_plan_clip_factors.restype = i32
     lib.ou_plan_graph_step.argtypes = [vp, ctypes.POINTER(ou_hparams), vp]
     lib.ou_plan_graph_step.restype = i32
+    lib.ou_plan_graph_step_clip.argtypes = [vp, ctypes.POINTER(ou_hparams), f32, vp]
+    lib.ou_plan_graph_step_clip.restype = i32
     lib.ou_plan_describe.argtypes = [vp, ctypes.POINTER(ctypes.c_int32),
                                      ctypes.POINTER(i64), ctypes.POINTER(i64)]
     lib.ou_plan_describe.restype = i32

@@ -375,12 +375,18 @@ struct Group {
     const WorkItem* d_items;
     const void* fn;
     int64_t grid;
-    // graph replay
-    hipGraphNode_t node;
+    // graph replay: node of the plain step (0) and of the clipped step's
+    // three passes (1-3)
+    hipGraphNode_t node[4];
     // argument storage for launches and graph nodes
     StepScalars sc;
     int32_t chunk32;
     void* args[5];
+    float clip_mu, clip_lr;
+    const float* clip_seg_out;
+    void* clip_args1[4];
+    void* clip_args2[5];
+    void* clip_args3[6];
     // update-norm clipping: one item per (segment, 2048-element chunk),
     // binary64 partial sums per item, two floats (fl32(lr*s), s) per segment
     int64_t n_segs;
@@ -399,8 +405,10 @@ struct ou_plan_s {
     void* dmem = nullptr;
     std::vector<std::pair<int, int64_t>> seg_map;   // caller's index -> (group, slot), group -1 if n = 0
     std::vector<ou::Group> groups;
-    hipGraph_t graph = nullptr;
+    hipGraph_t graph = nullptr;            // plain step
     hipGraphExec_t exec = nullptr;
+    hipGraph_t clip_graph = nullptr;       // clipped step
+    hipGraphExec_t clip_exec = nullptr;
     int device = -1;
 };
 
@@ -562,6 +570,68 @@ void set_group_args(Group& g, const StepScalars& sc)
     g.args[4] = &g.sc;
 }
 
+// Arguments of the clipped step's three passes: (1) moments and partial
+// norms per (segment, chunk); (2) one block per segment forms the clip
+// factor s and fl32(lr * s); (3) the parameter step over the regular work
+// list.
+void set_clip_args(Group& g, const StepScalars& sc, float max_unorm)
+{
+    g.sc = sc;
+    g.clip_mu = max_unorm;
+    g.clip_lr = sc.lr;
+    g.clip_seg_out = g.d_seg_out;
+    g.clip_args1[0] = const_cast<SegDesc**>(&g.d_segs);
+    g.clip_args1[1] = const_cast<WorkItem**>(&g.d_clip_items);
+    g.clip_args1[2] = &g.sc;
+    g.clip_args1[3] = &g.d_partials;
+    g.clip_args2[0] = const_cast<SegDesc**>(&g.d_segs);
+    g.clip_args2[1] = &g.d_partials;
+    g.clip_args2[2] = &g.clip_mu;
+    g.clip_args2[3] = &g.clip_lr;
+    g.clip_args2[4] = &g.d_seg_out;
+    g.clip_args3[0] = const_cast<SegDesc**>(&g.d_segs);
+    g.clip_args3[1] = const_cast<WorkItem**>(&g.d_items);
+    g.clip_args3[2] = &g.n_items;
+    g.clip_args3[3] = &g.chunk32;
+    g.clip_args3[4] = &g.sc;
+    g.clip_args3[5] = const_cast<float**>(&g.clip_seg_out);
+}
+
+// Launch shape of one launch of a group's step (pass 0: the plain step;
+// passes 1-3: the clipped step), with the arguments set above.
+int group_launch(int kind, Group& g, int pass, hipKernelNodeParams* kp)
+{
+    *kp = hipKernelNodeParams{};
+    int64_t grid = g.grid;
+    int block = g.L.waves * kWave, lds = g.L.lds;
+    const void* fn = g.fn;
+    void** args = g.args;
+    if (pass == 1) {
+        fn = clip_kernel(11, kind, g.dtype, 0);
+        grid = g.n_clip_items;
+        block = kClipThreadsHost;
+        lds = 0;
+        args = g.clip_args1;
+    } else if (pass == 2) {
+        fn = clip_kernel(12, kind, g.dtype, 0);
+        grid = g.n_segs;
+        block = kClipFinalThreadsHost;
+        lds = 0;
+        args = g.clip_args2;
+    } else if (pass == 3) {
+        fn = clip_kernel(13, kind, g.dtype, 0);
+        args = g.clip_args3;
+    }
+    if (!fn) return fail(OU_EINVAL, "no kernel for pass %d, dtype %d", pass, g.dtype);
+    kp->func = const_cast<void*>(fn);
+    kp->gridDim = dim3(static_cast<unsigned>(grid));
+    kp->blockDim = dim3(static_cast<unsigned>(block));
+    kp->sharedMemBytes = static_cast<unsigned>(lds);
+    kp->kernelParams = args;
+    kp->extra = nullptr;
+    return OU_OK;
+}
+
 int plan_launch(ou_plan_s* plan, const StepScalars& sc, hipStream_t stream)
 {
     for (Group& g : plan->groups) {
@@ -572,31 +642,84 @@ int plan_launch(ou_plan_s* plan, const StepScalars& sc, hipStream_t stream)
     return OU_OK;
 }
 
-// The clipped step of a plan: three launches per dtype group (moments and
-// partial norms per (segment, chunk); one block per segment for the clip
-// factors; the parameter step over the regular work list).
+// The clipped step of a plan: three launches per dtype group.
 int plan_launch_clip(ou_plan_s* plan, const StepScalars& sc, float max_unorm, hipStream_t stream)
 {
     for (Group& g : plan->groups) {
-        const void* f1 = clip_kernel(11, plan->kind, g.dtype, 0);
-        const void* f2 = clip_kernel(12, plan->kind, g.dtype, 0);
-        const void* f3 = clip_kernel(13, plan->kind, g.dtype, 0);
-        if (!f1 || !f2 || !f3) return fail(OU_EINVAL, "no clip kernels for dtype %d", g.dtype);
-        StepScalars s = sc;
-        float mu = max_unorm, lr = sc.lr;
-        void* a1[] = {const_cast<SegDesc**>(&g.d_segs), const_cast<WorkItem**>(&g.d_clip_items), &s,
-                      &g.d_partials};
-        hipError_t e = launch(f1, g.n_clip_items, kClipThreadsHost, 0, a1, stream);
-        if (e != hipSuccess) return hip_fail(e, "launch clip pass 1 (collection)");
-        void* a2[] = {const_cast<SegDesc**>(&g.d_segs), &g.d_partials, &mu, &lr, &g.d_seg_out};
-        e = launch(f2, g.n_segs, kClipFinalThreadsHost, 0, a2, stream);
-        if (e != hipSuccess) return hip_fail(e, "launch clip pass 2 (collection)");
-        const float* seg_out = g.d_seg_out;
-        void* a3[] = {const_cast<SegDesc**>(&g.d_segs), const_cast<WorkItem**>(&g.d_items), &g.n_items,
-                      &g.chunk32, &s, const_cast<float**>(&seg_out)};
-        e = launch(f3, g.grid, g.L.waves * kWave, g.L.lds, a3, stream);
-        if (e != hipSuccess) return hip_fail(e, "launch clip pass 3 (collection)");
+        set_clip_args(g, sc, max_unorm);
+        for (int pass = 1; pass <= 3; ++pass) {
+            hipKernelNodeParams kp;
+            if (int st = group_launch(plan->kind, g, pass, &kp)) return st;
+            hipError_t e = hipLaunchKernel(kp.func, kp.gridDim, kp.blockDim, kp.kernelParams,
+                                           kp.sharedMemBytes, stream);
+            if (e != hipSuccess)
+                return fail(OU_EHIP, "launch clip pass %d (collection): %s", pass, hipGetErrorString(e));
+        }
     }
+    return OU_OK;
+}
+
+// A step through a HIP graph: the plain step (one node per dtype group) or
+// the clipped one (a chain of three nodes per group).  Built and
+// instantiated on the first call of its form; later calls write the step's
+// scalars into the nodes and replay.  Groups touch disjoint memory, so their
+// nodes (or chains) are independent.
+int plan_graph_launch(ou_plan_s* plan, const StepScalars& sc, float max_unorm, bool clipped,
+                      hipStream_t s)
+{
+    for (Group& g : plan->groups) {
+        if (clipped)
+            set_clip_args(g, sc, max_unorm);
+        else
+            set_group_args(g, sc);
+    }
+    hipGraph_t& graph = clipped ? plan->clip_graph : plan->graph;
+    hipGraphExec_t& exec = clipped ? plan->clip_exec : plan->exec;
+    const int first = clipped ? 1 : 0, last = clipped ? 3 : 0;
+    hipError_t e;
+    if (!exec) {
+        auto drop = [&graph]() {
+            (void)hipGraphDestroy(graph);
+            graph = nullptr;
+        };
+        e = hipGraphCreate(&graph, 0);
+        if (e != hipSuccess) {
+            graph = nullptr;
+            return hip_fail(e, "hipGraphCreate");
+        }
+        for (Group& g : plan->groups) {
+            hipGraphNode_t prev = nullptr;
+            for (int pass = first; pass <= last; ++pass) {
+                hipKernelNodeParams kp;
+                if (int st = group_launch(plan->kind, g, pass, &kp)) {
+                    drop();
+                    return st;
+                }
+                e = hipGraphAddKernelNode(&g.node[pass], graph, prev ? &prev : nullptr, prev ? 1 : 0, &kp);
+                if (e != hipSuccess) {
+                    drop();
+                    return hip_fail(e, "hipGraphAddKernelNode");
+                }
+                prev = g.node[pass];
+            }
+        }
+        e = hipGraphInstantiate(&exec, graph, nullptr, nullptr, 0);
+        if (e != hipSuccess) {
+            exec = nullptr;
+            drop();
+            return hip_fail(e, "hipGraphInstantiate");
+        }
+    } else {
+        for (Group& g : plan->groups)
+            for (int pass = first; pass <= last; ++pass) {
+                hipKernelNodeParams kp;
+                if (int st = group_launch(plan->kind, g, pass, &kp)) return st;
+                e = hipGraphExecKernelNodeSetParams(exec, g.node[pass], &kp);
+                if (e != hipSuccess) return hip_fail(e, "hipGraphExecKernelNodeSetParams");
+            }
+    }
+    e = hipGraphLaunch(exec, s);
+    if (e != hipSuccess) return hip_fail(e, "hipGraphLaunch");
     return OU_OK;
 }
 
@@ -829,46 +952,23 @@ int ou_plan_graph_step(ou_plan plan, const ou_hparams* hp, void* stream)
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (capturing(s)) return fail(OU_ECAPTURE, "ou_plan_graph_step inside a stream capture");
     if (plan->groups.empty()) return OU_OK;
-    const StepScalars sc = make_scalars(*hp, plan->decay_after);
-    hipError_t e;
-    if (!plan->exec) {
-        e = hipGraphCreate(&plan->graph, 0);
-        if (e != hipSuccess) return hip_fail(e, "hipGraphCreate");
-        for (Group& g : plan->groups) {
-            set_group_args(g, sc);
-            hipKernelNodeParams kp{};
-            kp.func = const_cast<void*>(g.fn);
-            kp.gridDim = dim3(static_cast<unsigned>(g.grid));
-            kp.blockDim = dim3(static_cast<unsigned>(g.L.waves * kWave));
-            kp.sharedMemBytes = static_cast<unsigned>(g.L.lds);
-            kp.kernelParams = g.args;
-            kp.extra = nullptr;
-            // groups touch disjoint memory: independent nodes
-            e = hipGraphAddKernelNode(&g.node, plan->graph, nullptr, 0, &kp);
-            if (e != hipSuccess) return hip_fail(e, "hipGraphAddKernelNode");
-        }
-        e = hipGraphInstantiate(&plan->exec, plan->graph, nullptr, nullptr, 0);
-        if (e != hipSuccess) {
-            plan->exec = nullptr;
-            return hip_fail(e, "hipGraphInstantiate");
-        }
-    } else {
-        for (Group& g : plan->groups) {
-            set_group_args(g, sc);
-            hipKernelNodeParams kp{};
-            kp.func = const_cast<void*>(g.fn);
-            kp.gridDim = dim3(static_cast<unsigned>(g.grid));
-            kp.blockDim = dim3(static_cast<unsigned>(g.L.waves * kWave));
-            kp.sharedMemBytes = static_cast<unsigned>(g.L.lds);
-            kp.kernelParams = g.args;
-            kp.extra = nullptr;
-            e = hipGraphExecKernelNodeSetParams(plan->exec, g.node, &kp);
-            if (e != hipSuccess) return hip_fail(e, "hipGraphExecKernelNodeSetParams");
-        }
-    }
-    e = hipGraphLaunch(plan->exec, s);
-    if (e != hipSuccess) return hip_fail(e, "hipGraphLaunch");
-    return OU_OK;
+    return plan_graph_launch(plan, make_scalars(*hp, plan->decay_after), 0.0f, false, s);
+}
+
+__attribute__((visibility("default")))
+int ou_plan_graph_step_clip(ou_plan plan, const ou_hparams* hp, float max_unorm, void* stream)
+{
+    if (!plan || !hp) return fail(OU_EINVAL, "null plan or hparams");
+    if (!std::isfinite(max_unorm) || max_unorm < 0.0f)
+        return fail(OU_EINVAL, "max_unorm must be finite and >= 0 (got %g)", max_unorm);
+    if (int st = check_hparams(plan->kind, *hp)) return st;
+    if (int st = check_plan_device(plan)) return st;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (capturing(s)) return fail(OU_ECAPTURE, "ou_plan_graph_step_clip inside a stream capture");
+    if (max_unorm > 0.0f && !two_state(plan->kind))
+        return fail(OU_EINVAL, "update-norm clipping is defined for ADAM and ADEMAMIX only");
+    if (plan->groups.empty()) return OU_OK;
+    return plan_graph_launch(plan, make_scalars(*hp, plan->decay_after), max_unorm, max_unorm > 0.0f, s);
 }
 
 __attribute__((visibility("default")))
@@ -889,6 +989,8 @@ void ou_plan_destroy(ou_plan plan)
     if (!plan) return;
     if (plan->exec) (void)hipGraphExecDestroy(plan->exec);
     if (plan->graph) (void)hipGraphDestroy(plan->graph);
+    if (plan->clip_exec) (void)hipGraphExecDestroy(plan->clip_exec);
+    if (plan->clip_graph) (void)hipGraphDestroy(plan->clip_graph);
     if (plan->dmem) (void)hipFree(plan->dmem);
     delete plan;
 }

@@ -66,13 +66,11 @@ class _Collection:
     @torch.no_grad()
     def step(self, graph: bool = False, stream=None) -> None:
         """One step of the whole collection: plan launch, or graph replay.
-        With max_unorm > 0 every tensor's update is clipped by its own norms
-        (plan path only)."""
-        if graph and self.max_unorm > 0:
-            raise ValueError("update-norm clipping runs through the plan step, not graph replay")
+        With max_unorm > 0 every tensor's update is clipped by its own norms."""
         self.step_count += 1
         if self.max_unorm > 0:
-            self.plan.step_clip(self.hp, self.step_count, self.max_unorm, stream)
+            (self.plan.graph_step_clip if graph else self.plan.step_clip)(
+                self.hp, self.step_count, self.max_unorm, stream)
         elif graph:
             self.plan.graph_step(self.hp, self.step_count, stream)
         else:

@@ -36,6 +36,7 @@ def test_exports_every_header_function(L):
                           "ou_clip_workspace_bytes", "optimizer_update_32bit_clip",
                           "ou_plan_step_clip", "ou_plan_clip_factors",
                           "ou_plan_create", "ou_plan_step", "ou_plan_graph_step",
+                          "ou_plan_graph_step_clip",
                           "ou_plan_describe", "ou_plan_destroy", "ou_status_string",
                           "ou_last_error", "ou_8bit_qmap", "optimizer_update_8bit_blockwise",
                           "ou_plan8_create", "ou_plan8_step", "ou_plan8_graph_step",
@@ -185,6 +186,7 @@ def test_plan_and_multi_validation(L):
     assert L.ou_plan_graph_step(None, ctypes.byref(bad_hp), None) == OU_EINVAL
     assert L.ou_plan_describe(None, None, None, None) == OU_EINVAL
     assert L.ou_plan_step_clip(None, ctypes.byref(bad_hp), 1.0, None) == OU_EINVAL
+    assert L.ou_plan_graph_step_clip(None, ctypes.byref(bad_hp), 1.0, None) == OU_EINVAL
     assert L.ou_plan_clip_factors(None, None, 0) == OU_EINVAL
     L.ou_plan_destroy(None)
 

@@ -173,7 +173,9 @@ MIXED = [("fp32", 1000), ("bf16", 4096), ("fp16", 77), ("fp32", 1 << 16), ("bf16
 def test_plan_clip_equals_per_tensor_clip(kind):
     """A mixed-dtype collection: the plan's clipped step (per-tensor norms,
     three launches per dtype group) equals optimizer_update_32bit_clip on
-    each tensor bitwise, clip factors included, and matches the oracle."""
+    each tensor bitwise, clip factors included, and matches the oracle.  The
+    same steps replayed through the plan's clipped graph give the same bits;
+    the bound changes between steps, and one step is unclipped (bound 0)."""
     import optimizer_update_amd as ou
     orc = O.load()
     hp = O.HParams(lr=1e-2, weight_decay=0.01, skip_zeros=True)
@@ -188,16 +190,18 @@ def test_plan_clip_equals_per_tensor_clip(kind):
         return [(H.to_dev(p0, s), torch.empty(p0.size, dtype=W.STORAGE_TORCH[s], device="cuda"),
                  torch.zeros(k * p0.size, device="cuda"), torch.zeros(p0.size, device="cuda"))
                 for s, p0, _ in host]
-    a, b = dev(), dev()
+    a, b, c = dev(), dev(), dev()
     plan = ou.Plan(kind, a)
+    gplan = ou.Plan(kind, c)
     ws = ou.clip_workspace(max(p0.size for _, p0, _ in host), "cuda")
-    bound = 0.3
+    bounds = [0.3, 0.0, 0.5, 0.3]
     last_b = []
-    for t in range(1, 5):
-        for (s, _, gs), x, y in zip(host, a, b):
-            x[1].copy_(W.to_torch(gs[t - 1], s, "cuda"))
-            y[1].copy_(W.to_torch(gs[t - 1], s, "cuda"))
+    for t, bound in enumerate(bounds, start=1):
+        for (s, _, gs), x, y, z in zip(host, a, b, c):
+            for w in (x, y, z):
+                w[1].copy_(W.to_torch(gs[t - 1], s, "cuda"))
         plan.step_clip(php, t, bound)
+        gplan.graph_step_clip(php, t, bound)
         last_b = []
         for (s, _, _), y in zip(host, b):
             ou.optimizer_update_32bit_clip(kind, *y, step=t, lr=hp.lr, weight_decay=hp.weight_decay,
@@ -206,22 +210,26 @@ def test_plan_clip_equals_per_tensor_clip(kind):
     torch.cuda.synchronize()
     fa = plan.clip_factors()
     assert fa == last_b, (fa, last_b)
+    assert gplan.clip_factors() == fa
     assert min(fa) < 1.0
-    for i, ((s, p0, gs), x, y) in enumerate(zip(host, a, b)):
+    for i, ((s, p0, gs), x, y, z) in enumerate(zip(host, a, b, c)):
         for j in (0, 2, 3):
             assert W.from_torch(x[j]).tobytes() == W.from_torch(y[j]).tobytes(), (kind, i, j)
+            assert W.from_torch(z[j]).tobytes() == W.from_torch(x[j]).tobytes(), (kind, i, j, "graph")
         pr = p0.copy()
         s1r, s2r = W.zero_states(p0.size, kind)
-        for t in range(1, 5):
+        for t, bound in enumerate(bounds, start=1):
             orc.update_f32_clip(H.KIND[kind], H.DT[s], pr, gs[t - 1], s1r, s2r, hp, t, bound)
         H.assert_parity(W.from_torch(x[0]), pr, s, f"p {i}", bitwise=False)
         H.assert_parity(W.from_torch(x[2]), s1r, "fp32", f"s1 {i}")
         H.assert_parity(W.from_torch(x[3]), s2r, "fp32", f"s2 {i}")
     plan.close()
+    gplan.close()
 
 
 def test_collection_optimizer_clip_plan_equals_per_tensor():
-    """AdEMAMix32(max_unorm=...): plan steps and per-tensor steps agree bitwise."""
+    """AdEMAMix32(max_unorm=...): plan steps, graph replays and per-tensor
+    steps agree bitwise."""
     import optimizer_update_amd as ou
     gen = W.rng(0, 16, 0)
     sizes = [1024, 4096, 16384, 1 << 20, 33]
@@ -229,18 +237,21 @@ def test_collection_optimizer_clip_plan_equals_per_tensor():
     gs = [W.grads(n, "normal", "bf16", gen, sigma=0.01) for n in sizes]
     mk = lambda: ou.AdEMAMix32([H.to_dev(p, "bf16") for p in ps], lr=1e-3, weight_decay=0.01,
                                grads=[H.to_dev(g, "bf16") for g in gs], max_unorm=1e-3)
-    x, y = mk(), mk()
+    x, y, z = mk(), mk(), mk()
     for _ in range(5):
         x.step()
         y.step_per_tensor()
+        z.step(graph=True)
     torch.cuda.synchronize()
-    for u, v in zip(x.params + x.state1 + x.state2, y.params + y.state1 + y.state2):
+    for u, v, w in zip(x.params + x.state1 + x.state2, y.params + y.state1 + y.state2,
+                       z.params + z.state1 + z.state2):
         assert W.from_torch(u).tobytes() == W.from_torch(v).tobytes()
+        assert W.from_torch(w).tobytes() == W.from_torch(u).tobytes()
     assert min(x.plan.clip_factors()) < 1.0
-    with pytest.raises(ValueError):
-        x.step(graph=True)
+    assert z.plan.clip_factors() == x.plan.clip_factors()
     x.close()
     y.close()
+    z.close()
 
 
 @pytest.mark.parametrize("kind", ["adam", "ademamix"])
