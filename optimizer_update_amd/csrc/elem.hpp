@@ -12,7 +12,8 @@
 // default lowering for gfx950) and denormals preserved, so each line is one
 // IEEE operation rounded to nearest even.  The two divisions by the bias
 // corrections take a cheaper route to the same correctly rounded quotient
-// (div_step_constant, stepdiv.hpp).
+// (div_step_constant, stepdiv.hpp); the 8-bit kernels take the square root
+// by a shorter form of the same correctly rounded sequence (sqrt_rn).
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -59,15 +60,39 @@ __device__ __forceinline__ void update_moments(float g, float& m, float& v, floa
     if constexpr (KIND == kAdemamix) m2 = s.beta3 * m2 + s.omb3 * g;
 }
 
+// Square root, correctly rounded.  The hardware root is within one ulp; of
+// it and its two neighbours, the signs of the exact residuals x - r'*r
+// (fused multiply-adds) pick the rounded root.  For x >= 2^-96 (or +inf)
+// this is the compiler's own correctly rounded sequence without the two
+// steps that only other inputs need: rescaling a tiny x by 2^32 (and the
+// root by 2^-16), and passing +-0 and +inf through unchanged (the
+// residuals leave +inf in place).  A wave takes that short form when all
+// its active lanes qualify, otherwise the full sequence; the results are
+// the same bits either way.  The branch splits straight-line code, which
+// costs the memory-bound 32-bit kernels more than the instructions it
+// saves; the 8-bit kernels, bound by instruction issue, use it.
+__device__ __forceinline__ float sqrt_rn(float x)
+{
+    if (__builtin_amdgcn_ballot_w64(!(x >= 0x1p-96f)) != 0) return __builtin_sqrtf(x);
+    const float r = __builtin_amdgcn_sqrtf(x);
+    const uint32_t b = __builtin_bit_cast(uint32_t, r);
+    const float down = __builtin_bit_cast(float, b - 1u);
+    const float up = __builtin_bit_cast(float, b + 1u);
+    float s = r;
+    if (__builtin_fmaf(-down, r, x) <= 0.0f) s = down;
+    if (__builtin_fmaf(-up, r, x) > 0.0f) s = up;
+    return s;
+}
+
 // The update direction from the (new) moments: the parameter moves by
 // lr * direction.  Bias correction of m and v only; alpha mixes in the slow
-// EMA (not bias-corrected).
-template <int KIND>
+// EMA (not bias-corrected).  SHORT_ROOT: the square root by sqrt_rn.
+template <int KIND, bool SHORT_ROOT = false>
 __device__ __forceinline__ float direction(float m, float v, float m2, const StepScalars& s)
 {
     const float mh = div_step_constant(m, s.rbc1);   // m / bc1
     const float vh = div_step_constant(v, s.rbc2);   // v / bc2
-    const float den = __builtin_sqrtf(vh) + s.eps;
+    const float den = (SHORT_ROOT ? sqrt_rn(vh) : __builtin_sqrtf(vh)) + s.eps;
     float num = mh;
     if constexpr (KIND == kAdemamix) num = mh + s.alpha * m2;
     return num / den;
@@ -119,13 +144,13 @@ __device__ __forceinline__ float update_one_state(float p, float g, float& m, co
 // One element: moments, direction, parameter (two-state kinds), or the
 // one-state rule.  p is the widened parameter; returns the new parameter
 // before rounding to storage.
-template <int KIND>
+template <int KIND, bool SHORT_ROOT = false>
 __device__ __forceinline__ float update_element(float p, float g, float& m, float& v,
                                                 float& m2, const StepScalars& s)
 {
     if constexpr (kTwoState<KIND>) {
         update_moments<KIND>(g, m, v, m2, s);
-        return step_param(p, direction<KIND>(m, v, m2, s), s.decay, s.lr, s.decay_after);
+        return step_param(p, direction<KIND, SHORT_ROOT>(m, v, m2, s), s.decay, s.lr, s.decay_after);
     } else {
         return update_one_state<KIND>(p, g, m, s);
     }

@@ -1082,6 +1082,24 @@ int ou__narrow(int dtype, const float* in, uint16_t* out, int64_t n, void* strea
 }
 
 __attribute__((visibility("default")))
+int ou__sqrt(const float* in, float* out, int64_t n, void* stream)
+{
+    if (!in || !out || n <= 0) return fail(OU_EINVAL, "sqrt: bad arguments");
+    if (reinterpret_cast<uintptr_t>(in) % 4 || reinterpret_cast<uintptr_t>(out) % 4)
+        return fail(OU_EALIGN, "sqrt: misaligned buffers");
+    if (validate_only()) return OU_OK;
+    const DeviceProps* dp = nullptr;
+    if (int st = g_devices.current(&dp)) return st;
+    const int64_t grid = std::max<int64_t>(1, std::min<int64_t>((n + 255) / 256, 1 << 20));
+    const float* a0 = in;
+    float* a1 = out;
+    void* args[] = {const_cast<float**>(&a0), &a1, &n};
+    hipError_t e = launch(sqrt_kernel(), grid, 256, 0, args, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "launch sqrt");
+    return OU_OK;
+}
+
+__attribute__((visibility("default")))
 int ou__stream_probe(float* p, const float* g, float* s1, float* s2, int64_t n, void* stream)
 {
     if (!p || !g || !s1 || !s2 || n <= 0 || n % 4) return fail(OU_EINVAL, "stream probe: bad arguments");

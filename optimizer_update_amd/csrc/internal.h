@@ -75,6 +75,9 @@ const void* stream_probe_kernel(int unroll);
 
 // The update kernels' storage rounding alone, dtype OU_F16 or OU_BF16 (test hook).
 const void* narrow_kernel(int dtype);
+
+// The update kernels' square root alone (test hook).
+const void* sqrt_kernel();
 constexpr int kClipChunkElems = 2048;   // elements per partial-norm chunk
 constexpr int kClipThreadsHost = 256;   // threads of pass 1
 constexpr int kClipFinalThreadsHost = 1024;   // threads of pass 2

@@ -756,7 +756,21 @@ k_narrow(const float* __restrict__ in, typename S::raw* __restrict__ out, int64_
         out[i] = S::narrow(in[i]);
 }
 
+// The 8-bit kernels' square root (sqrt_rn of elem.hpp) on n binary32
+// values, for testing it on every bit pattern (test hook).  Consecutive
+// values go to consecutive lanes, so a wave whose inputs are all >= 2^-96
+// takes sqrt_rn's short form.
+__global__ void __launch_bounds__(256)
+k_sqrt(const float* __restrict__ in, float* __restrict__ out, int64_t n)
+{
+    const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
+    for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < n; i += stride)
+        out[i] = sqrt_rn(in[i]);
+}
+
 }  // namespace
+
+const void* sqrt_kernel() { return reinterpret_cast<const void*>(&k_sqrt); }
 
 const void* narrow_kernel(int dtype)
 {

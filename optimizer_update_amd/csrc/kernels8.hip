@@ -10,9 +10,10 @@
 // One wave owns one block: lane l holds elements 4l .. 4l+3 (one dwordx4 of
 // an fp32 stream, dwordx2 of a 16-bit one, one dword of codes per state).
 // Per block: dequantize (code value x absmax), the 32-bit rule of elem.hpp
-// on the fp32 values, the block's new absmax by a wave max (exact, so the
-// order does not matter: DPP rotations inside each 16-lane row, then the
-// four row results), then each state is requantized: x = value *
+// on the fp32 values, the block's new absmax of every state by one wave
+// reduction (exact, so the order does not matter: the states are paired
+// across the wave's halves and rows by lane swaps, then DPP rotations
+// finish each 16-lane row), then each state is requantized: x = value *
 // fl32(1 / absmax), and the magnitude index of |x| comes from a key table
 // indexed by the top bits of x plus one decision point (qmap.hpp).  The
 // tables (10 KiB) are copied to LDS once per workgroup.  The parameter
@@ -106,21 +107,50 @@ __device__ __forceinline__ float lane_float(float x, int lane)
     return __builtin_bit_cast(float, lane_value(__builtin_bit_cast(uint32_t, x), lane));
 }
 
-// Largest of the lanes' values, each a non-negative binary32 that is not a
-// NaN (so that the order of the bit patterns as integers is the order of
-// the values); every lane must be active.  Rotations by 1, 2, 4, 8 leave
-// each 16-lane row's maximum in all its lanes; the four rows are then
-// combined on the scalar unit.
-__device__ __forceinline__ float wave_max(float x)
+// Maxima over the wave of two or three lane values, each a non-negative
+// binary32 that is not a NaN (so that the order of the bit patterns as
+// integers is the order of the values); every lane must be active.
+// v_permlane32_swap exchanges rows 2-3 of its first operand with rows 0-1
+// of its second, v_permlane16_swap the odd rows of the first with the even
+// rows of the second (rows of 16 lanes), so the maximum of each swapped
+// pair folds two halves, or two rows, of different states into one
+// register; rotations by 1, 2, 4, 8 then finish every row.
+__device__ __forceinline__ uint32_t max_swap32(uint32_t a, uint32_t b)
 {
-    uint32_t b = __builtin_bit_cast(uint32_t, x);
+    const auto s = __builtin_amdgcn_permlane32_swap(a, b, false, false);
+    return max(static_cast<uint32_t>(s[0]), static_cast<uint32_t>(s[1]));
+}
+
+__device__ __forceinline__ uint32_t max_swap16(uint32_t a, uint32_t b)
+{
+    const auto s = __builtin_amdgcn_permlane16_swap(a, b, false, false);
+    return max(static_cast<uint32_t>(s[0]), static_cast<uint32_t>(s[1]));
+}
+
+__device__ __forceinline__ uint32_t row_max(uint32_t b)
+{
     b = max(b, row_ror<1>(b));
     b = max(b, row_ror<2>(b));
     b = max(b, row_ror<4>(b));
-    b = max(b, row_ror<8>(b));
-    const uint32_t r = max(max(lane_value(b, 0), lane_value(b, 16)),
-                           max(lane_value(b, 32), lane_value(b, 48)));
-    return __builtin_bit_cast(float, r);
+    return max(b, row_ror<8>(b));
+}
+
+// Two states: lanes 0-31 get the maximum of x, lanes 32-63 that of y.
+__device__ __forceinline__ float wave_max2(float x, float y)
+{
+    uint32_t z = max_swap32(__builtin_bit_cast(uint32_t, x), __builtin_bit_cast(uint32_t, y));
+    z = max_swap16(z, z);   // rows 0-1: x over all lanes, rows 2-3: y
+    return __builtin_bit_cast(float, row_max(z));
+}
+
+// Three states: lanes 0-15 get the maximum of x, 16-31 and 48-63 that of w,
+// 32-47 that of y.
+__device__ __forceinline__ float wave_max3(float x, float y, float w)
+{
+    const uint32_t z = max_swap32(__builtin_bit_cast(uint32_t, x), __builtin_bit_cast(uint32_t, y));
+    const uint32_t ww = __builtin_bit_cast(uint32_t, w);
+    const uint32_t h = max_swap32(ww, ww);   // every row: w over two rows
+    return __builtin_bit_cast(float, row_max(max_swap16(z, h)));
 }
 
 // The inputs of one quantization block, as loaded by one wave: lane l
@@ -238,7 +268,7 @@ __device__ __forceinline__ void finish_block8(const Seg8& d, int64_t b, const QL
         }
         const float gj = S::widen(graw[j]);
         if (sc.skip_zeros && gj == 0.0f) continue;   // moments keep their values, p is not written
-        const float pn = update_element<KIND>(S::widen(praw[j]), gj, m[j], v[j], m2[j], sc);
+        const float pn = update_element<KIND, true>(S::widen(praw[j]), gj, m[j], v[j], m2[j], sc);
         praw[j] = S::narrow(pn);
     }
 
@@ -251,21 +281,21 @@ __device__ __forceinline__ void finish_block8(const Seg8& d, int64_t b, const QL
         l2 = __builtin_fmaxf(l2, __builtin_fabsf(v[j]));
         if constexpr (kMix) l3 = __builtin_fmaxf(l3, __builtin_fabsf(m2[j]));
     }
-    l1 = wave_max(l1);
-    l2 = wave_max(l2);
-    if constexpr (kMix) l3 = wave_max(l3);
+    // lane of each state's maximum in l
+    constexpr int kLane2 = 32, kLane3 = 16;
+    const float l = kMix ? wave_max3(l1, l2, l3) : wave_max2(l1, l2);
+    l1 = lane_float(l, 0);
+    l2 = lane_float(l, kLane2);
+    if constexpr (kMix) l3 = lane_float(l, kLane3);
 
     // requantize: x = value * fl32(1 / absmax).  With absmax = 0 every
     // value is +-0 or NaN, and r = 0 gives x = +-0 or NaN: code 0, as for
-    // the definition's x = 0.  The states' maxima are wave-uniform: one
-    // division serves them all (lanes 0-31 / 32-63, or thirds for three).
-    float l = (lane < (kMix ? 21 : 32)) ? l1 : l2;
-    if constexpr (kMix) l = (lane < 42) ? l : l3;
+    // the definition's x = 0.  One division serves all states.
     const float r = (l > 0.0f) ? 1.0f / l : 0.0f;
     const float r1 = lane_float(r, 0);
-    const float r2 = lane_float(r, kMix ? 21 : 32);
+    const float r2 = lane_float(r, kLane2);
     float r3 = 0.0f;
-    if constexpr (kMix) r3 = lane_float(r, 42);
+    if constexpr (kMix) r3 = lane_float(r, kLane3);
     uint32_t o1 = 0, o2 = 0, o3 = 0;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {

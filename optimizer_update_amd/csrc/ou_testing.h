@@ -40,6 +40,10 @@ void ou__force_xcd(int run);
 // OU_BF16) on n values: out[i] = narrow(in[i]).  Asynchronous on `stream`.
 int ou__narrow(int dtype, const float* in, uint16_t* out, int64_t n, void* stream);
 
+// The 8-bit update kernels' square root on n values: out[i] = sqrt(in[i]),
+// correctly rounded.  Asynchronous on `stream`.
+int ou__sqrt(const float* in, float* out, int64_t n, void* stream);
+
 // Bandwidth probe: the traffic of the plain fp32 Adam update of n elements
 // (p, g, s1, s2 read; p, s1, s2 written back unchanged) in the same launch
 // shape, with no arithmetic; n a multiple of 4, buffers 16-byte aligned.

@@ -50,7 +50,8 @@ def test_exports_every_header_function(L):
     # nothing else is exported besides the test hooks
     assert exported - set(names) == {"ou__select_single", "ou__force_single", "ou__force_multi",
                                      "ou__step_scalars", "ou__force_8bit", "ou__validate_only",
-                                     "ou__force_xcd", "ou__stream_probe", "ou__narrow"}
+                                     "ou__force_xcd", "ou__stream_probe", "ou__narrow",
+                                     "ou__sqrt"}
 
 
 def test_header_is_plain_c_and_matches_ctypes_layout(tmp_path):
@@ -417,3 +418,11 @@ def test_narrow_hook_validation(L):
     assert L.ou__narrow(1, 0x10000, 0x20000, 0, None) == OU_EINVAL
     assert L.ou__narrow(1, 0x10002, 0x20000, 16, None) == OU_EALIGN
     assert L.ou__narrow(2, 0x10000, 0x20001, 16, None) == OU_EALIGN
+
+
+def test_sqrt_hook_validation(L):
+    """The square-root hook's argument checks (test hook)."""
+    assert L.ou__sqrt(0x10000, 0x20000, 16, None) == OU_OK
+    assert L.ou__sqrt(0x10000, 0x20000, 0, None) == OU_EINVAL
+    assert L.ou__sqrt(0, 0x20000, 16, None) == OU_EINVAL
+    assert L.ou__sqrt(0x10002, 0x20000, 16, None) == OU_EALIGN

@@ -39,3 +39,23 @@ def test_kernel_rounding_exhaustive():
             same = (got == want) | (nan & _nan16(got, exp_mask, man_mask))
             assert same.all(), (dtype, lo, int(np.argmin(same)), int((~same).sum()))
         del x_dev
+
+
+def test_kernel_sqrt_exhaustive():
+    """The 8-bit update kernels' square root (short form for waves whose inputs
+    are all >= 2^-96, the full sequence otherwise) on all 2^32 patterns, in
+    16 chunks of 2^28: bitwise equal to numpy's IEEE binary32 square root; a
+    NaN (every negative input included) gives a NaN."""
+    assert torch.cuda.is_available(), "GPU tests need a HIP device"
+    L = H.lib()
+    chunk = 1 << 28
+    out = torch.empty(chunk, dtype=torch.float32, device="cuda")
+    with np.errstate(invalid="ignore"):
+        for lo in range(-(1 << 31), 1 << 31, chunk):
+            x_dev = torch.arange(lo, lo + chunk, dtype=torch.int32, device="cuda").view(torch.float32)
+            st = L.ou__sqrt(x_dev.data_ptr(), out.data_ptr(), chunk, H.stream_handle())
+            assert st == 0, H.last_error(L)
+            got = out.cpu().numpy()
+            want = np.sqrt(np.arange(lo, lo + chunk, dtype=np.int32).view(np.float32))
+            same = (got.view(np.uint32) == want.view(np.uint32)) | (np.isnan(got) & np.isnan(want))
+            assert same.all(), (lo, int(np.argmin(same)), int((~same).sum()))
