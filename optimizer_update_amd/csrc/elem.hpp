@@ -159,7 +159,9 @@ __device__ __forceinline__ float update_element(float p, float g, float& m, floa
 // ---- storage types ---------------------------------------------------------
 // Storage<T> widens to binary32 exactly and narrows with round to nearest,
 // ties to even (gfx950 conversion instructions: v_cvt_f16_f32 under the
-// default round-to-nearest mode, v_cvt_pk_bf16_f32 for bfloat16).
+// default round-to-nearest mode, v_cvt_pk_bf16_f32 for bfloat16).  The
+// 16-bit types also narrow two values into one packed word (narrow2: the
+// first in the low half), one v_cvt_pk_f16_f32 / v_cvt_pk_bf16_f32.
 struct F32 {
     using raw = float;
     static constexpr int bytes = 4;
@@ -167,9 +169,12 @@ struct F32 {
     __device__ __forceinline__ static raw narrow(float x) { return x; }
 };
 
+using f32x2 = float __attribute__((ext_vector_type(2)));
+
 struct F16 {
     using raw = uint16_t;
     static constexpr int bytes = 2;
+    using pair = _Float16 __attribute__((ext_vector_type(2)));
     __device__ __forceinline__ static float widen(raw x)
     {
         return static_cast<float>(__builtin_bit_cast(_Float16, x));
@@ -178,11 +183,16 @@ struct F16 {
     {
         return __builtin_bit_cast(uint16_t, static_cast<_Float16>(x));
     }
+    __device__ __forceinline__ static uint32_t narrow2(float a, float b)
+    {
+        return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, pair));
+    }
 };
 
 struct BF16 {
     using raw = uint16_t;
     static constexpr int bytes = 2;
+    using pair = __bf16 __attribute__((ext_vector_type(2)));
     __device__ __forceinline__ static float widen(raw x)
     {
         return __builtin_bit_cast(float, static_cast<uint32_t>(x) << 16);
@@ -190,6 +200,10 @@ struct BF16 {
     __device__ __forceinline__ static raw narrow(float x)
     {
         return __builtin_bit_cast(uint16_t, static_cast<__bf16>(x));
+    }
+    __device__ __forceinline__ static uint32_t narrow2(float a, float b)
+    {
+        return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, pair));
     }
 };
 

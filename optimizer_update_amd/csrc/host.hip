@@ -1065,17 +1065,19 @@ void ou__force_xcd(int run) { g_force_xcd = run; }
 __attribute__((visibility("default")))
 int ou__narrow(int dtype, const float* in, uint16_t* out, int64_t n, void* stream)
 {
-    const void* fn = narrow_kernel(dtype);
-    if (!fn || !in || !out || n <= 0) return fail(OU_EINVAL, "narrow: bad arguments");
-    if (reinterpret_cast<uintptr_t>(in) % 4 || reinterpret_cast<uintptr_t>(out) % 2)
+    const bool pairs = dtype >= 16;
+    const void* fn = narrow_kernel(pairs ? dtype - 16 : dtype, pairs);
+    if (!fn || !in || !out || n <= 0 || (pairs && n % 2)) return fail(OU_EINVAL, "narrow: bad arguments");
+    if (reinterpret_cast<uintptr_t>(in) % 4 || reinterpret_cast<uintptr_t>(out) % (pairs ? 4 : 2))
         return fail(OU_EALIGN, "narrow: misaligned buffers");
     if (validate_only()) return OU_OK;
     const DeviceProps* dp = nullptr;
     if (int st = g_devices.current(&dp)) return st;
-    const int64_t grid = std::max<int64_t>(1, std::min<int64_t>((n + 255) / 256, 1 << 20));
+    int64_t count = pairs ? n / 2 : n;
+    const int64_t grid = std::max<int64_t>(1, std::min<int64_t>((count + 255) / 256, 1 << 20));
     const float* a0 = in;
     uint16_t* a1 = out;
-    void* args[] = {const_cast<float**>(&a0), &a1, &n};
+    void* args[] = {const_cast<float**>(&a0), &a1, &count};
     hipError_t e = launch(fn, grid, 256, 0, args, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail(e, "launch narrow");
     return OU_OK;

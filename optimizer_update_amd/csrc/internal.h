@@ -73,8 +73,9 @@ const void* clip_kernel(int pass, int kind, int dtype, int unroll);
 // Bandwidth probe with the plain fp32 Adam update's traffic (test hook).
 const void* stream_probe_kernel(int unroll);
 
-// The update kernels' storage rounding alone, dtype OU_F16 or OU_BF16 (test hook).
-const void* narrow_kernel(int dtype);
+// The update kernels' storage rounding alone, dtype OU_F16 or OU_BF16, one
+// value at a time or by packed pairs (test hook).
+const void* narrow_kernel(int dtype, bool pairs);
 
 // The update kernels' square root alone (test hook).
 const void* sqrt_kernel();

@@ -756,6 +756,17 @@ k_narrow(const float* __restrict__ in, typename S::raw* __restrict__ out, int64_
         out[i] = S::narrow(in[i]);
 }
 
+// The same by pairs (S::narrow2, the 8-bit kernels' packed form): n even,
+// out 4-byte aligned.
+template <typename S>
+__global__ void __launch_bounds__(256)
+k_narrow2(const float* __restrict__ in, uint32_t* __restrict__ out, int64_t npairs)
+{
+    const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
+    for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < npairs; i += stride)
+        out[i] = S::narrow2(in[2 * i], in[2 * i + 1]);
+}
+
 // The 8-bit kernels' square root (sqrt_rn of elem.hpp) on n binary32
 // values, for testing it on every bit pattern (test hook).  Consecutive
 // values go to consecutive lanes, so a wave whose inputs are all >= 2^-96
@@ -772,10 +783,12 @@ k_sqrt(const float* __restrict__ in, float* __restrict__ out, int64_t n)
 
 const void* sqrt_kernel() { return reinterpret_cast<const void*>(&k_sqrt); }
 
-const void* narrow_kernel(int dtype)
+const void* narrow_kernel(int dtype, bool pairs)
 {
-    if (dtype == 1) return reinterpret_cast<const void*>(&k_narrow<F16>);
-    if (dtype == 2) return reinterpret_cast<const void*>(&k_narrow<BF16>);
+    if (dtype == 1) return pairs ? reinterpret_cast<const void*>(&k_narrow2<F16>)
+                                 : reinterpret_cast<const void*>(&k_narrow<F16>);
+    if (dtype == 2) return pairs ? reinterpret_cast<const void*>(&k_narrow2<BF16>)
+                                 : reinterpret_cast<const void*>(&k_narrow<BF16>);
     return nullptr;
 }
 

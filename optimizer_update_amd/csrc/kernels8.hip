@@ -252,24 +252,37 @@ __device__ __forceinline__ void finish_block8(const Seg8& d, int64_t b, const QL
     const raw* graw = in.graw;
     const bool* live = in.live;
 
-    // dequantize and update
-    float m[4], v[4], m2[4];
+    // dequantize and update.  A dense block (whole, no skipped elements:
+    // wave-uniform) updates every element with no per-element branch, and
+    // with 16-bit storage narrows its new parameters in pairs at the store.
+    const bool dense = full && !sc.skip_zeros;
+    float m[4], v[4], m2[4], pn[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
         m[j] = deq_signed(T, (w1 >> (8 * j)) & 0xffu) * A1;
         v[j] = T.t.umag[(w2 >> (8 * j)) & 0xffu] * A2;
         m2[j] = 0.0f;
         if constexpr (kMix) m2[j] = deq_signed(T, (w3 >> (8 * j)) & 0xffu) * A3;
-        if (!WIDE && !live[j]) {
-            m[j] = 0.0f;
-            v[j] = 0.0f;
-            m2[j] = 0.0f;
-            continue;
+    }
+    if (dense) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            pn[j] = update_element<KIND, true>(S::widen(praw[j]), S::widen(graw[j]), m[j], v[j], m2[j], sc);
+            if constexpr (S::bytes == 4) praw[j] = pn[j];
         }
-        const float gj = S::widen(graw[j]);
-        if (sc.skip_zeros && gj == 0.0f) continue;   // moments keep their values, p is not written
-        const float pn = update_element<KIND, true>(S::widen(praw[j]), gj, m[j], v[j], m2[j], sc);
-        praw[j] = S::narrow(pn);
+    } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            if (!WIDE && !live[j]) {
+                m[j] = 0.0f;
+                v[j] = 0.0f;
+                m2[j] = 0.0f;
+                continue;
+            }
+            const float gj = S::widen(graw[j]);
+            if (sc.skip_zeros && gj == 0.0f) continue;   // moments keep their values, p is not written
+            praw[j] = S::narrow(update_element<KIND, true>(S::widen(praw[j]), gj, m[j], v[j], m2[j], sc));
+        }
     }
 
     // new absmax of each state (maxNum from 0: a NaN is passed over, so
@@ -311,7 +324,9 @@ __device__ __forceinline__ void finish_block8(const Seg8& d, int64_t b, const QL
                               __builtin_bit_cast(uint32_t, praw[2]), __builtin_bit_cast(uint32_t, praw[3])};
             __builtin_nontemporal_store(xp, reinterpret_cast<u32x4*>(p + e0));
         } else {
-            const u32x2 xp = {static_cast<uint32_t>(praw[0]) | (static_cast<uint32_t>(praw[1]) << 16),
+            const u32x2 xp =
+                dense ? u32x2{S::narrow2(pn[0], pn[1]), S::narrow2(pn[2], pn[3])}
+                      : u32x2{static_cast<uint32_t>(praw[0]) | (static_cast<uint32_t>(praw[1]) << 16),
                               static_cast<uint32_t>(praw[2]) | (static_cast<uint32_t>(praw[3]) << 16)};
             __builtin_nontemporal_store(xp, reinterpret_cast<u32x2*>(p + e0));
         }

@@ -37,7 +37,9 @@ void ou__force_multi(int waves, int epl, int unroll, int chunk, int lds);
 void ou__force_xcd(int run);
 
 // The update kernels' rounding of binary32 to the storage dtype (OU_F16 or
-// OU_BF16) on n values: out[i] = narrow(in[i]).  Asynchronous on `stream`.
+// OU_BF16) on n values: out[i] = narrow(in[i]).  dtype + 16 takes the packed
+// form of the 8-bit kernels, two values per conversion (n even, out 4-byte
+// aligned).  Asynchronous on `stream`.
 int ou__narrow(int dtype, const float* in, uint16_t* out, int64_t n, void* stream);
 
 // The 8-bit update kernels' square root on n values: out[i] = sqrt(in[i]),

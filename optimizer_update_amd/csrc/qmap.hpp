@@ -81,14 +81,16 @@ inline constexpr QTables kQTablesHost = make_qtables();
 // #{k : bound[k] < a}.  The binary32 pattern of a, shifted right by 16 (sign,
 // exponent, top 7 mantissa bits), names a bucket [s, s') of width at most
 // 2^-7 of its binade; for a in [2^-27, 2) the key is that number, and
-// smaller or larger a clamp to the first or last key (kQKeyBase and
-// kQKeyBase + kQKeys - 1).  A bucket never holds more than one decision
-// point, so with est = the index of the bucket's start s (the key table's
-// entry key - kQKeyBase), the index of any a in the bucket is
-// est + (bound[est] < a).  Below 2^-27 every a has index 0; a >= 2
-// (infinity, after a reciprocal that overflowed) takes the largest index,
-// where the +inf sentinel stops the count.  The test suite checks the
-// composition below against the definition for every binary32 input.
+// larger a clamp to the last key (kQKeyBase + kQKeys - 1).  A bucket never
+// holds more than one decision point, so with est = the index of the
+// bucket's start s (the key table's entry key - kQKeyBase), the index of any
+// a in the bucket is est + (bound[est] < a).  Every magnitude below 2^-27
+// has index 0 (both types' first decision points lie above 2^-26), so the
+// quantizer raises smaller magnitudes to 2^-27 (qmagnitude), which changes
+// no index and keeps every key at or above kQKeyBase; a >= 2 (infinity,
+// after a reciprocal that overflowed) takes the largest index, where the
+// +inf sentinel stops the count.  The test suite checks the composition
+// below against the definition for every binary32 input.
 constexpr int kQKeyBase = 100 << 7;   // bits >> 16 of 2^-27
 constexpr int kQKeys = 28 << 7;       // binades 2^-27 .. 2^0
 
@@ -120,19 +122,23 @@ constexpr QKeys make_qkeys(const QTables& t)
 
 inline constexpr QKeys kQKeysHost = make_qkeys(kQTablesHost);
 
-// The magnitude the quantizer classifies: |x|, with NaN mapped to 0 (maxNum
-// returns the number when one operand is a quiet NaN), so a NaN takes index
-// 0.  x is a product (a state times its block's reciprocal), never a
-// signaling NaN.
-constexpr float qmagnitude(float x) { return __builtin_fmaxf(__builtin_fabsf(x), 0.0f); }
+// The magnitude the quantizer classifies: |x| raised to at least 2^-27,
+// with NaN mapped to 2^-27 (maxNum returns the number when one operand is a
+// quiet NaN), so a NaN takes index 0.  x is a product (a state times its
+// block's reciprocal), never a signaling NaN.
+constexpr float kQFloor = 0x1p-27f;
+static_assert(__builtin_bit_cast(uint32_t, kQFloor) >> 16 == kQKeyBase, "floor is the first key");
+static_assert(kQTablesHost.sbound[0] > 0x1p-26f && kQTablesHost.ubound[0] > 0x1p-26f,
+              "magnitudes below 2^-26 have index 0");
+constexpr float qmagnitude(float x) { return __builtin_fmaxf(__builtin_fabsf(x), kQFloor); }
 
-// Key of a = qmagnitude(x): bits >> 16 clamped to
-// [kQKeyBase, kQKeyBase + kQKeys - 1].
+// Key of a = qmagnitude(x) (so a >= 2^-27): bits >> 16, at most
+// kQKeyBase + kQKeys - 1.
 constexpr uint32_t qkey(float a)
 {
     const uint32_t k = __builtin_bit_cast(uint32_t, a) >> 16;
-    constexpr uint32_t lo = kQKeyBase, hi = kQKeyBase + kQKeys - 1;
-    return k < lo ? lo : (k > hi ? hi : k);
+    constexpr uint32_t hi = kQKeyBase + kQKeys - 1;
+    return k > hi ? hi : k;
 }
 
 // Magnitude index of a from est = the key table's entry for qkey(a).

@@ -418,6 +418,10 @@ def test_narrow_hook_validation(L):
     assert L.ou__narrow(1, 0x10000, 0x20000, 0, None) == OU_EINVAL
     assert L.ou__narrow(1, 0x10002, 0x20000, 16, None) == OU_EALIGN
     assert L.ou__narrow(2, 0x10000, 0x20001, 16, None) == OU_EALIGN
+    assert L.ou__narrow(18, 0x10000, 0x20000, 16, None) == OU_OK
+    assert L.ou__narrow(17, 0x10000, 0x20000, 15, None) == OU_EINVAL
+    assert L.ou__narrow(18, 0x10000, 0x20002, 16, None) == OU_EALIGN
+    assert L.ou__narrow(16, 0x10000, 0x20000, 16, None) == OU_EINVAL
 
 
 def test_sqrt_hook_validation(L):

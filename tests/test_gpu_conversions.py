@@ -20,8 +20,9 @@ def _nan16(h: np.ndarray, exp_mask: int, man_mask: int) -> np.ndarray:
 
 def test_kernel_rounding_exhaustive():
     """All 2^32 patterns in 16 chunks of 2^28: binary16 and bfloat16 codes
-    equal the oracle's bitwise; a NaN gives a NaN (payloads are not part of
-    the contract)."""
+    equal the oracle's bitwise, one value at a time (the 32-bit kernels) and
+    by packed pairs (the 8-bit kernels); a NaN gives a NaN (payloads are not
+    part of the contract)."""
     assert torch.cuda.is_available(), "GPU tests need a HIP device"
     L = H.lib()
     orc = O.load()
@@ -32,12 +33,13 @@ def test_kernel_rounding_exhaustive():
         x = np.arange(lo, lo + chunk, dtype=np.int32).view(np.float32)
         nan = np.isnan(x)
         for dtype, exp_mask, man_mask in ((O.F16, 0x7c00, 0x03ff), (O.BF16, 0x7f80, 0x007f)):
-            st = L.ou__narrow(dtype, x_dev.data_ptr(), out.data_ptr(), chunk, H.stream_handle())
-            assert st == 0, H.last_error(L)
-            got = out.cpu().numpy().view(np.uint16)
             want = orc.f32_to_storage(x, dtype)
-            same = (got == want) | (nan & _nan16(got, exp_mask, man_mask))
-            assert same.all(), (dtype, lo, int(np.argmin(same)), int((~same).sum()))
+            for mode in (0, 16):
+                st = L.ou__narrow(dtype + mode, x_dev.data_ptr(), out.data_ptr(), chunk, H.stream_handle())
+                assert st == 0, H.last_error(L)
+                got = out.cpu().numpy().view(np.uint16)
+                same = (got == want) | (nan & _nan16(got, exp_mask, man_mask))
+                assert same.all(), (dtype, mode, lo, int(np.argmin(same)), int((~same).sum()))
         del x_dev
 
 
