@@ -483,9 +483,12 @@ def bench_collection(torch, ou, W, dev, time_rounds):
 
 
 def cpu_baseline(torch, W, dev):
-    """The CPU oracle on a bounded sample of the headline workload: the same
-    2^28-element fp32 Adam inputs (same generator and seed), 10 steps, on
-    all host cores (about 10 s of single-core work)."""
+    """The CPU oracle on bounded samples: the headline workload's 2^28-element
+    fp32 Adam inputs (same generator and seed), 10 steps on all host cores
+    (the reported value) and 2 more on one thread; and the model-like
+    collection (505 bf16 tensors, AdamW, the collection benchmark's
+    generator and seed), 3 steps on all host cores.  About 25 s of
+    single-core work in all."""
     import numpy as np
 
     import oracle as O
@@ -506,10 +509,40 @@ def cpu_baseline(torch, W, dev):
         orc.update_f32(O.ADAM, O.F32, p, g, s1, s2, hp, t, nthreads=cores)
     dt = time.perf_counter() - t0
     gbs = W.bytes_per_element("adam", "fp32") * n * steps / dt / 1e9
-    return {"value": round(gbs, 2), "unit": "GB/s", "cores": cores, "kind": "oracle",
-            "sample": f"the headline workload itself (fp32 Adam, 2^28 elements, same seed), {steps} "
-                      f"steps, {dt:.2f} s wall on {cores} threads, OpenMP static schedule",
-            "elements_per_s": round(n * steps / dt, 0)}
+    out = {"value": round(gbs, 2), "unit": "GB/s", "cores": cores, "kind": "oracle",
+           "sample": f"the headline workload itself (fp32 Adam, 2^28 elements, same seed), {steps} "
+                     f"steps, {dt:.2f} s wall on {cores} threads, OpenMP static schedule",
+           "elements_per_s": round(n * steps / dt, 0)}
+    # the same tensor, two more steps on one thread
+    t0 = time.perf_counter()
+    for t in range(steps + 1, steps + 3):
+        orc.update_f32(O.ADAM, O.F32, p, g, s1, s2, hp, t, nthreads=1)
+    dt1 = time.perf_counter() - t0
+    out["single_thread"] = {"value": round(W.bytes_per_element("adam", "fp32") * n * 2 / dt1 / 1e9, 2),
+                            "unit": "GB/s", "steps": 2, "elements_per_s": round(n * 2 / dt1, 0)}
+    del p, g, s1, s2
+    # the model-like collection: bf16 AdamW over 505 tensors, 3 steps
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(4)
+    tensors = []
+    for _, shp in W.model_collection():
+        m = W.numel(shp)
+        pb = torch.empty(m, device=dev).uniform_(-1, 1, generator=gen).to(torch.bfloat16)
+        gb = (torch.randn(m, device=dev, generator=gen) * 0.01).to(torch.bfloat16)
+        tensors.append((pb.cpu().view(torch.int16).numpy().view(np.uint16).copy(),
+                        gb.cpu().view(torch.int16).numpy().view(np.uint16).copy(),
+                        np.zeros(m, np.float32), np.zeros(m, np.float32)))
+    hpc = O.HParams(lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.01)
+    elems = sum(t[0].size for t in tensors)
+    t0 = time.perf_counter()
+    for t in range(1, 4):
+        for pc, gc, m1, m2 in tensors:
+            orc.update_f32(O.ADAM, O.BF16, pc, gc, m1, m2, hpc, t, nthreads=cores)
+    dtc = (time.perf_counter() - t0) / 3
+    out["collection_505"] = {"us_per_step": round(dtc * 1e6, 1),
+                             "GBps": round(W.bytes_per_element("adam", "bf16") * elems / dtc / 1e9, 2),
+                             "steps": 3, "cores": cores, "tensors": len(tensors), "elements": elems}
+    return out
 
 
 if __name__ == "__main__":
