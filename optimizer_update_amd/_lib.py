@@ -133,6 +133,8 @@ def load(path: str = LIBRARY) -> ctypes.CDLL:
     lib.ou__narrow.restype = i32
     lib.ou__sqrt.argtypes = [vp, vp, i64, vp]
     lib.ou__sqrt.restype = i32
+    lib.ou__recip8.argtypes = [vp, vp, i64, vp]
+    lib.ou__recip8.restype = i32
     lib.ou__stream_probe.argtypes = [vp, vp, vp, vp, i64, vp]
     lib.ou__stream_probe.restype = i32
     lib.ou__force_xcd.argtypes = [i32]

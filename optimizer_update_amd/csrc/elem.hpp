@@ -71,9 +71,11 @@ __device__ __forceinline__ void update_moments(float g, float& m, float& v, floa
 // the same bits either way.  The branch splits straight-line code, which
 // costs the memory-bound 32-bit kernels more than the instructions it
 // saves; the 8-bit kernels, bound by instruction issue, use it.
-__device__ __forceinline__ float sqrt_rn(float x)
+//
+// sqrt_short is the short form alone, for x >= 2^-96 or +inf; sqrt_rn4 takes
+// four roots with one decision for the wave.
+__device__ __forceinline__ float sqrt_short(float x)
 {
-    if (__builtin_amdgcn_ballot_w64(!(x >= 0x1p-96f)) != 0) return __builtin_sqrtf(x);
     const float r = __builtin_amdgcn_sqrtf(x);
     const uint32_t b = __builtin_bit_cast(uint32_t, r);
     const float down = __builtin_bit_cast(float, b - 1u);
@@ -84,18 +86,52 @@ __device__ __forceinline__ float sqrt_rn(float x)
     return s;
 }
 
+__device__ __forceinline__ float sqrt_rn(float x)
+{
+    if (__builtin_amdgcn_ballot_w64(!(x >= 0x1p-96f)) != 0) return __builtin_sqrtf(x);
+    return sqrt_short(x);
+}
+
+__device__ __forceinline__ void sqrt_rn4(const float (&x)[4], float (&r)[4])
+{
+    bool tiny = false;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) tiny |= !(x[j] >= 0x1p-96f);
+    if (__builtin_amdgcn_ballot_w64(tiny) != 0) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) r[j] = __builtin_sqrtf(x[j]);
+    } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) r[j] = sqrt_short(x[j]);
+    }
+}
+
 // The update direction from the (new) moments: the parameter moves by
 // lr * direction.  Bias correction of m and v only; alpha mixes in the slow
 // EMA (not bias-corrected).  SHORT_ROOT: the square root by sqrt_rn.
-template <int KIND, bool SHORT_ROOT = false>
-__device__ __forceinline__ float direction(float m, float v, float m2, const StepScalars& s)
+// The two halves (bias_corrected, direction_from) let a caller take
+// several elements' square roots together.
+__device__ __forceinline__ void bias_corrected(float m, float v, const StepScalars& s, float& mh, float& vh)
 {
-    const float mh = div_step_constant(m, s.rbc1);   // m / bc1
-    const float vh = div_step_constant(v, s.rbc2);   // v / bc2
-    const float den = (SHORT_ROOT ? sqrt_rn(vh) : __builtin_sqrtf(vh)) + s.eps;
+    mh = div_step_constant(m, s.rbc1);   // m / bc1
+    vh = div_step_constant(v, s.rbc2);   // v / bc2
+}
+
+template <int KIND>
+__device__ __forceinline__ float direction_from(float mh, float root_vh, float m2, const StepScalars& s)
+{
+    const float den = root_vh + s.eps;
     float num = mh;
     if constexpr (KIND == kAdemamix) num = mh + s.alpha * m2;
     return num / den;
+}
+
+template <int KIND, bool SHORT_ROOT = false>
+__device__ __forceinline__ float direction(float m, float v, float m2, const StepScalars& s)
+{
+    float mh, vh;
+    bias_corrected(m, v, s, mh, vh);
+    return direction_from<KIND>(mh, SHORT_ROOT ? sqrt_rn(vh) : __builtin_sqrtf(vh), m2, s);
 }
 
 // Decoupled weight decay of the old parameter and the step (Loshchilov &

@@ -392,4 +392,22 @@ void ou__force_8bit(int waves, int blocks_per_wave, int chunk_blocks, int scalar
     g8_scalar = scalar_only;
 }
 
+__attribute__((visibility("default")))
+int ou__recip8(const float* in, float* out, int64_t n, void* stream)
+{
+    if (!in || !out || n <= 0) return fail(OU_EINVAL, "recip8: bad arguments");
+    if (reinterpret_cast<uintptr_t>(in) % 4 || reinterpret_cast<uintptr_t>(out) % 4)
+        return fail(OU_EALIGN, "recip8: misaligned buffers");
+    if (validate_only()) return OU_OK;
+    const DeviceProps* dp = nullptr;
+    if (int st = current_device(&dp)) return st;
+    const int64_t grid = std::max<int64_t>(1, std::min<int64_t>((n + 255) / 256, 1 << 20));
+    const float* a0 = in;
+    float* a1 = out;
+    void* args[] = {const_cast<float**>(&a0), &a1, &n};
+    hipError_t e = launch(recip_kernel8(), grid, 256, 0, args, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "launch recip8");
+    return OU_OK;
+}
+
 }  // extern "C"

@@ -123,4 +123,7 @@ static_assert(sizeof(Seg8) == 72, "Seg8 layout");
 // int32 blocks per item, StepScalars).  nullptr for other kinds.
 const void* kernel8(bool multi, int kind, int dtype);
 
+// The 8-bit kernels' reciprocal of a block maximum alone (test hook).
+const void* recip_kernel8();
+
 }  // namespace ou

@@ -153,6 +153,22 @@ __device__ __forceinline__ float wave_max3(float x, float y, float w)
     return __builtin_bit_cast(float, row_max(max_swap16(z, h)));
 }
 
+// fl32(1 / l) for a block maximum l (non-negative, not a NaN), and 0 for
+// l = 0 or +inf: the binary64 reciprocal estimate refined by two Newton
+// steps (within 2^-53 of 1/l, relative), rounded once.  A quotient of two
+// binary32 numbers is never a binary32 rounding midpoint and lies far enough
+// from every one that rounding a value this close gives the correctly
+// rounded quotient; the test suite compares it with 1/l for every binary32
+// l >= 0.  With l = +inf the estimate is a NaN, so the select covers it.
+__device__ __forceinline__ float recip_max(float l)
+{
+    const double d = static_cast<double>(l);
+    double y = __builtin_amdgcn_rcp(d);
+    y = __builtin_fma(__builtin_fma(-d, y, 1.0), y, y);
+    y = __builtin_fma(__builtin_fma(-d, y, 1.0), y, y);
+    return (l > 0.0f && l < __builtin_huge_valf()) ? static_cast<float>(y) : 0.0f;
+}
+
 // The inputs of one quantization block, as loaded by one wave: lane l
 // holds elements 4l .. 4l+3.  WIDE: the block is known to be whole and on
 // the wide path (no per-element checks).
@@ -265,9 +281,18 @@ __device__ __forceinline__ void finish_block8(const Seg8& d, int64_t b, const QL
         if constexpr (kMix) m2[j] = deq_signed(T, (w3 >> (8 * j)) & 0xffu) * A3;
     }
     if (dense) {
+        // update_element's steps, the four square roots together
+        float mh[4], vh[4], root[4];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            pn[j] = update_element<KIND, true>(S::widen(praw[j]), S::widen(graw[j]), m[j], v[j], m2[j], sc);
+            update_moments<KIND>(S::widen(graw[j]), m[j], v[j], m2[j], sc);
+            bias_corrected(m[j], v[j], sc, mh[j], vh[j]);
+        }
+        sqrt_rn4(vh, root);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            pn[j] = step_param(S::widen(praw[j]), direction_from<KIND>(mh[j], root[j], m2[j], sc), sc.decay,
+                               sc.lr, sc.decay_after);
             if constexpr (S::bytes == 4) praw[j] = pn[j];
         }
     } else {
@@ -303,8 +328,8 @@ __device__ __forceinline__ void finish_block8(const Seg8& d, int64_t b, const QL
 
     // requantize: x = value * fl32(1 / absmax).  With absmax = 0 every
     // value is +-0 or NaN, and r = 0 gives x = +-0 or NaN: code 0, as for
-    // the definition's x = 0.  One division serves all states.
-    const float r = (l > 0.0f) ? 1.0f / l : 0.0f;
+    // the definition's x = 0.  One reciprocal serves all states.
+    const float r = recip_max(l);
     const float r1 = lane_float(r, 0);
     const float r2 = lane_float(r, kLane2);
     float r3 = 0.0f;
@@ -457,6 +482,15 @@ k8_multi(const Seg8* __restrict__ segs, const WorkItem* __restrict__ items, int6
         run_blocks8<KIND, S>(d, b0, 1, chunk_blocks, T, sc, lane);
 }
 
+// recip_max on n values (test hook).
+__global__ void __launch_bounds__(256)
+k8_recip(const float* __restrict__ in, float* __restrict__ out, int64_t n)
+{
+    const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
+    for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < n; i += stride)
+        out[i] = recip_max(in[i]);
+}
+
 template <int KIND, typename S>
 const void* pick8(bool multi)
 {
@@ -476,6 +510,8 @@ const void* pick8_dtype(bool multi, int dtype)
 }
 
 }  // namespace
+
+const void* recip_kernel8() { return reinterpret_cast<const void*>(&k8_recip); }
 
 const void* kernel8(bool multi, int kind, int dtype)
 {

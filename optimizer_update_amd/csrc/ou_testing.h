@@ -46,6 +46,11 @@ int ou__narrow(int dtype, const float* in, uint16_t* out, int64_t n, void* strea
 // correctly rounded.  Asynchronous on `stream`.
 int ou__sqrt(const float* in, float* out, int64_t n, void* stream);
 
+// The 8-bit kernels' reciprocal of a block maximum on n values: out[i] =
+// fl32(1 / in[i]) for in[i] > 0 finite, 0 for +0 and +inf (negative inputs
+// and NaN are outside its domain and give 0).  Asynchronous on `stream`.
+int ou__recip8(const float* in, float* out, int64_t n, void* stream);
+
 // Bandwidth probe: the traffic of the plain fp32 Adam update of n elements
 // (p, g, s1, s2 read; p, s1, s2 written back unchanged) in the same launch
 // shape, with no arithmetic; n a multiple of 4, buffers 16-byte aligned.

@@ -51,7 +51,7 @@ def test_exports_every_header_function(L):
     assert exported - set(names) == {"ou__select_single", "ou__force_single", "ou__force_multi",
                                      "ou__step_scalars", "ou__force_8bit", "ou__validate_only",
                                      "ou__force_xcd", "ou__stream_probe", "ou__narrow",
-                                     "ou__sqrt"}
+                                     "ou__sqrt", "ou__recip8"}
 
 
 def test_header_is_plain_c_and_matches_ctypes_layout(tmp_path):
@@ -425,8 +425,12 @@ def test_narrow_hook_validation(L):
 
 
 def test_sqrt_hook_validation(L):
-    """The square-root hook's argument checks (test hook)."""
+    """The square-root and reciprocal hooks' argument checks (test hooks)."""
     assert L.ou__sqrt(0x10000, 0x20000, 16, None) == OU_OK
     assert L.ou__sqrt(0x10000, 0x20000, 0, None) == OU_EINVAL
     assert L.ou__sqrt(0, 0x20000, 16, None) == OU_EINVAL
     assert L.ou__sqrt(0x10002, 0x20000, 16, None) == OU_EALIGN
+    assert L.ou__recip8(0x10000, 0x20000, 16, None) == OU_OK
+    assert L.ou__recip8(0x10000, 0x20000, -1, None) == OU_EINVAL
+    assert L.ou__recip8(0x10000, 0, 16, None) == OU_EINVAL
+    assert L.ou__recip8(0x10000, 0x20001, 16, None) == OU_EALIGN

@@ -61,3 +61,26 @@ def test_kernel_sqrt_exhaustive():
             want = np.sqrt(np.arange(lo, lo + chunk, dtype=np.int32).view(np.float32))
             same = (got.view(np.uint32) == want.view(np.uint32)) | (np.isnan(got) & np.isnan(want))
             assert same.all(), (lo, int(np.argmin(same)), int((~same).sum()))
+
+
+def test_kernel_block_reciprocal_exhaustive():
+    """The 8-bit kernels' reciprocal of a block maximum (binary64 estimate,
+    two Newton steps, one rounding) on every binary32 l in [+0, +inf], in 8
+    chunks of 2^28: bitwise equal to numpy's IEEE binary32 1 / l for l > 0
+    finite, and 0 for +0 and +inf."""
+    assert torch.cuda.is_available(), "GPU tests need a HIP device"
+    L = H.lib()
+    chunk = 1 << 28
+    out = torch.empty(chunk, dtype=torch.float32, device="cuda")
+    top = 0x7f800000   # +inf
+    with np.errstate(divide="ignore", over="ignore"):
+        for lo in range(0, top + 1, chunk):
+            cnt = min(chunk, top + 1 - lo)
+            x_dev = torch.arange(lo, lo + cnt, dtype=torch.int32, device="cuda").view(torch.float32)
+            st = L.ou__recip8(x_dev.data_ptr(), out.data_ptr(), cnt, H.stream_handle())
+            assert st == 0, H.last_error(L)
+            got = out[:cnt].cpu().numpy()
+            x = np.arange(lo, lo + cnt, dtype=np.int32).view(np.float32)
+            want = np.where((x > 0) & np.isfinite(x), np.float32(1.0) / x, np.float32(0.0)).astype(np.float32)
+            same = got.view(np.uint32) == want.view(np.uint32)
+            assert same.all(), (lo, int(np.argmin(same)), int((~same).sum()))
