@@ -11,6 +11,7 @@ library, or without a GPU, calls raise.
     optimizer_update_32bit_clip(..., max_unorm=..., workspace=...)   update-norm clipping
     optimizer_update_32bit_multi(kind, segments, hp, step)
     Plan(kind, segments)  -> .step(hp, step) / .graph_step(hp, step) / .close()
+                             .step_clip / .graph_step_clip(hp, step, max_unorm)
     AdamW32, AdEMAMix32, Momentum32, RMSprop32, Adagrad32, Lion32
                            collection optimizers over a fixed parameter list
 
