@@ -185,9 +185,12 @@ int check_segment(int kind, const ou_segment& s, int idx, std::vector<Range>* ra
     return OU_OK;
 }
 
-// No written range may overlap any other range (read-only ranges may share).
+// No range may run past the end of the address space, and no written range
+// may overlap any other range (read-only ranges may share).
 int check_overlap(std::vector<Range>& r)
 {
+    for (const Range& x : r)
+        if (x.hi < x.lo) return fail(OU_EINVAL, "segment %d: a buffer runs past the end of the address space", x.seg);
     std::sort(r.begin(), r.end(), [](const Range& a, const Range& b) { return a.lo < b.lo; });
     // Sweep: track the written range reaching furthest and any range reaching furthest.
     uintptr_t any_hi = 0, w_hi = 0;

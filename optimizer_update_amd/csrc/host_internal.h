@@ -36,7 +36,8 @@ struct Range {
     bool written;
     int seg;
 };
-// No written range may overlap any other range (read-only ranges may share).
+// OU_EINVAL if a range wraps past the end of the address space; OU_EOVERLAP
+// if a written range overlaps any other range (read-only ranges may share).
 int check_overlap(std::vector<Range>& r);
 
 StepScalars make_scalars(const ou_hparams& h, int decay_after);

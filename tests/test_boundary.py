@@ -434,3 +434,115 @@ def test_sqrt_hook_validation(L):
     assert L.ou__recip8(0x10000, 0x20000, -1, None) == OU_EINVAL
     assert L.ou__recip8(0x10000, 0, 16, None) == OU_EINVAL
     assert L.ou__recip8(0x10000, 0x20001, 16, None) == OU_EALIGN
+
+
+# ---- validation against a brute-force reference (property-based) -----------
+
+from hypothesis import HealthCheck, given, settings  # noqa: E402
+from hypothesis import strategies as st  # noqa: E402
+
+_SLOT = 256    # bytes between neighbouring slots: buffers of up to 512 B reach over two
+_BASE = 0x100000
+
+
+def _addr(slot, off):
+    return _BASE + slot * _SLOT + off
+
+
+_SEGMENT = st.tuples(st.integers(0, 31), st.integers(0, 31), st.integers(0, 31), st.integers(0, 31),
+                     st.integers(1, 64), st.sampled_from([0, 1, 2]),
+                     st.sampled_from([0, 0, 0, 0, 1, 2]))   # slots p g s1 s2, n, dtype, misalignment
+
+
+def _expected(kind, segments):
+    """The documented rules, checked pair by pair: a misaligned pointer gives
+    OU_EALIGN (segments are checked in order, before any overlap); then any two
+    byte ranges that intersect, one of them written, give OU_EOVERLAP."""
+    two = kind in (0, 1)
+    ranges = []
+    for sp, sg, s1, s2, n, dtype, mis in segments:
+        sb = 4 if dtype == 0 else 2
+        p, g, a1, a2 = _addr(sp, mis), _addr(sg, 0), _addr(s1, 0), _addr(s2, 0)
+        if p % sb or g % sb or a1 % 4 or (two and a2 % 4):
+            return OU_EALIGN
+        ranges += [(p, p + n * sb, True), (g, g + n * sb, False),
+                   (a1, a1 + (2 if kind == 1 else 1) * n * 4, True)]
+        if two:
+            ranges.append((a2, a2 + n * 4, True))
+    for i in range(len(ranges)):
+        for j in range(i + 1, len(ranges)):
+            (lo1, hi1, w1), (lo2, hi2, w2) = ranges[i], ranges[j]
+            if (w1 or w2) and lo1 < hi2 and lo2 < hi1:
+                return OU_EOVERLAP
+    return OU_OK
+
+
+@settings(max_examples=400, deadline=None, suppress_health_check=[HealthCheck.function_scoped_fixture])
+@given(kind=st.sampled_from([0, 1, 2]), segments=st.lists(_SEGMENT, min_size=1, max_size=5))
+def test_collection_validation_matches_pairwise_rules(L, kind, segments):
+    """ou_plan_create and optimizer_update_32bit_multi return what the
+    pairwise reference gives, on random layouts where overlaps and
+    misalignments are common (a sort-and-sweep against an O(n^2) check)."""
+    rows = [(_addr(sp, mis), _addr(sg, 0), _addr(s1, 0), _addr(s2, 0), n, dtype, 0)
+            for sp, sg, s1, s2, n, dtype, mis in segments]
+    want = _expected(kind, segments)
+    h = ctypes.c_void_p()
+    assert L.ou_plan_create(kind, _segs(*rows), len(rows), ctypes.byref(h)) == want
+    assert not h.value
+    hp = _lib.ou_hparams(0.9, 0.999, 0.9999, 5.0, 1e-8, 0.0, 1e-3, 0, 1)
+    assert L.optimizer_update_32bit_multi(kind, _segs(*rows), len(rows), ctypes.byref(hp), None) == want
+
+
+def test_ranges_past_the_end_of_the_address_space(L):
+    """A buffer that would run past 2^64 is rejected (OU_EINVAL), not wrapped
+    into a small range that escapes the overlap check."""
+    top = (1 << 64) - 64
+    assert _call(L, p=top, n=32) == OU_EINVAL
+    assert _call(L, s2=top & ~3, n=32) == OU_EINVAL
+    h = ctypes.c_void_p()
+    assert L.ou_plan_create(0, _segs((0x100000, top, 0x300000, 0x400000, 1024, 0, 0)), 1,
+                            ctypes.byref(h)) == OU_EINVAL
+    assert _call(L, p=top - 4 * 32, n=32) == OU_OK
+
+
+_SEGMENT8 = st.tuples(st.lists(st.integers(0, 63), min_size=6, max_size=6), st.integers(1, 300),
+                      st.sampled_from([0, 1, 2]), st.sampled_from([0] * 12 + [1, 2]),
+                      st.sampled_from([0] * 12 + [1, 2]))  # slots p g c1 c2 a1 a2, n, dtype, p / a1 offsets
+
+
+def _expected8(kind, segments):
+    """The 8-bit segment rules pair by pair: param/grad aligned to their
+    element size and absmax to 4 bytes (codes have no alignment), else
+    OU_EALIGN; then intersecting byte ranges with one of them written give
+    OU_EOVERLAP (codes k*n and n bytes, absmax 4 B per 256-element block)."""
+    k = 2 if kind == 1 else 1
+    ranges = []
+    for slots, n, dtype, mp, ma in segments:
+        sb = 4 if dtype == 0 else 2
+        p, g, c1, c2, a1, a2 = (_addr(s, 0) for s in slots)
+        p += mp
+        a1 += ma
+        if p % sb or g % sb or a1 % 4 or a2 % 4:
+            return OU_EALIGN
+        nb = -(-n // 256)
+        ranges += [(p, p + n * sb, True), (g, g + n * sb, False), (c1, c1 + k * n, True), (c2, c2 + n, True),
+                   (a1, a1 + k * nb * 4, True), (a2, a2 + nb * 4, True)]
+    for i in range(len(ranges)):
+        for j in range(i + 1, len(ranges)):
+            (lo1, hi1, w1), (lo2, hi2, w2) = ranges[i], ranges[j]
+            if (w1 or w2) and lo1 < hi2 and lo2 < hi1:
+                return OU_EOVERLAP
+    return OU_OK
+
+
+@settings(max_examples=300, deadline=None, suppress_health_check=[HealthCheck.function_scoped_fixture])
+@given(kind=st.sampled_from([0, 1]), segments=st.lists(_SEGMENT8, min_size=1, max_size=4))
+def test_8bit_collection_validation_matches_pairwise_rules(L, kind, segments):
+    """ou_plan8_create returns what the pairwise reference gives."""
+    arr = (_lib.ou_segment8 * len(segments))()
+    for i, (slots, n, dtype, mp, ma) in enumerate(segments):
+        p, g, c1, c2, a1, a2 = (_addr(s, 0) for s in slots)
+        arr[i] = _lib.ou_segment8(p + mp, g, c1, c2, a1 + ma, a2, n, dtype, 0)
+    h = ctypes.c_void_p()
+    assert L.ou_plan8_create(kind, arr, len(segments), ctypes.byref(h)) == _expected8(kind, segments)
+    assert not h.value
