@@ -1,9 +1,9 @@
 """GPU tests of the collection entry points and stream/graph plumbing.
 
 A plan over a mixed-dtype collection (one launch per dtype group), the eager
-multi-tensor entry, work on a non-default stream, and a plan step captured
-into the caller's own HIP graph: each must give, bitwise, what one direct
-call per tensor gives, and match the oracle.
+multi-tensor entry, work on a non-default stream, and a plan step (plain or
+clipped) captured into the caller's own HIP graph: each must give, bitwise,
+what one direct call per tensor gives, and match the oracle.
 """
 from __future__ import annotations
 
@@ -161,6 +161,50 @@ def test_plan_step_captured_in_caller_graph():
     eplan.close()
 
 
+def test_plan_step_clip_captured_in_caller_graph():
+    """ou_plan_step_clip (three launches per dtype group, partial norms in the
+    plan) is capture-safe too: each replay of the captured clipped step, with
+    eager work between replays, equals the same step run eagerly, clip
+    factors included."""
+    import optimizer_update_amd as ou
+    kind = "adam"
+    host = _collection(kind, 4)
+    hp = ou.HParams(lr=1e-2, weight_decay=0.01)
+    segs = _device(kind, host)
+    eager = _device(kind, host)
+    plan = ou.Plan(kind, segs)
+    eplan = ou.Plan(kind, eager)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=s):
+        plan.step_clip(hp, 1, 0.05, stream=s)
+    torch.cuda.synchronize()
+    p0 = [x[0].clone() for x in segs]
+    for rep in range(3):
+        for (p, _, s1, s2), pp in zip(segs, p0):
+            p.copy_(pp)
+            s1.zero_()
+            s2.zero_()
+        for (p, _, s1, s2), (sh, pinit, _) in zip(eager, host):
+            p.copy_(W.to_torch(pinit, sh, "cuda"))
+            s1.zero_()
+            s2.zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        eplan.step_clip(hp, 1, 0.05)
+        torch.zeros(1 << 16, device="cuda").add_(1.0)   # unrelated eager work
+        torch.cuda.synchronize()
+        for x, y in zip(segs, eager):
+            for j in (0, 2, 3):
+                assert _bits(x[j]) == _bits(y[j]), (rep, j)
+        fa, fb = plan.clip_factors(), eplan.clip_factors()
+        assert fa == fb and min(fa) < 1.0, (fa, fb)
+    plan.close()
+    eplan.close()
+
+
 def test_graph_step_rejected_under_capture_and_multi_too():
     """Entry points that build or launch their own graph, or allocate, refuse
     to run inside a caller's capture instead of corrupting it."""
@@ -178,6 +222,7 @@ def test_graph_step_rejected_under_capture_and_multi_too():
         with torch.cuda.graph(graph, stream=s):
             x.add_(1.0)      # keep the captured graph non-empty
             for fn in (lambda: plan.graph_step(hp, 1, stream=s),
+                       lambda: plan.graph_step_clip(hp, 1, 0.5, stream=s),
                        lambda: ou.optimizer_update_32bit_multi("adam", segs, hp, 1, stream=s)):
                 try:
                     fn()
@@ -185,5 +230,5 @@ def test_graph_step_rejected_under_capture_and_multi_too():
                     errors.append(e.status)
     finally:
         torch.cuda.synchronize()
-    assert errors == [-7, -7]
+    assert errors == [-7, -7, -7]
     plan.close()
