@@ -279,7 +279,7 @@ class Plan:
 
     def step(self, hp: HParams, step: int, stream=None) -> None:
         c = hp.c(step)
-        check(_on(self.device.index, self._lib.ou_plan_step, self._h, ctypes.byref(c),
+        check(_on(self.device.index, self._lib.ou_plan_step, self._h, c,
                   self._stream(stream)), self._lib)
 
     def step_clip(self, hp: HParams, step: int, max_unorm: float, stream=None) -> None:
@@ -427,7 +427,7 @@ class Plan8:
         c = hp.c(step)
         sh = (_raw_stream(self.device.index) if stream is None
               else (stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)))
-        check(_on(self.device.index, self._lib.ou_plan8_step, self._h, ctypes.byref(c), sh),
+        check(_on(self.device.index, self._lib.ou_plan8_step, self._h, c, sh),
               self._lib)
 
     def graph_step(self, hp: HParams, step: int, stream=None) -> None:

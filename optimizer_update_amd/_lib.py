@@ -142,8 +142,27 @@ def load(path: str = LIBRARY) -> ctypes.CDLL:
     lib.ou__validate_only.argtypes = [i32]
     lib.ou__validate_only.restype = None
     if path == LIBRARY:
+        _install_fast(lib)
         _lib = lib
     return lib
+
+
+# Per-step entry points that the CPython module _fast also exposes.
+FAST_ENTRY_POINTS = ("optimizer_update_32bit", "optimizer_update_8bit_blockwise", "ou_plan_step",
+                     "ou_plan8_step")
+
+
+def _install_fast(lib: ctypes.CDLL) -> None:
+    """Route the per-step entry points of the in-tree library through _fast
+    when it is built: the same C functions of the same loaded library, the
+    same positional arguments, converted in C instead of by ctypes (a struct
+    argument is passed as the struct or its address, not as byref())."""
+    try:
+        from . import _fast
+    except ImportError:
+        return
+    for name in FAST_ENTRY_POINTS:
+        setattr(lib, name, getattr(_fast, name))
 
 
 def check(status: int, lib: ctypes.CDLL | None = None) -> None:

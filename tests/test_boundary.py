@@ -183,7 +183,7 @@ def test_plan_and_multi_validation(L):
     assert L.ou_plan_create(0, _segs(ok), 1, None) == OU_EINVAL
     bad_hp = _lib.ou_hparams(0.9, 0.999, 0.9999, 5.0, 1e-8, 0.0, 1e-3, 0, 0)
     assert L.optimizer_update_32bit_multi(0, _segs(ok), 1, ctypes.byref(bad_hp), None) == OU_EINVAL
-    assert L.ou_plan_step(None, ctypes.byref(bad_hp), None) == OU_EINVAL
+    assert L.ou_plan_step(None, bad_hp, None) == OU_EINVAL
     assert L.ou_plan_graph_step(None, ctypes.byref(bad_hp), None) == OU_EINVAL
     assert L.ou_plan_describe(None, None, None, None) == OU_EINVAL
     assert L.ou_plan_step_clip(None, ctypes.byref(bad_hp), 1.0, None) == OU_EINVAL
