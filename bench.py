@@ -244,7 +244,8 @@ def main():
                 "device": props.name, "arch": getattr(props, "gcnArchName", None),
                 "cu_count": props.multi_processor_count,
                 "hbm_bytes": props.total_memory, "l2_bytes": getattr(props, "L2_cache_size", None),
-                "kernel_sources_sha": kernel_sha(), "kernel8_sources_sha": kernel_sha(KERNEL8_SOURCES)},
+                "kernel_sources_sha": kernel_sha(), "kernel8_sources_sha": kernel_sha(KERNEL8_SOURCES),
+                "binding": ("_fast" if isinstance(ou.load().optimizer_update_32bit, type(len)) else "ctypes")},
     }
     if kind.endswith("8") and not clip:
         alu = alu_roofline(f"{kind[:-1]}_{storage}", n, ms)
