@@ -155,8 +155,10 @@ FAST_ENTRY_POINTS = ("optimizer_update_32bit", "optimizer_update_8bit_blockwise"
 def _install_fast(lib: ctypes.CDLL) -> None:
     """Route the per-step entry points of the in-tree library through _fast
     when it is built: the same C functions of the same loaded library, the
-    same positional arguments, converted in C instead of by ctypes (a struct
-    argument is passed as the struct or its address, not as byref())."""
+    same positional arguments, converted in C instead of by ctypes.  A
+    struct argument is the ou_hparams instance or its int address (not
+    byref(), pointer() or c_void_p: those raise TypeError).  Like ctypes,
+    the calls release the GIL while the library runs."""
     try:
         from . import _fast
     except ImportError:

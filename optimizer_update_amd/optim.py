@@ -15,7 +15,13 @@ smaller ones to the 32-bit path, one plan each.
 
 Parameters and gradients must be contiguous CUDA (HIP) tensors whose
 storage stays in place for the optimizer's lifetime: the plan holds their
-addresses.
+addresses.  When the optimizer takes its gradients from ``Parameter.grad``
+(no ``grads=`` argument), every step checks that each parameter's ``.grad``
+is still the tensor the plan was built on: a ``zero_grad(set_to_none=True)``
+elsewhere (torch's default) makes the next backward allocate new gradient
+tensors, and the plan is then rebuilt on them (a step with a parameter whose
+``.grad`` is None raises).  The optimizers' own ``zero_grad()`` zeroes the
+captured gradients in place, which keeps the plan.
 """
 from __future__ import annotations
 
@@ -31,17 +37,8 @@ class _Collection:
 
     def __init__(self, params, hp: HParams, grads=None, max_unorm: float = 0.0,
                  decay_after: bool = False):
-        self.params = [p.data if isinstance(p, torch.nn.Parameter) else p for p in params]
-        if grads is None:
-            grads = []
-            for p, src in zip(self.params, params):
-                g = getattr(src, "grad", None)
-                if g is None:
-                    g = torch.zeros_like(p)
-                    if isinstance(src, torch.nn.Parameter):
-                        src.grad = g
-                grads.append(g)
-        self.grads = list(grads)
+        params = list(params)
+        self.params, self.grads, self._sources = _params_and_grads(params, grads)
         self.hp = hp
         self.decay_after = bool(decay_after)
         two = _kind(self.kind) in TWO_STATE
@@ -57,8 +54,24 @@ class _Collection:
         self.max_unorm = float(max_unorm)
         self._workspace = None
         self._direct = None
-        self.plan = Plan(self.kind, list(zip(self.params, self.grads, self.state1, self.state2)),
-                         decay_after=self.decay_after)
+        self.plan = self._build_plan()
+
+    def _build_plan(self) -> Plan:
+        return Plan(self.kind, list(zip(self.params, self.grads, self.state1, self.state2)),
+                    decay_after=self.decay_after)
+
+    def _sync_grads(self) -> None:
+        """Rebuild the plan if a parameter's .grad is no longer the captured tensor."""
+        if _grads_moved(self._sources, self.grads):
+            self.plan.close()
+            self.plan = self._build_plan()
+            self._direct = None
+
+    def zero_grad(self, set_to_none: bool = False) -> None:
+        """Zero the captured gradients in place (the plan keeps its
+        addresses; set_to_none is accepted for torch's signature and ignored)."""
+        del set_to_none
+        _zero_in_place(self._sources, self.grads)
 
     def segments(self):
         return list(zip(self.params, self.grads, self.state1, self.state2))
@@ -67,6 +80,7 @@ class _Collection:
     def step(self, graph: bool = False, stream=None) -> None:
         """One step of the whole collection: plan launch, or graph replay.
         With max_unorm > 0 every tensor's update is clipped by its own norms."""
+        self._sync_grads()
         self.step_count += 1
         if self.max_unorm > 0:
             (self.plan.graph_step_clip if graph else self.plan.step_clip)(
@@ -80,6 +94,7 @@ class _Collection:
     def step_per_tensor(self, stream=None) -> None:
         """The same step as one direct call per tensor (the tensors were
         checked when the optimizer was built; only the step changes)."""
+        self._sync_grads()
         self.step_count += 1
         h = self.hp
         if self.max_unorm > 0:
@@ -199,17 +214,53 @@ class Lion32(_Collection):
 
 
 def _params_and_grads(params, grads):
+    """(parameter data, gradients, sources): sources[i] is the Parameter
+    whose .grad the optimizer follows, or None when the gradients were given
+    explicitly (or the parameter is a plain tensor)."""
+    params = list(params)
     ps = [p.data if isinstance(p, torch.nn.Parameter) else p for p in params]
-    if grads is None:
-        grads = []
-        for p, src in zip(ps, params):
-            g = getattr(src, "grad", None)
-            if g is None:
-                g = torch.zeros_like(p)
-                if isinstance(src, torch.nn.Parameter):
-                    src.grad = g
-            grads.append(g)
-    return ps, list(grads)
+    if grads is not None:
+        return ps, list(grads), [None] * len(ps)
+    gs, sources = [], []
+    for p, src in zip(ps, params):
+        g = getattr(src, "grad", None)
+        if g is None:
+            g = torch.zeros_like(p)
+            if isinstance(src, torch.nn.Parameter):
+                src.grad = g
+        gs.append(g)
+        sources.append(src if isinstance(src, torch.nn.Parameter) else None)
+    return ps, gs, sources
+
+
+def _grads_moved(sources, grads) -> bool:
+    """True (and grads updated) if a followed Parameter's .grad is a tensor
+    at another address than the captured one; raises if it is None.  The
+    same address (the allocator handed the memory back) needs no rebuild."""
+    moved = False
+    for i, src in enumerate(sources):
+        if src is None:
+            continue
+        g = src.grad
+        if g is grads[i]:
+            continue
+        if g is None:
+            raise RuntimeError(f"parameter {i} has no .grad: run backward before step(), and use the "
+                               "optimizer's zero_grad() (in place) rather than set_to_none=True")
+        if g.shape != grads[i].shape or g.dtype != grads[i].dtype or g.device != grads[i].device:
+            raise RuntimeError(f"parameter {i}: .grad changed shape, dtype or device")
+        if not g.is_contiguous():
+            raise RuntimeError(f"parameter {i}: .grad is not contiguous")
+        moved |= g.data_ptr() != grads[i].data_ptr()
+        grads[i] = g
+    return moved
+
+
+def _zero_in_place(sources, grads) -> None:
+    for i, src in enumerate(sources):
+        if src is not None and src.grad is not None and src.grad is not grads[i]:
+            src.grad.zero_()
+    torch._foreach_zero_(list(grads))
 
 
 class _Collection8:
@@ -221,34 +272,51 @@ class _Collection8:
 
     def __init__(self, params, hp: HParams, grads=None, min_8bit_size: int = 4096,
                  decay_after: bool = False):
-        self.params, self.grads = _params_and_grads(params, grads)
+        self.params, self.grads, self._sources = _params_and_grads(params, grads)
         self.hp = hp
         self.min_8bit_size = int(min_8bit_size)
         self.decay_after = bool(decay_after)
         self.step_count = 0
         self.state = []            # per parameter: ("8bit", s1, s2, a1, a2) or ("32bit", s1, s2)
-        seg8, seg32 = [], []
-        for p, g in zip(self.params, self.grads):
+        for p in self.params:
             if p.numel() >= self.min_8bit_size:
                 n1, n2, na1, na2 = state8_sizes(self.kind, p.numel())
                 st = ("8bit", torch.zeros(n1, dtype=torch.uint8, device=p.device),
                       torch.zeros(n2, dtype=torch.uint8, device=p.device),
                       torch.zeros(na1, dtype=torch.float32, device=p.device),
                       torch.zeros(na2, dtype=torch.float32, device=p.device))
-                seg8.append((p, g, *st[1:]))
             else:
                 n1, n2 = state_sizes(self.kind, p.numel())
                 st = ("32bit", torch.zeros(n1, dtype=torch.float32, device=p.device),
                       torch.zeros(n2, dtype=torch.float32, device=p.device))
-                seg32.append((p, g, *st[1:]))
             self.state.append(st)
+        self.plan8 = self.plan32 = None
+        self._build_plans()
+
+    def _build_plans(self) -> None:
+        seg8, seg32 = [], []
+        for p, g, st in zip(self.params, self.grads, self.state):
+            (seg8 if st[0] == "8bit" else seg32).append((p, g, *st[1:]))
         self.plan8 = Plan8(self.kind, seg8, decay_after=self.decay_after) if seg8 else None
         self.plan32 = Plan(self.kind, seg32, decay_after=self.decay_after) if seg32 else None
+
+    def _sync_grads(self) -> None:
+        """Rebuild the plans if a parameter's .grad is no longer the captured tensor."""
+        if _grads_moved(self._sources, self.grads):
+            self.close()
+            self._build_plans()
+
+    def zero_grad(self, set_to_none: bool = False) -> None:
+        """Zero the captured gradients in place (the plans keep their
+        addresses; set_to_none is accepted for torch's signature and ignored)."""
+        del set_to_none
+        _zero_in_place(self._sources, self.grads)
 
     @torch.no_grad()
     def step(self, graph: bool = False, stream=None) -> None:
         """One step: the 8-bit plan, then the 32-bit plan (one launch per
         dtype group each), or the replay of their HIP graphs."""
+        self._sync_grads()
         self.step_count += 1
         if self.plan8 is not None:
             (self.plan8.graph_step if graph else self.plan8.step)(self.hp, self.step_count, stream)
@@ -258,6 +326,7 @@ class _Collection8:
     @torch.no_grad()
     def step_per_tensor(self, stream=None) -> None:
         """The same step as one direct call per tensor (the eager loop)."""
+        self._sync_grads()
         self.step_count += 1
         h = self.hp
         kw = dict(step=self.step_count, lr=h.lr, beta1=h.beta1, beta2=h.beta2, beta3=h.beta3,

@@ -83,6 +83,32 @@ def test_plan_steps_take_the_struct_or_its_address(libs):
             f(None, ctypes.byref(hp), None)
 
 
+@pytest.mark.parametrize("form", ["pointer", "c_void_p", "short_bytearray", "long_bytearray", "str"])
+def test_plan_steps_reject_buffers_that_are_not_the_struct(libs, form):
+    """Objects whose buffer is not an ou_hparams (a ctypes pointer or
+    c_void_p exports its 8-byte pointer cell, a bytearray may be short) are
+    refused with TypeError: the library must never read 40 bytes from a
+    smaller buffer."""
+    fast, _ = libs
+    hp = _lib.ou_hparams(0.9, 0.999, 0.9999, 5.0, 1e-8, 0.0, 1e-3, 0, 1)
+    arg = {"pointer": lambda: ctypes.pointer(hp),
+           "c_void_p": lambda: ctypes.c_void_p(ctypes.addressof(hp)),
+           "short_bytearray": lambda: bytearray(4),
+           "long_bytearray": lambda: bytearray(64),
+           "str": lambda: "hparams"}[form]()
+    for name in ("ou_plan_step", "ou_plan8_step"):
+        with pytest.raises(TypeError):
+            getattr(fast, name)(None, arg, None)
+
+
+def test_plan_steps_accept_a_struct_sized_buffer(libs):
+    fast, _ = libs
+    raw = bytearray(ctypes.sizeof(_lib.ou_hparams))
+    for name in ("ou_plan_step", "ou_plan8_step"):
+        assert getattr(fast, name)(None, raw, None) == OU_EINVAL   # null plan, checked by the library
+
+
+
 def test_argument_errors_raise(libs):
     fast, _ = libs
     with pytest.raises(TypeError):
