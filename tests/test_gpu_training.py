@@ -91,7 +91,7 @@ def test_set_to_none_gradients_are_followed(which):
     plan on the new buffers and trains as with in-place zeroing: the
     parameters agree within 1e-4 of each tensor's scale after the same
     steps (the backward's GEMMs need not be bitwise repeatable; a step on
-    stale or freed gradient buffers would be off by orders more).
+    stale or freed gradient buffers would be off by orders more)."""
     import optimizer_update_amd as ou
     make = {"adamw32": lambda ps: ou.AdamW32(ps, lr=3e-3, weight_decay=0.01),
             "adamw8bit": lambda ps: ou.AdamW8bit(ps, lr=3e-3, weight_decay=0.01, min_8bit_size=4096)}[which]
