@@ -162,6 +162,29 @@ int optimizer_update_32bit_clip(int kind, int dtype, void* param, const void* gr
                                 int skip_zeros, float max_unorm, void* workspace,
                                 int64_t workspace_bytes, void* stream);
 
+/* The clipped step of optimizer_update_32bit_clip without a workspace, for
+ * callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * partial norms and the clip factor live in a static device array of the
+ * library, 8 MiB + 256 bytes per GPU, held from the first call on a device
+ * until the process ends.  Same arguments and results (bitwise) as
+ * optimizer_update_32bit_clip, minus workspace and workspace_bytes; n may
+ * be at most ou_clip_noalloc_max_elements() = 2^30 (larger n: OU_EINVAL,
+ * nothing launched).  The call allocates nothing: no hipMalloc, hipFree or
+ * allocating library routine.  All calls on one GPU share the array, so
+ * calls that overlap in time on one GPU (other streams, other host
+ * threads) race; calls in one stream's order do not.  After a call the
+ * clip factor s of its step is not readable by the caller (use the
+ * workspace form for that). */
+int optimizer_update_32bit_clip_noalloc(int kind, int dtype, void* param, const void* grad,
+                                        float* state1, float* state2, int64_t n,
+                                        float beta1, float beta2, float beta3, float alpha,
+                                        float eps, float weight_decay, int64_t step, float lr,
+                                        int skip_zeros, float max_unorm, void* stream);
+
+/* Largest n optimizer_update_32bit_clip_noalloc accepts (2^30). */
+int64_t ou_clip_noalloc_max_elements(void);
+
 /* One optimizer step over a collection of nseg tensors (any mix of
  * dtypes), one launch per dtype group (the eager optimizer.step() of
  * section "B300 benchmark and acceptance").  Convenience form: builds and

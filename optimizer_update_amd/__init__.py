@@ -9,6 +9,7 @@ library, or without a GPU, calls raise.
 
     optimizer_update_32bit(kind, param, grad, state1, state2, step=..., lr=..., ...)
     optimizer_update_32bit_clip(..., max_unorm=..., workspace=...)   update-norm clipping
+    optimizer_update_32bit_clip_noalloc(..., max_unorm=...)   the same, allocating nothing
     optimizer_update_32bit_multi(kind, segments, hp, step)
     Plan(kind, segments)  -> .step(hp, step) / .graph_step(hp, step) / .close()
                              .step_clip / .graph_step_clip(hp, step, max_unorm)
@@ -33,6 +34,7 @@ from ._lib import OptimizerUpdateError, check, load
 
 __all__ = ["HParams", "optimizer_update_32bit", "optimizer_update_32bit_clip",
            "clip_workspace_bytes", "clip_workspace", "clip_scale",
+           "optimizer_update_32bit_clip_noalloc", "clip_noalloc_max_elements",
            "optimizer_update_32bit_multi", "Plan",
            "OptimizerUpdateError", "KINDS", "DTYPES", "load", "state_sizes"]
 
@@ -229,6 +231,34 @@ def optimizer_update_32bit_clip(kind, param: torch.Tensor, grad: torch.Tensor,
                                              _stream(param, stream))
     check(st, lib)
     return workspace
+
+
+def optimizer_update_32bit_clip_noalloc(kind, param: torch.Tensor, grad: torch.Tensor,
+                                        state1: torch.Tensor, state2: torch.Tensor | None, *,
+                                        step: int, lr: float, max_unorm: float, beta1: float = 0.9,
+                                        beta2: float = 0.999, beta3: float = 0.9999,
+                                        alpha: float = 5.0, eps: float = 1e-8,
+                                        weight_decay: float = 0.0, skip_zeros: bool = False,
+                                        decay_after: bool = False, stream=None) -> None:
+    """``optimizer_update_32bit_clip`` without a workspace: the library's
+    static device scratch holds the partial norms, so nothing is allocated
+    (n up to ``clip_noalloc_max_elements()``).  Calls that overlap in time
+    on one GPU share that scratch and race."""
+    k = _kind(kind, decay_after)
+    n, dt = _tensor_args(k, param, grad, state1, state2)
+    lib = load()
+    with _on_device(param.device):
+        st = lib.optimizer_update_32bit_clip_noalloc(k, dt, param.data_ptr(), grad.data_ptr(),
+                                                     state1.data_ptr(), _ptr(state2), n, beta1, beta2,
+                                                     beta3, alpha, eps, weight_decay, int(step), lr,
+                                                     int(bool(skip_zeros)), max_unorm,
+                                                     _stream(param, stream))
+    check(st, lib)
+
+
+def clip_noalloc_max_elements() -> int:
+    """Largest tensor ``optimizer_update_32bit_clip_noalloc`` accepts."""
+    return int(load().ou_clip_noalloc_max_elements())
 
 
 def _segments(kind: int, segments) -> ctypes.Array:

@@ -79,6 +79,11 @@ def load(path: str = LIBRARY) -> ctypes.CDLL:
     lib.optimizer_update_32bit_clip.argtypes = [i32, i32, vp, vp, vp, vp, i64, f32, f32, f32, f32,
                                                 f32, f32, i64, f32, i32, f32, vp, i64, vp]
     lib.optimizer_update_32bit_clip.restype = i32
+    lib.optimizer_update_32bit_clip_noalloc.argtypes = [i32, i32, vp, vp, vp, vp, i64, f32, f32, f32,
+                                                        f32, f32, f32, i64, f32, i32, f32, vp]
+    lib.optimizer_update_32bit_clip_noalloc.restype = i32
+    lib.ou_clip_noalloc_max_elements.argtypes = []
+    lib.ou_clip_noalloc_max_elements.restype = i64
     lib.optimizer_update_32bit_multi.argtypes = [i32, ctypes.POINTER(ou_segment), ctypes.c_int32,
                                                  ctypes.POINTER(ou_hparams), vp]
     lib.optimizer_update_32bit_multi.restype = i32

@@ -735,6 +735,156 @@ int check_plan_device(ou_plan_s* plan)
     return OU_OK;
 }
 
+// Workspace of the clipped step: 256 bytes (the factor fl32(lr*s), s at
+// bytes 0-7), then one binary64 pair of partial sums per 2,048-element chunk.
+constexpr int64_t clip_workspace_bytes(int64_t n)
+{
+    return 256 + (n > 0 ? (n + kClipChunkElems - 1) / kClipChunkElems : 0) * 16;
+}
+
+// ---- the static device scratch of optimizer_update_32bit_clip_noalloc -------
+//
+// For callers that cannot allocate device memory: the clipped step's chunk
+// partial norms (16 B per 2,048 elements) and its clip factor (256 B) live
+// in this file-scope device array, 8 MiB + 256 B, enough for 2^30 elements.
+// Every GPU the library runs on holds its own copy until the process ends.
+// In host code `scratch` names a host-side stand-in, never device memory:
+// its device address comes from hipGetSymbolAddress, once per device with
+// that device current, and only that address is passed to kernels.  Calls
+// on one GPU share the array, so calls that overlap in time on one GPU
+// (different streams, or host threads) race.  Nothing in it has to start
+// at zero: pass 1 writes every chunk's partial sums before pass 2 reads
+// them, and pass 2 writes the factor that pass 3 reads.
+constexpr int64_t kScratchMaxElems = int64_t(1) << 30;
+constexpr int64_t kScratchBytes = clip_workspace_bytes(kScratchMaxElems);
+static_assert(kScratchBytes == 256 + (int64_t(16) << 19), "8 MiB + 256 B");
+
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+class ScratchCache {
+public:
+    // Device address of `scratch` on the current device.
+    int current(void** out)
+    {
+        int dev = 0;
+        hipError_t e = hipGetDevice(&dev);
+        if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+        if (dev < 0 || dev >= kMaxDevices) return fail(OU_EUNSUPPORTED, "device id %d", dev);
+        void* p = ptr_[dev].load(std::memory_order_acquire);
+        if (!p) {
+            std::lock_guard<std::mutex> lk(mu_);
+            p = ptr_[dev].load(std::memory_order_relaxed);
+            if (!p) {
+                e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+                if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+                if (!p || reinterpret_cast<uintptr_t>(p) % 256)
+                    return fail(OU_EHIP, "hipGetSymbolAddress(scratch) returned an unaligned address");
+                ptr_[dev].store(p, std::memory_order_release);
+            }
+        }
+        *out = p;
+        return OU_OK;
+    }
+
+private:
+    std::mutex mu_;
+    std::atomic<void*> ptr_[kMaxDevices] = {};
+};
+
+ScratchCache g_scratch;
+
+// The clipped step of one tensor.  With `static_scratch` the chunk partials
+// and the clip factor live in this file's device array `scratch` (tensors
+// of at most kScratchMaxElems elements), otherwise in the caller's
+// workspace.  Nothing here allocates device memory.
+int clip_step(int kind_arg, int dtype, void* param, const void* grad, float* state1, float* state2, int64_t n,
+              float beta1, float beta2, float beta3, float alpha, float eps, float weight_decay, int64_t step,
+              float lr, int skip_zeros, float max_unorm, void* workspace, int64_t workspace_bytes,
+              bool static_scratch, void* stream)
+{
+    if (!std::isfinite(max_unorm) || max_unorm < 0.0f)
+        return fail(OU_EINVAL, "max_unorm must be finite and >= 0 (got %g)", max_unorm);
+    if (max_unorm == 0.0f)
+        return optimizer_update_32bit(kind_arg, dtype, param, grad, state1, state2, n, beta1, beta2,
+                                      beta3, alpha, eps, weight_decay, step, lr, skip_zeros, stream);
+    int kind = 0, after = 0;
+    if (int st = split_kind(kind_arg, &kind, &after)) return st;
+    if (!two_state(kind))
+        return fail(OU_EINVAL, "update-norm clipping is defined for ADAM and ADEMAMIX only");
+    ou_hparams h;
+    h.beta1 = beta1; h.beta2 = beta2; h.beta3 = beta3; h.alpha = alpha; h.eps = eps;
+    h.weight_decay = weight_decay; h.lr = lr; h.skip_zeros = skip_zeros; h.step = step;
+    if (int st = check_hparams(kind, h)) return st;
+    ou_segment s{param, grad, state1, state2, n, dtype, 0};
+    std::vector<Range> ranges;
+    ranges.reserve(5);
+    if (int st = check_segment(kind, s, 0, &ranges)) return st;
+    if (n == 0) return OU_OK;
+    const int64_t need = clip_workspace_bytes(n);
+    if (static_scratch) {
+        if (n > kScratchMaxElems)
+            return fail(OU_EINVAL, "n = %lld exceeds the %lld elements the library's static scratch serves; "
+                        "use optimizer_update_32bit_clip with a workspace", (long long)n,
+                        (long long)kScratchMaxElems);
+    } else {
+        if (!workspace) return fail(OU_EINVAL, "null workspace with max_unorm > 0");
+        if (reinterpret_cast<uintptr_t>(workspace) % 16) return fail(OU_EALIGN, "workspace not 16-byte aligned");
+        if (workspace_bytes < need)
+            return fail(OU_EINVAL, "workspace has %lld bytes, needs %lld", (long long)workspace_bytes, (long long)need);
+        const uintptr_t W = reinterpret_cast<uintptr_t>(workspace);
+        ranges.push_back({W, W + static_cast<uintptr_t>(need), true, 1});
+    }
+    if (int st = check_overlap(ranges)) return st;
+    if (validate_only()) return OU_OK;
+    const DeviceProps* dp = nullptr;
+    if (int st = g_devices.current(&dp)) return st;
+    if (static_scratch) {
+        if (int st = g_scratch.current(&workspace)) return st;
+    }
+
+    bool vec = streams_16b_aligned(kind, s);
+    SingleLaunch L = select_single(*dp, kind, dtype, n, vec, false);
+    L.epl = 4;
+    apply_single_forcing(&L, &vec);
+    L.epl = 4;
+    const void* f1 = clip_kernel(1, kind, dtype, 0);
+    const void* f2 = clip_kernel(2, kind, dtype, 0);
+    const void* f3 = clip_kernel(3, kind, dtype, L.unroll);
+    // pass 3 covers groups of 4 elements
+    const int64_t groups = (n + 3) / 4;
+    const int64_t per_block = static_cast<int64_t>(L.block) * L.unroll;
+    int64_t grid3 = g_force_grid.load() ? L.grid : (groups + per_block - 1) / per_block;
+    grid3 = std::max<int64_t>(1, std::min<int64_t>(grid3, INT32_MAX));
+    if (!f1 || !f2 || !f3 || L.block < kWave || L.block > 1024 || L.block % kWave ||
+        L.lds < 0 || L.lds > dp->lds_per_block)
+        return fail(OU_EINVAL, "no clip kernel for block=%d unroll=%d", L.block, L.unroll);
+    const int64_t chunks = (n + kClipChunkElems - 1) / kClipChunkElems;
+    if (chunks > INT32_MAX) return fail(OU_EINVAL, "tensor too large");
+    StepScalars sc = make_scalars(h, after);
+    int32_t vec_ok = vec ? 1 : 0;
+    float* out = static_cast<float*>(workspace);
+    double2* partials = reinterpret_cast<double2*>(static_cast<unsigned char*>(workspace) + 256);
+    hipStream_t hs = static_cast<hipStream_t>(stream);
+    const void* cp = param;
+    int32_t xcd1 = xcd_log2_for(chunks, xcd_run_forced(kXcdRun));
+    int32_t xcd3 = xcd_log2_for(grid3, xcd_run_forced(kXcdRun));
+    void* a1[] = {&cp, const_cast<void**>(&grad), &state1, &state2, &n, &sc, &vec_ok, &partials, &xcd1};
+    // pass 1 ends in a block barrier: it runs best at full occupancy
+    int lds1 = 0;
+    if (int c = g_force_lds.load()) lds1 = c < 0 ? 0 : c;
+    hipError_t e = launch(f1, chunks, kClipThreadsHost, lds1, a1, hs);
+    if (e != hipSuccess) return hip_fail(e, "launch clip pass 1");
+    float lr_arg = lr;
+    void* a2[] = {&partials, const_cast<int64_t*>(&chunks), &max_unorm, &lr_arg, &out};
+    e = launch(f2, 1, kClipFinalThreadsHost, 0, a2, hs);
+    if (e != hipSuccess) return hip_fail(e, "launch clip pass 2");
+    const float* lr_eff = out;
+    void* a3[] = {&param, const_cast<void**>(&grad), &state1, &state2, &n, &sc, &vec_ok, &lr_eff, &xcd3};
+    e = launch(f3, grid3, L.block, L.lds, a3, hs);
+    if (e != hipSuccess) return hip_fail(e, "launch clip pass 3");
+    return OU_OK;
+}
+
 }  // namespace
 }  // namespace ou
 
@@ -784,11 +934,7 @@ int optimizer_update_32bit(int kind_arg, int dtype, void* param, const void* gra
 }
 
 __attribute__((visibility("default")))
-int64_t ou_clip_workspace_bytes(int64_t n)
-{
-    const int64_t chunks = n > 0 ? (n + kClipChunkElems - 1) / kClipChunkElems : 0;
-    return 256 + chunks * 16;
-}
+int64_t ou_clip_workspace_bytes(int64_t n) { return clip_workspace_bytes(n); }
 
 __attribute__((visibility("default")))
 int optimizer_update_32bit_clip(int kind_arg, int dtype, void* param, const void* grad, float* state1,
@@ -797,78 +943,22 @@ int optimizer_update_32bit_clip(int kind_arg, int dtype, void* param, const void
                                 int skip_zeros, float max_unorm, void* workspace,
                                 int64_t workspace_bytes, void* stream)
 {
-    if (!std::isfinite(max_unorm) || max_unorm < 0.0f)
-        return fail(OU_EINVAL, "max_unorm must be finite and >= 0 (got %g)", max_unorm);
-    if (max_unorm == 0.0f)
-        return optimizer_update_32bit(kind_arg, dtype, param, grad, state1, state2, n, beta1, beta2,
-                                      beta3, alpha, eps, weight_decay, step, lr, skip_zeros, stream);
-    int kind = 0, after = 0;
-    if (int st = split_kind(kind_arg, &kind, &after)) return st;
-    if (!two_state(kind))
-        return fail(OU_EINVAL, "update-norm clipping is defined for ADAM and ADEMAMIX only");
-    ou_hparams h;
-    h.beta1 = beta1; h.beta2 = beta2; h.beta3 = beta3; h.alpha = alpha; h.eps = eps;
-    h.weight_decay = weight_decay; h.lr = lr; h.skip_zeros = skip_zeros; h.step = step;
-    if (int st = check_hparams(kind, h)) return st;
-    ou_segment s{param, grad, state1, state2, n, dtype, 0};
-    std::vector<Range> ranges;
-    ranges.reserve(5);
-    if (int st = check_segment(kind, s, 0, &ranges)) return st;
-    if (n == 0) return OU_OK;
-    const int64_t need = ou_clip_workspace_bytes(n);
-    if (!workspace) return fail(OU_EINVAL, "null workspace with max_unorm > 0");
-    if (reinterpret_cast<uintptr_t>(workspace) % 16) return fail(OU_EALIGN, "workspace not 16-byte aligned");
-    if (workspace_bytes < need)
-        return fail(OU_EINVAL, "workspace has %lld bytes, needs %lld", (long long)workspace_bytes, (long long)need);
-    const uintptr_t W = reinterpret_cast<uintptr_t>(workspace);
-    ranges.push_back({W, W + static_cast<uintptr_t>(need), true, 1});
-    if (int st = check_overlap(ranges)) return st;
-    if (validate_only()) return OU_OK;
-    const DeviceProps* dp = nullptr;
-    if (int st = g_devices.current(&dp)) return st;
-
-    bool vec = streams_16b_aligned(kind, s);
-    SingleLaunch L = select_single(*dp, kind, dtype, n, vec, false);
-    L.epl = 4;
-    apply_single_forcing(&L, &vec);
-    L.epl = 4;
-    const void* f1 = clip_kernel(1, kind, dtype, 0);
-    const void* f2 = clip_kernel(2, kind, dtype, 0);
-    const void* f3 = clip_kernel(3, kind, dtype, L.unroll);
-    // pass 3 covers groups of 4 elements
-    const int64_t groups = (n + 3) / 4;
-    const int64_t per_block = static_cast<int64_t>(L.block) * L.unroll;
-    int64_t grid3 = g_force_grid.load() ? L.grid : (groups + per_block - 1) / per_block;
-    grid3 = std::max<int64_t>(1, std::min<int64_t>(grid3, INT32_MAX));
-    if (!f1 || !f2 || !f3 || L.block < kWave || L.block > 1024 || L.block % kWave ||
-        L.lds < 0 || L.lds > dp->lds_per_block)
-        return fail(OU_EINVAL, "no clip kernel for block=%d unroll=%d", L.block, L.unroll);
-    const int64_t chunks = (n + kClipChunkElems - 1) / kClipChunkElems;
-    if (chunks > INT32_MAX) return fail(OU_EINVAL, "tensor too large");
-    StepScalars sc = make_scalars(h, after);
-    int32_t vec_ok = vec ? 1 : 0;
-    float* out = static_cast<float*>(workspace);
-    double2* partials = reinterpret_cast<double2*>(static_cast<unsigned char*>(workspace) + 256);
-    hipStream_t hs = static_cast<hipStream_t>(stream);
-    const void* cp = param;
-    int32_t xcd1 = xcd_log2_for(chunks, xcd_run_forced(kXcdRun));
-    int32_t xcd3 = xcd_log2_for(grid3, xcd_run_forced(kXcdRun));
-    void* a1[] = {&cp, const_cast<void**>(&grad), &state1, &state2, &n, &sc, &vec_ok, &partials, &xcd1};
-    // pass 1 ends in a block barrier: it runs best at full occupancy
-    int lds1 = 0;
-    if (int c = g_force_lds.load()) lds1 = c < 0 ? 0 : c;
-    hipError_t e = launch(f1, chunks, kClipThreadsHost, lds1, a1, hs);
-    if (e != hipSuccess) return hip_fail(e, "launch clip pass 1");
-    float lr_arg = lr;
-    void* a2[] = {&partials, const_cast<int64_t*>(&chunks), &max_unorm, &lr_arg, &out};
-    e = launch(f2, 1, kClipFinalThreadsHost, 0, a2, hs);
-    if (e != hipSuccess) return hip_fail(e, "launch clip pass 2");
-    const float* lr_eff = out;
-    void* a3[] = {&param, const_cast<void**>(&grad), &state1, &state2, &n, &sc, &vec_ok, &lr_eff, &xcd3};
-    e = launch(f3, grid3, L.block, L.lds, a3, hs);
-    if (e != hipSuccess) return hip_fail(e, "launch clip pass 3");
-    return OU_OK;
+    return clip_step(kind_arg, dtype, param, grad, state1, state2, n, beta1, beta2, beta3, alpha, eps,
+                     weight_decay, step, lr, skip_zeros, max_unorm, workspace, workspace_bytes, false, stream);
 }
+
+__attribute__((visibility("default")))
+int optimizer_update_32bit_clip_noalloc(int kind_arg, int dtype, void* param, const void* grad,
+                                        float* state1, float* state2, int64_t n, float beta1, float beta2,
+                                        float beta3, float alpha, float eps, float weight_decay,
+                                        int64_t step, float lr, int skip_zeros, float max_unorm, void* stream)
+{
+    return clip_step(kind_arg, dtype, param, grad, state1, state2, n, beta1, beta2, beta3, alpha, eps,
+                     weight_decay, step, lr, skip_zeros, max_unorm, nullptr, 0, true, stream);
+}
+
+__attribute__((visibility("default")))
+int64_t ou_clip_noalloc_max_elements(void) { return kScratchMaxElems; }
 
 __attribute__((visibility("default")))
 int optimizer_update_32bit_multi(int kind_arg, const ou_segment* segs, int32_t nseg, const ou_hparams* hp,

@@ -40,7 +40,8 @@ def test_exports_every_header_function(L):
                           "ou_plan_describe", "ou_plan_destroy", "ou_status_string",
                           "ou_last_error", "ou_8bit_qmap", "optimizer_update_8bit_blockwise",
                           "ou_plan8_create", "ou_plan8_step", "ou_plan8_graph_step",
-                          "ou_plan8_destroy"}
+                          "ou_plan8_destroy", "optimizer_update_32bit_clip_noalloc",
+                          "ou_clip_noalloc_max_elements"}
     for n in names:
         assert hasattr(L, n), n
     out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIBRARY], capture_output=True,
@@ -198,6 +199,36 @@ def _clip(L, max_unorm=1.0, ws=0x800000, wsb=None, n=4096, p=0x10000, kind=0, **
     return L.optimizer_update_32bit_clip(kind, 0, p, 0x20000, 0x30000, 0x40000, n, 0.9, 0.999, 0.9999,
                                          5.0, 1e-8, 0.0, kw.get("step", 1), 1e-3, 0, max_unorm,
                                          ws, wsb, None)
+
+
+def _clip_noalloc(L, max_unorm=1.0, n=4096, p=0x10000, kind=0, dtype=0, s2=0x40000):
+    return L.optimizer_update_32bit_clip_noalloc(kind, dtype, p, 0x20000, 0x30000, s2, n, 0.9, 0.999,
+                                                 0.9999, 5.0, 1e-8, 0.0, 1, 1e-3, 0, max_unorm, None)
+
+
+def test_clip_noalloc_validation(L):
+    """The allocation-free clipped step checks what the workspace form
+    checks, minus the workspace, and refuses tensors beyond its static
+    scratch (2^30 elements) before touching a device."""
+    big = 1 << 30
+    assert L.ou_clip_noalloc_max_elements() == big
+    assert _clip_noalloc(L) == OU_OK
+    assert _clip_noalloc(L, n=0) == OU_OK
+    assert _clip_noalloc(L, max_unorm=0.0) == OU_OK
+    assert _clip_noalloc(L, max_unorm=-1.0) == OU_EINVAL
+    assert _clip_noalloc(L, max_unorm=float("nan")) == OU_EINVAL
+    assert _clip_noalloc(L, kind=2) == OU_EINVAL                  # one-state kind with clipping
+    assert _clip_noalloc(L, p=0x10002) == OU_EALIGN
+    assert _clip_noalloc(L, s2=0x10000 + 64) == OU_EOVERLAP       # state2 inside param
+    spread = dict(p=0x10_0000_0000, s2=0x40_0000_0000)
+    args = (0, 0, spread["p"], 0x20_0000_0000, 0x30_0000_0000, spread["s2"])
+    hp = (0.9, 0.999, 0.9999, 5.0, 1e-8, 0.0, 1, 1e-3, 0, 1.0, None)
+    assert L.optimizer_update_32bit_clip_noalloc(*args, big, *hp) == OU_OK
+    assert L.optimizer_update_32bit_clip_noalloc(*args, big + 1, *hp) == OU_EINVAL
+    assert b"static scratch" in L.ou_last_error()
+    # the workspace form has no such limit
+    assert L.optimizer_update_32bit_clip(*args, big + 1, *hp[:-1], 0x50_0000_0000,
+                                         L.ou_clip_workspace_bytes(big + 1), None) == OU_OK
 
 
 def test_clip_entry_validation(L):
