@@ -11,9 +11,10 @@ bit patterns; states as ``float32``.  Every call updates its arguments in
 place, exactly like the product entry points.
 
 ``oracle_update_f32`` is the parity oracle.  ``oracle_update_f64`` exists to
-check the formulas against closed forms.  Parity is pinned for every function
-here (see ``tests/test_oracle_*.py``) except where a docstring says
-"parity unpinned".
+check the formulas against closed forms.  Every exported function is pinned
+to something other than itself by the pins in ``tests/oracle_pins.py``, run
+by ``tests/test_oracle.py``; the readings that no pin can separate (points
+where the page is silent) are listed there as "parity unpinned".
 """
 from __future__ import annotations
 

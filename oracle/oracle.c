@@ -772,13 +772,17 @@ int oracle_qcode(int is_signed, float x)
     return idx;
 }
 
-/* Normalised value of a code. */
+/* Normalised value of a code: the magnitude its index selects, negated
+ * when the signed type's bit 7 is set. */
 float oracle_qvalue(int is_signed, int code)
 {
     float mags[256];
     oracle_qmap(is_signed, mags);
     if (!is_signed) return mags[code & 0xff];
     float v = mags[code & 0x7f];
+#if ORACLE_PLANT == 29
+    return v;                                       /* planted: sign bit ignored */
+#endif
     return (code & 0x80) ? -v : v;
 }
 

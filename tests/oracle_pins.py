@@ -924,6 +924,28 @@ def pin_quantizer_nearest(orc):
                 assert c == (orc.qcode(True, -float(x)) | 0x80), x
 
 
+def pin_qvalue_codes(orc):
+    """The decoder, on all 256 codes of both types: a code's value is the
+    magnitude its index selects in the map, negative when the signed type's
+    bit 7 is set (decoded here from the map and the code layout, not with
+    the oracle's decoder); values rise with the magnitude index; and the
+    quantizer, whose decision-point count shares no code with the decoder,
+    maps every value back to its own code (signed 0x80, minus zero, comes
+    back as +0's code 0)."""
+    for signed in (True, False):
+        codes = np.arange(256, dtype=np.uint8)
+        vals = np.array([orc.qvalue(signed, int(c)) for c in codes], np.float32)
+        want = _deq(orc, codes, np.ones(1, np.float32), signed)
+        assert np.array_equal(vals.view(np.uint32), want.view(np.uint32)), signed
+        mags = vals[:128] if signed else vals
+        assert mags[0] == 0.0 and mags[-1] == 1.0 and np.all(np.diff(mags) > 0), signed
+        if signed:
+            assert np.all(vals[129:] < 0) and np.array_equal(-vals[128:], vals[:128])
+        for c in codes:
+            back = orc.qcode(signed, float(vals[c]))
+            assert back == (0 if (signed and c == 0x80) else c), (signed, int(c), back)
+
+
 def _uniform_block_grads(n, T, storage, gen):
     """Gradients whose magnitude is constant inside each 256-element block
     (drawn per block and step) with a fixed sign per element."""
@@ -1109,7 +1131,8 @@ INDEPENDENT = [pin_closed_form_f64, pin_f32_tracks_f64, pin_first_step_by_hand,
                pin_one_state_torch, pin_one_state_closed_form_f64, pin_one_state_zero_gradient,
                pin_lion_by_hand, pin_decay_after_by_hand, pin_decay_after_closed_form_f64,
                pin_decay_after_invariants, pin_decay_after_clip, pin_qmap_structure,
-               pin_quantizer_nearest, pin_8bit_uniform_blocks_match_32bit, pin_8bit_first_step,
+               pin_quantizer_nearest, pin_qvalue_codes, pin_8bit_uniform_blocks_match_32bit,
+               pin_8bit_first_step,
                pin_8bit_zero_gradient, pin_8bit_block_independence, pin_8bit_tracks_32bit]
 ALL = INDEPENDENT + [pin_exact_emulation, pin_exact_emulation_one_state,
                      pin_exact_emulation_decay_after]
