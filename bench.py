@@ -6,16 +6,19 @@ Headline ("step"): one Adam update (fp32 param/grad/states) of a flat tensor
 of 2^28 elements, inputs resident in HBM.  value = algorithmic bytes
 (28 B/element: read p, g, m, v; write p, m, v) / time per step, in GB/s.
 
-Also measured (same JSON line): the other kinds and storages at 2^28 and
-fp32 Adam at 2^30; a plain device copy as the achievable-bandwidth
-reference; the model-like collection (505 bf16 tensors, AdamW) as an eager
-per-tensor loop, one plan launch and graph replay, its small-tensor subset,
-and the launch floor (a 1-element update); the CPU oracle on the headline
-workload for a bounded number of steps.
+Also measured (same JSON line): the headline traffic's ceilings on the
+headline's own buffers (its reads alone, its writes alone and the
+read/write mix with no arithmetic, several launch shapes each); the other
+kinds and storages at 2^28, Adam and AdEMAMix with fp32 and bf16 storage at
+2^30; a plain device copy; the model-like collection (505 bf16 tensors,
+AdamW) as an eager per-tensor loop, one plan launch and graph replay, its
+small-tensor subsets, the page's direct cells and the launch floors; the
+CPU oracle on the headline workload for a bounded number of steps.
 
 Timing: HIP events on the stream the kernels run on, W untimed warmups, then
-K timed steps between device synchronisations.  Secondary cases report the
-median and p10/p90 of 7 rounds.
+K timed steps between device synchronisations, with an event between steps
+so that every step's time is recorded (step_samples_ms).  Secondary cases
+report the median, p10/p90 and every sample of 7 rounds.
 """
 from __future__ import annotations
 
@@ -135,20 +138,22 @@ def main():
 
     def time_exact(step, steps, warmup):
         """W warmups, then exactly K steps between synchronisations; HIP events
-        on the current stream (where the library launches)."""
+        on the current stream (where the library launches), one before every
+        step and one after the last, so every step's time is recorded as
+        well as the total."""
         for _ in range(warmup):
             step()
         torch.cuda.synchronize()
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
         t0 = time.perf_counter()
-        e0.record()
-        for _ in range(steps):
+        ev[0].record()
+        for i in range(steps):
             step()
-        e1.record()
+            ev[i + 1].record()
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
-        return e0.elapsed_time(e1) / steps, wall / steps * 1e3
+        per_step = [ev[i].elapsed_time(ev[i + 1]) for i in range(steps)]
+        return ev[0].elapsed_time(ev[-1]) / steps, wall / steps * 1e3, per_step
 
     def time_rounds(step, iters, rounds=7, warmup=20):
         """Median, p10, p90 of per-step ms over `rounds` samples of `iters` steps."""
@@ -165,9 +170,10 @@ def main():
             e1.record()
             torch.cuda.synchronize()
             samples.append(e0.elapsed_time(e1) / iters)
-        samples.sort()
-        q = lambda f: samples[min(len(samples) - 1, int(round(f * (len(samples) - 1))))]
-        return {"median_ms": statistics.median(samples), "p10_ms": q(0.1), "p90_ms": q(0.9)}
+        srt = sorted(samples)
+        q = lambda f: srt[min(len(srt) - 1, int(round(f * (len(srt) - 1))))]
+        return {"median_ms": statistics.median(srt), "p10_ms": q(0.1), "p90_ms": q(0.9),
+                "samples_ms": [round(x, 5) for x in samples]}
 
     if args.copy_only:
         src = torch.empty(1 << 28, device=dev).uniform_()
@@ -220,7 +226,7 @@ def main():
                                            eps=hp_head.eps, weight_decay=hp_head.weight_decay,
                                            max_unorm=1e-3, workspace=ws)
         bpe = 40 if (kind, storage) == ("adam", "fp32") else bpe
-    ms, wall_ms = time_exact(stepper, args.steps, args.warmup)
+    ms, wall_ms, step_ms = time_exact(stepper, args.steps, args.warmup)
     gbs = bpe * n / (ms * 1e-3) / 1e9
 
     out = {
@@ -239,6 +245,7 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None},
         "host_wall_ms_per_step": round(wall_ms, 4),
+        "step_samples_ms": [round(x, 5) for x in step_ms],
         "kernel_sources_sha": kernel_sha(),
         "env": {"torch": torch.__version__, "hip": getattr(torch.version, "hip", None),
                 "device": props.name, "arch": getattr(props, "gcnArchName", None),
@@ -254,38 +261,13 @@ def main():
             out["roofline"] = {**alu, "traffic": None}
     probe = None
     if not args.quick and args.case == "adam:fp32:28":
-        # the same traffic in the same launch shape with no arithmetic, on the
-        # same buffers (p, g, m, v read; p, m, v written back unchanged): what
-        # this read/write mix reaches on this device, in this run
-        # in several launch shapes (block, groups per lane, blocks per CU,
-        # XCD run); the best is a measured lower bound on the mix's ceiling
-        lib = ou._lib.load()
-        sh = torch.cuda.current_stream().cuda_stream
-
-        def probe_step():
-            st = lib.ou__stream_probe(head[0].data_ptr(), head[1].data_ptr(), head[2].data_ptr(),
-                                      head[3].data_ptr(), n, sh)
-            if st != 0:
-                raise RuntimeError(lib.ou_last_error().decode())
-        shapes = {"128x4 2/CU run32": (128, 4, 55296, 32), "256x2 2/CU run16": (256, 2, 55296, 16),
-                  "256x2 full run16": (256, 2, -1, 16), "256x1 full run16": (256, 1, -1, 16),
-                  "512x2 2/CU run16": (512, 2, 55296, 16), "256x4 2/CU run32": (256, 4, 55296, 32),
-                  "256x2 2/CU block order": (256, 2, 55296, -1)}
-        probe = {}
-        try:
-            for name, (blk, unr, lds, run) in shapes.items():
-                lib.ou__force_single(blk, 4, unr, 0, 0, lds)
-                lib.ou__force_xcd(run)
-                r = time_rounds(probe_step, iters=10, rounds=5, warmup=5)
-                probe[name] = round(28 * n / (r["median_ms"] * 1e-3) / 1e9, 1)
-        finally:
-            lib.ou__force_single(0, 0, 0, 0, 0, 0)
-            lib.ou__force_xcd(0)
-        best = max(probe, key=probe.get)
-        probe = {"GBps_by_shape": probe, "best_shape": best, "GBps": probe[best],
-                 "what": "4 fp32 streams read, 3 written back unchanged, no arithmetic"}
-        out["roofline"]["stream_probe_GBps"] = probe["GBps"]
-        out["roofline"]["frac_of_stream_probe"] = round(gbs / probe["GBps"], 4)
+        probe = bandwidth_ceilings(torch, ou, head, n, time_rounds)
+        out["roofline"]["stream_probe_GBps"] = probe["mix_4r3w"]["GBps"]
+        out["roofline"]["frac_of_stream_probe"] = round(gbs / probe["mix_4r3w"]["GBps"], 4)
+        out["roofline"]["read_only_GBps"] = probe["read_4"]["GBps"]
+        out["roofline"]["write_only_GBps"] = probe["write_3"]["GBps"]
+        out["roofline"]["serial_bound_GBps"] = probe["serial_bound_GBps"]
+        out["roofline"]["frac_of_serial_bound"] = round(gbs / probe["serial_bound_GBps"], 4)
     tr = os.path.join(ROOT, "profiles", "traffic_single_adam_fp32_256M.json")
     if os.path.exists(tr) and args.case == "adam:fp32:28":
         with open(tr) as f:
@@ -303,11 +285,13 @@ def main():
         r = time_rounds(lambda: dst.copy_(src), iters=20)
         cases["copy_fp32_2^28"] = {**r, "GBps": round(2 * 4 * (1 << 28) / (r["median_ms"] * 1e-3) / 1e9, 1)}
         if probe:
-            cases["stream_probe_4r3w_fp32_2^28"] = probe
+            cases["bandwidth_ceilings_fp32_2^28"] = probe
         del src, dst
         torch.cuda.empty_cache()
         for ck, cs, cl in (("adam", "bf16", 28), ("ademamix", "fp32", 28), ("ademamix", "bf16", 28),
-                           ("adam", "fp32", 30), ("lion", "fp32", 28), ("momentum", "bf16", 28),
+                           ("adam", "fp32", 30), ("adam", "bf16", 30), ("ademamix", "fp32", 30),
+                           ("ademamix", "bf16", 30),
+                           ("lion", "fp32", 28), ("momentum", "bf16", 28),
                            ("adam8", "fp32", 28), ("adam8", "bf16", 28), ("ademamix8", "bf16", 28)):
             cn = 1 << cl
             hp = hp_kind[ck.rstrip("8")]
@@ -352,6 +336,68 @@ def main():
     print(json.dumps(out))
 
 
+# LDS per CU of gfx950 (160 KiB): a kernel with no LDS of its own that
+# reserves lds_for(b) bytes of dynamic LDS runs at most b blocks per CU.
+LDS_PER_CU = 160 * 1024
+
+
+def lds_for(blocks_per_cu: int) -> int:
+    if blocks_per_cu <= 0:
+        return -1                      # no cap (the library's "off" value)
+    return (LDS_PER_CU // (blocks_per_cu + 1) + 1024) & ~1023
+
+
+def bandwidth_ceilings(torch, ou, head, n, time_rounds):
+    """What the headline's traffic reaches with no arithmetic, on the
+    headline's own buffers in the same run: its four reads alone, its three
+    writes alone and the 4-read/3-write mix, each in several launch shapes
+    (threads per block x groups per lane, resident blocks per CU, tiles per
+    XCD run); the best shape of each is reported.  The serial bound is the
+    rate if the reads ran at the read-only rate and then the writes at the
+    write-only rate: 28 / (16 / R + 12 / W) B per element."""
+    lib = ou._lib.load()
+    sh = torch.cuda.current_stream().cuda_stream
+    ptrs = [t.data_ptr() for t in head]
+    nvec = n // 4
+    shapes = {"64x2 8/CU run64": (64, 2, 8, 64), "64x2 8/CU run128": (64, 2, 8, 128),
+              "128x2 4/CU run64": (128, 2, 4, 64), "256x2 2/CU run16": (256, 2, 2, 16),
+              "128x4 2/CU run32": (128, 4, 2, 32), "256x2 full run16": (256, 2, 0, 16),
+              "512x2 full run16": (512, 2, 0, 16), "256x4 full block order": (256, 4, 0, -1)}
+    modes = (("read_4", 1, 16), ("mix_4r3w", 0, 28), ("write_3", 2, 12))   # writes last: they clobber
+    res = {}
+    try:
+        for name, mode, bpe in modes:
+            by = {}
+            for sname, (blk, unr, per_cu, run) in shapes.items():
+                lib.ou__force_single(blk, 4, unr, nvec // (blk * unr), 0, lds_for(per_cu))
+                lib.ou__force_xcd(run)
+
+                def step(mode=mode):
+                    st = lib.ou__stream_probe(mode, *ptrs, n, sh)
+                    if st != 0:
+                        raise RuntimeError(lib.ou_last_error().decode())
+                r = time_rounds(step, iters=10, rounds=5, warmup=5)
+                by[sname] = round(bpe * n / (r["median_ms"] * 1e-3) / 1e9, 1)
+            best = max(by, key=by.get)
+            res[name] = {"GBps": by[best], "best_shape": best, "GBps_by_shape": by,
+                         "bytes_per_element": bpe}
+    finally:
+        lib.ou__force_single(0, 0, 0, 0, 0, 0)
+        lib.ou__force_xcd(0)
+    r, w = res["read_4"]["GBps"], res["write_3"]["GBps"]
+    res["serial_bound_GBps"] = round(28 / (16 / r + 12 / w), 1)
+    res["what"] = ("fp32 streams of 2^28 elements: read_4 reads p, g, m, v; write_3 writes p, m, v; "
+                   "mix_4r3w reads four and writes three back; no arithmetic")
+    return res
+
+
+def _us(r: dict) -> dict:
+    """A time_rounds result in microseconds: median, p10, p90 and every sample."""
+    return {"median_us": round(r["median_ms"] * 1e3, 2), "p10_us": round(r["p10_ms"] * 1e3, 2),
+            "p90_us": round(r["p90_ms"] * 1e3, 2),
+            "samples_us": [round(x * 1e3, 2) for x in r["samples_ms"]]}
+
+
 def bench_collection(torch, ou, W, dev, time_rounds):
     """Model-like collection (bf16 AdamW): full step, the subsets of tensors
     of <= 16,384 and <= 4,096 elements, each as per-tensor loop, one plan
@@ -382,8 +428,7 @@ def bench_collection(torch, ou, W, dev, time_rounds):
                          ("graph", lambda: opt.step(graph=True))):
             iters = 5 if mode == "per_tensor_loop" else 50
             r = time_rounds(fn, iters=iters, rounds=7, warmup=5)
-            d[mode] = {k: round(v * 1e3, 2) for k, v in r.items()}   # ms -> us
-            d[mode] = {"median_us": d[mode]["median_ms"], "p10_us": d[mode]["p10_ms"], "p90_us": d[mode]["p90_ms"]}
+            d[mode] = _us(r)
         d["plan_GBps"] = round(bytes_ / (d["plan"]["median_us"] * 1e-6) / 1e9, 1)
         d["plan_describe"] = opt.plan.describe()
         res[label] = d
@@ -407,8 +452,7 @@ def bench_collection(torch, ou, W, dev, time_rounds):
                      ("graph", lambda: opt.step(graph=True))):
         iters = 5 if mode == "per_tensor_loop" else 50
         r = time_rounds(fn, iters=iters, rounds=7, warmup=5)
-        d[mode] = {"median_us": round(r["median_ms"] * 1e3, 2), "p10_us": round(r["p10_ms"] * 1e3, 2),
-                   "p90_us": round(r["p90_ms"] * 1e3, 2)}
+        d[mode] = _us(r)
     d["plans_GBps"] = round(bytes8 / (d["plans"]["median_us"] * 1e-6) / 1e9, 1)
     res["adamw8bit_505"] = d
     opt.close()
@@ -420,8 +464,7 @@ def bench_collection(torch, ou, W, dev, time_rounds):
     for mode, fn in (("per_tensor_loop", opt.step_per_tensor), ("plan", lambda: opt.step())):
         iters = 5 if mode == "per_tensor_loop" else 30
         r = time_rounds(fn, iters=iters, rounds=7, warmup=5)
-        d[mode] = {"median_us": round(r["median_ms"] * 1e3, 2), "p10_us": round(r["p10_ms"] * 1e3, 2),
-                   "p90_us": round(r["p90_ms"] * 1e3, 2)}
+        d[mode] = _us(r)
     d["plan_GBps"] = round(bytes_m / (d["plan"]["median_us"] * 1e-6) / 1e9, 1)
     res["ademamix32_505"] = d
     opt.close()
@@ -449,7 +492,7 @@ def bench_collection(torch, ou, W, dev, time_rounds):
                     st["t"] += 1
                     lib.optimizer_update_32bit(*args, st["t"], 1e-3, 0, stream)
                 r = time_rounds(call, iters=100, rounds=7, warmup=20)
-                cells[f"{kind}_{storage}_{n}"] = round(r["median_ms"] * 1e3, 2)
+                cells[f"{kind}_{storage}_{n}"] = _us(r)
     res["direct_cells_us"] = cells
     # launch floor: a 1-element update through the C ABI, back to back
     one = [torch.zeros(1, device=dev) for _ in range(4)]
@@ -459,7 +502,7 @@ def bench_collection(torch, ou, W, dev, time_rounds):
         t["i"] += 1
         ou.optimizer_update_32bit("adam", one[0], one[1], one[2], one[3], step=t["i"], lr=1e-3)
     r = time_rounds(tiny, iters=200, rounds=7, warmup=50)
-    res["launch_floor_1_element_us"] = round(r["median_ms"] * 1e3, 2)
+    res["launch_floor_1_element_us"] = _us(r)
     # the floors under it: a one-element kernel launched straight through
     # ctypes (the library's test hook that rounds one value to bf16), and the
     # replay of a one-node graph (a plan over one one-element tensor)
@@ -469,7 +512,7 @@ def bench_collection(torch, ou, W, dev, time_rounds):
     def empty_launch():
         lib.ou__narrow(2, one_in.data_ptr(), one_out.data_ptr(), 1, stream)
     r = time_rounds(empty_launch, iters=200, rounds=7, warmup=50)
-    res["launch_floor_bare_kernel_us"] = round(r["median_ms"] * 1e3, 2)
+    res["launch_floor_bare_kernel_us"] = _us(r)
     plan1 = ou.Plan("adam", [tuple(one)])
     hp1 = ou.HParams(lr=1e-3)
     t1 = {"i": 0}
@@ -478,7 +521,7 @@ def bench_collection(torch, ou, W, dev, time_rounds):
         t1["i"] += 1
         plan1.graph_step(hp1, t1["i"])
     r = time_rounds(graph1, iters=100, rounds=7, warmup=20)
-    res["graph_floor_1_node_us"] = round(r["median_ms"] * 1e3, 2)
+    res["graph_floor_1_node_us"] = _us(r)
     plan1.close()
     return res
 

@@ -251,17 +251,27 @@ StepScalars make_scalars(const ou_hparams& h, int decay_after)
 // Single tensor.  Every lane takes UNROLL groups of 4 elements (one
 // dwordx4 of each fp32 stream, dwordx2 of a 16-bit one).  Small tensors (the
 // launch-latency regime) get one block sized to the tensor.  Large ones get
-// one 256-thread block (the plain fp32 Adam update: 128 threads with 4
-// groups per lane) per tile of 2,048 elements, a grid that covers the
-// tensor, and at most two resident blocks per CU (8 waves): measured on
-// MI355X at 2^28 elements, that cap lifts every kind and storage by 6-10%
-// over full occupancy (fp32 Adam 5.9 -> 6.4 TB/s), because fewer tiles in
-// flight keep the seven streams' DRAM accesses more local.  Grid-stride and
-// persistent grids, with or without register double-buffering, were slower.
-// Tiles per XCD run of large single-tensor launches and of plan blocks
-// (measured on MI355X).
-constexpr int kXcdRun = 16;
+// one-wave blocks of 2 groups per lane (a 512-element tile per block), a
+// grid that covers the tensor, at most 8 resident blocks per CU once the
+// grid oversubscribes the CUs 4 times over, and tiles in runs of 64 per XCD.
+// Measured on MI355X in 21 interleaved rounds per case against the earlier
+// shapes (256 x 2 at two blocks per CU and runs of 16; fp32 Adam 128 x 4 and
+// runs of 32): Adam and AdEMAMix, fp32 and bf16 storage, 2^28 and 2^30
+// elements, +2 to +4% in seven of the eight cases and even (-1 to 0%) for
+// fp32 AdEMAMix at 2^30; runs of 128 were as good at 2^28 but 3-6% slower
+// at 2^30.  Capping residency at all (8 waves per CU instead of up to 32)
+// keeps fewer tiles in flight, and the seven streams' DRAM accesses more
+// local: 6-10% over full occupancy.  Grid-stride and persistent grids,
+// with or without register double-buffering, were slower.
+//
+// The clipped step's parameter pass (plain = false: p, m, v read, p
+// written) keeps 256-thread blocks of 2 groups per lane, two blocks per CU
+// and runs of 16.
+constexpr int kXcdRun = 64;
+constexpr int kXcdRunClip = 16;
 constexpr int kXcdRunMulti = 16;
+constexpr int kSingleBlocksPerCu = 8;
+constexpr int kClipBlocksPerCu = 2;
 
 // Tile runs per XCD (xcd_tile): log2 of the run length for grids of at
 // least 64 runs, else -1 (block order).
@@ -281,6 +291,8 @@ int xcd_run_forced(int run)
 
 SingleLaunch select_single(const DeviceProps& d, int kind, int dtype, int64_t n, bool vec, bool plain)
 {
+    (void)kind;
+    (void)dtype;
     SingleLaunch L;
     L.epl = 4;
     L.lds = 0;
@@ -294,27 +306,14 @@ SingleLaunch select_single(const DeviceProps& d, int kind, int dtype, int64_t n,
         if (L.grid < 1) L.grid = 1;
         return L;
     }
-    L.block = 256;
+    L.block = plain ? kWave : 256;
     L.unroll = 2;
-    int run = kXcdRun;
-    // The plain fp32 Adam update of a large tensor (four fp32 streams in,
-    // three out; the grids that get the occupancy cap): the same 2,048-element
-    // tile as 128 threads x 4 groups, in runs of 32 tiles per XCD -- 2.5-3 %
-    // faster at 2^28 on MI355X, measured on three boxes.  Not
-    // for the other kinds: with AdEMAMix's fifth stream four groups per lane
-    // spill, and 16-bit storage runs 10 % slower in that shape; not for the
-    // clip's parameter pass either (10 % slower).
-    const int64_t tiles = (units + 511) / 512;   // both shapes take 512 groups per block
-    if (plain && kind == OU_ADAM && dtype == OU_F32 && d.cu_count > 0 && tiles >= 8LL * d.cu_count) {
-        L.block = 128;
-        L.unroll = 4;
-        run = 32;
-    }
+    const int per_cu = plain ? kSingleBlocksPerCu : kClipBlocksPerCu;
     const int64_t per_block = static_cast<int64_t>(L.block) * L.unroll;
     L.grid = std::max<int64_t>(1, std::min<int64_t>((units + per_block - 1) / per_block, INT32_MAX));
     // cap only when the grid oversubscribes the CUs several times over
-    if (d.cu_count > 0 && L.grid >= 8LL * d.cu_count) L.lds = lds_cap(d, 2);
-    L.xcd_log2 = xcd_log2_for(L.grid, run);
+    if (d.cu_count > 0 && L.grid >= 4LL * per_cu * d.cu_count) L.lds = lds_cap(d, per_cu);
+    L.xcd_log2 = xcd_log2_for(L.grid, plain ? kXcdRun : kXcdRunClip);
     return L;
 }
 
@@ -866,8 +865,8 @@ int clip_step(int kind_arg, int dtype, void* param, const void* grad, float* sta
     double2* partials = reinterpret_cast<double2*>(static_cast<unsigned char*>(workspace) + 256);
     hipStream_t hs = static_cast<hipStream_t>(stream);
     const void* cp = param;
-    int32_t xcd1 = xcd_log2_for(chunks, xcd_run_forced(kXcdRun));
-    int32_t xcd3 = xcd_log2_for(grid3, xcd_run_forced(kXcdRun));
+    int32_t xcd1 = xcd_log2_for(chunks, xcd_run_forced(kXcdRunClip));
+    int32_t xcd3 = xcd_log2_for(grid3, xcd_run_forced(kXcdRunClip));
     void* a1[] = {&cp, const_cast<void**>(&grad), &state1, &state2, &n, &sc, &vec_ok, &partials, &xcd1};
     // pass 1 ends in a block barrier: it runs best at full occupancy
     int lds1 = 0;
@@ -919,7 +918,7 @@ int optimizer_update_32bit(int kind_arg, int dtype, void* param, const void* gra
     bool vec = streams_16b_aligned(kind, s);
     SingleLaunch L = select_single(*dp, kind, dtype, n, vec, true);
     apply_single_forcing(&L, &vec);
-    const void* fn = single_kernel(kind, dtype, L.epl, L.unroll);
+    const void* fn = single_kernel(kind, dtype, L.epl, L.unroll, L.block);
     if (!fn || L.block < kWave || L.block > 1024 || L.block % kWave || L.grid < 1 || L.grid > INT32_MAX ||
         L.lds < 0 || L.lds > dp->lds_per_block)
         return fail(OU_EINVAL, "no kernel for block=%d epl=%d unroll=%d grid=%lld", L.block, L.epl,
@@ -1195,9 +1194,10 @@ int ou__sqrt(const float* in, float* out, int64_t n, void* stream)
 }
 
 __attribute__((visibility("default")))
-int ou__stream_probe(float* p, const float* g, float* s1, float* s2, int64_t n, void* stream)
+int ou__stream_probe(int mode, float* p, const float* g, float* s1, float* s2, int64_t n, void* stream)
 {
-    if (!p || !g || !s1 || !s2 || n <= 0 || n % 4) return fail(OU_EINVAL, "stream probe: bad arguments");
+    if (mode < 0 || mode > 2 || !p || !g || !s1 || !s2 || n <= 0 || n % 4)
+        return fail(OU_EINVAL, "stream probe: bad arguments");
     const uintptr_t a = reinterpret_cast<uintptr_t>(p) | reinterpret_cast<uintptr_t>(g) |
                         reinterpret_cast<uintptr_t>(s1) | reinterpret_cast<uintptr_t>(s2);
     if (a % 16) return fail(OU_EALIGN, "stream probe: buffers must be 16-byte aligned");
@@ -1207,7 +1207,7 @@ int ou__stream_probe(float* p, const float* g, float* s1, float* s2, int64_t n, 
     bool vec = true;
     SingleLaunch L = select_single(*dp, OU_ADAM, OU_F32, n, vec, true);
     apply_single_forcing(&L, &vec);
-    const void* fn = stream_probe_kernel(L.unroll);
+    const void* fn = stream_probe_kernel(mode, L.unroll);
     if (!fn || L.epl != 4 || !vec || L.block < kWave || L.block > 1024 || L.block % kWave ||
         L.grid < 1 || L.grid > INT32_MAX || L.lds < 0 || L.lds > dp->lds_per_block)
         return fail(OU_EINVAL, "stream probe: no kernel for this shape");

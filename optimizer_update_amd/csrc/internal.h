@@ -60,9 +60,9 @@ struct DeviceProps {
 // `blocks` resident blocks per CU (0 when the device does not say).
 int lds_cap(const DeviceProps& d, int blocks);
 
-// Kernel entry for the single-tensor streaming kernel (nullptr if the
-// combination is not instantiated).
-const void* single_kernel(int kind, int dtype, int epl, int unroll);
+// Kernel entry for the single-tensor streaming kernel launched with `block`
+// threads (nullptr if the combination is not instantiated).
+const void* single_kernel(int kind, int dtype, int epl, int unroll, int block);
 // Kernel entry for the multi-tensor kernel.
 const void* multi_kernel(int kind, int dtype, int epl, int unroll);
 // Kernels of update-norm clipping: pass 1 (moments and chunk partial
@@ -70,8 +70,10 @@ const void* multi_kernel(int kind, int dtype, int epl, int unroll);
 // 11, 12, 13: the same passes over a plan's collection.
 const void* clip_kernel(int pass, int kind, int dtype, int unroll);
 
-// Bandwidth probe with the plain fp32 Adam update's traffic (test hook).
-const void* stream_probe_kernel(int unroll);
+// Bandwidth probes (test hook): mode 0 the plain fp32 Adam update's
+// traffic (4 fp32 streams read, 3 written), mode 1 its reads alone, mode 2
+// its writes alone.
+const void* stream_probe_kernel(int mode, int unroll);
 
 // The update kernels' storage rounding alone, dtype OU_F16 or OU_BF16, one
 // value at a time or by packed pairs (test hook).

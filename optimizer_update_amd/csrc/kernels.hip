@@ -165,8 +165,14 @@ struct Group {
 // ---- single tensor ------------------------------------------------------------
 
 
-template <int KIND, typename S, int EPL, int U>
-__global__ void __launch_bounds__(1024)
+// MAXT is the largest block the instantiation accepts.  With four groups
+// per lane in flight AdEMAMix's five fp32 streams need more than the 128
+// VGPRs a lane may hold under a 1024-thread bound (it spills), so the
+// four-group shapes of at most 256 threads have a 256-thread instantiation
+// of their own; larger blocks take the 1024-thread one.  The arithmetic is
+// the same inline update_element in both.
+template <int KIND, typename S, int EPL, int U, int MAXT>
+__global__ void __launch_bounds__(MAXT)
 k_single(typename S::raw* __restrict__ p, const typename S::raw* __restrict__ g,
          float* __restrict__ s1, float* __restrict__ s2, int64_t n, StepScalars sc,
          int32_t vec_ok, int32_t xcd_log2)
@@ -607,12 +613,14 @@ k_clip_apply_multi(const SegDesc* __restrict__ segs, const WorkItem* __restrict_
 // ---- instantiation tables ---------------------------------------------------------
 
 template <int KIND, typename S, int EPL>
-const void* pick_single(int unroll)
+const void* pick_single(int unroll, int block)
 {
     switch (unroll) {
-    case 1: return reinterpret_cast<const void*>(&k_single<KIND, S, EPL, 1>);
-    case 2: return reinterpret_cast<const void*>(&k_single<KIND, S, EPL, 2>);
-    case 4: return reinterpret_cast<const void*>(&k_single<KIND, S, EPL, 4>);
+    case 1: return reinterpret_cast<const void*>(&k_single<KIND, S, EPL, 1, 1024>);
+    case 2: return reinterpret_cast<const void*>(&k_single<KIND, S, EPL, 2, 1024>);
+    case 4:
+        return block <= 256 ? reinterpret_cast<const void*>(&k_single<KIND, S, EPL, 4, 256>)
+                            : reinterpret_cast<const void*>(&k_single<KIND, S, EPL, 4, 1024>);
     default: return nullptr;
     }
 }
@@ -629,35 +637,35 @@ const void* pick_multi(int unroll)
 }
 
 template <int KIND, typename S>
-const void* pick(bool multi, int epl, int unroll)
+const void* pick(bool multi, int epl, int unroll, int block)
 {
-    if (epl == 4) return multi ? pick_multi<KIND, S, 4>(unroll) : pick_single<KIND, S, 4>(unroll);
+    if (epl == 4) return multi ? pick_multi<KIND, S, 4>(unroll) : pick_single<KIND, S, 4>(unroll, block);
     if constexpr (kTwoState<KIND>) {   // 8 elements per lane only for the two-state kinds
-        if (epl == 8) return multi ? pick_multi<KIND, S, 8>(unroll) : pick_single<KIND, S, 8>(unroll);
+        if (epl == 8) return multi ? pick_multi<KIND, S, 8>(unroll) : pick_single<KIND, S, 8>(unroll, block);
     }
     return nullptr;
 }
 
 template <int KIND>
-const void* pick_dtype(bool multi, int dtype, int epl, int unroll)
+const void* pick_dtype(bool multi, int dtype, int epl, int unroll, int block)
 {
     switch (dtype) {
-    case 0: return pick<KIND, F32>(multi, epl, unroll);
-    case 1: return pick<KIND, F16>(multi, epl, unroll);
-    case 2: return pick<KIND, BF16>(multi, epl, unroll);
+    case 0: return pick<KIND, F32>(multi, epl, unroll, block);
+    case 1: return pick<KIND, F16>(multi, epl, unroll, block);
+    case 2: return pick<KIND, BF16>(multi, epl, unroll, block);
     default: return nullptr;
     }
 }
 
-const void* pick_all(bool multi, int kind, int dtype, int epl, int unroll)
+const void* pick_all(bool multi, int kind, int dtype, int epl, int unroll, int block)
 {
     switch (kind) {
-    case kAdam: return pick_dtype<kAdam>(multi, dtype, epl, unroll);
-    case kAdemamix: return pick_dtype<kAdemamix>(multi, dtype, epl, unroll);
-    case kMomentum: return pick_dtype<kMomentum>(multi, dtype, epl, unroll);
-    case kRmsprop: return pick_dtype<kRmsprop>(multi, dtype, epl, unroll);
-    case kAdagrad: return pick_dtype<kAdagrad>(multi, dtype, epl, unroll);
-    case kLion: return pick_dtype<kLion>(multi, dtype, epl, unroll);
+    case kAdam: return pick_dtype<kAdam>(multi, dtype, epl, unroll, block);
+    case kAdemamix: return pick_dtype<kAdemamix>(multi, dtype, epl, unroll, block);
+    case kMomentum: return pick_dtype<kMomentum>(multi, dtype, epl, unroll, block);
+    case kRmsprop: return pick_dtype<kRmsprop>(multi, dtype, epl, unroll, block);
+    case kAdagrad: return pick_dtype<kAdagrad>(multi, dtype, epl, unroll, block);
+    case kLion: return pick_dtype<kLion>(multi, dtype, epl, unroll, block);
     default: return nullptr;
     }
 }
@@ -700,15 +708,23 @@ const void* clip_kernel(int pass, int kind, int dtype, int unroll)
 
 namespace {
 
-// ---- bandwidth probe (test hook) ------------------------------------------------
+// ---- bandwidth probes (test hook) -----------------------------------------------
 
-// The plain fp32 Adam update's traffic with no arithmetic: four fp32 streams
-// read, three written back, in k_single's tiles, groups, non-temporal
-// accesses and XCD runs.  Each stored value is the loaded one xor (g & mask)
-// with mask = 0 from the host: the gradient is really read, no store can be
-// dropped as rewriting the loaded value, and every value written equals the
-// one read.  It measures what this read/write mix reaches on the device.
-template <int U>
+// The plain fp32 Adam update's traffic with no arithmetic, in k_single's
+// tiles, groups, non-temporal accesses and XCD runs, and its two halves:
+//   MODE 0: four fp32 streams read (p, g, m, v), three written back (p, m,
+//           v).  Each stored value is the loaded one xor (g & mask), mask = 0
+//           from the host: the gradient is really read, no store can be
+//           dropped as rewriting the loaded value, and every value written
+//           equals the one read.
+//   MODE 1: the four reads alone.  The xor of everything read is stored only
+//           if it matches a pattern under the runtime mask (never, with
+//           mask = 0), so no load can be dropped and nothing is written.
+//   MODE 2: the three writes alone: p, m, v receive a value formed from the
+//           runtime mask and the index (their contents are destroyed).
+// They measure what this read/write mix, its reads and its writes reach on
+// the device.
+template <int MODE, int U>
 __global__ void __launch_bounds__(1024)
 k_stream_probe(float* __restrict__ p, const float* __restrict__ g, float* __restrict__ s1,
                float* __restrict__ s2, int64_t nvec, uint32_t mask, int32_t xcd_log2)
@@ -716,32 +732,53 @@ k_stream_probe(float* __restrict__ p, const float* __restrict__ g, float* __rest
     const int64_t bdim = blockDim.x;
     const int64_t nthreads = static_cast<int64_t>(gridDim.x) * bdim;
     const int64_t bid = xcd_tile(blockIdx.x, gridDim.x, xcd_log2);
+    uint32_t acc = 0;
     for (int64_t base = bid * bdim * U + threadIdx.x; base < nvec; base += nthreads * U) {
         Words<4> wp[U], wg[U], wm[U], wv[U];
+        if constexpr (MODE != 2) {
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int64_t vi = base + u * bdim;
-            if (vi >= nvec) continue;
-            wp[u] = load_words<4>(p + 4 * vi);
-            wg[u] = load_words<4>(g + 4 * vi);
-            wm[u] = load_words<4>(s1 + 4 * vi);
-            wv[u] = load_words<4>(s2 + 4 * vi);
-        }
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int64_t vi = base + u * bdim;
-            if (vi >= nvec) continue;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {   // every stored value depends on the mask
-                const uint32_t x = wg[u].w[j] & mask;
-                wp[u].w[j] ^= x;
-                wm[u].w[j] ^= x;
-                wv[u].w[j] ^= x;
+            for (int u = 0; u < U; ++u) {
+                const int64_t vi = base + u * bdim;
+                if (vi >= nvec) continue;
+                wp[u] = load_words<4>(p + 4 * vi);
+                wg[u] = load_words<4>(g + 4 * vi);
+                wm[u] = load_words<4>(s1 + 4 * vi);
+                wv[u] = load_words<4>(s2 + 4 * vi);
             }
-            store_words<4>(p + 4 * vi, wp[u]);
-            store_words<4>(s1 + 4 * vi, wm[u]);
-            store_words<4>(s2 + 4 * vi, wv[u]);
         }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int64_t vi = base + u * bdim;
+            if (vi >= nvec) continue;
+            if constexpr (MODE == 1) {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) acc ^= wp[u].w[j] ^ wg[u].w[j] ^ wm[u].w[j] ^ wv[u].w[j];
+            } else {
+                if constexpr (MODE == 2) {
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const uint32_t x = mask ^ static_cast<uint32_t>(4 * vi + j);
+                        wp[u].w[j] = x;
+                        wm[u].w[j] = x;
+                        wv[u].w[j] = x;
+                    }
+                } else {
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {   // every stored value depends on the mask
+                        const uint32_t x = wg[u].w[j] & mask;
+                        wp[u].w[j] ^= x;
+                        wm[u].w[j] ^= x;
+                        wv[u].w[j] ^= x;
+                    }
+                }
+                store_words<4>(p + 4 * vi, wp[u]);
+                store_words<4>(s1 + 4 * vi, wm[u]);
+                store_words<4>(s2 + 4 * vi, wv[u]);
+            }
+        }
+    }
+    if constexpr (MODE == 1) {
+        if (mask != 0 && (acc & mask) == 0x9e3779b9u) p[0] = static_cast<float>(acc);
     }
 }
 
@@ -792,24 +829,35 @@ const void* narrow_kernel(int dtype, bool pairs)
     return nullptr;
 }
 
-const void* stream_probe_kernel(int unroll)
+template <int MODE>
+const void* pick_probe(int unroll)
 {
     switch (unroll) {
-    case 1: return reinterpret_cast<const void*>(&k_stream_probe<1>);
-    case 2: return reinterpret_cast<const void*>(&k_stream_probe<2>);
-    case 4: return reinterpret_cast<const void*>(&k_stream_probe<4>);
+    case 1: return reinterpret_cast<const void*>(&k_stream_probe<MODE, 1>);
+    case 2: return reinterpret_cast<const void*>(&k_stream_probe<MODE, 2>);
+    case 4: return reinterpret_cast<const void*>(&k_stream_probe<MODE, 4>);
     default: return nullptr;
     }
 }
 
-const void* single_kernel(int kind, int dtype, int epl, int unroll)
+const void* stream_probe_kernel(int mode, int unroll)
 {
-    return pick_all(false, kind, dtype, epl, unroll);
+    switch (mode) {
+    case 0: return pick_probe<0>(unroll);
+    case 1: return pick_probe<1>(unroll);
+    case 2: return pick_probe<2>(unroll);
+    default: return nullptr;
+    }
+}
+
+const void* single_kernel(int kind, int dtype, int epl, int unroll, int block)
+{
+    return pick_all(false, kind, dtype, epl, unroll, block);
 }
 
 const void* multi_kernel(int kind, int dtype, int epl, int unroll)
 {
-    return pick_all(true, kind, dtype, epl, unroll);
+    return pick_all(true, kind, dtype, epl, unroll, 0);
 }
 
 }  // namespace ou

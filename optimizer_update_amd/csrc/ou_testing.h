@@ -51,11 +51,14 @@ int ou__sqrt(const float* in, float* out, int64_t n, void* stream);
 // and NaN are outside its domain and give 0).  Asynchronous on `stream`.
 int ou__recip8(const float* in, float* out, int64_t n, void* stream);
 
-// Bandwidth probe: the traffic of the plain fp32 Adam update of n elements
-// (p, g, s1, s2 read; p, s1, s2 written back unchanged) in the same launch
-// shape, with no arithmetic; n a multiple of 4, buffers 16-byte aligned.
-// Asynchronous on `stream`.  For measuring what the read/write mix reaches.
-int ou__stream_probe(float* p, const float* g, float* s1, float* s2, int64_t n, void* stream);
+// Bandwidth probes in the launch shape of the plain fp32 Adam update of n
+// elements, with no arithmetic; n a multiple of 4, buffers 16-byte aligned.
+// mode 0: its traffic (p, g, s1, s2 read; p, s1, s2 written back
+// unchanged); mode 1: the four reads alone (nothing written); mode 2: the
+// three writes alone (p, s1, s2 overwritten with a pattern).  Asynchronous
+// on `stream`.  For measuring what the read/write mix, its reads and its
+// writes reach.
+int ou__stream_probe(int mode, float* p, const float* g, float* s1, float* s2, int64_t n, void* stream);
 
 // While on != 0, every entry point returns OU_OK right after its argument
 // checks, before it queries or touches a device: no launch, no allocation

@@ -38,7 +38,8 @@ class _Collection:
     def __init__(self, params, hp: HParams, grads=None, max_unorm: float = 0.0,
                  decay_after: bool = False):
         params = list(params)
-        self.params, self.grads, self._sources = _params_and_grads(params, grads)
+        self.params, self.grads, sources = _params_and_grads(params, grads)
+        self._followed = _followed(sources)
         self.hp = hp
         self.decay_after = bool(decay_after)
         two = _kind(self.kind) in TWO_STATE
@@ -62,7 +63,7 @@ class _Collection:
 
     def _sync_grads(self) -> None:
         """Rebuild the plan if a parameter's .grad is no longer the captured tensor."""
-        if _grads_moved(self._sources, self.grads):
+        if self._followed and _grads_moved(self._followed, self.grads):
             self.plan.close()
             self.plan = self._build_plan()
             self._direct = None
@@ -71,7 +72,7 @@ class _Collection:
         """Zero the captured gradients in place (the plan keeps its
         addresses; set_to_none is accepted for torch's signature and ignored)."""
         del set_to_none
-        _zero_in_place(self._sources, self.grads)
+        _zero_in_place(self._followed, self.grads)
 
     def segments(self):
         return list(zip(self.params, self.grads, self.state1, self.state2))
@@ -233,14 +234,18 @@ def _params_and_grads(params, grads):
     return ps, gs, sources
 
 
-def _grads_moved(sources, grads) -> bool:
+def _followed(sources) -> list:
+    """(index, Parameter) of the parameters whose .grad the optimizer follows."""
+    return [(i, src) for i, src in enumerate(sources) if src is not None]
+
+
+def _grads_moved(followed, grads) -> bool:
     """True (and grads updated) if a followed Parameter's .grad is a tensor
     at another address than the captured one; raises if it is None.  The
-    same address (the allocator handed the memory back) needs no rebuild."""
+    same address (the allocator handed the memory back) needs no rebuild.
+    Gradients given explicitly are not followed and cost nothing here."""
     moved = False
-    for i, src in enumerate(sources):
-        if src is None:
-            continue
+    for i, src in followed:
         g = src.grad
         if g is grads[i]:
             continue
@@ -256,9 +261,9 @@ def _grads_moved(sources, grads) -> bool:
     return moved
 
 
-def _zero_in_place(sources, grads) -> None:
-    for i, src in enumerate(sources):
-        if src is not None and src.grad is not None and src.grad is not grads[i]:
+def _zero_in_place(followed, grads) -> None:
+    for i, src in followed:
+        if src.grad is not None and src.grad is not grads[i]:
             src.grad.zero_()
     torch._foreach_zero_(list(grads))
 
@@ -272,7 +277,8 @@ class _Collection8:
 
     def __init__(self, params, hp: HParams, grads=None, min_8bit_size: int = 4096,
                  decay_after: bool = False):
-        self.params, self.grads, self._sources = _params_and_grads(params, grads)
+        self.params, self.grads, sources = _params_and_grads(params, grads)
+        self._followed = _followed(sources)
         self.hp = hp
         self.min_8bit_size = int(min_8bit_size)
         self.decay_after = bool(decay_after)
@@ -302,7 +308,7 @@ class _Collection8:
 
     def _sync_grads(self) -> None:
         """Rebuild the plans if a parameter's .grad is no longer the captured tensor."""
-        if _grads_moved(self._sources, self.grads):
+        if self._followed and _grads_moved(self._followed, self.grads):
             self.close()
             self._build_plans()
 
@@ -310,7 +316,7 @@ class _Collection8:
         """Zero the captured gradients in place (the plans keep their
         addresses; set_to_none is accepted for torch's signature and ignored)."""
         del set_to_none
-        _zero_in_place(self._sources, self.grads)
+        _zero_in_place(self._followed, self.grads)
 
     @torch.no_grad()
     def step(self, graph: bool = False, stream=None) -> None:

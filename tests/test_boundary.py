@@ -265,9 +265,9 @@ def test_status_strings(L):
 def test_dispatch_with_mocked_device(L, cu, lds_cu, lds_blk):
     """Launch selection from fabricated device properties: the grid covers
     the tensor, blocks are whole waves, small tensors get one block, the
-    occupancy cap reserves LDS so that exactly two blocks fit per CU (or none
-    when the device reports no LDS size), and the choice depends only on the
-    arguments."""
+    occupancy cap of grids that oversubscribe the CUs reserves LDS so that
+    exactly eight one-wave blocks fit per CU (or none when the device
+    reports no LDS size), and the choice depends only on the arguments."""
     out = (ctypes.c_int64 * 5)()
     for n in (1, 2, 31, 64, 255, 256, 1023, 1024, 1025, 4095, 4096, 4097, 65539, 1 << 20,
               (1 << 28) + 3, 1 << 30):
@@ -284,8 +284,9 @@ def test_dispatch_with_mocked_device(L, cu, lds_cu, lds_blk):
                 if units <= 1024:
                     assert grid * block >= units and grid <= 16 and lds == 0
                 if lds:
-                    assert 2 * lds <= lds_cu < 3 * lds and lds <= lds_blk and grid >= 8 * cu
-                elif lds_cu and grid >= 8 * cu:
+                    assert 8 * lds <= lds_cu < 9 * lds and lds <= lds_blk and grid >= 32 * cu
+                    assert block == 64
+                elif lds_cu and grid >= 32 * cu:
                     raise AssertionError("large grids get the occupancy cap")
                 again = (ctypes.c_int64 * 5)()
                 L.ou__select_single(cu, lds_cu, lds_blk, 0, dtype, n, aligned, again)
@@ -434,11 +435,13 @@ def test_step_constant_division_exhaustive(tmp_path):
 
 def test_stream_probe_validation(L):
     """The bandwidth probe's argument checks (test hook)."""
-    assert L.ou__stream_probe(0x10000, 0x20000, 0x30000, 0x40000, 1 << 20, None) == OU_OK
-    assert L.ou__stream_probe(0x10000, 0x20000, 0x30000, 0x40000, 6, None) == OU_EINVAL
-    assert L.ou__stream_probe(0x10000, 0x20000, 0x30000, 0x40000, 0, None) == OU_EINVAL
-    assert L.ou__stream_probe(0, 0x20000, 0x30000, 0x40000, 16, None) == OU_EINVAL
-    assert L.ou__stream_probe(0x10004, 0x20000, 0x30000, 0x40000, 16, None) == OU_EALIGN
+    for mode in (0, 1, 2):
+        assert L.ou__stream_probe(mode, 0x10000, 0x20000, 0x30000, 0x40000, 1 << 20, None) == OU_OK
+        assert L.ou__stream_probe(mode, 0x10000, 0x20000, 0x30000, 0x40000, 6, None) == OU_EINVAL
+        assert L.ou__stream_probe(mode, 0x10000, 0x20000, 0x30000, 0x40000, 0, None) == OU_EINVAL
+        assert L.ou__stream_probe(mode, 0, 0x20000, 0x30000, 0x40000, 16, None) == OU_EINVAL
+        assert L.ou__stream_probe(mode, 0x10004, 0x20000, 0x30000, 0x40000, 16, None) == OU_EALIGN
+    assert L.ou__stream_probe(3, 0x10000, 0x20000, 0x30000, 0x40000, 16, None) == OU_EINVAL
 
 
 def test_narrow_hook_validation(L):

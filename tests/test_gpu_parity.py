@@ -317,19 +317,32 @@ def test_xcd_tile_runs_bitwise(orc, L, kind, storage):
                 assert a.tobytes() == b_.tobytes(), f"plan run {run} differs in {name}"
 
 
-def test_stream_probe_leaves_buffers_unchanged(L):
-    """The bandwidth probe reads four streams and writes three back: every
-    buffer keeps its bits (the sizes put it on the large-tensor shape, with
-    XCD runs and a partial last run)."""
+def test_stream_probes_touch_what_they_say(L):
+    """The bandwidth probes on the large-tensor shape (XCD runs and a partial
+    last run): the mix reads four streams and writes three back, so every
+    buffer keeps its bits; the read probe writes nothing; the write probe
+    fills p, s1 and s2 with its pattern (mask 0: element i holds the bits of
+    i) and leaves g alone."""
     n = (1 << 22) + 4 * 1000
     gen = W.rng(0, 9, n)
     host = [gen.standard_normal(n).astype(np.float32) for _ in range(4)]
     dev = [torch.from_numpy(h).cuda() for h in host]
-    st = L.ou__stream_probe(*(d.data_ptr() for d in dev), n, H.stream_handle())
+    for mode in (0, 1):
+        st = L.ou__stream_probe(mode, *(d.data_ptr() for d in dev), n, H.stream_handle())
+        assert st == 0, H.last_error(L)
+        torch.cuda.synchronize()
+        for h, d in zip(host, dev):
+            assert d.cpu().numpy().tobytes() == h.tobytes(), mode
+    st = L.ou__stream_probe(2, *(d.data_ptr() for d in dev), n, H.stream_handle())
     assert st == 0, H.last_error(L)
     torch.cuda.synchronize()
-    for h, d in zip(host, dev):
-        assert d.cpu().numpy().tobytes() == h.tobytes()
+    pattern = np.arange(n, dtype=np.uint32)
+    for i, (h, d) in enumerate(zip(host, dev)):
+        got = d.cpu().numpy()
+        if i == 1:
+            assert got.tobytes() == h.tobytes()
+        else:
+            assert np.array_equal(got.view(np.uint32), pattern), i
 
 
 # ----------------------------------------------------------------- sentinel

@@ -65,7 +65,7 @@ def _check_sample(orc, kind, storage, n, p0, g0, got, idx, hp, steps):
 
 @pytest.mark.parametrize("kind,storage,log2n", [
     ("adam", "fp32", 28), ("adam", "bf16", 28), ("ademamix", "fp32", 28), ("ademamix", "bf16", 28),
-    ("adam", "fp32", 30), ("ademamix", "bf16", 30)])
+    ("adam", "fp32", 30), ("adam", "bf16", 30), ("ademamix", "fp32", 30), ("ademamix", "bf16", 30)])
 def test_flat_tensor_100_steps(orc, kind, storage, log2n):
     """A single flat tensor, grads N(0, 1e-3^2) fixed, 100 steps through the
     direct entry (the benchmark's launch shape), sampled against the oracle."""
