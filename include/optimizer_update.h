@@ -317,6 +317,26 @@ int ou_plan8_graph_step(ou_plan8 plan, const ou_hparams* hp, void* stream);
 
 void ou_plan8_destroy(ou_plan8 plan);
 
+/* ---- one graph over several plans ----------------------------------------
+ *
+ * The page's AdamW8bit collections (sections "Problem" and "B300 benchmark
+ * and acceptance") step two plans per optimizer step: the tensors of at
+ * least min_8bit_size elements through an 8-bit plan, the others through a
+ * 32-bit plan.  An ou_graph replays the plain steps of any set of plans on
+ * one device as a single HIP graph: built and instantiated on the first
+ * ou_graph_step, later steps write the step's scalars (per plan, with its
+ * own kind and decay order) into the kernel nodes and replay.  The launches
+ * run in one chain, the 32-bit plans in the order given, then the 8-bit
+ * ones; results are bitwise those of ou_plan_step / ou_plan8_step on each
+ * plan.  The plans must outlive the graph (destroy the graph first) and are
+ * not copied.  ou_graph_step is not allowed while `stream` is being
+ * captured; hp must be valid for every plan's kind. */
+typedef struct ou_graph_s* ou_graph;
+int ou_graph_create(const ou_plan* plans, int32_t nplans, const ou_plan8* plans8, int32_t nplans8,
+                    ou_graph* out);
+int ou_graph_step(ou_graph graph, const ou_hparams* hp, void* stream);
+void ou_graph_destroy(ou_graph graph);
+
 const char* ou_status_string(int status);
 const char* ou_last_error(void);
 

@@ -98,6 +98,13 @@ def _raw_stream(index: int) -> int:
     return torch.cuda.current_stream(index).cuda_stream
 
 
+_GET_DEVICE = getattr(torch._C, "_cuda_getDevice", None) or torch.cuda.current_device
+
+
+def _stream_arg(stream) -> int:
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
 def _on(index: int, fn, *args):
     """fn(*args) with device `index` current, switching only when it is not."""
     prev = torch.cuda.current_device()
@@ -306,11 +313,20 @@ class Plan:
             check(self._lib.ou_plan_create(self.kind, arr, len(self._tensors), ctypes.byref(h)),
                   self._lib)
         self._h = h
+        self._index = self.device.index
 
     def step(self, hp: HParams, step: int, stream=None) -> None:
+        """One step (``ou_plan_step``): the per-step path of a collection,
+        kept to a few attribute lookups and one call into the library when
+        the plan's device is current."""
         c = hp.c(step)
-        check(_on(self.device.index, self._lib.ou_plan_step, self._h, c,
-                  self._stream(stream)), self._lib)
+        idx = self._index
+        sh = _raw_stream(idx) if stream is None else _stream_arg(stream)
+        fn = self._lib.ou_plan_step
+        h = self._h.value
+        st = fn(h, c, sh) if _GET_DEVICE() == idx else _on(idx, fn, h, c, sh)
+        if st:
+            check(st, self._lib)
 
     def step_clip(self, hp: HParams, step: int, max_unorm: float, stream=None) -> None:
         """One step with update-norm clipping per tensor (``ou_plan_step_clip``)."""
@@ -452,13 +468,17 @@ class Plan8:
             check(self._lib.ou_plan8_create(self.kind, arr, len(self._tensors), ctypes.byref(h)),
                   self._lib)
         self._h = h
+        self._index = self.device.index
 
     def step(self, hp: HParams, step: int, stream=None) -> None:
         c = hp.c(step)
-        sh = (_raw_stream(self.device.index) if stream is None
-              else (stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)))
-        check(_on(self.device.index, self._lib.ou_plan8_step, self._h, c, sh),
-              self._lib)
+        idx = self._index
+        sh = _raw_stream(idx) if stream is None else _stream_arg(stream)
+        fn = self._lib.ou_plan8_step
+        h = self._h.value
+        st = fn(h, c, sh) if _GET_DEVICE() == idx else _on(idx, fn, h, c, sh)
+        if st:
+            check(st, self._lib)
 
     def graph_step(self, hp: HParams, step: int, stream=None) -> None:
         """The same step replayed from a HIP graph (``ou_plan8_graph_step``)."""
@@ -481,7 +501,48 @@ class Plan8:
             pass
 
 
-__all__ += ["QBLOCK", "qmap", "state8_sizes", "optimizer_update_8bit_blockwise", "Plan8"]
+class Graph:
+    """One HIP graph over the plain steps of several plans (``ou_graph``):
+    32-bit plans, then 8-bit plans, replayed as one chain of launches with
+    each step's scalars written into its nodes.  The plans must stay open
+    until this graph is closed."""
+
+    def __init__(self, plans=(), plans8=()):
+        self._plans = [p for p in plans if p is not None]
+        self._plans8 = [p for p in plans8 if p is not None]
+        every = self._plans + self._plans8
+        self.device = every[0].device if every else torch.device("cuda", torch.cuda.current_device())
+        if any(p.device != self.device for p in every):
+            raise ValueError("all plans of a graph must be on one device")
+        self._lib = load()
+        a = (ctypes.c_void_p * max(1, len(self._plans)))(*[p._h.value for p in self._plans])
+        b = (ctypes.c_void_p * max(1, len(self._plans8)))(*[p._h.value for p in self._plans8])
+        h = ctypes.c_void_p()
+        check(self._lib.ou_graph_create(a, len(self._plans), b, len(self._plans8), ctypes.byref(h)),
+              self._lib)
+        self._h = h
+
+    def step(self, hp: HParams, step: int, stream=None) -> None:
+        c = hp.c(step)
+        sh = (_raw_stream(self.device.index) if stream is None
+              else (stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)))
+        with _on_device(self.device):
+            check(self._lib.ou_graph_step(self._h, ctypes.byref(c), sh), self._lib)
+
+    def close(self) -> None:
+        if getattr(self, "_h", None) is not None and self._h.value:
+            torch.cuda.synchronize(self.device)
+            self._lib.ou_graph_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+__all__ += ["QBLOCK", "qmap", "state8_sizes", "optimizer_update_8bit_blockwise", "Plan8", "Graph"]
 
 from .optim import AdamW32, AdEMAMix32, Adagrad32, Lion32, Momentum32, RMSprop32  # noqa: E402
 from .optim import AdamW8bit, AdEMAMix8bit  # noqa: E402

@@ -119,6 +119,13 @@ def load(path: str = LIBRARY) -> ctypes.CDLL:
     lib.ou_plan8_graph_step.restype = i32
     lib.ou_plan8_destroy.argtypes = [vp]
     lib.ou_plan8_destroy.restype = None
+    lib.ou_graph_create.argtypes = [ctypes.POINTER(vp), ctypes.c_int32, ctypes.POINTER(vp), ctypes.c_int32,
+                                    ctypes.POINTER(vp)]
+    lib.ou_graph_create.restype = i32
+    lib.ou_graph_step.argtypes = [vp, ctypes.POINTER(ou_hparams), vp]
+    lib.ou_graph_step.restype = i32
+    lib.ou_graph_destroy.argtypes = [vp]
+    lib.ou_graph_destroy.restype = None
     lib.ou_status_string.argtypes = [i32]
     lib.ou_status_string.restype = ctypes.c_char_p
     lib.ou_last_error.argtypes = []

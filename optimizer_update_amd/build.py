@@ -17,7 +17,8 @@ CSRC = os.path.join(HERE, "csrc")
 LIBRARY = os.path.join(HERE, "liboptimizer_update.so")
 FAST = os.path.join(HERE, "_fast" + sysconfig.get_config_var("EXT_SUFFIX"))
 SOURCES = [os.path.join(CSRC, "kernels.hip"), os.path.join(CSRC, "host.hip"),
-           os.path.join(CSRC, "kernels8.hip"), os.path.join(CSRC, "host8.hip")]
+           os.path.join(CSRC, "kernels8.hip"), os.path.join(CSRC, "host8.hip"),
+           os.path.join(CSRC, "host_graph.hip")]
 HEADERS = [os.path.join(CSRC, "elem.hpp"), os.path.join(CSRC, "internal.h"),
            os.path.join(CSRC, "host_internal.h"), os.path.join(CSRC, "qmap.hpp"),
            os.path.join(CSRC, "stepdiv.hpp"), os.path.join(CSRC, "ou_testing.h"),

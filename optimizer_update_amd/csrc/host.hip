@@ -265,13 +265,16 @@ StepScalars make_scalars(const ou_hparams& h, int decay_after)
 // with or without register double-buffering, were slower.
 //
 // The clipped step's parameter pass (plain = false: p, m, v read, p
-// written) keeps 256-thread blocks of 2 groups per lane, two blocks per CU
-// and runs of 16.
+// written) takes the same one-wave blocks and runs of 64 with no residency
+// cap, and its moments pass (256-thread blocks, one 2,048-element chunk
+// each, a block barrier at the end) runs of 64 at full occupancy: measured
+// per pass on MI355X at 2^28 (fp32 Adam), passes 1 and 3 take 1,036 and 689
+// us against 1,142 and 698 us with 256-thread blocks at two per CU and runs
+// of 16 (6.16 against 5.76 TB/s for the whole step, over 40 B per element).
 constexpr int kXcdRun = 64;
-constexpr int kXcdRunClip = 16;
+constexpr int kXcdRunClip = 64;
 constexpr int kXcdRunMulti = 16;
 constexpr int kSingleBlocksPerCu = 8;
-constexpr int kClipBlocksPerCu = 2;
 
 // Tile runs per XCD (xcd_tile): log2 of the run length for grids of at
 // least 64 runs, else -1 (block order).
@@ -306,13 +309,13 @@ SingleLaunch select_single(const DeviceProps& d, int kind, int dtype, int64_t n,
         if (L.grid < 1) L.grid = 1;
         return L;
     }
-    L.block = plain ? kWave : 256;
+    L.block = kWave;
     L.unroll = 2;
-    const int per_cu = plain ? kSingleBlocksPerCu : kClipBlocksPerCu;
     const int64_t per_block = static_cast<int64_t>(L.block) * L.unroll;
     L.grid = std::max<int64_t>(1, std::min<int64_t>((units + per_block - 1) / per_block, INT32_MAX));
     // cap only when the grid oversubscribes the CUs several times over
-    if (d.cu_count > 0 && L.grid >= 4LL * per_cu * d.cu_count) L.lds = lds_cap(d, per_cu);
+    if (plain && d.cu_count > 0 && L.grid >= 4LL * kSingleBlocksPerCu * d.cu_count)
+        L.lds = lds_cap(d, kSingleBlocksPerCu);
     L.xcd_log2 = xcd_log2_for(L.grid, plain ? kXcdRun : kXcdRunClip);
     return L;
 }
@@ -321,24 +324,41 @@ SingleLaunch select_single(const DeviceProps& d, int kind, int dtype, int64_t n,
 // work item) is a multiple of 64 * EPL * unroll so chunk starts keep 16-byte
 // alignment.  Large collections get the same cap of two resident blocks per
 // CU as large single tensors.
+// Measured on MI355X in 15 interleaved rounds per shape with the 505-tensor
+// bf16 collection (287.9 M elements) and its 408 tensors of <= 16,384
+// elements (3.4 M): a large collection runs as the large single tensor
+// does, one-wave blocks of 2 groups per lane with one 512-element chunk
+// each, at most 8 per CU, in runs of 64 blocks per XCD (990.6 us, 1% ahead
+// of 4-wave blocks of 1024-element chunks at 2 per CU, and of the 1-wave
+// shape with 1024-element chunks or runs of 32); a collection of small
+// tensors needs short chunks to put enough waves on the GPU: 256-element
+// chunks, one group per lane, 4 waves per block, no cap (13.3 us, 6% ahead
+// of 512-element chunks with 2 groups).  The collection of tensors of
+// <= 4,096 elements takes 4.4-4.6 us in every shape (bound by the launch).
+constexpr int64_t kLargeCollection = int64_t(1) << 24;
+
 MultiLaunch select_multi(const DeviceProps& d, int dtype, int64_t total_elements)
 {
     (void)dtype;
     MultiLaunch L;
-    L.waves = 4;
     L.epl = 4;
-    L.unroll = 2;
-    L.lds = total_elements >= (int64_t(1) << 24) ? lds_cap(d, 2) : 0;
+    if (total_elements >= kLargeCollection) {
+        L.waves = 1;
+        L.unroll = 2;
+        L.lds = lds_cap(d, kSingleBlocksPerCu);
+        L.xcd_run = kXcdRun;
+    } else {
+        L.waves = 4;
+        L.unroll = 1;
+        L.lds = 0;
+        L.xcd_run = kXcdRunMulti;
+    }
     return L;
 }
 
-// Measured on MI355X with the 505-tensor bf16 collection and its 408 small
-// tensors: 1024-element chunks give the best full step (~5.8 TB/s, the work
-// list costs 8 B per 1024 elements), while a collection of small tensors
-// needs 512-element chunks to put enough waves on the GPU (12.6 vs 15.7 us).
 int64_t select_chunk(int64_t total_elements)
 {
-    return total_elements >= (int64_t(1) << 24) ? 1024 : 512;
+    return total_elements >= kLargeCollection ? 512 : 256;
 }
 
 void apply_single_forcing(SingleLaunch* L, bool* vec)
@@ -494,10 +514,10 @@ int build_plan(int kind_arg, const ou_segment* segs, int32_t nseg, ou_plan_s** o
         std::stable_sort(G.items.begin(), G.items.end(),
                          [](const auto& a, const auto& b) { return a.first > b.first; });
         const int64_t nblk = static_cast<int64_t>(G.items.size()) / G.L.waves;
-        xcd_order(G.items, G.L.waves, xcd_log2_for(nblk, xcd_run_forced(kXcdRunMulti)));
+        xcd_order(G.items, G.L.waves, xcd_log2_for(nblk, xcd_run_forced(G.L.xcd_run)));
         // clip pass 1 runs one block per clip item
         const int64_t nclip = static_cast<int64_t>(G.clip_items.size());
-        xcd_order(G.clip_items, 1, xcd_log2_for(nclip, xcd_run_forced(kXcdRunMulti)));
+        xcd_order(G.clip_items, 1, xcd_log2_for(nclip, xcd_run_forced(kXcdRunClip)));
         if (G.segs.empty()) continue;
         bytes = align16(bytes + G.segs.size() * sizeof(SegDesc));
         bytes = align16(bytes + G.items.size() * sizeof(WorkItem));
@@ -662,10 +682,12 @@ int plan_launch_clip(ou_plan_s* plan, const StepScalars& sc, float max_unorm, hi
 }
 
 // A step through a HIP graph: the plain step (one node per dtype group) or
-// the clipped one (a chain of three nodes per group).  Built and
-// instantiated on the first call of its form; later calls write the step's
-// scalars into the nodes and replay.  Groups touch disjoint memory, so their
-// nodes (or chains) are independent.
+// the clipped one (three nodes per group).  Built and instantiated on the
+// first call of its form; later calls write the step's scalars into the
+// nodes and replay.  All nodes form one chain: groups touch disjoint memory
+// and could run side by side, but measured on MI355X a replay costs ~16 us
+// of host time for a chain of 1-3 kernel nodes and 31-81 us for 2-3
+// independent ones.
 int plan_graph_launch(ou_plan_s* plan, const StepScalars& sc, float max_unorm, bool clipped,
                       hipStream_t s)
 {
@@ -689,8 +711,8 @@ int plan_graph_launch(ou_plan_s* plan, const StepScalars& sc, float max_unorm, b
             graph = nullptr;
             return hip_fail(e, "hipGraphCreate");
         }
+        hipGraphNode_t prev = nullptr;
         for (Group& g : plan->groups) {
-            hipGraphNode_t prev = nullptr;
             for (int pass = first; pass <= last; ++pass) {
                 hipKernelNodeParams kp;
                 if (int st = group_launch(plan->kind, g, pass, &kp)) {
@@ -885,6 +907,27 @@ int clip_step(int kind_arg, int dtype, void* param, const void* grad, float* sta
 }
 
 }  // namespace
+
+// Kernel-node parameters of a plan's plain step, one per dtype group, for a
+// graph that spans several plans (host_graph.hip).  The parameters point
+// into the plan's own argument storage; they are valid until the plan's next
+// step of any form.
+int plan_node_params(ou_plan_s* plan, const ou_hparams& hp, std::vector<hipKernelNodeParams>* out)
+{
+    if (int st = check_hparams(plan->kind, hp)) return st;
+    if (int st = check_plan_device(plan)) return st;
+    const StepScalars sc = make_scalars(hp, plan->decay_after);
+    for (Group& g : plan->groups) {
+        set_group_args(g, sc);
+        hipKernelNodeParams kp;
+        if (int st = group_launch(plan->kind, g, 0, &kp)) return st;
+        out->push_back(kp);
+    }
+    return OU_OK;
+}
+
+int plan_device(const ou_plan_s* plan) { return plan->device; }
+
 }  // namespace ou
 
 // =============================================================== C ABI

@@ -174,6 +174,26 @@ int check_plan8(ou_plan8 plan, const ou_hparams* hp)
 
 }  // namespace
 
+namespace ou {
+
+// Kernel-node parameters of an 8-bit plan's step, one per dtype group, for a
+// graph that spans several plans (host_graph.hip); valid until the plan's
+// next step of any form.
+int plan8_node_params(ou_plan8_s* plan, const ou_hparams& hp, std::vector<hipKernelNodeParams>* out)
+{
+    if (int st = check_plan8(plan, &hp)) return st;
+    const StepScalars sc = make_scalars(hp, plan->decay_after);
+    for (ou_plan8_s::Group& g : plan->groups) {
+        set_args8(g, sc);
+        out->push_back(node_params8(g));
+    }
+    return OU_OK;
+}
+
+int plan8_device(const ou_plan8_s* plan) { return plan->device; }
+
+}  // namespace ou
+
 extern "C" {
 
 __attribute__((visibility("default")))
@@ -346,12 +366,14 @@ int ou_plan8_graph_step(ou_plan8 plan, const ou_hparams* hp, void* stream)
     if (!plan->exec) {
         e = hipGraphCreate(&plan->graph, 0);
         if (e != hipSuccess) return hip_fail(e, "hipGraphCreate");
+        hipGraphNode_t prev = nullptr;
         for (ou_plan8_s::Group& g : plan->groups) {
             set_args8(g, sc);
             const hipKernelNodeParams kp = node_params8(g);
-            // groups touch disjoint memory: independent nodes
-            e = hipGraphAddKernelNode(&g.node, plan->graph, nullptr, 0, &kp);
+            // one chain (a replay of independent nodes costs far more host time)
+            e = hipGraphAddKernelNode(&g.node, plan->graph, prev ? &prev : nullptr, prev ? 1 : 0, &kp);
             if (e != hipSuccess) return hip_fail(e, "hipGraphAddKernelNode");
+            prev = g.node;
         }
         e = hipGraphInstantiate(&plan->exec, plan->graph, nullptr, nullptr, 0);
         if (e != hipSuccess) {

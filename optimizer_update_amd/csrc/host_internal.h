@@ -63,4 +63,14 @@ void xcd_order(std::vector<T>& items, int per_block, int log2c)
 }
 bool capturing(hipStream_t stream);
 
+// Kernel-node parameters of one plain step of a plan (a node per dtype
+// group; the hyperparameters checked for the plan's kind, the current device
+// checked against the plan's), appended to `out` in launch order; they
+// point into the plan's argument storage and stay valid until the plan's
+// next step.  For graphs that span several plans.
+int plan_node_params(ou_plan_s* plan, const ou_hparams& hp, std::vector<hipKernelNodeParams>* out);
+int plan8_node_params(ou_plan8_s* plan, const ou_hparams& hp, std::vector<hipKernelNodeParams>* out);
+int plan_device(const ou_plan_s* plan);
+int plan8_device(const ou_plan8_s* plan);
+
 }  // namespace ou

@@ -45,6 +45,7 @@ struct MultiLaunch {
     int epl;      // 4 or 8
     int unroll;   // 1, 2 or 4
     int lds;      // dynamic LDS bytes reserved to cap blocks per CU (0 = no cap)
+    int xcd_run;  // blocks per XCD run of the work list's order (xcd_tile)
 };
 
 // Device facts the launch selection depends on (cached per device id).

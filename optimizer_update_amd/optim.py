@@ -27,7 +27,7 @@ from __future__ import annotations
 
 import torch
 
-from . import (DTYPES, TWO_STATE, HParams, Plan, Plan8, _kind, _on_device, _ptr, _raw_stream,
+from . import (DTYPES, TWO_STATE, Graph, HParams, Plan, Plan8, _kind, _on_device, _ptr, _raw_stream,
                _tensor_args, check, clip_workspace, load, optimizer_update_8bit_blockwise,
                optimizer_update_32bit, optimizer_update_32bit_clip, state8_sizes, state_sizes)
 
@@ -77,7 +77,6 @@ class _Collection:
     def segments(self):
         return list(zip(self.params, self.grads, self.state1, self.state2))
 
-    @torch.no_grad()
     def step(self, graph: bool = False, stream=None) -> None:
         """One step of the whole collection: plan launch, or graph replay.
         With max_unorm > 0 every tensor's update is clipped by its own norms."""
@@ -297,6 +296,7 @@ class _Collection8:
                       torch.zeros(n2, dtype=torch.float32, device=p.device))
             self.state.append(st)
         self.plan8 = self.plan32 = None
+        self._graph = None
         self._build_plans()
 
     def _build_plans(self) -> None:
@@ -318,16 +318,21 @@ class _Collection8:
         del set_to_none
         _zero_in_place(self._followed, self.grads)
 
-    @torch.no_grad()
     def step(self, graph: bool = False, stream=None) -> None:
         """One step: the 8-bit plan, then the 32-bit plan (one launch per
-        dtype group each), or the replay of their HIP graphs."""
+        dtype group each), or one HIP graph over both (built on the first
+        graph step)."""
         self._sync_grads()
         self.step_count += 1
+        if graph:
+            if self._graph is None:
+                self._graph = Graph([self.plan32], [self.plan8])
+            self._graph.step(self.hp, self.step_count, stream)
+            return
         if self.plan8 is not None:
-            (self.plan8.graph_step if graph else self.plan8.step)(self.hp, self.step_count, stream)
+            self.plan8.step(self.hp, self.step_count, stream)
         if self.plan32 is not None:
-            (self.plan32.graph_step if graph else self.plan32.step)(self.hp, self.step_count, stream)
+            self.plan32.step(self.hp, self.step_count, stream)
 
     @torch.no_grad()
     def step_per_tensor(self, stream=None) -> None:
@@ -357,6 +362,9 @@ class _Collection8:
                 a.copy_(b)
 
     def close(self) -> None:
+        if self._graph is not None:       # the graph goes before its plans
+            self._graph.close()
+            self._graph = None
         for plan in (self.plan8, self.plan32):
             if plan is not None:
                 plan.close()

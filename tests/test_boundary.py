@@ -41,7 +41,8 @@ def test_exports_every_header_function(L):
                           "ou_last_error", "ou_8bit_qmap", "optimizer_update_8bit_blockwise",
                           "ou_plan8_create", "ou_plan8_step", "ou_plan8_graph_step",
                           "ou_plan8_destroy", "optimizer_update_32bit_clip_noalloc",
-                          "ou_clip_noalloc_max_elements"}
+                          "ou_clip_noalloc_max_elements", "ou_graph_create", "ou_graph_step",
+                          "ou_graph_destroy"}
     for n in names:
         assert hasattr(L, n), n
     out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIBRARY], capture_output=True,
@@ -204,6 +205,26 @@ def _clip(L, max_unorm=1.0, ws=0x800000, wsb=None, n=4096, p=0x10000, kind=0, **
 def _clip_noalloc(L, max_unorm=1.0, n=4096, p=0x10000, kind=0, dtype=0, s2=0x40000):
     return L.optimizer_update_32bit_clip_noalloc(kind, dtype, p, 0x20000, 0x30000, s2, n, 0.9, 0.999,
                                                  0.9999, 5.0, 1e-8, 0.0, 1, 1e-3, 0, max_unorm, None)
+
+
+def test_graph_entry_validation(L):
+    """ou_graph_create and ou_graph_step reject what they must before any
+    device work: a null output handle, negative counts, null arrays or
+    plans, a null graph or hparams."""
+    vp = ctypes.c_void_p
+    h = vp()
+    none = (vp * 1)()
+    assert L.ou_graph_create(none, 0, none, 0, None) == OU_EINVAL
+    assert L.ou_graph_create(none, -1, none, 0, ctypes.byref(h)) == OU_EINVAL
+    assert L.ou_graph_create(None, 1, none, 0, ctypes.byref(h)) == OU_EINVAL
+    assert L.ou_graph_create(none, 1, none, 0, ctypes.byref(h)) == OU_EINVAL      # plan 0 is null
+    assert L.ou_graph_create(none, 0, none, 1, ctypes.byref(h)) == OU_EINVAL      # 8-bit plan 0 is null
+    assert L.ou_graph_create(none, 0, none, 0, ctypes.byref(h)) == OU_OK and h.value
+    hp = _lib.ou_hparams(0.9, 0.999, 0.9999, 5.0, 1e-8, 0.0, 1e-3, 0, 1)
+    assert L.ou_graph_step(None, ctypes.byref(hp), None) == OU_EINVAL
+    assert L.ou_graph_step(h, None, None) == OU_EINVAL
+    L.ou_graph_destroy(h)
+    L.ou_graph_destroy(None)
 
 
 def test_clip_noalloc_validation(L):

@@ -232,3 +232,53 @@ def test_graph_step_rejected_under_capture_and_multi_too():
         torch.cuda.synchronize()
     assert errors == [-7, -7, -7]
     plan.close()
+
+
+@pytest.mark.parametrize("kind", ["adam", "ademamix"])
+def test_one_graph_over_several_plans(kind):
+    """ou_graph: one HIP graph over a mixed-dtype 32-bit plan (three dtype
+    groups), a second 32-bit plan with the other decay order and a
+    mixed-dtype 8-bit plan (six chained launches).  Every replay equals the
+    plans' own steps bitwise, with eager torch work and synchronisations
+    between replays."""
+    import optimizer_update_amd as ou
+    hp = ou.HParams(lr=1e-3, weight_decay=0.01)
+    host = _collection(kind, 3)
+    host_b = _collection(kind, 4)
+    gen8 = W.rng(0, 12, 0)
+    host8 = [(s, W.params(n, s, gen8), W.grads(n, "normal", s, gen8))
+             for s, n in (("bf16", 5000), ("fp32", 4096 + 37), ("fp16", 70000))]
+
+    def state8(s, p, g):
+        sizes = ou.state8_sizes(kind, p.size)
+        return (H.to_dev(p, s), H.to_dev(g, s), torch.zeros(sizes[0], dtype=torch.uint8, device="cuda"),
+                torch.zeros(sizes[1], dtype=torch.uint8, device="cuda"), torch.zeros(sizes[2], device="cuda"),
+                torch.zeros(sizes[3], device="cuda"))
+
+    def build():
+        a = _device(kind, host)
+        b = _device(kind, host_b)
+        c = [state8(*x) for x in host8]
+        return a, b, c, ou.Plan(kind, a), ou.Plan(kind, b, decay_after=True), ou.Plan8(kind, c)
+
+    ref = build()
+    got = build()
+    graph = ou.Graph([got[3], got[4]], [got[5]])
+    steps = 4
+    for t in range(1, steps + 1):
+        ref[3].step(hp, t)
+        ref[4].step(hp, t)
+        ref[5].step(hp, t)
+        graph.step(hp, t)
+        if t == 2:              # eager work and a synchronisation between replays
+            torch.cuda.synchronize()
+            _ = (got[0][0][0].float() * 3).sum().item()
+    torch.cuda.synchronize()
+    graph.close()
+    for r, x in zip(ref[:3], got[:3]):
+        for tr, tx in zip(r, x):
+            for u, v in zip(tr, tx):
+                assert u.dtype == v.dtype
+                assert u.cpu().view(torch.uint8).numpy().tobytes() == v.cpu().view(torch.uint8).numpy().tobytes()
+    for p in ref[3:] + got[3:]:
+        p.close()
