@@ -42,10 +42,15 @@ KERNEL_SOURCES = ("optimizer_update_amd/csrc/kernels.hip", "optimizer_update_amd
 KERNEL8_SOURCES = ("optimizer_update_amd/csrc/kernels8.hip", "optimizer_update_amd/csrc/qmap.hpp",
                    "optimizer_update_amd/csrc/elem.hpp", "optimizer_update_amd/csrc/stepdiv.hpp",
                    "optimizer_update_amd/csrc/host8.hip")
-# VALU issue peak for the kernels as built (packed-fp32 instructions off):
-# MI355X's 157.3 TFLOP/s fp32 vector rate counts packed FMAs (2 per lane);
-# unpacked, each SIMD retires 16 lanes per cycle, one wave64 instruction per
-# 4 cycles: 256 CUs x 4 SIMDs x 2.4 GHz / 4 = 614.4 G wave64 instructions/s
+# Nominal VALU issue rate for the kernels as built (packed-fp32 instructions
+# off): MI355X's 157.3 TFLOP/s fp32 vector rate counts packed FMAs (2 per
+# lane); unpacked, each SIMD retires 16 lanes per cycle, one full-rate wave64
+# instruction per 4 cycles (a quad-cycle): 256 CUs x 4 SIMDs x 2.4 GHz / 4 =
+# 614.4 G wave64 instructions/s.  The 8-bit cases' ALU roofline uses the rate
+# measured in the same run by a VALU-only probe kernel instead, and counts
+# the kernels' VALU work in busy quad-cycles (SQ_ACTIVE_INST_VALU), which
+# weights the binary64 and transcendental instructions that take more than
+# one.
 VALU_PEAK_G = 256 * 4 * 2.4 / 4
 
 
@@ -188,21 +193,30 @@ def main():
         print(json.dumps(bench_collection(torch, ou, W, dev, time_rounds)))
         return
 
-    valu8 = None   # committed VALU instruction counts of the 8-bit kernel
+    valu8 = None   # committed VALU counts of the 8-bit kernel (per 256-element block)
     vf = os.path.join(ROOT, "profiles", "valu_k8_single_256M.json")
     if os.path.exists(vf):
         with open(vf) as f:
             v = json.load(f)
         if v.get("kernel8_sources_sha") == kernel_sha(KERNEL8_SOURCES):
-            valu8 = v["valu_wave_instructions_per_block"]
+            valu8 = v
+    valu_peak = None if args.quick else valu_issue_rate(torch, ou, dev, time_rounds)
 
     def alu_roofline(case_key, n, ms):
-        """VALU issue rate of an 8-bit case from the committed counter value."""
-        if not valu8 or case_key not in valu8:
+        """VALU work of an 8-bit case (committed SQ_ACTIVE_INST_VALU per block,
+        in quad-cycles) per second, against the VALU-only probe's issue rate
+        measured in this run (and the nominal 614.4 G/s)."""
+        if not valu8 or case_key not in valu8.get("valu_quad_cycles_per_block", {}):
             return None
-        achieved = valu8[case_key] * (n // 256) / (ms * 1e-3) / 1e9
-        return {"bound": "alu", "achieved": round(achieved, 1), "peak": VALU_PEAK_G,
-                "unit": "G VALU wave-instructions/s", "frac": round(achieved / VALU_PEAK_G, 4)}
+        blocks = n // 256
+        cycles = valu8["valu_quad_cycles_per_block"][case_key] * blocks / (ms * 1e-3) / 1e9
+        instrs = valu8["valu_wave_instructions_per_block"][case_key] * blocks / (ms * 1e-3) / 1e9
+        peak = valu_peak["G_per_s"] if valu_peak else VALU_PEAK_G
+        return {"bound": "alu", "achieved": round(cycles, 1), "peak": round(peak, 1),
+                "unit": "G VALU quad-cycles/s", "frac": round(cycles / peak, 4),
+                "peak_source": "VALU-only probe in this run" if valu_peak else "nominal",
+                "frac_of_nominal_614.4": round(cycles / VALU_PEAK_G, 4),
+                "wave_instructions_G_per_s": round(instrs, 1)}
 
     # ---------------------------------------------------------------- headline
     parts = args.case.split(":")
@@ -286,6 +300,8 @@ def main():
         cases["copy_fp32_2^28"] = {**r, "GBps": round(2 * 4 * (1 << 28) / (r["median_ms"] * 1e-3) / 1e9, 1)}
         if probe:
             cases["bandwidth_ceilings_fp32_2^28"] = probe
+        if valu_peak:
+            cases["valu_issue_probe"] = valu_peak
         del src, dst
         torch.cuda.empty_cache()
         for ck, cs, cl in (("adam", "bf16", 28), ("ademamix", "fp32", 28), ("ademamix", "bf16", 28),
@@ -334,6 +350,27 @@ def main():
         if not args.no_cpu:
             out["cpu_baseline"] = cpu_baseline(torch, W, dev)
     print(json.dumps(out))
+
+
+def valu_issue_rate(torch, ou, dev, time_rounds):
+    """The device's VALU issue rate, measured: the probe kernel runs 32
+    full-rate binary32 FMAs per round on registers, 4,096 rounds per lane,
+    8 blocks of 4 waves per CU (every SIMD full), and nothing else."""
+    lib = ou._lib.load()
+    out = torch.zeros(1, device=dev)
+    blocks = 8 * torch.cuda.get_device_properties(dev).multi_processor_count
+    rounds = 4096
+    sh = torch.cuda.current_stream().cuda_stream
+
+    def run():
+        st = lib.ou__valu_probe(blocks, rounds, out.data_ptr(), sh)
+        if st != 0:
+            raise RuntimeError(lib.ou_last_error().decode())
+    r = time_rounds(run, iters=5, rounds=7, warmup=3)
+    instr = blocks * 4 * rounds * 32
+    return {"G_per_s": round(instr / (r["median_ms"] * 1e-3) / 1e9, 1), "median_ms": round(r["median_ms"], 4),
+            "wave_instructions": instr, "blocks": blocks,
+            "what": "32 independent v_fmac_f32 per round per lane, 4,096 rounds, 4-wave blocks, 8 per CU"}
 
 
 # LDS per CU of gfx950 (160 KiB): a kernel with no LDS of its own that

@@ -20,11 +20,16 @@
 namespace ou {
 namespace {
 
-// Launch shape: 4 waves per workgroup; a wave takes a run of blocks (single
-// tensor, select_bpw8) or one work item of up to 16 blocks (collection; 16
-// measured best on the bf16 AdamW8bit collection against 2, 4, 8 and 32),
-// so a workgroup's table copy into LDS serves 4 runs.
+// Launch shape: 4 waves per workgroup (8 for a single tensor with fp32
+// storage); a wave takes a run of blocks (single tensor, select_bpw8) or one
+// work item of up to 16 blocks (collection; 16 measured best on the bf16
+// AdamW8bit collection against 2, 4, 8 and 32, and 4 waves against 8), so a
+// workgroup's table copy into LDS serves 4 (8) runs.  Measured on MI355X at
+// 2^28 elements in interleaved rounds: fp32 storage 715 us with 8 waves of
+// 4 blocks against 742 us with 4 waves of 8; 16-bit storage gains nothing
+// from 8 waves.
 constexpr int kWaves8 = 4;
+constexpr int kWaves8F32 = 8;
 constexpr int kChunkBlocks8 = 16;
 // Workgroups per XCD run (xcd_tile), single tensors and the launch order of
 // plan work items.
@@ -38,11 +43,11 @@ int64_t nblocks(int64_t n) { return (n + kQBlock - 1) / kQBlock; }
 // Blocks per wave of the single-tensor kernel: as many as still leave 4
 // workgroups per CU (a longer run amortizes the table copy and keeps the
 // two-block pipeline full), even (the wide path takes blocks in pairs), and
-// at most 16 for 16-bit storage, 8 for fp32 (measured at 2^28 elements:
+// at most 16 for 16-bit storage, 4 for fp32 (measured at 2^28 elements:
 // longer runs stop paying there).
 int32_t select_bpw8(const DeviceProps& dp, int dtype, int64_t nb, int waves)
 {
-    const int64_t cap = dtype == OU_F32 ? 8 : 16;
+    const int64_t cap = dtype == OU_F32 ? 4 : 16;
     const int64_t cus = dp.cu_count > 0 ? dp.cu_count : 1;
     const int64_t b = std::min(cap, std::max<int64_t>(2, nb / (cus * 4 * waves)));
     return static_cast<int32_t>(b & ~int64_t(1));
@@ -228,7 +233,7 @@ int optimizer_update_8bit_blockwise(int kind_arg, int dtype, void* param, const 
     const DeviceProps* dp = nullptr;
     if (int st = current_device(&dp)) return st;
 
-    int waves = kWaves8;
+    int waves = dtype == OU_F32 ? kWaves8F32 : kWaves8;
     if (int w = g8_waves.load()) waves = w;
     const void* fn = kernel8(false, kind, dtype);
     if (!fn || waves < 1 || waves > 16) return fail(OU_EINVAL, "no 8-bit kernel for waves=%d", waves);

@@ -82,6 +82,9 @@ const void* narrow_kernel(int dtype, bool pairs);
 
 // The update kernels' square root alone (test hook).
 const void* sqrt_kernel();
+
+// VALU issue probe: 32 binary32 FMAs per round per lane, no memory (test hook).
+const void* valu_probe_kernel();
 constexpr int kClipChunkElems = 2048;   // elements per partial-norm chunk
 constexpr int kClipThreadsHost = 256;   // threads of pass 1
 constexpr int kClipFinalThreadsHost = 1024;   // threads of pass 2

@@ -53,7 +53,7 @@ def test_exports_every_header_function(L):
     assert exported - set(names) == {"ou__select_single", "ou__force_single", "ou__force_multi",
                                      "ou__step_scalars", "ou__force_8bit", "ou__validate_only",
                                      "ou__force_xcd", "ou__stream_probe", "ou__narrow",
-                                     "ou__sqrt", "ou__recip8"}
+                                     "ou__sqrt", "ou__recip8", "ou__valu_probe"}
 
 
 def test_header_is_plain_c_and_matches_ctypes_layout(tmp_path):
