@@ -54,11 +54,43 @@ KERNEL8_SOURCES = ("optimizer_update_amd/csrc/kernels8.hip", "optimizer_update_a
 VALU_PEAK_G = 256 * 4 * 2.4 / 4
 
 
+def code_text(src: str) -> str:
+    """C/C++/HIP source with its comments and blank lines removed and each
+    line's surrounding whitespace stripped; string and character literals
+    are kept whole (a "//" inside one is not a comment)."""
+    out = []
+    i, n = 0, len(src)
+    while i < n:
+        c = src[i]
+        if c in "\"'":
+            j = i + 1
+            while j < n and src[j] != c:
+                j += 2 if src[j] == "\\" else 1
+            out.append(src[i:j + 1])
+            i = j + 1
+        elif src.startswith("//", i):
+            while i < n and src[i] != "\n":
+                i += 1
+        elif src.startswith("/*", i):
+            j = src.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+            out.append(" ")
+        else:
+            out.append(c)
+            i += 1
+    lines = (ln.strip() for ln in "".join(out).split("\n"))
+    return "\n".join(ln for ln in lines if ln)
+
+
 def kernel_sha(files=KERNEL_SOURCES) -> str:
+    """Hash of the code (not the comments) of the sources that shape a
+    kernel: the committed counter records are keyed by it, so a record
+    stays valid across comment edits and lapses with any change of code."""
     h = hashlib.sha256()
     for f in files:
-        with open(os.path.join(ROOT, f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, f), encoding="utf-8") as fh:
+            h.update(code_text(fh.read()).encode())
+        h.update(b"\0")
     return h.hexdigest()[:16]
 
 

@@ -322,8 +322,8 @@ SingleLaunch select_single(const DeviceProps& d, int kind, int dtype, int64_t n,
 
 // Multi tensor: waves per block, EPL and unroll; the chunk (elements per
 // work item) is a multiple of 64 * EPL * unroll so chunk starts keep 16-byte
-// alignment.  Large collections get the same cap of two resident blocks per
-// CU as large single tensors.
+// alignment.  Large collections get the shape and the cap of eight resident
+// blocks per CU of large single tensors.
 // Measured on MI355X in 15 interleaved rounds per shape with the 505-tensor
 // bf16 collection (287.9 M elements) and its 408 tensors of <= 16,384
 // elements (3.4 M): a large collection runs as the large single tensor

@@ -358,6 +358,26 @@ def test_product_path_never_touches_the_oracle():
     assert "import oracle" in body.split("\ndef ")[0]
 
 
+def test_kernel_hash_ignores_comments_only():
+    """The benchmark keys its committed counter records by a hash of the
+    kernels' code: comments, blank lines and indentation do not change it,
+    any token of code does, and a comment marker inside a literal is code."""
+    import importlib.util
+    spec = importlib.util.spec_from_file_location("bench_mod", os.path.join(ROOT, "bench.py"))
+    bench = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(bench)
+    a = 'int x = 1; // one\n/* block\n comment */\n\n    float y = 2.0f;\nconst char* s = "a//b/*c*/";\n'
+    b = 'int x = 1;\nfloat y = 2.0f;   // two\n  const char* s = "a//b/*c*/";'
+    assert bench.code_text(a) == bench.code_text(b)
+    assert bench.code_text(a) == 'int x = 1;\nfloat y = 2.0f;\nconst char* s = "a//b/*c*/";'
+    assert bench.code_text(a.replace("2.0f", "3.0f")) != bench.code_text(a)
+    assert bench.code_text("char c = '\\''; // q\nchar d = '/';") == "char c = '\\'';\nchar d = '/';"
+    for f in bench.KERNEL_SOURCES + bench.KERNEL8_SOURCES:
+        src = open(os.path.join(ROOT, f)).read()
+        code = re.sub(r'"(?:\\.|[^"\\])*"', '""', bench.code_text(src))   # literals out
+        assert code.count("{") == code.count("}") and code.count("(") == code.count(")"), f
+
+
 def test_binding_rejects_host_tensors():
     import torch
 
