@@ -430,8 +430,7 @@ __device__ __forceinline__ void run_wide8(const Seg8& d, int64_t b0, int64_t str
 // [w*W*R, (w+1)*W*R) with W waves of R blocks each, interleaved so that the
 // W waves work on W neighbouring blocks at a time.
 template <int KIND, typename S>
-__global__ void __launch_bounds__(1024)
-k8_single(Seg8 d, StepScalars sc, int32_t blocks_per_wave, int32_t xcd_log2)
+__device__ __forceinline__ void single8(Seg8 d, StepScalars sc, int32_t blocks_per_wave, int32_t xcd_log2)
 {
     __shared__ QLds T;
     const int waves = static_cast<int>(blockDim.x) / kWave;
@@ -448,6 +447,27 @@ k8_single(Seg8 d, StepScalars sc, int32_t blocks_per_wave, int32_t xcd_log2)
         run_wide8<KIND, S>(d, first, waves, blocks_per_wave, T, sc, lane, a);
     else
         run_blocks8<KIND, S>(d, first, waves, blocks_per_wave, T, sc, lane);
+}
+
+template <int KIND, typename S>
+__global__ void __launch_bounds__(1024)
+k8_single(Seg8 d, StepScalars sc, int32_t blocks_per_wave, int32_t xcd_log2)
+{
+    single8<KIND, S>(d, sc, blocks_per_wave, xcd_log2);
+}
+
+// The same with at least 6 waves resident per SIMD (at most 80 VGPRs, 3 of
+// them spilled), for Adam with fp32 storage: that kernel reaches neither
+// the VALU issue rate nor HBM's, and at 83 VGPRs only 5 waves per SIMD
+// hide its latencies.  Measured on MI355X at 2^28 elements, interleaved
+// with the 5-wave build: -0.6% and -1.7% of the time on two boxes.  The
+// 16-bit kernels are issue-bound and lost 1-9% under the same bound (the
+// AdEMAMix ones spill), AdEMAMix with fp32 storage lost 0.6% at 5 waves.
+template <int KIND, typename S>
+__global__ void __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(6)))
+k8_single_w6(Seg8 d, StepScalars sc, int32_t blocks_per_wave, int32_t xcd_log2)
+{
+    single8<KIND, S>(d, sc, blocks_per_wave, xcd_log2);
 }
 
 // Collection: one wave per work item (segment, run of `chunk_blocks`
@@ -494,8 +514,15 @@ k8_recip(const float* __restrict__ in, float* __restrict__ out, int64_t n)
 template <int KIND, typename S>
 const void* pick8(bool multi)
 {
-    return multi ? reinterpret_cast<const void*>(&k8_multi<KIND, S>)
-                 : reinterpret_cast<const void*>(&k8_single<KIND, S>);
+    if (multi) return reinterpret_cast<const void*>(&k8_multi<KIND, S>);
+    return reinterpret_cast<const void*>(&k8_single<KIND, S>);
+}
+
+template <>
+const void* pick8<kAdam, F32>(bool multi)
+{
+    if (multi) return reinterpret_cast<const void*>(&k8_multi<kAdam, F32>);
+    return reinterpret_cast<const void*>(&k8_single_w6<kAdam, F32>);
 }
 
 template <int KIND>
