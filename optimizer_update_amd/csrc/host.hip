@@ -561,11 +561,11 @@ int build_plan(int kind_arg, const ou_segment* segs, int32_t nseg, ou_plan_s** o
             off = align16(off + G.segs.size() * 2 * sizeof(float));
             grp.fn = multi_kernel(kind, dt, grp.L.epl, grp.L.unroll);
             if (!grp.fn || grp.chunk % (kWave * grp.L.epl) != 0 || grp.chunk > INT32_MAX ||
-                grp.chunk % 4 != 0) {
+                grp.chunk % 4 != 0 || grp.L.waves < 1 || grp.L.waves * kWave > kMultiMaxThreads) {
                 (void)hipFree(plan->dmem);
                 delete plan;
-                return fail(OU_EINVAL, "no multi-tensor kernel for epl=%d unroll=%d chunk=%lld",
-                            grp.L.epl, grp.L.unroll, (long long)grp.chunk);
+                return fail(OU_EINVAL, "no multi-tensor kernel for waves=%d epl=%d unroll=%d chunk=%lld",
+                            grp.L.waves, grp.L.epl, grp.L.unroll, (long long)grp.chunk);
             }
             grp.grid = (grp.n_items + grp.L.waves - 1) / grp.L.waves;
             grp.chunk32 = static_cast<int32_t>(grp.chunk);

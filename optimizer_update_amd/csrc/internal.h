@@ -39,6 +39,10 @@ struct SingleLaunch {
     int xcd_log2; // XCD tile runs of 2^xcd_log2 tiles (k_single's xcd_tile), -1: block order
 };
 
+// Launch bound of the multi-tensor kernels (k_multi, k_clip_apply_multi):
+// at most 8 waves per block.
+constexpr int kMultiMaxThreads = 512;
+
 // Launch shape of the multi-tensor kernel.
 struct MultiLaunch {
     int waves;    // waves per block: 1, 2, 4 or 8

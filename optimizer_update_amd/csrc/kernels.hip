@@ -205,7 +205,7 @@ k_single(typename S::raw* __restrict__ p, const typename S::raw* __restrict__ g,
 // ---- multi tensor ---------------------------------------------------------------
 
 template <int KIND, typename S, int EPL, int U>
-__global__ void __launch_bounds__(512)
+__global__ void __launch_bounds__(kMultiMaxThreads)
 k_multi(const SegDesc* __restrict__ segs, const WorkItem* __restrict__ items, int64_t n_items,
         int32_t chunk, StepScalars sc)
 {
@@ -563,7 +563,7 @@ k_clip_apply(typename S::raw* __restrict__ p, const typename S::raw* __restrict_
 // Pass 3, collection: one wave per item of the plan's regular work list,
 // with the segment's clipped learning rate.
 template <int KIND, typename S>
-__global__ void __launch_bounds__(512)
+__global__ void __launch_bounds__(kMultiMaxThreads)
 k_clip_apply_multi(const SegDesc* __restrict__ segs, const WorkItem* __restrict__ items,
                    int64_t n_items, int32_t chunk, StepScalars sc, const float* __restrict__ seg_out)
 {

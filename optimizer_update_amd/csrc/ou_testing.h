@@ -27,7 +27,9 @@ int ou__select_single(int cu_count, int lds_per_cu, int lds_per_block, int kind,
 void ou__force_single(int block, int epl, int unroll, int64_t grid, int scalar_only, int lds);
 
 // Force the multi-tensor shape used by plans created afterwards
-// (0 = no forcing; lds -1 = no cap).  chunk must be a multiple of 64 * epl * unroll.
+// (0 = no forcing; lds -1 = no cap).  chunk must be a multiple of 64 * epl * unroll
+// and waves at most 8 (the kernels' 512-thread launch bound); plan creation
+// refuses other shapes with OU_EINVAL.
 void ou__force_multi(int waves, int epl, int unroll, int chunk, int lds);
 
 // Force the XCD tile runs (xcd_tile) of the single-tensor kernel and of

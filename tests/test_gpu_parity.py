@@ -254,6 +254,22 @@ def test_launch_variants_bitwise(orc, L, kind, storage):
                 plan.close()
 
 
+def test_forced_multi_shape_beyond_launch_bound_is_refused(L):
+    """The multi-tensor kernels take at most 8 waves per block (their
+    512-thread launch bound): a plan forced to 16 is refused at creation with
+    OU_EINVAL, before anything is launched, and the next plan is unaffected."""
+    from optimizer_update_amd import OptimizerUpdateError, Plan
+    segs = [tuple(torch.zeros(1024, device="cuda") for _ in range(4))]
+    L.ou__force_multi(16, 4, 1, 256, -1)
+    try:
+        with pytest.raises(OptimizerUpdateError, match="waves=16"):
+            Plan("adam", segs)
+    finally:
+        L.ou__force_multi(0, 0, 0, 0, 0)
+    plan = Plan("adam", segs)
+    plan.close()
+
+
 @pytest.mark.parametrize("kind", KINDS)
 @pytest.mark.parametrize("storage", ["fp32", "bf16"])
 def test_xcd_tile_runs_bitwise(orc, L, kind, storage):
