@@ -18,7 +18,10 @@ CPU oracle on the headline workload for a bounded number of steps.
 Timing: HIP events on the stream the kernels run on, W untimed warmups, then
 K timed steps between device synchronisations, with an event between steps
 so that every step's time is recorded (step_samples_ms).  Secondary cases
-report the median, p10/p90 and every sample of 7 rounds.
+report the median, p10/p90 and every sample of 7 rounds.  The small-tensor
+subsets fit in the 256 MB Infinity Cache, which serves back-to-back steps
+in part: their plan step is also timed cold (plan_cold), each sample after
+a 1 GiB write that evicts them.
 """
 from __future__ import annotations
 
@@ -460,6 +463,30 @@ def bandwidth_ceilings(torch, ou, head, n, time_rounds):
     return res
 
 
+def time_cold(torch, step, flush, samples=50, warmup=3):
+    """Per-step ms of `step` run cold: before each sample a write over
+    `flush` (1 GiB, four times what MI355X's 256 MB Infinity Cache holds)
+    evicts the step's tensors, as the forward and backward passes of a
+    training step would; two events bracket the step alone.  Median, p10,
+    p90 and every sample."""
+    for _ in range(warmup):
+        step()
+    out = []
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    for _ in range(samples):
+        flush.zero_()
+        e0.record()
+        step()
+        e1.record()
+        torch.cuda.synchronize()
+        out.append(e0.elapsed_time(e1))
+    srt = sorted(out)
+    q = lambda f: srt[min(len(srt) - 1, int(round(f * (len(srt) - 1))))]
+    return {"median_ms": statistics.median(srt), "p10_ms": q(0.1), "p90_ms": q(0.9),
+            "samples_ms": [round(x, 5) for x in out]}
+
+
 def _us(r: dict) -> dict:
     """A time_rounds result in microseconds: median, p10, p90 and every sample."""
     return {"median_us": round(r["median_ms"] * 1e3, 2), "p10_us": round(r["p10_ms"] * 1e3, 2),
@@ -499,6 +526,12 @@ def bench_collection(torch, ou, W, dev, time_rounds):
             r = time_rounds(fn, iters=iters, rounds=7, warmup=5)
             d[mode] = _us(r)
         d["plan_GBps"] = round(bytes_ / (d["plan"]["median_us"] * 1e-6) / 1e9, 1)
+        if bytes_ < (1 << 30):
+            # back-to-back steps over tensors this small are served partly by the
+            # Infinity Cache; the same step after a 1 GiB write is the cold figure
+            flush = torch.empty(1 << 28, device=dev)
+            d["plan_cold"] = _us(time_cold(torch, lambda: opt.step(), flush))
+            del flush
         d["plan_describe"] = opt.plan.describe()
         res[label] = d
         opt.close()
