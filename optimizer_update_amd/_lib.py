@@ -149,7 +149,7 @@ def load(path: str = LIBRARY) -> ctypes.CDLL:
     lib.ou__recip8.restype = i32
     lib.ou__stream_probe.argtypes = [i32, vp, vp, vp, vp, i64, vp]
     lib.ou__stream_probe.restype = i32
-    lib.ou__valu_probe.argtypes = [i64, ctypes.c_int32, vp, vp]
+    lib.ou__valu_probe.argtypes = [i32, i64, ctypes.c_int32, vp, vp]
     lib.ou__valu_probe.restype = i32
     lib.ou__force_xcd.argtypes = [i32]
     lib.ou__force_xcd.restype = None

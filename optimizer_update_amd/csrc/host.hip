@@ -1264,16 +1264,18 @@ int ou__stream_probe(int mode, float* p, const float* g, float* s1, float* s2, i
 }
 
 __attribute__((visibility("default")))
-int ou__valu_probe(int64_t blocks, int32_t iters, float* out, void* stream)
+int ou__valu_probe(int op, int64_t blocks, int32_t iters, float* out, void* stream)
 {
-    if (blocks < 1 || blocks > INT32_MAX || iters < 1 || !out) return fail(OU_EINVAL, "valu probe: bad arguments");
+    const void* fn = valu_probe_kernel(op);
+    if (!fn || blocks < 1 || blocks > INT32_MAX || iters < 1 || !out)
+        return fail(OU_EINVAL, "valu probe: bad arguments");
     if (reinterpret_cast<uintptr_t>(out) % 4) return fail(OU_EALIGN, "valu probe: misaligned output");
     if (validate_only()) return OU_OK;
     const DeviceProps* dp = nullptr;
     if (int st = g_devices.current(&dp)) return st;
     uint32_t mask = 0;
     void* args[] = {&out, &iters, &mask};
-    hipError_t e = launch(valu_probe_kernel(), blocks, 256, 0, args, static_cast<hipStream_t>(stream));
+    hipError_t e = launch(fn, blocks, 256, 0, args, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail(e, "launch valu probe");
     return OU_OK;
 }

@@ -88,7 +88,7 @@ const void* narrow_kernel(int dtype, bool pairs);
 const void* sqrt_kernel();
 
 // VALU issue probe: 32 binary32 FMAs per round per lane, no memory (test hook).
-const void* valu_probe_kernel();
+const void* valu_probe_kernel(int op);   // 0: FMA chains, 1: add chains; nullptr otherwise
 constexpr int kClipChunkElems = 2048;   // elements per partial-norm chunk
 constexpr int kClipThreadsHost = 256;   // threads of pass 1
 constexpr int kClipFinalThreadsHost = 1024;   // threads of pass 2

@@ -782,26 +782,29 @@ k_stream_probe(float* __restrict__ p, const float* __restrict__ g, float* __rest
     }
 }
 
-// VALU issue probe (test hook): every lane runs `iters` rounds of 32
-// independent binary32 fused multiply-adds (8 chains, 4 deep per round) on
-// registers, with no memory traffic; the result is stored only if it
-// matches a pattern under the runtime mask (never, with mask = 0).  Run
-// with enough waves to fill every SIMD, it measures the rate at which the
-// device issues full-rate VALU instructions (one quad-cycle each).
+// VALU issue probe (test hook): every lane runs `iters` rounds of 64
+// independent full-rate binary32 operations (8 chains, 8 deep per round)
+// on registers, with no memory traffic; the result is stored only if it
+// matches a pattern under the runtime mask (never, with mask = 0).  OP 0:
+// fused multiply-adds (v_fmac_f32); OP 1: additions (v_add_f32), which
+// draw less power, so the clock can stay higher.  Run with enough waves to
+// fill every SIMD, it measures the rate at which the device issues
+// full-rate VALU instructions (one quad-cycle each) under that load.
+template <int OP>
 __global__ void __launch_bounds__(256)
 k_valu_probe(float* __restrict__ out, int32_t iters, uint32_t mask)
 {
     float x[8];
 #pragma unroll
     for (int k = 0; k < 8; ++k) x[k] = static_cast<float>(threadIdx.x + k);
-    // runtime operands (mask = 0), so that every FMA is a 4-byte v_fmac_f32
+    // runtime operands (mask = 0), so that no operation folds away
     const float a = __builtin_bit_cast(float, 0x3a800000u ^ mask);
     const float b = __builtin_bit_cast(float, 0x3f7fbe77u ^ mask) * static_cast<float>(threadIdx.x & 1);
     for (int32_t i = 0; i < iters; ++i) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
+        for (int r = 0; r < 8; ++r)
 #pragma unroll
-            for (int k = 0; k < 8; ++k) x[k] = __builtin_fmaf(a, b, x[k]);
+            for (int k = 0; k < 8; ++k) x[k] = OP == 0 ? __builtin_fmaf(a, b, x[k]) : x[k] + a;
     }
     float acc = 0.0f;
 #pragma unroll
@@ -847,7 +850,14 @@ k_sqrt(const float* __restrict__ in, float* __restrict__ out, int64_t n)
 
 const void* sqrt_kernel() { return reinterpret_cast<const void*>(&k_sqrt); }
 
-const void* valu_probe_kernel() { return reinterpret_cast<const void*>(&k_valu_probe); }
+const void* valu_probe_kernel(int op)
+{
+    switch (op) {
+    case 0: return reinterpret_cast<const void*>(&k_valu_probe<0>);
+    case 1: return reinterpret_cast<const void*>(&k_valu_probe<1>);
+    default: return nullptr;
+    }
+}
 
 const void* narrow_kernel(int dtype, bool pairs)
 {

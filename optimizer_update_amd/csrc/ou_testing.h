@@ -63,10 +63,12 @@ int ou__recip8(const float* in, float* out, int64_t n, void* stream);
 int ou__stream_probe(int mode, float* p, const float* g, float* s1, float* s2, int64_t n, void* stream);
 
 // VALU issue probe: `blocks` blocks of 256 threads, each lane running
-// `iters` rounds of 32 independent binary32 FMAs on registers (32 * iters
-// VALU instructions per wave, no memory traffic; `out` is never written).
-// Asynchronous on `stream`.  For measuring the device's VALU issue rate.
-int ou__valu_probe(int64_t blocks, int32_t iters, float* out, void* stream);
+// `iters` rounds of 64 independent full-rate binary32 operations on
+// registers (64 * iters VALU instructions per wave, no memory traffic; `out`
+// is never written): op 0 fused multiply-adds, op 1 additions (less power
+// per instruction).  Asynchronous on `stream`.  For measuring the device's
+// VALU issue rate; OU_EINVAL for another op.
+int ou__valu_probe(int op, int64_t blocks, int32_t iters, float* out, void* stream);
 
 // While on != 0, every entry point returns OU_OK right after its argument
 // checks, before it queries or touches a device: no launch, no allocation

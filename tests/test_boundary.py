@@ -485,6 +485,20 @@ def test_stream_probe_validation(L):
     assert L.ou__stream_probe(3, 0x10000, 0x20000, 0x30000, 0x40000, 16, None) == OU_EINVAL
 
 
+def test_valu_probe_validation(L):
+    """The VALU probe takes op 0 (FMA chains) or 1 (add chains), at least one
+    block and one round, and an aligned output; the rest is OU_EINVAL or
+    OU_EALIGN before any launch."""
+    for op in (0, 1):
+        assert L.ou__valu_probe(op, 2048, 16, 0x10000, None) == OU_OK
+    assert L.ou__valu_probe(2, 2048, 16, 0x10000, None) == OU_EINVAL
+    assert L.ou__valu_probe(-1, 2048, 16, 0x10000, None) == OU_EINVAL
+    assert L.ou__valu_probe(0, 0, 16, 0x10000, None) == OU_EINVAL
+    assert L.ou__valu_probe(0, 2048, 0, 0x10000, None) == OU_EINVAL
+    assert L.ou__valu_probe(0, 2048, 16, 0, None) == OU_EINVAL
+    assert L.ou__valu_probe(0, 2048, 16, 0x10002, None) == OU_EALIGN
+
+
 def test_narrow_hook_validation(L):
     """The storage-rounding hook's argument checks (test hook)."""
     assert L.ou__narrow(1, 0x10000, 0x20000, 16, None) == OU_OK
