@@ -39,8 +39,9 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0
 METRIC = "optimizer-update GB/s (% of HBM peak) on 256M elems; µs per mixed small-tensor step"
 # the kernels and the launch selection that shapes them
-KERNEL_SOURCES = ("optimizer_update_amd/csrc/kernels.hip", "optimizer_update_amd/csrc/elem.hpp",
-                  "optimizer_update_amd/csrc/stepdiv.hpp", "optimizer_update_amd/csrc/host.hip")
+KERNEL_SOURCES = ("optimizer_update_amd/csrc/kernels.hip", "optimizer_update_amd/csrc/stream.hpp",
+                  "optimizer_update_amd/csrc/elem.hpp", "optimizer_update_amd/csrc/stepdiv.hpp",
+                  "optimizer_update_amd/csrc/host.hip")
 # the 8-bit kernels and their launch selection
 KERNEL8_SOURCES = ("optimizer_update_amd/csrc/kernels8.hip", "optimizer_update_amd/csrc/qmap.hpp",
                    "optimizer_update_amd/csrc/elem.hpp", "optimizer_update_amd/csrc/stepdiv.hpp",

@@ -18,10 +18,12 @@ LIBRARY = os.path.join(HERE, "liboptimizer_update.so")
 FAST = os.path.join(HERE, "_fast" + sysconfig.get_config_var("EXT_SUFFIX"))
 SOURCES = [os.path.join(CSRC, "kernels.hip"), os.path.join(CSRC, "host.hip"),
            os.path.join(CSRC, "kernels8.hip"), os.path.join(CSRC, "host8.hip"),
-           os.path.join(CSRC, "host_graph.hip")]
+           os.path.join(CSRC, "host_graph.hip"), os.path.join(CSRC, "probes.hip"),
+           os.path.join(CSRC, "host_probes.hip")]
 HEADERS = [os.path.join(CSRC, "elem.hpp"), os.path.join(CSRC, "internal.h"),
            os.path.join(CSRC, "host_internal.h"), os.path.join(CSRC, "qmap.hpp"),
            os.path.join(CSRC, "stepdiv.hpp"), os.path.join(CSRC, "ou_testing.h"),
+           os.path.join(CSRC, "stream.hpp"),
            os.path.join(os.path.dirname(HERE), "include", "optimizer_update.h")]
 
 HIPCC_FLAGS = [

@@ -46,6 +46,10 @@ hipError_t launch(const void* fn, int64_t grid, int block, int lds, void** args,
 
 // log2 of the XCD tile run for a grid (xcd_tile), or -1, after forcing.
 int xcd_log2_for(int64_t grid, int run);
+// Launch shape of the single-tensor update (plain = false: the clipped
+// step's parameter pass), and the test hooks' forcing of it.
+SingleLaunch select_single(const DeviceProps& d, int kind, int dtype, int64_t n, bool vec, bool plain);
+void apply_single_forcing(SingleLaunch* L, bool* vec);
 int xcd_run_forced(int run);
 
 // A plan's work list in launch order: block b (items [b*per_block,
