@@ -252,8 +252,9 @@ StepScalars make_scalars(const ou_hparams& h, int decay_after)
 // dwordx4 of each fp32 stream, dwordx2 of a 16-bit one).  Small tensors (the
 // launch-latency regime) get one block sized to the tensor.  Large ones get
 // one-wave blocks of 2 groups per lane (a 512-element tile per block), a
-// grid that covers the tensor, at most 8 resident blocks per CU once the
-// grid oversubscribes the CUs 4 times over, and tiles in runs of 64 per XCD.
+// grid that covers the tensor, a cap on resident blocks per CU once the
+// grid oversubscribes the CUs 4 times over (single_blocks_per_cu), and
+// tiles in runs of 64 per XCD.
 // Measured on MI355X in 21 interleaved rounds per case against the earlier
 // shapes (256 x 2 at two blocks per CU and runs of 16; fp32 Adam 128 x 4 and
 // runs of 32): Adam and AdEMAMix, fp32 and bf16 storage, 2^28 and 2^30
@@ -276,6 +277,21 @@ constexpr int kXcdRunClip = 64;
 constexpr int kXcdRunMulti = 16;
 constexpr int kSingleBlocksPerCu = 8;
 
+// Resident one-wave blocks per CU of a large single tensor.  With fp32
+// storage the two-state kinds keep fewer tiles in flight: measured on
+// MI355X in 12-16 interleaved rounds per cap on two boxes, fp32 Adam ran
+// 0.4-1.5% faster at 7 than at 8 (2^28 and 2^30 elements) and fp32
+// AdEMAMix (five fp32 streams read) 1-3.8% faster at 6 than at 8 at 2^28,
+// level at 2^30; 16-bit storage and the one-state kinds were level from 8
+// to 12 and keep 8.
+int single_blocks_per_cu(int kind, int dtype)
+{
+    if (dtype != OU_F32) return kSingleBlocksPerCu;
+    if (kind == OU_ADAM) return 7;
+    if (kind == OU_ADEMAMIX) return 6;
+    return kSingleBlocksPerCu;
+}
+
 // Tile runs per XCD (xcd_tile): log2 of the run length for grids of at
 // least 64 runs, else -1 (block order).
 int xcd_log2_for(int64_t grid, int run)
@@ -294,8 +310,6 @@ int xcd_run_forced(int run)
 
 SingleLaunch select_single(const DeviceProps& d, int kind, int dtype, int64_t n, bool vec, bool plain)
 {
-    (void)kind;
-    (void)dtype;
     SingleLaunch L;
     L.epl = 4;
     L.lds = 0;
@@ -315,7 +329,7 @@ SingleLaunch select_single(const DeviceProps& d, int kind, int dtype, int64_t n,
     L.grid = std::max<int64_t>(1, std::min<int64_t>((units + per_block - 1) / per_block, INT32_MAX));
     // cap only when the grid oversubscribes the CUs several times over
     if (plain && d.cu_count > 0 && L.grid >= 4LL * kSingleBlocksPerCu * d.cu_count)
-        L.lds = lds_cap(d, kSingleBlocksPerCu);
+        L.lds = lds_cap(d, single_blocks_per_cu(kind, dtype));
     L.xcd_log2 = xcd_log2_for(L.grid, plain ? kXcdRun : kXcdRunClip);
     return L;
 }

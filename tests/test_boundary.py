@@ -287,14 +287,16 @@ def test_dispatch_with_mocked_device(L, cu, lds_cu, lds_blk):
     """Launch selection from fabricated device properties: the grid covers
     the tensor, blocks are whole waves, small tensors get one block, the
     occupancy cap of grids that oversubscribe the CUs reserves LDS so that
-    exactly eight one-wave blocks fit per CU (or none when the device
-    reports no LDS size), and the choice depends only on the arguments."""
+    exactly the kind's number of one-wave blocks fit per CU (7 for fp32
+    Adam, 6 for fp32 AdEMAMix, 8 otherwise; none when the device reports no
+    LDS size), and the choice depends only on the arguments."""
     out = (ctypes.c_int64 * 5)()
-    for n in (1, 2, 31, 64, 255, 256, 1023, 1024, 1025, 4095, 4096, 4097, 65539, 1 << 20,
-              (1 << 28) + 3, 1 << 30):
-        for dtype in (0, 1, 2):
+    for kind, dtype in ((k, d) for k in (0, 1, 2, 5) for d in (0, 1, 2)):
+        per_cu = {(0, 0): 7, (1, 0): 6}.get((kind, dtype), 8)
+        for n in (1, 2, 31, 64, 255, 256, 1023, 1024, 1025, 4095, 4096, 4097, 65539, 1 << 20,
+                  (1 << 28) + 3, 1 << 30):
             for aligned in (0, 1):
-                assert L.ou__select_single(cu, lds_cu, lds_blk, 0, dtype, n, aligned, out) == 0
+                assert L.ou__select_single(cu, lds_cu, lds_blk, kind, dtype, n, aligned, out) == 0
                 block, epl, unroll, grid, lds = list(out)
                 assert block % 64 == 0 and 64 <= block <= 1024
                 assert epl in (4, 8) and unroll in (1, 2, 4)
@@ -305,12 +307,12 @@ def test_dispatch_with_mocked_device(L, cu, lds_cu, lds_blk):
                 if units <= 1024:
                     assert grid * block >= units and grid <= 16 and lds == 0
                 if lds:
-                    assert 8 * lds <= lds_cu < 9 * lds and lds <= lds_blk and grid >= 32 * cu
-                    assert block == 64
+                    assert per_cu * lds <= lds_cu < (per_cu + 1) * lds and lds <= lds_blk
+                    assert grid >= 32 * cu and block == 64
                 elif lds_cu and grid >= 32 * cu:
                     raise AssertionError("large grids get the occupancy cap")
                 again = (ctypes.c_int64 * 5)()
-                L.ou__select_single(cu, lds_cu, lds_blk, 0, dtype, n, aligned, again)
+                L.ou__select_single(cu, lds_cu, lds_blk, kind, dtype, n, aligned, again)
                 assert list(again) == list(out)
 
 
