@@ -336,8 +336,11 @@ SingleLaunch select_single(const DeviceProps& d, int kind, int dtype, int64_t n,
 
 // Multi tensor: waves per block, EPL and unroll; the chunk (elements per
 // work item) is a multiple of 64 * EPL * unroll so chunk starts keep 16-byte
-// alignment.  Large collections get the shape and the cap of eight resident
-// blocks per CU of large single tensors.
+// alignment.  Large collections get the shape and the residency cap of
+// large single tensors (single_blocks_per_cu): with fp32 storage over the
+// 505-tensor collection (287.9 M elements), 16 interleaved rounds per cap,
+// Adam ran 3.6% faster at 7 blocks per CU than at 8 and AdEMAMix 4.7%
+// faster at 6.
 // Measured on MI355X in 15 interleaved rounds per shape with the 505-tensor
 // bf16 collection (287.9 M elements) and its 408 tensors of <= 16,384
 // elements (3.4 M): a large collection runs as the large single tensor
@@ -351,15 +354,14 @@ SingleLaunch select_single(const DeviceProps& d, int kind, int dtype, int64_t n,
 // <= 4,096 elements takes 4.4-4.6 us in every shape (bound by the launch).
 constexpr int64_t kLargeCollection = int64_t(1) << 24;
 
-MultiLaunch select_multi(const DeviceProps& d, int dtype, int64_t total_elements)
+MultiLaunch select_multi(const DeviceProps& d, int kind, int dtype, int64_t total_elements)
 {
-    (void)dtype;
     MultiLaunch L;
     L.epl = 4;
     if (total_elements >= kLargeCollection) {
         L.waves = 1;
         L.unroll = 2;
-        L.lds = lds_cap(d, kSingleBlocksPerCu);
+        L.lds = lds_cap(d, single_blocks_per_cu(kind, dtype));
         L.xcd_run = kXcdRun;
     } else {
         L.waves = 4;
@@ -486,7 +488,7 @@ int build_plan(int kind_arg, const ou_segment* segs, int32_t nseg, ou_plan_s** o
     int64_t group_elems[3] = {0, 0, 0};
     for (int i = 0; i < nseg; ++i) group_elems[segs[i].dtype] += segs[i].n;
     for (int dt = 0; dt < 3; ++dt) {
-        hg[dt].L = select_multi(*dp, dt, group_elems[dt]);
+        hg[dt].L = select_multi(*dp, kind, dt, group_elems[dt]);
         if (int w = g_force_waves.load()) hg[dt].L.waves = w;
         if (int e = g_force_mepl.load()) hg[dt].L.epl = e;
         if (int u = g_force_munroll.load()) hg[dt].L.unroll = u;
