@@ -277,18 +277,19 @@ constexpr int kXcdRunClip = 64;
 constexpr int kXcdRunMulti = 16;
 constexpr int kSingleBlocksPerCu = 8;
 
-// Resident one-wave blocks per CU of a large single tensor.  With fp32
-// storage the two-state kinds keep fewer tiles in flight: measured on
-// MI355X in 12-16 interleaved rounds per cap on two boxes, fp32 Adam ran
-// 0.4-1.5% faster at 7 than at 8 (2^28 and 2^30 elements) and fp32
-// AdEMAMix (five fp32 streams read) 1-3.8% faster at 6 than at 8 at 2^28,
-// level at 2^30; 16-bit storage and the one-state kinds were level from 8
-// to 12 and keep 8.
+// Resident one-wave blocks per CU of a large single tensor or collection,
+// from the bytes a tile reads per element (2 storage values and 1-3 fp32
+// states): the more it reads, the fewer tiles in flight keep the streams'
+// DRAM accesses local.  Measured on MI355X in 10-20 interleaved rounds per
+// cap on four boxes: reading 20 B (fp32 AdEMAMix) 6 beat 8 by 0.1-4.7%,
+// reading 16 B (fp32 Adam, 16-bit AdEMAMix) 7 beat 8 by 0.1-3.9%, reading
+// 12 B or less (16-bit Adam, the one-state kinds) 8 was level with 10-12.
 int single_blocks_per_cu(int kind, int dtype)
 {
-    if (dtype != OU_F32) return kSingleBlocksPerCu;
-    if (kind == OU_ADAM) return 7;
-    if (kind == OU_ADEMAMIX) return 6;
+    const int states = kind == OU_ADEMAMIX ? 3 : two_state(kind) ? 2 : 1;
+    const int reads = 2 * storage_bytes(dtype) + 4 * states;
+    if (reads >= 20) return 6;
+    if (reads >= 16) return 7;
     return kSingleBlocksPerCu;
 }
 
@@ -337,10 +338,11 @@ SingleLaunch select_single(const DeviceProps& d, int kind, int dtype, int64_t n,
 // Multi tensor: waves per block, EPL and unroll; the chunk (elements per
 // work item) is a multiple of 64 * EPL * unroll so chunk starts keep 16-byte
 // alignment.  Large collections get the shape and the residency cap of
-// large single tensors (single_blocks_per_cu): with fp32 storage over the
-// 505-tensor collection (287.9 M elements), 16 interleaved rounds per cap,
-// Adam ran 3.6% faster at 7 blocks per CU than at 8 and AdEMAMix 4.7%
-// faster at 6.
+// large single tensors (single_blocks_per_cu): over the 505-tensor
+// collection (287.9 M elements), 10-16 interleaved rounds per cap, fp32
+// Adam ran 3.6-3.9% faster at 7 blocks per CU than at 8, fp32 AdEMAMix
+// 3.8-4.7% faster at 6 and bf16 AdEMAMix 2.5% faster at 7; bf16 Adam was
+// level from 8 to 10.
 // Measured on MI355X in 15 interleaved rounds per shape with the 505-tensor
 // bf16 collection (287.9 M elements) and its 408 tensors of <= 16,384
 // elements (3.4 M): a large collection runs as the large single tensor

@@ -287,12 +287,13 @@ def test_dispatch_with_mocked_device(L, cu, lds_cu, lds_blk):
     """Launch selection from fabricated device properties: the grid covers
     the tensor, blocks are whole waves, small tensors get one block, the
     occupancy cap of grids that oversubscribe the CUs reserves LDS so that
-    exactly the kind's number of one-wave blocks fit per CU (7 for fp32
-    Adam, 6 for fp32 AdEMAMix, 8 otherwise; none when the device reports no
-    LDS size), and the choice depends only on the arguments."""
+    exactly the kind's number of one-wave blocks fit per CU (by the bytes a
+    tile reads per element: 20 B fp32 AdEMAMix 6, 16 B fp32 Adam and 16-bit
+    AdEMAMix 7, 8 otherwise; none when the device reports no LDS size), and
+    the choice depends only on the arguments."""
     out = (ctypes.c_int64 * 5)()
     for kind, dtype in ((k, d) for k in (0, 1, 2, 5) for d in (0, 1, 2)):
-        per_cu = {(0, 0): 7, (1, 0): 6}.get((kind, dtype), 8)
+        per_cu = {(0, 0): 7, (1, 0): 6, (1, 1): 7, (1, 2): 7}.get((kind, dtype), 8)
         for n in (1, 2, 31, 64, 255, 256, 1023, 1024, 1025, 4095, 4096, 4097, 65539, 1 << 20,
                   (1 << 28) + 3, 1 << 30):
             for aligned in (0, 1):
