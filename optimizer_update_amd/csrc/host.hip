@@ -293,6 +293,22 @@ int single_blocks_per_cu(int kind, int dtype)
     return kSingleBlocksPerCu;
 }
 
+// The clipped step's pass 1 (256-thread blocks of 2,048-element chunks,
+// reading p, g, m, v and writing m, v and a partial sum) keeps at most 5
+// blocks (20 waves) per CU once its grid oversubscribes the CUs 4 times
+// over.  Measured on MI355X at 2^28 fp32 elements, per pass in one kernel
+// trace: 1,007 us at 4 or 5 blocks per CU against 1,039 us at full
+// occupancy (8 blocks), 1,022-1,035 us at 6-8 and 1,075-1,216 us at 2-3.
+// Pass 3 ran best with no cap (693 us against 711 us at 8 one-wave
+// blocks per CU) and keeps none.
+constexpr int kClipMomentsBlocksPerCu = 5;
+
+int clip_moments_lds(const DeviceProps& d, int64_t grid)
+{
+    if (d.cu_count <= 0 || grid < 4LL * kClipMomentsBlocksPerCu * d.cu_count) return 0;
+    return lds_cap(d, kClipMomentsBlocksPerCu);
+}
+
 // Tile runs per XCD (xcd_tile): log2 of the run length for grids of at
 // least 64 runs, else -1 (block order).
 int xcd_log2_for(int64_t grid, int run)
@@ -431,6 +447,7 @@ struct Group {
     // binary64 partial sums per item, two floats (fl32(lr*s), s) per segment
     int64_t n_segs;
     int64_t n_clip_items;
+    int clip_lds1;   // dynamic LDS of pass 1 (its residency cap, clip_moments_lds)
     const WorkItem* d_clip_items;
     double2* d_partials;
     float* d_seg_out;
@@ -559,6 +576,7 @@ int build_plan(int kind_arg, const ou_segment* segs, int32_t nseg, ou_plan_s** o
             grp.n_items = static_cast<int64_t>(G.items.size());
             grp.n_segs = static_cast<int64_t>(G.segs.size());
             grp.n_clip_items = static_cast<int64_t>(G.clip_items.size());
+            grp.clip_lds1 = clip_moments_lds(*dp, grp.n_clip_items);
             grp.d_segs = reinterpret_cast<const SegDesc*>(base + off);
             std::memcpy(host.data() + off, G.segs.data(), G.segs.size() * sizeof(SegDesc));
             off = align16(off + G.segs.size() * sizeof(SegDesc));
@@ -650,7 +668,7 @@ int group_launch(int kind, Group& g, int pass, hipKernelNodeParams* kp)
         fn = clip_kernel(11, kind, g.dtype, 0);
         grid = g.n_clip_items;
         block = kClipThreadsHost;
-        lds = 0;
+        lds = g.clip_lds1;
         args = g.clip_args1;
     } else if (pass == 2) {
         fn = clip_kernel(12, kind, g.dtype, 0);
@@ -908,8 +926,7 @@ int clip_step(int kind_arg, int dtype, void* param, const void* grad, float* sta
     int32_t xcd1 = xcd_log2_for(chunks, xcd_run_forced(kXcdRunClip));
     int32_t xcd3 = xcd_log2_for(grid3, xcd_run_forced(kXcdRunClip));
     void* a1[] = {&cp, const_cast<void**>(&grad), &state1, &state2, &n, &sc, &vec_ok, &partials, &xcd1};
-    // pass 1 ends in a block barrier: it runs best at full occupancy
-    int lds1 = 0;
+    int lds1 = clip_moments_lds(*dp, chunks);
     if (int c = g_force_lds.load()) lds1 = c < 0 ? 0 : c;
     hipError_t e = launch(f1, chunks, kClipThreadsHost, lds1, a1, hs);
     if (e != hipSuccess) return hip_fail(e, "launch clip pass 1");
