@@ -678,6 +678,7 @@ int group_launch(int kind, Group& g, int pass, hipKernelNodeParams* kp)
         args = g.clip_args2;
     } else if (pass == 3) {
         fn = clip_kernel(13, kind, g.dtype, 0);
+        lds = 0;   // the parameter pass runs best with no residency cap (clip_moments_lds)
         args = g.clip_args3;
     }
     if (!fn) return fail(OU_EINVAL, "no kernel for pass %d, dtype %d", pass, g.dtype);
