@@ -551,6 +551,15 @@ def bench_collection(torch, ou, W, dev, time_rounds):
             d["plan_cold"] = _us(time_cold(torch, lambda: opt.step(), flush))
             del flush
         d["plan_describe"] = opt.plan.describe()
+        if label == "full_505":
+            # update-norm clipping per tensor over the same collection: pass 1
+            # reads p, g, m, v and writes m, v (20 B/element in bf16), pass 3
+            # reads p, m, v and writes p (12 B/element)
+            copt = ou.AdamW32(opt.params, lr=1e-3, weight_decay=0.01, grads=opt.grads, max_unorm=1e-3)
+            r = time_rounds(lambda: copt.step(), iters=20, rounds=7, warmup=5)
+            d["plan_max_unorm"] = _us(r)
+            d["plan_max_unorm_GBps"] = round(32 * elems / (r["median_ms"] * 1e-3) / 1e9, 1)
+            copt.close()
         res[label] = d
         opt.close()
         torch.cuda.empty_cache()
