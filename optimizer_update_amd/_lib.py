@@ -133,6 +133,8 @@ def load(path: str = LIBRARY) -> ctypes.CDLL:
     # test hooks (not in the public header)
     lib.ou__select_single.argtypes = [i32, i32, i32, i32, i32, i64, i32, ctypes.POINTER(i64)]
     lib.ou__select_single.restype = i32
+    lib.ou__select_multi.argtypes = [i32, i32, i32, i32, i32, i64, ctypes.POINTER(i64)]
+    lib.ou__select_multi.restype = i32
     lib.ou__force_single.argtypes = [i32, i32, i32, i64, i32, i32]
     lib.ou__force_single.restype = None
     lib.ou__force_multi.argtypes = [i32, i32, i32, i32, i32]

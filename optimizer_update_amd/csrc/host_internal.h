@@ -50,6 +50,12 @@ int xcd_log2_for(int64_t grid, int run);
 // step's parameter pass), and the test hooks' forcing of it.
 SingleLaunch select_single(const DeviceProps& d, int kind, int dtype, int64_t n, bool vec, bool plain);
 void apply_single_forcing(SingleLaunch* L, bool* vec);
+// Launch shape and chunk (elements per work item) of a plan's dtype group
+// holding `total_elements`, before any test forcing.
+MultiLaunch select_multi(const DeviceProps& d, int kind, int dtype, int64_t total_elements);
+int64_t select_chunk(int64_t total_elements);
+// Dynamic LDS of the clipped step's pass 1 for a grid of `grid` chunks.
+int clip_moments_lds(const DeviceProps& d, int64_t grid);
 int xcd_run_forced(int run);
 
 // A plan's work list in launch order: block b (items [b*per_block,

@@ -14,6 +14,28 @@ using namespace ou;
 extern "C" {
 
 __attribute__((visibility("default")))
+int ou__select_multi(int cu_count, int lds_per_cu, int lds_per_block, int kind, int dtype, int64_t total_elements,
+                     int64_t out[7])
+{
+    if (!out || cu_count < 0 || lds_per_cu < 0 || lds_per_block < 0 || total_elements < 0) return OU_EINVAL;
+    DeviceProps d;
+    d.cu_count = cu_count;
+    d.lds_per_cu = lds_per_cu;
+    d.lds_per_block = lds_per_block;
+    d.gfx950 = true;
+    const MultiLaunch L = select_multi(d, kind, dtype, total_elements);
+    out[0] = L.waves;
+    out[1] = L.epl;
+    out[2] = L.unroll;
+    out[3] = L.lds;
+    out[4] = L.xcd_run;
+    out[5] = select_chunk(total_elements);
+    // pass 1 of a clipped step over the same elements, one block per chunk
+    out[6] = clip_moments_lds(d, (total_elements + kClipChunkElems - 1) / kClipChunkElems);
+    return OU_OK;
+}
+
+__attribute__((visibility("default")))
 int ou__narrow(int dtype, const float* in, uint16_t* out, int64_t n, void* stream)
 {
     const bool pairs = dtype >= 16;

@@ -21,6 +21,12 @@ extern "C" {
 int ou__select_single(int cu_count, int lds_per_cu, int lds_per_block, int kind, int dtype, int64_t n,
                       int aligned, int64_t out[5]);
 
+// Launch shape a plan would pick for a dtype group of `total_elements`
+// on such a device: out = {waves, epl, unroll, lds, xcd_run, chunk, lds of
+// the clipped step's pass 1 over as many elements}.
+int ou__select_multi(int cu_count, int lds_per_cu, int lds_per_block, int kind, int dtype,
+                     int64_t total_elements, int64_t out[7]);
+
 // Force the single-tensor launch shape (0 = no forcing for that field;
 // lds -1 = no occupancy cap); scalar_only != 0 forces the
 // one-element-per-lane path.  Process-wide.

@@ -53,7 +53,7 @@ def test_exports_every_header_function(L):
     assert exported - set(names) == {"ou__select_single", "ou__force_single", "ou__force_multi",
                                      "ou__step_scalars", "ou__force_8bit", "ou__validate_only",
                                      "ou__force_xcd", "ou__stream_probe", "ou__narrow",
-                                     "ou__sqrt", "ou__recip8", "ou__valu_probe"}
+                                     "ou__sqrt", "ou__recip8", "ou__valu_probe", "ou__select_multi"}
 
 
 def test_header_is_plain_c_and_matches_ctypes_layout(tmp_path):
@@ -315,6 +315,38 @@ def test_dispatch_with_mocked_device(L, cu, lds_cu, lds_blk):
                 again = (ctypes.c_int64 * 5)()
                 L.ou__select_single(cu, lds_cu, lds_blk, kind, dtype, n, aligned, again)
                 assert list(again) == list(out)
+
+
+@pytest.mark.parametrize("cu,lds_cu,lds_blk", [(80, 65536, 65536), (256, 163840, 163840), (256, 0, 0)])
+def test_plan_shape_selection(L, cu, lds_cu, lds_blk):
+    """A plan's dtype group: collections of 2^24 elements or more take
+    one-wave blocks of 512-element work items in runs of 64 with the
+    single-tensor cap for the kind and storage (6, 7 or 8 blocks per CU by the
+    bytes read per element; none when the device reports no LDS size);
+    smaller ones 4-wave blocks of 256-element items, no cap, runs of 16.  The
+    clipped step's pass 1 keeps 5 blocks per CU once its grid of 2,048-element
+    chunks is 20 times the CU count."""
+    out = (ctypes.c_int64 * 7)()
+    for kind, dtype in ((k, d) for k in (0, 1, 2, 5) for d in (0, 1, 2)):
+        per_cu = {(0, 0): 7, (1, 0): 6, (1, 1): 7, (1, 2): 7}.get((kind, dtype), 8)
+        for total in (1, 4096, 3440640, (1 << 24) - 1, 1 << 24, 287866880):
+            assert L.ou__select_multi(cu, lds_cu, lds_blk, kind, dtype, total, out) == 0
+            waves, epl, unroll, lds, run, chunk, lds1 = list(out)
+            assert epl == 4 and chunk % (64 * epl * unroll) == 0 and waves * 64 <= 512
+            if total >= 1 << 24:
+                assert (waves, unroll, run, chunk) == (1, 2, 64, 512)
+                if lds_cu:
+                    assert per_cu * lds <= lds_cu < (per_cu + 1) * lds and lds <= lds_blk
+                else:
+                    assert lds == 0
+            else:
+                assert (waves, unroll, lds, run, chunk) == (4, 1, 0, 16, 256)
+            chunks = -(-total // 2048)
+            if lds_cu and chunks >= 20 * cu:
+                assert 5 * lds1 <= lds_cu < 6 * lds1
+            else:
+                assert lds1 == 0
+    assert L.ou__select_multi(cu, lds_cu, lds_blk, 0, 0, -1, out) == OU_EINVAL
 
 
 def test_step_scalars_match_oracle_bitwise(L):
