@@ -107,7 +107,7 @@ def _stream_arg(stream) -> int:
 
 def _on(index: int, fn, *args):
     """fn(*args) with device `index` current, switching only when it is not."""
-    prev = torch.cuda.current_device()
+    prev = _GET_DEVICE()
     if prev == index:
         return fn(*args)
     torch.cuda.set_device(index)
@@ -142,34 +142,50 @@ class _on_device:
         return False
 
 
-def _tensor_args(kind: int, param, grad, state1, state2) -> tuple[int, int]:
+def _tensor_args(kind: int, param, grad, state1, state2) -> tuple[int, int, int]:
+    """Check one tensor's four operands; returns (n, dtype code, device index).
+    The common case costs one attribute read per property and tensor; the
+    specific error is worked out only when a check fails."""
     kind &= ~_lib.OU_DECAY_AFTER
     two = kind in TWO_STATE
     if not two and state2 is not None:
         raise ValueError("the one-state kinds take state2=None")
-    named = [("param", param), ("grad", grad), ("state1", state1)]
-    if two:
-        named.append(("state2", state2))
-    for name, t in named:
-        if not isinstance(t, torch.Tensor) or not t.is_cuda:
-            raise ValueError(f"{name} must be a tensor on a HIP device")
-        if not t.is_contiguous():
-            raise ValueError(f"{name} must be contiguous")
-    dt = DTYPES.get(param.dtype)
-    if dt is None or grad.dtype != param.dtype:
+    try:
+        dev = param.get_device()
+        ok = (dev >= 0 and grad.get_device() == dev and state1.get_device() == dev
+              and param.is_contiguous() and grad.is_contiguous() and state1.is_contiguous()
+              and (not two or (state2.get_device() == dev and state2.is_contiguous())))
+    except AttributeError:
+        ok = False
+    if not ok:
+        _tensor_error(param, grad, state1, state2, two)
+    pdt = param.dtype
+    dt = DTYPES.get(pdt)
+    if dt is None or grad.dtype != pdt:
         raise ValueError("param and grad must share one of float32/float16/bfloat16")
     if state1.dtype != torch.float32 or (two and state2.dtype != torch.float32):
         raise ValueError("states must be float32")
     n = param.numel()
-    s1 = 2 * n if kind == _lib.OU_ADEMAMIX else n
+    s1 = state1.numel()
     s2 = state2.numel() if two else 0
-    if grad.numel() != n or state1.numel() != s1 or (two and s2 != n):
-        raise ValueError(f"sizes: param {n}, grad {grad.numel()}, state1 {state1.numel()} "
-                         f"(want {s1}), state2 {s2} (want {n if two else 0})")
-    dev = param.get_device()
-    if grad.get_device() != dev or state1.get_device() != dev or (two and state2.get_device() != dev):
-        raise ValueError("all tensors must be on one device")
-    return n, dt
+    if grad.numel() != n or s1 != (2 * n if kind == _lib.OU_ADEMAMIX else n) or (two and s2 != n):
+        raise ValueError(f"sizes: param {n}, grad {grad.numel()}, state1 {s1} "
+                         f"(want {2 * n if kind == _lib.OU_ADEMAMIX else n}), state2 {s2} "
+                         f"(want {n if two else 0})")
+    return n, dt, dev
+
+
+def _tensor_error(param, grad, state1, state2, two: bool):
+    """Raise the ValueError that names the first operand failing a check."""
+    named = [("param", param), ("grad", grad), ("state1", state1)]
+    if two:
+        named.append(("state2", state2))
+    for name, t in named:
+        if not isinstance(t, torch.Tensor) or t.get_device() < 0:
+            raise ValueError(f"{name} must be a tensor on a HIP device")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    raise ValueError("all tensors must be on one device")
 
 
 def _ptr(t) -> int | None:
@@ -185,12 +201,16 @@ def optimizer_update_32bit(kind, param: torch.Tensor, grad: torch.Tensor, state1
     decay_after: decay the updated parameter, (p - lr*u)*d (Adam, AdEMAMix,
     Lion)."""
     k = _kind(kind, decay_after)
-    n, dt = _tensor_args(k, param, grad, state1, state2)
+    n, dt, dev = _tensor_args(k, param, grad, state1, state2)
     lib = load()
-    st = _on(param.get_device(), lib.optimizer_update_32bit, k, dt, param.data_ptr(),
-             grad.data_ptr(), state1.data_ptr(), _ptr(state2), n, beta1, beta2, beta3, alpha,
-             eps, weight_decay, int(step), lr, int(bool(skip_zeros)), _stream(param, stream))
-    check(st, lib)
+    args = (k, dt, param.data_ptr(), grad.data_ptr(), state1.data_ptr(),
+            None if state2 is None else state2.data_ptr(), n, beta1, beta2, beta3, alpha, eps,
+            weight_decay, int(step), lr, int(bool(skip_zeros)),
+            _raw_stream(dev) if stream is None else _stream_arg(stream))
+    fn = lib.optimizer_update_32bit
+    st = fn(*args) if _GET_DEVICE() == dev else _on(dev, fn, *args)
+    if st:
+        check(st, lib)
 
 
 def clip_workspace_bytes(n: int) -> int:
@@ -221,7 +241,7 @@ def optimizer_update_32bit_clip(kind, param: torch.Tensor, grad: torch.Tensor,
     ``clip_workspace_bytes(n)`` bytes (allocated here if None); returned so
     that ``clip_scale`` can read the clip factor."""
     k = _kind(kind, decay_after)
-    n, dt = _tensor_args(k, param, grad, state1, state2)
+    n, dt, _ = _tensor_args(k, param, grad, state1, state2)
     if workspace is None and max_unorm > 0 and n > 0:
         workspace = clip_workspace(n, param.device)
     if workspace is not None and (not workspace.is_cuda or workspace.dtype != torch.uint8
@@ -252,7 +272,7 @@ def optimizer_update_32bit_clip_noalloc(kind, param: torch.Tensor, grad: torch.T
     (n up to ``clip_noalloc_max_elements()``).  Calls that overlap in time
     on one GPU share that scratch and race."""
     k = _kind(kind, decay_after)
-    n, dt = _tensor_args(k, param, grad, state1, state2)
+    n, dt, _ = _tensor_args(k, param, grad, state1, state2)
     lib = load()
     with _on_device(param.device):
         st = lib.optimizer_update_32bit_clip_noalloc(k, dt, param.data_ptr(), grad.data_ptr(),
@@ -271,7 +291,7 @@ def clip_noalloc_max_elements() -> int:
 def _segments(kind: int, segments) -> ctypes.Array:
     arr = (_lib.ou_segment * len(segments))()
     for i, (p, g, s1, s2) in enumerate(segments):
-        n, dt = _tensor_args(kind, p, g, s1, s2)
+        n, dt, _ = _tensor_args(kind, p, g, s1, s2)
         arr[i] = _lib.ou_segment(p.data_ptr(), g.data_ptr(), s1.data_ptr(), _ptr(s2), n, dt, 0)
     return arr
 
@@ -404,15 +424,23 @@ def state8_sizes(kind, n: int) -> tuple[int, int, int, int]:
     return k * n, n, k * nb, nb
 
 
-def _tensor8_args(kind: int, param, grad, state1, state2, absmax1, absmax2) -> tuple[int, int]:
-    for name, t in (("param", param), ("grad", grad), ("state1", state1), ("state2", state2),
-                    ("absmax1", absmax1), ("absmax2", absmax2)):
-        if not isinstance(t, torch.Tensor) or not t.is_cuda:
-            raise ValueError(f"{name} must be a tensor on a HIP device")
-        if not t.is_contiguous():
-            raise ValueError(f"{name} must be contiguous")
-        if t.device != param.device:
-            raise ValueError("all tensors must be on one device")
+def _tensor8_args(kind: int, param, grad, state1, state2, absmax1,
+                  absmax2) -> tuple[int, int, int]:
+    """Check the six operands of an 8-bit update; returns (n, dtype code,
+    device index)."""
+    ts = (param, grad, state1, state2, absmax1, absmax2)
+    try:
+        dev = param.get_device()
+        ok = dev >= 0 and all(t.get_device() == dev and t.is_contiguous() for t in ts)
+    except AttributeError:
+        ok = False
+    if not ok:
+        for name, t in zip(("param", "grad", "state1", "state2", "absmax1", "absmax2"), ts):
+            if not isinstance(t, torch.Tensor) or t.get_device() < 0:
+                raise ValueError(f"{name} must be a tensor on a HIP device")
+            if not t.is_contiguous():
+                raise ValueError(f"{name} must be contiguous")
+        raise ValueError("all tensors must be on one device")
     dt = DTYPES.get(param.dtype)
     if dt is None or grad.dtype != param.dtype:
         raise ValueError("param and grad must share one of float32/float16/bfloat16")
@@ -425,7 +453,7 @@ def _tensor8_args(kind: int, param, grad, state1, state2, absmax1, absmax2) -> t
     got = (state1.numel(), state2.numel(), absmax1.numel(), absmax2.numel())
     if grad.numel() != n or got != want:
         raise ValueError(f"sizes: n {n}, grad {grad.numel()}, states/absmax {got} (want {want})")
-    return n, dt
+    return n, dt, dev
 
 
 def optimizer_update_8bit_blockwise(kind, param: torch.Tensor, grad: torch.Tensor,
@@ -438,15 +466,16 @@ def optimizer_update_8bit_blockwise(kind, param: torch.Tensor, grad: torch.Tenso
     """One update with 8-bit block-wise states (uint8 codes, fp32 absmax per
     256 elements), in place."""
     k = _kind(kind, decay_after)
-    n, dt = _tensor8_args(k, param, grad, state1, state2, absmax1, absmax2)
+    n, dt, dev = _tensor8_args(k, param, grad, state1, state2, absmax1, absmax2)
     lib = load()
-    with _on_device(param.device):
-        st = lib.optimizer_update_8bit_blockwise(k, dt, param.data_ptr(), grad.data_ptr(),
-                                                 state1.data_ptr(), state2.data_ptr(),
-                                                 absmax1.data_ptr(), absmax2.data_ptr(), n, beta1,
-                                                 beta2, beta3, alpha, eps, weight_decay, int(step),
-                                                 lr, int(bool(skip_zeros)), _stream(param, stream))
-    check(st, lib)
+    args = (k, dt, param.data_ptr(), grad.data_ptr(), state1.data_ptr(), state2.data_ptr(),
+            absmax1.data_ptr(), absmax2.data_ptr(), n, beta1, beta2, beta3, alpha, eps,
+            weight_decay, int(step), lr, int(bool(skip_zeros)),
+            _raw_stream(dev) if stream is None else _stream_arg(stream))
+    fn = lib.optimizer_update_8bit_blockwise
+    st = fn(*args) if _GET_DEVICE() == dev else _on(dev, fn, *args)
+    if st:
+        check(st, lib)
 
 
 class Plan8:
@@ -460,7 +489,7 @@ class Plan8:
                        else torch.device("cuda", torch.cuda.current_device()))
         arr = (_lib.ou_segment8 * len(self._tensors))()
         for i, s in enumerate(self._tensors):
-            n, dt = _tensor8_args(self.kind, *s)
+            n, dt, _ = _tensor8_args(self.kind, *s)
             arr[i] = _lib.ou_segment8(*(t.data_ptr() for t in s), n, dt, 0)
         self._lib = load()
         h = ctypes.c_void_p()

@@ -282,3 +282,59 @@ def test_one_graph_over_several_plans(kind):
                 assert u.cpu().view(torch.uint8).numpy().tobytes() == v.cpu().view(torch.uint8).numpy().tobytes()
     for p in ref[3:] + got[3:]:
         p.close()
+
+
+def test_direct_ops_name_the_bad_operand():
+    """The binding's checks of the direct ops: each kind of bad operand is
+    refused with a ValueError naming it, before anything is launched, and a
+    good call afterwards still updates."""
+    import optimizer_update_amd as ou
+    n = 1000
+    p, g, m, v = (torch.zeros(n, device="cuda") for _ in range(4))
+    g.fill_(1e-3)
+
+    def call(*ts, kind="adam"):
+        ou.optimizer_update_32bit(kind, *ts, step=1, lr=1e-3)
+
+    strided = torch.zeros(2 * n, device="cuda")[::2]
+    cases = [((p, g, m.cpu(), v), "adam", "state1 must be a tensor on a HIP device"),
+             ((p, g, 1.0, v), "adam", "state1 must be a tensor on a HIP device"),
+             ((p, strided, m, v), "adam", "grad must be contiguous"),
+             ((p, g, m, strided), "adam", "state2 must be contiguous"),
+             ((p, g, m, v), "lion", "one-state kinds take state2=None"),
+             ((p, g.bfloat16(), m, v), "adam", "param and grad must share"),
+             ((p.double(), g.double(), m, v), "adam", "param and grad must share"),
+             ((p, g, m.double(), v), "adam", "states must be float32"),
+             ((p, g, m[:-1], v), "adam", "sizes"),
+             ((p, g, m, v), "ademamix", "sizes"),
+             ((p, g[:-1], m, v), "adam", "sizes")]
+    for ts, kind, msg in cases:
+        with pytest.raises(ValueError, match=msg):
+            call(*ts, kind=kind)
+    torch.cuda.synchronize()
+    assert p.abs().sum().item() == 0            # nothing ran
+    call(p, g, m, v)
+    torch.cuda.synchronize()
+    assert (p < 0).all().item()                 # the good call stepped against g > 0
+
+    sizes = ou.state8_sizes("adam", n)
+    c1, c2 = (torch.zeros(s, dtype=torch.uint8, device="cuda") for s in sizes[:2])
+    a1, a2 = (torch.zeros(s, device="cuda") for s in sizes[2:])
+
+    def call8(*ts):
+        ou.optimizer_update_8bit_blockwise("adam", *ts, step=1, lr=1e-3)
+
+    cases8 = [((p, g, c1, c2, a1.cpu(), a2), "absmax1 must be a tensor on a HIP device"),
+              ((p, g, c1, c2, a1, None), "absmax2 must be a tensor on a HIP device"),
+              ((p, g, c1, torch.zeros(2 * n, dtype=torch.uint8, device="cuda")[::2], a1, a2),
+               "state2 must be contiguous"),
+              ((p, g, c1.float(), c2, a1, a2), "8-bit states must be uint8"),
+              ((p, g, c1, c2, a1.double(), a2), "absmax buffers must be float32"),
+              ((p, g, c1[:-1], c2, a1, a2), "sizes")]
+    for ts, msg in cases8:
+        with pytest.raises(ValueError, match=msg):
+            call8(*ts)
+    before = p.clone()
+    call8(p, g, c1, c2, a1, a2)
+    torch.cuda.synchronize()
+    assert (p < before).all().item()
