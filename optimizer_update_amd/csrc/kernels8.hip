@@ -27,6 +27,8 @@
 // are long enough to amortize the table copy.  Per block the chain costs
 // about 300 VALU instructions against 2.5-4 KiB of HBM traffic, so the
 // kernel sits between the two rooflines rather than on either.
+#include <type_traits>
+
 #include "internal.h"
 #include "qmap.hpp"
 
@@ -169,6 +171,54 @@ __device__ __forceinline__ float recip_max(float l)
     return (l > 0.0f && l < __builtin_huge_valf()) ? static_cast<float>(y) : 0.0f;
 }
 
+// Buffer resources over the arrays of one run of whole blocks, based at the
+// run's first block b0.  Inside the run an access is the lane's 32-bit byte
+// offset (a vector register that never changes) plus the block's byte
+// offset from b0 (a scalar register), so a block takes no vector address
+// arithmetic; the accesses are non-temporal like the per-pointer ones.  The
+// record count is the largest the descriptor holds, as every offset stays
+// within the run's few kilobytes.
+struct Run8 {
+    __amdgpu_buffer_rsrc_t p, g, c1, c2, c3;
+    int64_t b0;
+};
+
+constexpr int kBufRsrcWord3 = 0x00020000;   // raw 32-bit records (CDNA descriptor format)
+constexpr int kBufNonTemporal = 2;          // cache-policy operand: nt
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t run_rsrc(const void* base)
+{
+    // the address is the same on every lane: read it from the first, so the
+    // descriptor is known to sit in scalar registers
+    const uint64_t a = reinterpret_cast<uint64_t>(base);
+    const uint32_t lo = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(a)));
+    const uint32_t hi = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(a >> 32)));
+    void* const u = reinterpret_cast<void*>((static_cast<uint64_t>(hi) << 32) | lo);
+    return __builtin_amdgcn_make_buffer_rsrc(u, 0, 0x7fffffff, kBufRsrcWord3);
+}
+
+template <int KIND, typename S>
+__device__ __forceinline__ Run8 make_run8(const Seg8& d, int64_t b0)
+{
+    using raw = typename S::raw;
+    Run8 r;
+    const int64_t e = b0 * kQBlock;
+    r.p = run_rsrc(static_cast<const raw*>(d.p) + e);
+    r.g = run_rsrc(static_cast<const raw*>(d.g) + e);
+    r.c1 = run_rsrc(d.c1 + e);
+    r.c2 = run_rsrc(d.c2 + e);
+    r.c3 = run_rsrc(KIND == kAdemamix ? d.c1 + d.n + e : d.c1 + e);
+    r.b0 = b0;
+    return r;
+}
+
+// Byte offset of block b from the run's start in an array of T.
+template <typename T>
+__device__ __forceinline__ int32_t run_off(const Run8& r, int64_t b)
+{
+    return static_cast<int32_t>((b - r.b0) * kQBlock * static_cast<int64_t>(sizeof(T)));
+}
+
 // The inputs of one quantization block, as loaded by one wave: lane l
 // holds elements 4l .. 4l+3.  WIDE: the block is known to be whole and on
 // the wide path (no per-element checks).
@@ -182,7 +232,7 @@ struct Block8 {
 };
 
 template <int KIND, typename S, bool WIDE>
-__device__ __forceinline__ Block8<S> load_block8(const Seg8& d, int64_t b, int lane)
+__device__ __forceinline__ Block8<S> load_block8(const Seg8& d, int64_t b, int lane, const Run8& run)
 {
     using raw = typename S::raw;
     constexpr bool kMix = KIND == kAdemamix;
@@ -203,9 +253,30 @@ __device__ __forceinline__ Block8<S> load_block8(const Seg8& d, int64_t b, int l
     bool* live = in.live;
     uint32_t w1 = 0, w2 = 0, w3 = 0;
     if (in.full) {
+        // lane l's four elements: 4l .. 4l+3 of the block
+        using Vec = typename std::conditional<S::bytes == 4, u32x4, u32x2>::type;
+        Vec xp, xg;
+        if constexpr (WIDE) {
+            const uint32_t lo = static_cast<uint32_t>(lane) * 4u;   // byte offset of the lane's codes
+            const int32_t so = run_off<raw>(run, b), sc = run_off<uint8_t>(run, b);
+            if constexpr (S::bytes == 4) {
+                xp = __builtin_amdgcn_raw_buffer_load_b128(run.p, lo * 4u, so, kBufNonTemporal);
+                xg = __builtin_amdgcn_raw_buffer_load_b128(run.g, lo * 4u, so, kBufNonTemporal);
+            } else {
+                xp = __builtin_amdgcn_raw_buffer_load_b64(run.p, lo * 2u, so, kBufNonTemporal);
+                xg = __builtin_amdgcn_raw_buffer_load_b64(run.g, lo * 2u, so, kBufNonTemporal);
+            }
+            w1 = __builtin_amdgcn_raw_buffer_load_b32(run.c1, lo, sc, kBufNonTemporal);
+            w2 = __builtin_amdgcn_raw_buffer_load_b32(run.c2, lo, sc, kBufNonTemporal);
+            if constexpr (kMix) w3 = __builtin_amdgcn_raw_buffer_load_b32(run.c3, lo, sc, kBufNonTemporal);
+        } else {
+            xp = __builtin_nontemporal_load(reinterpret_cast<const Vec*>(p + e0));
+            xg = __builtin_nontemporal_load(reinterpret_cast<const Vec*>(g + e0));
+            w1 = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(c1 + e0));
+            w2 = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(c2 + e0));
+            if constexpr (kMix) w3 = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(c1 + n + e0));
+        }
         if constexpr (S::bytes == 4) {
-            const u32x4 xp = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p + e0));
-            const u32x4 xg = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(g + e0));
             // Elements are copied to scalars before the bit cast: this
             // compiler reads element 0 for a bit cast of a vector element.
             const uint32_t p0 = xp.x, p1 = xp.y, p2 = xp.z, p3 = xp.w;
@@ -215,16 +286,11 @@ __device__ __forceinline__ Block8<S> load_block8(const Seg8& d, int64_t b, int l
             graw[0] = __builtin_bit_cast(float, g0); graw[1] = __builtin_bit_cast(float, g1);
             graw[2] = __builtin_bit_cast(float, g2); graw[3] = __builtin_bit_cast(float, g3);
         } else {
-            const u32x2 xp = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p + e0));
-            const u32x2 xg = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(g + e0));
             praw[0] = static_cast<raw>(xp.x & 0xffffu); praw[1] = static_cast<raw>(xp.x >> 16);
             praw[2] = static_cast<raw>(xp.y & 0xffffu); praw[3] = static_cast<raw>(xp.y >> 16);
             graw[0] = static_cast<raw>(xg.x & 0xffffu); graw[1] = static_cast<raw>(xg.x >> 16);
             graw[2] = static_cast<raw>(xg.y & 0xffffu); graw[3] = static_cast<raw>(xg.y >> 16);
         }
-        w1 = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(c1 + e0));
-        w2 = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(c2 + e0));
-        if constexpr (kMix) w3 = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(c1 + n + e0));
 #pragma unroll
         for (int j = 0; j < 4; ++j) live[j] = true;
     } else {
@@ -250,9 +316,11 @@ __device__ __forceinline__ Block8<S> load_block8(const Seg8& d, int64_t b, int l
 }
 
 // Dequantize, update, requantize and store one block loaded by load_block8.
-template <int KIND, typename S, bool WIDE>
+// DENSE (with WIDE): skip_zeros is off, so every block is dense.
+template <int KIND, typename S, bool WIDE, bool DENSE = false>
 __device__ __forceinline__ void finish_block8(const Seg8& d, int64_t b, const QLds& T,
-                                              const StepScalars& sc, int lane, Block8<S>& in)
+                                              const StepScalars& sc, int lane, Block8<S>& in,
+                                              const Run8& run)
 {
     using raw = typename S::raw;
     constexpr bool kMix = KIND == kAdemamix;
@@ -271,7 +339,8 @@ __device__ __forceinline__ void finish_block8(const Seg8& d, int64_t b, const QL
     // dequantize and update.  A dense block (whole, no skipped elements:
     // wave-uniform) updates every element with no per-element branch, and
     // with 16-bit storage narrows its new parameters in pairs at the store.
-    const bool dense = full && !sc.skip_zeros;
+    // On the wide path the choice is made once per run (DENSE).
+    const bool dense = WIDE ? DENSE : (full && !sc.skip_zeros);
     float m[4], v[4], m2[4], pn[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -344,20 +413,34 @@ __device__ __forceinline__ void finish_block8(const Seg8& d, int64_t b, const QL
 
     // store
     if (full) {
+        const uint32_t lo = static_cast<uint32_t>(lane) * 4u;
         if constexpr (S::bytes == 4) {
             const u32x4 xp = {__builtin_bit_cast(uint32_t, praw[0]), __builtin_bit_cast(uint32_t, praw[1]),
                               __builtin_bit_cast(uint32_t, praw[2]), __builtin_bit_cast(uint32_t, praw[3])};
-            __builtin_nontemporal_store(xp, reinterpret_cast<u32x4*>(p + e0));
+            if constexpr (WIDE)
+                __builtin_amdgcn_raw_buffer_store_b128(xp, run.p, lo * 4u, run_off<raw>(run, b), kBufNonTemporal);
+            else
+                __builtin_nontemporal_store(xp, reinterpret_cast<u32x4*>(p + e0));
         } else {
             const u32x2 xp =
                 dense ? u32x2{S::narrow2(pn[0], pn[1]), S::narrow2(pn[2], pn[3])}
                       : u32x2{static_cast<uint32_t>(praw[0]) | (static_cast<uint32_t>(praw[1]) << 16),
                               static_cast<uint32_t>(praw[2]) | (static_cast<uint32_t>(praw[3]) << 16)};
-            __builtin_nontemporal_store(xp, reinterpret_cast<u32x2*>(p + e0));
+            if constexpr (WIDE)
+                __builtin_amdgcn_raw_buffer_store_b64(xp, run.p, lo * 2u, run_off<raw>(run, b), kBufNonTemporal);
+            else
+                __builtin_nontemporal_store(xp, reinterpret_cast<u32x2*>(p + e0));
         }
-        __builtin_nontemporal_store(o1, reinterpret_cast<uint32_t*>(c1 + e0));
-        __builtin_nontemporal_store(o2, reinterpret_cast<uint32_t*>(c2 + e0));
-        if constexpr (kMix) __builtin_nontemporal_store(o3, reinterpret_cast<uint32_t*>(c1 + n + e0));
+        if constexpr (WIDE) {
+            const int32_t so = run_off<uint8_t>(run, b);
+            __builtin_amdgcn_raw_buffer_store_b32(o1, run.c1, lo, so, kBufNonTemporal);
+            __builtin_amdgcn_raw_buffer_store_b32(o2, run.c2, lo, so, kBufNonTemporal);
+            if constexpr (kMix) __builtin_amdgcn_raw_buffer_store_b32(o3, run.c3, lo, so, kBufNonTemporal);
+        } else {
+            __builtin_nontemporal_store(o1, reinterpret_cast<uint32_t*>(c1 + e0));
+            __builtin_nontemporal_store(o2, reinterpret_cast<uint32_t*>(c2 + e0));
+            if constexpr (kMix) __builtin_nontemporal_store(o3, reinterpret_cast<uint32_t*>(c1 + n + e0));
+        }
     } else {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
@@ -384,14 +467,15 @@ __device__ __forceinline__ void run_blocks8(const Seg8& d, int64_t b0, int64_t s
                                             const QLds& T, const StepScalars& sc, int lane)
 {
     if (count <= 0 || b0 >= d.nb) return;
-    Block8<S> cur = load_block8<KIND, S, false>(d, b0, lane);
+    const Run8 none{};   // per-pointer accesses only
+    Block8<S> cur = load_block8<KIND, S, false>(d, b0, lane, none);
     for (int r = 0; r < count; ++r) {
         const int64_t b = b0 + static_cast<int64_t>(r) * stride;
         const int64_t bn = b + stride;
         const bool more = (r + 1 < count) && bn < d.nb;
         Block8<S> nxt;
-        if (more) nxt = load_block8<KIND, S, false>(d, bn, lane);
-        finish_block8<KIND, S, false>(d, b, T, sc, lane, cur);
+        if (more) nxt = load_block8<KIND, S, false>(d, bn, lane, none);
+        finish_block8<KIND, S, false>(d, b, T, sc, lane, cur, none);
         if (!more) break;
         cur = nxt;
     }
@@ -406,24 +490,37 @@ __device__ __forceinline__ bool wide_run8(const Seg8& d, int64_t b0, int64_t str
 }
 
 // The same blocks when wide_run8 holds, with `a` holding block b0's
-// inputs.  Two block buffers alternate and every load is unconditional,
-// so the loads of one block stay in flight while the other is computed
-// (no register copies between iterations, whose waits would drain them).
-template <int KIND, typename S>
+// inputs and `run` based at b0.  Two block buffers alternate and every load
+// is unconditional, so the loads of one block stay in flight while the
+// other is computed (no register copies between iterations, whose waits
+// would drain them).  DENSE: skip_zeros is off (straight-line blocks).
+template <int KIND, typename S, bool DENSE>
 __device__ __forceinline__ void run_wide8(const Seg8& d, int64_t b0, int64_t stride, int count,
-                                          const QLds& T, const StepScalars& sc, int lane, Block8<S> a)
+                                          const QLds& T, const StepScalars& sc, int lane, Block8<S> a,
+                                          const Run8& run)
 {
     int64_t b = b0;
     for (int r = 2; r < count; r += 2) {
-        Block8<S> c = load_block8<KIND, S, true>(d, b + stride, lane);
-        finish_block8<KIND, S, true>(d, b, T, sc, lane, a);
-        a = load_block8<KIND, S, true>(d, b + 2 * stride, lane);
-        finish_block8<KIND, S, true>(d, b + stride, T, sc, lane, c);
+        Block8<S> c = load_block8<KIND, S, true>(d, b + stride, lane, run);
+        finish_block8<KIND, S, true, DENSE>(d, b, T, sc, lane, a, run);
+        a = load_block8<KIND, S, true>(d, b + 2 * stride, lane, run);
+        finish_block8<KIND, S, true, DENSE>(d, b + stride, T, sc, lane, c, run);
         b += 2 * stride;
     }
-    Block8<S> c = load_block8<KIND, S, true>(d, b + stride, lane);
-    finish_block8<KIND, S, true>(d, b, T, sc, lane, a);
-    finish_block8<KIND, S, true>(d, b + stride, T, sc, lane, c);
+    Block8<S> c = load_block8<KIND, S, true>(d, b + stride, lane, run);
+    finish_block8<KIND, S, true, DENSE>(d, b, T, sc, lane, a, run);
+    finish_block8<KIND, S, true, DENSE>(d, b + stride, T, sc, lane, c, run);
+}
+
+template <int KIND, typename S>
+__device__ __forceinline__ void run_wide8_any(const Seg8& d, int64_t b0, int64_t stride, int count,
+                                              const QLds& T, const StepScalars& sc, int lane,
+                                              const Block8<S>& a, const Run8& run)
+{
+    if (sc.skip_zeros)
+        run_wide8<KIND, S, false>(d, b0, stride, count, T, sc, lane, a, run);
+    else
+        run_wide8<KIND, S, true>(d, b0, stride, count, T, sc, lane, a, run);
 }
 
 // Single tensor: workgroup w (in XCD runs, xcd_tile) takes blocks
@@ -440,11 +537,12 @@ __device__ __forceinline__ void single8(Seg8 d, StepScalars sc, int32_t blocks_p
     const int64_t first = wg * waves * blocks_per_wave + wave;
     // the first block's loads overlap the table copy
     const bool wide = wide_run8(d, first, waves, blocks_per_wave);
+    const Run8 run = make_run8<KIND, S>(d, first);   // scalar work only; used when wide
     Block8<S> a;
-    if (wide) a = load_block8<KIND, S, true>(d, first, lane);
+    if (wide) a = load_block8<KIND, S, true>(d, first, lane, run);
     load_qtables(&T);
     if (wide)
-        run_wide8<KIND, S>(d, first, waves, blocks_per_wave, T, sc, lane, a);
+        run_wide8_any<KIND, S>(d, first, waves, blocks_per_wave, T, sc, lane, a, run);
     else
         run_blocks8<KIND, S>(d, first, waves, blocks_per_wave, T, sc, lane);
 }
@@ -492,12 +590,13 @@ k8_multi(const Seg8* __restrict__ segs, const WorkItem* __restrict__ items, int6
         b0 = static_cast<int64_t>(__builtin_amdgcn_readfirstlane(it.chunk)) * chunk_blocks;
         // the first block's loads overlap the table copy
         wide = wide_run8(d, b0, 1, chunk_blocks);
-        if (wide) a = load_block8<KIND, S, true>(d, b0, lane);
     }
+    const Run8 run = make_run8<KIND, S>(d, b0);   // scalar work only; used when wide
+    if (wide) a = load_block8<KIND, S, true>(d, b0, lane, run);
     load_qtables(&T);   // every thread reaches the barrier
     if (!active) return;
     if (wide)
-        run_wide8<KIND, S>(d, b0, 1, chunk_blocks, T, sc, lane, a);
+        run_wide8_any<KIND, S>(d, b0, 1, chunk_blocks, T, sc, lane, a, run);
     else
         run_blocks8<KIND, S>(d, b0, 1, chunk_blocks, T, sc, lane);
 }
