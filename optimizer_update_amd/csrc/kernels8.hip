@@ -415,12 +415,17 @@ __device__ __forceinline__ void finish_block8(const Seg8& d, int64_t b, const QL
     if (full) {
         const uint32_t lo = static_cast<uint32_t>(lane) * 4u;
         if constexpr (S::bytes == 4) {
+            // A 16-byte store stays a global store, also on the wide path:
+            // after a buffer store of more than 8 bytes with a scalar
+            // offset the compiler inserts no wait state before an
+            // instruction that overwrites the data registers, and on gfx950
+            // that write can reach the store (seen as a wrong first word in
+            // some lanes when the next instruction reused the register).
+            // Global stores get the wait state; stores of 4 and 8 bytes
+            // need none.
             const u32x4 xp = {__builtin_bit_cast(uint32_t, praw[0]), __builtin_bit_cast(uint32_t, praw[1]),
                               __builtin_bit_cast(uint32_t, praw[2]), __builtin_bit_cast(uint32_t, praw[3])};
-            if constexpr (WIDE)
-                __builtin_amdgcn_raw_buffer_store_b128(xp, run.p, lo * 4u, run_off<raw>(run, b), kBufNonTemporal);
-            else
-                __builtin_nontemporal_store(xp, reinterpret_cast<u32x4*>(p + e0));
+            __builtin_nontemporal_store(xp, reinterpret_cast<u32x4*>(p + e0));
         } else {
             const u32x2 xp =
                 dense ? u32x2{S::narrow2(pn[0], pn[1]), S::narrow2(pn[2], pn[3])}

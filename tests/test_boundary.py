@@ -670,3 +670,19 @@ def test_8bit_collection_validation_matches_pairwise_rules(L, kind, segments):
     h = ctypes.c_void_p()
     assert L.ou_plan8_create(kind, arr, len(segments), ctypes.byref(h)) == _expected8(kind, segments)
     assert not h.value
+
+
+def test_no_buffer_store_wider_than_8_bytes():
+    """Kernels store at most 8 bytes per lane through buffer descriptors.
+    After a wider buffer store with a scalar offset the compiler inserts no
+    wait state before an instruction that overwrites the data registers,
+    and on gfx950 such a write reached the store (a wrong first word in
+    some lanes, varying from run to run); 16-byte stores go through global
+    addresses, which get the wait state."""
+    import glob
+    for path in glob.glob(os.path.join(ROOT, "optimizer_update_amd", "csrc", "*.hip")) + \
+            glob.glob(os.path.join(ROOT, "optimizer_update_amd", "csrc", "*.hpp")):
+        code = open(path).read()
+        for wide in ("raw_buffer_store_b96", "raw_buffer_store_b128", "struct_buffer_store_b96",
+                     "struct_buffer_store_b128", "raw_ptr_buffer_store"):
+            assert wide not in code, f"{os.path.basename(path)} uses {wide}"
