@@ -442,7 +442,11 @@ struct Group {
     const float* clip_seg_out;
     void* clip_args1[4];
     void* clip_args2[5];
-    void* clip_args3[6];
+    void* clip_args3[7];
+    // pass 3's shape: threads per work item, block, grid
+    int32_t clip_item_threads;
+    int clip_block3;
+    int64_t clip_grid3;
     // update-norm clipping: one item per (segment, 2048-element chunk),
     // binary64 partial sums per item, two floats (fl32(lr*s), s) per segment
     int64_t n_segs;
@@ -605,6 +609,19 @@ int build_plan(int kind_arg, const ou_segment* segs, int32_t nseg, ou_plan_s** o
             }
             grp.grid = (grp.n_items + grp.L.waves - 1) / grp.L.waves;
             grp.chunk32 = static_cast<int32_t>(grp.chunk);
+            // The clipped step's parameter pass (three streams read, one
+            // written) gives a 512-element item of the large shape to a
+            // two-wave block, one group per lane, as the single-tensor
+            // parameter pass does; other shapes keep one wave per item.
+            if (grp.L.waves == 1 && grp.L.unroll == 2) {
+                grp.clip_item_threads = 2 * kWave;
+                grp.clip_block3 = 2 * kWave;
+                grp.clip_grid3 = grp.n_items;
+            } else {
+                grp.clip_item_threads = kWave;
+                grp.clip_block3 = grp.L.waves * kWave;
+                grp.clip_grid3 = grp.grid;
+            }
             plan->groups.push_back(grp);
         }
         e = hipMemcpy(plan->dmem, host.data(), bytes, hipMemcpyHostToDevice);
@@ -653,6 +670,7 @@ void set_clip_args(Group& g, const StepScalars& sc, float max_unorm)
     g.clip_args3[3] = &g.chunk32;
     g.clip_args3[4] = &g.sc;
     g.clip_args3[5] = const_cast<float**>(&g.clip_seg_out);
+    g.clip_args3[6] = &g.clip_item_threads;
 }
 
 // Launch shape of one launch of a group's step (pass 0: the plain step;
@@ -678,6 +696,8 @@ int group_launch(int kind, Group& g, int pass, hipKernelNodeParams* kp)
         args = g.clip_args2;
     } else if (pass == 3) {
         fn = clip_kernel(13, kind, g.dtype, 0);
+        grid = g.clip_grid3;
+        block = g.clip_block3;
         lds = 0;   // the parameter pass runs best with no residency cap (clip_moments_lds)
         args = g.clip_args3;
     }
@@ -903,6 +923,16 @@ int clip_step(int kind_arg, int dtype, void* param, const void* grad, float* sta
     bool vec = streams_16b_aligned(kind, s);
     SingleLaunch L = select_single(*dp, kind, dtype, n, vec, false);
     L.epl = 4;
+    // The parameter pass (three streams read, one written) takes its
+    // 512-element tiles as two-wave blocks of one group per lane: over
+    // 2^28 fp32 elements, 2 x 8 interleaved rounds on one MI355X, 657.8 us
+    // against 687.2 us for one-wave blocks of two groups (the plain update's
+    // shape, which in turn beats this one by 13% on the 4-read, 3-write
+    // update); 256 x 2 took 668.8 us, 512 x 1 676.3 us.
+    if (L.block == kWave && L.unroll == 2) {
+        L.block = 2 * kWave;
+        L.unroll = 1;
+    }
     apply_single_forcing(&L, &vec);
     L.epl = 4;
     const void* f1 = clip_kernel(1, kind, dtype, 0);

@@ -512,16 +512,20 @@ k_clip_apply(typename S::raw* __restrict__ p, const typename S::raw* __restrict_
 }
 
 // Pass 3, collection: one wave per item of the plan's regular work list,
-// with the segment's clipped learning rate.
+// with the segment's clipped learning rate.  item_threads (a multiple of
+// the wave, dividing the block) work on one item together, so an item's
+// 4-element groups are spread over item_threads / 64 waves.
 template <int KIND, typename S>
 __global__ void __launch_bounds__(kMultiMaxThreads)
 k_clip_apply_multi(const SegDesc* __restrict__ segs, const WorkItem* __restrict__ items,
-                   int64_t n_items, int32_t chunk, StepScalars sc, const float* __restrict__ seg_out)
+                   int64_t n_items, int32_t chunk, StepScalars sc, const float* __restrict__ seg_out,
+                   int32_t item_threads)
 {
     using raw = typename S::raw;
-    const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) / kWave);
-    const int lane = static_cast<int>(threadIdx.x) % kWave;
-    const int64_t w = static_cast<int64_t>(blockIdx.x) * (blockDim.x / kWave) + wave;
+    const int per_block = static_cast<int>(blockDim.x) / item_threads;   // items per block
+    const int slot = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) / item_threads);
+    const int lane = static_cast<int>(threadIdx.x) % item_threads;
+    const int64_t w = static_cast<int64_t>(blockIdx.x) * per_block + slot;
     if (w >= n_items) return;
     const WorkItem it = items[w];
     const int seg = __builtin_amdgcn_readfirstlane(it.seg);
@@ -536,7 +540,7 @@ k_clip_apply_multi(const SegDesc* __restrict__ segs, const WorkItem* __restrict_
     const float* __restrict__ s1 = d.s1;
     const float* __restrict__ s2 = d.s2;
     const int64_t nv = d.vec_ok ? len / 4 : 0;   // chunk starts are multiples of 4
-    for (int64_t j4 = lane; j4 < nv; j4 += kWave) {
+    for (int64_t j4 = lane; j4 < nv; j4 += item_threads) {
         const int64_t e0 = start + 4 * j4;
         Words<SDW> wp = load_words<SDW>(p + e0), wg;
         if (sc.skip_zeros) wg = load_words<SDW>(g + e0);
@@ -557,7 +561,7 @@ k_clip_apply_multi(const SegDesc* __restrict__ segs, const WorkItem* __restrict_
         for (int j = 0; j < 4; ++j) set_raw<S>(wp, j, S::narrow(pv[j]));
         store_words<SDW>(p + e0, wp);
     }
-    for (int64_t i = start + 4 * nv + lane; i < start + len; i += kWave)
+    for (int64_t i = start + 4 * nv + lane; i < start + len; i += item_threads)
         clip_step1<KIND, S>(p, g, s1, s2, n, i, sc, lr);
 }
 
