@@ -290,3 +290,61 @@ def test_plan_clip_xcd_orders(kind):
     assert min(results[-1][1]) < 1.0
     for run in (4, 16):
         assert results[run] == results[-1], run
+
+
+@pytest.mark.parametrize("kind", ["adam", "ademamix"])
+def test_plan_clip_two_waves_per_item_equals_per_tensor(kind):
+    """The large collections' shape (one-wave blocks, two groups per lane,
+    512-element items), forced on a small mixed collection: the clipped
+    step's parameter pass gives each item to a two-wave block.  Items that
+    end inside the first wave's share, ragged tails and a misaligned tensor
+    give the per-tensor clipped step's bits and clip factors."""
+    import optimizer_update_amd as ou
+    L = H.lib()
+    hp = O.HParams(lr=1e-2, weight_decay=0.01, skip_zeros=True)
+    php = H.pkg_hp(hp)
+    k = 2 if kind == "ademamix" else 1
+    gen = W.rng(0, 17, 1)
+    spec = (("bf16", 1000), ("fp32", 513), ("bf16", 255), ("fp32", (1 << 16) + 3), ("bf16", 70001),
+            ("fp32", 4))
+    host = [(s, W.params(n, s, gen), [W.cast_storage(np.where(gen.random(n) < 0.1, 0.0,
+                                                              gen.standard_normal(n)), s)
+                                      for _ in range(3)]) for s, n in spec]
+
+    def dev(offset):
+        out = []
+        for i, (s, p0, _) in enumerate(host):
+            off = offset if i == 4 else 0      # one tensor off 16-byte alignment
+            P = H.to_dev(np.concatenate([np.zeros(off, p0.dtype), p0]), s)[off:]
+            out.append((P, torch.empty(p0.size, dtype=W.STORAGE_TORCH[s], device="cuda"),
+                        torch.zeros(k * p0.size, device="cuda"), torch.zeros(p0.size, device="cuda")))
+        return out
+    a, b = dev(1), dev(1)
+    L.ou__force_multi(1, 4, 2, 512, -1)
+    try:
+        plan = ou.Plan(kind, a)
+    finally:
+        L.ou__force_multi(0, 0, 0, 0, 0)
+    try:
+        # 512-element items: 2 + 1 + 137 (bf16) and 2 + 129 + 1 (fp32)
+        assert plan.describe()["work_items"] == 272
+        ws = ou.clip_workspace(max(p0.size for _, p0, _ in host), "cuda")
+        last = []
+        for t in range(1, 4):
+            for (s, _, gs), x, y in zip(host, a, b):
+                x[1].copy_(W.to_torch(gs[t - 1], s, "cuda"))
+                y[1].copy_(W.to_torch(gs[t - 1], s, "cuda"))
+            plan.step_clip(php, t, 0.3)
+            last = []
+            for y in b:
+                ou.optimizer_update_32bit_clip(kind, *y, step=t, lr=hp.lr, weight_decay=hp.weight_decay,
+                                               skip_zeros=True, max_unorm=0.3, workspace=ws)
+                last.append(ou.clip_scale(ws))
+        torch.cuda.synchronize()
+        assert plan.clip_factors() == last
+        assert min(last) < 1.0
+        for i, (x, y) in enumerate(zip(a, b)):
+            for j in (0, 2, 3):
+                assert W.from_torch(x[j]).tobytes() == W.from_torch(y[j]).tobytes(), (kind, i, j)
+    finally:
+        plan.close()
