@@ -315,9 +315,24 @@ __device__ __forceinline__ Block8<S> load_block8(const Seg8& d, int64_t b, int l
     return in;
 }
 
+// The bias corrections of a dense run.  Once beta^t is below half an ulp
+// of 1 (for beta1 = 0.9 from step 165, for beta2 = 0.999 from step 17,318),
+// fl32(1 - beta^t) is exactly 1, its binary64 reciprocal is 1 and the
+// division returns its operand unchanged (every value; the moments are
+// results of arithmetic, never signalling NaNs), so the run leaves it out:
+// BC bit 0 for m / bc1, bit 1 for v / bc2.
+template <int BC>
+__device__ __forceinline__ void bias_corrected_bc(float m, float v, const StepScalars& s, float& mh,
+                                                  float& vh)
+{
+    mh = (BC & 1) ? m : div_step_constant(m, s.rbc1);
+    vh = (BC & 2) ? v : div_step_constant(v, s.rbc2);
+}
+
 // Dequantize, update, requantize and store one block loaded by load_block8.
-// DENSE (with WIDE): skip_zeros is off, so every block is dense.
-template <int KIND, typename S, bool WIDE, bool DENSE = false>
+// DENSE (with WIDE): skip_zeros is off, so every block is dense; BC (dense
+// runs): the bias corrections that are exactly 1 (bias_corrected_bc).
+template <int KIND, typename S, bool WIDE, bool DENSE = false, int BC = 0>
 __device__ __forceinline__ void finish_block8(const Seg8& d, int64_t b, const QLds& T,
                                               const StepScalars& sc, int lane, Block8<S>& in,
                                               const Run8& run)
@@ -355,7 +370,7 @@ __device__ __forceinline__ void finish_block8(const Seg8& d, int64_t b, const QL
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             update_moments<KIND>(S::widen(graw[j]), m[j], v[j], m2[j], sc);
-            bias_corrected(m[j], v[j], sc, mh[j], vh[j]);
+            bias_corrected_bc<BC>(m[j], v[j], sc, mh[j], vh[j]);
         }
         sqrt_rn4(vh, root);
 #pragma unroll
@@ -498,8 +513,9 @@ __device__ __forceinline__ bool wide_run8(const Seg8& d, int64_t b0, int64_t str
 // inputs and `run` based at b0.  Two block buffers alternate and every load
 // is unconditional, so the loads of one block stay in flight while the
 // other is computed (no register copies between iterations, whose waits
-// would drain them).  DENSE: skip_zeros is off (straight-line blocks).
-template <int KIND, typename S, bool DENSE>
+// would drain them).  DENSE: skip_zeros is off (straight-line blocks); BC:
+// as for finish_block8.
+template <int KIND, typename S, bool DENSE, int BC>
 __device__ __forceinline__ void run_wide8(const Seg8& d, int64_t b0, int64_t stride, int count,
                                           const QLds& T, const StepScalars& sc, int lane, Block8<S> a,
                                           const Run8& run)
@@ -507,14 +523,14 @@ __device__ __forceinline__ void run_wide8(const Seg8& d, int64_t b0, int64_t str
     int64_t b = b0;
     for (int r = 2; r < count; r += 2) {
         Block8<S> c = load_block8<KIND, S, true>(d, b + stride, lane, run);
-        finish_block8<KIND, S, true, DENSE>(d, b, T, sc, lane, a, run);
+        finish_block8<KIND, S, true, DENSE, BC>(d, b, T, sc, lane, a, run);
         a = load_block8<KIND, S, true>(d, b + 2 * stride, lane, run);
-        finish_block8<KIND, S, true, DENSE>(d, b + stride, T, sc, lane, c, run);
+        finish_block8<KIND, S, true, DENSE, BC>(d, b + stride, T, sc, lane, c, run);
         b += 2 * stride;
     }
     Block8<S> c = load_block8<KIND, S, true>(d, b + stride, lane, run);
-    finish_block8<KIND, S, true, DENSE>(d, b, T, sc, lane, a, run);
-    finish_block8<KIND, S, true, DENSE>(d, b + stride, T, sc, lane, c, run);
+    finish_block8<KIND, S, true, DENSE, BC>(d, b, T, sc, lane, a, run);
+    finish_block8<KIND, S, true, DENSE, BC>(d, b + stride, T, sc, lane, c, run);
 }
 
 template <int KIND, typename S>
@@ -523,9 +539,13 @@ __device__ __forceinline__ void run_wide8_any(const Seg8& d, int64_t b0, int64_t
                                               const Block8<S>& a, const Run8& run)
 {
     if (sc.skip_zeros)
-        run_wide8<KIND, S, false>(d, b0, stride, count, T, sc, lane, a, run);
+        run_wide8<KIND, S, false, 0>(d, b0, stride, count, T, sc, lane, a, run);
+    else if (sc.rbc1 == 1.0 && sc.rbc2 == 1.0)
+        run_wide8<KIND, S, true, 3>(d, b0, stride, count, T, sc, lane, a, run);
+    else if (sc.rbc1 == 1.0)   // beta1 < beta2: m's correction reaches 1 first
+        run_wide8<KIND, S, true, 1>(d, b0, stride, count, T, sc, lane, a, run);
     else
-        run_wide8<KIND, S, true>(d, b0, stride, count, T, sc, lane, a, run);
+        run_wide8<KIND, S, true, 0>(d, b0, stride, count, T, sc, lane, a, run);
 }
 
 // Single tensor: workgroup w (in XCD runs, xcd_tile) takes blocks

@@ -376,3 +376,32 @@ def test_8bit_beyond_2_31_elements(orc):
         off += m
     del P, P2, G, a, b
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("kind", list(KIND))
+@pytest.mark.parametrize("storage", ["fp32", "bf16"])
+def test_8bit_bias_corrections_reaching_one(orc, L, kind, storage):
+    """Whole-block runs leave out a bias correction once fl32(1 - beta^t)
+    is exactly 1.  Steps 1-2 (neither is 1), 200-201 (m's is 1 for
+    beta1 = 0.9), 10^6 and 10^6 + 1 (both are 1), and with beta1 = 0.999,
+    beta2 = 0.9 step 200 (only v's is 1, which takes the general path): the
+    parameters, codes and absmax equal the oracle's bitwise."""
+    n = (1 << 20) + 5
+    for b1, b2 in ((0.9, 0.999), (0.999, 0.9)):
+        hp = O.HParams(lr=1e-3, beta1=b1, beta2=b2, weight_decay=0.01)
+        key = (21, list(KIND).index(kind), H.DT[storage], int(b1 * 1000))
+        p0 = W.params(n, storage, W.rng(3, *key))
+        P = H.to_dev(p0, storage)
+        G = torch.empty(n, dtype=W.STORAGE_TORCH[storage], device="cuda")
+        st = _dev_states(kind, n)
+        ref = (p0.copy(), *_zero_host(kind, n))
+        for i, t in enumerate((1, 2, 200, 201, 10 ** 6, 10 ** 6 + 1)):
+            g = W.grads(n, "normal", storage, W.rng(3, *key, i))
+            G.copy_(W.to_torch(g, storage, "cuda"))
+            rc = _raw8(L, kind, storage, P, G, st, n, hp, t)
+            assert rc == 0, H.last_error(L)
+            orc.update_8bit_f32(KIND[kind], H.DT[storage], ref[0], g, *ref[1:], hp, t)
+            if t in (2, 201, 10 ** 6 + 1):
+                torch.cuda.synchronize()
+                got = (W.from_torch(P), *(x.cpu().numpy() for x in st))
+                _assert_same(got, ref, storage, f"{kind} {storage} b1={b1} step {t}")
