@@ -56,6 +56,9 @@ KERNEL8_SOURCES = ("optimizer_update_amd/csrc/kernels8.hip", "optimizer_update_a
 # instructions that take more than one, against this peak, and reports
 # beside it what VALU-only probe kernels reach in the same run.
 VALU_PEAK_G = 256 * 4 * 2.4 / 4
+# Step at which the late-training cases start: far past the step where
+# fl32(1 - beta^t) reaches 1 for the default betas (0.9, 0.999).
+LATE_STEP = 1_000_000
 
 
 def code_text(src: str) -> str:
@@ -106,7 +109,8 @@ def parse():
     ap.add_argument("--quick", action="store_true", help="headline only (for profiling runs)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--case", default="adam:fp32:28",
-                    help="headline case kind:storage:log2n (profiling runs)")
+                    help="headline case kind:storage:log2n[:clip|:late] (profiling runs; late: steps from "
+                         "1,000,001, where the bias corrections are 1)")
     ap.add_argument("--collection-only", action="store_true",
                     help="only the model-like collection measurements (profiling runs)")
     ap.add_argument("--copy-only", action="store_true",
@@ -158,8 +162,8 @@ def main():
                "adagrad": ou.HParams(lr=1e-2, beta1=0.0, beta2=0.0, eps=1e-10, weight_decay=0.0),
                "lion": ou.HParams(lr=1e-4, beta1=0.9, beta2=0.99, eps=0.0, weight_decay=0.1)}
 
-    def flat_stepper(kind, tensors, hp):
-        state = {"t": 0}
+    def flat_stepper(kind, tensors, hp, start=0):
+        state = {"t": start}
         if kind.endswith("8"):
             def step8():
                 state["t"] += 1
@@ -260,12 +264,13 @@ def main():
     parts = args.case.split(":")
     kind, storage, log2n = parts[:3]
     clip = len(parts) > 3 and parts[3] == "clip"
+    late = len(parts) > 3 and parts[3] == "late"   # steps from LATE_STEP (bias corrections of 1)
     n = 1 << int(log2n)
     bpe = (W.bytes_per_element_8bit(kind[:-1], storage) if kind.endswith("8")
            else W.bytes_per_element(kind, storage))
     hp_head = hp_kind[kind.rstrip("8")]
     head = make_flat(kind, storage, n, seed=0)
-    stepper = flat_stepper(kind, head, hp_head)
+    stepper = flat_stepper(kind, head, hp_head, start=LATE_STEP if late else 0)
     if clip:   # update-norm clipping (profiling runs): three launches, 40 B/element
         ws = ou.clip_workspace(n, dev)
         cst = {"t": 0}
@@ -286,7 +291,8 @@ def main():
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "f32", "data": "synthetic",
-        "config": {"workload": f"{kind}_{storage}_flat_2^{log2n}" + ("_max_unorm" if clip else ""),
+        "config": {"workload": f"{kind}_{storage}_flat_2^{log2n}" + ("_max_unorm" if clip else "")
+                   + ("_late" if late else ""),
                    "n": n, "kind": kind,
                    "param_grad_storage": storage,
                    "states": "8-bit block-wise, 256 per block" if kind.endswith("8") else "fp32",
@@ -369,6 +375,22 @@ def main():
         for ck, cs in (("adam8", "fp32"), ("adam8", "bf16"), ("ademamix8", "bf16")):
             c = cases[f"{ck}_{cs}_2^28"]
             c["alu_roofline"] = alu_roofline(f"{ck[:-1]}_{cs}", 1 << 28, c["median_ms"], valu_peak)
+        # the 8-bit cases above run steps 1-90, where both bias corrections
+        # differ from 1; late in training (from step 17,318 for beta2 = 0.999)
+        # both are exactly 1 and the kernels leave the divisions out
+        for ck, cs in (("adam8", "bf16"), ("ademamix8", "bf16")):
+            cn = 1 << 28
+            hp = hp_kind[ck.rstrip("8")]
+            ts = make_flat(ck, cs, cn, seed=28)
+            r = time_rounds(flat_stepper(ck, ts, hp, start=LATE_STEP), iters=10)
+            b = W.bytes_per_element_8bit(ck[:-1], cs)
+            gb = b * cn / (r["median_ms"] * 1e-3) / 1e9
+            cases[f"{ck}_{cs}_2^28_late"] = {
+                **r, "from_step": LATE_STEP + 1, "GBps": round(gb, 1), "frac_of_peak": round(gb / HBM_PEAK_GBS, 4),
+                "bytes_per_element": b,
+                "alu_roofline": alu_roofline(f"{ck[:-1]}_{cs}_late", cn, r["median_ms"], valu_peak)}
+            del ts
+            torch.cuda.empty_cache()
         # update-norm clipping: three launches, 40 B/element for fp32 Adam
         # (pass 1 reads p, g, m, v and writes m, v; pass 3 reads p, m, v and writes p)
         cn = 1 << 28
@@ -583,6 +605,11 @@ def bench_collection(torch, ou, W, dev, time_rounds):
         r = time_rounds(fn, iters=iters, rounds=7, warmup=5)
         d[mode] = _us(r)
     d["plans_GBps"] = round(bytes8 / (d["plans"]["median_us"] * 1e-6) / 1e9, 1)
+    # the plans' rounds above run steps 41-395 (m's bias correction reaches 1
+    # at step 165); late in training both corrections are 1
+    opt.step_count = LATE_STEP
+    d["plans_late"] = _us(time_rounds(lambda: opt.step(), iters=50, rounds=7, warmup=5))
+    d["plans_late_GBps"] = round(bytes8 / (d["plans_late"]["median_us"] * 1e-6) / 1e9, 1)
     res["adamw8bit_505"] = d
     opt.close()
     # the page's AdEMAMix32bit collection: fp32 states for every tensor
