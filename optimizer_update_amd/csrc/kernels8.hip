@@ -25,8 +25,9 @@
 // maximum, a reciprocal, the quantizer), so a wave keeps the next block's
 // loads in flight while it computes one (run_wide8), and runs of blocks
 // are long enough to amortize the table copy.  Per block the chain costs
-// about 300 VALU instructions against 2.5-4 KiB of HBM traffic, so the
-// kernel sits between the two rooflines rather than on either.
+// 260-360 VALU instructions against 2.5-4 KiB of HBM traffic: with 16-bit
+// storage the kernel issues VALU work near the chip's peak rate, with fp32
+// storage it sits between the two rooflines.
 #include <type_traits>
 
 #include "internal.h"
