@@ -13,8 +13,8 @@ place, exactly like the product entry points.
 ``oracle_update_f32`` is the parity oracle.  ``oracle_update_f64`` exists to
 check the formulas against closed forms.  Every exported function is pinned
 to something other than itself by the pins in ``tests/oracle_pins.py``, run
-by ``tests/test_oracle.py``; the readings that no pin can separate (points
-where the page is silent) are listed there as "parity unpinned".
+by ``tests/test_oracle.py``.  Where the page is silent, the reading taken is
+stated in ``oracle.c`` at the function it governs.
 """
 from __future__ import annotations
 
@@ -120,7 +120,7 @@ class Oracle:
         lib.oracle_update1_f64.restype = ci
         lib.oracle_qmap.argtypes = [ci, vp]
         lib.oracle_qmap.restype = ci
-        lib.oracle_qcode.argtypes = [ci, f32]
+        lib.oracle_qcode.argtypes = [ci, f32, f32]
         lib.oracle_qcode.restype = ci
         lib.oracle_qvalue.argtypes = [ci, ci]
         lib.oracle_qvalue.restype = f32
@@ -226,9 +226,10 @@ class Oracle:
         count = self._lib.oracle_qmap(int(bool(signed)), _ptr(out))
         return out[:count].copy()
 
-    def qcode(self, signed: bool, x: float) -> int:
-        """Code of a normalised value (``oracle_qcode``)."""
-        return int(self._lib.oracle_qcode(int(bool(signed)), float(x)))
+    def qcode(self, signed: bool, value: float, absmax: float = 1.0) -> int:
+        """Code of a state value in a block with the given absmax
+        (``oracle_qcode``): the magnitude nearest to |value| / absmax."""
+        return int(self._lib.oracle_qcode(int(bool(signed)), float(value), float(absmax)))
 
     def qvalue(self, signed: bool, code: int) -> float:
         """Normalised value of a code (``oracle_qvalue``)."""

@@ -744,31 +744,49 @@ int oracle_qmap(int is_signed, float* mags)
     return k;
 }
 
-/* Decision points between neighbouring magnitudes: the midpoint of two
- * binary32 values, formed exactly in binary64 and rounded to binary32.  A
- * magnitude a rounds to index #{k : b_k < a}: to the nearest magnitude, a
- * value exactly on a decision point going to the smaller one. */
-static int qmap_index(const float* mags, int count, float a)
+/* Magnitude index of |value| / absmax: the index of the magnitude nearest to
+ * that ratio in exact arithmetic, a ratio exactly halfway between two
+ * magnitudes going to the smaller one.  That is the number of exact
+ * midpoints (mag[k] + mag[k+1]) / 2 lying strictly below the ratio, counted
+ * here as mid * absmax < |value|.  Both sides are exact in binary64: a
+ * midpoint of two neighbouring binary32 magnitudes has at most 26
+ * significant bits and absmax 24, so their product needs at most 50, and no
+ * product comes near binary64's subnormal range.  The ratio is 0 for finite
+ * values in a block whose absmax is infinite, and every value is +-0 or NaN
+ * when the absmax is 0; a NaN compares false and gets index 0. */
+static int qmap_index(const float* mags, int count, float value, float absmax)
 {
+    const double av = fabs((double)value);
+    const double A = (double)absmax;
+#if ORACLE_PLANT == 30
+    /* planted: the ratio taken as value * fl32(1 / absmax) against binary32
+     * midpoints (a rounded normalisation) */
+    const float x = absmax > 0.0f ? fabsf(value) * (1.0f / absmax) : 0.0f;
+#endif
     int idx = 0;
     for (int k = 0; k + 1 < count; k++) {
-        float b = (float)(((double)mags[k] + (double)mags[k + 1]) * 0.5);
+        double mid = ((double)mags[k] + (double)mags[k + 1]) * 0.5;
 #if ORACLE_PLANT == 23
-        b = mags[k + 1];                            /* planted: truncation, not nearest */
+        mid = (double)mags[k + 1];                  /* planted: truncation, not nearest */
 #endif
-        if (b < a) idx++;
+#if ORACLE_PLANT == 30
+        if ((float)mid < x) idx++;
+        continue;
+#endif
+        if (mid * A < av) idx++;
     }
     return idx;
 }
 
-/* Code of a normalised value x in [-1, 1] (x >= 0 for the unsigned type). */
-int oracle_qcode(int is_signed, float x)
+/* Code of a state value in a block with the given absmax (|value| <= absmax):
+ * the magnitude index of qmap_index, and for the signed type bit 7 for
+ * value < 0 (not for -0 or NaN). */
+int oracle_qcode(int is_signed, float value, float absmax)
 {
     float mags[256];
     int count = oracle_qmap(is_signed, mags);
-    float a = fabsf(x);
-    int idx = qmap_index(mags, count, a);
-    if (is_signed && x < 0.0f) idx |= 0x80;
+    int idx = qmap_index(mags, count, value, absmax);
+    if (is_signed && value < 0.0f) idx |= 0x80;
     return idx;
 }
 
@@ -800,11 +818,10 @@ float oracle_qvalue(int is_signed, int code)
  *      their values and its parameter is not written);
  *   3. the new absmax of each state is the largest |value| in the block
  *      (maxNum: a NaN is passed over);
- *   4. each state is stored as the code of x = value * fl32(1 / absmax) (one
- *      correctly rounded reciprocal per block, then a product per element;
- *      x = 0 when the absmax is 0).  The code's magnitude index counts the
- *      decision points below |x|, so an x just above 1 (or infinite, when
- *      1 / absmax overflows) takes the largest magnitude and a NaN takes 0.
+ *   4. each state is stored as the code of the magnitude nearest to
+ *      |value| / absmax in exact arithmetic (qmap_index: a ratio exactly
+ *      halfway goes to the smaller magnitude, a NaN to index 0), with the
+ *      signed type's bit 7 set for value < 0.
  * The parameter moves with the moments before they are quantized.  Zero
  * codes with zero absmax are the zero state.  Returns 0, -1 on an invalid
  * kind or dtype, -2 if out of memory. */
@@ -882,21 +899,15 @@ int oracle_update_8bit_f32(int kind_arg, int dtype, void* param, const void* gra
         a2 = old_a2 > 0.0f ? old_a2 : a2;
 #endif
         /* 4. quantize */
-        float r1 = a1 > 0.0f ? 1.0f / a1 : 0.0f;
-        float r2 = a2 > 0.0f ? 1.0f / a2 : 0.0f;
-        float r3 = a3 > 0.0f ? 1.0f / a3 : 0.0f;
         for (int k = 0; k < len; k++) {
             int64_t i = i0 + k;
-            float x1 = a1 > 0.0f ? m[k] * r1 : 0.0f;
-            float x2 = a2 > 0.0f ? v[k] * r2 : 0.0f;
-            int c1 = qmap_index(smag, 128, fabsf(x1));
-            if (x1 < 0.0f) c1 |= 0x80;
+            int c1 = qmap_index(smag, 128, m[k], a1);
+            if (m[k] < 0.0f) c1 |= 0x80;
             state1[i] = (uint8_t)c1;
-            state2[i] = (uint8_t)qmap_index(umag, 256, fabsf(x2));
+            state2[i] = (uint8_t)qmap_index(umag, 256, v[k], a2);
             if (two) {
-                float x3 = a3 > 0.0f ? m2[k] * r3 : 0.0f;
-                int c3 = qmap_index(smag, 128, fabsf(x3));
-                if (x3 < 0.0f) c3 |= 0x80;
+                int c3 = qmap_index(smag, 128, m2[k], a3);
+                if (m2[k] < 0.0f) c3 |= 0x80;
                 state1[n + i] = (uint8_t)c3;
             }
         }

@@ -892,36 +892,76 @@ def pin_qmap_structure(orc):
             assert np.allclose(dec, want, rtol=1e-6, atol=0), (signed, E)
 
 
+def _nearest_exact(mags: np.ndarray, value: float, absmax: float) -> int:
+    """Index of the magnitude nearest to |value| / absmax in exact rational
+    arithmetic, ties to the smaller magnitude: the argmin of the distances
+    over the float64 estimate's neighbours (magnitudes are at least 1e-9
+    apart relative, so the exact nearest is one of them)."""
+    if not (absmax > 0.0) or math.isinf(absmax) or math.isnan(value):
+        return 0
+    rho = Fraction(abs(float(value))) / Fraction(float(absmax))
+    j = int(np.searchsorted(mags, abs(value) / absmax))
+    cand = [k for k in (j - 2, j - 1, j, j + 1) if 0 <= k < mags.size]
+    return min(cand, key=lambda k: (abs(Fraction(float(mags[k])) - rho), k))
+
+
 def pin_quantizer_nearest(orc):
-    """The quantizer picks a nearest magnitude (exact arithmetic), either one
-    when x lies within 2 binary32 ulps of the midpoint; every magnitude maps
-    to itself; the code is monotone in x; the sign bit carries the sign."""
+    """The quantizer's code is the magnitude nearest to |value| / absmax in
+    exact arithmetic, a ratio exactly halfway going to the smaller magnitude
+    (brute force with rationals, not the oracle's midpoint count), for
+    absmax values across the binary32 range (subnormal, near 1, near the
+    largest) and values drawn uniformly, log-uniformly, on the rounded
+    midpoints times absmax and their binary32 neighbours, and on exact
+    ties; every magnitude times a power of two maps to itself; the code is
+    monotone in the value; the sign bit is set for value < 0 only (-0 and
+    NaN take code 0); an infinite absmax gives finite values code 0."""
     gen = rng(41, 0)
+    f32 = np.float32
+    absmaxes = [f32(1.0), f32(2.0 ** -149), f32(3 * 2.0 ** -140), f32(2.0 ** -130), f32(0.7),
+                f32(3.4e38), f32(2.0 ** 100)] + list(
+        (10.0 ** gen.uniform(-40, 38, 10)).astype(np.float32))
     for signed in (True, False):
         mags = orc.qmap(signed).astype(np.float64)
         mids = (mags[:-1] + mags[1:]) / 2
-        xs = np.concatenate([gen.uniform(0, 1, 3000), 10.0 ** gen.uniform(-9, 0, 3000),
-                             mids, np.nextafter(mids.astype(np.float32), 2).astype(np.float64),
-                             np.nextafter(mids.astype(np.float32), -1).astype(np.float64)])
-        xs = np.clip(xs.astype(np.float32), 0, 1)
+        for A in absmaxes:
+            A = f32(A)
+            vals = [gen.uniform(0, 1, 60) * A, 10.0 ** gen.uniform(-9, 0, 60) * A,
+                    mids * float(A)]
+            v = np.concatenate(vals).astype(np.float32)
+            near = np.concatenate([np.nextafter(v[-mids.size:], f32(np.inf)),
+                                   np.nextafter(v[-mids.size:], f32(0))])
+            v = np.concatenate([v, near, [A, f32(0)]])
+            v = v[np.abs(v) <= A]
+            for x in v:
+                want = _nearest_exact(mags, float(x), float(A))
+                got = orc.qcode(signed, float(x), float(A))
+                assert got == want, (signed, float(x), float(A), got, want)
+                if signed and x > 0:
+                    assert orc.qcode(True, -float(x), float(A)) == (want | 0x80), (float(x), float(A))
+            prev = -1
+            for x in np.sort(v[::7]):
+                c = orc.qcode(signed, float(x), float(A))
+                assert c >= prev, (signed, float(x), float(A))
+                prev = c
+        # exact ties: midpoints that binary32 holds, times powers of two
+        ties = [k for k, m in enumerate(mids) if float(f32(m)) == m]
+        assert ties, signed
+        for k in ties:
+            for e in (-100, -20, 0, 60):
+                A = math.ldexp(1.0, e)
+                x = float(f32(mids[k] * A))
+                assert x == mids[k] * A
+                assert orc.qcode(signed, x, A) == k, (signed, k, e)   # the smaller of the two
+                assert orc.qcode(signed, float(np.nextafter(f32(x), f32(np.inf))), A) == k + 1
         for k, m in enumerate(mags):
-            assert orc.qcode(signed, float(np.float32(m))) == k, (signed, k)
-            if signed and k > 0:
-                assert orc.qcode(True, -float(np.float32(m))) == (k | 0x80)
-        prev = -1
-        for x in np.sort(xs):
-            c = orc.qcode(signed, float(x))
-            assert c >= prev, (signed, x)
-            prev = c
-            d = np.abs(mags - float(x))
-            near = np.flatnonzero(d <= d.min() * (1 + 1e-12))
-            if c not in near:
-                ulp = float(np.spacing(np.float32(x)))
-                assert np.min(np.abs(mids - float(x))) <= 2 * ulp, (signed, x, c, near)
-        if signed:
-            for x in gen.uniform(-1, 0, 500).astype(np.float32):
-                c = orc.qcode(True, float(x))
-                assert c == (orc.qcode(True, -float(x)) | 0x80), x
+            for e in (-90, -3, 0, 27):
+                A = math.ldexp(1.0, e)
+                assert orc.qcode(signed, float(f32(m)) * A, A) == k, (signed, k, e)
+        for A in (1.0, 2.0 ** -100, float(f32(3.4e38))):
+            assert orc.qcode(signed, -0.0, A) == 0 and orc.qcode(signed, float("nan"), A) == 0
+        assert orc.qcode(signed, 0.0, 0.0) == 0
+        assert orc.qcode(signed, -5.0, float("inf")) == (0x80 if signed else 0)
+        assert orc.qcode(signed, float("inf"), float("inf")) == 0
 
 
 def pin_qvalue_codes(orc):
@@ -942,7 +982,7 @@ def pin_qvalue_codes(orc):
         if signed:
             assert np.all(vals[129:] < 0) and np.array_equal(-vals[128:], vals[:128])
         for c in codes:
-            back = orc.qcode(signed, float(vals[c]))
+            back = orc.qcode(signed, float(vals[c]), 1.0)
             assert back == (0 if (signed and c == 0x80) else c), (signed, int(c), back)
 
 

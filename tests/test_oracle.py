@@ -48,7 +48,7 @@ def test_conversion_exhaustive_native(tmp_path):
     assert out.returncode == 0 and out.stdout.startswith("ok"), out.stdout + out.stderr
 
 
-@pytest.mark.parametrize("plant", range(1, 30))
+@pytest.mark.parametrize("plant", range(1, 31))
 def test_planted_mistake_is_caught(plant, tmp_path):
     """A copy of the oracle with one planted mistake (dropped bias
     correction, eps inside the root, decay after the update, decay sign,
@@ -61,7 +61,8 @@ def test_planted_mistake_is_caught(plant, tmp_path):
     dampening; 8-bit: truncating quantizer, absmax of the old states,
     parameter moved with the quantized moments, first moment's sign
     dropped, blocks of 512, top magnitude left at its bin centre, the
-    decoder ignoring the sign bit) must fail at least one pin that does not
+    decoder ignoring the sign bit, the ratio normalised by a rounded
+    reciprocal against rounded midpoints) must fail at least one pin that does not
     retype the formulas."""
     path = O.build(str(tmp_path / f"liboracle_plant{plant}.so"), plant=plant)
     bad = O.Oracle(path)
