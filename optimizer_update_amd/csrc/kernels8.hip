@@ -13,10 +13,12 @@
 // on the fp32 values, the block's new absmax of every state by one wave
 // reduction (exact, so the order does not matter: the states are paired
 // across the wave's halves and rows by lane swaps, then DPP rotations
-// finish each 16-lane row), then each state is requantized: x = value *
-// fl32(1 / absmax), and the magnitude index of |x| comes from a key table
-// indexed by the top bits of x plus one decision point (qmap.hpp).  The
-// tables (10 KiB) are copied to LDS once per workgroup.  The parameter
+// finish each 16-lane row), then each state is requantized to the
+// magnitude nearest to |value| / absmax: a key table indexed by the top
+// bits of the binary64 estimate |value| * (1 / absmax) names the one
+// midpoint that can lie near the ratio, and one exact binary64 comparison
+// of that midpoint times absmax with |value| decides (qmap.hpp).  The
+// tables (12.5 KiB) are copied to LDS once per workgroup.  The parameter
 // moves with the moments before quantization.  A partial last block, or a
 // tensor whose streams are not aligned for the wide accesses, runs the same
 // steps one element per slot.
@@ -47,16 +49,18 @@ static_assert(sizeof(QTables) % 4 == 0 && sizeof(QKeys) % 4 == 0, "tables are co
 
 __constant__ QSrc kQ = {make_qtables(), make_qkeys(make_qtables())};
 
-// LDS layout: each key table starts at the byte offset of its first key
-// (kQKeyBase) so that a clamped key, plus 0 or kQKeys, is the entry's LDS
-// address with no subtraction; the gap below holds nothing.
+// LDS layout: the key tables follow the other tables, so the entry of key k
+// (k >= kQKeyFirst) sits at byte k + kKeyAt, a constant offset of the LDS
+// read, plus kQKeys for the unsigned type.
 struct QLds {
     QTables t;
-    uint8_t gap[kQKeyBase - sizeof(QTables)];
-    uint8_t ks[kQKeys];   // signed type: entry of key k at byte k
-    uint8_t ku[kQKeys];   // unsigned type: at byte k + kQKeys
+    uint8_t ks[kQKeys];   // signed type: entry of bucket t = key - kQKeyFirst
+    uint8_t ku[kQKeys];   // unsigned type
 };
-static_assert(offsetof(QLds, ks) == kQKeyBase && offsetof(QLds, ku) == kQKeyBase + kQKeys, "QLds layout");
+constexpr int kKeyAt = static_cast<int>(sizeof(QTables)) - kQKeyFirst;
+static_assert(kKeyAt >= 0 && offsetof(QLds, ks) == sizeof(QTables) &&
+                  offsetof(QLds, ku) == sizeof(QTables) + kQKeys,
+              "QLds layout");
 
 using u32x4 = uint32_t __attribute__((ext_vector_type(4)));
 using u32x2 = uint32_t __attribute__((ext_vector_type(2)));
@@ -69,7 +73,7 @@ __device__ __forceinline__ void load_qtables(QLds* T)
     const uint32_t* src = reinterpret_cast<const uint32_t*>(&kQ);
     uint32_t* dst = reinterpret_cast<uint32_t*>(T);
     for (int i = static_cast<int>(threadIdx.x); i < kTableWords + kKeyWords; i += static_cast<int>(blockDim.x))
-        dst[i < kTableWords ? i : i - kTableWords + kQKeyBase / 4] = src[i];
+        dst[i] = src[i];
     __syncthreads();
 }
 
@@ -78,19 +82,20 @@ __device__ __forceinline__ float deq_signed(const QLds& T, uint32_t code)
     return T.t.svalue[code];
 }
 
-// Codes of a product x (qmap.hpp): the key is the LDS address of its entry.
-__device__ __forceinline__ uint32_t quant_signed(const QLds& T, float x)
+// Code of a state v in a block with absmax A and reciprocal r (qmap.hpp):
+// the key of the estimate |v| * r, plus a constant, is the LDS address of
+// its entry.
+__device__ __forceinline__ uint32_t quant_signed(const QLds& T, float v, double r, double A)
 {
-    const float a = qmagnitude(x);
-    const uint32_t est = reinterpret_cast<const uint8_t*>(&T)[qkey(a)];
-    return qsigned(x, qindex(est, T.t.sbound, a));
+    const uint32_t est = reinterpret_cast<const uint8_t*>(&T)[qkey(static_cast<double>(__builtin_fabsf(v)) * r) + kKeyAt];
+    return qsigned(v, qindex(est, T.t.sbound, A, v));
 }
 
-__device__ __forceinline__ uint32_t quant_unsigned(const QLds& T, float x)
+__device__ __forceinline__ uint32_t quant_unsigned(const QLds& T, float v, double r, double A)
 {
-    const float a = qmagnitude(x);
-    const uint32_t est = reinterpret_cast<const uint8_t*>(&T)[qkey(a) + kQKeys];
-    return qindex(est, T.t.ubound, a);
+    const uint32_t est =
+        reinterpret_cast<const uint8_t*>(&T)[qkey(static_cast<double>(__builtin_fabsf(v)) * r) + kKeyAt + kQKeys];
+    return qindex(est, T.t.ubound, A, v);
 }
 
 // Value of lane (l + N) mod 16 of the same 16-lane row (DPP row_ror:N).
@@ -108,6 +113,14 @@ __device__ __forceinline__ uint32_t lane_value(uint32_t x, int lane)
 __device__ __forceinline__ float lane_float(float x, int lane)
 {
     return __builtin_bit_cast(float, lane_value(__builtin_bit_cast(uint32_t, x), lane));
+}
+
+__device__ __forceinline__ double lane_double(double x, int lane)
+{
+    const uint64_t u = __builtin_bit_cast(uint64_t, x);
+    const uint64_t lo = lane_value(static_cast<uint32_t>(u), lane);
+    const uint64_t hi = lane_value(static_cast<uint32_t>(u >> 32), lane);
+    return __builtin_bit_cast(double, (hi << 32) | lo);
 }
 
 // Maxima over the wave of two or three lane values, each a non-negative
@@ -156,20 +169,32 @@ __device__ __forceinline__ float wave_max3(float x, float y, float w)
     return __builtin_bit_cast(float, row_max(max_swap16(z, h)));
 }
 
-// fl32(1 / l) for a block maximum l (non-negative, not a NaN), and 0 for
-// l = 0 or +inf: the binary64 reciprocal estimate refined by two Newton
-// steps (within 2^-53 of 1/l, relative), rounded once.  A quotient of two
-// binary32 numbers is never a binary32 rounding midpoint and lies far enough
-// from every one that rounding a value this close gives the correctly
-// rounded quotient; the test suite compares it with 1/l for every binary32
-// l >= 0.  With l = +inf the estimate is a NaN, so the select covers it.
-__device__ __forceinline__ float recip_max(float l)
+// 1 / l in binary64 for a block maximum l (non-negative, not a NaN), and 0
+// for l = 0 or +inf: the binary64 reciprocal estimate refined by two Newton
+// steps (a probe over every positive binary32 measured 2^-53 relative).
+// The quantizer needs it within 2^-22 (qmap.hpp), which recip_max's test
+// shows: rounded to binary32 it is the correctly rounded 1/l for every
+// binary32 l >= 0, so it lies within one binary32 ulp of 1/l, 2^-23
+// relative while 1/l is a normal binary32 and at most 2^-22 for the
+// subnormal 1/l of l > 2^126 (1/l >= 2^-128).  With l = +inf the estimate
+// is a NaN, so the select covers it.
+__device__ __forceinline__ double recip_max64(float l)
 {
     const double d = static_cast<double>(l);
     double y = __builtin_amdgcn_rcp(d);
     y = __builtin_fma(__builtin_fma(-d, y, 1.0), y, y);
     y = __builtin_fma(__builtin_fma(-d, y, 1.0), y, y);
-    return (l > 0.0f && l < __builtin_huge_valf()) ? static_cast<float>(y) : 0.0f;
+    return (l > 0.0f && l < __builtin_huge_valf()) ? y : 0.0;
+}
+
+// recip_max64 rounded to binary32 (the test hook): a quotient of two
+// binary32 numbers is never a binary32 rounding midpoint and lies far
+// enough from every one that rounding a value this close gives the
+// correctly rounded quotient; the test suite compares it with 1/l for every
+// binary32 l >= 0.
+__device__ __forceinline__ float recip_max(float l)
+{
+    return static_cast<float>(recip_max64(l));
 }
 
 // Buffer resources over the arrays of one run of whole blocks, based at the
@@ -411,20 +436,23 @@ __device__ __forceinline__ void finish_block8(const Seg8& d, int64_t b, const QL
     l2 = lane_float(l, kLane2);
     if constexpr (kMix) l3 = lane_float(l, kLane3);
 
-    // requantize: x = value * fl32(1 / absmax).  With absmax = 0 every
-    // value is +-0 or NaN, and r = 0 gives x = +-0 or NaN: code 0, as for
-    // the definition's x = 0.  One reciprocal serves all states.
-    const float r = recip_max(l);
-    const float r1 = lane_float(r, 0);
-    const float r2 = lane_float(r, kLane2);
-    float r3 = 0.0f;
-    if constexpr (kMix) r3 = lane_float(r, kLane3);
+    // requantize to the magnitude nearest to |value| / absmax.  With
+    // absmax 0 (every value +-0 or NaN) or +inf the reciprocal is 0 and the
+    // estimate 0 or NaN, which the key takes to the first bucket, and the
+    // exact comparison gives index 0 as the definition does.  One
+    // reciprocal instruction sequence serves all states.
+    const double r = recip_max64(l);
+    const double r1 = lane_double(r, 0);
+    const double r2 = lane_double(r, kLane2);
+    double r3 = 0.0;
+    if constexpr (kMix) r3 = lane_double(r, kLane3);
+    const double A1d = l1, A2d = l2, A3d = l3;
     uint32_t o1 = 0, o2 = 0, o3 = 0;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-        o1 |= quant_signed(T, m[j] * r1) << (8 * j);
-        o2 |= quant_unsigned(T, v[j] * r2) << (8 * j);
-        if constexpr (kMix) o3 |= quant_signed(T, m2[j] * r3) << (8 * j);
+        o1 |= quant_signed(T, m[j], r1, A1d) << (8 * j);
+        o2 |= quant_unsigned(T, v[j], r2, A2d) << (8 * j);
+        if constexpr (kMix) o3 |= quant_signed(T, m2[j], r3, A3d) << (8 * j);
     }
 
     // store

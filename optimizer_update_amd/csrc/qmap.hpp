@@ -19,10 +19,14 @@
 // evaluated in binary64 and rounded once.  The largest magnitude is set to
 // 1 so that a block's largest state (normalised to +-1) is kept exactly.
 //
-// Decision points: bound[k] = fl32((mag[k] + mag[k+1]) / 2) (exact in
-// binary64, rounded once).  A magnitude a quantizes to #{k : bound[k] < a}:
-// the nearest magnitude, a value exactly on a decision point going to the
-// smaller one.
+// Quantizing: a state value v in a block whose largest |state| is A takes
+// the magnitude nearest to |v| / A in exact arithmetic, a ratio exactly
+// halfway between two magnitudes going to the smaller one: its index is the
+// number of exact midpoints mid[k] = (mag[k] + mag[k+1]) / 2 lying strictly
+// below |v| / A, i.e. with mid[k] * A < |v|.  A midpoint of two neighbouring
+// binary32 magnitudes has at most 26 significant bits, so mid[k] * A is
+// exact in binary64 and the comparison is exact.  The signed code adds bit
+// 7 for v < 0.
 #pragma once
 
 #include <stdint.h>
@@ -32,13 +36,13 @@ namespace ou {
 constexpr int kQBlock = 256;   // elements per quantization block (one wave x 4)
 
 struct QTables {
+    double sbound[128];  // signed type: exact midpoints 0..126; entry 127 = +inf
+    double ubound[256];  // unsigned type: exact midpoints 0..254; entry 255 = +inf
     float smag[128];     // signed type: magnitudes by index
-    float sbound[128];   // decision points 0..126; entry 127 = +inf
     float umag[256];     // unsigned type
-    float ubound[256];   // decision points 0..254; entry 255 = +inf
     float svalue[256];   // signed type: value of each code byte (sign bit 7)
 };
-static_assert(sizeof(QTables) == 1024 * 4, "QTables layout");
+static_assert(sizeof(QTables) == 384 * 8 + 640 * 4, "QTables layout");
 
 constexpr void build_magnitudes(float* mag, int payload)
 {
@@ -57,11 +61,27 @@ constexpr void build_magnitudes(float* mag, int payload)
     mag[k - 1] = 1.0f;
 }
 
-constexpr void build_bounds(const float* mag, float* bound, int count)
+// Exact midpoints (two binary32 values within a factor 16 of each other sum
+// exactly in binary64) and the +inf sentinel that stops the count.
+constexpr void build_bounds(const float* mag, double* bound, int count)
 {
     for (int k = 0; k + 1 < count; ++k)
-        bound[k] = static_cast<float>((static_cast<double>(mag[k]) + static_cast<double>(mag[k + 1])) * 0.5);
-    bound[count - 1] = __builtin_huge_valf();   // no value lies above it
+        bound[k] = (static_cast<double>(mag[k]) + static_cast<double>(mag[k + 1])) * 0.5;
+    bound[count - 1] = __builtin_huge_val();
+}
+
+// Significant bits of a positive binary64 value.
+constexpr int significant_bits(double x)
+{
+    while (x < 4503599627370496.0) x *= 2.0;   // scale to [2^52, ...): an integer
+    while (x >= 9007199254740992.0) x *= 0.5;  // exact: back into [2^52, 2^53)
+    uint64_t m = static_cast<uint64_t>(x);
+    int bits = 53;
+    while ((m & 1u) == 0) {
+        m >>= 1;
+        --bits;
+    }
+    return bits;
 }
 
 constexpr QTables make_qtables()
@@ -77,24 +97,44 @@ constexpr QTables make_qtables()
 
 inline constexpr QTables kQTablesHost = make_qtables();
 
-// Quantizing without a search.  The magnitude index of a >= 0 is
-// #{k : bound[k] < a}.  The binary32 pattern of a, shifted right by 16 (sign,
-// exponent, top 7 mantissa bits), names a bucket [s, s') of width at most
-// 2^-7 of its binade; for a in [2^-27, 2) the key is that number, and
-// larger a clamp to the last key (kQKeyBase + kQKeys - 1).  A bucket never
-// holds more than one decision point, so with est = the index of the
-// bucket's start s (the key table's entry key - kQKeyBase), the index of any
-// a in the bucket is est + (bound[est] < a).  Every magnitude below 2^-27
-// has index 0 (both types' first decision points lie above 2^-26), so the
-// quantizer raises smaller magnitudes to 2^-27 (qmagnitude), which changes
-// no index and keeps every key at or above kQKeyBase; a >= 2 (infinity,
-// after a reciprocal that overflowed) takes the largest index, where the
-// +inf sentinel stops the count.  The test suite checks the composition
-// below against the definition for every binary32 input.
-constexpr int kQKeyBase = 100 << 7;   // bits >> 16 of 2^-27
-constexpr int kQKeys = 28 << 7;       // binades 2^-27 .. 2^0
+constexpr bool midpoints_fit(const double* bound, int count)
+{
+    for (int k = 0; k + 1 < count; ++k)
+        if (!(bound[k] > 0x1p-26) || significant_bits(bound[k]) > 29) return false;
+    return true;
+}
+static_assert(midpoints_fit(kQTablesHost.sbound, 128) && midpoints_fit(kQTablesHost.ubound, 256),
+              "mid * absmax is exact in binary64 (at most 29 + 24 bits) and every midpoint lies above 2^-26");
 
-constexpr uint32_t count_below(const float* bound, int count, float a)
+// Finding the index without a search.  The kernels estimate the ratio as
+// x = |v| * r in binary64, with r the block's reciprocal 1 / A (within
+// 2^-22 relative, see the kernels), so x is within 2^-21 of |v| / A.  The
+// key of x is bits 13..24 of its upper word: the low 5 exponent bits and the
+// top 7 fraction bits.  For x in [2^-27, 2) (its exponent field 996..1023)
+// that is 512 + t, where t numbers the 3,584 buckets [s_t, s_t+1) of width
+// 2^-7 of a binade from s_0 = 2^-27; x is first raised to 2^-27 (NaN too),
+// which moves no index because every midpoint lies above 2^-26.  The key
+// table holds est[t] = #{k : mid[k] < s_t (1 - 2^-20)} (0 for t = 0), and
+// every bucket widened to [s_t (1 - 2^-20), s_t+1 (1 + 2^-20)] holds at
+// most one midpoint (checked below), which is then mid[est[t]].  So the
+// index of |v| / A is est[t] + (mid[est[t]] * A < |v|): below that
+// midpoint est[t], above it est[t] + 1, and with no midpoint in the
+// widened bucket mid[est[t]] lies above the ratio.  The ratio never
+// exceeds 1, so x stays below 2; the +inf sentinel stops the count at the
+// top.
+constexpr int kQKeys = 28 << 7;       // binades 2^-27 .. 2^0, 128 buckets each
+constexpr int kQKeyFirst = 4 << 7;    // key of 2^-27: (996 & 31) << 7
+constexpr double kQFloor = 0x1p-27;
+constexpr double kQMargin = 0x1p-20;
+
+constexpr double bucket_start(int t)
+{
+    double s = 1.0 + static_cast<double>(t % 128) / 128.0;
+    for (int e = t / 128; e < 27; ++e) s *= 0.5;   // exact
+    return s;
+}
+
+constexpr uint32_t count_below(const double* bound, int count, double a)
 {
     int lo = 0, hi = count - 1;   // bound[0 .. count-2] sorted
     while (lo < hi) {
@@ -105,7 +145,7 @@ constexpr uint32_t count_below(const float* bound, int count, float a)
 }
 
 struct QKeys {
-    uint8_t s[kQKeys];   // signed type: index of each bucket's start
+    uint8_t s[kQKeys];   // signed type: est of each bucket
     uint8_t u[kQKeys];   // unsigned type
 };
 
@@ -113,42 +153,50 @@ constexpr QKeys make_qkeys(const QTables& t)
 {
     QKeys k{};
     for (int i = 0; i < kQKeys; ++i) {
-        const float start = __builtin_bit_cast(float, static_cast<uint32_t>(i + kQKeyBase) << 16);
-        k.s[i] = static_cast<uint8_t>(count_below(t.sbound, 128, start));
-        k.u[i] = static_cast<uint8_t>(count_below(t.ubound, 256, start));
+        const double lo = i == 0 ? 0.0 : bucket_start(i) * (1.0 - kQMargin);
+        k.s[i] = static_cast<uint8_t>(count_below(t.sbound, 128, lo));
+        k.u[i] = static_cast<uint8_t>(count_below(t.ubound, 256, lo));
     }
     return k;
 }
 
 inline constexpr QKeys kQKeysHost = make_qkeys(kQTablesHost);
 
-// The magnitude the quantizer classifies: |x| raised to at least 2^-27,
-// with NaN mapped to 2^-27 (maxNum returns the number when one operand is a
-// quiet NaN), so a NaN takes index 0.  x is a product (a state times its
-// block's reciprocal), never a signaling NaN.
-constexpr float kQFloor = 0x1p-27f;
-static_assert(__builtin_bit_cast(uint32_t, kQFloor) >> 16 == kQKeyBase, "floor is the first key");
-static_assert(kQTablesHost.sbound[0] > 0x1p-26f && kQTablesHost.ubound[0] > 0x1p-26f,
-              "magnitudes below 2^-26 have index 0");
-constexpr float qmagnitude(float x) { return __builtin_fmaxf(__builtin_fabsf(x), kQFloor); }
-
-// Key of a = qmagnitude(x) (so a >= 2^-27): bits >> 16, at most
-// kQKeyBase + kQKeys - 1.
-constexpr uint32_t qkey(float a)
+constexpr bool one_midpoint_per_bucket(const double* bound, int count)
 {
-    const uint32_t k = __builtin_bit_cast(uint32_t, a) >> 16;
-    constexpr uint32_t hi = kQKeyBase + kQKeys - 1;
-    return k > hi ? hi : k;
+    for (int i = 0; i < kQKeys; ++i) {
+        const double lo = i == 0 ? 0.0 : bucket_start(i) * (1.0 - kQMargin);
+        const double hi = (i + 1 < kQKeys ? bucket_start(i + 1) : 2.0) * (1.0 + kQMargin);
+        if (count_below(bound, count, hi) - count_below(bound, count, lo) > 1) return false;
+    }
+    return true;
+}
+static_assert(one_midpoint_per_bucket(kQTablesHost.sbound, 128) &&
+                  one_midpoint_per_bucket(kQTablesHost.ubound, 256),
+              "a widened key bucket holds at most one midpoint");
+
+// Key of the ratio estimate x (>= 0, or NaN): x raised to 2^-27 (fmax
+// returns the number when the other operand is a NaN), then bits 13..24 of
+// the upper word; kQKeyFirst for x <= 2^-27, kQKeyFirst + kQKeys - 1 at
+// most for x < 2.
+constexpr uint32_t qkey(double x)
+{
+    const double a = __builtin_fmax(x, kQFloor);
+    const uint32_t hi = static_cast<uint32_t>(__builtin_bit_cast(uint64_t, a) >> 32);
+    return (hi >> 13) & 0xfffu;
+}
+static_assert(qkey(kQFloor) == kQKeyFirst && qkey(0.0) == kQKeyFirst &&
+                  qkey(0x1.fffffffffffffp0) == kQKeyFirst + kQKeys - 1 &&
+                  qkey(bucket_start(1000)) == kQKeyFirst + 1000,
+              "key layout");
+
+// Magnitude index of |v| / A from est = the key table's entry.
+constexpr uint32_t qindex(uint32_t est, const double* bound, double A, float v)
+{
+    return est + ((bound[est] * A < static_cast<double>(__builtin_fabsf(v))) ? 1u : 0u);
 }
 
-// Magnitude index of a from est = the key table's entry for qkey(a).
-constexpr uint32_t qindex(uint32_t est, const float* bound, float a)
-{
-    return est + ((bound[est] < a) ? 1u : 0u);
-}
-
-// Signed code: the sign bit for x < 0 (not for -0 or NaN, whose magnitude
-// index is 0).
-constexpr uint32_t qsigned(float x, uint32_t idx) { return (x < 0.0f) ? (idx | 0x80u) : idx; }
+// Signed code: the sign bit for v < 0 (not for -0 or NaN).
+constexpr uint32_t qsigned(float v, uint32_t idx) { return (v < 0.0f) ? (idx | 0x80u) : idx; }
 
 }  // namespace ou

@@ -482,9 +482,13 @@ def test_8bit_qmap_matches_the_oracle(L):
 
 
 def test_8bit_quantizer_exhaustive(tmp_path):
-    """The kernels' key-table quantizer (qmap.hpp), compiled for the host:
-    for every binary32 value in [0, 2], infinity and NaN it returns the index
-    of the definition, #{k : bound[k] < a} (NaN -> 0)."""
+    """The kernels' quantizer (qmap.hpp: key table of the binary64 ratio
+    estimate, then one exact comparison), compiled for the host: for a set of
+    absmax values from subnormal to the largest binary32, every value within
+    2^-26 of absmax and a sample below, with the reciprocal exact and moved
+    2^-21 either way, it returns the index of the magnitude nearest to
+    |value| / absmax in exact arithmetic (ties to the smaller; NaN, absmax 0
+    and infinite absmax -> 0), and the signed code's bit 7 for value < 0."""
     src = os.path.join(os.path.dirname(__file__), "native", "qindex_check.cpp")
     inc = os.path.join(os.path.dirname(os.path.dirname(__file__)), "optimizer_update_amd", "csrc")
     exe = tmp_path / "qindex_check"
