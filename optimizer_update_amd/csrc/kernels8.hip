@@ -83,18 +83,18 @@ __device__ __forceinline__ float deq_signed(const QLds& T, uint32_t code)
 }
 
 // Code of a state v in a block with absmax A and reciprocal r (qmap.hpp):
-// the key of the estimate |v| * r, plus a constant, is the LDS address of
-// its entry.
+// the key of the estimate |v| * r + 2^-27, plus a constant, is the LDS
+// address of its entry.
 __device__ __forceinline__ uint32_t quant_signed(const QLds& T, float v, double r, double A)
 {
-    const uint32_t est = reinterpret_cast<const uint8_t*>(&T)[qkey(static_cast<double>(__builtin_fabsf(v)) * r) + kKeyAt];
+    const uint32_t est = reinterpret_cast<const uint8_t*>(&T)[qkey(qestimate(v, r)) + kKeyAt];
     return qsigned(v, qindex(est, T.t.sbound, A, v));
 }
 
 __device__ __forceinline__ uint32_t quant_unsigned(const QLds& T, float v, double r, double A)
 {
     const uint32_t est =
-        reinterpret_cast<const uint8_t*>(&T)[qkey(static_cast<double>(__builtin_fabsf(v)) * r) + kKeyAt + kQKeys];
+        reinterpret_cast<const uint8_t*>(&T)[qkey(qestimate(v, r)) + kKeyAt + kQKeys];
     return qindex(est, T.t.ubound, A, v);
 }
 

@@ -107,24 +107,32 @@ static_assert(midpoints_fit(kQTablesHost.sbound, 128) && midpoints_fit(kQTablesH
               "mid * absmax is exact in binary64 (at most 29 + 24 bits) and every midpoint lies above 2^-26");
 
 // Finding the index without a search.  The kernels estimate the ratio as
-// x = |v| * r in binary64, with r the block's reciprocal 1 / A (within
-// 2^-22 relative, see the kernels), so x is within 2^-21 of |v| / A.  The
-// key of x is bits 13..24 of its upper word: the low 5 exponent bits and the
-// top 7 fraction bits.  For x in [2^-27, 2) (its exponent field 996..1023)
-// that is 512 + t, where t numbers the 3,584 buckets [s_t, s_t+1) of width
-// 2^-7 of a binade from s_0 = 2^-27; x is first raised to 2^-27 (NaN too),
-// which moves no index because every midpoint lies above 2^-26.  The key
-// table holds est[t] = #{k : mid[k] < s_t (1 - 2^-20)} (0 for t = 0), and
-// every bucket widened to [s_t (1 - 2^-20), s_t+1 (1 + 2^-20)] holds at
-// most one midpoint (checked below), which is then mid[est[t]].  So the
-// index of |v| / A is est[t] + (mid[est[t]] * A < |v|): below that
-// midpoint est[t], above it est[t] + 1, and with no midpoint in the
-// widened bucket mid[est[t]] lies above the ratio.  The ratio never
-// exceeds 1, so x stays below 2; the +inf sentinel stops the count at the
-// top.
+// y = fl64(|v| * r + 2^-27) (one binary64 fused multiply-add), with r the
+// block's reciprocal 1 / A (within 2^-22 relative, see the kernels); the
+// added 2^-27 keeps y at or above 2^-27 without a comparison.  The key of y
+// is bits 13..24 of its upper word: the low 5 exponent bits and the top 7
+// fraction bits.  For y in [2^-27, 2) (its exponent field 996..1023) that
+// is 512 + t, where t numbers the 3,584 buckets [s_t, s_t+1) of width 2^-7
+// of a binade from s_0 = 2^-27.  A value y in bucket t means a ratio
+// X = |v| / A in
+//     [(s_t (1 - 2^-53) - 2^-27) / (1 + 2^-22),
+//      (s_t+1 (1 + 2^-53) - 2^-27) / (1 - 2^-22)),
+// which the tables widen to [lo_t, hi_t] below (about 2^-20 relative, plus
+// an absolute 2^-80).  The key table holds est[t] = #{k : mid[k] < lo_t},
+// and every widened bucket holds at most one midpoint (checked below),
+// which is then mid[est[t]].  So the index of |v| / A is
+// est[t] + (mid[est[t]] * A < |v|): below that midpoint est[t], above it
+// est[t] + 1, and with no midpoint in the widened bucket mid[est[t]] lies
+// above the ratio.  A ratio never exceeds 1, so a finite y stays below
+// 1 + 2^-20; the buckets from 1.5 up are reached only by a NaN y (a NaN
+// state, or an infinite one in a block with absmax +inf, where r = 0):
+// every quiet NaN has exponent field 2047 and the top fraction bit set, so
+// its key lies in those buckets, whose entry is 0, and the comparison with
+// a NaN is false.  The +inf sentinel stops the count at the top.
 constexpr int kQKeys = 28 << 7;       // binades 2^-27 .. 2^0, 128 buckets each
 constexpr int kQKeyFirst = 4 << 7;    // key of 2^-27: (996 & 31) << 7
-constexpr double kQFloor = 0x1p-27;
+constexpr int kQKeyNaN = (27 << 7) + 64;   // first bucket from 1.5 (t): NaN keys only
+constexpr double kQOffset = 0x1p-27;
 constexpr double kQMargin = 0x1p-20;
 
 constexpr double bucket_start(int t)
@@ -132,6 +140,20 @@ constexpr double bucket_start(int t)
     double s = 1.0 + static_cast<double>(t % 128) / 128.0;
     for (int e = t / 128; e < 27; ++e) s *= 0.5;   // exact
     return s;
+}
+
+// The widened ratio range of bucket t (s_t - 2^-27 is exact: both are
+// multiples of 2^-34 below 2).
+constexpr double bucket_lo(int t)
+{
+    const double s = bucket_start(t);
+    const double x = (s - kQOffset - s * 0x1p-52) * (1.0 - kQMargin) - 0x1p-80;
+    return x > 0.0 ? x : 0.0;
+}
+constexpr double bucket_hi(int t)
+{
+    const double s = t + 1 < kQKeys ? bucket_start(t + 1) : 2.0;
+    return (s - kQOffset + s * 0x1p-52) * (1.0 + kQMargin) + 0x1p-80;
 }
 
 constexpr uint32_t count_below(const double* bound, int count, double a)
@@ -152,42 +174,50 @@ struct QKeys {
 constexpr QKeys make_qkeys(const QTables& t)
 {
     QKeys k{};
-    for (int i = 0; i < kQKeys; ++i) {
-        const double lo = i == 0 ? 0.0 : bucket_start(i) * (1.0 - kQMargin);
-        k.s[i] = static_cast<uint8_t>(count_below(t.sbound, 128, lo));
-        k.u[i] = static_cast<uint8_t>(count_below(t.ubound, 256, lo));
+    for (int i = 0; i < kQKeyNaN; ++i) {
+        k.s[i] = static_cast<uint8_t>(count_below(t.sbound, 128, bucket_lo(i)));
+        k.u[i] = static_cast<uint8_t>(count_below(t.ubound, 256, bucket_lo(i)));
     }
-    return k;
+    return k;   // buckets from kQKeyNaN on stay 0
 }
 
 inline constexpr QKeys kQKeysHost = make_qkeys(kQTablesHost);
 
 constexpr bool one_midpoint_per_bucket(const double* bound, int count)
 {
-    for (int i = 0; i < kQKeys; ++i) {
-        const double lo = i == 0 ? 0.0 : bucket_start(i) * (1.0 - kQMargin);
-        const double hi = (i + 1 < kQKeys ? bucket_start(i + 1) : 2.0) * (1.0 + kQMargin);
-        if (count_below(bound, count, hi) - count_below(bound, count, lo) > 1) return false;
-    }
+    for (int i = 0; i < kQKeyNaN; ++i)
+        if (count_below(bound, count, bucket_hi(i)) - count_below(bound, count, bucket_lo(i)) > 1) return false;
     return true;
 }
 static_assert(one_midpoint_per_bucket(kQTablesHost.sbound, 128) &&
                   one_midpoint_per_bucket(kQTablesHost.ubound, 256),
               "a widened key bucket holds at most one midpoint");
+static_assert(bucket_lo(kQKeyNaN) > 1.25, "finite ratio estimates stay below the NaN buckets");
 
-// Key of the ratio estimate x (>= 0, or NaN): x raised to 2^-27 (fmax
-// returns the number when the other operand is a NaN), then bits 13..24 of
-// the upper word; kQKeyFirst for x <= 2^-27, kQKeyFirst + kQKeys - 1 at
-// most for x < 2.
-constexpr uint32_t qkey(double x)
+// The ratio estimate of a state v (binary32) for reciprocal r >= 0: one
+// binary64 fused multiply-add.  A constexpr template so that the kernels
+// and the host check compile the same code (constexpr functions are callable
+// on both sides; a fused multiply-add has no constant evaluation, which the
+// compiler accepts in a template).
+template <class Float>
+constexpr double qestimate(Float v, double r)
 {
-    const double a = __builtin_fmax(x, kQFloor);
-    const uint32_t hi = static_cast<uint32_t>(__builtin_bit_cast(uint64_t, a) >> 32);
+    static_assert(sizeof(Float) == 4, "a binary32 state");
+    return __builtin_fma(static_cast<double>(__builtin_fabsf(v)), r, kQOffset);
+}
+
+// Key of an estimate y (>= 2^-27, or a quiet NaN): bits 13..24 of the
+// upper word; kQKeyFirst for y in the first bucket, kQKeyFirst + kQKeys - 1
+// at most for y < 2 and for every quiet NaN.
+constexpr uint32_t qkey(double y)
+{
+    const uint32_t hi = static_cast<uint32_t>(__builtin_bit_cast(uint64_t, y) >> 32);
     return (hi >> 13) & 0xfffu;
 }
-static_assert(qkey(kQFloor) == kQKeyFirst && qkey(0.0) == kQKeyFirst &&
-                  qkey(0x1.fffffffffffffp0) == kQKeyFirst + kQKeys - 1 &&
-                  qkey(bucket_start(1000)) == kQKeyFirst + 1000,
+static_assert(qkey(kQOffset) == kQKeyFirst && qkey(0x1.fffffffffffffp0) == kQKeyFirst + kQKeys - 1 &&
+                  qkey(bucket_start(1000)) == kQKeyFirst + 1000 &&
+                  qkey(1.5) == kQKeyFirst + kQKeyNaN &&
+                  qkey(__builtin_nan("")) >= kQKeyFirst + kQKeyNaN,
               "key layout");
 
 // Magnitude index of |v| / A from est = the key table's entry.

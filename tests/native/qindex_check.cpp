@@ -1,6 +1,6 @@
 // Host check of the 8-bit quantizer of the library
 // (optimizer_update_amd/csrc/qmap.hpp), composed as the kernels compose it:
-// the key of the binary64 estimate |v| * r, the key table's est, and one
+// the key of the binary64 estimate |v| * r + 2^-27, the key table's est, and one
 // exact comparison est + (bound[est] * A < |v|); the signed code adds bit 7
 // for v < 0.  The expected index is that of the magnitude nearest to |v| / A
 // in exact arithmetic, ties to the smaller: the number of midpoints of
@@ -45,7 +45,7 @@ static uint32_t kernel_index(bool is_signed, float v, double r, double A)
 {
     const QTables& T = kQTablesHost;
     const QKeys& K = kQKeysHost;
-    const uint32_t t = qkey(static_cast<double>(std::fabs(v)) * r) - kQKeyFirst;
+    const uint32_t t = qkey(qestimate(v, r)) - kQKeyFirst;
     if (t >= static_cast<uint32_t>(kQKeys)) return 0xffffffffu;   // outside the table: an error
     if (is_signed) return qsigned(v, qindex(K.s[t], T.sbound, A, v));
     return qindex(K.u[t], T.ubound, A, v);
