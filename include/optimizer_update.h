@@ -263,11 +263,11 @@ void ou_plan_destroy(ou_plan plan);
  *      is not written);
  *   3. the new absmax of each moment is its largest |value| in the block;
  *   4. each moment is stored as the code of the magnitude nearest to
- *      |x|, x = value * fl32(1 / absmax) (one reciprocal per block; x = 0
- *      when absmax is 0): its index counts the decision points below |x|,
- *      the binary32 roundings of the exact midpoints between neighbouring
- *      magnitudes, so a value exactly halfway goes to the smaller magnitude,
- *      an x above 1 to the largest and a NaN to 0.
+ *      |value| / absmax in exact arithmetic: its index counts the exact
+ *      midpoints mid of neighbouring magnitudes with mid * absmax < |value|,
+ *      so a ratio exactly halfway goes to the smaller magnitude; bit 7 of a
+ *      signed code is set for value < 0; a NaN value, and a finite value in
+ *      a block whose absmax is +inf, take index 0.
  * All-zero codes with zero absmax are the zero state.
  *
  * Layout: state1 holds n codes (ADAM) or 2n (ADEMAMIX: fast EMA at [0, n),

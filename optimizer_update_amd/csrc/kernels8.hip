@@ -15,8 +15,8 @@
 // across the wave's halves and rows by lane swaps, then DPP rotations
 // finish each 16-lane row), then each state is requantized to the
 // magnitude nearest to |value| / absmax: a key table indexed by the top
-// bits of the binary64 estimate |value| * (1 / absmax) names the one
-// midpoint that can lie near the ratio, and one exact binary64 comparison
+// bits of the binary64 estimate |value| * (1 / absmax) + 2^-27 names the
+// one midpoint that can lie near the ratio, and one exact binary64 comparison
 // of that midpoint times absmax with |value| decides (qmap.hpp).  The
 // tables (12.5 KiB) are copied to LDS once per workgroup.  The parameter
 // moves with the moments before quantization.  A partial last block, or a
@@ -27,7 +27,7 @@
 // maximum, a reciprocal, the quantizer), so a wave keeps the next block's
 // loads in flight while it computes one (run_wide8), and runs of blocks
 // are long enough to amortize the table copy.  Per block the chain costs
-// 260-360 VALU instructions against 2.5-4 KiB of HBM traffic: with 16-bit
+// 270-380 VALU instructions against 2.5-4 KiB of HBM traffic: with 16-bit
 // storage the kernel issues VALU work near the chip's peak rate, with fp32
 // storage it sits between the two rooflines.
 #include <type_traits>

@@ -4,8 +4,8 @@ The page "Investigate a 256-thread SM103 path for small 32-bit optimizer
 tensors" times AdamW8bit collections whose small tensors (below
 min_8bit_size = 4,096 elements) take the 32-bit path; these tests cover the
 8-bit leg and the routing.  The kernels perform the oracle's steps with the
-same binary32 operations, the same decision points and an exact (order-free)
-block maximum, so parameters, codes and absmax must be bit-identical to the
+same binary32 operations, the same exact nearest-magnitude quantizer and an
+exact (order-free) block maximum, so parameters, codes and absmax must be bit-identical to the
 oracle, across the kernel's launch shapes, the element-by-element path and
 plans.
 """
