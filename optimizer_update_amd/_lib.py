@@ -149,6 +149,8 @@ def load(path: str = LIBRARY) -> ctypes.CDLL:
     lib.ou__sqrt.restype = i32
     lib.ou__recip8.argtypes = [vp, vp, i64, vp]
     lib.ou__recip8.restype = i32
+    lib.ou__quant8.argtypes = [vp, vp, vp, vp, i64, vp]
+    lib.ou__quant8.restype = i32
     lib.ou__stream_probe.argtypes = [i32, vp, vp, vp, vp, i64, vp]
     lib.ou__stream_probe.restype = i32
     lib.ou__valu_probe.argtypes = [i32, i64, ctypes.c_int32, vp, vp]

@@ -437,4 +437,24 @@ int ou__recip8(const float* in, float* out, int64_t n, void* stream)
     return OU_OK;
 }
 
+__attribute__((visibility("default")))
+int ou__quant8(const float* v, const float* absmax, uint8_t* cs, uint8_t* cu, int64_t n, void* stream)
+{
+    if (!v || !absmax || !cs || !cu || n <= 0) return fail(OU_EINVAL, "quant8: bad arguments");
+    if (reinterpret_cast<uintptr_t>(v) % 4 || reinterpret_cast<uintptr_t>(absmax) % 4)
+        return fail(OU_EALIGN, "quant8: misaligned buffers");
+    if (validate_only()) return OU_OK;
+    const DeviceProps* dp = nullptr;
+    if (int st = current_device(&dp)) return st;
+    const int64_t grid = std::max<int64_t>(1, std::min<int64_t>((n + 255) / 256, 1 << 16));
+    const float* a0 = v;
+    const float* a1 = absmax;
+    uint8_t* a2 = cs;
+    uint8_t* a3 = cu;
+    void* args[] = {const_cast<float**>(&a0), const_cast<float**>(&a1), &a2, &a3, &n};
+    hipError_t e = launch(quant_kernel8(), grid, 256, 0, args, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "launch quant8");
+    return OU_OK;
+}
+
 }  // extern "C"

@@ -136,4 +136,7 @@ const void* kernel8(bool multi, int kind, int dtype);
 // The 8-bit kernels' reciprocal of a block maximum alone (test hook).
 const void* recip_kernel8();
 
+// The 8-bit kernels' quantizer alone (test hook).
+const void* quant_kernel8();
+
 }  // namespace ou

@@ -664,6 +664,27 @@ k8_recip(const float* __restrict__ in, float* __restrict__ out, int64_t n)
         out[i] = recip_max(in[i]);
 }
 
+// The quantizer alone on n (value, absmax) pairs (test hook): the signed
+// code of value and the unsigned code of |value|, with the reciprocal of
+// absmax taken as the update kernels take that of a block maximum.  absmax
+// must be >= 0 and not a NaN, and |value| <= absmax (or a NaN value, or an
+// infinite absmax), as in a block.
+__global__ void __launch_bounds__(256)
+k8_quant(const float* __restrict__ v, const float* __restrict__ absmax, uint8_t* __restrict__ cs,
+         uint8_t* __restrict__ cu, int64_t n)
+{
+    __shared__ QLds T;
+    load_qtables(&T);   // every thread reaches the barrier
+    const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
+    for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < n; i += stride) {
+        const float x = v[i];
+        const float a = absmax[i];
+        const double r = recip_max64(a);
+        cs[i] = static_cast<uint8_t>(quant_signed(T, x, r, a));
+        cu[i] = static_cast<uint8_t>(quant_unsigned(T, __builtin_fabsf(x), r, a));
+    }
+}
+
 template <int KIND, typename S>
 const void* pick8(bool multi)
 {
@@ -692,6 +713,7 @@ const void* pick8_dtype(bool multi, int dtype)
 }  // namespace
 
 const void* recip_kernel8() { return reinterpret_cast<const void*>(&k8_recip); }
+const void* quant_kernel8() { return reinterpret_cast<const void*>(&k8_quant); }
 
 const void* kernel8(bool multi, int kind, int dtype)
 {

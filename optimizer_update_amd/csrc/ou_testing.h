@@ -59,6 +59,12 @@ int ou__sqrt(const float* in, float* out, int64_t n, void* stream);
 // and NaN are outside its domain and give 0).  Asynchronous on `stream`.
 int ou__recip8(const float* in, float* out, int64_t n, void* stream);
 
+// The 8-bit kernels' quantizer on n pairs: cs[i] = signed code of v[i],
+// cu[i] = unsigned code of |v[i]|, each in a block whose absmax is
+// absmax[i] (>= 0, not a NaN, with |v[i]| <= absmax[i] unless v[i] is a NaN
+// or absmax[i] is +inf).  Asynchronous on `stream`.
+int ou__quant8(const float* v, const float* absmax, uint8_t* cs, uint8_t* cu, int64_t n, void* stream);
+
 // Bandwidth probes in the launch shape of the plain fp32 Adam update of n
 // elements, with no arithmetic; n a multiple of 4, buffers 16-byte aligned.
 // mode 0: its traffic (p, g, s1, s2 read; p, s1, s2 written back

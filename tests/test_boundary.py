@@ -53,7 +53,8 @@ def test_exports_every_header_function(L):
     assert exported - set(names) == {"ou__select_single", "ou__force_single", "ou__force_multi",
                                      "ou__step_scalars", "ou__force_8bit", "ou__validate_only",
                                      "ou__force_xcd", "ou__stream_probe", "ou__narrow",
-                                     "ou__sqrt", "ou__recip8", "ou__valu_probe", "ou__select_multi"}
+                                     "ou__sqrt", "ou__recip8", "ou__quant8", "ou__valu_probe",
+                                     "ou__select_multi"}
 
 
 def test_header_is_plain_c_and_matches_ctypes_layout(tmp_path):
@@ -553,7 +554,7 @@ def test_narrow_hook_validation(L):
 
 
 def test_sqrt_hook_validation(L):
-    """The square-root and reciprocal hooks' argument checks (test hooks)."""
+    """The square-root, reciprocal and quantizer hooks' argument checks (test hooks)."""
     assert L.ou__sqrt(0x10000, 0x20000, 16, None) == OU_OK
     assert L.ou__sqrt(0x10000, 0x20000, 0, None) == OU_EINVAL
     assert L.ou__sqrt(0, 0x20000, 16, None) == OU_EINVAL
@@ -562,6 +563,10 @@ def test_sqrt_hook_validation(L):
     assert L.ou__recip8(0x10000, 0x20000, -1, None) == OU_EINVAL
     assert L.ou__recip8(0x10000, 0, 16, None) == OU_EINVAL
     assert L.ou__recip8(0x10000, 0x20001, 16, None) == OU_EALIGN
+    assert L.ou__quant8(0x10000, 0x20000, 0x30000, 0x40000, 16, None) == OU_OK
+    assert L.ou__quant8(0x10000, 0x20000, 0x30000, 0x40000, 0, None) == OU_EINVAL
+    assert L.ou__quant8(0x10000, 0x20000, 0, 0x40000, 16, None) == OU_EINVAL
+    assert L.ou__quant8(0x10000, 0x20002, 0x30000, 0x40000, 16, None) == OU_EALIGN
 
 
 # ---- validation against a brute-force reference (property-based) -----------

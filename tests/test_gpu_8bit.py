@@ -405,3 +405,73 @@ def test_8bit_bias_corrections_reaching_one(orc, L, kind, storage):
                 torch.cuda.synchronize()
                 got = (W.from_torch(P), *(x.cpu().numpy() for x in st))
                 _assert_same(got, ref, storage, f"{kind} {storage} b1={b1} step {t}")
+
+
+def _quantizer_cases(orc):
+    """(value, absmax) pairs where a quantizer goes wrong if it is not the
+    exact nearest magnitude: midpoints of both types times absmax, rounded to
+    binary32, with their neighbours two ulps either way; exact ties (midpoints
+    that binary32 holds, times a power-of-two absmax); values uniform and
+    log-uniform below absmax, both signs; the block's own absmax; +-0 and
+    NaN; absmax from subnormal to the largest binary32, 0 and +inf."""
+    gen = np.random.default_rng(8080)
+    f32 = np.float32
+    fmax = np.finfo(np.float32).max
+    mids = []
+    for signed in (True, False):
+        mags = orc.qmap(signed).astype(np.float64)
+        mids.append((mags[:-1] + mags[1:]) / 2)
+    mids = np.concatenate(mids)
+    ties = np.unique(mids[mids.astype(np.float32).astype(np.float64) == mids])
+    vals, amax = [], []
+    for A in [f32(1.0), f32(0.7), f32(1.234567e-3), f32(2.0 ** -149), f32(3 * 2.0 ** -140),
+              f32(2.0 ** -130), f32(3.4e38), fmax, f32(2.0 ** 100), f32(2.0 ** -20)]:
+        near = (mids * float(A)).astype(np.float32)
+        group = [near]
+        for k in (1, 2):
+            up, dn = near.copy(), near.copy()
+            for _ in range(k):
+                up = np.nextafter(up, f32(np.inf))
+                dn = np.nextafter(dn, f32(0))
+            group += [up, dn]
+        group += [(gen.uniform(0, 1, 3000) * float(A)).astype(np.float32),
+                  (10.0 ** gen.uniform(-10, 0, 3000) * float(A)).astype(np.float32),
+                  np.array([A, 0.0], np.float32)]
+        if float(A) in (1.0, 2.0 ** -20, 2.0 ** 100, 2.0 ** -130):   # powers of two: exact ties
+            group.append((ties * float(A)).astype(np.float32))
+        v = np.concatenate(group)
+        v = v[np.abs(v) <= A]
+        v = np.concatenate([v, -v[::3], np.array([-0.0, np.nan], np.float32)])
+        vals.append(v)
+        amax.append(np.full(v.size, A, np.float32))
+    # absmax 0 (a block of zeros and NaNs) and +inf (finite values, and +-inf)
+    vals.append(np.array([0.0, -0.0, np.nan], np.float32))
+    amax.append(np.zeros(3, np.float32))
+    v = np.array([0.0, 1.0, -2.0, 3e38, -1e-30, np.inf, -np.inf, np.nan], np.float32)
+    vals.append(v)
+    amax.append(np.full(v.size, np.inf, np.float32))
+    return np.concatenate(vals), np.concatenate(amax)
+
+
+def test_device_quantizer_matches_oracle(orc, L):
+    """The kernels' quantizer (the ou__quant8 hook runs the update kernels'
+    composition: reciprocal of absmax, offset estimate, LDS key table, one
+    exact binary64 comparison) gives the oracle's code on every pair of
+    _quantizer_cases: signed code of the value, unsigned code of |value|."""
+    v, a = _quantizer_cases(orc)
+    n = v.size
+    dv = torch.from_numpy(v).cuda()
+    da = torch.from_numpy(a).cuda()
+    cs = torch.full((n,), 0xAA, dtype=torch.uint8, device="cuda")
+    cu = torch.full((n,), 0xAA, dtype=torch.uint8, device="cuda")
+    st = L.ou__quant8(dv.data_ptr(), da.data_ptr(), cs.data_ptr(), cu.data_ptr(), n, H.stream_handle())
+    assert st == 0, H.last_error(L)
+    got_s = cs.cpu().numpy()
+    got_u = cu.cpu().numpy()
+    want_s = np.array([orc.qcode(True, float(x), float(y)) for x, y in zip(v, a)], np.uint8)
+    want_u = np.array([orc.qcode(False, abs(float(x)), float(y)) for x, y in zip(v, a)], np.uint8)
+    bad_s = np.nonzero(got_s != want_s)[0]
+    bad_u = np.nonzero(got_u != want_u)[0]
+    assert bad_s.size == 0, [(float(v[i]), float(a[i]), int(got_s[i]), int(want_s[i])) for i in bad_s[:5]]
+    assert bad_u.size == 0, [(float(v[i]), float(a[i]), int(got_u[i]), int(want_u[i])) for i in bad_u[:5]]
+    assert n > 50000
