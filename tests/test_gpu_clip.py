@@ -6,8 +6,9 @@ whose order differs between the GPU (fixed chunk tree) and the oracle
 last bit except when it lies that close to a binary32 rounding boundary.
 The tests therefore require: moments bitwise equal to the oracle (they do
 not depend on s), s within 1 ulp of the oracle's, parameters within the
-parity tolerance (and report whether they are bitwise equal); and, across
-the GPU's own launch variants, everything bitwise identical.
+parity tolerance, and bitwise equal whenever every step's s equals the
+oracle's (all but at most two of the cases); and, across the GPU's own
+launch variants, everything bitwise identical.
 """
 from __future__ import annotations
 
@@ -83,8 +84,14 @@ def test_clip_matches_oracle(kind, storage):
             r = H.assert_parity(P, pr, storage, "p " + what, bitwise=False)
             H.assert_parity(S1, s1r, "fp32", "state1 " + what)
             H.assert_parity(S2, s2r, "fp32", "state2 " + what)
+            if [np.float32(x).tobytes() for x in scales] == [np.float32(x).tobytes() for x in oscales]:
+                # every step's clip factor equal to the oracle's: the rest of
+                # the step is the same binary32 arithmetic, so p is bitwise equal
+                assert r["bitwise"], (what, r)
             report.append((n, bound, r["bitwise"], scales == oscales))
     print("clip parity (n, max_unorm, p bitwise, s bitwise):", report)
+    # the factors differ only next to a rounding boundary of binary32
+    assert sum(1 for x in report if x[3]) >= len(report) - 2, report
 
 
 @pytest.mark.parametrize("kind", ["adam", "ademamix"])
@@ -160,7 +167,9 @@ def test_clip_large_tensor_full_compare():
                for t, g in enumerate(gsteps, start=1)]
     assert all(_ulps(a, b) <= 1 for a, b in zip(scales, oscales)), (scales, oscales)
     assert max(oscales) < 1.0
-    H.assert_parity(P, pr, "fp32", "p 2^26", bitwise=False)
+    r = H.assert_parity(P, pr, "fp32", "p 2^26", bitwise=False)
+    if [np.float32(x).tobytes() for x in scales] == [np.float32(x).tobytes() for x in oscales]:
+        assert r["bitwise"], r   # equal clip factors: the rest is the same binary32 arithmetic
     H.assert_parity(S1, s1r, "fp32", "m 2^26")
     H.assert_parity(S2, s2r, "fp32", "v 2^26")
 
